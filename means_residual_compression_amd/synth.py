@@ -1,0 +1,176 @@
+"""Seeded synthetic inputs shaped like the video KV caches the QVG pages evaluate on.
+
+This module only draws random numbers and lays them out; it holds none of the
+compression method's arithmetic, so both the CPU oracle and the HIP path can be
+fed from it without sharing any of the method.
+
+The pages' real caches (LongCat-Video-13B, HY-WorldPlay-8B, Self-Forcing-Wan-1.3B;
+howistudyai.com page, "The test" section) are not available, so these stand in
+for them.  Every generator is a pure function of its integer seed.
+
+Token model (one head of K or V), following the pages' spatiotemporal-redundancy
+description (note.zhuruihan.top, "Semantic-Aware Smoothing"; paper.rainbus.top,
+novelty paragraph: max|K| ~ 1e2, max|V| ~ 1e3):
+
+    token(f, y, x) = base[y, x] + 0.05 * f * drift[y, x] + eps,
+    base, drift ~ N(0, 1)^d,   eps ~ N(0, 0.1^2)^d,
+
+with 4 outlier channels per head (drawn from a seeded permutation) whose base
+entries are multiplied by `outlier_scale`.  Tokens are ordered
+i = f * (Hg * Wg) + y * Wg + x.  Values are drawn in float64 and rounded (RNE)
+to the storage dtype.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+K_KIND, V_KIND = 0, 1
+OUTLIER_SCALE = {K_KIND: 1e2, V_KIND: 1e3}
+
+
+def _rng(*key: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([int(k) for k in key]))
+
+
+def round_to(x64: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
+    """fp64 numpy array -> CPU tensor of `dtype` (RNE through fp32)."""
+    t = torch.from_numpy(np.ascontiguousarray(x64, dtype=np.float32))
+    return t.to(dtype) if dtype != torch.float32 else t
+
+
+def _head_fields(rng: np.random.Generator, Hg: int, Wg: int, d: int, outlier_scale: float):
+    outl = rng.permutation(d)[:4]
+    base = rng.standard_normal((Hg, Wg, d))
+    drift = rng.standard_normal((Hg, Wg, d))
+    base[..., outl] *= outlier_scale
+    return base, drift, outl
+
+
+def video_head(seed: int, F: int, Hg: int, Wg: int, d: int, outlier_scale: float,
+               scene_len: int | None = None, n_tokens: int | None = None) -> np.ndarray:
+    """One head-tensor [N, d] (fp64).  With `scene_len`, base and drift are
+    re-drawn every `scene_len` frames and f restarts at 0 in each scene.
+    `n_tokens` truncates the (F x Hg x Wg) grid in token order."""
+    rng = _rng(seed)
+    P = Hg * Wg
+    N = F * P if n_tokens is None else n_tokens
+    out = np.empty((N, d), dtype=np.float64)
+    fields = None
+    for f in range(F):
+        lo = f * P
+        if lo >= N:
+            break
+        if scene_len is None:
+            if fields is None:
+                fields = _head_fields(rng, Hg, Wg, d, outlier_scale)
+            fl = f
+        else:
+            if f % scene_len == 0:
+                fields = _head_fields(rng, Hg, Wg, d, outlier_scale)
+            fl = f % scene_len
+        base, drift, _ = fields
+        hi = min(N, lo + P)
+        frame = base + 0.05 * fl * drift + 0.1 * rng.standard_normal((Hg, Wg, d))
+        out[lo:hi] = frame.reshape(P, d)[: hi - lo]
+    return out
+
+
+def video_cache(cfg: int, kind: int, heads: int, F: int, Hg: int, Wg: int, d: int,
+                outlier_scale: float, dtype: torch.dtype, scene_len: int | None = None,
+                n_tokens: int | None = None, head_ids=None) -> torch.Tensor:
+    """[heads, N, d] CPU tensor; head h uses seed (1000 + 100*cfg + h, kind)."""
+    ids = range(heads) if head_ids is None else head_ids
+    hs = [video_head(_seed(cfg, kind, h), F, Hg, Wg, d, outlier_scale, scene_len, n_tokens)
+          for h in ids]
+    return round_to(np.stack(hs), dtype)
+
+
+def _seed(cfg: int, kind: int, h: int) -> int:
+    return (1000 + 100 * cfg + h) * 2 + kind
+
+
+# ---------------------------------------------------------------- stream chunks
+def stream_chunk(cfg: int, kind: int, heads: int, chunk: int, frames_per_chunk: int,
+                 Hg: int, Wg: int, d: int, outlier_scale: float,
+                 dtype: torch.dtype) -> torch.Tensor:
+    """Chunk `chunk` of a continuing video: global frames
+    [chunk*fpc, (chunk+1)*fpc); base and drift are fixed per head, so each
+    chunk continues the previous chunk's drift."""
+    P = Hg * Wg
+    out = np.empty((heads, frames_per_chunk * P, d), dtype=np.float64)
+    for h in range(heads):
+        base, drift, _ = _head_fields(_rng(_seed(cfg, kind, h)), Hg, Wg, d, outlier_scale)
+        rng = _rng(_seed(cfg, kind, h), chunk + 1)
+        for j in range(frames_per_chunk):
+            f = chunk * frames_per_chunk + j
+            frame = base + 0.05 * f * drift + 0.1 * rng.standard_normal((Hg, Wg, d))
+            out[h, j * P:(j + 1) * P] = frame.reshape(P, d)
+    return round_to(out, dtype)
+
+
+# ---------------------------------------------------------------- k-means init draws
+def init_indices(seed: int, H: int, T: int, N: int, C: int) -> np.ndarray:
+    """Seeded cold-start draw: for each (head, stage) C distinct token indices
+    in [0, N), as int32 [H, T, C].  This is the random draw the method makes at
+    k-means initialisation; it is an input to both implementations."""
+    out = np.empty((H, max(T, 1), C), dtype=np.int32)
+    for h in range(H):
+        for t in range(max(T, 1)):
+            out[h, t] = _rng(seed, h, t).choice(N, size=C, replace=False)
+    return out[:, :T] if T > 0 else out[:, :0]
+
+
+# ---------------------------------------------------------------- named workloads
+CONFIGS = {
+    # name: (cfg id, F, Hg, Wg, d, heads per kind, dtype, kinds, scene_len, N)
+    0: dict(F=16, Hg=16, Wg=16, d=64, heads=1, dtype=torch.float32, kinds=(K_KIND,),
+            outlier={K_KIND: 50.0}, C=16, T=1, iters=10, bits=2, group=32),
+    1: dict(F=21, Hg=30, Wg=52, d=128, heads=12, dtype=torch.bfloat16, kinds=(K_KIND, V_KIND),
+            outlier=OUTLIER_SCALE, C=256, T=2, iters=8, bits=2, group=64),
+    2: dict(F=3, Hg=30, Wg=52, d=128, heads=12, dtype=torch.bfloat16, kinds=(K_KIND, V_KIND),
+            outlier=OUTLIER_SCALE, C=256, T=2, iters=10, iters_warm=3, bits=2, group=64,
+            chunks=20),
+    3: dict(F=85, Hg=39, Wg=40, d=128, heads=32, dtype=torch.bfloat16, kinds=(K_KIND, V_KIND),
+            outlier=OUTLIER_SCALE, C=256, T=4, iters=8, bits=2, group=64, scene_len=21,
+            n_tokens=131072),
+}
+
+
+def config_cache(cfg: int, heads: int | None = None, n_tokens: int | None = None) -> torch.Tensor:
+    """All head-tensors of a configuration stacked K-then-V: [kinds*heads, N, d].
+    `heads`/`n_tokens` give a smaller sample of the same workload."""
+    c = CONFIGS[cfg]
+    nh = c["heads"] if heads is None else heads
+    N = c.get("n_tokens") if n_tokens is None else n_tokens
+    parts = [video_cache(cfg, k, nh, c["F"], c["Hg"], c["Wg"], c["d"], c["outlier"][k],
+                         c["dtype"], c.get("scene_len"), N) for k in c["kinds"]]
+    return torch.cat(parts, 0)
+
+
+# ---------------------------------------------------------------- decode-side record
+def random_record(seed: int, H: int, N: int, d: int, T: int, C: int, bits: int, group: int,
+                  Hg: int = 512, Wg: int = 512):
+    """A pre-compressed record drawn directly from a seed (decode-only workload):
+    uniform random code bytes; per-group FP8 scale bytes drawn uniformly from
+    the E4M3 codes of small positive values; per-stage assignments that are
+    spatially coherent (a hash of the 4x4 patch block and the stage); bf16
+    centroids ~ N(0, 4^-t).  Tokens are laid out on an Hg x Wg grid (frames
+    follow in token order).  Returns numpy/torch CPU arrays."""
+    rng = _rng(seed)
+    codes = rng.integers(0, 256, size=(H, N, d * bits // 8), dtype=np.uint8)
+    # E4M3 bytes 0x18..0x3F cover roughly 0.02..1.9 (exponent field 3..7).
+    scales = rng.integers(0x18, 0x40, size=(H, N, d // group), dtype=np.uint8)
+    i = np.arange(N)
+    y = (i // Wg) % Hg
+    x = i % Wg
+    assign = np.empty((H, T, N), dtype=np.uint8)
+    for h in range(H):
+        for t in range(T):
+            salt = _rng(seed, h, t).integers(0, 2**31)
+            key = (y // 4) * 1_000_003 + (x // 4) * 7919 + salt
+            key = (key * 2654435761) % (2**32)
+            assign[h, t] = ((key >> 8) % C).astype(np.uint8)
+    cents = np.stack([np.stack([rng.standard_normal((C, d)) * (0.5 ** (t + 1)) for t in range(T)])
+                      for _ in range(H)])
+    return codes, scales, assign, round_to(cents, torch.bfloat16)

@@ -1,0 +1,180 @@
+"""QVG CPU oracle (test infrastructure only).
+
+Plain C implementation in ``qvg_oracle.c`` (see its header for the passages of
+the Quant VideoGen pages each function follows), loaded with ctypes and wrapped
+for numpy arrays.  Only the tests, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` use this package; the product library never does.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qvg_oracle.c")
+_LIB = os.path.join(_HERE, "libqvg_oracle.so")
+GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+             "-pthread"]
+
+DT_F32, DT_BF16 = 0, 1
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ct.CDLL(_LIB)
+        p, i64, i32, f32 = ct.c_void_p, ct.c_int64, ct.c_int, ct.c_float
+        L.qvgo_e4m3_encode.argtypes, L.qvgo_e4m3_encode.restype = [f32], ct.c_uint8
+        L.qvgo_e4m3_decode.argtypes, L.qvgo_e4m3_decode.restype = [ct.c_uint8], f32
+        L.qvgo_f32_to_bf16.argtypes, L.qvgo_f32_to_bf16.restype = [f32], ct.c_uint16
+        L.qvgo_dist.argtypes, L.qvgo_dist.restype = [p, p, i32], ct.c_double
+        L.qvgo_assign.argtypes = [p, i64, i32, p, i32, p]
+        L.qvgo_update.argtypes = [p, i64, i32, p, i32, p, p]
+        L.qvgo_kmeans.argtypes = [p, i64, i32, p, i32, i32, p]
+        L.qvgo_quantize.argtypes = [p, i64, i32, i32, i32, p, p]
+        L.qvgo_compress.argtypes = [p, i32, i64, i64, i32, i32, i32, i32, i32, i32, p, p,
+                                    p, p, p, p, p, i32]
+        L.qvgo_decompress.argtypes = [p, p, p, p, i32, i64, i64, i32, i32, i32, i32, i32,
+                                      p, i32, i32]
+        for f in ("qvgo_assign", "qvgo_update", "qvgo_kmeans", "qvgo_quantize",
+                  "qvgo_compress", "qvgo_decompress"):
+            getattr(L, f).restype = None
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ct.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+# ----------------------------------------------------------------- codecs
+def e4m3_encode(s: float) -> int:
+    return int(lib().qvgo_e4m3_encode(float(s)))
+
+
+def e4m3_decode(code: int) -> float:
+    return float(lib().qvgo_e4m3_decode(int(code)))
+
+
+def f32_to_bf16_bits(x: float) -> int:
+    return int(lib().qvgo_f32_to_bf16(float(x)))
+
+
+# ---------------------------------------------------------------- k-means
+def dist(r, c) -> float:
+    r = _c(r, np.float32)
+    c = _c(c, np.float32)
+    return float(lib().qvgo_dist(_ptr(r), _ptr(c), r.shape[-1]))
+
+
+def assign(R, C) -> np.ndarray:
+    R = _c(R, np.float32)
+    C = _c(C, np.float32)
+    pi = np.empty(R.shape[0], np.int32)
+    lib().qvgo_assign(_ptr(R), R.shape[0], R.shape[1], _ptr(C), C.shape[0], _ptr(pi))
+    return pi
+
+
+def update(R, pi, C):
+    """Returns (new centroids, counts); C is not modified."""
+    R = _c(R, np.float32)
+    pi = _c(pi, np.int32)
+    Cn = np.array(C, dtype=np.float32, copy=True, order="C")
+    cnt = np.empty(Cn.shape[0], np.int64)
+    lib().qvgo_update(_ptr(R), R.shape[0], R.shape[1], _ptr(pi), Cn.shape[0], _ptr(Cn),
+                      _ptr(cnt))
+    return Cn, cnt
+
+
+def kmeans(R, C0, iters):
+    R = _c(R, np.float32)
+    C = np.array(C0, dtype=np.float32, copy=True, order="C")
+    pi = np.zeros(R.shape[0], np.int32)
+    lib().qvgo_kmeans(_ptr(R), R.shape[0], R.shape[1], _ptr(C), C.shape[0], iters, _ptr(pi))
+    return C, pi
+
+
+def quantize(R, bits, G):
+    R = _c(R, np.float32)
+    N, d = R.shape
+    codes = np.empty((N, d * bits // 8), np.uint8)
+    scales = np.empty((N, d // G), np.uint8)
+    lib().qvgo_quantize(_ptr(R), N, d, bits, G, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+# ------------------------------------------------------------ whole path
+def _as_store(X):
+    """numpy fp32 -> (array, DT_F32); bf16 given as uint16 bit patterns -> DT_BF16."""
+    if X.dtype == np.uint16:
+        return _c(X, np.uint16), DT_BF16
+    return _c(X, np.float32), DT_F32
+
+
+def compress(X, C, T, iters, bits, G, init_idx=None, init_c=None, threads=None):
+    """X: [H, N, d] fp32, or bf16 bit patterns as uint16.  Returns dict with
+    codes, scales, assign [H,T,N] uint8, cent [H,T,C,d] (same storage as X),
+    cache [H,T,C,d] fp32."""
+    X, dt = _as_store(X)
+    H, N, d = X.shape
+    if T > 0 and init_idx is None and init_c is None:
+        raise ValueError("cold start needs init_idx or init_c")
+    idx = None if init_idx is None else _c(init_idx, np.int32)
+    ic = None if init_c is None else _c(init_c, np.float32)
+    out = dict(codes=np.empty((H, N, d * bits // 8), np.uint8),
+               scales=np.empty((H, N, d // G), np.uint8),
+               assign=np.zeros((H, T, N), np.uint8),
+               cent=np.zeros((H, T, C, d), X.dtype),
+               cache=np.zeros((H, T, C, d), np.float32))
+    lib().qvgo_compress(_ptr(X), dt, H, N, d, C, T, iters, bits, G, _ptr(idx), _ptr(ic),
+                        _ptr(out["codes"]), _ptr(out["scales"]), _ptr(out["assign"]),
+                        _ptr(out["cent"]), _ptr(out["cache"]), threads or default_threads())
+    return out
+
+
+def decompress(codes, scales, assign, cent, bits, G, out_bf16=None, threads=None):
+    """cent: [H,T,C,d] fp32 or uint16 (bf16 bits).  Output dtype follows the
+    centroid storage unless out_bf16 is given.  Returns fp32 array or uint16
+    bf16 bit patterns."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    assign = _c(assign, np.uint8)
+    cent, cdt = _as_store(cent)
+    H, T, C, d = cent.shape if cent.ndim == 4 else (codes.shape[0], 0, 1, codes.shape[2] * 8 // bits)
+    N = codes.shape[1]
+    if out_bf16 is None:
+        out_bf16 = cdt == DT_BF16
+    out = np.empty((H, N, d), np.uint16 if out_bf16 else np.float32)
+    lib().qvgo_decompress(_ptr(codes), _ptr(scales), _ptr(assign), _ptr(cent), cdt, H, N, d, C,
+                          T, bits, G, _ptr(out), DT_BF16 if out_bf16 else DT_F32,
+                          threads or default_threads())
+    return out
+
+
+def bf16_bits_to_f32(b) -> np.ndarray:
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
