@@ -1,0 +1,193 @@
+/*
+ * qvg.h -- C ABI of the QVG KV-cache compress/decompress library for MI355X
+ * (gfx950).  Implements the hot path of Quant VideoGen ("Auto-Regressive Long
+ * Video Generation via 2-Bit KV-Cache Quantization"), as described on:
+ *
+ *   note.zhuruihan.top  -- sections "Semantic-Aware Smoothing",
+ *                          "Progressive Residual Quantization",
+ *                          "Algorithm-System Co-design";
+ *   paper.rainbus.top   -- method paragraph (SAS steps a-c, PRQ, Q, DQ);
+ *   howistudyai.com     -- "Step-by-step" (chunking, C=256, uint8 assignments).
+ *
+ * One "head-tensor" is one X in R^{N x d} (one attention head of K or of V).
+ * H head-tensors are processed per call, all independent.
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are HIP device memory owned by the caller, contiguous,
+ *    row-major, with the shapes given below.  Host pointers are marked (host).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously; no entry point synchronises the stream, except that a
+ *    host-memory argument (init_idx) is copied before the call returns.
+ *  - Arguments are validated on the host before anything is enqueued; an
+ *    invalid call returns a status and enqueues nothing.  The library never
+ *    aborts and allocates no device memory: scratch comes from the caller's
+ *    workspace.  qvg_last_error() describes the most recent failure of the
+ *    calling thread.
+ *  - Inputs must be finite.  Results for NaN/Inf inputs are unspecified.
+ *  - Results are deterministic: the same inputs give bit-identical outputs.
+ *  - Calls that share a workspace or an output buffer on the same stream are
+ *    ordered by the stream; concurrent calls on different streams need their
+ *    own workspaces.
+ */
+#ifndef QVG_H
+#define QVG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QVG_OK = 0,
+    QVG_ERR_INVALID_ARG = 1, /* null pointer, bad size or inconsistent arguments */
+    QVG_ERR_UNSUPPORTED = 2, /* well-formed but outside what the kernels implement */
+    QVG_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the size query */
+    QVG_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} qvg_status;
+
+typedef enum { QVG_F32 = 0, QVG_BF16 = 1 } qvg_dtype;
+
+/* Method parameters.
+ *   C      clusters per stage (k-means k), 1 <= C <= 256 (assignments are
+ *          stored as uint8, howistudyai.com "Step-by-step"), C <= N.
+ *   T      progressive residual stages, 0 <= T <= 8 (T = 0 is plain
+ *          per-group quantization of X).
+ *   iters  k-means iterations per stage, each one assign followed by one
+ *          update; >= 1 when T >= 1.  The stored assignments come from the
+ *          last assign, the stored centroids from the last update.
+ *   bits   2 or 4 (INT2 / INT4 codes).
+ *   group  G, channels per quantization group along d; d % G == 0 and
+ *          G % 8 == 0, 8 <= G <= 256.
+ * Supported head dims: d in {64, 128}. */
+typedef struct {
+    int32_t C;
+    int32_t T;
+    int32_t iters;
+    int32_t bits;
+    int32_t group;
+} qvg_params;
+
+/* A compressed record of H head-tensors (paper.rainbus.top, method paragraph:
+ * X_INT and S_x, plus C(t) and pi(t) for every stage).
+ *   codes      [H][N][d*bits/8]  packed codes; element k of a token row sits
+ *                                in byte k*bits/8 at bit offset
+ *                                bits*(k mod 8/bits), little-endian.
+ *   scales     [H][N][d/G]       FP8 E4M3 (OCP e4m3fn) scale codes, >= 0.
+ *   assign     [H][T][N]         uint8 cluster index of each token per stage.
+ *   centroids  [H][T][C][d]      stage centroids in the record dtype (the
+ *                                dtype of X: bf16 or fp32).
+ * Quantized level of code q: (2q - (2^bits - 1)) * scale. */
+typedef struct {
+    uint8_t *codes;
+    uint8_t *scales;
+    uint8_t *assign;
+    void *centroids;
+} qvg_record;
+
+/* Human-readable name of a status code (static string). */
+const char *qvg_status_string(qvg_status s);
+
+/* Message for the calling thread's most recent non-OK status (static
+ * thread-local buffer; "" if none). */
+const char *qvg_last_error(void);
+
+/* Bytes of device workspace that qvg_compress / qvg_compress_stream need for
+ * these sizes; 0 if the arguments are invalid.  The workspace must be 256-byte
+ * aligned. */
+size_t qvg_workspace_size(int64_t H, int64_t N, int64_t d, qvg_dtype dtype,
+                          const qvg_params *p);
+
+/* Compress H head-tensors X [H][N][d] (bf16 or fp32) into `out`.
+ *
+ * note.zhuruihan.top "Semantic-Aware Smoothing" and "Progressive Residual
+ * Quantization"; paper.rainbus.top method paragraph.  R(0) = X; for stage
+ * t = 1..T: k-means (squared Euclidean, ties to the smallest index, empty
+ * clusters keep their centroid) over the tokens of R(t-1) for `iters`
+ * iterations; the centroids rounded to the record dtype are stored and
+ * subtracted, R(t) = R(t-1) - C(t)[pi(t)] in fp32.  R(T) is quantized per
+ * group of G channels: s = max|r| / (2^b - 1) rounded to the nearest finite
+ * E4M3 value (ties to even, saturating at 448); code q = nearest level, a tie
+ * going to the upper level; a zero scale gives the middle code everywhere.
+ *
+ * Stage-t k-means starts from:
+ *   init_idx (host, int32 [H][T][C]): rows init_idx[h][t][0..C) of R(t-1);
+ *            indices must be in [0, N) (duplicates allowed);
+ *   else init_centroids (device, fp32 [H][T][C][d]).
+ * Exactly one of them must be non-NULL when T >= 1.
+ * cache_out (device, fp32 [H][T][C][d], nullable) receives each stage's final
+ * fp32 centroids before rounding (the streaming centroid cache).
+ * Workspace: `ws` of at least qvg_workspace_size() bytes. */
+qvg_status qvg_compress(const void *x, qvg_dtype dtype, int64_t H, int64_t N, int64_t d,
+                        const qvg_params *p, const int32_t *init_idx,
+                        const float *init_centroids, float *cache_out, const qvg_record *out,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* Streaming compress of one chunk [H][N][d] with the centroid cache
+ * (note.zhuruihan.top "Algorithm-System Co-design": the previous chunk's
+ * centroids initialise the next chunk's k-means).
+ *   cache (device, fp32 [H][T][C][d]) is read as the stage initialisation when
+ *   warm != 0 and is overwritten with this chunk's final centroids.
+ *   warm != 0: k-means runs `iters_warm` iterations from the cache.
+ *   warm == 0: k-means runs p->iters iterations from init_idx (host, as in
+ *   qvg_compress).
+ * The record is self-contained: decompress needs no other chunk. */
+qvg_status qvg_compress_stream(const void *chunk, qvg_dtype dtype, int64_t H, int64_t N,
+                               int64_t d, const qvg_params *p, int32_t iters_warm, float *cache,
+                               int warm, const int32_t *init_idx, const qvg_record *out, void *ws,
+                               size_t ws_bytes, void *stream);
+
+/* Fused decompression (paper.rainbus.top method paragraph, DQ;
+ * note.zhuruihan.top "Algorithm-System Co-design", fused dequantization
+ * kernel): per element x = level(q) * scale, then x += C(t)[pi(t)] for
+ * t = T down to 1 in fp32, rounded once (RNE) to out_dtype.
+ *   rec_dtype: dtype of rec->centroids.  out: device [H][N][d] in out_dtype. */
+qvg_status qvg_decompress(const qvg_record *rec, qvg_dtype rec_dtype, int64_t H, int64_t N,
+                          int64_t d, const qvg_params *p, void *out, qvg_dtype out_dtype,
+                          void *stream);
+
+/* ---- single steps of the path (each is one piece of the compress above) ---- */
+
+/* Bytes of workspace qvg_kmeans_assign needs. */
+size_t qvg_assign_workspace_size(int64_t H, int64_t N, int64_t d, int32_t C);
+
+/* k-means assignment step (paper.rainbus.top method paragraph, SAS a):
+ * assign[h][i] = argmin_j ||r_hi - c_hj||^2 with fp64 distances, ties to the
+ * smallest j.  r: device [H][N][d] (dtype); centroids: device fp32 [H][C][d];
+ * assign: device uint8 [H][N]. */
+qvg_status qvg_kmeans_assign(const void *r, qvg_dtype dtype, int64_t H, int64_t N, int64_t d,
+                             const float *centroids, int32_t C, uint8_t *assign, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/* Bytes of workspace qvg_kmeans_update needs. */
+size_t qvg_update_workspace_size(int64_t H, int64_t N, int32_t C);
+
+/* k-means update step (note.zhuruihan.top SAS step 2, centroid = mean value):
+ * centroids[h][j] = fp32(sum_{i: assign=j} r_hi / n_j) with the sum in fp64
+ * in token order; clusters with no member keep their value.
+ * centroids: device fp32 [H][C][d], read and written. */
+qvg_status qvg_kmeans_update(const void *r, qvg_dtype dtype, int64_t H, int64_t N, int64_t d,
+                             const uint8_t *assign, int32_t C, float *centroids, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/* Centroid subtraction (paper.rainbus.top method paragraph, SAS c):
+ * r_out[h][i] = fp32(r[h][i] - chat[h][assign[h][i]]).  chat: device
+ * [H][C][d] in cdtype; r_out: device fp32 [H][N][d] (may alias r when r is
+ * fp32). */
+qvg_status qvg_sas_subtract(const void *r, qvg_dtype dtype, int64_t H, int64_t N, int64_t d,
+                            const uint8_t *assign, const void *chat, qvg_dtype cdtype, int32_t C,
+                            float *r_out, void *stream);
+
+/* Group quantization and packing of a residual (paper.rainbus.top method
+ * paragraph, Q) as in qvg_compress.  r: device [H][N][d] (dtype); codes
+ * [H][N][d*bits/8]; scales [H][N][d/group]. */
+qvg_status qvg_group_quant_pack(const void *r, qvg_dtype dtype, int64_t H, int64_t N, int64_t d,
+                                int32_t bits, int32_t group, uint8_t *codes, uint8_t *scales,
+                                void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QVG_H */

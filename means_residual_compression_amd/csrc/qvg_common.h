@@ -1,0 +1,132 @@
+// Internal definitions shared by the QVG HIP kernels and host code (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qvg {
+
+constexpr int kMaxC = 256;  // assignments are uint8
+constexpr int kMaxT = 8;
+constexpr int kTile = 32;   // tokens (and centroids) per 32x32 MFMA tile
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// Per-head statistics, one row of kStatWords uint32 per (head, stage).
+// Non-negative floats are stored as their bit patterns so that integer
+// atomicMax is an order-independent (deterministic) float max.
+enum StatSlot : int {
+  S_MAXR = 0,    // max |r| over the stage's input residual
+  S_MAXC = 1,    // max |c| over the stage's initial centroids
+  S_B0 = 2,      // bounds of the current centroid table, double-buffered:
+                 // [2 + 4*p + 0] max ||c*sc||, [+1] max ||c*sc - fp16(c*sc)||,
+                 // [+2] max ||fp16(c*sc)||, [+3] max ||c*sc||^2
+  kStatWords = 16,
+};
+
+// Device scratch carved from the caller's workspace.
+struct Ws {
+  float *rbuf;        // fp32 [H][N][d]   residual R(t) between stages
+  half8 *rt;          // fp16 fragments [H][NT][KC][64] of the scaled residual
+  float2 *tb;         // [H][NT*32]        per-token (||r~||, ||r*sc - r~||) bounds
+  float *cent;        // fp32 [H][Cp][d]   working centroids
+  half8 *ctab;        // fp16 fragments [H][CB][KC][64] of the scaled centroids
+  float *cinit;       // fp32 [H][CB][2][16] accumulator init -||c*sc||^2 / 2
+  uint32_t *stats;    // [H][T'][kStatWords]
+  int4 *recheck;      // [H*NT*32] (head, token, j1, j2)
+  int2 *fallback;     // [H*NT*32] (head, token)
+  uint32_t *counters; // [4]: 0 recheck entries, 1 fallback entries
+  int32_t *sorted;    // [H][N] token ids grouped by cluster, token order inside
+  int32_t *offs;      // [H][Cp+1] cluster segment offsets into `sorted`
+  int32_t *idx;       // [H][T][C] device copy of the seeded init indices
+};
+
+__host__ __device__ inline int pad32(int x) { return (x + 31) & ~31; }
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+// Round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static __forceinline__ float get(const float *p, int64_t i) { return p[i]; }
+  __device__ static __forceinline__ void put(float *p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ static __forceinline__ float get(const uint16_t *p, int64_t i) {
+    return bf16_to_f32(p[i]);
+  }
+  __device__ static __forceinline__ void put(uint16_t *p, int64_t i, float v) {
+    p[i] = f32_to_bf16(v);
+  }
+};
+
+// Load 8 consecutive elements starting at p[i] (i multiple of 8) as fp32.
+__device__ __forceinline__ void load8(const float *p, int64_t i, float v[8]) {
+  const float4 a = *reinterpret_cast<const float4 *>(p + i);
+  const float4 b = *reinterpret_cast<const float4 *>(p + i + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void load8(const uint16_t *p, int64_t i, float v[8]) {
+  const uint4 a = *reinterpret_cast<const uint4 *>(p + i);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    v[2 * m] = __uint_as_float(w[m] << 16);
+    v[2 * m + 1] = __uint_as_float(w[m] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void store8(float *p, int64_t i, const float v[8]) {
+  *reinterpret_cast<float4 *>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4 *>(p + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void store8(uint16_t *p, int64_t i, const float v[8]) {
+  uint4 a;
+  a.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  a.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  a.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+  a.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+  *reinterpret_cast<uint4 *>(p + i) = a;
+}
+
+// -------------------------------------------------------------- FP8 E4M3
+// OCP E4M3 ("e4m3fn"): 4 exponent bits (bias 7), 3 mantissa bits, largest
+// finite 448.  Encode s >= 0 with round-to-nearest-even, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+  if (!(s < 464.0f)) return 0x7Eu;  // >= 464 (and the tie at 464) -> 448
+  if (s < 0.015625f) {              // below 2^-6: subnormal grid m * 2^-9
+    return (uint32_t)__builtin_rintf(s * 512.0f);  // 0..8; 8 is 2^-6 (code 8)
+  }
+  const uint32_t u = __float_as_uint(s);
+  // keep 3 mantissa bits with round-to-nearest-even (carries into the exponent)
+  const uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;
+  return r - ((127u - 7u) << 3);
+}
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Power-of-two exponent e such that values up to `m` scaled by 2^-e stay
+// below 2^14 (well inside fp16 range).
+__device__ __forceinline__ int scale_exp(float m) {
+  if (!(m > 0.0f)) return 0;
+  return ilogbf(m) - 13;
+}
+
+__device__ __forceinline__ float stat_f(const uint32_t *s, int slot) {
+  return __uint_as_float(s[slot]);
+}
+
+}  // namespace qvg

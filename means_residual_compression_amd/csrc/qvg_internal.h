@@ -1,0 +1,54 @@
+// Host-side launcher interface between the C ABI and the kernel files.
+#pragma once
+
+#include <algorithm>
+
+#include "qvg_common.h"
+
+namespace qvg {
+
+// Everything one stage of k-means needs.  `r` is the stage input residual
+// [H][N][D] (bf16 X at the first stage, fp32 afterwards).
+struct KmArgs {
+  int H, N, C, Cp, NT;
+  const void *r;
+  const int32_t *idx;  // device [H][..][C] init rows, or nullptr
+  int64_t idx_hstride;
+  const float *init;   // device [H][..][C][D] init centroids, or nullptr
+  int64_t init_hstride;
+  uint8_t *assign;     // stage slice of [H][T][N]
+  int64_t assign_hstride;
+  Ws ws;
+  uint32_t *ws_stats;  // stats row of this stage; per-head stride stat_stride
+  int stat_stride;
+  float kappa;         // relative error coefficient of the MFMA keys
+};
+
+template <typename Tin>
+bool launch_absmax(const void *x, int H, int64_t per_head, uint32_t *stats, int stat_stride,
+                   int slot, hipStream_t s);
+template <typename Tin, int D>
+bool launch_kmeans_stage_begin(const KmArgs &a, hipStream_t s);
+template <typename Tin, int D>
+bool launch_assign(const KmArgs &a, int bslot, hipStream_t s);
+template <typename Tin, typename Tc, int D>
+bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int64_t rec_hstride,
+                   float *cache, int64_t cache_hstride, hipStream_t s);
+
+// Elementwise kernels (qvg_quant.hip).
+bool launch_fill_u32(uint32_t *p, int64_t n, hipStream_t s);
+// r_out = r - chat[assign] (fp32), stats max|r_out| into stats[h*stride+slot]
+// when stats is non-null.
+bool launch_subtract(const void *r, bool r_bf16, int H, int N, int D, int C, const uint8_t *assign,
+                     int64_t assign_hstride, const void *chat, bool c_bf16, int64_t chat_hstride,
+                     float *r_out, uint32_t *stats, int stat_stride, int slot, hipStream_t s);
+// codes/scales of (r - chat[assign]) or of r when assign is null.  Assignment
+// bytes >= C are clamped to C-1 in every kernel that gathers centroids.
+bool launch_quant(const void *r, bool r_bf16, int H, int N, int D, int C, const uint8_t *assign,
+                  int64_t assign_hstride, const void *chat, bool c_bf16, int64_t chat_hstride,
+                  int bits, int G, uint8_t *codes, uint8_t *scales, hipStream_t s);
+bool launch_dequant(const uint8_t *codes, const uint8_t *scales, const uint8_t *assign,
+                    const void *cent, bool c_bf16, int H, int N, int D, int C, int T, int bits,
+                    int G, void *out, bool out_bf16, hipStream_t s);
+
+}  // namespace qvg

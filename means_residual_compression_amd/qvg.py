@@ -1,0 +1,246 @@
+"""Thin ctypes binding of libqvg.so (C ABI in include/qvg.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libqvg.so.  PyTorch supplies device memory and the current stream.  There is
+no fallback: if the library is missing or a call fails, an exception is
+raised.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqvg.so")
+
+QVG_F32, QVG_BF16 = 0, 1
+_STATUS = {0: "QVG_OK", 1: "QVG_ERR_INVALID_ARG", 2: "QVG_ERR_UNSUPPORTED",
+           3: "QVG_ERR_WORKSPACE", 4: "QVG_ERR_HIP"}
+EXPORTS = ["qvg_status_string", "qvg_last_error", "qvg_workspace_size", "qvg_compress",
+           "qvg_compress_stream", "qvg_decompress", "qvg_assign_workspace_size",
+           "qvg_kmeans_assign", "qvg_update_workspace_size", "qvg_kmeans_update",
+           "qvg_sas_subtract", "qvg_group_quant_pack"]
+
+
+class QvgError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Params(ct.Structure):
+    _fields_ = [("C", ct.c_int32), ("T", ct.c_int32), ("iters", ct.c_int32),
+                ("bits", ct.c_int32), ("group", ct.c_int32)]
+
+
+class _Record(ct.Structure):
+    _fields_ = [("codes", ct.c_void_p), ("scales", ct.c_void_p), ("assign", ct.c_void_p),
+                ("centroids", ct.c_void_p)]
+
+
+@dataclass
+class Record:
+    """Compressed record of H head-tensors (device tensors)."""
+    codes: torch.Tensor      # uint8 [H, N, d*bits/8]
+    scales: torch.Tensor     # uint8 [H, N, d/G] (E4M3 codes)
+    assign: torch.Tensor     # uint8 [H, T, N]
+    centroids: torch.Tensor  # [H, T, C, d] in the input dtype
+
+    def _c(self) -> _Record:
+        return _Record(self.codes.data_ptr(), self.scales.data_ptr(), self.assign.data_ptr(),
+                       self.centroids.data_ptr())
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size()
+                   for t in (self.codes, self.scales, self.assign, self.centroids))
+
+
+_lib = None
+
+
+def lib() -> ct.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m means_residual_compression_amd.build`")
+        L = ct.CDLL(LIB_PATH)
+        p, i64, i32, sz = ct.c_void_p, ct.c_int64, ct.c_int32, ct.c_size_t
+        P = ct.POINTER(Params)
+        R = ct.POINTER(_Record)
+        sig = {
+            "qvg_status_string": ([ct.c_int], ct.c_char_p),
+            "qvg_last_error": ([], ct.c_char_p),
+            "qvg_workspace_size": ([i64, i64, i64, ct.c_int, P], sz),
+            "qvg_compress": ([p, ct.c_int, i64, i64, i64, P, p, p, p, R, p, sz, p], ct.c_int),
+            "qvg_compress_stream": ([p, ct.c_int, i64, i64, i64, P, i32, p, ct.c_int, p, R, p,
+                                     sz, p], ct.c_int),
+            "qvg_decompress": ([R, ct.c_int, i64, i64, i64, P, p, ct.c_int, p], ct.c_int),
+            "qvg_assign_workspace_size": ([i64, i64, i64, i32], sz),
+            "qvg_kmeans_assign": ([p, ct.c_int, i64, i64, i64, p, i32, p, p, sz, p], ct.c_int),
+            "qvg_update_workspace_size": ([i64, i64, i32], sz),
+            "qvg_kmeans_update": ([p, ct.c_int, i64, i64, i64, p, i32, p, p, sz, p], ct.c_int),
+            "qvg_sas_subtract": ([p, ct.c_int, i64, i64, i64, p, p, ct.c_int, i32, p, p],
+                                 ct.c_int),
+            "qvg_group_quant_pack": ([p, ct.c_int, i64, i64, i64, i32, i32, p, p, p], ct.c_int),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes, f.restype = args, res
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise QvgError(status, lib().qvg_last_error().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return QVG_BF16
+    if t.dtype == torch.float32:
+        return QVG_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _torch_dt(code: int) -> torch.dtype:
+    return torch.bfloat16 if code == QVG_BF16 else torch.float32
+
+
+def _stream():
+    return ct.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def params(C: int, T: int, iters: int, bits: int, group: int) -> Params:
+    return Params(C, T, iters, bits, group)
+
+
+def workspace_size(H, N, d, dtype: torch.dtype, p: Params) -> int:
+    code = QVG_BF16 if dtype == torch.bfloat16 else QVG_F32
+    n = lib().qvg_workspace_size(H, N, d, code, ct.byref(p))
+    if n == 0:
+        raise QvgError(1, "invalid sizes or parameters for the workspace query")
+    return n
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    # torch allocations are 512-byte aligned, which satisfies the 256-byte rule
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def empty_record(H, N, d, p: Params, dtype: torch.dtype, device) -> Record:
+    return Record(
+        codes=torch.empty((H, N, d * p.bits // 8), dtype=torch.uint8, device=device),
+        scales=torch.empty((H, N, d // p.group), dtype=torch.uint8, device=device),
+        assign=torch.zeros((H, p.T, N), dtype=torch.uint8, device=device),
+        centroids=torch.zeros((H, p.T, p.C, d), dtype=dtype, device=device))
+
+
+def _idx_ptr(init_idx):
+    if init_idx is None:
+        return None, None
+    a = np.ascontiguousarray(init_idx, dtype=np.int32)
+    return a, a.ctypes.data_as(ct.c_void_p)
+
+
+def compress(x: torch.Tensor, p: Params, init_idx=None, init_centroids=None, cache_out=None,
+             ws: torch.Tensor | None = None, out: Record | None = None) -> Record:
+    """x: [H, N, d] bf16/fp32 device tensor.  init_idx: host int32 [H, T, C]."""
+    _dev(x, "x")
+    H, N, d = x.shape
+    out = out or empty_record(H, N, d, p, x.dtype, x.device)
+    ws = ws if ws is not None else alloc_workspace(workspace_size(H, N, d, x.dtype, p), x.device)
+    keep, idx_p = _idx_ptr(init_idx)
+    rec = out._c()
+    _check(lib().qvg_compress(
+        x.data_ptr(), _dt(x), H, N, d, ct.byref(p), idx_p,
+        None if init_centroids is None else init_centroids.data_ptr(),
+        None if cache_out is None else cache_out.data_ptr(), ct.byref(rec),
+        ws.data_ptr(), ws.numel(), _stream()))
+    del keep
+    return out
+
+
+def compress_stream(chunk: torch.Tensor, p: Params, iters_warm: int, cache: torch.Tensor,
+                    warm: bool, init_idx=None, ws: torch.Tensor | None = None,
+                    out: Record | None = None) -> Record:
+    _dev(chunk, "chunk")
+    H, N, d = chunk.shape
+    out = out or empty_record(H, N, d, p, chunk.dtype, chunk.device)
+    ws = ws if ws is not None else alloc_workspace(workspace_size(H, N, d, chunk.dtype, p),
+                                                   chunk.device)
+    keep, idx_p = _idx_ptr(init_idx)
+    rec = out._c()
+    _check(lib().qvg_compress_stream(
+        chunk.data_ptr(), _dt(chunk), H, N, d, ct.byref(p), iters_warm, cache.data_ptr(),
+        1 if warm else 0, idx_p, ct.byref(rec), ws.data_ptr(), ws.numel(), _stream()))
+    del keep
+    return out
+
+
+def decompress(rec: Record, p: Params, out_dtype: torch.dtype | None = None,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    H, N = rec.codes.shape[:2]
+    d = rec.codes.shape[2] * 8 // p.bits
+    cdt = rec.centroids.dtype
+    odt = out_dtype or cdt
+    if out is None:
+        out = torch.empty((H, N, d), dtype=odt, device=rec.codes.device)
+    r = rec._c()
+    _check(lib().qvg_decompress(ct.byref(r), _dt(rec.centroids), H, N, d, ct.byref(p),
+                                out.data_ptr(), _dt(out), _stream()))
+    return out
+
+
+def kmeans_assign(r: torch.Tensor, centroids: torch.Tensor, ws=None) -> torch.Tensor:
+    _dev(r, "r")
+    H, N, d = r.shape
+    C = centroids.shape[1]
+    out = torch.empty((H, N), dtype=torch.uint8, device=r.device)
+    n = lib().qvg_assign_workspace_size(H, N, d, C)
+    ws = ws if ws is not None else alloc_workspace(max(n, 256), r.device)
+    _check(lib().qvg_kmeans_assign(r.data_ptr(), _dt(r), H, N, d, centroids.data_ptr(), C,
+                                   out.data_ptr(), ws.data_ptr(), ws.numel(), _stream()))
+    return out
+
+
+def kmeans_update(r: torch.Tensor, assign: torch.Tensor, centroids: torch.Tensor, ws=None):
+    """Updates `centroids` (fp32 [H, C, d]) in place and returns it."""
+    _dev(r, "r")
+    H, N, d = r.shape
+    C = centroids.shape[1]
+    n = lib().qvg_update_workspace_size(H, N, C)
+    ws = ws if ws is not None else alloc_workspace(max(n, 256), r.device)
+    _check(lib().qvg_kmeans_update(r.data_ptr(), _dt(r), H, N, d, assign.data_ptr(), C,
+                                   centroids.data_ptr(), ws.data_ptr(), ws.numel(), _stream()))
+    return centroids
+
+
+def sas_subtract(r: torch.Tensor, assign: torch.Tensor, chat: torch.Tensor) -> torch.Tensor:
+    _dev(r, "r")
+    H, N, d = r.shape
+    out = torch.empty((H, N, d), dtype=torch.float32, device=r.device)
+    _check(lib().qvg_sas_subtract(r.data_ptr(), _dt(r), H, N, d, assign.data_ptr(),
+                                  chat.data_ptr(), _dt(chat), chat.shape[1], out.data_ptr(),
+                                  _stream()))
+    return out
+
+
+def group_quant_pack(r: torch.Tensor, bits: int, group: int):
+    _dev(r, "r")
+    H, N, d = r.shape
+    codes = torch.empty((H, N, d * bits // 8), dtype=torch.uint8, device=r.device)
+    scales = torch.empty((H, N, d // group), dtype=torch.uint8, device=r.device)
+    _check(lib().qvg_group_quant_pack(r.data_ptr(), _dt(r), H, N, d, bits, group,
+                                      codes.data_ptr(), scales.data_ptr(), _stream()))
+    return codes, scales

@@ -45,12 +45,13 @@ def lib():
         L.qvgo_assign.argtypes = [p, i64, i32, p, i32, p]
         L.qvgo_update.argtypes = [p, i64, i32, p, i32, p, p]
         L.qvgo_kmeans.argtypes = [p, i64, i32, p, i32, i32, p]
+        L.qvgo_subtract.argtypes = [p, i64, i32, p, p, p]
         L.qvgo_quantize.argtypes = [p, i64, i32, i32, i32, p, p]
         L.qvgo_compress.argtypes = [p, i32, i64, i64, i32, i32, i32, i32, i32, i32, p, p,
                                     p, p, p, p, p, i32]
         L.qvgo_decompress.argtypes = [p, p, p, p, i32, i64, i64, i32, i32, i32, i32, i32,
                                       p, i32, i32]
-        for f in ("qvgo_assign", "qvgo_update", "qvgo_kmeans", "qvgo_quantize",
+        for f in ("qvgo_assign", "qvgo_update", "qvgo_kmeans", "qvgo_quantize", "qvgo_subtract",
                   "qvgo_compress", "qvgo_decompress"):
             getattr(L, f).restype = None
         _lib = L
@@ -119,6 +120,16 @@ def kmeans(R, C0, iters):
     return C, pi
 
 
+def subtract(R, pi, C):
+    """fp32 residual R - C[pi] (C already in fp32 values of the stored centroids)."""
+    R = _c(R, np.float32)
+    pi = _c(pi, np.int32)
+    C = _c(C, np.float32)
+    out = np.empty_like(R)
+    lib().qvgo_subtract(_ptr(R), R.shape[0], R.shape[1], _ptr(pi), _ptr(C), _ptr(out))
+    return out
+
+
 def quantize(R, bits, G):
     R = _c(R, np.float32)
     N, d = R.shape
@@ -165,7 +176,7 @@ def decompress(codes, scales, assign, cent, bits, G, out_bf16=None, threads=None
     scales = _c(scales, np.uint8)
     assign = _c(assign, np.uint8)
     cent, cdt = _as_store(cent)
-    H, T, C, d = cent.shape if cent.ndim == 4 else (codes.shape[0], 0, 1, codes.shape[2] * 8 // bits)
+    H, T, C, d = cent.shape
     N = codes.shape[1]
     if out_bf16 is None:
         out_bf16 = cdt == DT_BF16

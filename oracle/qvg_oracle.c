@@ -152,6 +152,16 @@ void qvgo_update(const float *R, int64_t N, int d, const int32_t *pi, int nC, fl
     free(cnt);
 }
 
+/* [SAS] step (c): residual of each token, r - C[pi(r)], one fp32 subtraction
+ * per element; C given as fp32 values (already rounded to the storage dtype). */
+void qvgo_subtract(const float *R, int64_t N, int d, const int32_t *pi, const float *C,
+                   float *out)
+{
+    for (int64_t i = 0; i < N; ++i)
+        for (int k = 0; k < d; ++k)
+            out[i * d + k] = R[i * d + k] - C[(int64_t)pi[i] * d + k];
+}
+
 /* Lloyd's k-means from the given initial centroids: iters x (assign, update). */
 void qvgo_kmeans(const float *R, int64_t N, int d, float *C, int nC, int iters, int32_t *pi)
 {

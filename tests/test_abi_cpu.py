@@ -1,0 +1,125 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports
+every symbol include/qvg.h declares, and rejects invalid arguments with the
+documented status codes before touching the device."""
+import ctypes as ct
+import os
+import re
+
+import numpy as np
+import pytest
+
+from means_residual_compression_amd import qvg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qvg.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qvg_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = qvg.lib()
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(qvg.EXPORTS)
+
+
+def test_status_strings():
+    L = qvg.lib()
+    assert L.qvg_status_string(0) == b"QVG_OK"
+    assert L.qvg_status_string(4) == b"QVG_ERR_HIP"
+    assert L.qvg_status_string(99) == b"QVG_UNKNOWN_STATUS"
+
+
+def _ws(H, N, d, dt, **kw):
+    p = qvg.params(**{**dict(C=256, T=2, iters=8, bits=2, group=64), **kw})
+    return qvg.lib().qvg_workspace_size(H, N, d, dt, ct.byref(p))
+
+
+def test_workspace_size_query():
+    assert _ws(24, 32760, 128, qvg.QVG_BF16) > 24 * 32760 * 128 * 4  # holds the fp32 residual
+    assert _ws(1, 4096, 64, qvg.QVG_F32, C=16, T=1, iters=10, group=32) > 0
+    assert _ws(1, 4096, 96, qvg.QVG_F32) == 0       # d unsupported
+    assert _ws(1, 100, 128, qvg.QVG_F32, C=101) == 0  # C > N
+    assert _ws(1, 4096, 128, qvg.QVG_F32, bits=3) == 0
+    assert _ws(1, 4096, 128, qvg.QVG_F32, group=48) == 0
+    assert _ws(1, 4096, 128, qvg.QVG_F32, T=9) == 0
+    assert _ws(1, 4096, 128, qvg.QVG_F32, C=257) == 0
+    assert _ws(1, 4096, 128, qvg.QVG_F32, T=0, C=1000) == 0  # C still bounded for T=0
+
+
+def _compress(H=2, N=1000, d=128, dt=qvg.QVG_BF16, x=FAKE, idx="ok", init_c=None, ws=FAKE,
+              ws_bytes=None, rec=True, **kw):
+    L = qvg.lib()
+    p = qvg.params(**{**dict(C=16, T=2, iters=3, bits=2, group=64), **kw})
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    keep = None
+    ip = None
+    if isinstance(idx, str):
+        keep = np.zeros((H, max(p.T, 1), p.C), np.int32)
+        if idx == "bad":
+            keep[-1, -1, -1] = N
+        ip = keep.ctypes.data_as(ct.c_void_p)
+    r = qvg._Record(FAKE, FAKE, FAKE, FAKE) if rec else None
+    st = L.qvg_compress(x, dt, H, N, d, ct.byref(p), ip, init_c, None,
+                        ct.byref(r) if rec else None, ws, ws_bytes, None)
+    return st, L.qvg_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(x=None), INVALID, "non-NULL"),
+    (dict(rec=False), INVALID, "non-NULL"),
+    (dict(d=96), UNSUPPORTED, "head dims"),
+    (dict(C=300), UNSUPPORTED, "C=300"),
+    (dict(bits=3), UNSUPPORTED, "bits=3"),
+    (dict(group=48), UNSUPPORTED, "group=48"),
+    (dict(T=9), UNSUPPORTED, "T=9"),
+    (dict(N=10, C=16), INVALID, "exceeds N"),
+    (dict(iters=0), INVALID, "iterations"),
+    (dict(H=0), INVALID, "H=0"),
+    (dict(dt=7), INVALID, "dtype"),
+    (dict(idx=None), INVALID, "exactly one"),
+    (dict(init_c=FAKE), INVALID, "exactly one"),
+    (dict(ws=None), WORKSPACE, "NULL"),
+    (dict(ws_bytes=1024), WORKSPACE, "smaller"),
+    (dict(ws=FAKE + 8), WORKSPACE, "aligned"),
+    (dict(idx="bad"), INVALID, "outside [0, N"),
+])
+def test_compress_rejects(kw, status, msg):
+    st, err = _compress(**kw)
+    assert st == status, err
+    assert msg in err
+
+
+def test_decompress_and_steps_reject():
+    L = qvg.lib()
+    p = qvg.params(16, 2, 3, 2, 64)
+    r = qvg._Record(FAKE, FAKE, FAKE, FAKE)
+    assert L.qvg_decompress(None, 1, 2, 100, 128, ct.byref(p), FAKE, 1, None) == INVALID
+    assert L.qvg_decompress(ct.byref(r), 1, 2, 100, 128, ct.byref(p), None, 1, None) == INVALID
+    assert L.qvg_decompress(ct.byref(r), 1, 2, 100, 128, ct.byref(p), FAKE, 5, None) == INVALID
+    bad = qvg.params(16, 2, 3, 4, 12)
+    assert L.qvg_decompress(ct.byref(r), 1, 2, 100, 128, ct.byref(bad), FAKE, 1, None) == UNSUPPORTED
+    assert L.qvg_kmeans_assign(FAKE, 1, 2, 100, 128, FAKE, 0, FAKE, FAKE, 1 << 30, None) == UNSUPPORTED
+    assert L.qvg_kmeans_assign(FAKE, 1, 2, 100, 128, FAKE, 16, FAKE, FAKE, 16, None) == WORKSPACE
+    assert L.qvg_kmeans_update(FAKE, 1, 2, 100, 128, None, 16, FAKE, FAKE, 1 << 30, None) == INVALID
+    assert L.qvg_sas_subtract(FAKE, 1, 2, 100, 128, FAKE, FAKE, 9, 16, FAKE, None) == INVALID
+    assert L.qvg_group_quant_pack(FAKE, 1, 2, 100, 128, 2, 256, FAKE, FAKE, None) == UNSUPPORTED
+    assert L.qvg_compress_stream(FAKE, 1, 2, 100, 128, ct.byref(p), 3, None, 1, None,
+                                 ct.byref(r), FAKE, 1 << 40, None) == INVALID
+    assert L.qvg_compress_stream(FAKE, 1, 2, 100, 128, ct.byref(p), 3, FAKE, 0, None,
+                                 ct.byref(r), FAKE, 1 << 40, None) == INVALID
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(qvg, "_lib", None)
+    monkeypatch.setattr(qvg, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        qvg.lib()

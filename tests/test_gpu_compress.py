@@ -1,0 +1,147 @@
+"""End-to-end GPU parity of qvg_compress / qvg_decompress / qvg_compress_stream
+against the CPU oracle on the same seeded inputs (bit-exact records and
+reconstructions), including the workload's tiny fp32 configuration in full,
+the Self-Forcing-shaped bf16 cache at full size, multi-stage and INT4 runs,
+ragged token counts, the C = N and T = 0 special cases, caller-supplied and
+streamed (warm-started) initialisation, and run-to-run determinism."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from means_residual_compression_amd import qvg, synth
+from gpu_util import DEV, bits16, mismatch_report, rec_equal, say, to_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_both(x, p, idx=None, init_c=None, threads=None):
+    """GPU compress+decompress and oracle compress+decompress of the same input."""
+    xd = x.to(DEV)
+    cache = torch.zeros((x.shape[0], p.T, p.C, x.shape[2]), dtype=torch.float32, device=DEV)
+    rec = qvg.compress(xd, p, init_idx=idx,
+                       init_centroids=None if init_c is None else torch.from_numpy(init_c).to(DEV),
+                       cache_out=cache)
+    out = qvg.decompress(rec, p)
+    torch.cuda.synchronize()
+    ref = oracle.compress(to_oracle(x), C=p.C, T=p.T, iters=p.iters, bits=p.bits, G=p.group,
+                          init_idx=idx, init_c=init_c, threads=threads)
+    ref_out = oracle.decompress(ref["codes"], ref["scales"], ref["assign"], ref["cent"], p.bits,
+                                p.group)
+    return rec, out, cache, ref, ref_out
+
+
+def _check(rec, out, cache, ref, ref_out):
+    bad = rec_equal(rec, ref)
+    assert not bad, f"record fields differ from the oracle: {bad}"
+    if ref["cache"].size:
+        assert np.array_equal(cache.cpu().numpy(), ref["cache"])
+    got = bits16(out) if out.dtype == torch.bfloat16 else out.cpu().numpy()
+    assert np.array_equal(got, ref_out), mismatch_report(got, ref_out)
+
+
+def test_tiny_fp32_config_full():
+    """16 frames x 16x16 grid, d=64, fp32, C=16, 10 iterations, T=1, INT2 G=32."""
+    c = synth.CONFIGS[0]
+    x = synth.config_cache(0)
+    p = qvg.params(C=c["C"], T=c["T"], iters=c["iters"], bits=c["bits"], group=c["group"])
+    idx = synth.init_indices(100, x.shape[0], p.T, x.shape[1], p.C)
+    say("tiny fp32 config", tuple(x.shape))
+    _check(*_run_both(x, p, idx))
+
+
+@pytest.mark.parametrize("T,bits,G,C,N", [(2, 2, 64, 64, 1500), (3, 4, 64, 50, 1203),
+                                          (4, 2, 16, 256, 2101), (1, 4, 128, 256, 4681)])
+def test_multistage_bf16(T, bits, G, C, N):
+    x = synth.video_cache(1, 0, 1, 4, 30, 52, 128, 1e2, torch.bfloat16, n_tokens=N)
+    x = torch.cat([x, synth.video_cache(1, 1, 1, 4, 30, 52, 128, 1e3, torch.bfloat16,
+                                        n_tokens=N)])
+    p = qvg.params(C=C, T=T, iters=3, bits=bits, group=G)
+    idx = synth.init_indices(200 + T, x.shape[0], T, N, C)
+    say("multistage", T, bits, G, C, N)
+    _check(*_run_both(x, p, idx))
+
+
+def test_T0_plain_quantization():
+    x = synth.video_cache(1, 1, 2, 2, 30, 52, 128, 1e3, torch.bfloat16)
+    p = qvg.params(C=1, T=0, iters=1, bits=2, group=64)
+    say("T=0")
+    _check(*_run_both(x, p))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_C_equals_N_is_lossless(dtype):
+    N = 200
+    x = synth.video_cache(0, 0, 2, 1, 10, 20, 64, 50.0, dtype)
+    idx = np.stack([np.stack([np.random.default_rng(h * 7 + t).permutation(N) for t in range(2)])
+                    for h in range(2)]).astype(np.int32)
+    p = qvg.params(C=N, T=2, iters=2, bits=2, group=32)
+    say("C=N", dtype)
+    rec, out, cache, ref, ref_out = _run_both(x, p, idx)
+    _check(rec, out, cache, ref, ref_out)
+    assert torch.equal(out.cpu(), x)
+    assert int(rec.scales.max()) == 0
+
+
+def test_duplicate_init_indices_and_caller_init():
+    x = synth.video_cache(1, 0, 2, 3, 30, 52, 128, 1e2, torch.bfloat16)
+    N = x.shape[1]
+    idx = synth.init_indices(300, 2, 2, N, 32)
+    idx[:, :, 5] = idx[:, :, 4]  # duplicate rows: one of the two clusters stays empty
+    p = qvg.params(C=32, T=2, iters=4, bits=2, group=64)
+    say("duplicate init rows")
+    _check(*_run_both(x, p, idx))
+    init_c = np.random.default_rng(3).standard_normal((2, 2, 32, 128)).astype(np.float32) * 50
+    say("caller-supplied init centroids")
+    _check(*_run_both(x, p, init_c=init_c))
+
+
+def test_streaming_warm_start_chain():
+    """Chunks of 3 frames: chunk 0 cold, chunks 1-3 warm-started from the
+    previous chunk's cached centroids, checked against the oracle run with the
+    oracle's own cache as its initialisation."""
+    c = dict(Hg=30, Wg=52, d=128, outlier_scale=1e2, dtype=torch.bfloat16)
+    p = qvg.params(C=64, T=2, iters=4, bits=2, group=64)
+    H = 2
+    cache = torch.zeros((H, p.T, p.C, 128), dtype=torch.float32, device=DEV)
+    ref_cache = None
+    for k in range(4):
+        ch = synth.stream_chunk(2, 0, H, k, 3, **c)
+        N = ch.shape[1]
+        warm = k > 0
+        idx = None if warm else synth.init_indices(400, H, p.T, N, p.C)
+        say("stream chunk", k, "warm" if warm else "cold")
+        rec = qvg.compress_stream(ch.to(DEV), p, 2, cache, warm, init_idx=idx)
+        out = qvg.decompress(rec, p)
+        torch.cuda.synchronize()
+        ref = oracle.compress(to_oracle(ch), C=p.C, T=p.T, iters=2 if warm else p.iters,
+                              bits=p.bits, G=p.group, init_idx=idx, init_c=ref_cache)
+        ref_cache = ref["cache"]
+        ref_out = oracle.decompress(ref["codes"], ref["scales"], ref["assign"], ref["cent"],
+                                    p.bits, p.group)
+        _check(rec, out, cache, ref, ref_out)
+
+
+def test_deterministic_rerun():
+    x = synth.video_cache(1, 1, 3, 3, 30, 52, 128, 1e3, torch.bfloat16).to(DEV)
+    p = qvg.params(C=128, T=2, iters=3, bits=2, group=64)
+    idx = synth.init_indices(500, 3, 2, x.shape[1], 128)
+    say("determinism")
+    a = qvg.compress(x, p, init_idx=idx)
+    b = qvg.compress(x, p, init_idx=idx)
+    torch.cuda.synchronize()
+    for f in ("codes", "scales", "assign", "centroids"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+
+
+def test_self_forcing_cache_full_size():
+    """21 frames x 30x52 = 32760 tokens, d=128, bf16, C=256, 8 iterations,
+    T=2, INT2 G=64: all 12 K and 12 V head-tensors, record and reconstruction
+    bit-exact against the oracle."""
+    cfg = synth.CONFIGS[1]
+    x = synth.config_cache(1)
+    p = qvg.params(C=cfg["C"], T=cfg["T"], iters=cfg["iters"], bits=cfg["bits"],
+                   group=cfg["group"])
+    idx = synth.init_indices(1, x.shape[0], p.T, x.shape[1], p.C)
+    say("self-forcing full size", tuple(x.shape))
+    _check(*_run_both(x, p, idx))

@@ -1,0 +1,151 @@
+"""GPU parity of each step of the path against the CPU oracle, through the C ABI.
+
+Every kernel of the path is checked bit-for-bit on the same seeded inputs:
+quantize+pack, subtract, fused dequant, k-means assign (exact argmin, ties to
+the smallest index) and k-means update (fp64 token-order means).  Sizes span
+several tiles and a ragged tail.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from means_residual_compression_amd import qvg, synth
+from gpu_util import DEV, as_f32, bits16, mismatch_report, say, to_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _residual_like(seed, H, N, d, dtype):
+    """Rows whose magnitudes span many binades, plus all-zero rows, rows that
+    saturate the E4M3 scale and rows whose scales are E4M3 subnormals."""
+    rng = np.random.default_rng(seed)
+    r = rng.standard_normal((H, N, d)) * np.exp(rng.uniform(-9, 6, (H, N, 1)))
+    r[:, ::37] = 0.0
+    r[:, 5::41, : d // 2] *= 3000.0
+    r[:, 7::43] *= 1e-4
+    return synth.round_to(r, dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d,bits,G", [(128, 2, 64), (128, 4, 64), (128, 2, 16), (64, 2, 32),
+                                      (64, 4, 64), (128, 4, 128)])
+def test_group_quant_pack(dtype, d, bits, G):
+    H, N = 3, 1037
+    r = _residual_like(1, H, N, d, dtype)
+    say("group_quant_pack", dtype, d, bits, G)
+    codes, scales = qvg.group_quant_pack(r.to(DEV), bits, G)
+    torch.cuda.synchronize()
+    rf = as_f32(r)
+    for h in range(H):
+        c_ref, s_ref = oracle.quantize(rf[h], bits, G)
+        assert np.array_equal(scales[h].cpu().numpy(), s_ref), mismatch_report(scales[h].cpu(), s_ref)
+        assert np.array_equal(codes[h].cpu().numpy(), c_ref), mismatch_report(codes[h].cpu(), c_ref)
+
+
+@pytest.mark.parametrize("rdt,cdt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.float32),
+                                     (torch.float32, torch.bfloat16)])
+def test_sas_subtract(rdt, cdt):
+    H, N, d, C = 2, 999, 128, 37
+    rng = np.random.default_rng(2)
+    r = _residual_like(2, H, N, d, rdt)
+    chat = synth.round_to(rng.standard_normal((H, C, d)) * 10, cdt)
+    pi = torch.from_numpy(rng.integers(0, C, (H, N)).astype(np.uint8))
+    say("sas_subtract", rdt, cdt)
+    out = qvg.sas_subtract(r.to(DEV), pi.to(DEV), chat.to(DEV))
+    torch.cuda.synchronize()
+    for h in range(H):
+        ref = oracle.subtract(as_f32(r[h]), pi[h].numpy().astype(np.int32), as_f32(chat[h]))
+        assert np.array_equal(out[h].cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("T,C,bits,G,cdt,odt", [
+    (0, 1, 2, 64, torch.bfloat16, torch.bfloat16),
+    (1, 256, 2, 64, torch.bfloat16, torch.bfloat16),
+    (2, 256, 2, 64, torch.bfloat16, torch.float32),
+    (4, 256, 2, 64, torch.bfloat16, torch.bfloat16),
+    (3, 40, 4, 32, torch.float32, torch.float32),
+    (4, 256, 4, 16, torch.float32, torch.bfloat16),
+])
+def test_fused_dequant(T, C, bits, G, cdt, odt):
+    H, N, d = 3, 2085, 128
+    codes, scales, assign, cent = synth.random_record(11 + T, H, N, d, T, C, bits, G, Hg=40, Wg=52)
+    cent = cent.to(cdt)
+    p = qvg.params(C=C, T=T, iters=1, bits=bits, group=G)
+    rec = qvg.Record(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                     torch.from_numpy(assign).to(DEV), cent.to(DEV))
+    say("fused_dequant", T, C, bits, G, cdt, odt)
+    out = qvg.decompress(rec, p, out_dtype=odt)
+    torch.cuda.synchronize()
+    ref = oracle.decompress(codes, scales, assign, to_oracle(cent), bits, G,
+                            out_bf16=odt == torch.bfloat16)
+    got = bits16(out) if odt == torch.bfloat16 else out.cpu().numpy()
+    assert np.array_equal(got, ref), mismatch_report(got, ref)
+
+
+def _video(H, N, d, kind_mix=True, seed_cfg=1):
+    c = synth.CONFIGS[1]
+    heads = []
+    for h in range(H):
+        kind = h % 2 if kind_mix else 0
+        x = synth.video_head(synth._seed(seed_cfg, kind, h), 8, c["Hg"], c["Wg"], d,
+                             synth.OUTLIER_SCALE[kind], n_tokens=N)
+        heads.append(x)
+    return synth.round_to(np.stack(heads), torch.bfloat16)
+
+
+@pytest.mark.parametrize("C", [256, 100, 33, 3, 2, 1])
+def test_kmeans_assign_bf16_video(C):
+    H, N, d = 4, 2500, 128
+    x = _video(H, N, d)
+    xf = as_f32(x)
+    # realistic centroids: two Lloyd iterations of the oracle from seeded rows
+    idx = synth.init_indices(21, H, 1, N, C)[:, 0]
+    cents = np.stack([oracle.kmeans(xf[h], xf[h][idx[h]], 2)[0] for h in range(H)])
+    say("kmeans_assign bf16 video C=", C)
+    pi = qvg.kmeans_assign(x.to(DEV), torch.from_numpy(cents).to(DEV))
+    torch.cuda.synchronize()
+    for h in range(H):
+        ref = oracle.assign(xf[h], cents[h])
+        assert np.array_equal(pi[h].cpu().numpy().astype(np.int32), ref), \
+            mismatch_report(pi[h].cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_kmeans_assign_fp32_residual_and_ties(d):
+    H, N, C = 2, 1500, 64
+    rng = np.random.default_rng(5)
+    r = (rng.standard_normal((H, N, d)) * np.exp(rng.uniform(-3, 3, (H, N, 1)))).astype(np.float32)
+    cents = r[:, rng.choice(N, C, replace=False)].copy()
+    cents[:, 10] = cents[:, 3]          # exact duplicate: ties must go to index 3
+    cents[:, 20] = 0.0
+    cents[:, 21] = 0.0                  # duplicate zero centroids
+    r[:, 100] = 0.0                     # a zero token equidistant from both
+    say("kmeans_assign fp32 d=", d)
+    pi = qvg.kmeans_assign(torch.from_numpy(r).to(DEV), torch.from_numpy(cents).to(DEV))
+    torch.cuda.synchronize()
+    for h in range(H):
+        ref = oracle.assign(r[h], cents[h])
+        assert np.array_equal(pi[h].cpu().numpy().astype(np.int32), ref), \
+            mismatch_report(pi[h].cpu().numpy(), ref)
+        assert 10 not in set(pi[h].cpu().numpy().tolist())
+        assert 21 not in set(pi[h].cpu().numpy().tolist())
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 128), (torch.float32, 64)])
+def test_kmeans_update(dtype, d):
+    H, N, C = 3, 3001, 200
+    rng = np.random.default_rng(6)
+    r = _residual_like(6, H, N, d, dtype)
+    pi = rng.integers(0, C - 5, (H, N)).astype(np.uint8)  # clusters C-5..C-1 stay empty
+    pi[:, :700] = 7                                       # one large cluster
+    old = rng.standard_normal((H, C, d)).astype(np.float32)
+    cent = torch.from_numpy(old.copy()).to(DEV)
+    say("kmeans_update", dtype, d)
+    qvg.kmeans_update(r.to(DEV), torch.from_numpy(pi).to(DEV), cent)
+    torch.cuda.synchronize()
+    rf = as_f32(r)
+    for h in range(H):
+        ref, cnt = oracle.update(rf[h], pi[h].astype(np.int32), old[h])
+        assert np.array_equal(cent[h].cpu().numpy(), ref), mismatch_report(cent[h].cpu().numpy(), ref)
+        assert np.array_equal(cent[h, C - 5:].cpu().numpy(), old[h, C - 5:])
