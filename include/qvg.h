@@ -16,8 +16,11 @@
  *  - Device pointers are HIP device memory owned by the caller, contiguous,
  *    row-major, with the shapes given below.  Host pointers are marked (host).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
- *    asynchronously; no entry point synchronises the stream, except that a
- *    host-memory argument (init_idx) is copied before the call returns.
+ *    asynchronously and no entry point synchronises the stream.  The one host
+ *    array argument (init_idx) is read by a host-to-device copy enqueued on
+ *    `stream`: from pageable memory the HIP runtime stages it before the call
+ *    returns; from pinned memory the caller must keep it unchanged until the
+ *    stream has passed the call.
  *  - Arguments are validated on the host before anything is enqueued; an
  *    invalid call returns a status and enqueues nothing.  The library never
  *    aborts and allocates no device memory: scratch comes from the caller's
@@ -185,6 +188,23 @@ qvg_status qvg_sas_subtract(const void *r, qvg_dtype dtype, int64_t H, int64_t N
 qvg_status qvg_group_quant_pack(const void *r, qvg_dtype dtype, int64_t H, int64_t N, int64_t d,
                                 int32_t bits, int32_t group, uint8_t *codes, uint8_t *scales,
                                 void *stream);
+
+/* ---- diagnostics ---- */
+
+/* Per-kernel launch timing.  While enabled, every kernel launch of the
+ * library is bracketed by two HIP events recorded on its launch stream (the
+ * caller's stream).  Kernel names: "kmeans_assign", "kmeans_recheck",
+ * "kmeans_fallback", "kmeans_sort", "kmeans_accumulate", "kmeans_init",
+ * "kmeans_prepare", "kmeans_tables", "absmax", "sas_subtract",
+ * "group_quant_pack", "fused_dequant", "fill".  Host-side bookkeeping only;
+ * results of the path are unchanged. */
+void qvg_timing_enable(int on);
+/* Forget all recorded launches (waits for their events). */
+void qvg_timing_reset(void);
+/* Waits for the recorded launches of `kernel`, stores the sum of their
+ * durations in *total_ms and returns how many there were (-1 on a HIP
+ * error). */
+int64_t qvg_timing_read(const char *kernel, double *total_ms);
 
 #ifdef __cplusplus
 }

@@ -7,6 +7,21 @@
 
 namespace qvg {
 
+// Brackets one kernel launch with HIP events on its stream while timing is
+// enabled (qvg_timing_enable); a no-op otherwise.
+class TimerScope {
+ public:
+  TimerScope(const char *name, hipStream_t s);
+  ~TimerScope();
+  TimerScope(const TimerScope &) = delete;
+  TimerScope &operator=(const TimerScope &) = delete;
+
+ private:
+  const char *name_;
+  hipStream_t s_;
+  hipEvent_t a_;
+};
+
 // Everything one stage of k-means needs.  `r` is the stage input residual
 // [H][N][D] (bf16 X at the first stage, fp32 afterwards).
 struct KmArgs {

@@ -579,8 +579,9 @@ bool launch_absmax(const void *x, int H, int64_t per_head, uint32_t *stats, int 
                    int slot, hipStream_t s) {
   int64_t blocks = (per_head / 8 + 255) / 256;
   dim3 grid((unsigned)std::min<int64_t>(blocks, 1024), H);
+  { TimerScope ts_("absmax", s);
   hipLaunchKernelGGL(k_absmax<Tin>, grid, dim3(256), 0, s, (const Tin *)x, per_head, stats,
-                     stat_stride, slot);
+                     stat_stride, slot); }
   QVG_CHECK_LAUNCH();
   return true;
 }
@@ -588,16 +589,19 @@ bool launch_absmax(const void *x, int H, int64_t per_head, uint32_t *stats, int 
 template <typename Tin, int D>
 bool launch_kmeans_stage_begin(const KmArgs &a, hipStream_t s) {
   dim3 gc((a.Cp + 3) / 4, a.H);
+  { TimerScope ts_("kmeans_init", s);
   hipLaunchKernelGGL((k_init<Tin, D>), gc, dim3(256), 0, s, (const Tin *)a.r, a.N, a.idx,
                      a.idx_hstride, a.init, a.init_hstride, a.C, a.Cp, a.ws.cent, a.ws_stats,
-                     a.stat_stride);
+                     a.stat_stride); }
   QVG_CHECK_LAUNCH();
   dim3 gp((a.NT * kTile + 255) / 256, a.H);
+  { TimerScope ts_("kmeans_prepare", s);
   hipLaunchKernelGGL((k_prepare<Tin, D>), gp, dim3(256), 0, s, (const Tin *)a.r, a.N, a.NT,
-                     a.ws_stats, a.stat_stride, a.ws.rt, a.ws.tb);
+                     a.ws_stats, a.stat_stride, a.ws.rt, a.ws.tb); }
   QVG_CHECK_LAUNCH();
+  { TimerScope ts_("kmeans_tables", s);
   hipLaunchKernelGGL((k_tables<D>), gc, dim3(256), 0, s, a.ws.cent, a.C, a.Cp, a.ws_stats,
-                     a.ws_stats, a.stat_stride, (int)S_B0, a.ws.ctab, a.ws.cinit);
+                     a.ws_stats, a.stat_stride, (int)S_B0, a.ws.ctab, a.ws.cinit); }
   QVG_CHECK_LAUNCH();
   return true;
 }
@@ -616,17 +620,20 @@ bool launch_assign(const KmArgs &a, int bslot, hipStream_t s) {
     attr_set = true;
   }
   dim3 grid((a.NT + tiles_per_wg - 1) / tiles_per_wg, a.H);
+  { TimerScope ts_("kmeans_assign", s);
   hipLaunchKernelGGL((k_assign<D>), grid, dim3(256), lds, s, a.ws.rt, a.ws.tb, a.ws.ctab,
                      a.ws.cinit, a.ws_stats, a.stat_stride, bslot, a.N, a.NT, CB, tiles_per_wg,
                      a.assign, a.assign_hstride, a.ws.recheck, a.ws.fallback, a.ws.counters,
-                     a.kappa);
+                     a.kappa); }
   QVG_CHECK_LAUNCH();
+  { TimerScope ts_("kmeans_recheck", s);
   hipLaunchKernelGGL((k_recheck<Tin, D>), dim3(512), dim3(256), 0, s, (const Tin *)a.r, a.N,
-                     a.ws.cent, a.Cp, a.ws.recheck, a.ws.counters, a.assign, a.assign_hstride);
+                     a.ws.cent, a.Cp, a.ws.recheck, a.ws.counters, a.assign, a.assign_hstride); }
   QVG_CHECK_LAUNCH();
+  { TimerScope ts_("kmeans_fallback", s);
   hipLaunchKernelGGL((k_fallback<Tin, D>), dim3(512), dim3(256), 0, s, (const Tin *)a.r, a.N,
                      a.ws.cent, a.C, a.Cp, a.ws.fallback, a.ws.counters, a.assign,
-                     a.assign_hstride);
+                     a.assign_hstride); }
   QVG_CHECK_LAUNCH();
   return true;
 }
@@ -634,15 +641,17 @@ bool launch_assign(const KmArgs &a, int bslot, hipStream_t s) {
 template <typename Tin, typename Tc, int D>
 bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int64_t rec_hstride,
                    float *cache, int64_t cache_hstride, hipStream_t s) {
+  { TimerScope ts_("kmeans_sort", s);
   hipLaunchKernelGGL(k_sort, dim3(a.H), dim3(1024), 0, s, a.assign, a.assign_hstride, a.N, a.C,
                      a.Cp, a.ws.sorted, a.ws.offs, a.ws_stats, a.stat_stride, next_bslot,
-                     a.ws.counters);
+                     a.ws.counters); }
   QVG_CHECK_LAUNCH();
   dim3 gc((a.Cp + 3) / 4, a.H);
+  { TimerScope ts_("kmeans_accumulate", s);
   hipLaunchKernelGGL((k_accumulate<Tin, Tc, D>), gc, dim3(256), 0, s, (const Tin *)a.r, a.N,
                      a.ws.sorted, a.ws.offs, a.C, a.Cp, a.ws.cent, a.ws_stats, a.ws_stats,
                      a.stat_stride, next_bslot, tables ? a.ws.ctab : nullptr, a.ws.cinit, rec_c,
-                     rec_hstride, cache, cache_hstride);
+                     rec_hstride, cache, cache_hstride); }
   QVG_CHECK_LAUNCH();
   return true;
 }

@@ -156,6 +156,7 @@ __global__ void k_dequant(const uint8_t *__restrict__ codes, const uint8_t *__re
 bool launch_fill_u32(uint32_t *p, int64_t n, hipStream_t s) {
   if (n <= 0) return true;
   const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  TimerScope ts_("fill", s);
   hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
   QVG_CHECK_LAUNCH();
   return true;
@@ -166,6 +167,7 @@ bool launch_subtract(const void *r, bool r_bf16, int H, int N, int D, int C, con
                      float *r_out, uint32_t *stats, int stat_stride, int slot, hipStream_t s) {
   const int64_t threads = (int64_t)N * (D / 8);
   dim3 grid((unsigned)((threads + 255) / 256), H);
+  TimerScope ts_("sas_subtract", s);
 #define QVG_SUB(TI, TC)                                                                       \
   hipLaunchKernelGGL((k_subtract<TI, TC>), grid, dim3(256), 0, s, (const TI *)r, N, D, C, assign, \
                      assign_hstride, (const TC *)chat, chat_hstride, r_out, stats, stat_stride, \
@@ -184,6 +186,7 @@ bool launch_quant(const void *r, bool r_bf16, int H, int N, int D, int C, const 
                   int bits, int G, uint8_t *codes, uint8_t *scales, hipStream_t s) {
   const int64_t threads = (int64_t)N * (D / 8);
   dim3 grid((unsigned)((threads + 255) / 256), H);
+  TimerScope ts_("group_quant_pack", s);
 #define QVG_Q(TI, TC, B)                                                                        \
   hipLaunchKernelGGL((k_quant<TI, TC, B>), grid, dim3(256), 0, s, (const TI *)r, N, D, C, assign, \
                      assign_hstride, (const TC *)chat, chat_hstride, G, codes, scales)
@@ -204,6 +207,7 @@ bool launch_dequant(const uint8_t *codes, const uint8_t *scales, const uint8_t *
                     int G, void *out, bool out_bf16, hipStream_t s) {
   const int64_t threads = (int64_t)N * (D / 8);
   dim3 grid((unsigned)((threads + 255) / 256), H);
+  TimerScope ts_("fused_dequant", s);
 #define QVG_DQ(TC, TO, B)                                                                      \
   hipLaunchKernelGGL((k_dequant<TC, TO, B>), grid, dim3(256), 0, s, codes, scales, assign,    \
                      (const TC *)cent, N, D, C, T, G, (TO *)out)

@@ -23,7 +23,8 @@ _STATUS = {0: "QVG_OK", 1: "QVG_ERR_INVALID_ARG", 2: "QVG_ERR_UNSUPPORTED",
 EXPORTS = ["qvg_status_string", "qvg_last_error", "qvg_workspace_size", "qvg_compress",
            "qvg_compress_stream", "qvg_decompress", "qvg_assign_workspace_size",
            "qvg_kmeans_assign", "qvg_update_workspace_size", "qvg_kmeans_update",
-           "qvg_sas_subtract", "qvg_group_quant_pack"]
+           "qvg_sas_subtract", "qvg_group_quant_pack", "qvg_timing_enable", "qvg_timing_reset",
+           "qvg_timing_read"]
 
 
 class QvgError(RuntimeError):
@@ -87,6 +88,9 @@ def lib() -> ct.CDLL:
             "qvg_sas_subtract": ([p, ct.c_int, i64, i64, i64, p, p, ct.c_int, i32, p, p],
                                  ct.c_int),
             "qvg_group_quant_pack": ([p, ct.c_int, i64, i64, i64, i32, i32, p, p, p], ct.c_int),
+            "qvg_timing_enable": ([ct.c_int], None),
+            "qvg_timing_reset": ([], None),
+            "qvg_timing_read": ([ct.c_char_p, ct.POINTER(ct.c_double)], i64),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -147,8 +151,14 @@ def empty_record(H, N, d, p: Params, dtype: torch.dtype, device) -> Record:
 
 
 def _idx_ptr(init_idx):
+    """Host int32 [H, T, C] indices: a numpy array, or a CPU torch tensor
+    (pinned memory keeps the library's host-to-device copy asynchronous)."""
     if init_idx is None:
         return None, None
+    if isinstance(init_idx, torch.Tensor):
+        if init_idx.is_cuda or init_idx.dtype != torch.int32 or not init_idx.is_contiguous():
+            raise ValueError("init_idx must be a contiguous host int32 tensor")
+        return init_idx, ct.c_void_p(init_idx.data_ptr())
     a = np.ascontiguousarray(init_idx, dtype=np.int32)
     return a, a.ctypes.data_as(ct.c_void_p)
 
@@ -244,3 +254,26 @@ def group_quant_pack(r: torch.Tensor, bits: int, group: int):
     _check(lib().qvg_group_quant_pack(r.data_ptr(), _dt(r), H, N, d, bits, group,
                                       codes.data_ptr(), scales.data_ptr(), _stream()))
     return codes, scales
+
+
+# ------------------------------------------------------------ diagnostics
+KERNELS = ["kmeans_assign", "kmeans_recheck", "kmeans_fallback", "kmeans_sort",
+           "kmeans_accumulate", "kmeans_init", "kmeans_prepare", "kmeans_tables", "absmax",
+           "sas_subtract", "group_quant_pack", "fused_dequant", "fill"]
+
+
+def timing_enable(on: bool = True):
+    lib().qvg_timing_enable(1 if on else 0)
+
+
+def timing_reset():
+    lib().qvg_timing_reset()
+
+
+def timing_read(kernel: str):
+    """(total_ms, launches) of the recorded launches of `kernel`."""
+    ms = ct.c_double(0.0)
+    n = lib().qvg_timing_read(kernel.encode(), ct.byref(ms))
+    if n < 0:
+        raise QvgError(4, "timing read failed")
+    return ms.value, int(n)

@@ -171,6 +171,8 @@ def random_record(seed: int, H: int, N: int, d: int, T: int, C: int, bits: int, 
             key = (y // 4) * 1_000_003 + (x // 4) * 7919 + salt
             key = (key * 2654435761) % (2**32)
             assign[h, t] = ((key >> 8) % C).astype(np.uint8)
-    cents = np.stack([np.stack([rng.standard_normal((C, d)) * (0.5 ** (t + 1)) for t in range(T)])
-                      for _ in range(H)])
+    cents = np.zeros((H, T, C, d))
+    for h in range(H):
+        for t in range(T):
+            cents[h, t] = rng.standard_normal((C, d)) * (0.5 ** (t + 1))
     return codes, scales, assign, round_to(cents, torch.bfloat16)
