@@ -191,6 +191,14 @@ qvg_status qvg_group_quant_pack(const void *r, qvg_dtype dtype, int64_t H, int64
 
 /* ---- diagnostics ---- */
 
+/* After a qvg_compress / qvg_compress_stream call that used workspace `ws`
+ * with these arguments has completed (this call synchronises the device),
+ * copies out[2k] = tokens whose assignment needed the top-2 exact re-check and
+ * out[2k+1] = tokens that needed the exact scan over all centroids, for the
+ * call's k-means iterations k = 0..n_iters-1 (stage-major; at most 64). */
+qvg_status qvg_candidate_counts(const void *ws, int64_t H, int64_t N, int64_t d, qvg_dtype dtype,
+                                const qvg_params *p, uint32_t *out, int32_t n_iters);
+
 /* Per-kernel launch timing.  While enabled, every kernel launch of the
  * library is bracketed by two HIP events recorded on its launch stream (the
  * caller's stream).  Kernel names: "kmeans_assign", "kmeans_recheck",

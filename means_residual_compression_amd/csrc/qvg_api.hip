@@ -36,7 +36,7 @@ size_t up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 // Workspace layout shared by the size query and the carve-up.
 struct Layout {
-  size_t rbuf, rt, tb, cent, ctab, cinit, stats, recheck, fallback, counters, sorted, offs, idx;
+  size_t rbuf, rt, tb, cent, ctab, cinit, cbnd, stats, recheck, fallback, counters, sorted, offs, hist, idx;
   size_t total;
 };
 
@@ -54,12 +54,14 @@ Layout make_layout(int64_t H, int64_t N, int64_t d, int64_t C, int64_t T, bool n
   L.cent = take((size_t)(H * Cp * d * 4));
   L.ctab = take((size_t)(H * Cp * d * 2));
   L.cinit = take((size_t)(H * Cp * 4));
+  L.cbnd = take((size_t)(H * Cp * 16));
   L.stats = take((size_t)(H * Ts * kStatWords * 4));
   L.recheck = take((size_t)(H * NT * kTile * 16));
   L.fallback = take((size_t)(H * NT * kTile * 8));
-  L.counters = take(16);
+  L.counters = take(kCounterWords * 4);
   L.sorted = take((size_t)(H * N * 4));
   L.offs = take((size_t)(H * (Cp + 1) * 4));
+  L.hist = take((size_t)(H * ((N + kSortChunk - 1) / kSortChunk) * kMaxC * 4));
   L.idx = take(need_idx ? (size_t)(H * T * C * 4) : 0);
   L.total = o;
   return L;
@@ -74,12 +76,14 @@ Ws carve(void *ws, const Layout &L) {
   w.cent = (float *)(b + L.cent);
   w.ctab = (half8 *)(b + L.ctab);
   w.cinit = (float *)(b + L.cinit);
+  w.cbnd = (float4 *)(b + L.cbnd);
   w.stats = (uint32_t *)(b + L.stats);
   w.recheck = (int4 *)(b + L.recheck);
   w.fallback = (int2 *)(b + L.fallback);
   w.counters = (uint32_t *)(b + L.counters);
   w.sorted = (int32_t *)(b + L.sorted);
   w.offs = (int32_t *)(b + L.offs);
+  w.hist = (uint32_t *)(b + L.hist);
   w.idx = (int32_t *)(b + L.idx);
   return w;
 }
@@ -132,7 +136,7 @@ qvg_status run_compress(const void *x, int64_t H, int64_t N, const qvg_params *p
   const bool x_bf16 = std::is_same<Tin, uint16_t>::value;
   const bool c_bf16 = std::is_same<Tc, uint16_t>::value;
   const int stat_stride = std::max(T, 1) * kStatWords;
-  if (!launch_fill_u32(w.stats, (int64_t)H * stat_stride, s) || !launch_fill_u32(w.counters, 4, s))
+  if (!launch_fill_u32(w.stats, (int64_t)H * stat_stride, s) || !launch_fill_u32(w.counters, kCounterWords, s))
     return hip_fail("fill");
   if (T == 0) {
     if (!launch_quant(x, x_bf16, (int)H, (int)N, D, 1, nullptr, 0, nullptr, false, 0, p->bits,
@@ -168,12 +172,13 @@ qvg_status run_compress(const void *x, int64_t H, int64_t N, const qvg_params *p
       const bool last = it == iters - 1;
       ok = in_bf16 ? launch_assign<uint16_t, D>(a, bslot, s) : launch_assign<float, D>(a, bslot, s);
       if (!ok) return hip_fail("kmeans_assign");
+      const int log_slot = t * iters + it;
       ok = in_bf16 ? launch_update<uint16_t, Tc, D>(a, next, !last, last ? rec_c : nullptr,
                                                     rec_hstride, last ? cache_t : nullptr,
-                                                    rec_hstride, s)
+                                                    rec_hstride, log_slot, s)
                    : launch_update<float, Tc, D>(a, next, !last, last ? rec_c : nullptr,
                                                  rec_hstride, last ? cache_t : nullptr,
-                                                 rec_hstride, s);
+                                                 rec_hstride, log_slot, s);
       if (!ok) return hip_fail("kmeans_update");
     }
     if (t < T - 1) {
@@ -297,6 +302,20 @@ qvg_status qvg_decompress(const qvg_record *rec, qvg_dtype rec_dtype, int64_t H,
   return QVG_OK;
 }
 
+qvg_status qvg_candidate_counts(const void *ws, int64_t H, int64_t N, int64_t d, qvg_dtype dtype,
+                                const qvg_params *p, uint32_t *out, int32_t n_iters) {
+  g_err[0] = 0;
+  qvg_status st = check_params(H, N, d, dtype, p, p ? std::max(p->iters, 1) : 1);
+  if (st != QVG_OK) return st;
+  if (!ws || !out || n_iters < 0 || n_iters > kCounterLog)
+    return fail(QVG_ERR_INVALID_ARG, "ws/out NULL or n_iters outside [0, %d]", kCounterLog);
+  const Layout L = make_layout(H, N, d, p->C, p->T, p->T >= 2, p->T > 0);
+  if (hipMemcpy(out, (const char *)ws + L.counters + 16, (size_t)n_iters * 8,
+                hipMemcpyDeviceToHost) != hipSuccess)
+    return hip_fail("read candidate counts");
+  return QVG_OK;
+}
+
 size_t qvg_assign_workspace_size(int64_t H, int64_t N, int64_t d, int32_t C) {
   if (check_dims(H, N, d, QVG_F32) != QVG_OK || C < 1 || C > kMaxC || C > N) return 0;
   return make_layout(H, N, d, C, 1, false, false).total;
@@ -321,7 +340,7 @@ qvg_status qvg_kmeans_assign(const void *r, qvg_dtype dtype, int64_t H, int64_t 
   a.r = r; a.idx = nullptr; a.idx_hstride = 0; a.init = centroids; a.init_hstride = (int64_t)C * d;
   a.assign = assign; a.assign_hstride = N; a.ws = w; a.ws_stats = w.stats;
   a.stat_stride = kStatWords; a.kappa = kappa_for(d);
-  if (!launch_fill_u32(w.stats, H * kStatWords, s) || !launch_fill_u32(w.counters, 4, s)) return hip_fail("fill");
+  if (!launch_fill_u32(w.stats, H * kStatWords, s) || !launch_fill_u32(w.counters, kCounterWords, s)) return hip_fail("fill");
   const bool bf = dtype == QVG_BF16;
   bool ok;
   if (d == 64)
@@ -341,9 +360,10 @@ size_t qvg_update_workspace_size(int64_t H, int64_t N, int32_t C) {
   if (H < 1 || N < 1 || C < 1 || C > kMaxC) return 0;
   size_t o = 0;
   o = up(o + (size_t)(H * kStatWords * 4));  // stats
-  o = up(o + 16);                            // counters
+  o = up(o + kCounterWords * 4);             // counters
   o = up(o + (size_t)(H * N * 4));           // sorted
   o = up(o + (size_t)(H * (C + 1) * 4));     // offs
+  o = up(o + (size_t)(H * ((N + kSortChunk - 1) / kSortChunk) * kMaxC * 4));  // hist
   return o;
 }
 
@@ -361,9 +381,10 @@ qvg_status qvg_kmeans_update(const void *r, qvg_dtype dtype, int64_t H, int64_t 
   Ws w{};
   size_t o = 0;
   w.stats = (uint32_t *)(b + o); o = up(o + (size_t)(H * kStatWords * 4));
-  w.counters = (uint32_t *)(b + o); o = up(o + 16);
+  w.counters = (uint32_t *)(b + o); o = up(o + kCounterWords * 4);
   w.sorted = (int32_t *)(b + o); o = up(o + (size_t)(H * N * 4));
-  w.offs = (int32_t *)(b + o);
+  w.offs = (int32_t *)(b + o); o = up(o + (size_t)(H * (C + 1) * 4));
+  w.hist = (uint32_t *)(b + o);
   w.cent = centroids;
   KmArgs a;
   a.H = (int)H; a.N = (int)N; a.C = C; a.Cp = C; a.NT = 0;
@@ -374,11 +395,11 @@ qvg_status qvg_kmeans_update(const void *r, qvg_dtype dtype, int64_t H, int64_t 
   const bool bf = dtype == QVG_BF16;
   bool ok;
   if (d == 64)
-    ok = bf ? launch_update<uint16_t, float, 64>(a, S_B0, false, nullptr, 0, nullptr, 0, s)
-            : launch_update<float, float, 64>(a, S_B0, false, nullptr, 0, nullptr, 0, s);
+    ok = bf ? launch_update<uint16_t, float, 64>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, s)
+            : launch_update<float, float, 64>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, s);
   else
-    ok = bf ? launch_update<uint16_t, float, 128>(a, S_B0, false, nullptr, 0, nullptr, 0, s)
-            : launch_update<float, float, 128>(a, S_B0, false, nullptr, 0, nullptr, 0, s);
+    ok = bf ? launch_update<uint16_t, float, 128>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, s)
+            : launch_update<float, float, 128>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, s);
   return ok ? QVG_OK : hip_fail("kmeans_update");
 }
 

@@ -9,6 +9,9 @@ namespace qvg {
 constexpr int kMaxC = 256;  // assignments are uint8
 constexpr int kMaxT = 8;
 constexpr int kTile = 32;   // tokens (and centroids) per 32x32 MFMA tile
+constexpr int kSortChunk = 1024; // tokens per block of the counting sort
+constexpr int kCounterLog = 64;  // iterations whose candidate counts are kept
+constexpr int kCounterWords = 4 + 2 * kCounterLog;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -34,12 +37,15 @@ struct Ws {
   float *cent;        // fp32 [H][Cp][d]   working centroids
   half8 *ctab;        // fp16 fragments [H][CB][KC][64] of the scaled centroids
   float *cinit;       // fp32 [H][CB][2][16] accumulator init -||c*sc||^2 / 2
+  float4 *cbnd;       // [H][Cp] per-centroid bounds (||c*sc||, ||c*sc - c~||, ||c~||, ||c*sc||^2)
   uint32_t *stats;    // [H][T'][kStatWords]
   int4 *recheck;      // [H*NT*32] (head, token, j1, j2)
   int2 *fallback;     // [H*NT*32] (head, token)
-  uint32_t *counters; // [4]: 0 recheck entries, 1 fallback entries
+  uint32_t *counters; // [kCounterWords]: 0 recheck entries, 1 fallback entries of
+                      // the running assign; 4 + 2k (+1): counts of iteration k
   int32_t *sorted;    // [H][N] token ids grouped by cluster, token order inside
   int32_t *offs;      // [H][Cp+1] cluster segment offsets into `sorted`
+  uint32_t *hist;     // [H][ceil(N/kSortChunk)][256] per-chunk cluster counts
   int32_t *idx;       // [H][T][C] device copy of the seeded init indices
 };
 

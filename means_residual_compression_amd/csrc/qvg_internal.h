@@ -48,7 +48,7 @@ template <typename Tin, int D>
 bool launch_assign(const KmArgs &a, int bslot, hipStream_t s);
 template <typename Tin, typename Tc, int D>
 bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int64_t rec_hstride,
-                   float *cache, int64_t cache_hstride, hipStream_t s);
+                   float *cache, int64_t cache_hstride, int log_slot, hipStream_t s);
 
 // Elementwise kernels (qvg_quant.hip).
 bool launch_fill_u32(uint32_t *p, int64_t n, hipStream_t s);

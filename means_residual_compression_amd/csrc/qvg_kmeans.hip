@@ -31,6 +31,33 @@ __device__ __forceinline__ void atomic_max_pos(uint32_t *p, float v) {
   atomicMax(p, __float_as_uint(v));
 }
 
+// Workgroup copy global -> LDS with U loads in flight per thread.
+template <int U, typename T>
+__device__ __forceinline__ void block_copy(T *__restrict__ dst, const T *__restrict__ src, int n) {
+  const int step = U * (int)blockDim.x;
+  int base = 0;
+  for (; base + step <= n; base += step) {  // full rounds: no per-load condition
+    T tmp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) tmp[u] = src[base + u * (int)blockDim.x + (int)threadIdx.x];
+#pragma unroll
+    for (int u = 0; u < U; ++u) dst[base + u * (int)blockDim.x + (int)threadIdx.x] = tmp[u];
+  }
+  for (int q = base + (int)threadIdx.x; q < n; q += (int)blockDim.x) dst[q] = src[q];
+}
+
+// Max over a workgroup of up to 1024 threads (result valid in thread 0).
+__device__ __forceinline__ float block_max(float m) {
+  __shared__ float part[16];
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) part[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, part[w]);
+  return m;
+}
+
 template <typename Tin>
 __device__ __forceinline__ float head_scale(const uint32_t *st) {
   return ldexpf(1.0f, -scale_exp(fmaxf(stat_f(st, S_MAXR), stat_f(st, S_MAXC))));
@@ -51,8 +78,8 @@ __global__ void k_absmax(const Tin *__restrict__ x, int64_t per_head, uint32_t *
 #pragma unroll
     for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
   }
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0) atomic_max_pos(stats + (int64_t)h * stat_stride + slot, m);
+  m = block_max(m);
+  if (threadIdx.x == 0) atomic_max_pos(stats + (int64_t)h * stat_stride + slot, m);
 }
 
 // --------------------------------------------------------------- init
@@ -88,50 +115,54 @@ __global__ void k_init(const Tin *__restrict__ r, int N, const int32_t *__restri
 }
 
 // ------------------------------------------------------------ prepare
-// Thread per token: fp16 fragments of r * 2^-e for the MFMA B operand and the
-// token's bounds (||r~||, ||r*2^-e - r~||), both rounded up.
+// fp16 fragments of r * 2^-e for the MFMA B operand and each token's bounds
+// (||r~||, ||r*2^-e - r~||), rounded up.  D/8 lanes per token, each 8
+// channels, so a token row is read contiguously.
 // Fragment layout: [h][tile][kc][lane][8]; lane l holds token tile*32 + l%32
 // and channels kc*16 + 8*(l/32) + 0..7.
 template <typename Tin, int D>
 __global__ void k_prepare(const Tin *__restrict__ r, int N, int NT, const uint32_t *stats,
                           int stat_stride, half8 *__restrict__ rt, float2 *__restrict__ tb) {
-  constexpr int KC = D / 16;
+  constexpr int KC = D / 16, LPT = D / 8;
   const int h = blockIdx.y;
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= NT * kTile) return;
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool live = g < (int64_t)NT * kTile * LPT;
+  const int i = live ? (int)(g / LPT) : 0;
+  const int q = (int)(g % LPT);
   const float sc = head_scale<Tin>(stats + (int64_t)h * stat_stride);
-  const int tile = i / kTile, col = i % kTile;
-  half8 *frag = rt + ((int64_t)h * NT + tile) * KC * 64;
-  float n2 = 0.0f, e2 = 0.0f;
+  float v[8];
+  if (live && i < N) {
+    load8(r, ((int64_t)h * N + i) * D + q * 8, v);
+  } else {
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      float v[8];
-      if (i < N) {
-        load8(r, ((int64_t)h * N + i) * D + kc * 16 + hf * 8, v);
-      } else {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) v[m] = 0.0f;
-      }
-      half8 o;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float s = v[m] * sc;
-        const _Float16 q = (_Float16)s;
-        const float b = (float)q;
-        o[m] = q;
-        n2 += b * b;
-        e2 += (s - b) * (s - b);
-      }
-      frag[kc * 64 + col + 32 * hf] = o;
-    }
+    for (int m = 0; m < 8; ++m) v[m] = 0.0f;
   }
-  // sequential fp32 sums of D squares: relative error below 2^-12; the
-  // 1e-30 absolute term covers values that underflowed when scaled
-  const float up = 1.0f + 0x1p-12f;
-  tb[(int64_t)h * NT * kTile + i] =
-      make_float2(sqrtf(n2 * up) * (1.0f + 0x1p-20f), sqrtf(e2 * up) * (1.0f + 0x1p-20f) + 1e-30f);
+  float n2 = 0.0f, e2 = 0.0f;
+  half8 o;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const float s = v[m] * sc;
+    const _Float16 hq = (_Float16)s;
+    const float b = (float)hq;
+    o[m] = hq;
+    n2 += b * b;
+    e2 += (s - b) * (s - b);
+  }
+#pragma unroll
+  for (int off = 1; off < LPT; off <<= 1) {
+    n2 += __shfl_xor(n2, off);
+    e2 += __shfl_xor(e2, off);
+  }
+  if (!live) return;
+  const int tile = i / kTile, col = i % kTile, kc = q / 2, hf = q % 2;
+  rt[((int64_t)h * NT + tile) * KC * 64 + kc * 64 + col + 32 * hf] = o;
+  if (q == 0) {
+    // fp32 sums of D squares in any order: relative error below 2^-12; the
+    // 1e-30 absolute term covers values that underflowed when scaled
+    const float up = 1.0f + 0x1p-12f;
+    tb[(int64_t)h * NT * kTile + i] = make_float2(sqrtf(n2 * up) * (1.0f + 0x1p-20f),
+                                                  sqrtf(e2 * up) * (1.0f + 0x1p-20f) + 1e-30f);
+  }
 }
 
 // -------------------------------------------------------------- tables
@@ -141,7 +172,7 @@ __global__ void k_prepare(const Tin *__restrict__ r, int N, int NT, const uint32
 template <int D>
 __device__ __forceinline__ void emit_tables(int h, int j, int Cp, const float *cv, float sc,
                                             half8 *__restrict__ ctab, float *__restrict__ cinit,
-                                            uint32_t *bounds) {
+                                            float4 *__restrict__ cbnd, uint32_t *bounds) {
   constexpr int KC = D / 16, PER = D / 64;
   const int lane = threadIdx.x & 63;
   const int CB = Cp / kTile;
@@ -176,10 +207,15 @@ __device__ __forceinline__ void emit_tables(int h, int j, int Cp, const float *c
     const int rr = j % kTile, hf2 = (rr / 4) % 2, a = 4 * (rr / 8) + rr % 4;
     cinit[(((int64_t)h * CB + j / kTile) * 2 + hf2) * 16 + a] = (float)(-0.5 * n2);
     const float up = 1.0f + 0x1p-12f;
-    atomic_max_pos(bounds + 0, (float)sqrt(n2) * (1.0f + 0x1p-20f));
-    atomic_max_pos(bounds + 1, sqrtf(e2 * up) * (1.0f + 0x1p-20f) + 1e-30f);
-    atomic_max_pos(bounds + 2, sqrtf(t2 * up) * (1.0f + 0x1p-20f));
-    atomic_max_pos(bounds + 3, (float)n2 * (1.0f + 0x1p-20f));
+    const float4 bd = make_float4((float)sqrt(n2) * (1.0f + 0x1p-20f),
+                                  sqrtf(e2 * up) * (1.0f + 0x1p-20f) + 1e-30f,
+                                  sqrtf(t2 * up) * (1.0f + 0x1p-20f),
+                                  (float)n2 * (1.0f + 0x1p-20f));
+    cbnd[(int64_t)h * Cp + j] = bd;
+    atomic_max_pos(bounds + 0, bd.x);
+    atomic_max_pos(bounds + 1, bd.y);
+    atomic_max_pos(bounds + 2, bd.z);
+    atomic_max_pos(bounds + 3, bd.w);
   }
 }
 
@@ -187,7 +223,7 @@ __device__ __forceinline__ void emit_tables(int h, int j, int Cp, const float *c
 // keys never enter the top-2.
 template <int D>
 __device__ __forceinline__ void emit_pad(int h, int j, int Cp, half8 *__restrict__ ctab,
-                                         float *__restrict__ cinit) {
+                                         float *__restrict__ cinit, float4 *__restrict__ cbnd) {
   constexpr int KC = D / 16, PER = D / 64;
   const int lane = threadIdx.x & 63;
   const int CB = Cp / kTile;
@@ -200,6 +236,7 @@ __device__ __forceinline__ void emit_pad(int h, int j, int Cp, half8 *__restrict
   if (lane == 0) {
     const int rr = j % kTile, hf2 = (rr / 4) % 2, a = 4 * (rr / 8) + rr % 4;
     cinit[(((int64_t)h * CB + j / kTile) * 2 + hf2) * 16 + a] = -3.0e38f;
+    cbnd[(int64_t)h * Cp + j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   }
 }
 
@@ -207,14 +244,14 @@ __device__ __forceinline__ void emit_pad(int h, int j, int Cp, half8 *__restrict
 template <int D>
 __global__ void k_tables(const float *__restrict__ cent, int C, int Cp, const uint32_t *stats,
                          uint32_t *stats_w, int stat_stride, int bslot, half8 *__restrict__ ctab,
-                         float *__restrict__ cinit) {
+                         float *__restrict__ cinit, float4 *__restrict__ cbnd) {
   constexpr int PER = D / 64;
   const int h = blockIdx.y;
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (j >= Cp) return;
   if (j >= C) {
-    emit_pad<D>(h, j, Cp, ctab, cinit);
+    emit_pad<D>(h, j, Cp, ctab, cinit, cbnd);
     return;
   }
   const uint32_t *st = stats + (int64_t)h * stat_stride;
@@ -222,52 +259,77 @@ __global__ void k_tables(const float *__restrict__ cent, int C, int Cp, const ui
   float cv[PER];
 #pragma unroll
   for (int m = 0; m < PER; ++m) cv[m] = cent[((int64_t)h * Cp + j) * D + lane * PER + m];
-  emit_tables<D>(h, j, Cp, cv, sc, ctab, cinit, stats_w + (int64_t)h * stat_stride + bslot);
+  emit_tables<D>(h, j, Cp, cv, sc, ctab, cinit, cbnd, stats_w + (int64_t)h * stat_stride + bslot);
 }
 
 // ------------------------------------------------------------- assign
-// Workgroup: 4 waves, one head, `tiles_per_wg` consecutive 32-token tiles.
-// Each wave handles two tiles at a time against every 32-centroid block held
-// in LDS (fp16 fragments + accumulator inits).
+// Per-candidate error bound of a key (see the file header):
+//   E = er*||c|| + rn*||c - c~|| + kappa*(rn*||c~|| + n/2) + 2^-40*(rn+||c~||+er+ec)^2
+// with rn = ||r~||, er = ||r*sc - r~||; every factor is an upper bound.  The
+// kappa term covers fp32 accumulation of the MFMA (any order) and the 8-bit
+// index embedded in the key; the last term covers the fp64 rounding of the
+// exact distances the decision has to agree with.
+__device__ __forceinline__ float key_bound(float rn, float er, float cn, float ec, float ctn,
+                                           float n, float kappa) {
+  const float rc = rn + ctn + er + ec;
+  const float e = er * cn + rn * ec + kappa * fmaf(rn, ctn, 0.5f * n) + 0x1p-40f * rc * rc;
+  return e * (1.0f + 0x1p-20f) + 1e-37f;
+}
+
+// Persistent workgroups of 8 waves.  A work item is (head, 16 consecutive
+// 32-token tiles); each workgroup takes a contiguous range of work items and
+// reloads the head's tables into LDS only when the head changes.  Each wave
+// multiplies two token tiles (B operand, registers) by every 32-centroid
+// block (A operand, LDS).
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_assign(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_assign(
     const half8 *__restrict__ rt, const float2 *__restrict__ tb, const half8 *__restrict__ ctab,
-    const float *__restrict__ cinit, const uint32_t *__restrict__ stats, int stat_stride,
-    int bslot, int N, int NT, int CB, int tiles_per_wg, uint8_t *__restrict__ assign,
+    const float *__restrict__ cinit, const float4 *__restrict__ cbnd,
+    const uint32_t *__restrict__ stats, int stat_stride, int bslot, int N, int NT, int CB,
+    int groups_per_head, int total_groups, int groups_per_wg, uint8_t *__restrict__ assign,
     int64_t assign_hstride, int4 *__restrict__ recheck, int2 *__restrict__ fallback,
     uint32_t *__restrict__ counters, float kappa) {
   constexpr int KC = D / 16;
+  constexpr int TPG = 16;  // tiles per work item
   extern __shared__ __align__(16) unsigned char smem[];
   half8 *ctab_s = reinterpret_cast<half8 *>(smem);
   float *cinit_s = reinterpret_cast<float *>(smem + (size_t)CB * KC * 64 * sizeof(half8));
-
-  const int h = blockIdx.y;
+  float4 *cbnd_s = reinterpret_cast<float4 *>(cinit_s + CB * 32);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  {
-    const half8 *src = ctab + (int64_t)h * CB * KC * 64;
-    for (int q = threadIdx.x; q < CB * KC * 64; q += 256) ctab_s[q] = src[q];
-    const float *ci = cinit + (int64_t)h * CB * 32;
-    for (int q = threadIdx.x; q < CB * 32; q += 256) cinit_s[q] = ci[q];
-  }
-  __syncthreads();
-
-  const uint32_t *st = stats + (int64_t)h * stat_stride + bslot;
-  const float cmax = __uint_as_float(st[0]), ecmax = __uint_as_float(st[1]);
-  const float ctmax = __uint_as_float(st[2]), nmax = __uint_as_float(st[3]);
   const int half = lane >> 5;
   const uint32_t halfbits = (uint32_t)half << 2;
-
-  const int tile_lo = blockIdx.x * tiles_per_wg;
-  const int tile_hi = min(NT, tile_lo + tiles_per_wg);
-  for (int t0 = tile_lo + 2 * wave; t0 < tile_hi; t0 += 8) {
-    const bool has1 = t0 + 1 < tile_hi;
-    half8 b0[KC], b1[KC];
-    const half8 *f0 = rt + ((int64_t)h * NT + t0) * KC * 64 + lane;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      b0[kc] = f0[kc * 64];
-      b1[kc] = has1 ? f0[(KC + kc) * 64] : b0[kc];
+  // +inf and the mask live in VGPRs the compiler cannot see through, so that
+  // a max is one v_med3_f32 (no canonicalising moves) and inserting the index
+  // is one v_and_or_b32
+  float INF;
+  asm volatile("v_mov_b32 %0, 0x7f800000" : "=v"(INF));
+  uint32_t vmask;
+  asm volatile("v_mov_b32 %0, 0xffffff00" : "=v"(vmask));
+  const int Cp = CB * kTile;
+  int cached_h = -1;
+  const int g_lo = blockIdx.x * groups_per_wg;
+  const int g_hi = min(total_groups, g_lo + groups_per_wg);
+  for (int g = g_lo; g < g_hi; ++g) {
+    const int h = g / groups_per_head;
+    const int tile_lo = (g % groups_per_head) * TPG;
+    if (h != cached_h) {  // uniform over the workgroup
+      __syncthreads();
+      block_copy<8>(ctab_s, ctab + (int64_t)h * CB * KC * 64, CB * KC * 64);
+      block_copy<1>(cinit_s, cinit + (int64_t)h * CB * 32, CB * 32);
+      block_copy<1>(cbnd_s, cbnd + (int64_t)h * Cp, Cp);
+      __syncthreads();
+      cached_h = h;
     }
+    const int t0 = tile_lo + 2 * wave;
+    if (t0 >= NT) continue;
+    const int t1 = min(t0 + 1, NT - 1);
+    const half8 *f0 = rt + ((int64_t)h * NT + t0) * KC * 64 + lane;
+    const half8 *f1 = rt + ((int64_t)h * NT + t1) * KC * 64 + lane;
+    half8 b0[KC], b1[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) b0[kc] = f0[kc * 64];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) b1[kc] = f1[kc * 64];
     float a1 = -3.4e38f, a2 = -3.4e38f, a3 = -3.4e38f;
     float c1 = -3.4e38f, c2 = -3.4e38f, c3 = -3.4e38f;
     for (int cb = 0; cb < CB; ++cb) {
@@ -293,14 +355,14 @@ __global__ __launch_bounds__(256, 2) void k_assign(
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
         const uint32_t enc = base | (uint32_t)(8 * (a / 4) + (a % 4));
-        const float x0 = __uint_as_float((__float_as_uint(acc0[a]) & 0xFFFFFF00u) | enc);
-        const float x1 = __uint_as_float((__float_as_uint(acc1[a]) & 0xFFFFFF00u) | enc);
+        const float x0 = __uint_as_float((__float_as_uint(acc0[a]) & vmask) | enc);
+        const float x1 = __uint_as_float((__float_as_uint(acc1[a]) & vmask) | enc);
         a3 = __builtin_amdgcn_fmed3f(a2, a3, x0);
         a2 = __builtin_amdgcn_fmed3f(a1, a2, x0);
-        a1 = fmaxf(a1, x0);
+        a1 = __builtin_amdgcn_fmed3f(a1, x0, INF);
         c3 = __builtin_amdgcn_fmed3f(c2, c3, x1);
         c2 = __builtin_amdgcn_fmed3f(c1, c2, x1);
-        c1 = fmaxf(c1, x1);
+        c1 = __builtin_amdgcn_fmed3f(c1, x1, INF);
       }
     }
     // lanes >= 32 saw the rows with bit 2 set
@@ -314,31 +376,32 @@ __global__ __launch_bounds__(256, 2) void k_assign(
     // lanes >= 32 keep tile t0+1
     float m1 = half ? c1 : a1, m2 = half ? c2 : a2, m3 = half ? c3 : a3;
     const float s1 = half ? a1 : c1, s2 = half ? a2 : c2, s3 = half ? a3 : c3;
-    const float o1 = __shfl_xor(s1, 32), o2 = __shfl_xor(s2, 32), o3 = __shfl_xor(s3, 32);
-    const float oo[3] = {o1, o2, o3};
+    const float oo[3] = {__shfl_xor(s1, 32), __shfl_xor(s2, 32), __shfl_xor(s3, 32)};
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
       m3 = __builtin_amdgcn_fmed3f(m2, m3, oo[q]);
       m2 = __builtin_amdgcn_fmed3f(m1, m2, oo[q]);
-      m1 = fmaxf(m1, oo[q]);
+      m1 = __builtin_amdgcn_fmed3f(m1, oo[q], INF);
     }
     const int tile = t0 + half;
     const int tok = tile * kTile + (lane & 31);
-    if (tile < tile_hi && tok < N) {
+    if (tile < NT && tok < N) {
+      const uint32_t *st = stats + (int64_t)h * stat_stride + bslot;
+      const float cmax = __uint_as_float(st[0]), ecmax = __uint_as_float(st[1]);
+      const float ctmax = __uint_as_float(st[2]), nmax = __uint_as_float(st[3]);
       const float2 b = tb[(int64_t)h * NT * kTile + tok];
-      const float rn = b.x, er = b.y;
-      const float big = fmaf(rn, ctmax, 0.5f * nmax);
-      const float rc = rn + ctmax + er + ecmax;
-      float eps = er * cmax + rn * ecmax + kappa * big + 0x1p-40f * rc * rc;
-      eps = eps * (1.0f + 0x1p-20f) + 1e-37f;
-      const int j1 = (int)(__float_as_uint(m1) & 0xFFu);
-      const int j2 = (int)(__float_as_uint(m2) & 0xFFu);
+      const int j1 = min((int)(__float_as_uint(m1) & 0xFFu), Cp - 1);
+      const int j2 = min((int)(__float_as_uint(m2) & 0xFFu), Cp - 1);
+      const float4 B1 = cbnd_s[j1], B2 = cbnd_s[j2];
+      const float e1 = key_bound(b.x, b.y, B1.x, B1.y, B1.z, B1.w, kappa);
+      const float e2 = key_bound(b.x, b.y, B2.x, B2.y, B2.z, B2.w, kappa);
+      const float eg = key_bound(b.x, b.y, cmax, ecmax, ctmax, nmax, kappa);
       const float g12 = (m1 - m2) * (1.0f - 0x1p-20f);
       const float g13 = (m1 - m3) * (1.0f - 0x1p-20f);
       uint8_t *dst = assign + (int64_t)h * assign_hstride + tok;
-      if (g12 > 2.0f * eps) {
+      if (g12 > e1 + e2) {
         *dst = (uint8_t)j1;
-      } else if (g13 > 2.0f * eps) {
+      } else if (g13 > e1 + eg) {
         const uint32_t pos = atomicAdd(counters + 0, 1u);
         recheck[pos] = make_int4(h, tok, j1, j2);
       } else {
@@ -350,12 +413,13 @@ __global__ __launch_bounds__(256, 2) void k_assign(
 }
 
 // ------------------------------------------------------------ resolve
-// Exact fp64 squared distance, channel order, no fused multiply-add.
+// Exact fp64 squared distance, channel order, no fused multiply-add: the same
+// arithmetic as a plain sequential loop.
 template <typename Tin, int D>
-__device__ __forceinline__ double exact_dist(const Tin *__restrict__ row,
-                                             const float *__restrict__ c) {
+__device__ __attribute__((noinline)) double exact_dist(const Tin *__restrict__ row,
+                                                       const float *__restrict__ c) {
   double acc = 0.0;
-#pragma unroll
+#pragma unroll 1
   for (int k = 0; k < D; k += 8) {
     float v[8], w[8];
     load8(row, k, v);
@@ -369,129 +433,303 @@ __device__ __forceinline__ double exact_dist(const Tin *__restrict__ row,
   return acc;
 }
 
-// Thread per re-check entry: the nearer of the two candidates.
+// Both the sequential fp64 sum and any other fp64 summation order of the D
+// non-negative terms lie within gamma_{D+2} of the exact distance, so when two
+// distances computed in another order differ by more than
+// 2*gamma*(D1 + D2) (with slack), the sequential ones order the same way.
+template <int D>
+__device__ __forceinline__ double order_tol() {
+  return (2.0 * (D + 4) * 0x1p-53) * 1.01;
+}
+
+// Re-check of the two candidates: D/8 lanes per entry, each lane 8 channels,
+// fp64 partial sums combined by a fixed butterfly; the sequential fp64 replica
+// decides only when the margin is too thin to settle the order.
 template <typename Tin, int D>
-__global__ void k_recheck(const Tin *__restrict__ r, int N, const float *__restrict__ cent,
+__global__ __launch_bounds__(256) void k_recheck(const Tin *__restrict__ r, int N, const float *__restrict__ cent,
                           int Cp, const int4 *__restrict__ list,
                           const uint32_t *__restrict__ counters, uint8_t *__restrict__ assign,
                           int64_t assign_hstride) {
+  constexpr int LPE = D / 8, EPW = 64 / LPE;
   const uint32_t n = counters[0];
-  for (uint32_t e = blockIdx.x * blockDim.x + threadIdx.x; e < n; e += gridDim.x * blockDim.x) {
-    const int4 q = list[e];
+  const int lane = threadIdx.x & 63, sub = lane / LPE, li = lane % LPE;
+  const uint32_t gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const uint32_t nw = (gridDim.x * blockDim.x) >> 6;
+  for (uint32_t base = gw * EPW; base < n; base += nw * EPW) {
+    const uint32_t e = base + sub;
+    const bool live = e < n;
+    const int4 q = live ? list[e] : make_int4(0, 0, 0, 0);
     const Tin *row = r + ((int64_t)q.x * N + q.y) * D;
     const float *cb = cent + (int64_t)q.x * Cp * D;
-    const double d1 = exact_dist<Tin, D>(row, cb + (int64_t)q.z * D);
-    const double d2 = exact_dist<Tin, D>(row, cb + (int64_t)q.w * D);
-    const int j = (d2 < d1 || (d2 == d1 && q.w < q.z)) ? q.w : q.z;
-    assign[(int64_t)q.x * assign_hstride + q.y] = (uint8_t)j;
+    double s1 = 0.0, s2 = 0.0;
+    if (live) {
+      float v[8], w1[8], w2[8];
+      load8(row, li * 8, v);
+      load8(cb + (int64_t)q.z * D, li * 8, w1);
+      load8(cb + (int64_t)q.w * D, li * 8, w2);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const double d1 = (double)v[m] - (double)w1[m];
+        const double d2 = (double)v[m] - (double)w2[m];
+        s1 = __dadd_rn(s1, __dmul_rn(d1, d1));
+        s2 = __dadd_rn(s2, __dmul_rn(d2, d2));
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < LPE; o <<= 1) {
+      s1 = __dadd_rn(s1, __shfl_xor(s1, o));
+      s2 = __dadd_rn(s2, __shfl_xor(s2, o));
+    }
+    if (live && li == 0) {
+      const double diff = s2 - s1, tol = (s1 + s2) * order_tol<D>();
+      int j;
+      if (diff > tol) {
+        j = q.z;
+      } else if (diff < -tol) {
+        j = q.w;
+      } else {
+        const double d1 = exact_dist<Tin, D>(row, cb + (int64_t)q.z * D);
+        const double d2 = exact_dist<Tin, D>(row, cb + (int64_t)q.w * D);
+        j = (d2 < d1 || (d2 == d1 && q.w < q.z)) ? q.w : q.z;
+      }
+      assign[(int64_t)q.x * assign_hstride + q.y] = (uint8_t)j;
+    }
   }
 }
 
-// Wave per fallback entry: exact scan over all C centroids.
+// Exact scan over all centroids for the tokens the bound could not settle:
+// one wave per entry (grid-stride, so entries of any head spread over the
+// whole GPU), each lane owns centroids lane + 64m.  fp32 direct distances
+// (4 interleaved partial sums; within gamma_{D+2} of each distance in any
+// order) keep only the centroids that can still be the minimum; those get an
+// fp64 distance (4 partial sums), and any whose order against the best is not
+// settled by the margin get the sequential fp64 distance, the same arithmetic
+// as a plain loop.  Smallest distance wins, ties to the smallest index.
 template <typename Tin, int D>
-__global__ void k_fallback(const Tin *__restrict__ r, int N, const float *__restrict__ cent,
-                           int C, int Cp, const int2 *__restrict__ list,
-                           const uint32_t *__restrict__ counters, uint8_t *__restrict__ assign,
-                           int64_t assign_hstride) {
+__global__ __launch_bounds__(256) void k_fallback(const Tin *__restrict__ r, int N,
+                                                  const float *__restrict__ cent, int C, int Cp,
+                                                  const int2 *__restrict__ list,
+                                                  const uint32_t *__restrict__ counters,
+                                                  uint8_t *__restrict__ assign,
+                                                  int64_t assign_hstride) {
+  constexpr int D4 = D / 4;
+  constexpr float g32 = (float)(D + 2) * 0x1p-24f;
+  __shared__ float4 rsm[4][D4];
   const uint32_t n = counters[1];
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float4 *rs = rsm[wave];
   const uint32_t nw = gridDim.x * (blockDim.x >> 6);
-  for (uint32_t e = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); e < n; e += nw) {
+  for (uint32_t e = blockIdx.x * (blockDim.x >> 6) + wave; e < n; e += nw) {
     const int2 q = list[e];
     const Tin *row = r + ((int64_t)q.x * N + q.y) * D;
-    const float *cb = cent + (int64_t)q.x * Cp * D;
-    double best = 0.0;
-    int bj = -1;
-    for (int j = lane; j < C; j += 64) {
-      const double dj = exact_dist<Tin, D>(row, cb + (int64_t)j * D);
-      if (bj < 0 || dj < best) {
-        best = dj;
-        bj = j;
+    const float *ch = cent + (int64_t)q.x * Cp * D;
+    if (lane < D4) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = Elem<Tin>::get(row, lane * 4 + u);
+      rs[lane] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    __threadfence_block();
+    __builtin_amdgcn_wave_barrier();
+    float d32[4];
+    float mloc = __builtin_inff();
+    {
+      float4 acc[4];
+      const float4 *cj[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        acc[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+        cj[m] = reinterpret_cast<const float4 *>(ch + (int64_t)min(lane + 64 * m, C - 1) * D);
+      }
+#pragma unroll 4
+      for (int k4 = 0; k4 < D4; ++k4) {
+        const float4 x = rs[k4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float4 c = cj[m][k4];
+          const float dx = x.x - c.x, dy = x.y - c.y, dz = x.z - c.z, dw = x.w - c.w;
+          acc[m].x = __fadd_rn(acc[m].x, __fmul_rn(dx, dx));
+          acc[m].y = __fadd_rn(acc[m].y, __fmul_rn(dy, dy));
+          acc[m].z = __fadd_rn(acc[m].z, __fmul_rn(dz, dz));
+          acc[m].w = __fadd_rn(acc[m].w, __fmul_rn(dw, dw));
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float s = (acc[m].x + acc[m].y) + (acc[m].z + acc[m].w);
+        d32[m] = lane + 64 * m < C ? s : __builtin_inff();
+        mloc = fminf(mloc, d32[m]);
+      }
+    }
+    for (int o = 32; o > 0; o >>= 1) mloc = fminf(mloc, __shfl_xor(mloc, o));
+    const float cut = mloc * (1.0f + 3.0f * g32) * (1.0f + 0x1p-20f) + 1e-37f;
+    double dp[4];
+    double best = __builtin_inf();
+    int bj = 0x7fffffff;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int j = lane + 64 * m;
+      dp[m] = __builtin_inf();
+      if (j < C && d32[m] <= cut) {
+        const float4 *c4 = reinterpret_cast<const float4 *>(ch + (int64_t)j * D);
+        double p0 = 0.0, p1 = 0.0, p2 = 0.0, p3 = 0.0;
+#pragma unroll 4
+        for (int k4 = 0; k4 < D4; ++k4) {
+          const float4 x = rs[k4], c = c4[k4];
+          const double dx = (double)x.x - (double)c.x, dy = (double)x.y - (double)c.y;
+          const double dz = (double)x.z - (double)c.z, dw = (double)x.w - (double)c.w;
+          p0 = __dadd_rn(p0, __dmul_rn(dx, dx));
+          p1 = __dadd_rn(p1, __dmul_rn(dy, dy));
+          p2 = __dadd_rn(p2, __dmul_rn(dz, dz));
+          p3 = __dadd_rn(p3, __dmul_rn(dw, dw));
+        }
+        dp[m] = (p0 + p1) + (p2 + p3);
+        if (dp[m] < best) {
+          best = dp[m];
+          bj = j;
+        }
       }
     }
     for (int o = 32; o > 0; o >>= 1) {
       const double ob = __shfl_xor(best, o);
       const int oj = __shfl_xor(bj, o);
-      if (oj >= 0 && (bj < 0 || ob < best || (ob == best && oj < bj))) {
+      if (ob < best || (ob == best && oj < bj)) {
         best = ob;
         bj = oj;
       }
     }
+    const double tol = order_tol<D>();
+    bool near = false;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      near |= (lane + 64 * m != bj) && dp[m] - best <= tol * (dp[m] + best);
+    if (__ballot(near) != 0ull) {
+      double sb = __builtin_inf();
+      int sj = 0x7fffffff;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int j = lane + 64 * m;
+        if (j < C && (j == bj || dp[m] - best <= tol * (dp[m] + best))) {
+          const double d = exact_dist<Tin, D>(row, ch + (int64_t)j * D);
+          if (d < sb) {
+            sb = d;
+            sj = j;
+          }
+        }
+      }
+      for (int o = 32; o > 0; o >>= 1) {
+        const double ob = __shfl_xor(sb, o);
+        const int oj = __shfl_xor(sj, o);
+        if (ob < sb || (ob == sb && oj < sj)) {
+          sb = ob;
+          sj = oj;
+        }
+      }
+      bj = sj;
+    }
     if (lane == 0) assign[(int64_t)q.x * assign_hstride + q.y] = (uint8_t)bj;
+    __threadfence_block();
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
 // --------------------------------------------------------------- sort
-// One workgroup (16 waves) per head: stable counting sort of token ids by
-// cluster.  Each wave owns a contiguous token range; ranks inside a 64-token
-// group come from ballots, so token order is kept within every cluster.
-// Also clears the next bound slot and (head 0) the candidate-list counters.
-__global__ __launch_bounds__(1024) void k_sort(const uint8_t *__restrict__ assign,
-                                               int64_t assign_hstride, int N, int C, int Cp,
-                                               int32_t *__restrict__ sorted,
-                                               int32_t *__restrict__ offs, uint32_t *stats,
-                                               int stat_stride, int clear_slot,
-                                               uint32_t *counters) {
-  __shared__ uint32_t hist[16][kMaxC];
-  __shared__ uint32_t tot[kMaxC];
-  const int h = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Stable counting sort of token ids by cluster, in two kernels over chunks of
+// kSortChunk tokens: k_hist counts each chunk; k_scatter derives every
+// chunk's start position per cluster from the counts and writes the ids with
+// ranks taken from ballots, so token order is kept within every cluster.
+// k_hist also clears the next bound slot of the head and (first chunk of head
+// 0) logs and clears the candidate-list counters.
+__global__ __launch_bounds__(256) void k_hist(const uint8_t *__restrict__ assign,
+                                              int64_t assign_hstride, int N,
+                                              uint32_t *__restrict__ hist, uint32_t *stats,
+                                              int stat_stride, int clear_slot,
+                                              uint32_t *counters, int log_slot) {
+  __shared__ uint32_t cnt[kMaxC];
+  const int h = blockIdx.y, b = blockIdx.x;
+  const int nb = gridDim.x;
+  cnt[threadIdx.x] = 0;
+  if (b == 0 && threadIdx.x < 4) stats[(int64_t)h * stat_stride + clear_slot + threadIdx.x] = 0;
+  if (b == 0 && h == 0 && threadIdx.x < 2) {
+    // keep the finished iteration's candidate counts for diagnostics
+    if (log_slot >= 0 && log_slot < kCounterLog)
+      counters[4 + 2 * log_slot + threadIdx.x] = counters[threadIdx.x];
+    counters[threadIdx.x] = 0;
+  }
+  __syncthreads();
   const uint8_t *a = assign + (int64_t)h * assign_hstride;
-  const int chunk = (((N + 15) / 16) + 63) & ~63;
-  const int lo = min(N, wave * chunk), hi = min(N, lo + chunk);
-  for (int q = threadIdx.x; q < 16 * kMaxC; q += 1024) (&hist[0][0])[q] = 0;
-  if (threadIdx.x < 4) stats[(int64_t)h * stat_stride + clear_slot + threadIdx.x] = 0;
-  if (h == 0 && threadIdx.x < 2) counters[threadIdx.x] = 0;
+  const int lo = b * kSortChunk, hi = min(N, lo + kSortChunk);
+  for (int i = lo + threadIdx.x; i < hi; i += 256) atomicAdd(&cnt[a[i]], 1u);
   __syncthreads();
-  for (int i = lo + lane; i < hi; i += 64) atomicAdd(&hist[wave][a[i]], 1u);
-  __syncthreads();
-  if (threadIdx.x < kMaxC) {
-    uint32_t s = 0;
-    for (int w = 0; w < 16; ++w) s += hist[w][threadIdx.x];
-    tot[threadIdx.x] = s;
+  hist[((int64_t)h * nb + b) * kMaxC + threadIdx.x] = cnt[threadIdx.x];
+}
+
+__global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ assign,
+                                                 int64_t assign_hstride, int N, int Cp,
+                                                 const uint32_t *__restrict__ hist,
+                                                 int32_t *__restrict__ sorted,
+                                                 int32_t *__restrict__ offs) {
+  __shared__ uint32_t scan[kMaxC];
+  __shared__ uint32_t wbase[4][kMaxC];
+  const int h = blockIdx.y, b = blockIdx.x, nb = gridDim.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const uint8_t *a = assign + (int64_t)h * assign_hstride;
+  const int lo = b * kSortChunk, hi = min(N, lo + kSortChunk);
+  // this chunk's predecessors and all chunks, for byte value t
+  const uint32_t *hh = hist + (int64_t)h * nb * kMaxC + t;
+  uint32_t pre = 0, tot = 0;
+  for (int bb = 0; bb < nb; ++bb) {
+    const uint32_t c = hh[(int64_t)bb * kMaxC];
+    tot += c;
+    pre += bb < b ? c : 0u;
   }
+  // exclusive scan of the totals over the 256 byte values (Hillis-Steele);
+  // assignment bytes >= C (corrupt input only) get slots after the clusters
+  uint32_t mine = tot;
+  scan[t] = mine;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    // exclusive scan over all 256 byte values, so that assignment bytes >= C
-    // (possible only for corrupt input) still get in-range slots after the
-    // real clusters' segments
-    uint32_t run = 0;
-    for (int j = 0; j < kMaxC; ++j) {
-      const uint32_t t = tot[j];
-      tot[j] = run;
-      if (j <= Cp) offs[(int64_t)h * (Cp + 1) + j] = (int32_t)run;
-      run += t;
-    }
-    if (Cp == kMaxC) offs[(int64_t)h * (Cp + 1) + Cp] = (int32_t)run;
+  for (int o = 1; o < kMaxC; o <<= 1) {
+    const uint32_t add = t >= o ? scan[t - o] : 0u;
+    __syncthreads();
+    scan[t] = mine = mine + add;
+    __syncthreads();
   }
+  const uint32_t excl = mine - tot;
+  if (b == 0) {
+    if (t <= Cp) offs[(int64_t)h * (Cp + 1) + t] = (int32_t)excl;
+    if (Cp == kMaxC && t == kMaxC - 1) offs[(int64_t)h * (Cp + 1) + Cp] = (int32_t)mine;
+  }
+  // per-wave counts inside the chunk (each wave owns a quarter, in order)
+  for (int w = 0; w < 4; ++w) wbase[w][t] = 0;
   __syncthreads();
-  if (threadIdx.x < kMaxC) {
-    uint32_t run = tot[threadIdx.x];
-    for (int w = 0; w < 16; ++w) {
-      const uint32_t c = hist[w][threadIdx.x];
-      hist[w][threadIdx.x] = run;
+  const int q = (kSortChunk / 4);
+  const int wlo = min(hi, lo + wave * q), whi = min(hi, wlo + q);
+  for (int i = wlo + lane; i < whi; i += 64) atomicAdd(&wbase[wave][a[i]], 1u);
+  __syncthreads();
+  {
+    uint32_t run = excl + pre;
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t c = wbase[w][t];
+      wbase[w][t] = run;
       run += c;
     }
   }
   __syncthreads();
   int32_t *out = sorted + (int64_t)h * N;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int g = lo; g < hi; g += 64) {
+  for (int g = wlo; g < whi; g += 64) {
     const int i = g + lane;
-    const bool valid = i < hi;
+    const bool valid = i < whi;
     const uint32_t j = valid ? a[i] : 0u;
     uint64_t m = __ballot(valid);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const uint64_t bb = __ballot(valid && ((j >> b) & 1u));
-      m &= ((j >> b) & 1u) ? bb : ~bb;
+    for (int bit = 0; bit < 8; ++bit) {
+      const uint64_t bb = __ballot(valid && ((j >> bit) & 1u));
+      m &= ((j >> bit) & 1u) ? bb : ~bb;
     }
-    if (valid) {
-      const uint32_t rank = __popcll(m & lt);
-      out[hist[wave][j] + rank] = i;
-    }
+    if (valid) out[wbase[wave][j] + __popcll(m & lt)] = i;
     __builtin_amdgcn_wave_barrier();
-    if (valid && (m >> lane) == 1ull) hist[wave][j] += __popcll(m);
+    if (valid && (m >> lane) == 1ull) wbase[wave][j] += __popcll(m);
     __builtin_amdgcn_wave_barrier();
   }
 }
@@ -507,7 +745,8 @@ __global__ void k_accumulate(const Tin *__restrict__ r, int N, const int32_t *__
                              const int32_t *__restrict__ offs, int C, int Cp,
                              float *__restrict__ cent, const uint32_t *stats, uint32_t *stats_w,
                              int stat_stride, int bslot, half8 *__restrict__ ctab,
-                             float *__restrict__ cinit, Tc *__restrict__ rec_c,
+                             float *__restrict__ cinit, float4 *__restrict__ cbnd,
+                             Tc *__restrict__ rec_c,
                              int64_t rec_hstride, float *__restrict__ cache,
                              int64_t cache_hstride) {
   constexpr int PER = D / 64;
@@ -516,33 +755,51 @@ __global__ void k_accumulate(const Tin *__restrict__ r, int N, const int32_t *__
   const int lane = threadIdx.x & 63;
   if (j >= Cp) return;
   if (j >= C) {
-    if (ctab) emit_pad<D>(h, j, Cp, ctab, cinit);
+    if (ctab) emit_pad<D>(h, j, Cp, ctab, cinit, cbnd);
     return;
   }
-  const int32_t lo = offs[(int64_t)h * (Cp + 1) + j], hi = offs[(int64_t)h * (Cp + 1) + j + 1];
+  // cluster bounds are wave-uniform: keep them in scalar registers
+  const int32_t lo = __builtin_amdgcn_readfirstlane(offs[(int64_t)h * (Cp + 1) + j]);
+  const int32_t hi = __builtin_amdgcn_readfirstlane(offs[(int64_t)h * (Cp + 1) + j + 1]);
   const int32_t *mem = sorted + (int64_t)h * N;
   const Tin *rh = r + (int64_t)h * N * D + lane * PER;
   double s[PER];
 #pragma unroll
   for (int m = 0; m < PER; ++m) s[m] = 0.0;
-  int32_t p = lo;
-  for (; p + 8 <= hi; p += 8) {
-    float v[8][PER];
+  // Member ids are read 64 at a time (one per lane, the next 64 prefetched)
+  // and broadcast with readlane; member rows are loaded B at a time (indices
+  // past the end are clamped, their values unused), one batch ahead of the
+  // adds, which stay in token order.
+  constexpr int B = 16;
+  int32_t ids = mem[min(lo + lane, max(hi - 1, lo))];
+  for (int32_t base = lo; base < hi; base += 64) {
+    const int cnt = min(64, hi - base);
+    const int32_t next = mem[min(base + 64 + lane, max(hi - 1, lo))];
+    float va[B][PER], vb[B][PER];
+    auto load = [&](int u0, float (&v)[B][PER]) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t row = (int64_t)mem[p + u] * D;
+      for (int u = 0; u < B; ++u) {
+        const int64_t row = (int64_t)__builtin_amdgcn_readlane(ids, min(u0 + u, cnt - 1)) * D;
 #pragma unroll
-      for (int m = 0; m < PER; ++m) v[u][m] = Elem<Tin>::get(rh, row + m);
+        for (int m = 0; m < PER; ++m) v[u][m] = Elem<Tin>::get(rh, row + m);
+      }
+    };
+    auto add = [&](int u0, const float (&v)[B][PER]) {
+#pragma unroll
+      for (int u = 0; u < B; ++u)
+        if (u0 + u < cnt)
+#pragma unroll
+          for (int m = 0; m < PER; ++m) s[m] = __dadd_rn(s[m], (double)v[u][m]);
+    };
+    load(0, va);
+    for (int u0 = 0; u0 < cnt; u0 += 2 * B) {
+      if (u0 + B < cnt) load(u0 + B, vb);
+      add(u0, va);
+      if (u0 + B >= cnt) break;
+      if (u0 + 2 * B < cnt) load(u0 + 2 * B, va);
+      add(u0 + B, vb);
     }
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int m = 0; m < PER; ++m) s[m] = __dadd_rn(s[m], (double)v[u][m]);
-  }
-  for (; p < hi; ++p) {
-    const int64_t row = (int64_t)mem[p] * D;
-#pragma unroll
-    for (int m = 0; m < PER; ++m) s[m] = __dadd_rn(s[m], (double)Elem<Tin>::get(rh, row + m));
+    ids = next;
   }
   float *cj = cent + ((int64_t)h * Cp + j) * D + lane * PER;
   float cv[PER];
@@ -555,7 +812,7 @@ __global__ void k_accumulate(const Tin *__restrict__ r, int N, const int32_t *__
   if (ctab) {
     const uint32_t *st = stats + (int64_t)h * stat_stride;
     const float sc = ldexpf(1.0f, -scale_exp(fmaxf(stat_f(st, S_MAXR), stat_f(st, S_MAXC))));
-    emit_tables<D>(h, j, Cp, cv, sc, ctab, cinit, stats_w + (int64_t)h * stat_stride + bslot);
+    emit_tables<D>(h, j, Cp, cv, sc, ctab, cinit, cbnd, stats_w + (int64_t)h * stat_stride + bslot);
   }
   if (rec_c) {
 #pragma unroll
@@ -567,21 +824,39 @@ __global__ void k_accumulate(const Tin *__restrict__ r, int N, const int32_t *__
 }
 
 // ============================================================ launchers
-namespace {
-template <int D> int kc_of() { return D / 16; }
-}
-
 #define QVG_CHECK_LAUNCH() \
   do { if (hipGetLastError() != hipSuccess) return false; } while (0)
+
+namespace {
+// Compute units of the current device (cached per device id).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Raise a kernel's dynamic LDS limit once per process.
+bool allow_lds(const void *fn, size_t bytes) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) ==
+         hipSuccess;
+}
+}  // namespace
 
 template <typename Tin>
 bool launch_absmax(const void *x, int H, int64_t per_head, uint32_t *stats, int stat_stride,
                    int slot, hipStream_t s) {
-  int64_t blocks = (per_head / 8 + 255) / 256;
-  dim3 grid((unsigned)std::min<int64_t>(blocks, 1024), H);
-  { TimerScope ts_("absmax", s);
+  const int64_t blocks = (per_head / 8 + 255) / 256;
+  dim3 grid((unsigned)std::min<int64_t>(blocks, 64), H);
+  TimerScope ts_("absmax", s);
   hipLaunchKernelGGL(k_absmax<Tin>, grid, dim3(256), 0, s, (const Tin *)x, per_head, stats,
-                     stat_stride, slot); }
+                     stat_stride, slot);
   QVG_CHECK_LAUNCH();
   return true;
 }
@@ -589,70 +864,90 @@ bool launch_absmax(const void *x, int H, int64_t per_head, uint32_t *stats, int 
 template <typename Tin, int D>
 bool launch_kmeans_stage_begin(const KmArgs &a, hipStream_t s) {
   dim3 gc((a.Cp + 3) / 4, a.H);
-  { TimerScope ts_("kmeans_init", s);
-  hipLaunchKernelGGL((k_init<Tin, D>), gc, dim3(256), 0, s, (const Tin *)a.r, a.N, a.idx,
-                     a.idx_hstride, a.init, a.init_hstride, a.C, a.Cp, a.ws.cent, a.ws_stats,
-                     a.stat_stride); }
-  QVG_CHECK_LAUNCH();
-  dim3 gp((a.NT * kTile + 255) / 256, a.H);
-  { TimerScope ts_("kmeans_prepare", s);
-  hipLaunchKernelGGL((k_prepare<Tin, D>), gp, dim3(256), 0, s, (const Tin *)a.r, a.N, a.NT,
-                     a.ws_stats, a.stat_stride, a.ws.rt, a.ws.tb); }
-  QVG_CHECK_LAUNCH();
-  { TimerScope ts_("kmeans_tables", s);
-  hipLaunchKernelGGL((k_tables<D>), gc, dim3(256), 0, s, a.ws.cent, a.C, a.Cp, a.ws_stats,
-                     a.ws_stats, a.stat_stride, (int)S_B0, a.ws.ctab, a.ws.cinit); }
-  QVG_CHECK_LAUNCH();
+  {
+    TimerScope ts_("kmeans_init", s);
+    hipLaunchKernelGGL((k_init<Tin, D>), gc, dim3(256), 0, s, (const Tin *)a.r, a.N, a.idx,
+                       a.idx_hstride, a.init, a.init_hstride, a.C, a.Cp, a.ws.cent, a.ws_stats,
+                       a.stat_stride);
+    QVG_CHECK_LAUNCH();
+  }
+  {
+    const int64_t threads = (int64_t)a.NT * kTile * (D / 8);
+    dim3 gp((unsigned)((threads + 255) / 256), a.H);
+    TimerScope ts_("kmeans_prepare", s);
+    hipLaunchKernelGGL((k_prepare<Tin, D>), gp, dim3(256), 0, s, (const Tin *)a.r, a.N, a.NT,
+                       a.ws_stats, a.stat_stride, a.ws.rt, a.ws.tb);
+    QVG_CHECK_LAUNCH();
+  }
+  {
+    TimerScope ts_("kmeans_tables", s);
+    hipLaunchKernelGGL((k_tables<D>), gc, dim3(256), 0, s, a.ws.cent, a.C, a.Cp, a.ws_stats,
+                       a.ws_stats, a.stat_stride, (int)S_B0, a.ws.ctab, a.ws.cinit, a.ws.cbnd);
+    QVG_CHECK_LAUNCH();
+  }
   return true;
 }
 
 template <typename Tin, int D>
 bool launch_assign(const KmArgs &a, int bslot, hipStream_t s) {
-  constexpr int KC = D / 16;
+  constexpr int KC = D / 16, TPG = 16;
   const int CB = a.Cp / kTile;
-  const size_t lds = (size_t)CB * KC * 64 * sizeof(half8) + (size_t)CB * 32 * sizeof(float);
-  const int tiles_per_wg = 16;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void *)k_assign<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            96 * 1024) != hipSuccess)
-      return false;
-    attr_set = true;
+  const size_t lds = (size_t)CB * KC * 64 * sizeof(half8) + (size_t)CB * 32 * sizeof(float) +
+                     (size_t)a.Cp * sizeof(float4);
+  static bool attr_assign = allow_lds((const void *)k_assign<D>, 96 * 1024);
+  if (!attr_assign) return false;
+  const int groups_per_head = (a.NT + TPG - 1) / TPG;
+  const int total = groups_per_head * a.H;
+  const int target = 2 * cu_count();
+  const int per_wg = (total + target - 1) / target;
+  const int grid = (total + per_wg - 1) / per_wg;
+  {
+    TimerScope ts_("kmeans_assign", s);
+    hipLaunchKernelGGL((k_assign<D>), dim3(grid), dim3(512), lds, s, a.ws.rt, a.ws.tb,
+                       a.ws.ctab, a.ws.cinit, a.ws.cbnd, a.ws_stats, a.stat_stride, bslot, a.N,
+                       a.NT, CB, groups_per_head, total, per_wg, a.assign, a.assign_hstride,
+                       a.ws.recheck, a.ws.fallback, a.ws.counters, a.kappa);
+    QVG_CHECK_LAUNCH();
   }
-  dim3 grid((a.NT + tiles_per_wg - 1) / tiles_per_wg, a.H);
-  { TimerScope ts_("kmeans_assign", s);
-  hipLaunchKernelGGL((k_assign<D>), grid, dim3(256), lds, s, a.ws.rt, a.ws.tb, a.ws.ctab,
-                     a.ws.cinit, a.ws_stats, a.stat_stride, bslot, a.N, a.NT, CB, tiles_per_wg,
-                     a.assign, a.assign_hstride, a.ws.recheck, a.ws.fallback, a.ws.counters,
-                     a.kappa); }
-  QVG_CHECK_LAUNCH();
-  { TimerScope ts_("kmeans_recheck", s);
-  hipLaunchKernelGGL((k_recheck<Tin, D>), dim3(512), dim3(256), 0, s, (const Tin *)a.r, a.N,
-                     a.ws.cent, a.Cp, a.ws.recheck, a.ws.counters, a.assign, a.assign_hstride); }
-  QVG_CHECK_LAUNCH();
-  { TimerScope ts_("kmeans_fallback", s);
-  hipLaunchKernelGGL((k_fallback<Tin, D>), dim3(512), dim3(256), 0, s, (const Tin *)a.r, a.N,
-                     a.ws.cent, a.C, a.Cp, a.ws.fallback, a.ws.counters, a.assign,
-                     a.assign_hstride); }
-  QVG_CHECK_LAUNCH();
+  {
+    TimerScope ts_("kmeans_recheck", s);
+    hipLaunchKernelGGL((k_recheck<Tin, D>), dim3(1024), dim3(256), 0, s, (const Tin *)a.r, a.N,
+                       a.ws.cent, a.Cp, a.ws.recheck, a.ws.counters, a.assign,
+                       a.assign_hstride);
+    QVG_CHECK_LAUNCH();
+  }
+  {
+    TimerScope ts_("kmeans_fallback", s);
+    hipLaunchKernelGGL((k_fallback<Tin, D>), dim3(512), dim3(256), 0, s, (const Tin *)a.r, a.N,
+                       a.ws.cent, a.C, a.Cp, a.ws.fallback, a.ws.counters, a.assign,
+                       a.assign_hstride);
+    QVG_CHECK_LAUNCH();
+  }
   return true;
 }
 
 template <typename Tin, typename Tc, int D>
 bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int64_t rec_hstride,
-                   float *cache, int64_t cache_hstride, hipStream_t s) {
-  { TimerScope ts_("kmeans_sort", s);
-  hipLaunchKernelGGL(k_sort, dim3(a.H), dim3(1024), 0, s, a.assign, a.assign_hstride, a.N, a.C,
-                     a.Cp, a.ws.sorted, a.ws.offs, a.ws_stats, a.stat_stride, next_bslot,
-                     a.ws.counters); }
-  QVG_CHECK_LAUNCH();
-  dim3 gc((a.Cp + 3) / 4, a.H);
-  { TimerScope ts_("kmeans_accumulate", s);
-  hipLaunchKernelGGL((k_accumulate<Tin, Tc, D>), gc, dim3(256), 0, s, (const Tin *)a.r, a.N,
-                     a.ws.sorted, a.ws.offs, a.C, a.Cp, a.ws.cent, a.ws_stats, a.ws_stats,
-                     a.stat_stride, next_bslot, tables ? a.ws.ctab : nullptr, a.ws.cinit, rec_c,
-                     rec_hstride, cache, cache_hstride); }
-  QVG_CHECK_LAUNCH();
+                   float *cache, int64_t cache_hstride, int log_slot, hipStream_t s) {
+  {
+    const int nb = (a.N + kSortChunk - 1) / kSortChunk;
+    TimerScope ts_("kmeans_sort", s);
+    hipLaunchKernelGGL(k_hist, dim3(nb, a.H), dim3(256), 0, s, a.assign, a.assign_hstride, a.N,
+                       a.ws.hist, a.ws_stats, a.stat_stride, next_bslot, a.ws.counters, log_slot);
+    QVG_CHECK_LAUNCH();
+    hipLaunchKernelGGL(k_scatter, dim3(nb, a.H), dim3(256), 0, s, a.assign, a.assign_hstride,
+                       a.N, a.Cp, a.ws.hist, a.ws.sorted, a.ws.offs);
+    QVG_CHECK_LAUNCH();
+  }
+  {
+    dim3 gc((a.Cp + 3) / 4, a.H);
+    TimerScope ts_("kmeans_accumulate", s);
+    hipLaunchKernelGGL((k_accumulate<Tin, Tc, D>), gc, dim3(256), 0, s, (const Tin *)a.r, a.N,
+                       a.ws.sorted, a.ws.offs, a.C, a.Cp, a.ws.cent, a.ws_stats, a.ws_stats,
+                       a.stat_stride, next_bslot, tables ? a.ws.ctab : nullptr, a.ws.cinit,
+                       a.ws.cbnd, rec_c, rec_hstride, cache, cache_hstride);
+    QVG_CHECK_LAUNCH();
+  }
   return true;
 }
 
@@ -660,9 +955,9 @@ bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int6
   template bool launch_kmeans_stage_begin<Tin, D>(const KmArgs &, hipStream_t);               \
   template bool launch_assign<Tin, D>(const KmArgs &, int, hipStream_t);                      \
   template bool launch_update<Tin, float, D>(const KmArgs &, int, bool, float *, int64_t,     \
-                                             float *, int64_t, hipStream_t);                  \
+                                             float *, int64_t, int, hipStream_t);             \
   template bool launch_update<Tin, uint16_t, D>(const KmArgs &, int, bool, uint16_t *,        \
-                                                int64_t, float *, int64_t, hipStream_t);
+                                                int64_t, float *, int64_t, int, hipStream_t);
 QVG_INST(float, 64)
 QVG_INST(float, 128)
 QVG_INST(uint16_t, 64)

@@ -48,9 +48,15 @@ __global__ void k_subtract(const Tin *__restrict__ r, int N, int D, int C, const
     }
     store8(out, off, v);
   }
-  if (stats) {
+  if (stats) {  // one atomic per workgroup
+    __shared__ float part[4];
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if ((threadIdx.x & 63) == 0) atomicMax(stats + (int64_t)h * stat_stride + slot, __float_as_uint(m));
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      m = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+      atomicMax(stats + (int64_t)h * stat_stride + slot, __float_as_uint(m));
+    }
   }
 }
 

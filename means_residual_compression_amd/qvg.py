@@ -24,7 +24,7 @@ EXPORTS = ["qvg_status_string", "qvg_last_error", "qvg_workspace_size", "qvg_com
            "qvg_compress_stream", "qvg_decompress", "qvg_assign_workspace_size",
            "qvg_kmeans_assign", "qvg_update_workspace_size", "qvg_kmeans_update",
            "qvg_sas_subtract", "qvg_group_quant_pack", "qvg_timing_enable", "qvg_timing_reset",
-           "qvg_timing_read"]
+           "qvg_timing_read", "qvg_candidate_counts"]
 
 
 class QvgError(RuntimeError):
@@ -91,6 +91,7 @@ def lib() -> ct.CDLL:
             "qvg_timing_enable": ([ct.c_int], None),
             "qvg_timing_reset": ([], None),
             "qvg_timing_read": ([ct.c_char_p, ct.POINTER(ct.c_double)], i64),
+            "qvg_candidate_counts": ([p, i64, i64, i64, ct.c_int, P, p, i32], ct.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -277,3 +278,13 @@ def timing_read(kernel: str):
     if n < 0:
         raise QvgError(4, "timing read failed")
     return ms.value, int(n)
+
+
+def candidate_counts(ws: torch.Tensor, x: torch.Tensor, p: Params, n_iters: int) -> np.ndarray:
+    """[n_iters, 2] (re-checked, fully scanned) token counts of the last compress
+    that used `ws` for input shaped like `x` (synchronises the device)."""
+    H, N, d = x.shape
+    out = np.zeros(2 * n_iters, np.uint32)
+    _check(lib().qvg_candidate_counts(ws.data_ptr(), H, N, d, _dt(x), ct.byref(p),
+                                      out.ctypes.data_as(ct.c_void_p), n_iters))
+    return out.reshape(n_iters, 2)
