@@ -164,11 +164,14 @@ qvg_status qvg_kmeans_assign(const void *r, qvg_dtype dtype, int64_t H, int64_t 
                              size_t ws_bytes, void *stream);
 
 /* Bytes of workspace qvg_kmeans_update needs. */
-size_t qvg_update_workspace_size(int64_t H, int64_t N, int32_t C);
+size_t qvg_update_workspace_size(int64_t H, int64_t N, int64_t d, int32_t C);
 
 /* k-means update step (note.zhuruihan.top SAS step 2, centroid = mean value):
- * centroids[h][j] = fp32(sum_{i: assign=j} r_hi / n_j) with the sum in fp64
- * in token order; clusters with no member keep their value.
+ * centroids[h][j] = fp32(sum_{i: assign=j} r_hi / n_j) with fp64 sums: the
+ * members, in token order, are summed in fp64 in chunks of 64 and the chunk
+ * sums are added in order (identical to one sequential fp64 sum whenever the
+ * fp64 sums are exact, e.g. for bf16 inputs); the fp64 mean is rounded to
+ * fp32.  Clusters with no member keep their value.
  * centroids: device fp32 [H][C][d], read and written. */
 qvg_status qvg_kmeans_update(const void *r, qvg_dtype dtype, int64_t H, int64_t N, int64_t d,
                              const uint8_t *assign, int32_t C, float *centroids, void *ws,

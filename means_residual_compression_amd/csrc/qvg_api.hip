@@ -36,7 +36,8 @@ size_t up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 // Workspace layout shared by the size query and the carve-up.
 struct Layout {
-  size_t rbuf, rt, tb, cent, ctab, cinit, cbnd, stats, recheck, fallback, counters, sorted, offs, hist, idx;
+  size_t rbuf, rt, tb, cent, ctab, cinit, cbnd, stats, recheck, fallback, counters, sorted, offs, hist,
+      cofs, chunk_j, part, idx;
   size_t total;
 };
 
@@ -62,6 +63,9 @@ Layout make_layout(int64_t H, int64_t N, int64_t d, int64_t C, int64_t T, bool n
   L.sorted = take((size_t)(H * N * 4));
   L.offs = take((size_t)(H * (Cp + 1) * 4));
   L.hist = take((size_t)(H * ((N + kSortChunk - 1) / kSortChunk) * kMaxC * 4));
+  L.cofs = take((size_t)(H * (Cp + 1) * 4));
+  L.chunk_j = take((size_t)(H * max_chunks((int)N, (int)Cp) * 4));
+  L.part = take((size_t)(H * max_chunks((int)N, (int)Cp) * d * 8));
   L.idx = take(need_idx ? (size_t)(H * T * C * 4) : 0);
   L.total = o;
   return L;
@@ -84,6 +88,9 @@ Ws carve(void *ws, const Layout &L) {
   w.sorted = (int32_t *)(b + L.sorted);
   w.offs = (int32_t *)(b + L.offs);
   w.hist = (uint32_t *)(b + L.hist);
+  w.cofs = (int32_t *)(b + L.cofs);
+  w.chunk_j = (int32_t *)(b + L.chunk_j);
+  w.part = (double *)(b + L.part);
   w.idx = (int32_t *)(b + L.idx);
   return w;
 }
@@ -356,14 +363,17 @@ qvg_status qvg_kmeans_assign(const void *r, qvg_dtype dtype, int64_t H, int64_t 
   return ok ? QVG_OK : hip_fail("kmeans_assign");
 }
 
-size_t qvg_update_workspace_size(int64_t H, int64_t N, int32_t C) {
-  if (H < 1 || N < 1 || C < 1 || C > kMaxC) return 0;
+size_t qvg_update_workspace_size(int64_t H, int64_t N, int64_t d, int32_t C) {
+  if (check_dims(H, N, d, QVG_F32) != QVG_OK || C < 1 || C > kMaxC) return 0;
   size_t o = 0;
   o = up(o + (size_t)(H * kStatWords * 4));  // stats
   o = up(o + kCounterWords * 4);             // counters
   o = up(o + (size_t)(H * N * 4));           // sorted
   o = up(o + (size_t)(H * (C + 1) * 4));     // offs
   o = up(o + (size_t)(H * ((N + kSortChunk - 1) / kSortChunk) * kMaxC * 4));  // hist
+  o = up(o + (size_t)(H * (C + 1) * 4));                                        // cofs
+  o = up(o + (size_t)(H * max_chunks((int)N, C) * 4));                           // chunk_j
+  o = up(o + (size_t)(H * max_chunks((int)N, C) * d * 8));                       // part
   return o;
 }
 
@@ -375,7 +385,7 @@ qvg_status qvg_kmeans_update(const void *r, qvg_dtype dtype, int64_t H, int64_t 
   if (st != QVG_OK) return st;
   if (C < 1 || C > kMaxC) return fail(QVG_ERR_UNSUPPORTED, "C=%d must be in [1, 256]", C);
   if (!r || !assign || !centroids) return fail(QVG_ERR_INVALID_ARG, "NULL pointer argument");
-  const size_t need = qvg_update_workspace_size(H, N, C);
+  const size_t need = qvg_update_workspace_size(H, N, d, C);
   if (!ws || ws_bytes < need) return fail(QVG_ERR_WORKSPACE, "workspace smaller than %zu bytes", need);
   char *b = (char *)ws;
   Ws w{};
@@ -384,7 +394,10 @@ qvg_status qvg_kmeans_update(const void *r, qvg_dtype dtype, int64_t H, int64_t 
   w.counters = (uint32_t *)(b + o); o = up(o + kCounterWords * 4);
   w.sorted = (int32_t *)(b + o); o = up(o + (size_t)(H * N * 4));
   w.offs = (int32_t *)(b + o); o = up(o + (size_t)(H * (C + 1) * 4));
-  w.hist = (uint32_t *)(b + o);
+  w.hist = (uint32_t *)(b + o); o = up(o + (size_t)(H * ((N + kSortChunk - 1) / kSortChunk) * kMaxC * 4));
+  w.cofs = (int32_t *)(b + o); o = up(o + (size_t)(H * (C + 1) * 4));
+  w.chunk_j = (int32_t *)(b + o); o = up(o + (size_t)(H * max_chunks((int)N, C) * 4));
+  w.part = (double *)(b + o);
   w.cent = centroids;
   KmArgs a;
   a.H = (int)H; a.N = (int)N; a.C = C; a.Cp = C; a.NT = 0;

@@ -10,6 +10,7 @@ constexpr int kMaxC = 256;  // assignments are uint8
 constexpr int kMaxT = 8;
 constexpr int kTile = 32;   // tokens (and centroids) per 32x32 MFMA tile
 constexpr int kSortChunk = 1024; // tokens per block of the counting sort
+constexpr int kAccChunk = 64;    // cluster members per partial sum of the update
 constexpr int kCounterLog = 64;  // iterations whose candidate counts are kept
 constexpr int kCounterWords = 4 + 2 * kCounterLog;
 
@@ -46,10 +47,18 @@ struct Ws {
   int32_t *sorted;    // [H][N] token ids grouped by cluster, token order inside
   int32_t *offs;      // [H][Cp+1] cluster segment offsets into `sorted`
   uint32_t *hist;     // [H][ceil(N/kSortChunk)][256] per-chunk cluster counts
+  int32_t *cofs;      // [H][Cp+1] first member-chunk of each cluster
+  int32_t *chunk_j;   // [H][max_chunks] cluster of each member-chunk
+  double *part;       // [H][max_chunks][d] fp64 partial sums of member-chunks
   int32_t *idx;       // [H][T][C] device copy of the seeded init indices
 };
 
 __host__ __device__ inline int pad32(int x) { return (x + 31) & ~31; }
+// Upper bound on member-chunks per head: every cluster adds at most one
+// partially filled chunk.
+__host__ __device__ inline int max_chunks(int N, int Cp) {
+  return (N + kAccChunk - 1) / kAccChunk + Cp;
+}
 
 // ------------------------------------------------------------------ bf16
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

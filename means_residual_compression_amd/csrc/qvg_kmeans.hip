@@ -212,10 +212,6 @@ __device__ __forceinline__ void emit_tables(int h, int j, int Cp, const float *c
                                   sqrtf(t2 * up) * (1.0f + 0x1p-20f),
                                   (float)n2 * (1.0f + 0x1p-20f));
     cbnd[(int64_t)h * Cp + j] = bd;
-    atomic_max_pos(bounds + 0, bd.x);
-    atomic_max_pos(bounds + 1, bd.y);
-    atomic_max_pos(bounds + 2, bd.z);
-    atomic_max_pos(bounds + 3, bd.w);
   }
 }
 
@@ -295,6 +291,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   half8 *ctab_s = reinterpret_cast<half8 *>(smem);
   float *cinit_s = reinterpret_cast<float *>(smem + (size_t)CB * KC * 64 * sizeof(half8));
   float4 *cbnd_s = reinterpret_cast<float4 *>(cinit_s + CB * 32);
+  __shared__ float4 hmax_s;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5;
   const uint32_t halfbits = (uint32_t)half << 2;
@@ -317,6 +314,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       block_copy<8>(ctab_s, ctab + (int64_t)h * CB * KC * 64, CB * KC * 64);
       block_copy<1>(cinit_s, cinit + (int64_t)h * CB * 32, CB * 32);
       block_copy<1>(cbnd_s, cbnd + (int64_t)h * Cp, Cp);
+      __syncthreads();
+      // per-head maxima of the per-centroid bounds (bound for all centroids)
+      if (wave == 0) {
+        float4 mx = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int q = lane; q < Cp; q += 64) {
+          const float4 b = cbnd_s[q];
+          mx.x = fmaxf(mx.x, b.x);
+          mx.y = fmaxf(mx.y, b.y);
+          mx.z = fmaxf(mx.z, b.z);
+          mx.w = fmaxf(mx.w, b.w);
+        }
+        for (int o = 32; o > 0; o >>= 1) {
+          mx.x = fmaxf(mx.x, __shfl_xor(mx.x, o));
+          mx.y = fmaxf(mx.y, __shfl_xor(mx.y, o));
+          mx.z = fmaxf(mx.z, __shfl_xor(mx.z, o));
+          mx.w = fmaxf(mx.w, __shfl_xor(mx.w, o));
+        }
+        if (lane == 0) hmax_s = mx;
+      }
       __syncthreads();
       cached_h = h;
     }
@@ -385,30 +401,41 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
     const int tile = t0 + half;
     const int tok = tile * kTile + (lane & 31);
-    if (tile < NT && tok < N) {
-      const uint32_t *st = stats + (int64_t)h * stat_stride + bslot;
-      const float cmax = __uint_as_float(st[0]), ecmax = __uint_as_float(st[1]);
-      const float ctmax = __uint_as_float(st[2]), nmax = __uint_as_float(st[3]);
+    const bool live = tile < NT && tok < N;
+    int kind = 0;  // 0 settled, 1 re-check, 2 full scan
+    int j1 = 0, j2 = 0;
+    if (live) {
+      const float4 hm = hmax_s;
       const float2 b = tb[(int64_t)h * NT * kTile + tok];
-      const int j1 = min((int)(__float_as_uint(m1) & 0xFFu), Cp - 1);
-      const int j2 = min((int)(__float_as_uint(m2) & 0xFFu), Cp - 1);
+      j1 = min((int)(__float_as_uint(m1) & 0xFFu), Cp - 1);
+      j2 = min((int)(__float_as_uint(m2) & 0xFFu), Cp - 1);
       const float4 B1 = cbnd_s[j1], B2 = cbnd_s[j2];
       const float e1 = key_bound(b.x, b.y, B1.x, B1.y, B1.z, B1.w, kappa);
       const float e2 = key_bound(b.x, b.y, B2.x, B2.y, B2.z, B2.w, kappa);
-      const float eg = key_bound(b.x, b.y, cmax, ecmax, ctmax, nmax, kappa);
+      const float eg = key_bound(b.x, b.y, hm.x, hm.y, hm.z, hm.w, kappa);
       const float g12 = (m1 - m2) * (1.0f - 0x1p-20f);
       const float g13 = (m1 - m3) * (1.0f - 0x1p-20f);
-      uint8_t *dst = assign + (int64_t)h * assign_hstride + tok;
       if (g12 > e1 + e2) {
-        *dst = (uint8_t)j1;
-      } else if (g13 > e1 + eg) {
-        const uint32_t pos = atomicAdd(counters + 0, 1u);
-        recheck[pos] = make_int4(h, tok, j1, j2);
+        assign[(int64_t)h * assign_hstride + tok] = (uint8_t)j1;
       } else {
-        const uint32_t pos = atomicAdd(counters + 1, 1u);
-        fallback[pos] = make_int2(h, tok);
+        kind = g13 > e1 + eg ? 1 : 2;
       }
     }
+    // list appends: one atomic per wave and list, slots from mbcnt
+    const uint64_t m_re = __ballot(kind == 1), m_fb = __ballot(kind == 2);
+    const uint32_t lt_re = __builtin_amdgcn_mbcnt_hi((uint32_t)(m_re >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m_re, 0u));
+    const uint32_t lt_fb = __builtin_amdgcn_mbcnt_hi((uint32_t)(m_fb >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m_fb, 0u));
+    uint32_t base_re = 0, base_fb = 0;
+    if (lane == 0) {
+      if (m_re) base_re = atomicAdd(counters + 0, (uint32_t)__popcll(m_re));
+      if (m_fb) base_fb = atomicAdd(counters + 1, (uint32_t)__popcll(m_fb));
+    }
+    base_re = __shfl(base_re, 0);
+    base_fb = __shfl(base_fb, 0);
+    if (kind == 1) recheck[base_re + lt_re] = make_int4(h, tok, j1, j2);
+    if (kind == 2) fallback[base_fb + lt_fb] = make_int2(h, tok);
   }
 }
 
@@ -498,13 +525,12 @@ __global__ __launch_bounds__(256) void k_recheck(const Tin *__restrict__ r, int 
 }
 
 // Exact scan over all centroids for the tokens the bound could not settle:
-// one wave per entry (grid-stride, so entries of any head spread over the
-// whole GPU), each lane owns centroids lane + 64m.  fp32 direct distances
-// (4 interleaved partial sums; within gamma_{D+2} of each distance in any
-// order) keep only the centroids that can still be the minimum; those get an
-// fp64 distance (4 partial sums), and any whose order against the best is not
-// settled by the margin get the sequential fp64 distance, the same arithmetic
-// as a plain loop.  Smallest distance wins, ties to the smallest index.
+// one workgroup per entry (grid-stride), thread j owns centroid j.  fp64
+// distances with 4 interleaved partial sums (within gamma_{D+4} of the exact
+// distance in any order) pick the best; any centroid whose order against the
+// best is not settled by that margin gets the sequential fp64 distance, the
+// same arithmetic as a plain loop.  Smallest distance wins, ties to the
+// smallest index.
 template <typename Tin, int D>
 __global__ __launch_bounds__(256) void k_fallback(const Tin *__restrict__ r, int N,
                                                   const float *__restrict__ cent, int C, int Cp,
@@ -512,84 +538,47 @@ __global__ __launch_bounds__(256) void k_fallback(const Tin *__restrict__ r, int
                                                   const uint32_t *__restrict__ counters,
                                                   uint8_t *__restrict__ assign,
                                                   int64_t assign_hstride) {
-  constexpr int D4 = D / 4;
-  constexpr float g32 = (float)(D + 2) * 0x1p-24f;
-  __shared__ float4 rsm[4][D4];
+  constexpr int D4 = D / 4, HB = D4 / 2;
+  __shared__ float4 rs[D4];
+  __shared__ double wbest[4];
+  __shared__ int wbj[4], wnear[4];
   const uint32_t n = counters[1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float4 *rs = rsm[wave];
-  const uint32_t nw = gridDim.x * (blockDim.x >> 6);
-  for (uint32_t e = blockIdx.x * (blockDim.x >> 6) + wave; e < n; e += nw) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const double tol = order_tol<D>();
+  for (uint32_t e = blockIdx.x; e < n; e += gridDim.x) {
     const int2 q = list[e];
     const Tin *row = r + ((int64_t)q.x * N + q.y) * D;
     const float *ch = cent + (int64_t)q.x * Cp * D;
-    if (lane < D4) {
+    if (t < D4) {
       float v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = Elem<Tin>::get(row, lane * 4 + u);
-      rs[lane] = make_float4(v[0], v[1], v[2], v[3]);
+      for (int u = 0; u < 4; ++u) v[u] = Elem<Tin>::get(row, t * 4 + u);
+      rs[t] = make_float4(v[0], v[1], v[2], v[3]);
     }
-    __threadfence_block();
-    __builtin_amdgcn_wave_barrier();
-    float d32[4];
-    float mloc = __builtin_inff();
-    {
-      float4 acc[4];
-      const float4 *cj[4];
+    __syncthreads();
+    const int j = min(t, C - 1);
+    const float4 *c4 = reinterpret_cast<const float4 *>(ch + (int64_t)j * D);
+    double p0 = 0.0, p1 = 0.0, p2 = 0.0, p3 = 0.0;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        acc[m] = make_float4(0.f, 0.f, 0.f, 0.f);
-        cj[m] = reinterpret_cast<const float4 *>(ch + (int64_t)min(lane + 64 * m, C - 1) * D);
-      }
-#pragma unroll 4
-      for (int k4 = 0; k4 < D4; ++k4) {
-        const float4 x = rs[k4];
+    for (int hb = 0; hb < 2; ++hb) {
+      float4 c[HB];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float4 c = cj[m][k4];
-          const float dx = x.x - c.x, dy = x.y - c.y, dz = x.z - c.z, dw = x.w - c.w;
-          acc[m].x = __fadd_rn(acc[m].x, __fmul_rn(dx, dx));
-          acc[m].y = __fadd_rn(acc[m].y, __fmul_rn(dy, dy));
-          acc[m].z = __fadd_rn(acc[m].z, __fmul_rn(dz, dz));
-          acc[m].w = __fadd_rn(acc[m].w, __fmul_rn(dw, dw));
-        }
-      }
+      for (int k = 0; k < HB; ++k) c[k] = c4[hb * HB + k];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float s = (acc[m].x + acc[m].y) + (acc[m].z + acc[m].w);
-        d32[m] = lane + 64 * m < C ? s : __builtin_inff();
-        mloc = fminf(mloc, d32[m]);
+      for (int k = 0; k < HB; ++k) {
+        const float4 x = rs[hb * HB + k];
+        const double dx = (double)x.x - (double)c[k].x, dy = (double)x.y - (double)c[k].y;
+        const double dz = (double)x.z - (double)c[k].z, dw = (double)x.w - (double)c[k].w;
+        p0 = __dadd_rn(p0, __dmul_rn(dx, dx));
+        p1 = __dadd_rn(p1, __dmul_rn(dy, dy));
+        p2 = __dadd_rn(p2, __dmul_rn(dz, dz));
+        p3 = __dadd_rn(p3, __dmul_rn(dw, dw));
       }
     }
-    for (int o = 32; o > 0; o >>= 1) mloc = fminf(mloc, __shfl_xor(mloc, o));
-    const float cut = mloc * (1.0f + 3.0f * g32) * (1.0f + 0x1p-20f) + 1e-37f;
-    double dp[4];
-    double best = __builtin_inf();
-    int bj = 0x7fffffff;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int j = lane + 64 * m;
-      dp[m] = __builtin_inf();
-      if (j < C && d32[m] <= cut) {
-        const float4 *c4 = reinterpret_cast<const float4 *>(ch + (int64_t)j * D);
-        double p0 = 0.0, p1 = 0.0, p2 = 0.0, p3 = 0.0;
-#pragma unroll 4
-        for (int k4 = 0; k4 < D4; ++k4) {
-          const float4 x = rs[k4], c = c4[k4];
-          const double dx = (double)x.x - (double)c.x, dy = (double)x.y - (double)c.y;
-          const double dz = (double)x.z - (double)c.z, dw = (double)x.w - (double)c.w;
-          p0 = __dadd_rn(p0, __dmul_rn(dx, dx));
-          p1 = __dadd_rn(p1, __dmul_rn(dy, dy));
-          p2 = __dadd_rn(p2, __dmul_rn(dz, dz));
-          p3 = __dadd_rn(p3, __dmul_rn(dw, dw));
-        }
-        dp[m] = (p0 + p1) + (p2 + p3);
-        if (dp[m] < best) {
-          best = dp[m];
-          bj = j;
-        }
-      }
-    }
+    const double dp = t < C ? (p0 + p1) + (p2 + p3) : __builtin_inf();
+    // workgroup argmin of (dp, j)
+    double best = dp;
+    int bj = t < C ? t : 0x7fffffff;
     for (int o = 32; o > 0; o >>= 1) {
       const double ob = __shfl_xor(best, o);
       const int oj = __shfl_xor(bj, o);
@@ -598,25 +587,28 @@ __global__ __launch_bounds__(256) void k_fallback(const Tin *__restrict__ r, int
         bj = oj;
       }
     }
-    const double tol = order_tol<D>();
-    bool near = false;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      near |= (lane + 64 * m != bj) && dp[m] - best <= tol * (dp[m] + best);
-    if (__ballot(near) != 0ull) {
-      double sb = __builtin_inf();
-      int sj = 0x7fffffff;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int j = lane + 64 * m;
-        if (j < C && (j == bj || dp[m] - best <= tol * (dp[m] + best))) {
-          const double d = exact_dist<Tin, D>(row, ch + (int64_t)j * D);
-          if (d < sb) {
-            sb = d;
-            sj = j;
-          }
-        }
+    if (lane == 0) {
+      wbest[wave] = best;
+      wbj[wave] = bj;
+    }
+    __syncthreads();
+    best = wbest[0];
+    bj = wbj[0];
+    for (int w = 1; w < 4; ++w)
+      if (wbest[w] < best || (wbest[w] == best && wbj[w] < bj)) {
+        best = wbest[w];
+        bj = wbj[w];
       }
+    // centroids whose order against the best is not settled by the margin
+    const bool near = t < C && t != bj && dp - best <= tol * (dp + best);
+    const uint64_t nb = __ballot(near);
+    if (lane == 0) wnear[wave] = nb != 0ull;
+    __syncthreads();
+    const bool any_near = wnear[0] | wnear[1] | wnear[2] | wnear[3];
+    if (any_near) {  // uniform over the workgroup
+      const bool mine = t < C && (t == bj || dp - best <= tol * (dp + best));
+      double sb = mine ? exact_dist<Tin, D>(row, ch + (int64_t)t * D) : __builtin_inf();
+      int sj = mine ? t : 0x7fffffff;
       for (int o = 32; o > 0; o >>= 1) {
         const double ob = __shfl_xor(sb, o);
         const int oj = __shfl_xor(sj, o);
@@ -625,11 +617,23 @@ __global__ __launch_bounds__(256) void k_fallback(const Tin *__restrict__ r, int
           sj = oj;
         }
       }
+      __syncthreads();
+      if (lane == 0) {
+        wbest[wave] = sb;
+        wbj[wave] = sj;
+      }
+      __syncthreads();
+      sb = wbest[0];
+      sj = wbj[0];
+      for (int w = 1; w < 4; ++w)
+        if (wbest[w] < sb || (wbest[w] == sb && wbj[w] < sj)) {
+          sb = wbest[w];
+          sj = wbj[w];
+        }
       bj = sj;
     }
-    if (lane == 0) assign[(int64_t)q.x * assign_hstride + q.y] = (uint8_t)bj;
-    __threadfence_block();
-    __builtin_amdgcn_wave_barrier();
+    if (t == 0) assign[(int64_t)q.x * assign_hstride + q.y] = (uint8_t)bj;
+    __syncthreads();
   }
 }
 
@@ -668,7 +672,9 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ass
                                                  int64_t assign_hstride, int N, int Cp,
                                                  const uint32_t *__restrict__ hist,
                                                  int32_t *__restrict__ sorted,
-                                                 int32_t *__restrict__ offs) {
+                                                 int32_t *__restrict__ offs,
+                                                 int32_t *__restrict__ cofs,
+                                                 int32_t *__restrict__ chunk_j, int maxch) {
   __shared__ uint32_t scan[kMaxC];
   __shared__ uint32_t wbase[4][kMaxC];
   const int h = blockIdx.y, b = blockIdx.x, nb = gridDim.x;
@@ -678,7 +684,18 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ass
   // this chunk's predecessors and all chunks, for byte value t
   const uint32_t *hh = hist + (int64_t)h * nb * kMaxC + t;
   uint32_t pre = 0, tot = 0;
-  for (int bb = 0; bb < nb; ++bb) {
+  int bb = 0;
+  for (; bb + 8 <= nb; bb += 8) {
+    uint32_t c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c[u] = hh[(int64_t)(bb + u) * kMaxC];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      tot += c[u];
+      pre += bb + u < b ? c[u] : 0u;
+    }
+  }
+  for (; bb < nb; ++bb) {
     const uint32_t c = hh[(int64_t)bb * kMaxC];
     tot += c;
     pre += bb < b ? c : 0u;
@@ -698,6 +715,23 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ass
   if (b == 0) {
     if (t <= Cp) offs[(int64_t)h * (Cp + 1) + t] = (int32_t)excl;
     if (Cp == kMaxC && t == kMaxC - 1) offs[(int64_t)h * (Cp + 1) + Cp] = (int32_t)mine;
+    // chunks of kAccChunk consecutive members per cluster: exclusive scan of
+    // the chunk counts of clusters 0..Cp-1, and the chunk -> cluster map
+    const uint32_t nch = t < Cp ? (tot + kAccChunk - 1) / kAccChunk : 0u;
+    __syncthreads();
+    uint32_t cm = nch;
+    scan[t] = cm;
+    __syncthreads();
+    for (int o = 1; o < kMaxC; o <<= 1) {
+      const uint32_t add = t >= o ? scan[t - o] : 0u;
+      __syncthreads();
+      scan[t] = cm = cm + add;
+      __syncthreads();
+    }
+    const uint32_t cex = cm - nch;
+    if (t <= Cp) cofs[(int64_t)h * (Cp + 1) + t] = (int32_t)cex;
+    if (Cp == kMaxC && t == kMaxC - 1) cofs[(int64_t)h * (Cp + 1) + Cp] = (int32_t)cm;
+    for (uint32_t q = 0; q < nch; ++q) chunk_j[(int64_t)h * maxch + cex + q] = t;
   }
   // per-wave counts inside the chunk (each wave owns a quarter, in order)
   for (int w = 0; w < 4; ++w) wbase[w][t] = 0;
@@ -735,20 +769,67 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ass
 }
 
 // ---------------------------------------------------------- accumulate
-// Wave per (head, cluster): c_j = fp32(sum of members in token order / n_j)
-// with fp64 sums; an empty cluster keeps its centroid.  Then emits the
-// centroid's tables for the next assign.  On the stage's last iteration it
-// also stores the record centroid (rounded to the record dtype) and the fp32
-// cache entry.
-template <typename Tin, typename Tc, int D>
-__global__ void k_accumulate(const Tin *__restrict__ r, int N, const int32_t *__restrict__ sorted,
-                             const int32_t *__restrict__ offs, int C, int Cp,
-                             float *__restrict__ cent, const uint32_t *stats, uint32_t *stats_w,
-                             int stat_stride, int bslot, half8 *__restrict__ ctab,
-                             float *__restrict__ cinit, float4 *__restrict__ cbnd,
-                             Tc *__restrict__ rec_c,
-                             int64_t rec_hstride, float *__restrict__ cache,
-                             int64_t cache_hstride) {
+// The members of each cluster (token order, from the counting sort) are cut
+// into chunks of kAccChunk.  k_chunk_sum: one wave per chunk sums its members'
+// rows in token order in fp64 (lanes over channels; all member rows in flight
+// at once).  k_finalize: one wave per cluster adds its chunk sums in chunk
+// order, divides in fp64 and rounds to fp32 (an empty cluster keeps its
+// centroid); this equals a single sequential fp64 sum whenever the fp64 sums
+// are exact, as they are for bf16 inputs.  It then emits the centroid's
+// tables for the next assign and, on the stage's last iteration, the record
+// centroid (rounded to the record dtype) and the fp32 cache entry.
+template <typename Tin, int D>
+__global__ __launch_bounds__(256) void k_chunk_sum(const Tin *__restrict__ r, int N, int Cp,
+                                                   const int32_t *__restrict__ sorted,
+                                                   const int32_t *__restrict__ offs,
+                                                   const int32_t *__restrict__ cofs,
+                                                   const int32_t *__restrict__ chunk_j,
+                                                   int maxch, double *__restrict__ part) {
+  constexpr int PER = D / 64, HB = kAccChunk / 2;
+  const int h = blockIdx.y;
+  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int total = __builtin_amdgcn_readfirstlane(cofs[(int64_t)h * (Cp + 1) + Cp]);
+  if (g >= total) return;
+  const int j = __builtin_amdgcn_readfirstlane(chunk_j[(int64_t)h * maxch + g]);
+  const int c0 = __builtin_amdgcn_readfirstlane(cofs[(int64_t)h * (Cp + 1) + j]);
+  const int o0 = __builtin_amdgcn_readfirstlane(offs[(int64_t)h * (Cp + 1) + j]);
+  const int o1 = __builtin_amdgcn_readfirstlane(offs[(int64_t)h * (Cp + 1) + j + 1]);
+  const int start = o0 + (g - c0) * kAccChunk;
+  const int cnt = min(kAccChunk, o1 - start);
+  const int32_t id = sorted[(int64_t)h * N + start + min(lane, cnt - 1)];
+  const Tin *rh = r + (int64_t)h * N * D + lane * PER;
+  double s[PER];
+#pragma unroll
+  for (int m = 0; m < PER; ++m) s[m] = 0.0;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    float v[HB][PER];
+#pragma unroll
+    for (int u = 0; u < HB; ++u) {
+      const int64_t row =
+          (int64_t)__builtin_amdgcn_readlane(id, min(half * HB + u, cnt - 1)) * D;
+#pragma unroll
+      for (int m = 0; m < PER; ++m) v[u][m] = Elem<Tin>::get(rh, row + m);
+    }
+#pragma unroll
+    for (int u = 0; u < HB; ++u)
+      if (half * HB + u < cnt)
+#pragma unroll
+        for (int m = 0; m < PER; ++m) s[m] = __dadd_rn(s[m], (double)v[u][m]);
+  }
+  double *dst = part + ((int64_t)h * maxch + g) * D + lane * PER;
+#pragma unroll
+  for (int m = 0; m < PER; ++m) dst[m] = s[m];
+}
+
+template <typename Tc, int D>
+__global__ __launch_bounds__(256) void k_finalize(
+    int C, int Cp, const int32_t *__restrict__ offs, const int32_t *__restrict__ cofs, int maxch,
+    const double *__restrict__ part, float *__restrict__ cent, const uint32_t *stats,
+    uint32_t *stats_w, int stat_stride, int bslot, half8 *__restrict__ ctab,
+    float *__restrict__ cinit, float4 *__restrict__ cbnd, Tc *__restrict__ rec_c,
+    int64_t rec_hstride, float *__restrict__ cache, int64_t cache_hstride) {
   constexpr int PER = D / 64;
   const int h = blockIdx.y;
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -758,52 +839,28 @@ __global__ void k_accumulate(const Tin *__restrict__ r, int N, const int32_t *__
     if (ctab) emit_pad<D>(h, j, Cp, ctab, cinit, cbnd);
     return;
   }
-  // cluster bounds are wave-uniform: keep them in scalar registers
-  const int32_t lo = __builtin_amdgcn_readfirstlane(offs[(int64_t)h * (Cp + 1) + j]);
-  const int32_t hi = __builtin_amdgcn_readfirstlane(offs[(int64_t)h * (Cp + 1) + j + 1]);
-  const int32_t *mem = sorted + (int64_t)h * N;
-  const Tin *rh = r + (int64_t)h * N * D + lane * PER;
+  const int n = __builtin_amdgcn_readfirstlane(offs[(int64_t)h * (Cp + 1) + j + 1] -
+                                               offs[(int64_t)h * (Cp + 1) + j]);
+  const int c0 = __builtin_amdgcn_readfirstlane(cofs[(int64_t)h * (Cp + 1) + j]);
+  const int nch = __builtin_amdgcn_readfirstlane(cofs[(int64_t)h * (Cp + 1) + j + 1]) - c0;
+  const double *ph = part + ((int64_t)h * maxch + c0) * D + lane * PER;
   double s[PER];
 #pragma unroll
   for (int m = 0; m < PER; ++m) s[m] = 0.0;
-  // Member ids are read 64 at a time (one per lane, the next 64 prefetched)
-  // and broadcast with readlane; member rows are loaded B at a time (indices
-  // past the end are clamped, their values unused), one batch ahead of the
-  // adds, which stay in token order.
-  constexpr int B = 16;
-  int32_t ids = mem[min(lo + lane, max(hi - 1, lo))];
-  for (int32_t base = lo; base < hi; base += 64) {
-    const int cnt = min(64, hi - base);
-    const int32_t next = mem[min(base + 64 + lane, max(hi - 1, lo))];
-    float va[B][PER], vb[B][PER];
-    auto load = [&](int u0, float (&v)[B][PER]) {
+  for (int q = 0; q < nch; q += 8) {
+    double v[8][PER];
 #pragma unroll
-      for (int u = 0; u < B; ++u) {
-        const int64_t row = (int64_t)__builtin_amdgcn_readlane(ids, min(u0 + u, cnt - 1)) * D;
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int m = 0; m < PER; ++m) v[u][m] = Elem<Tin>::get(rh, row + m);
-      }
-    };
-    auto add = [&](int u0, const float (&v)[B][PER]) {
+      for (int m = 0; m < PER; ++m) v[u][m] = ph[(int64_t)min(q + u, nch - 1) * D + m];
 #pragma unroll
-      for (int u = 0; u < B; ++u)
-        if (u0 + u < cnt)
+    for (int u = 0; u < 8; ++u)
+      if (q + u < nch)
 #pragma unroll
-          for (int m = 0; m < PER; ++m) s[m] = __dadd_rn(s[m], (double)v[u][m]);
-    };
-    load(0, va);
-    for (int u0 = 0; u0 < cnt; u0 += 2 * B) {
-      if (u0 + B < cnt) load(u0 + B, vb);
-      add(u0, va);
-      if (u0 + B >= cnt) break;
-      if (u0 + 2 * B < cnt) load(u0 + 2 * B, va);
-      add(u0 + B, vb);
-    }
-    ids = next;
+        for (int m = 0; m < PER; ++m) s[m] = __dadd_rn(s[m], v[u][m]);
   }
   float *cj = cent + ((int64_t)h * Cp + j) * D + lane * PER;
   float cv[PER];
-  const int32_t n = hi - lo;
 #pragma unroll
   for (int m = 0; m < PER; ++m) {
     cv[m] = n > 0 ? (float)(s[m] / (double)n) : cj[m];
@@ -918,7 +975,7 @@ bool launch_assign(const KmArgs &a, int bslot, hipStream_t s) {
   }
   {
     TimerScope ts_("kmeans_fallback", s);
-    hipLaunchKernelGGL((k_fallback<Tin, D>), dim3(512), dim3(256), 0, s, (const Tin *)a.r, a.N,
+    hipLaunchKernelGGL((k_fallback<Tin, D>), dim3(2048), dim3(256), 0, s, (const Tin *)a.r, a.N,
                        a.ws.cent, a.C, a.Cp, a.ws.fallback, a.ws.counters, a.assign,
                        a.assign_hstride);
     QVG_CHECK_LAUNCH();
@@ -936,16 +993,21 @@ bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int6
                        a.ws.hist, a.ws_stats, a.stat_stride, next_bslot, a.ws.counters, log_slot);
     QVG_CHECK_LAUNCH();
     hipLaunchKernelGGL(k_scatter, dim3(nb, a.H), dim3(256), 0, s, a.assign, a.assign_hstride,
-                       a.N, a.Cp, a.ws.hist, a.ws.sorted, a.ws.offs);
+                       a.N, a.Cp, a.ws.hist, a.ws.sorted, a.ws.offs, a.ws.cofs, a.ws.chunk_j,
+                       max_chunks(a.N, a.Cp));
     QVG_CHECK_LAUNCH();
   }
   {
-    dim3 gc((a.Cp + 3) / 4, a.H);
+    const int maxch = max_chunks(a.N, a.Cp);
     TimerScope ts_("kmeans_accumulate", s);
-    hipLaunchKernelGGL((k_accumulate<Tin, Tc, D>), gc, dim3(256), 0, s, (const Tin *)a.r, a.N,
-                       a.ws.sorted, a.ws.offs, a.C, a.Cp, a.ws.cent, a.ws_stats, a.ws_stats,
-                       a.stat_stride, next_bslot, tables ? a.ws.ctab : nullptr, a.ws.cinit,
-                       a.ws.cbnd, rec_c, rec_hstride, cache, cache_hstride);
+    hipLaunchKernelGGL((k_chunk_sum<Tin, D>), dim3((maxch + 3) / 4, a.H), dim3(256), 0, s,
+                       (const Tin *)a.r, a.N, a.Cp, a.ws.sorted, a.ws.offs, a.ws.cofs,
+                       a.ws.chunk_j, maxch, a.ws.part);
+    QVG_CHECK_LAUNCH();
+    hipLaunchKernelGGL((k_finalize<Tc, D>), dim3((a.Cp + 3) / 4, a.H), dim3(256), 0, s, a.C,
+                       a.Cp, a.ws.offs, a.ws.cofs, maxch, a.ws.part, a.ws.cent, a.ws_stats,
+                       a.ws_stats, a.stat_stride, next_bslot, tables ? a.ws.ctab : nullptr,
+                       a.ws.cinit, a.ws.cbnd, rec_c, rec_hstride, cache, cache_hstride);
     QVG_CHECK_LAUNCH();
   }
   return true;

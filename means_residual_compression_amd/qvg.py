@@ -83,7 +83,7 @@ def lib() -> ct.CDLL:
             "qvg_decompress": ([R, ct.c_int, i64, i64, i64, P, p, ct.c_int, p], ct.c_int),
             "qvg_assign_workspace_size": ([i64, i64, i64, i32], sz),
             "qvg_kmeans_assign": ([p, ct.c_int, i64, i64, i64, p, i32, p, p, sz, p], ct.c_int),
-            "qvg_update_workspace_size": ([i64, i64, i32], sz),
+            "qvg_update_workspace_size": ([i64, i64, i64, i32], sz),
             "qvg_kmeans_update": ([p, ct.c_int, i64, i64, i64, p, i32, p, p, sz, p], ct.c_int),
             "qvg_sas_subtract": ([p, ct.c_int, i64, i64, i64, p, p, ct.c_int, i32, p, p],
                                  ct.c_int),
@@ -230,7 +230,7 @@ def kmeans_update(r: torch.Tensor, assign: torch.Tensor, centroids: torch.Tensor
     _dev(r, "r")
     H, N, d = r.shape
     C = centroids.shape[1]
-    n = lib().qvg_update_workspace_size(H, N, C)
+    n = lib().qvg_update_workspace_size(H, N, d, C)
     ws = ws if ws is not None else alloc_workspace(max(n, 256), r.device)
     _check(lib().qvg_kmeans_update(r.data_ptr(), _dt(r), H, N, d, assign.data_ptr(), C,
                                    centroids.data_ptr(), ws.data_ptr(), ws.numel(), _stream()))
