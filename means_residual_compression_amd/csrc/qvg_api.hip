@@ -36,20 +36,18 @@ size_t up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 // Workspace layout shared by the size query and the carve-up.
 struct Layout {
-  size_t rbuf, rt, tb, cent, ctab, cinit, cbnd, stats, recheck, fallback, counters, sorted, offs, hist,
+  size_t rt, tb, cent, ctab, cinit, cbnd, stats, recheck, fallback, counters, sorted, offs, hist,
       cofs, chunk_j, part, idx;
   size_t total;
 };
 
-Layout make_layout(int64_t H, int64_t N, int64_t d, int64_t C, int64_t T, bool need_rbuf,
-                   bool need_idx) {
+Layout make_layout(int64_t H, int64_t N, int64_t d, int64_t C, int64_t T, bool need_idx) {
   const int64_t Cp = std::max<int64_t>(32, pad32((int)C));
   const int64_t NT = (N + kTile - 1) / kTile;
   const int64_t Ts = std::max<int64_t>(T, 1);
   Layout L{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = up(o + bytes); return at; };
-  L.rbuf = take(need_rbuf ? (size_t)(H * N * d * 4) : 0);
   L.rt = take((size_t)(H * NT * kTile * d * 2));
   L.tb = take((size_t)(H * NT * kTile * 8));
   L.cent = take((size_t)(H * Cp * d * 4));
@@ -74,7 +72,6 @@ Layout make_layout(int64_t H, int64_t N, int64_t d, int64_t C, int64_t T, bool n
 Ws carve(void *ws, const Layout &L) {
   char *b = (char *)ws;
   Ws w;
-  w.rbuf = (float *)(b + L.rbuf);
   w.rt = (half8 *)(b + L.rt);
   w.tb = (float2 *)(b + L.tb);
   w.cent = (float *)(b + L.cent);
@@ -141,12 +138,11 @@ qvg_status run_compress(const void *x, int64_t H, int64_t N, const qvg_params *p
   const int Cp = std::max(32, pad32(C));
   const int NT = (int)((N + kTile - 1) / kTile);
   const bool x_bf16 = std::is_same<Tin, uint16_t>::value;
-  const bool c_bf16 = std::is_same<Tc, uint16_t>::value;
   const int stat_stride = std::max(T, 1) * kStatWords;
   if (!launch_fill_u32(w.stats, (int64_t)H * stat_stride, s) || !launch_fill_u32(w.counters, kCounterWords, s))
     return hip_fail("fill");
   if (T == 0) {
-    if (!launch_quant(x, x_bf16, (int)H, (int)N, D, 1, nullptr, 0, nullptr, false, 0, p->bits,
+    if (!launch_quant(x, x_bf16, (int)H, (int)N, D, 1, nullptr, nullptr, 1, 0, p->bits,
                       p->group, out->codes, out->scales, s))
       return hip_fail("group_quant_pack");
     return QVG_OK;
@@ -155,9 +151,12 @@ qvg_status run_compress(const void *x, int64_t H, int64_t N, const qvg_params *p
     return hip_fail("absmax");
   const int64_t rec_hstride = (int64_t)T * C * D;
   for (int t = 0; t < T; ++t) {
+    if (t > 0 && !launch_stage_bound(w.stats + (int64_t)(t - 1) * kStatWords, stat_stride,
+                                     (int)H, s))
+      return hip_fail("stage bound");
     KmArgs a;
     a.H = (int)H; a.N = (int)N; a.C = C; a.Cp = Cp; a.NT = NT;
-    a.r = t == 0 ? x : (const void *)w.rbuf;
+    a.x = x; a.rec_pi = out->assign; a.rec_cent = out->centroids; a.Ts = T; a.nsub = t;
     a.idx = use_idx ? w.idx + (int64_t)t * C : nullptr;
     a.idx_hstride = (int64_t)T * C;
     a.init = use_idx ? nullptr : init_c + (int64_t)t * C * D;
@@ -168,7 +167,7 @@ qvg_status run_compress(const void *x, int64_t H, int64_t N, const qvg_params *p
     a.ws_stats = w.stats + (int64_t)t * kStatWords;
     a.stat_stride = stat_stride;
     a.kappa = kappa_for(D);
-    const bool in_bf16 = t == 0 && x_bf16;
+    const bool in_bf16 = x_bf16;
     bool ok = in_bf16 ? launch_kmeans_stage_begin<uint16_t, D>(a, s)
                       : launch_kmeans_stage_begin<float, D>(a, s);
     if (!ok) return hip_fail("k-means stage init");
@@ -188,17 +187,11 @@ qvg_status run_compress(const void *x, int64_t H, int64_t N, const qvg_params *p
                                                  rec_hstride, log_slot, s);
       if (!ok) return hip_fail("kmeans_update");
     }
-    if (t < T - 1) {
-      uint32_t *next_stats = w.stats + (int64_t)(t + 1) * kStatWords;
-      if (!launch_subtract(a.r, in_bf16, (int)H, (int)N, D, C, a.assign, a.assign_hstride, rec_c,
-                           c_bf16, rec_hstride, w.rbuf, next_stats, stat_stride, S_MAXR, s))
-        return hip_fail("sas_subtract");
-    } else {
-      if (!launch_quant(a.r, in_bf16, (int)H, (int)N, D, C, a.assign, a.assign_hstride, rec_c,
-                        c_bf16, rec_hstride, p->bits, p->group, out->codes, out->scales, s))
-        return hip_fail("group_quant_pack");
-    }
   }
+  // R(T), recomputed from x and the record, quantized and packed
+  if (!launch_quant(x, x_bf16, (int)H, (int)N, D, C, out->assign, out->centroids, T, T,
+                    p->bits, p->group, out->codes, out->scales, s))
+    return hip_fail("group_quant_pack");
   return QVG_OK;
 }
 
@@ -217,7 +210,7 @@ qvg_status compress_impl(const void *x, qvg_dtype dtype, int64_t H, int64_t N, i
       return fail(QVG_ERR_INVALID_ARG, "exactly one of init_idx and init_centroids must be given");
   }
   const bool use_idx = p->T > 0 && init_idx != nullptr;
-  const Layout L = make_layout(H, N, d, p->C, p->T, p->T >= 2, use_idx);
+  const Layout L = make_layout(H, N, d, p->C, p->T, use_idx);
   if (!ws) return fail(QVG_ERR_WORKSPACE, "workspace is NULL");
   if (ws_bytes < L.total)
     return fail(QVG_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, L.total);
@@ -261,7 +254,7 @@ const char *qvg_last_error(void) { return g_err; }
 
 size_t qvg_workspace_size(int64_t H, int64_t N, int64_t d, qvg_dtype dtype, const qvg_params *p) {
   if (check_params(H, N, d, dtype, p, p ? std::max(p->iters, 1) : 1) != QVG_OK) return 0;
-  return make_layout(H, N, d, p->C, p->T, p->T >= 2, p->T > 0).total;
+  return make_layout(H, N, d, p->C, p->T, p->T > 0).total;
 }
 
 qvg_status qvg_compress(const void *x, qvg_dtype dtype, int64_t H, int64_t N, int64_t d,
@@ -316,7 +309,7 @@ qvg_status qvg_candidate_counts(const void *ws, int64_t H, int64_t N, int64_t d,
   if (st != QVG_OK) return st;
   if (!ws || !out || n_iters < 0 || n_iters > kCounterLog)
     return fail(QVG_ERR_INVALID_ARG, "ws/out NULL or n_iters outside [0, %d]", kCounterLog);
-  const Layout L = make_layout(H, N, d, p->C, p->T, p->T >= 2, p->T > 0);
+  const Layout L = make_layout(H, N, d, p->C, p->T, p->T > 0);
   if (hipMemcpy(out, (const char *)ws + L.counters + 16, (size_t)n_iters * 8,
                 hipMemcpyDeviceToHost) != hipSuccess)
     return hip_fail("read candidate counts");
@@ -325,7 +318,7 @@ qvg_status qvg_candidate_counts(const void *ws, int64_t H, int64_t N, int64_t d,
 
 size_t qvg_assign_workspace_size(int64_t H, int64_t N, int64_t d, int32_t C) {
   if (check_dims(H, N, d, QVG_F32) != QVG_OK || C < 1 || C > kMaxC || C > N) return 0;
-  return make_layout(H, N, d, C, 1, false, false).total;
+  return make_layout(H, N, d, C, 1, false).total;
 }
 
 qvg_status qvg_kmeans_assign(const void *r, qvg_dtype dtype, int64_t H, int64_t N, int64_t d,
@@ -336,7 +329,7 @@ qvg_status qvg_kmeans_assign(const void *r, qvg_dtype dtype, int64_t H, int64_t 
   if (st != QVG_OK) return st;
   if (C < 1 || C > kMaxC || C > N) return fail(QVG_ERR_UNSUPPORTED, "C=%d must be in [1, min(256, N)]", C);
   if (!r || !centroids || !assign) return fail(QVG_ERR_INVALID_ARG, "NULL pointer argument");
-  const Layout L = make_layout(H, N, d, C, 1, false, false);
+  const Layout L = make_layout(H, N, d, C, 1, false);
   if (!ws || ws_bytes < L.total) return fail(QVG_ERR_WORKSPACE, "workspace smaller than %zu bytes", L.total);
   if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(QVG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   const Ws w = carve(ws, L);
@@ -344,7 +337,8 @@ qvg_status qvg_kmeans_assign(const void *r, qvg_dtype dtype, int64_t H, int64_t 
   KmArgs a;
   a.H = (int)H; a.N = (int)N; a.C = C; a.Cp = std::max(32, pad32(C));
   a.NT = (int)((N + kTile - 1) / kTile);
-  a.r = r; a.idx = nullptr; a.idx_hstride = 0; a.init = centroids; a.init_hstride = (int64_t)C * d;
+  a.x = r; a.rec_pi = nullptr; a.rec_cent = nullptr; a.Ts = 1; a.nsub = 0;
+  a.idx = nullptr; a.idx_hstride = 0; a.init = centroids; a.init_hstride = (int64_t)C * d;
   a.assign = assign; a.assign_hstride = N; a.ws = w; a.ws_stats = w.stats;
   a.stat_stride = kStatWords; a.kappa = kappa_for(d);
   if (!launch_fill_u32(w.stats, H * kStatWords, s) || !launch_fill_u32(w.counters, kCounterWords, s)) return hip_fail("fill");
@@ -401,7 +395,8 @@ qvg_status qvg_kmeans_update(const void *r, qvg_dtype dtype, int64_t H, int64_t 
   w.cent = centroids;
   KmArgs a;
   a.H = (int)H; a.N = (int)N; a.C = C; a.Cp = C; a.NT = 0;
-  a.r = r; a.idx = nullptr; a.idx_hstride = 0; a.init = nullptr; a.init_hstride = 0;
+  a.x = r; a.rec_pi = nullptr; a.rec_cent = nullptr; a.Ts = 1; a.nsub = 0;
+  a.idx = nullptr; a.idx_hstride = 0; a.init = nullptr; a.init_hstride = 0;
   a.assign = (uint8_t *)assign; a.assign_hstride = N; a.ws = w; a.ws_stats = w.stats;
   a.stat_stride = kStatWords; a.kappa = 0.0f;
   hipStream_t s = (hipStream_t)stream;
@@ -440,7 +435,7 @@ qvg_status qvg_group_quant_pack(const void *r, qvg_dtype dtype, int64_t H, int64
   st = check_quant(d, bits, group);
   if (st != QVG_OK) return st;
   if (!r || !codes || !scales) return fail(QVG_ERR_INVALID_ARG, "NULL pointer argument");
-  if (!launch_quant(r, dtype == QVG_BF16, (int)H, (int)N, (int)d, 1, nullptr, 0, nullptr, false, 0,
+  if (!launch_quant(r, dtype == QVG_BF16, (int)H, (int)N, (int)d, 1, nullptr, nullptr, 1, 0,
                     bits, group, codes, scales, (hipStream_t)stream))
     return hip_fail("group_quant_pack");
   return QVG_OK;

@@ -32,7 +32,6 @@ enum StatSlot : int {
 
 // Device scratch carved from the caller's workspace.
 struct Ws {
-  float *rbuf;        // fp32 [H][N][d]   residual R(t) between stages
   half8 *rt;          // fp16 fragments [H][NT][KC][64] of the scaled residual
   float2 *tb;         // [H][NT*32]        per-token (||r~||, ||r*sc - r~||) bounds
   float *cent;        // fp32 [H][Cp][d]   working centroids
@@ -112,6 +111,73 @@ __device__ __forceinline__ void store8(uint16_t *p, int64_t i, const float v[8])
   a.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
   a.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
   *reinterpret_cast<uint4 *>(p + i) = a;
+}
+
+// ------------------------------------------------------- stage residuals
+// The input residual of stage t, recomputed on the fly from the stage-0
+// input X and the record:  R(t) = X - C(1)[pi(1)] - ... - C(t)[pi(t)], one fp32
+// subtraction per stage in stage order (the same arithmetic as subtracting
+// stage by stage).  nsub = t; pi and cent are the record's assignments
+// [H][Ts][N] and centroids [H][Ts][C][D] (rounded to the record dtype T).
+template <typename T>
+struct ResView {
+  const T *x;
+  const uint8_t *pi;
+  const T *cent;
+  int N, D, C, Ts, nsub;
+
+  __device__ __forceinline__ int stage_j(int h, int s, int64_t i) const {
+    return min((int)pi[((int64_t)h * Ts + s) * N + i], C - 1);
+  }
+  __device__ __forceinline__ const T *stage_row(int h, int s, int j) const {
+    return cent + (((int64_t)h * Ts + s) * C + j) * D;
+  }
+  __device__ __forceinline__ float get(int h, int64_t i, int k) const {
+    float v = Elem<T>::get(x, ((int64_t)h * N + i) * D + k);
+    for (int s = 0; s < nsub; ++s) v = v - Elem<T>::get(stage_row(h, s, stage_j(h, s, i)), k);
+    return v;
+  }
+  __device__ __forceinline__ void load8(int h, int64_t i, int k0, float v[8]) const {
+    ::qvg::load8(x, ((int64_t)h * N + i) * D + k0, v);
+    for (int s = 0; s < nsub; ++s) {
+      float c[8];
+      ::qvg::load8(stage_row(h, s, stage_j(h, s, i)), k0, c);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) v[m] = v[m] - c[m];
+    }
+  }
+  // Same with the stage count fixed at compile time (branch-free, so the
+  // loads of all stages are issued together).
+  template <int NSUB>
+  __device__ __forceinline__ void load8_n(int h, int64_t i, int k0, float v[8]) const {
+    int js[NSUB > 0 ? NSUB : 1];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) js[s] = stage_j(h, s, i);
+    float c[NSUB > 0 ? NSUB : 1][8];
+    ::qvg::load8(x, ((int64_t)h * N + i) * D + k0, v);
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) ::qvg::load8(stage_row(h, s, js[s]), k0, c[s]);
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) v[m] = v[m] - c[s][m];
+  }
+};
+
+// Calls F.template operator()<NS>() with NS = n (0..8) as a compile-time value.
+template <typename F>
+inline void dispatch_nsub(int n, F &&f) {
+  switch (n) {
+    case 0: f.template operator()<0>(); break;
+    case 1: f.template operator()<1>(); break;
+    case 2: f.template operator()<2>(); break;
+    case 3: f.template operator()<3>(); break;
+    case 4: f.template operator()<4>(); break;
+    case 5: f.template operator()<5>(); break;
+    case 6: f.template operator()<6>(); break;
+    case 7: f.template operator()<7>(); break;
+    default: f.template operator()<8>(); break;
+  }
 }
 
 // -------------------------------------------------------------- FP8 E4M3

@@ -26,7 +26,13 @@ class TimerScope {
 // [H][N][D] (bf16 X at the first stage, fp32 afterwards).
 struct KmArgs {
   int H, N, C, Cp, NT;
-  const void *r;
+  // stage input residual R(t) = x - C(1)[pi(1)] - ... - C(t)[pi(t)] (see
+  // ResView): x [H][N][D] in the record dtype, record assignments and
+  // centroids with Ts stages, nsub = t
+  const void *x;
+  const uint8_t *rec_pi;
+  const void *rec_cent;
+  int Ts, nsub;
   const int32_t *idx;  // device [H][..][C] init rows, or nullptr
   int64_t idx_hstride;
   const float *init;   // device [H][..][C][D] init centroids, or nullptr
@@ -39,6 +45,7 @@ struct KmArgs {
   float kappa;         // relative error coefficient of the MFMA keys
 };
 
+bool launch_stage_bound(uint32_t *prev_stats, int stat_stride, int H, hipStream_t s);
 template <typename Tin>
 bool launch_absmax(const void *x, int H, int64_t per_head, uint32_t *stats, int stat_stride,
                    int slot, hipStream_t s);
@@ -57,11 +64,13 @@ bool launch_fill_u32(uint32_t *p, int64_t n, hipStream_t s);
 bool launch_subtract(const void *r, bool r_bf16, int H, int N, int D, int C, const uint8_t *assign,
                      int64_t assign_hstride, const void *chat, bool c_bf16, int64_t chat_hstride,
                      float *r_out, uint32_t *stats, int stat_stride, int slot, hipStream_t s);
-// codes/scales of (r - chat[assign]) or of r when assign is null.  Assignment
-// bytes >= C are clamped to C-1 in every kernel that gathers centroids.
-bool launch_quant(const void *r, bool r_bf16, int H, int N, int D, int C, const uint8_t *assign,
-                  int64_t assign_hstride, const void *chat, bool c_bf16, int64_t chat_hstride,
-                  int bits, int G, uint8_t *codes, uint8_t *scales, hipStream_t s);
+// codes/scales of the residual x - C(1)[pi(1)] - ... - C(nsub)[pi(nsub)]
+// (record assignments [H][Ts][N], centroids [H][Ts][C][D] in x's dtype).
+// Assignment bytes >= C are clamped to C-1 in every kernel that gathers
+// centroids.
+bool launch_quant(const void *x, bool bf16, int H, int N, int D, int C, const uint8_t *pi,
+                  const void *cent, int Ts, int nsub, int bits, int G, uint8_t *codes,
+                  uint8_t *scales, hipStream_t s);
 bool launch_dequant(const uint8_t *codes, const uint8_t *scales, const uint8_t *assign,
                     const void *cent, bool c_bf16, int H, int N, int D, int C, int T, int bits,
                     int G, void *out, bool out_bf16, hipStream_t s);

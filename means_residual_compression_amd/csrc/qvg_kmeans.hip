@@ -82,12 +82,25 @@ __global__ void k_absmax(const Tin *__restrict__ x, int64_t per_head, uint32_t *
   if (threadIdx.x == 0) atomic_max_pos(stats + (int64_t)h * stat_stride + slot, m);
 }
 
+// --------------------------------------------------------- stage bound
+// Scale bound for stage t >= 1: R(t) = R(t-1) - C^[pi] with |C^| at most the
+// larger of max|R(t-1)| and max|init centroids| (a centroid is a mean of rows
+// or an untouched initial value) times bf16 rounding, so
+// max|R(t)| <= (max|R(t-1)| + max(max|R(t-1)|, max|C0(t-1)|)) * (1 + 2^-7).
+__global__ void k_stage_bound(uint32_t *stats, int stat_stride, int H) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  uint32_t *st = stats + (int64_t)h * stat_stride;
+  const float r = __uint_as_float(st[S_MAXR]), c = __uint_as_float(st[S_MAXC]);
+  st[kStatWords + S_MAXR] = __float_as_uint((r + fmaxf(r, c)) * (1.0f + 0x1p-7f));
+}
+
 // --------------------------------------------------------------- init
 // Wave per (head, centroid): cent[h][j] = R[h][idx[h][j]] (gather) or
 // init[h][j] (copy); stats max |c| into S_MAXC.  Padded centroids j >= C
 // are zeroed.
 template <typename Tin, int D>
-__global__ void k_init(const Tin *__restrict__ r, int N, const int32_t *__restrict__ idx,
+__global__ void k_init(ResView<Tin> rv, const int32_t *__restrict__ idx,
                        int64_t idx_hstride, const float *__restrict__ init,
                        int64_t init_hstride, int C, int Cp, float *__restrict__ cent,
                        uint32_t *stats, int stat_stride) {
@@ -102,7 +115,7 @@ __global__ void k_init(const Tin *__restrict__ r, int N, const int32_t *__restri
     if (j < C) {
       if (idx) {
         const int64_t row = idx[(int64_t)h * idx_hstride + j];
-        v = Elem<Tin>::get(r, ((int64_t)h * N + row) * D + k);
+        v = rv.get(h, row, k);
       } else {
         v = init[(int64_t)h * init_hstride + (int64_t)j * D + k];
       }
@@ -120,9 +133,10 @@ __global__ void k_init(const Tin *__restrict__ r, int N, const int32_t *__restri
 // channels, so a token row is read contiguously.
 // Fragment layout: [h][tile][kc][lane][8]; lane l holds token tile*32 + l%32
 // and channels kc*16 + 8*(l/32) + 0..7.
-template <typename Tin, int D>
-__global__ void k_prepare(const Tin *__restrict__ r, int N, int NT, const uint32_t *stats,
-                          int stat_stride, half8 *__restrict__ rt, float2 *__restrict__ tb) {
+template <typename Tin, int D, int NSUB>
+__global__ void k_prepare(ResView<Tin> rv, int NT, const uint32_t *stats, int stat_stride,
+                          half8 *__restrict__ rt, float2 *__restrict__ tb) {
+  const int N = rv.N;
   constexpr int KC = D / 16, LPT = D / 8;
   const int h = blockIdx.y;
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -132,7 +146,7 @@ __global__ void k_prepare(const Tin *__restrict__ r, int N, int NT, const uint32
   const float sc = head_scale<Tin>(stats + (int64_t)h * stat_stride);
   float v[8];
   if (live && i < N) {
-    load8(r, ((int64_t)h * N + i) * D + q * 8, v);
+    rv.template load8_n<NSUB>(h, i, q * 8, v);
   } else {
 #pragma unroll
     for (int m = 0; m < 8; ++m) v[m] = 0.0f;
@@ -443,13 +457,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 // Exact fp64 squared distance, channel order, no fused multiply-add: the same
 // arithmetic as a plain sequential loop.
 template <typename Tin, int D>
-__device__ __attribute__((noinline)) double exact_dist(const Tin *__restrict__ row,
+__device__ __attribute__((noinline)) double exact_dist(const ResView<Tin> &rv, int h, int64_t i,
                                                        const float *__restrict__ c) {
   double acc = 0.0;
 #pragma unroll 1
   for (int k = 0; k < D; k += 8) {
     float v[8], w[8];
-    load8(row, k, v);
+    rv.load8(h, i, k, v);
     load8(c, k, w);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -473,7 +487,7 @@ __device__ __forceinline__ double order_tol() {
 // fp64 partial sums combined by a fixed butterfly; the sequential fp64 replica
 // decides only when the margin is too thin to settle the order.
 template <typename Tin, int D>
-__global__ __launch_bounds__(256) void k_recheck(const Tin *__restrict__ r, int N, const float *__restrict__ cent,
+__global__ __launch_bounds__(256) void k_recheck(ResView<Tin> rv, const float *__restrict__ cent,
                           int Cp, const int4 *__restrict__ list,
                           const uint32_t *__restrict__ counters, uint8_t *__restrict__ assign,
                           int64_t assign_hstride) {
@@ -486,12 +500,11 @@ __global__ __launch_bounds__(256) void k_recheck(const Tin *__restrict__ r, int 
     const uint32_t e = base + sub;
     const bool live = e < n;
     const int4 q = live ? list[e] : make_int4(0, 0, 0, 0);
-    const Tin *row = r + ((int64_t)q.x * N + q.y) * D;
     const float *cb = cent + (int64_t)q.x * Cp * D;
     double s1 = 0.0, s2 = 0.0;
     if (live) {
       float v[8], w1[8], w2[8];
-      load8(row, li * 8, v);
+      rv.load8(q.x, q.y, li * 8, v);
       load8(cb + (int64_t)q.z * D, li * 8, w1);
       load8(cb + (int64_t)q.w * D, li * 8, w2);
 #pragma unroll
@@ -515,8 +528,8 @@ __global__ __launch_bounds__(256) void k_recheck(const Tin *__restrict__ r, int 
       } else if (diff < -tol) {
         j = q.w;
       } else {
-        const double d1 = exact_dist<Tin, D>(row, cb + (int64_t)q.z * D);
-        const double d2 = exact_dist<Tin, D>(row, cb + (int64_t)q.w * D);
+        const double d1 = exact_dist<Tin, D>(rv, q.x, q.y, cb + (int64_t)q.z * D);
+        const double d2 = exact_dist<Tin, D>(rv, q.x, q.y, cb + (int64_t)q.w * D);
         j = (d2 < d1 || (d2 == d1 && q.w < q.z)) ? q.w : q.z;
       }
       assign[(int64_t)q.x * assign_hstride + q.y] = (uint8_t)j;
@@ -532,7 +545,7 @@ __global__ __launch_bounds__(256) void k_recheck(const Tin *__restrict__ r, int 
 // same arithmetic as a plain loop.  Smallest distance wins, ties to the
 // smallest index.
 template <typename Tin, int D>
-__global__ __launch_bounds__(256) void k_fallback(const Tin *__restrict__ r, int N,
+__global__ __launch_bounds__(256) void k_fallback(ResView<Tin> rv,
                                                   const float *__restrict__ cent, int C, int Cp,
                                                   const int2 *__restrict__ list,
                                                   const uint32_t *__restrict__ counters,
@@ -547,12 +560,11 @@ __global__ __launch_bounds__(256) void k_fallback(const Tin *__restrict__ r, int
   const double tol = order_tol<D>();
   for (uint32_t e = blockIdx.x; e < n; e += gridDim.x) {
     const int2 q = list[e];
-    const Tin *row = r + ((int64_t)q.x * N + q.y) * D;
     const float *ch = cent + (int64_t)q.x * Cp * D;
     if (t < D4) {
       float v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = Elem<Tin>::get(row, t * 4 + u);
+      for (int u = 0; u < 4; ++u) v[u] = rv.get(q.x, q.y, t * 4 + u);
       rs[t] = make_float4(v[0], v[1], v[2], v[3]);
     }
     __syncthreads();
@@ -607,7 +619,7 @@ __global__ __launch_bounds__(256) void k_fallback(const Tin *__restrict__ r, int
     const bool any_near = wnear[0] | wnear[1] | wnear[2] | wnear[3];
     if (any_near) {  // uniform over the workgroup
       const bool mine = t < C && (t == bj || dp - best <= tol * (dp + best));
-      double sb = mine ? exact_dist<Tin, D>(row, ch + (int64_t)t * D) : __builtin_inf();
+      double sb = mine ? exact_dist<Tin, D>(rv, q.x, q.y, ch + (int64_t)t * D) : __builtin_inf();
       int sj = mine ? t : 0x7fffffff;
       for (int o = 32; o > 0; o >>= 1) {
         const double ob = __shfl_xor(sb, o);
@@ -778,8 +790,8 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ass
 // are exact, as they are for bf16 inputs.  It then emits the centroid's
 // tables for the next assign and, on the stage's last iteration, the record
 // centroid (rounded to the record dtype) and the fp32 cache entry.
-template <typename Tin, int D>
-__global__ __launch_bounds__(256) void k_chunk_sum(const Tin *__restrict__ r, int N, int Cp,
+template <typename Tin, int D, int NSUB>
+__global__ __launch_bounds__(256) void k_chunk_sum(ResView<Tin> rv, int Cp,
                                                    const int32_t *__restrict__ sorted,
                                                    const int32_t *__restrict__ offs,
                                                    const int32_t *__restrict__ cofs,
@@ -797,8 +809,15 @@ __global__ __launch_bounds__(256) void k_chunk_sum(const Tin *__restrict__ r, in
   const int o1 = __builtin_amdgcn_readfirstlane(offs[(int64_t)h * (Cp + 1) + j + 1]);
   const int start = o0 + (g - c0) * kAccChunk;
   const int cnt = min(kAccChunk, o1 - start);
+  const int N = rv.N;
+  // lane u holds member u's token id and its cluster in every earlier stage
+  // (NSUB = the stage index, a template parameter so the member loop below
+  // has no branches and all its loads are issued back to back)
   const int32_t id = sorted[(int64_t)h * N + start + min(lane, cnt - 1)];
-  const Tin *rh = r + (int64_t)h * N * D + lane * PER;
+  int pj[NSUB > 0 ? NSUB : 1];
+#pragma unroll
+  for (int st = 0; st < NSUB; ++st) pj[st] = rv.stage_j(h, st, id);
+  const Tin *xh = rv.x + (int64_t)h * N * D + lane * PER;
   double s[PER];
 #pragma unroll
   for (int m = 0; m < PER; ++m) s[m] = 0.0;
@@ -807,10 +826,16 @@ __global__ __launch_bounds__(256) void k_chunk_sum(const Tin *__restrict__ r, in
     float v[HB][PER];
 #pragma unroll
     for (int u = 0; u < HB; ++u) {
-      const int64_t row =
-          (int64_t)__builtin_amdgcn_readlane(id, min(half * HB + u, cnt - 1)) * D;
+      const int src = min(half * HB + u, cnt - 1);
+      const int64_t row = __builtin_amdgcn_readlane(id, src);
 #pragma unroll
-      for (int m = 0; m < PER; ++m) v[u][m] = Elem<Tin>::get(rh, row + m);
+      for (int m = 0; m < PER; ++m) v[u][m] = Elem<Tin>::get(xh, row * D + m);
+#pragma unroll
+      for (int st = 0; st < NSUB; ++st) {  // R(t) = x - C(1)[pi(1)] - ... in stage order
+        const Tin *c = rv.stage_row(h, st, __builtin_amdgcn_readlane(pj[st], src)) + lane * PER;
+#pragma unroll
+        for (int m = 0; m < PER; ++m) v[u][m] = v[u][m] - Elem<Tin>::get(c, m);
+      }
     }
 #pragma unroll
     for (int u = 0; u < HB; ++u)
@@ -906,6 +931,14 @@ bool allow_lds(const void *fn, size_t bytes) {
 }
 }  // namespace
 
+bool launch_stage_bound(uint32_t *prev_stats, int stat_stride, int H, hipStream_t s) {
+  TimerScope ts_("kmeans_init", s);
+  hipLaunchKernelGGL(k_stage_bound, dim3((H + 63) / 64), dim3(64), 0, s, prev_stats,
+                     stat_stride, H);
+  QVG_CHECK_LAUNCH();
+  return true;
+}
+
 template <typename Tin>
 bool launch_absmax(const void *x, int H, int64_t per_head, uint32_t *stats, int stat_stride,
                    int slot, hipStream_t s) {
@@ -918,12 +951,27 @@ bool launch_absmax(const void *x, int H, int64_t per_head, uint32_t *stats, int 
   return true;
 }
 
+template <typename T>
+ResView<T> view_of(const KmArgs &a, int D) {
+  ResView<T> v;
+  v.x = (const T *)a.x;
+  v.pi = a.rec_pi;
+  v.cent = (const T *)a.rec_cent;
+  v.N = a.N;
+  v.D = D;
+  v.C = a.C;
+  v.Ts = a.Ts;
+  v.nsub = a.nsub;
+  return v;
+}
+
 template <typename Tin, int D>
 bool launch_kmeans_stage_begin(const KmArgs &a, hipStream_t s) {
+  const ResView<Tin> rv = view_of<Tin>(a, D);
   dim3 gc((a.Cp + 3) / 4, a.H);
   {
     TimerScope ts_("kmeans_init", s);
-    hipLaunchKernelGGL((k_init<Tin, D>), gc, dim3(256), 0, s, (const Tin *)a.r, a.N, a.idx,
+    hipLaunchKernelGGL((k_init<Tin, D>), gc, dim3(256), 0, s, rv, a.idx,
                        a.idx_hstride, a.init, a.init_hstride, a.C, a.Cp, a.ws.cent, a.ws_stats,
                        a.stat_stride);
     QVG_CHECK_LAUNCH();
@@ -932,8 +980,10 @@ bool launch_kmeans_stage_begin(const KmArgs &a, hipStream_t s) {
     const int64_t threads = (int64_t)a.NT * kTile * (D / 8);
     dim3 gp((unsigned)((threads + 255) / 256), a.H);
     TimerScope ts_("kmeans_prepare", s);
-    hipLaunchKernelGGL((k_prepare<Tin, D>), gp, dim3(256), 0, s, (const Tin *)a.r, a.N, a.NT,
-                       a.ws_stats, a.stat_stride, a.ws.rt, a.ws.tb);
+    dispatch_nsub(a.nsub, [&]<int NS>() {
+      hipLaunchKernelGGL((k_prepare<Tin, D, NS>), gp, dim3(256), 0, s, rv, a.NT, a.ws_stats,
+                         a.stat_stride, a.ws.rt, a.ws.tb);
+    });
     QVG_CHECK_LAUNCH();
   }
   {
@@ -947,6 +997,7 @@ bool launch_kmeans_stage_begin(const KmArgs &a, hipStream_t s) {
 
 template <typename Tin, int D>
 bool launch_assign(const KmArgs &a, int bslot, hipStream_t s) {
+  const ResView<Tin> rv = view_of<Tin>(a, D);
   constexpr int KC = D / 16, TPG = 16;
   const int CB = a.Cp / kTile;
   const size_t lds = (size_t)CB * KC * 64 * sizeof(half8) + (size_t)CB * 32 * sizeof(float) +
@@ -968,16 +1019,14 @@ bool launch_assign(const KmArgs &a, int bslot, hipStream_t s) {
   }
   {
     TimerScope ts_("kmeans_recheck", s);
-    hipLaunchKernelGGL((k_recheck<Tin, D>), dim3(1024), dim3(256), 0, s, (const Tin *)a.r, a.N,
-                       a.ws.cent, a.Cp, a.ws.recheck, a.ws.counters, a.assign,
-                       a.assign_hstride);
+    hipLaunchKernelGGL((k_recheck<Tin, D>), dim3(1024), dim3(256), 0, s, rv, a.ws.cent, a.Cp,
+                       a.ws.recheck, a.ws.counters, a.assign, a.assign_hstride);
     QVG_CHECK_LAUNCH();
   }
   {
     TimerScope ts_("kmeans_fallback", s);
-    hipLaunchKernelGGL((k_fallback<Tin, D>), dim3(2048), dim3(256), 0, s, (const Tin *)a.r, a.N,
-                       a.ws.cent, a.C, a.Cp, a.ws.fallback, a.ws.counters, a.assign,
-                       a.assign_hstride);
+    hipLaunchKernelGGL((k_fallback<Tin, D>), dim3(2048), dim3(256), 0, s, rv, a.ws.cent, a.C,
+                       a.Cp, a.ws.fallback, a.ws.counters, a.assign, a.assign_hstride);
     QVG_CHECK_LAUNCH();
   }
   return true;
@@ -1000,9 +1049,21 @@ bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int6
   {
     const int maxch = max_chunks(a.N, a.Cp);
     TimerScope ts_("kmeans_accumulate", s);
-    hipLaunchKernelGGL((k_chunk_sum<Tin, D>), dim3((maxch + 3) / 4, a.H), dim3(256), 0, s,
-                       (const Tin *)a.r, a.N, a.Cp, a.ws.sorted, a.ws.offs, a.ws.cofs,
-                       a.ws.chunk_j, maxch, a.ws.part);
+    const dim3 gcs((maxch + 3) / 4, a.H);
+#define QVG_CS(NS)                                                                           \
+  hipLaunchKernelGGL((k_chunk_sum<Tin, D, NS>), gcs, dim3(256), 0, s, view_of<Tin>(a, D), a.Cp, \
+                     a.ws.sorted, a.ws.offs, a.ws.cofs, a.ws.chunk_j, maxch, a.ws.part)
+    switch (a.nsub) {
+      case 0: QVG_CS(0); break;
+      case 1: QVG_CS(1); break;
+      case 2: QVG_CS(2); break;
+      case 3: QVG_CS(3); break;
+      case 4: QVG_CS(4); break;
+      case 5: QVG_CS(5); break;
+      case 6: QVG_CS(6); break;
+      default: QVG_CS(7); break;
+    }
+#undef QVG_CS
     QVG_CHECK_LAUNCH();
     hipLaunchKernelGGL((k_finalize<Tc, D>), dim3((a.Cp + 3) / 4, a.H), dim3(256), 0, s, a.C,
                        a.Cp, a.ws.offs, a.ws.cofs, maxch, a.ws.part, a.ws.cent, a.ws_stats,

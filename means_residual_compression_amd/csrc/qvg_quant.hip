@@ -69,28 +69,22 @@ __device__ __forceinline__ int floor_half(float u) {
   return f;
 }
 
-template <typename Tin, typename Tc, int BITS>
-__global__ void k_quant(const Tin *__restrict__ r, int N, int D, int C, const uint8_t *__restrict__ assign,
-                        int64_t assign_hstride, const Tc *__restrict__ chat, int64_t chat_hstride,
-                        int G, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+// Quantizes the residual R(T) = x - C(1)[pi(1)] - ... - C(T)[pi(T)] (the
+// view's nsub = T), recomputed from the input and the record.
+template <typename T, int BITS, int NSUB>
+__global__ void k_quant(ResView<T> rv, int G, uint8_t *__restrict__ codes,
+                        uint8_t *__restrict__ scales) {
   constexpr int L = (1 << BITS) - 1, MID = 1 << (BITS - 1);
   const int h = blockIdx.y;
+  const int N = rv.N, D = rv.D;
   const int lpt = D / 8, lpg = G / 8;
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const bool live = g < (int64_t)N * lpt;
   const int64_t i = live ? g / lpt : 0;
   const int q = (int)(g % lpt);
-  const int64_t off = ((int64_t)h * N + i) * D + q * 8;
   float v[8];
   if (live) {
-    load8(r, off, v);
-    if (assign) {
-      float c[8];
-      const int j = min((int)assign[(int64_t)h * assign_hstride + i], C - 1);
-      load8(chat + (int64_t)h * chat_hstride, (int64_t)j * D + q * 8, c);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = v[k] - c[k];
-    }
+    rv.template load8_n<NSUB>(h, i, q * 8, v);
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = 0.0f;
@@ -187,23 +181,37 @@ bool launch_subtract(const void *r, bool r_bf16, int H, int N, int D, int C, con
   return true;
 }
 
-bool launch_quant(const void *r, bool r_bf16, int H, int N, int D, int C, const uint8_t *assign,
-                  int64_t assign_hstride, const void *chat, bool c_bf16, int64_t chat_hstride,
-                  int bits, int G, uint8_t *codes, uint8_t *scales, hipStream_t s) {
+template <typename T>
+static void launch_quant_t(const void *x, int H, int N, int D, int C, const uint8_t *pi,
+                           const void *cent, int Ts, int nsub, int bits, int G, uint8_t *codes,
+                           uint8_t *scales, hipStream_t s) {
+  ResView<T> rv;
+  rv.x = (const T *)x;
+  rv.pi = pi;
+  rv.cent = (const T *)cent;
+  rv.N = N;
+  rv.D = D;
+  rv.C = C;
+  rv.Ts = Ts;
+  rv.nsub = nsub;
   const int64_t threads = (int64_t)N * (D / 8);
   dim3 grid((unsigned)((threads + 255) / 256), H);
+  dispatch_nsub(nsub, [&]<int NS>() {
+    if (bits == 2)
+      hipLaunchKernelGGL((k_quant<T, 2, NS>), grid, dim3(256), 0, s, rv, G, codes, scales);
+    else
+      hipLaunchKernelGGL((k_quant<T, 4, NS>), grid, dim3(256), 0, s, rv, G, codes, scales);
+  });
+}
+
+bool launch_quant(const void *x, bool bf16, int H, int N, int D, int C, const uint8_t *pi,
+                  const void *cent, int Ts, int nsub, int bits, int G, uint8_t *codes,
+                  uint8_t *scales, hipStream_t s) {
   TimerScope ts_("group_quant_pack", s);
-#define QVG_Q(TI, TC, B)                                                                        \
-  hipLaunchKernelGGL((k_quant<TI, TC, B>), grid, dim3(256), 0, s, (const TI *)r, N, D, C, assign, \
-                     assign_hstride, (const TC *)chat, chat_hstride, G, codes, scales)
-#define QVG_QB(TI, TC) \
-  do { if (bits == 2) QVG_Q(TI, TC, 2); else QVG_Q(TI, TC, 4); } while (0)
-  if (r_bf16 && c_bf16) QVG_QB(uint16_t, uint16_t);
-  else if (r_bf16) QVG_QB(uint16_t, float);
-  else if (c_bf16) QVG_QB(float, uint16_t);
-  else QVG_QB(float, float);
-#undef QVG_QB
-#undef QVG_Q
+  if (bf16)
+    launch_quant_t<uint16_t>(x, H, N, D, C, pi, cent, Ts, nsub, bits, G, codes, scales, s);
+  else
+    launch_quant_t<float>(x, H, N, D, C, pi, cent, Ts, nsub, bits, G, codes, scales, s);
   QVG_CHECK_LAUNCH();
   return true;
 }
