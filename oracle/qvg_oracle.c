@@ -60,14 +60,19 @@ float qvgo_bf16_to_f32(uint16_t b) { return bits_to_float((uint32_t)b << 16); }
 
 /* Round a finite float to the nearest bf16; on an exact tie pick the
  * candidate whose last mantissa bit is 0.  The two candidates are the value
- * truncated toward zero and the next bf16 away from zero. */
+ * truncated toward zero and the next bf16 away from zero.  Above the largest
+ * finite bf16 the next candidate is 2^128 as if the exponent were unbounded;
+ * choosing it means overflow, which IEEE 754 round-to-nearest turns into an
+ * infinity of the same sign (bits 0x7F80 / 0xFF80). */
 uint16_t qvgo_f32_to_bf16(float x)
 {
     uint32_t u = float_to_bits(x);
     uint32_t lo = u & 0xFFFF0000u;
     uint32_t hi = lo + 0x10000u;
+    double vhi = ((hi & 0x7FFFFFFFu) == 0x7F800000u) ? ldexp(x < 0 ? -1.0 : 1.0, 128)
+                                                     : (double)bits_to_float(hi);
     double dlo = fabs((double)x - (double)bits_to_float(lo));
-    double dhi = fabs((double)bits_to_float(hi) - (double)x);
+    double dhi = fabs(vhi - (double)x);
     if (dlo < dhi) return (uint16_t)(lo >> 16);
     if (dhi < dlo) return (uint16_t)(hi >> 16);
     return ((lo >> 16) & 1u) ? (uint16_t)(hi >> 16) : (uint16_t)(lo >> 16);

@@ -73,3 +73,23 @@ def test_bf16_rounding_matches_torch(oracle):
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     ours = np.array([oracle.f32_to_bf16_bits(v) for v in x], np.uint16)
     np.testing.assert_array_equal(ours, ref)
+
+
+def test_bf16_rounding_at_the_top_and_bottom(oracle):
+    """IEEE 754 round-to-nearest: values from the midpoint between the largest
+    bf16 (0x7F7F) and 2^128 upward overflow to infinity, values below it stay
+    finite; fp32 subnormals round like any other value."""
+    cases = {0x7F7F7FFF: 0x7F7F, 0x7F7F8000: 0x7F80, 0x7F7FFFFF: 0x7F80, 0xFF7F8000: 0xFF80,
+             0xFF7F7FFF: 0xFF7F, 0x7F7F0000: 0x7F7F, 0x00008000: 0x0000, 0x00018000: 0x0002,
+             0x80008001: 0x8001, 0x007FFFFF: 0x0080, 0x00000001: 0x0000, 0x80000000: 0x8000}
+    for u, want in cases.items():
+        v = np.array([u], np.uint32).view(np.float32)[0]
+        assert oracle.f32_to_bf16_bits(v) == want, hex(u)
+    # and a sweep of the last two bf16 binades and the subnormal range against torch
+    rng = np.random.default_rng(3)
+    u = np.concatenate([rng.integers(0x7E000000, 0x7F800000, 4000), rng.integers(0, 0x00800000, 4000)])
+    u = (u.astype(np.uint32) | (rng.integers(0, 2, u.size).astype(np.uint32) << 31))
+    x = u.view(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ours = np.array([oracle.f32_to_bf16_bits(v) for v in x], np.uint16)
+    np.testing.assert_array_equal(ours, ref)
