@@ -104,13 +104,33 @@ __device__ __forceinline__ void store8(float *p, int64_t i, const float v[8]) {
   *reinterpret_cast<float4 *>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
   *reinterpret_cast<float4 *>(p + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
+// Round-to-nearest-even fp32 -> bf16 with gfx950's v_cvt_pk_bf16_f32 (two
+// values per instruction); fp32 stores are unchanged.
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+  const bf16x2_t r = __builtin_convertvector((floatx2_t){a, b}, bf16x2_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
+}
 __device__ __forceinline__ void store8(uint16_t *p, int64_t i, const float v[8]) {
-  uint4 a;
-  a.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-  a.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-  a.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-  a.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
-  *reinterpret_cast<uint4 *>(p + i) = a;
+  *reinterpret_cast<uint4 *>(p + i) = make_uint4(pack_bf16_rne(v[0], v[1]), pack_bf16_rne(v[2], v[3]),
+                                                 pack_bf16_rne(v[4], v[5]), pack_bf16_rne(v[6], v[7]));
+}
+// The same as non-temporal stores: for streamed output that no later kernel
+// of the pass reads, so it does not displace cached data on its way out.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store8_stream(uint16_t *p, const float v[8]) {
+  const u32x4_t w = {pack_bf16_rne(v[0], v[1]), pack_bf16_rne(v[2], v[3]), pack_bf16_rne(v[4], v[5]),
+                     pack_bf16_rne(v[6], v[7])};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t *>(p));
+}
+__device__ __forceinline__ void store8_stream(float *p, const float v[8]) {
+  const u32x4_t a = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+  const u32x4_t b = {__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])};
+  __builtin_nontemporal_store(a, reinterpret_cast<u32x4_t *>(p));
+  __builtin_nontemporal_store(b, reinterpret_cast<u32x4_t *>(p + 4));
 }
 
 // ------------------------------------------------------- stage residuals
@@ -197,6 +217,14 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
   if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Branch-free decode of a non-negative E4M3 code: placing the 7 code bits at
+// fp32 bit 20 gives 2^(e-127)(1 + m/8) for e > 0 and the fp32 subnormal
+// m * 2^-129 for e = 0; scaling by 2^120 (exact) yields 2^(e-7)(1 + m/8) and
+// m * 2^-9 respectively.  Needs fp32 subnormals preserved (the default).
+__device__ __forceinline__ float e4m3_decode_bits(uint32_t c) {
+  return __uint_as_float((c & 0x7Fu) << 20) * 0x1p120f;
 }
 
 // Power-of-two exponent e such that values up to `m` scaled by 2^-e stay

@@ -114,39 +114,251 @@ __global__ void k_quant(ResView<T> rv, int G, uint8_t *__restrict__ codes,
 }
 
 // ------------------------------------------------------------- dequant
-template <typename Tc, typename To, int BITS>
-__global__ void k_dequant(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
-                          const uint8_t *__restrict__ assign, const Tc *__restrict__ cent, int N,
-                          int D, int C, int T, int G, To *__restrict__ out) {
+// The H*N token rows are cut into equal contiguous ranges, one per resident
+// workgroup slot; each range is processed in slices of `ch` channels by
+// separate workgroups that sit consecutively on one XCD (so a range's code
+// bytes come from HBM once).  A workgroup keeps in LDS (a) its head's
+// centroid tables of all T stages for its slice, as TL (fp32, or bf16 when
+// the centroids are bf16 and fp32 tables would not fit; re-staged where the
+// range crosses into the next head), and (b) a 256-entry table from a code
+// byte to the signed levels 2q - L of the codes it packs.  One lane handles 8
+// consecutive channels (so a wave's stores cover whole lines) of U
+// consecutive tokens per step; every global load of a step is issued before
+// the first use, and the U tokens are computed together so their LDS reads
+// overlap (tokens past the end are clamped; only their stores are skipped);
+// output goes out through non-temporal stores.
+// Per element:
+// x = fma(level, s_hat, C(T)[pi]) -- level * s_hat is exact, so this is the
+// rounded sum level*s_hat + C(T) -- then x += C(t)[pi(t)] for t = T-1..1 in
+// fp32, rounded once (RNE) to the output dtype.
+template <typename Tc, typename TL>
+__device__ __forceinline__ void stage_tables(TL *tab, const Tc *__restrict__ cent, int h, int T,
+                                             int C, int D, int ch, int c0) {
+  const int qpr = ch >> 2;  // 4-element quads per table row
+  const int nq = T * C * qpr;
+  for (int v0 = threadIdx.x; v0 < nq; v0 += 4 * blockDim.x) {
+    uint4 tmp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = min(v0 + i * (int)blockDim.x, nq - 1);
+      const int row = v / qpr, part = v - row * qpr;  // row = t*C + j
+      const Tc *src = cent + ((int64_t)h * T * C + row) * D + c0 + part * 4;
+      if constexpr (sizeof(Tc) == 2) {
+        const uint2 w = *reinterpret_cast<const uint2 *>(src);
+        tmp[i] = make_uint4(w.x, w.y, 0, 0);
+      } else {
+        tmp[i] = *reinterpret_cast<const uint4 *>(src);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = v0 + i * (int)blockDim.x;
+      if (v >= nq) continue;
+      if constexpr (sizeof(TL) == 2) {  // bf16 -> bf16, natural order
+        reinterpret_cast<uint2 *>(tab)[v] = make_uint2(tmp[i].x, tmp[i].y);
+      } else {
+        // fp32 rows are stored as two halves: quad 2m (channels 8m..8m+3) at
+        // quad m, quad 2m+1 at quad qpr/2 + m, so that the 8 lanes of a token
+        // read one contiguous 128-byte run per instruction (no bank conflicts).
+        const int row = v / qpr, part = v - row * qpr;
+        const int pq = row * qpr + (part & 1) * (qpr >> 1) + (part >> 1);
+        if constexpr (sizeof(Tc) == 2)  // bf16 -> fp32 (exact)
+          reinterpret_cast<uint4 *>(tab)[pq] =
+              make_uint4(tmp[i].x << 16, tmp[i].x & 0xFFFF0000u, tmp[i].y << 16, tmp[i].y & 0xFFFF0000u);
+        else
+          reinterpret_cast<uint4 *>(tab)[pq] = tmp[i];
+      }
+    }
+  }
+}
+
+// The 8 table values of channels kl..kl+7 of a row, as fp32 (fp32 rows use
+// the split layout written by stage_tables).
+__device__ __forceinline__ void lds_row8(const float *row, uint32_t kl, uint32_t ch, float c[8]) {
+  const float4 a = *reinterpret_cast<const float4 *>(row + (kl >> 1));
+  const float4 b = *reinterpret_cast<const float4 *>(row + (ch >> 1) + (kl >> 1));
+  c[0] = a.x, c[1] = a.y, c[2] = a.z, c[3] = a.w, c[4] = b.x, c[5] = b.y, c[6] = b.z, c[7] = b.w;
+}
+__device__ __forceinline__ void lds_row8(const uint16_t *row, uint32_t kl, uint32_t, float c[8]) {
+  const uint4 w = *reinterpret_cast<const uint4 *>(row + kl);
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[2 * i] = __uint_as_float(u[i] << 16);
+    c[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+  }
+}
+
+// Scale bytes of U consecutive rows holding 2^CG scale bytes each (CG <= 2,
+// so the U rows span at most 16 bytes): one load, then byte `soff` of each row.
+template <int CG, int U>
+__device__ __forceinline__ void scale_span(const uint8_t *sp, uint32_t soff, uint32_t *sb) {
+  constexpr int NB = U << CG;
+  uint32_t w[(NB + 3) / 4] = {};
+  __builtin_memcpy(w, sp, NB);
+#pragma unroll
+  for (int u = 0; u < U; ++u) sb[u] = (w[(u << CG) >> 2] >> (8 * (((u << CG) & 3) + soff))) & 0xFFu;
+}
+
+template <int BITS>
+constexpr int dequant_lut_bytes() {
+  return 256 * (8 / BITS) * 4;
+}
+
+template <typename Tc, typename TL, typename To, int BITS, int T>
+__global__ __launch_bounds__(1024) void k_dequant(const uint8_t *__restrict__ codes,
+                                                  const uint8_t *__restrict__ scales,
+                                                  const uint8_t *__restrict__ assign,
+                                                  const Tc *__restrict__ cent, int H, int N, int D,
+                                                  int C, int G, int ch_log2, int nranges,
+                                                  To *__restrict__ out) {
   constexpr int L = (1 << BITS) - 1;
-  const int h = blockIdx.y;
-  const int lpt = D / 8;
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= (int64_t)N * lpt) return;
-  const int64_t i = g / lpt;
-  const int q = (int)(g % lpt);
-  const int64_t row = (int64_t)h * N + i;
-  uint32_t packed;
-  if (BITS == 2) {
-    packed = reinterpret_cast<const uint16_t *>(codes + row * (D / 4))[q];
-  } else {
-    packed = reinterpret_cast<const uint32_t *>(codes + row * (D / 2))[q];
-  }
-  const float sh = e4m3_decode(scales[row * (D / G) + (q * 8) / G]);
-  float v[8];
+  constexpr int U = 4;         // consecutive tokens per lane per step
+  constexpr int PB = 8 / BITS; // codes per byte
+  extern __shared__ float4 smem4[];
+  float *lut = reinterpret_cast<float *>(smem4);  // [256][PB]
+  TL *tab = reinterpret_cast<TL *>(lut + 256 * PB);  // [T][C][ch]
+  const int ch = 1 << ch_log2;
+  const int slices = D >> ch_log2;
+  const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+  const int sl = k % slices;
+  const int r = (k / slices) * 8 + xcd;
+  if (r >= nranges) return;
+  for (int b = threadIdx.x; b < 256; b += blockDim.x) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int c = (int)((packed >> (BITS * k)) & (uint32_t)L);
-    v[k] = (float)(2 * c - L) * sh;  // exact: small integer times an E4M3 value
+    for (int i = 0; i < PB; ++i) lut[b * PB + i] = (float)(2 * ((b >> (BITS * i)) & L) - L);
   }
-  for (int t = T - 1; t >= 0; --t) {
-    const int j = min((int)assign[((int64_t)h * T + t) * N + i], C - 1);
-    float c[8];
-    load8(cent, (((int64_t)h * T + t) * C + j) * D + q * 8, c);
+  if (T == 0) __syncthreads();
+  const int64_t total = (int64_t)H * N;
+  const int64_t per = (total + nranges - 1) / nranges;
+  const int64_t a = r * per, b = min(total, a + per);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lpt_log2 = ch_log2 - 3;  // lanes per token = ch / 8
+  const int tpw = 64 >> lpt_log2;    // tokens per wave per unrolled slot
+  const uint32_t kl = (uint32_t)(lane & ((1 << lpt_log2) - 1)) * 8;  // lane's channel in the slice
+  const uint32_t k0 = (uint32_t)(sl * ch) + kl;                      // ... and in the row
+  // All per-row strides are powers of two: D, D*BITS/8 code bytes, D/G scale bytes.
+  const int d_log2 = __builtin_ctz(D);
+  const int db_log2 = d_log2 + __builtin_ctz(BITS) - 3;
+  const int dg_log2 = d_log2 - __builtin_ctz(G);
+  const uint32_t coff = k0 * BITS / 8, soff = k0 >> __builtin_ctz(G);
+  for (int64_t seg = a; seg < b;) {
+    const int h = (int)(seg / N);
+    const int64_t lo = seg - (int64_t)h * N, hi = min(b - (int64_t)h * N, (int64_t)N);
+    if (T > 0) {
+      __syncthreads();  // the previous head's tables are no longer read
+      stage_tables<Tc, TL>(tab, cent, h, T, C, D, ch, sl * ch);
+      __syncthreads();
+    }
+    // Segment-relative addressing: uniform 64-bit bases, 32-bit lane offsets
+    // (the launcher keeps a range's output below 2^31 bytes).
+    const int64_t row0 = (int64_t)h * N + lo;
+    const uint8_t *cbase = codes + (row0 << db_log2);
+    const uint8_t *sbase = scales + (row0 << dg_log2);
+    const uint8_t *abase[T > 0 ? T : 1];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = v[k] + c[k];
+    for (int t = 0; t < T; ++t) abase[t] = assign + ((int64_t)h * T + t) * N + lo;
+    char *obase = reinterpret_cast<char *>(out + (row0 << d_log2));
+    const uint32_t n = (uint32_t)(hi - lo);
+    const uint32_t step_w = (uint32_t)(tpw * U);  // tokens per wave step
+    const uint32_t step = (uint32_t)nw * step_w;
+    struct Batch {
+      uint32_t js[U][T > 0 ? T : 1];
+      uint32_t packed[U];
+      uint32_t sb[U];
+    };
+    // Global loads of one step.  A lane's U tokens are consecutive
+    // (rel .. rel+U-1), so where the whole wave step lies inside the segment
+    // (a wave-uniform test) each stage's assignment bytes and, for D/G <= 4,
+    // the scale bytes come in one wide load each; the tail loads per token,
+    // clamped to the last token.
+    auto fetch = [&](uint32_t rw, uint32_t rel, Batch &bt) {
+      if (rw + step_w <= n) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          uint32_t aw = 0;
+          __builtin_memcpy(&aw, abase[t] + rel, U);
+#pragma unroll
+          for (int u = 0; u < U; ++u) bt.js[u][t] = (aw >> (8 * u)) & 0xFFu;
+        }
+        const uint8_t *sp = sbase + (rel << dg_log2);
+        switch (dg_log2) {
+          case 0: scale_span<0, U>(sp, soff, bt.sb); break;
+          case 1: scale_span<1, U>(sp, soff, bt.sb); break;
+          case 2: scale_span<2, U>(sp, soff, bt.sb); break;
+          default:
+#pragma unroll
+            for (int u = 0; u < U; ++u) bt.sb[u] = sp[(u << dg_log2) + soff];
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t i = min(rel + (uint32_t)u, n - 1);
+#pragma unroll
+          for (int t = 0; t < T; ++t) bt.js[u][t] = abase[t][i];
+          bt.sb[u] = sbase[(i << dg_log2) + soff];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t i = min(rel + (uint32_t)u, n - 1);
+        if constexpr (BITS == 2)
+          bt.packed[u] = *reinterpret_cast<const uint16_t *>(cbase + ((i << db_log2) + coff));
+        else
+          bt.packed[u] = *reinterpret_cast<const uint32_t *>(cbase + ((i << db_log2) + coff));
+      }
+    };
+    auto emit = [&](uint32_t rel, const Batch &bt) {
+      // All U tokens are computed unconditionally (clamped inputs) so their
+      // LDS reads overlap; only the stores are guarded.
+      float v[U][8];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float sh = e4m3_decode_bits(bt.sb[u]);
+#pragma unroll
+        for (int m = 0; m < 8 / PB; ++m) {  // code bytes of the 8 channels
+          const uint32_t byte = (bt.packed[u] >> (8 * m)) & 0xFFu;
+          if constexpr (PB == 4) {
+            const float4 l4 = reinterpret_cast<const float4 *>(lut)[byte];
+            v[u][4 * m] = l4.x, v[u][4 * m + 1] = l4.y, v[u][4 * m + 2] = l4.z, v[u][4 * m + 3] = l4.w;
+          } else {
+            const float2 l2 = reinterpret_cast<const float2 *>(lut)[byte];
+            v[u][2 * m] = l2.x, v[u][2 * m + 1] = l2.y;
+          }
+        }
+        if constexpr (T > 0) {
+          float c[8];
+          lds_row8(tab + (((uint32_t)(T - 1) * C + min(bt.js[u][T - 1], (uint32_t)C - 1)) << ch_log2), kl, ch, c);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[u][e] = __builtin_fmaf(v[u][e], sh, c[e]);
+#pragma unroll
+          for (int t = T - 2; t >= 0; --t) {
+            lds_row8(tab + (((uint32_t)t * C + min(bt.js[u][t], (uint32_t)C - 1)) << ch_log2), kl, ch, c);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[u][e] = v[u][e] + c[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[u][e] = v[u][e] * sh;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t i = rel + (uint32_t)u;
+        if (i < n)
+          store8_stream(reinterpret_cast<To *>(obase + (((i << d_log2) + k0) * (uint32_t)sizeof(To))), v[u]);
+      }
+    };
+    // Control flow follows the wave's first token (uniform); lanes past the
+    // end load clamped tokens and skip their stores.
+    const uint32_t tl = ((uint32_t)lane >> lpt_log2) * U;
+    for (uint32_t rw = (uint32_t)(wave * step_w); rw < n; rw += step) {
+      Batch bt;
+      fetch(rw, rw + tl, bt);
+      emit(rw + tl, bt);
+    }
+    seg = (int64_t)h * N + hi;
   }
-  store8(out, row * D + q * 8, v);
 }
 
 // ============================================================ launchers
@@ -216,23 +428,86 @@ bool launch_quant(const void *x, bool bf16, int H, int N, int D, int C, const ui
   return true;
 }
 
+// Dequant table layout: the channel slice and the LDS table type.  fp32
+// tables (no per-element widening) are used when a slice of at least 64
+// channels (a whole 128-byte line of bf16 output per token) fits in 128 KB;
+// otherwise bf16 centroids stay bf16 in LDS; slices shrink only when even
+// that does not fit.
+struct DequantPlan {
+  int ch;
+  bool f32_tables;
+};
+static DequantPlan dequant_plan(int D, int C, int T, bool c_bf16) {
+  const size_t cap = 128 * 1024;
+  for (int ch = D; ch >= 64; ch /= 2)
+    if ((size_t)T * C * ch * 4 <= cap) return {ch, true};
+  const size_t esz = c_bf16 ? 2 : 4;
+  for (int ch = D; ch >= 16; ch /= 2)
+    if ((size_t)T * C * ch * esz <= cap) return {ch, !c_bf16};
+  return {16, !c_bf16};
+}
+
+template <typename Tc, typename TL, typename To, int BITS, int T>
+static bool launch_dequant_t(const uint8_t *codes, const uint8_t *scales, const uint8_t *assign,
+                             const void *cent, int H, int N, int D, int C, int G, int ch, void *out,
+                             hipStream_t s) {
+  const size_t lds = dequant_lut_bytes<BITS>() + (size_t)T * C * ch * sizeof(TL);
+  static const bool attr =
+      hipFuncSetAttribute((const void *)k_dequant<Tc, TL, To, BITS, T>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
+  if (!attr) return false;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(2, (160 * 1024) / lds));
+  const int slices = D / ch;
+  const int64_t rows = (int64_t)H * N;
+  int64_t want = (int64_t)per_cu * cus / slices;
+  // a range's output must stay below 2^31 bytes (32-bit offsets in the kernel)
+  want = std::max<int64_t>(want, (rows * D * (int64_t)sizeof(To) >> 30) + 1);
+  const int nranges = (int)std::max<int64_t>(1, std::min<int64_t>(rows, want));
+  const int grid = (nranges + 7) / 8 * 8 * slices;
+  hipLaunchKernelGGL((k_dequant<Tc, TL, To, BITS, T>), dim3(grid), dim3(1024), lds, s, codes,
+                     scales, assign, (const Tc *)cent, H, N, D, C, G, __builtin_ctz(ch), nranges,
+                     (To *)out);
+  return true;
+}
+
+template <typename Tc, typename To, int BITS>
+static bool launch_dequant_b(const uint8_t *codes, const uint8_t *scales, const uint8_t *assign,
+                             const void *cent, int H, int N, int D, int C, int T, int G, void *out,
+                             hipStream_t s) {
+  const DequantPlan pl = dequant_plan(D, C, T, sizeof(Tc) == 2);
+  bool ok = false;
+  auto go = [&]<int TT>() {
+    if constexpr (sizeof(Tc) == 4) {
+      ok = launch_dequant_t<Tc, float, To, BITS, TT>(codes, scales, assign, cent, H, N, D, C, G, pl.ch, out, s);
+    } else {
+      if (pl.f32_tables)
+        ok = launch_dequant_t<Tc, float, To, BITS, TT>(codes, scales, assign, cent, H, N, D, C, G, pl.ch, out, s);
+      else
+        ok = launch_dequant_t<Tc, uint16_t, To, BITS, TT>(codes, scales, assign, cent, H, N, D, C, G, pl.ch, out, s);
+    }
+  };
+  dispatch_nsub(T, go);
+  return ok;
+}
+
 bool launch_dequant(const uint8_t *codes, const uint8_t *scales, const uint8_t *assign,
                     const void *cent, bool c_bf16, int H, int N, int D, int C, int T, int bits,
                     int G, void *out, bool out_bf16, hipStream_t s) {
-  const int64_t threads = (int64_t)N * (D / 8);
-  dim3 grid((unsigned)((threads + 255) / 256), H);
   TimerScope ts_("fused_dequant", s);
-#define QVG_DQ(TC, TO, B)                                                                      \
-  hipLaunchKernelGGL((k_dequant<TC, TO, B>), grid, dim3(256), 0, s, codes, scales, assign,    \
-                     (const TC *)cent, N, D, C, T, G, (TO *)out)
-#define QVG_DQB(TC, TO) \
-  do { if (bits == 2) QVG_DQ(TC, TO, 2); else QVG_DQ(TC, TO, 4); } while (0)
-  if (c_bf16 && out_bf16) QVG_DQB(uint16_t, uint16_t);
-  else if (c_bf16) QVG_DQB(uint16_t, float);
-  else if (out_bf16) QVG_DQB(float, uint16_t);
-  else QVG_DQB(float, float);
-#undef QVG_DQB
+  if (T == 0) C = 1;
+  bool ok;
+#define QVG_DQ(TC, TO)                                                                          \
+  ok = bits == 2 ? launch_dequant_b<TC, TO, 2>(codes, scales, assign, cent, H, N, D, C, T, G, out, s) \
+                 : launch_dequant_b<TC, TO, 4>(codes, scales, assign, cent, H, N, D, C, T, G, out, s)
+  if (c_bf16 && out_bf16) QVG_DQ(uint16_t, uint16_t);
+  else if (c_bf16) QVG_DQ(uint16_t, float);
+  else if (out_bf16) QVG_DQ(float, uint16_t);
+  else QVG_DQ(float, float);
 #undef QVG_DQ
+  if (!ok) return false;
   QVG_CHECK_LAUNCH();
   return true;
 }

@@ -48,4 +48,6 @@ def mismatch_report(a: np.ndarray, b: np.ndarray) -> str:
     if a.shape != b.shape:
         return f"shape {a.shape} vs {b.shape}"
     diff = np.nonzero(a.reshape(-1) != b.reshape(-1))[0]
-    return f"{len(diff)} / {a.size} differ; first at flat {diff[:5].tolist()}"
+    fa, fb = a.reshape(-1), b.reshape(-1)
+    pairs = [(int(i), fa[i].item(), fb[i].item()) for i in diff[:8]]
+    return f"{len(diff)} / {a.size} differ; (flat index, got, want): {pairs}"

@@ -59,16 +59,20 @@ def test_sas_subtract(rdt, cdt):
         assert np.array_equal(out[h].cpu().numpy(), ref)
 
 
-@pytest.mark.parametrize("T,C,bits,G,cdt,odt", [
+@pytest.mark.parametrize("T,C,bits,G,cdt,odt,d", [
+    (*c, 128)[:7] for c in [
     (0, 1, 2, 64, torch.bfloat16, torch.bfloat16),
     (1, 256, 2, 64, torch.bfloat16, torch.bfloat16),
     (2, 256, 2, 64, torch.bfloat16, torch.float32),
     (4, 256, 2, 64, torch.bfloat16, torch.bfloat16),
     (3, 40, 4, 32, torch.float32, torch.float32),
     (4, 256, 4, 16, torch.float32, torch.bfloat16),
-])
-def test_fused_dequant(T, C, bits, G, cdt, odt):
-    H, N, d = 3, 2085, 128
+    (8, 256, 2, 64, torch.bfloat16, torch.float32),
+    (8, 256, 4, 32, torch.float32, torch.bfloat16, 64),
+    (2, 200, 2, 8, torch.bfloat16, torch.bfloat16, 64),
+]])
+def test_fused_dequant(T, C, bits, G, cdt, odt, d):
+    H, N = 3, 2085
     codes, scales, assign, cent = synth.random_record(11 + T, H, N, d, T, C, bits, G, Hg=40, Wg=52)
     cent = cent.to(cdt)
     p = qvg.params(C=C, T=T, iters=1, bits=bits, group=G)
@@ -81,6 +85,64 @@ def test_fused_dequant(T, C, bits, G, cdt, odt):
                             out_bf16=odt == torch.bfloat16)
     got = bits16(out) if odt == torch.bfloat16 else out.cpu().numpy()
     assert np.array_equal(got, ref), mismatch_report(got, ref)
+
+
+def _rounding_patterns(rng, n):
+    """fp32 bit patterns across every binade: exact bf16 ties (both parities),
+    one ulp either side of a tie, fp32 subnormals, zeros of both signs and the
+    values just below the fp32 maximum that round to infinity."""
+    u = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+    exp = (u >> 23) & 0xFF
+    u[exp == 0xFF] &= np.uint32(0xBFFFFFFF)  # no inf/NaN inputs
+    k = n // 8
+    u[0:k] = (u[0:k] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    u[k:2 * k] = (u[k:2 * k] & np.uint32(0xFFFF0000)) | np.uint32(0x7FFF)
+    u[2 * k:3 * k] = (u[2 * k:3 * k] & np.uint32(0xFFFF0000)) | np.uint32(0x8001)
+    u[3 * k:4 * k] &= np.uint32(0x807FFFFF)  # subnormal
+    u[4 * k:4 * k + 16] = np.array([0, 0x80000000, 0x7F7FFFFF, 0xFF7FFFFF, 0x7F7F8000, 0x7F7F7FFF,
+                                    0x00008000, 0x00018000, 0x80008000, 1, 0x807FFFFF, 0x007FFFFF,
+                                    0x3F808000, 0x3F818000, 0xBF808000, 0xBF818000], np.uint32)
+    return u.view(np.float32)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_fused_dequant_every_scale_code(bits):
+    """Scale bytes over every finite E4M3 code, subnormals included."""
+    H, N, d, C, T, G = 2, 1777, 128, 64, 2, 32
+    codes, scales, assign, cent = synth.random_record(21, H, N, d, T, C, bits, G, Hg=40, Wg=52)
+    rng = np.random.default_rng(4)
+    scales = rng.integers(0, 0x7F, scales.shape, dtype=np.uint8)
+    scales[:, :, 0] = np.arange(N * H).reshape(H, N) % 0x7F  # every code appears
+    p = qvg.params(C=C, T=T, iters=1, bits=bits, group=G)
+    rec = qvg.Record(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                     torch.from_numpy(assign).to(DEV), cent.to(DEV))
+    say("fused_dequant every scale code", bits)
+    out = qvg.decompress(rec, p, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.decompress(codes, scales, assign, to_oracle(cent), bits, G, out_bf16=False)
+    got = out.cpu().numpy()
+    assert np.array_equal(got, ref), mismatch_report(got, ref)
+
+
+def test_fused_dequant_bf16_rounding():
+    """With zero scales the output is the fp32 centroid rounded to bf16, so
+    crafted centroid bit patterns pin the output rounding (RNE) exactly."""
+    H, N, d, C = 2, 1500, 128, 50
+    rng = np.random.default_rng(5)
+    cent = _rounding_patterns(rng, H * C * d).reshape(H, 1, C, d).copy()
+    codes = rng.integers(0, 256, (H, N, d // 4), dtype=np.uint8)
+    scales = np.zeros((H, N, d // 64), np.uint8)
+    assign = rng.integers(0, C, (H, 1, N), dtype=np.uint8)
+    p = qvg.params(C=C, T=1, iters=1, bits=2, group=64)
+    rec = qvg.Record(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                     torch.from_numpy(assign).to(DEV), torch.from_numpy(cent).to(DEV))
+    say("fused_dequant rounding")
+    out = qvg.decompress(rec, p, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.decompress(codes, scales, assign, cent, 2, 64, out_bf16=True)
+    got = bits16(out)
+    assert np.array_equal(got, ref), mismatch_report(got, ref)
+    assert (got == 0x7F80).any() and (got == 0xFF80).any()  # overflow to infinity occurred
 
 
 def _video(H, N, d, kind_mix=True, seed_cfg=1):
