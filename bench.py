@@ -14,13 +14,17 @@ same workload (run on this host's cores), with a bit-exact parity check of
 that sample.
 
 Other workloads (--workload): decode (decode-side dequant of a 40 x 262144
-token, T=4 record), stream (20 chunks of 3 frames, warm vs cold), large
-(32 K + 32 V heads x 131072 tokens, T=4, INT2 and INT4), tiny (one 4096-token
-fp32 head).
+token, T=4 record).  --copy-calibration runs only a plain 256 MiB device copy,
+the reference that the HBM byte counters of the kernels are scaled by.
+
+The `traffic` field of a roofline is the kernel's measured HBM bytes per
+launch, read from profiles/<kernel>_<workload>_pmc.txt, and null when the
+kernel's sources have changed since those counters were taken.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -41,6 +45,52 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+# Sources whose text determines each timed kernel's code.
+CSRC = os.path.join(ROOT, "means_residual_compression_amd", "csrc")
+KERNEL_SOURCES = {
+    "kmeans_assign": ["qvg_kmeans.hip", "qvg_common.h", "qvg_internal.h"],
+    "fused_dequant": ["qvg_quant.hip", "qvg_common.h", "qvg_internal.h"],
+}
+COPY_BYTES = 256 << 20
+
+
+def source_digest(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel's sources changed after it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) == 2 and not line.startswith("#"):
+                vals[parts[0]] = parts[1]
+    if vals.get("source_sha256") != source_digest(kernel) or "hbm_bytes_per_launch" not in vals:
+        return None
+    return float(vals["hbm_bytes_per_launch"])
+
+
+def copy_calibration():
+    """A plain device copy of known size (read COPY_BYTES, write COPY_BYTES),
+    run a few times: the reference for scaling FETCH_SIZE / WRITE_SIZE."""
+    dev = torch.device("cuda:0")
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        torch.mul(a, 1.0, out=b)  # an elementwise kernel: reads a once, writes b once
+    torch.cuda.synchronize()
+    return {"copy_bytes": COPY_BYTES, "launches": 5}
 
 
 # ------------------------------------------------------------------ helpers
@@ -137,11 +187,13 @@ def run_selfforcing(args):
     rooflines = {
         "kmeans_assign": {"bound": "mfma", "achieved": asg_tflops, "peak": MFMA_F16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": asg_tflops / MFMA_F16_PEAK_TFLOPS,
-                          "traffic": None, "kernel": "kmeans_assign",
+                          "traffic": stored_traffic("kmeans_assign", "selfforcing"),
+                          "kernel": "kmeans_assign",
                           "per_launch": f"{asg_flops:.4g} flop (2*N*C*d over {H} head-tensors)",
                           "avg_ms": asg["avg_ms"]},
         "fused_dequant": {"bound": "hbm", "achieved": dq_gbps, "peak": HBM_PEAK_GBPS,
-                          "unit": "GB/s", "frac": dq_gbps / HBM_PEAK_GBPS, "traffic": None,
+                          "unit": "GB/s", "frac": dq_gbps / HBM_PEAK_GBPS,
+                          "traffic": stored_traffic("fused_dequant", "selfforcing"),
                           "kernel": "fused_dequant",
                           "per_launch": f"{dq_bytes} B", "avg_ms": dq["avg_ms"]},
     }
@@ -208,7 +260,8 @@ def run_decode(args):
             "config": {"workload": "decode-side record 40 heads x 262144 tokens, d=128, INT2 "
                                    "G=64, T=4, C=256, bf16 centroids and output"},
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                         "traffic": stored_traffic("fused_dequant", "decode"),
                          "kernel": "fused_dequant", "per_launch": f"{nbytes} B",
                          "avg_ms": dq["avg_ms"]},
             "cpu_baseline": None}
@@ -222,15 +275,19 @@ def main():
     ap.add_argument("--workload", default="selfforcing", choices=["selfforcing", "decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=None)
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this path needs no communication "
-              "(head-tensors are independent), and this build runs on a single MI355X. "
+        print("bench.py measures one GPU: head-tensors are independent and the path "
+              "exchanges nothing between GPUs, so there is no multi-GPU step to time. "
               "Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration()), flush=True)
+        return
     qvg.lib()
     res = run_selfforcing(args) if args.workload == "selfforcing" else run_decode(args)
     print(json.dumps(res), flush=True)
