@@ -118,9 +118,9 @@ __global__ void k_quant(ResView<T> rv, int G, uint8_t *__restrict__ codes,
 // workgroup slot; each range is processed in slices of `ch` channels by
 // separate workgroups that sit consecutively on one XCD (so a range's code
 // bytes come from HBM once).  A workgroup keeps in LDS (a) its head's
-// centroid tables of all T stages for its slice, as TL (fp32, or bf16 when
-// the centroids are bf16 and fp32 tables would not fit; re-staged where the
-// range crosses into the next head), and (b) a 256-entry table from a code
+// centroid tables of all T stages for its slice, in the centroid dtype
+// (re-staged where the range crosses into the next head), and (b) a
+// 256-entry table from a code
 // byte to the signed levels 2q - L of the codes it packs.  One lane handles 8
 // consecutive channels (so a wave's stores cover whole lines) of U
 // consecutive tokens per step; every global load of a step is issued before
@@ -232,7 +232,8 @@ __global__ __launch_bounds__(1024) void k_dequant(const uint8_t *__restrict__ co
   const int64_t total = (int64_t)H * N;
   const int64_t per = (total + nranges - 1) / nranges;
   const int64_t a = r * per, b = min(total, a + per);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lpt_log2 = ch_log2 - 3;  // lanes per token = ch / 8
   const int tpw = 64 >> lpt_log2;    // tokens per wave per unrolled slot
   const uint32_t kl = (uint32_t)(lane & ((1 << lpt_log2) - 1)) * 8;  // lane's channel in the slice
@@ -259,6 +260,9 @@ __global__ __launch_bounds__(1024) void k_dequant(const uint8_t *__restrict__ co
 #pragma unroll
     for (int t = 0; t < T; ++t) abase[t] = assign + ((int64_t)h * T + t) * N + lo;
     char *obase = reinterpret_cast<char *>(out + (row0 << d_log2));
+    const TL *tabt[T > 0 ? T : 1];  // stage tables of this slice
+#pragma unroll
+    for (int t = 0; t < T; ++t) tabt[t] = tab + (uint32_t)t * C * ch;
     const uint32_t n = (uint32_t)(hi - lo);
     const uint32_t step_w = (uint32_t)(tpw * U);  // tokens per wave step
     const uint32_t step = (uint32_t)nw * step_w;
@@ -328,12 +332,12 @@ __global__ __launch_bounds__(1024) void k_dequant(const uint8_t *__restrict__ co
         }
         if constexpr (T > 0) {
           float c[8];
-          lds_row8(tab + (((uint32_t)(T - 1) * C + min(bt.js[u][T - 1], (uint32_t)C - 1)) << ch_log2), kl, ch, c);
+          lds_row8(tabt[T - 1] + (min(bt.js[u][T - 1], (uint32_t)C - 1) << ch_log2), kl, ch, c);
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[u][e] = __builtin_fmaf(v[u][e], sh, c[e]);
 #pragma unroll
           for (int t = T - 2; t >= 0; --t) {
-            lds_row8(tab + (((uint32_t)t * C + min(bt.js[u][t], (uint32_t)C - 1)) << ch_log2), kl, ch, c);
+            lds_row8(tabt[t] + (min(bt.js[u][t], (uint32_t)C - 1) << ch_log2), kl, ch, c);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[u][e] = v[u][e] + c[e];
           }
@@ -342,6 +346,13 @@ __global__ __launch_bounds__(1024) void k_dequant(const uint8_t *__restrict__ co
           for (int e = 0; e < 8; ++e) v[u][e] = v[u][e] * sh;
         }
       }
+      // Keep the arithmetic of all U tokens ahead of the guarded stores (the
+      // compiler would otherwise sink each token's work into its store's
+      // branch and serialize the LDS reads).
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(v[u][e]));
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t i = rel + (uint32_t)u;
@@ -428,23 +439,18 @@ bool launch_quant(const void *x, bool bf16, int H, int N, int D, int C, const ui
   return true;
 }
 
-// Dequant table layout: the channel slice and the LDS table type.  fp32
-// tables (no per-element widening) are used when a slice of at least 64
-// channels (a whole 128-byte line of bf16 output per token) fits in 128 KB;
-// otherwise bf16 centroids stay bf16 in LDS; slices shrink only when even
-// that does not fit.
-struct DequantPlan {
-  int ch;
-  bool f32_tables;
-};
-static DequantPlan dequant_plan(int D, int C, int T, bool c_bf16) {
-  const size_t cap = 128 * 1024;
-  for (int ch = D; ch >= 64; ch /= 2)
-    if ((size_t)T * C * ch * 4 <= cap) return {ch, true};
-  const size_t esz = c_bf16 ? 2 : 4;
-  for (int ch = D; ch >= 16; ch /= 2)
-    if ((size_t)T * C * ch * esz <= cap) return {ch, !c_bf16};
-  return {16, !c_bf16};
+// Channel slice of the dequant's LDS tables (kept in the centroid dtype).
+// Slices of at least 64 channels keep a token's share of a bf16 output row a
+// whole 128-byte line; among those, one whose tables leave room for two
+// workgroups per CU is preferred, then one that fits at all; only when none
+// fits do slices drop below 64 channels.
+static int dequant_slice(int D, int C, int T, size_t esz, size_t lut) {
+  for (size_t cap : {80 * 1024, 160 * 1024})
+    for (int ch = D; ch >= 64; ch /= 2)
+      if (lut + (size_t)T * C * ch * esz <= cap) return ch;
+  for (int ch = 32; ch >= 16; ch /= 2)
+    if (lut + (size_t)T * C * ch * esz <= 160 * 1024) return ch;
+  return 16;
 }
 
 template <typename Tc, typename TL, typename To, int BITS, int T>
@@ -477,19 +483,11 @@ template <typename Tc, typename To, int BITS>
 static bool launch_dequant_b(const uint8_t *codes, const uint8_t *scales, const uint8_t *assign,
                              const void *cent, int H, int N, int D, int C, int T, int G, void *out,
                              hipStream_t s) {
-  const DequantPlan pl = dequant_plan(D, C, T, sizeof(Tc) == 2);
+  const int ch = dequant_slice(D, C, T, sizeof(Tc), dequant_lut_bytes<BITS>());
   bool ok = false;
-  auto go = [&]<int TT>() {
-    if constexpr (sizeof(Tc) == 4) {
-      ok = launch_dequant_t<Tc, float, To, BITS, TT>(codes, scales, assign, cent, H, N, D, C, G, pl.ch, out, s);
-    } else {
-      if (pl.f32_tables)
-        ok = launch_dequant_t<Tc, float, To, BITS, TT>(codes, scales, assign, cent, H, N, D, C, G, pl.ch, out, s);
-      else
-        ok = launch_dequant_t<Tc, uint16_t, To, BITS, TT>(codes, scales, assign, cent, H, N, D, C, G, pl.ch, out, s);
-    }
-  };
-  dispatch_nsub(T, go);
+  dispatch_nsub(T, [&]<int TT>() {
+    ok = launch_dequant_t<Tc, Tc, To, BITS, TT>(codes, scales, assign, cent, H, N, D, C, G, ch, out, s);
+  });
   return ok;
 }
 
