@@ -14,7 +14,9 @@ same workload (run on this host's cores), with a bit-exact parity check of
 that sample.
 
 Other workloads (--workload): decode (decode-side dequant of a 40 x 262144
-token, T=4 record).  --copy-calibration runs only a plain 256 MiB device copy,
+token, T=4 record), stream (20 chunks of 3 frames, warm-started against cold
+k-means, per-chunk time and MSE), large (32 K + 32 V head-tensors x 131072
+tokens, T=4, INT2 and INT4, per-stage MSE curve and record sizes).  --copy-calibration runs only a plain 256 MiB device copy,
 the reference that the HBM byte counters of the kernels are scaled by.
 
 The `traffic` field of a roofline is the kernel's measured HBM bytes per
@@ -267,12 +269,149 @@ def run_decode(args):
             "cpu_baseline": None}
 
 
+def _mse(x, y):
+    """Mean squared error per head-tensor in fp64 (measurement only)."""
+    return ((x.double() - y.double()) ** 2).mean(dim=(1, 2))
+
+
+def _events_ms(fn):
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    r = fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1), r
+
+
+def run_stream(args):
+    """A 60-frame stream in 20 chunks of 3 frames (4680 tokens) of 12 K + 12 V
+    head-tensors: cold chunks (10 iterations from seeded rows) against warm
+    chunks (3 iterations from the previous chunk's fp32 centroids)."""
+    dev = torch.device("cuda:0")
+    c = synth.CONFIGS[2]
+    log("generating the stream chunks ...")
+    chunks = []
+    for ci in range(c["chunks"]):
+        parts = [synth.stream_chunk(2, k, c["heads"], ci, c["F"], c["Hg"], c["Wg"], c["d"],
+                                    c["outlier"][k], c["dtype"]) for k in c["kinds"]]
+        chunks.append(torch.cat(parts, 0).to(dev))
+    H, N, d = chunks[0].shape
+    p = qvg.params(C=c["C"], T=c["T"], iters=c["iters"], bits=c["bits"], group=c["group"])
+    ws = qvg.alloc_workspace(qvg.workspace_size(H, N, d, chunks[0].dtype, p), dev)
+    rec = qvg.empty_record(H, N, d, p, chunks[0].dtype, dev)
+    out = torch.empty_like(chunks[0])
+    cache = torch.zeros((H, p.T, p.C, d), dtype=torch.float32, device=dev)
+    idx = [torch.from_numpy(synth.init_indices(2000 + ci, H, p.T, N, p.C)).pin_memory()
+           for ci in range(c["chunks"])]
+    res_modes = {}
+    for mode in ("cold", "warm"):
+        for _ in range(args.warmup):  # warm-up passes over the first chunks
+            qvg.compress(chunks[0], p, init_idx=idx[0], ws=ws, out=rec, cache_out=cache)
+        torch.cuda.synchronize()
+        times, mses = [], []
+        for ci, x in enumerate(chunks):
+            if mode == "cold" or ci == 0:
+                ms, _ = _events_ms(lambda: qvg.compress(x, p, init_idx=idx[ci], ws=ws, out=rec,
+                                                        cache_out=cache))
+            else:
+                ms, _ = _events_ms(lambda: qvg.compress_stream(x, p, c["iters_warm"], cache, True,
+                                                               ws=ws, out=rec))
+            qvg.decompress(rec, p, out=out)
+            times.append(ms)
+            mses.append(_mse(out, x).mean().item())
+        res_modes[mode] = {"ms_per_chunk": times, "mse_per_chunk": mses,
+                           "total_ms": sum(times),
+                           "tokens_per_s": H * N * len(chunks) / (sum(times) * 1e-3)}
+    warm, cold = res_modes["warm"], res_modes["cold"]
+    return {"metric": "streamed compress tokens/s (warm-started chunks)",
+            "value": warm["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+            "steps": len(chunks), "warmup": args.warmup,
+            "ms_per_step": warm["total_ms"] / len(chunks), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+            "config": {"workload": "stream of 20 chunks x 3 frames (4680 tokens), 12 K + 12 V "
+                                   "head-tensors, d=128, bf16, C=256, T=2, INT2 G=64; warm: 3 "
+                                   "iterations from the cache, cold: 10 from seeded rows"},
+            "warm": warm, "cold": cold,
+            "warm_speedup": cold["total_ms"] / warm["total_ms"],
+            "mse_ratio_warm_over_cold": float(np.mean(warm["mse_per_chunk"][1:]) /
+                                              np.mean(cold["mse_per_chunk"][1:])),
+            "roofline": None, "cpu_baseline": None}
+
+
+def run_large(args):
+    """The long-video cache: 32 K + 32 V head-tensors x 131072 tokens (4 scenes
+    of 21 frames on a 39x40 grid), d=128, bf16, C=256, 8 iterations, T=4,
+    INT2 and INT4 (G=64); the per-stage MSE curve and the record sizes."""
+    dev = torch.device("cuda:0")
+    c = synth.CONFIGS[3]
+    heads = args.large_heads or c["heads"]
+    log(f"generating the long-video cache ({2 * heads} head-tensors) ...")
+    x = synth.config_cache(3, heads=heads, workers=min(16, len(os.sched_getaffinity(0)))).to(dev)
+    H, N, d = x.shape
+    idx = torch.from_numpy(synth.init_indices(3, H, c["T"], N, c["C"])).pin_memory()
+    out = torch.empty_like(x)
+    res = {}
+    for bits in (2, 4):
+        p = qvg.params(C=c["C"], T=c["T"], iters=c["iters"], bits=bits, group=c["group"])
+        ws = qvg.alloc_workspace(qvg.workspace_size(H, N, d, x.dtype, p), dev)
+        rec = qvg.empty_record(H, N, d, p, x.dtype, dev)
+        ms = timed(lambda: qvg.compress(x, p, init_idx=idx, ws=ws, out=rec), args.steps,
+                   args.warmup)
+        kt = kernel_times(qvg.KERNELS)
+        dms, _ = _events_ms(lambda: qvg.decompress(rec, p, out=out))
+        mse = _mse(out, x)
+        asg = kt["kmeans_assign"]
+        asg_tflops = 2.0 * H * N * p.C * d / (asg["avg_ms"] * 1e-3) / 1e12
+        res[f"int{bits}"] = {
+            "compress_ms": ms, "compress_tokens_per_s": H * N / (ms * 1e-3),
+            "decompress_ms": dms, "mse_K": mse[:heads].mean().item(),
+            "mse_V": mse[heads:].mean().item(),
+            "record_bytes_per_head_tensor": rec.nbytes() // H,
+            "compression_ratio_vs_bf16": N * d * 2 / (rec.nbytes() / H),
+            "quantized_share": (rec.codes.numel() + rec.scales.numel()) / rec.nbytes(),
+            "assign_tflops": asg_tflops, "assign_mfma_frac": asg_tflops / MFMA_F16_PEAK_TFLOPS,
+            "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kt.items()}}
+        del ws, rec
+    # per-stage MSE curve (INT2): stage count t = 0..T with the same seeded rows
+    curve = {"K": [], "V": []}
+    for t in range(c["T"] + 1):
+        p = qvg.params(C=c["C"], T=t, iters=c["iters"], bits=2, group=c["group"])
+        rec = qvg.compress(x, p, init_idx=idx[:, :t].contiguous() if t else None)
+        qvg.decompress(rec, p, out=out)
+        mse = _mse(out, x)
+        curve["K"].append(mse[:heads].mean().item())
+        curve["V"].append(mse[heads:].mean().item())
+        del rec
+    for k in ("K", "V"):
+        curve[k + "_reduction_vs_naive"] = [curve[k][0] / m for m in curve[k]]
+    r2 = res["int2"]
+    return {"metric": "compress tokens/s, d=128 C=256 T=4 (long-video cache)",
+            "value": r2["compress_tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": r2["compress_ms"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+            "data": "synthetic",
+            "config": {"workload": f"long-video cache: {heads} K + {heads} V head-tensors x "
+                                   "131072 tokens (4 scenes x 21 frames x 39x40), d=128, bf16, "
+                                   "C=256, 8 iterations, T=4, G=64",
+                       "head_tensors": H, "tokens": N},
+            "int2": r2, "int4": res["int4"], "mse_curve_int2": curve,
+            "roofline": {"bound": "mfma", "achieved": r2["assign_tflops"],
+                         "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": r2["assign_mfma_frac"], "traffic": None,
+                         "kernel": "kmeans_assign"},
+            "cpu_baseline": None}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="selfforcing", choices=["selfforcing", "decode"])
+    ap.add_argument("--workload", default="selfforcing",
+                    choices=["selfforcing", "decode", "stream", "large"])
+    ap.add_argument("--large-heads", type=int, default=None,
+                    help="K (and V) head-tensors of the long-video cache (default 32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=None)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -289,7 +428,8 @@ def main():
         print(json.dumps(copy_calibration()), flush=True)
         return
     qvg.lib()
-    res = run_selfforcing(args) if args.workload == "selfforcing" else run_decode(args)
+    res = {"selfforcing": run_selfforcing, "decode": run_decode, "stream": run_stream,
+           "large": run_large}[args.workload](args)
     print(json.dumps(res), flush=True)
 
 

@@ -76,14 +76,28 @@ def video_head(seed: int, F: int, Hg: int, Wg: int, d: int, outlier_scale: float
     return out
 
 
+def _head_rounded(args):
+    seed, F, Hg, Wg, d, outlier_scale, scene_len, n_tokens, dtype = args
+    return round_to(video_head(seed, F, Hg, Wg, d, outlier_scale, scene_len, n_tokens), dtype)
+
+
 def video_cache(cfg: int, kind: int, heads: int, F: int, Hg: int, Wg: int, d: int,
                 outlier_scale: float, dtype: torch.dtype, scene_len: int | None = None,
-                n_tokens: int | None = None, head_ids=None) -> torch.Tensor:
-    """[heads, N, d] CPU tensor; head h uses seed (1000 + 100*cfg + h, kind)."""
-    ids = range(heads) if head_ids is None else head_ids
-    hs = [video_head(_seed(cfg, kind, h), F, Hg, Wg, d, outlier_scale, scene_len, n_tokens)
-          for h in ids]
-    return round_to(np.stack(hs), dtype)
+                n_tokens: int | None = None, head_ids=None, workers: int = 1) -> torch.Tensor:
+    """[heads, N, d] CPU tensor; head h uses seed (1000 + 100*cfg + h, kind).
+    `workers` > 1 draws the heads in that many processes (same values)."""
+    ids = list(range(heads) if head_ids is None else head_ids)
+    jobs = [(_seed(cfg, kind, h), F, Hg, Wg, d, outlier_scale, scene_len, n_tokens, dtype)
+            for h in ids]
+    if workers > 1 and len(jobs) > 1:
+        import concurrent.futures as cf
+        import multiprocessing as mp
+        with cf.ProcessPoolExecutor(min(workers, len(jobs)),
+                                    mp_context=mp.get_context("spawn")) as ex:
+            hs = list(ex.map(_head_rounded, jobs))
+    else:
+        hs = [_head_rounded(j) for j in jobs]
+    return torch.stack(hs)
 
 
 def _seed(cfg: int, kind: int, h: int) -> int:
@@ -137,14 +151,16 @@ CONFIGS = {
 }
 
 
-def config_cache(cfg: int, heads: int | None = None, n_tokens: int | None = None) -> torch.Tensor:
+def config_cache(cfg: int, heads: int | None = None, n_tokens: int | None = None,
+                 workers: int = 1) -> torch.Tensor:
     """All head-tensors of a configuration stacked K-then-V: [kinds*heads, N, d].
     `heads`/`n_tokens` give a smaller sample of the same workload."""
     c = CONFIGS[cfg]
     nh = c["heads"] if heads is None else heads
     N = c.get("n_tokens") if n_tokens is None else n_tokens
     parts = [video_cache(cfg, k, nh, c["F"], c["Hg"], c["Wg"], c["d"], c["outlier"][k],
-                         c["dtype"], c.get("scene_len"), N) for k in c["kinds"]]
+                         c["dtype"], c.get("scene_len"), N, workers=workers)
+             for k in c["kinds"]]
     return torch.cat(parts, 0)
 
 

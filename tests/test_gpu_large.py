@@ -1,0 +1,75 @@
+"""GPU parity at the two largest workload shapes, through the C ABI.
+
+* The long-video cache: 131072 tokens (84 frames of a 39x40 grid plus the
+  first 32 tokens of frame 84, scenes cut every 21 frames), d=128, bf16,
+  C=256, T=4 stages, INT2 and INT4 with G=64.  Whole records (assignments,
+  centroids, codes, scales, fp32 centroid cache) and reconstructions are
+  compared bit for bit with the oracle on one K and one V head-tensor.  The
+  oracle needs ~100 s per head at the workload's 8 iterations, so these runs
+  use 2 iterations per stage: every kernel and every stage transition still
+  runs at full size.
+* The decode-side record: 40 head-tensors x 262144 tokens, T=4, C=256, INT2
+  G=64, bf16 centroids; the fused dequant of every token is compared bit for
+  bit with the oracle's reconstruction.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from means_residual_compression_amd import qvg, synth
+from gpu_util import DEV, bits16, mismatch_report, rec_equal, say, to_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _threads():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _large_heads(kinds):
+    c = synth.CONFIGS[3]
+    parts = [synth.video_cache(3, k, 1, c["F"], c["Hg"], c["Wg"], c["d"], c["outlier"][k],
+                               c["dtype"], c["scene_len"], c["n_tokens"], head_ids=[0])
+             for k in kinds]
+    return torch.cat(parts, 0), c
+
+
+@pytest.mark.parametrize("bits,kinds", [(2, (synth.K_KIND, synth.V_KIND)), (4, (synth.V_KIND,))])
+def test_large_cache_full_size(bits, kinds):
+    x, c = _large_heads(kinds)
+    H, N, d = x.shape
+    p = qvg.params(C=c["C"], T=c["T"], iters=2, bits=bits, group=c["group"])
+    idx = synth.init_indices(3, H, p.T, N, p.C)
+    say("large cache", tuple(x.shape), "bits", bits)
+    cache = torch.zeros((H, p.T, p.C, d), dtype=torch.float32, device=DEV)
+    rec = qvg.compress(x.to(DEV), p, init_idx=idx, cache_out=cache)
+    out = qvg.decompress(rec, p)
+    torch.cuda.synchronize()
+    ref = oracle.compress(to_oracle(x), C=p.C, T=p.T, iters=p.iters, bits=p.bits, G=p.group,
+                          init_idx=idx, threads=min(H, _threads()))
+    bad = rec_equal(rec, ref)
+    assert not bad, f"record fields differ from the oracle: {bad}"
+    assert np.array_equal(cache.cpu().numpy(), ref["cache"])
+    ref_out = oracle.decompress(ref["codes"], ref["scales"], ref["assign"], ref["cent"], p.bits,
+                                p.group, threads=_threads())
+    got = bits16(out)
+    assert np.array_equal(got, ref_out), mismatch_report(got, ref_out)
+
+
+def test_decode_record_full_size():
+    H, N, d, T, C, bits, G = 40, 262144, 128, 4, 256, 2, 64
+    codes, scales, assign, cent = synth.random_record(4, H, N, d, T, C, bits, G)
+    p = qvg.params(C=C, T=T, iters=1, bits=bits, group=G)
+    rec = qvg.Record(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                     torch.from_numpy(assign).to(DEV), cent.to(DEV))
+    say("decode-side record", (H, N, d), "T", T)
+    out = qvg.decompress(rec, p, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    got = bits16(out)
+    del out, rec
+    ref = oracle.decompress(codes, scales, assign, to_oracle(cent), bits, G, out_bf16=True,
+                            threads=_threads())
+    assert np.array_equal(got, ref), mismatch_report(got, ref)
