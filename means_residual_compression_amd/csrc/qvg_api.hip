@@ -37,7 +37,7 @@ size_t up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 // Workspace layout shared by the size query and the carve-up.
 struct Layout {
   size_t rt, tb, cent, ctab, cinit, cbnd, stats, recheck, fallback, counters, sorted, offs, hist,
-      cofs, chunk_j, part, idx;
+      cofs, chunk_j, part, pflag, idx;
   size_t total;
 };
 
@@ -64,6 +64,7 @@ Layout make_layout(int64_t H, int64_t N, int64_t d, int64_t C, int64_t T, bool n
   L.cofs = take((size_t)(H * (Cp + 1) * 4));
   L.chunk_j = take((size_t)(H * max_chunks((int)N, (int)Cp) * 4));
   L.part = take((size_t)(H * max_chunks((int)N, (int)Cp) * d * 8));
+  L.pflag = take((size_t)(H * max_chunks((int)N, (int)Cp) * d * 4));
   L.idx = take(need_idx ? (size_t)(H * T * C * 4) : 0);
   L.total = o;
   return L;
@@ -88,6 +89,7 @@ Ws carve(void *ws, const Layout &L) {
   w.cofs = (int32_t *)(b + L.cofs);
   w.chunk_j = (int32_t *)(b + L.chunk_j);
   w.part = (double *)(b + L.part);
+  w.pflag = (uint32_t *)(b + L.pflag);
   w.idx = (int32_t *)(b + L.idx);
   return w;
 }
@@ -368,6 +370,7 @@ size_t qvg_update_workspace_size(int64_t H, int64_t N, int64_t d, int32_t C) {
   o = up(o + (size_t)(H * (C + 1) * 4));                                        // cofs
   o = up(o + (size_t)(H * max_chunks((int)N, C) * 4));                           // chunk_j
   o = up(o + (size_t)(H * max_chunks((int)N, C) * d * 8));                       // part
+  o = up(o + (size_t)(H * max_chunks((int)N, C) * d * 4));                       // pflag
   return o;
 }
 
@@ -391,7 +394,8 @@ qvg_status qvg_kmeans_update(const void *r, qvg_dtype dtype, int64_t H, int64_t 
   w.hist = (uint32_t *)(b + o); o = up(o + (size_t)(H * ((N + kSortChunk - 1) / kSortChunk) * kMaxC * 4));
   w.cofs = (int32_t *)(b + o); o = up(o + (size_t)(H * (C + 1) * 4));
   w.chunk_j = (int32_t *)(b + o); o = up(o + (size_t)(H * max_chunks((int)N, C) * 4));
-  w.part = (double *)(b + o);
+  w.part = (double *)(b + o); o = up(o + (size_t)(H * max_chunks((int)N, C) * d * 8));
+  w.pflag = (uint32_t *)(b + o);
   w.cent = centroids;
   KmArgs a;
   a.H = (int)H; a.N = (int)N; a.C = C; a.Cp = C; a.NT = 0;

@@ -48,7 +48,8 @@ struct Ws {
   uint32_t *hist;     // [H][ceil(N/kSortChunk)][256] per-chunk cluster counts
   int32_t *cofs;      // [H][Cp+1] first member-chunk of each cluster
   int32_t *chunk_j;   // [H][max_chunks] cluster of each member-chunk
-  double *part;       // [H][max_chunks][d] fp64 partial sums of member-chunks
+  double *part;
+  uint32_t *pflag;   // [H][maxch][D] per chunk and channel: max exponent | min lowest-bit << 16       // [H][max_chunks][d] fp64 partial sums of member-chunks
   int32_t *idx;       // [H][T][C] device copy of the seeded init indices
 };
 

@@ -17,10 +17,13 @@
 // The fp64 distances are computed exactly as a plain channel-order sum, so the
 // result is the exact argmin with ties to the smallest index.
 //
-// Update: tokens are grouped by cluster with a stable counting sort (one
-// workgroup per head), then one wave per cluster sums its members' rows in
-// token order in fp64 and divides: the mean is the same fp64 token-order sum
-// as a sequential loop.
+// Update: tokens are grouped by cluster with a stable counting sort, each
+// cluster's members (token order) are summed in fp64 in chunks of 64 and the
+// chunk sums added in chunk order.  Alongside, every chunk records per channel
+// the largest exponent and a lower bound on the lowest set bit of its values;
+// when those show that some partial sum of the cluster could round, the
+// cluster is summed again in one sequential token-order pass.  Either way the
+// sum equals the sequential fp64 sum of a plain loop.
 #include "qvg_common.h"
 #include "qvg_internal.h"
 
@@ -786,17 +789,33 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ass
 // rows in token order in fp64 (lanes over channels; all member rows in flight
 // at once).  k_finalize: one wave per cluster adds its chunk sums in chunk
 // order, divides in fp64 and rounds to fp32 (an empty cluster keeps its
-// centroid); this equals a single sequential fp64 sum whenever the fp64 sums
-// are exact, as they are for bf16 inputs.  It then emits the centroid's
-// tables for the next assign and, on the stage's last iteration, the record
-// centroid (rounded to the record dtype) and the fp32 cache entry.
+// centroid).  Exactness: every value is an integer multiple of 2^(lmin-150)
+// and smaller than 2^(emax-126) in magnitude (lmin = exponent field + trailing
+// zeros of the significand, a lower bound for subnormals; emax = largest
+// exponent field; zeros excluded), so for n members every partial sum, in any
+// order, is a multiple of 2^(lmin-150) below n*2^(emax-126); when
+// emax - lmin + ceil(log2 n) <= 29 all of them fit in 53 bits and the chunked
+// sum is the sequential one.  Otherwise the wave re-sums the cluster in one
+// token-order pass.  It then emits the centroid's tables for the next assign
+// and, on the stage's last iteration, the record centroid (rounded to the
+// record dtype) and the fp32 cache entry.
+
+// Exponent field and lowest-bit bound of an fp32 value (0xFFFF for zeros).
+__device__ __forceinline__ void exact_span(float v, uint32_t &emax, uint32_t &lmin) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t e = (b >> 23) & 0xFFu;
+  const uint32_t l = e + (uint32_t)__builtin_ctz(b | 0x800000u);
+  emax = max(emax, e);
+  lmin = min(lmin, v != 0.0f ? l : 0xFFFFu);
+}
 template <typename Tin, int D, int NSUB>
 __global__ __launch_bounds__(256) void k_chunk_sum(ResView<Tin> rv, int Cp,
                                                    const int32_t *__restrict__ sorted,
                                                    const int32_t *__restrict__ offs,
                                                    const int32_t *__restrict__ cofs,
                                                    const int32_t *__restrict__ chunk_j,
-                                                   int maxch, double *__restrict__ part) {
+                                                   int maxch, double *__restrict__ part,
+                                                   uint32_t *__restrict__ pflag) {
   constexpr int PER = D / 64, HB = kAccChunk / 2;
   const int h = blockIdx.y;
   const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -819,8 +838,9 @@ __global__ __launch_bounds__(256) void k_chunk_sum(ResView<Tin> rv, int Cp,
   for (int st = 0; st < NSUB; ++st) pj[st] = rv.stage_j(h, st, id);
   const Tin *xh = rv.x + (int64_t)h * N * D + lane * PER;
   double s[PER];
+  uint32_t emax[PER], lmin[PER];
 #pragma unroll
-  for (int m = 0; m < PER; ++m) s[m] = 0.0;
+  for (int m = 0; m < PER; ++m) s[m] = 0.0, emax[m] = 0, lmin[m] = 0xFFFFu;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     float v[HB][PER];
@@ -841,15 +861,23 @@ __global__ __launch_bounds__(256) void k_chunk_sum(ResView<Tin> rv, int Cp,
     for (int u = 0; u < HB; ++u)
       if (half * HB + u < cnt)
 #pragma unroll
-        for (int m = 0; m < PER; ++m) s[m] = __dadd_rn(s[m], (double)v[u][m]);
+        for (int m = 0; m < PER; ++m) {
+          s[m] = __dadd_rn(s[m], (double)v[u][m]);
+          exact_span(v[u][m], emax[m], lmin[m]);
+        }
   }
   double *dst = part + ((int64_t)h * maxch + g) * D + lane * PER;
+  uint32_t *fl = pflag + ((int64_t)h * maxch + g) * D + lane * PER;
 #pragma unroll
-  for (int m = 0; m < PER; ++m) dst[m] = s[m];
+  for (int m = 0; m < PER; ++m) {
+    dst[m] = s[m];
+    fl[m] = emax[m] | (lmin[m] << 16);
+  }
 }
 
-template <typename Tc, int D>
+template <typename Tin, typename Tc, int D>
 __global__ __launch_bounds__(256) void k_finalize(
+    ResView<Tin> rv, const int32_t *__restrict__ sorted, const uint32_t *__restrict__ pflag,
     int C, int Cp, const int32_t *__restrict__ offs, const int32_t *__restrict__ cofs, int maxch,
     const double *__restrict__ part, float *__restrict__ cent, const uint32_t *stats,
     uint32_t *stats_w, int stat_stride, int bslot, half8 *__restrict__ ctab,
@@ -869,20 +897,57 @@ __global__ __launch_bounds__(256) void k_finalize(
   const int c0 = __builtin_amdgcn_readfirstlane(cofs[(int64_t)h * (Cp + 1) + j]);
   const int nch = __builtin_amdgcn_readfirstlane(cofs[(int64_t)h * (Cp + 1) + j + 1]) - c0;
   const double *ph = part + ((int64_t)h * maxch + c0) * D + lane * PER;
+  const uint32_t *pf = pflag + ((int64_t)h * maxch + c0) * D + lane * PER;
   double s[PER];
+  int emax[PER], lmin[PER];
 #pragma unroll
-  for (int m = 0; m < PER; ++m) s[m] = 0.0;
+  for (int m = 0; m < PER; ++m) s[m] = 0.0, emax[m] = 0, lmin[m] = 0xFFFF;
   for (int q = 0; q < nch; q += 8) {
     double v[8][PER];
+    uint32_t f[8][PER];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int m = 0; m < PER; ++m) v[u][m] = ph[(int64_t)min(q + u, nch - 1) * D + m];
+      for (int m = 0; m < PER; ++m) {
+        v[u][m] = ph[(int64_t)min(q + u, nch - 1) * D + m];
+        f[u][m] = pf[(int64_t)min(q + u, nch - 1) * D + m];
+      }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (q + u < nch)
 #pragma unroll
-        for (int m = 0; m < PER; ++m) s[m] = __dadd_rn(s[m], v[u][m]);
+        for (int m = 0; m < PER; ++m) {
+          s[m] = __dadd_rn(s[m], v[u][m]);
+          emax[m] = max(emax[m], (int)(f[u][m] & 0xFFFFu));
+          lmin[m] = min(lmin[m], (int)(f[u][m] >> 16));
+        }
+  }
+  // Some partial sum might round: sum the cluster again, sequentially in
+  // token order (rare; members are read 32 at a time, added one by one).
+  const int lg = n > 1 ? 32 - __builtin_clz((uint32_t)(n - 1)) : 0;
+  bool risky = false;
+#pragma unroll
+  for (int m = 0; m < PER; ++m) risky |= emax[m] - lmin[m] + lg > 29;
+  if (__ballot(risky)) {
+    const int o0 = __builtin_amdgcn_readfirstlane(offs[(int64_t)h * (Cp + 1) + j]);
+    const int32_t *ids = sorted + (int64_t)h * rv.N + o0;
+#pragma unroll
+    for (int m = 0; m < PER; ++m) s[m] = 0.0;
+    for (int q = 0; q < n; q += 32) {
+      const int32_t myid = ids[min(q + (lane & 31), n - 1)];
+      float v[32][PER];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int64_t row = __builtin_amdgcn_readlane(myid, u);
+#pragma unroll
+        for (int m = 0; m < PER; ++m) v[u][m] = rv.get(h, row, lane * PER + m);
+      }
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+        if (q + u < n)
+#pragma unroll
+          for (int m = 0; m < PER; ++m) s[m] = __dadd_rn(s[m], (double)v[u][m]);
+    }
   }
   float *cj = cent + ((int64_t)h * Cp + j) * D + lane * PER;
   float cv[PER];
@@ -1052,7 +1117,8 @@ bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int6
     const dim3 gcs((maxch + 3) / 4, a.H);
 #define QVG_CS(NS)                                                                           \
   hipLaunchKernelGGL((k_chunk_sum<Tin, D, NS>), gcs, dim3(256), 0, s, view_of<Tin>(a, D), a.Cp, \
-                     a.ws.sorted, a.ws.offs, a.ws.cofs, a.ws.chunk_j, maxch, a.ws.part)
+                     a.ws.sorted, a.ws.offs, a.ws.cofs, a.ws.chunk_j, maxch, a.ws.part,      \
+                     a.ws.pflag)
     switch (a.nsub) {
       case 0: QVG_CS(0); break;
       case 1: QVG_CS(1); break;
@@ -1065,8 +1131,8 @@ bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int6
     }
 #undef QVG_CS
     QVG_CHECK_LAUNCH();
-    hipLaunchKernelGGL((k_finalize<Tc, D>), dim3((a.Cp + 3) / 4, a.H), dim3(256), 0, s, a.C,
-                       a.Cp, a.ws.offs, a.ws.cofs, maxch, a.ws.part, a.ws.cent, a.ws_stats,
+    hipLaunchKernelGGL((k_finalize<Tin, Tc, D>), dim3((a.Cp + 3) / 4, a.H), dim3(256), 0, s,
+                       view_of<Tin>(a, D), a.ws.sorted, a.ws.pflag, a.C, a.Cp, a.ws.offs, a.ws.cofs, maxch, a.ws.part, a.ws.cent, a.ws_stats,
                        a.ws_stats, a.stat_stride, next_bslot, tables ? a.ws.ctab : nullptr,
                        a.ws.cinit, a.ws.cbnd, rec_c, rec_hstride, cache, cache_hstride);
     QVG_CHECK_LAUNCH();
