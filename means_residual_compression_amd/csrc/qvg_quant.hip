@@ -70,47 +70,69 @@ __device__ __forceinline__ int floor_half(float u) {
 }
 
 // Quantizes the residual R(T) = x - C(1)[pi(1)] - ... - C(T)[pi(T)] (the
-// view's nsub = T), recomputed from the input and the record.
+// view's nsub = T), recomputed from the input and the record.  A lane covers
+// 8 channels of QU tokens: the stage indices of all QU tokens are loaded
+// first, then their input rows and centroid rows, so each wave has QU
+// independent chains of loads in flight.  Per group of G channels (G/8
+// adjacent lanes): a = max |r|, s = a / (2^b - 1) (IEEE division), E4M3
+// scale, codes floor(u / 2) + 2^(b-1) with u = r / s_hat, clamped.
+constexpr int QU = 4;
 template <typename T, int BITS, int NSUB>
-__global__ void k_quant(ResView<T> rv, int G, uint8_t *__restrict__ codes,
-                        uint8_t *__restrict__ scales) {
+__global__ __launch_bounds__(256) void k_quant(ResView<T> rv, int G, uint8_t *__restrict__ codes,
+                                               uint8_t *__restrict__ scales) {
   constexpr int L = (1 << BITS) - 1, MID = 1 << (BITS - 1);
   const int h = blockIdx.y;
   const int N = rv.N, D = rv.D;
   const int lpt = D / 8, lpg = G / 8;
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const bool live = g < (int64_t)N * lpt;
-  const int64_t i = live ? g / lpt : 0;
-  const int q = (int)(g % lpt);
-  float v[8];
-  if (live) {
-    rv.template load8_n<NSUB>(h, i, q * 8, v);
-  } else {
+  const int tpb = (int)blockDim.x / lpt;  // tokens per block and slot
+  const int q = (int)threadIdx.x % lpt;
+  const int64_t t0 = (int64_t)blockIdx.x * tpb * QU + threadIdx.x / lpt;
+  int64_t tok[QU];
+  int js[QU][NSUB > 0 ? NSUB : 1];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = 0.0f;
-  }
-  float a = 0.0f;
+  for (int u = 0; u < QU; ++u) {
+    tok[u] = t0 + (int64_t)u * tpb;
+    const int64_t i = min(tok[u], (int64_t)N - 1);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(v[k]));
-  for (int o = 1; o < lpg; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
-  const float s = a / (float)L;
-  const uint32_t e = e4m3_encode(s);
-  const float sh = e4m3_decode(e);
-  uint32_t packed = 0;
+    for (int st = 0; st < NSUB; ++st) js[u][st] = rv.stage_j(h, st, i);
+  }
+  float v[QU][8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    int c = MID;
-    if (sh != 0.0f) c = min(max(floor_half(v[k] / sh) + MID, 0), L);
-    packed |= (uint32_t)c << (BITS * k);
+  for (int u = 0; u < QU; ++u) load8(rv.x, ((int64_t)h * N + min(tok[u], (int64_t)N - 1)) * D + q * 8, v[u]);
+  float c[QU][NSUB > 0 ? NSUB : 1][8];
+#pragma unroll
+  for (int u = 0; u < QU; ++u)
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st) load8(rv.stage_row(h, st, js[u][st]), q * 8, c[u][st]);
+#pragma unroll
+  for (int u = 0; u < QU; ++u) {
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st)  // R(t) = x - C(1)[pi(1)] - ... in stage order
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[u][k] = v[u][k] - c[u][st][k];
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(v[u][k]));
+    for (int o = 1; o < lpg; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
+    const float sc = a / (float)L;
+    const uint32_t e = e4m3_encode(sc);
+    const float sh = e4m3_decode(e);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      int cd = MID;
+      if (sh != 0.0f) cd = min(max(floor_half(v[u][k] / sh) + MID, 0), L);
+      packed |= (uint32_t)cd << (BITS * k);
+    }
+    if (tok[u] >= N) continue;
+    const int64_t row = (int64_t)h * N + tok[u];
+    if (BITS == 2) {
+      reinterpret_cast<uint16_t *>(codes + row * (D / 4))[q] = (uint16_t)packed;
+    } else {
+      reinterpret_cast<uint32_t *>(codes + row * (D / 2))[q] = packed;
+    }
+    if (q % lpg == 0) scales[row * (D / G) + q / lpg] = (uint8_t)e;
   }
-  if (!live) return;
-  const int64_t row = (int64_t)h * N + i;
-  if (BITS == 2) {
-    reinterpret_cast<uint16_t *>(codes + row * (D / 4))[q] = (uint16_t)packed;
-  } else {
-    reinterpret_cast<uint32_t *>(codes + row * (D / 2))[q] = packed;
-  }
-  if (q % lpg == 0) scales[row * (D / G) + q / lpg] = (uint8_t)e;
 }
 
 // ------------------------------------------------------------- dequant
@@ -417,8 +439,8 @@ static void launch_quant_t(const void *x, int H, int N, int D, int C, const uint
   rv.C = C;
   rv.Ts = Ts;
   rv.nsub = nsub;
-  const int64_t threads = (int64_t)N * (D / 8);
-  dim3 grid((unsigned)((threads + 255) / 256), H);
+  const int tpb = 256 / (D / 8);  // tokens per block and slot
+  dim3 grid((unsigned)(((int64_t)N + (int64_t)tpb * QU - 1) / ((int64_t)tpb * QU)), H);
   dispatch_nsub(nsub, [&]<int NS>() {
     if (bits == 2)
       hipLaunchKernelGGL((k_quant<T, 2, NS>), grid, dim3(256), 0, s, rv, G, codes, scales);
