@@ -786,9 +786,10 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ass
 // ---------------------------------------------------------- accumulate
 // The members of each cluster (token order, from the counting sort) are cut
 // into chunks of kAccChunk.  k_chunk_sum: one wave per chunk sums its members'
-// rows in token order in fp64 (lanes over channels; all member rows in flight
-// at once).  k_finalize: one wave per cluster adds its chunk sums in chunk
-// order, divides in fp64 and rounds to fp32 (an empty cluster keeps its
+// rows in fp64 (a lane takes 8 channels of every (64/(D/8))-th member; the
+// lane groups are combined at the end).  k_finalize: one wave per cluster
+// adds its chunk sums in chunk order, divides in fp64 and rounds to fp32 (an
+// empty cluster keeps its
 // centroid).  Exactness: every value is an integer multiple of 2^(lmin-150)
 // and smaller than 2^(emax-126) in magnitude (lmin = exponent field + trailing
 // zeros of the significand, a lower bound for subnormals; emax = largest
@@ -816,7 +817,10 @@ __global__ __launch_bounds__(256) void k_chunk_sum(ResView<Tin> rv, int Cp,
                                                    const int32_t *__restrict__ chunk_j,
                                                    int maxch, double *__restrict__ part,
                                                    uint32_t *__restrict__ pflag) {
-  constexpr int PER = D / 64, HB = kAccChunk / 2;
+  constexpr int LPR = D / 8;              // lanes per member row (8 channels each)
+  constexpr int RPI = 64 / LPR;           // member rows per load instruction
+  constexpr int MPL = kAccChunk / RPI;    // members per lane
+  constexpr int MB = 4;                   // members per lane in flight
   const int h = blockIdx.y;
   const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -830,48 +834,62 @@ __global__ __launch_bounds__(256) void k_chunk_sum(ResView<Tin> rv, int Cp,
   const int cnt = min(kAccChunk, o1 - start);
   const int N = rv.N;
   // lane u holds member u's token id and its cluster in every earlier stage
-  // (NSUB = the stage index, a template parameter so the member loop below
-  // has no branches and all its loads are issued back to back)
+  // (NSUB = the stage index, a template parameter, so the loads below are
+  // issued without branches)
   const int32_t id = sorted[(int64_t)h * N + start + min(lane, cnt - 1)];
   int pj[NSUB > 0 ? NSUB : 1];
 #pragma unroll
   for (int st = 0; st < NSUB; ++st) pj[st] = rv.stage_j(h, st, id);
-  const Tin *xh = rv.x + (int64_t)h * N * D + lane * PER;
-  double s[PER];
-  uint32_t emax[PER], lmin[PER];
+  // this lane: channels q*8 .. q*8+7 of members sub, sub + RPI, ...
+  const int sub = lane / LPR, q = lane % LPR;
+  const Tin *xh = rv.x + (int64_t)h * N * D + q * 8;
+  double s[8];
+  uint32_t emax[8], lmin[8];
 #pragma unroll
-  for (int m = 0; m < PER; ++m) s[m] = 0.0, emax[m] = 0, lmin[m] = 0xFFFFu;
+  for (int e = 0; e < 8; ++e) s[e] = 0.0, emax[e] = 0, lmin[e] = 0xFFFFu;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    float v[HB][PER];
+  for (int k0 = 0; k0 < MPL; k0 += MB) {
+    float v[MB][8];
 #pragma unroll
-    for (int u = 0; u < HB; ++u) {
-      const int src = min(half * HB + u, cnt - 1);
-      const int64_t row = __builtin_amdgcn_readlane(id, src);
-#pragma unroll
-      for (int m = 0; m < PER; ++m) v[u][m] = Elem<Tin>::get(xh, row * D + m);
+    for (int k = 0; k < MB; ++k) {
+      const int src = min(sub + RPI * (k0 + k), cnt - 1);
+      const int64_t row = __shfl(id, src);
+      load8(xh, row * D, v[k]);
 #pragma unroll
       for (int st = 0; st < NSUB; ++st) {  // R(t) = x - C(1)[pi(1)] - ... in stage order
-        const Tin *c = rv.stage_row(h, st, __builtin_amdgcn_readlane(pj[st], src)) + lane * PER;
+        float c[8];
+        load8(rv.stage_row(h, st, __shfl(pj[st], src)), q * 8, c);
 #pragma unroll
-        for (int m = 0; m < PER; ++m) v[u][m] = v[u][m] - Elem<Tin>::get(c, m);
+        for (int e = 0; e < 8; ++e) v[k][e] = v[k][e] - c[e];
       }
     }
 #pragma unroll
-    for (int u = 0; u < HB; ++u)
-      if (half * HB + u < cnt)
+    for (int k = 0; k < MB; ++k)
+      if (sub + RPI * (k0 + k) < cnt)
 #pragma unroll
-        for (int m = 0; m < PER; ++m) {
-          s[m] = __dadd_rn(s[m], (double)v[u][m]);
-          exact_span(v[u][m], emax[m], lmin[m]);
+        for (int e = 0; e < 8; ++e) {
+          s[e] = __dadd_rn(s[e], (double)v[k][e]);
+          exact_span(v[k][e], emax[e], lmin[e]);
         }
   }
-  double *dst = part + ((int64_t)h * maxch + g) * D + lane * PER;
-  uint32_t *fl = pflag + ((int64_t)h * maxch + g) * D + lane * PER;
+  // combine the RPI member slots (in any order: the finalize pass only uses
+  // these sums when the spans prove every partial sum exact)
 #pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    dst[m] = s[m];
-    fl[m] = emax[m] | (lmin[m] << 16);
+  for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s[e] = __dadd_rn(s[e], __shfl_xor(s[e], off));
+      emax[e] = max(emax[e], (uint32_t)__shfl_xor((int)emax[e], off));
+      lmin[e] = min(lmin[e], (uint32_t)__shfl_xor((int)lmin[e], off));
+    }
+  if (sub == 0) {
+    double *dst = part + ((int64_t)h * maxch + g) * D + q * 8;
+    uint32_t *fl = pflag + ((int64_t)h * maxch + g) * D + q * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      dst[e] = s[e];
+      fl[e] = emax[e] | (lmin[e] << 16);
+    }
   }
 }
 
