@@ -114,16 +114,24 @@ def dequant_bytes(H, N, d, C, T, bits, G, out_bytes=2, c_bytes=2):
 
 
 def timed(step, steps, warmup):
+    """Wall time per step of `steps` steps after `warmup` untimed ones, with
+    no per-kernel events inside the timed region (each event pair costs a
+    few microseconds of GPU time), followed by a second pass of `steps`
+    steps with HIP events recorded around every library launch on its
+    stream, which gives the per-kernel durations (kernel_times)."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    qvg.timing_reset()
-    qvg.timing_enable(True)
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    qvg.timing_reset()
+    qvg.timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
     qvg.timing_enable(False)
     return (t1 - t0) * 1e3 / steps
 

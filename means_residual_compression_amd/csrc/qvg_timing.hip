@@ -25,7 +25,9 @@ size_t g_used = 0;
 hipEvent_t take_event() {
   if (g_used == g_pool.size()) {
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    // timing-only events: no system-scope fence (cache write-back and
+    // invalidate) when they are recorded, so they barely perturb the work
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     g_pool.push_back(e);
   }
   return g_pool[g_used++];
