@@ -490,10 +490,10 @@ __device__ __forceinline__ double order_tol() {
 // fp64 partial sums combined by a fixed butterfly; the sequential fp64 replica
 // decides only when the margin is too thin to settle the order.
 template <typename Tin, int D>
-__global__ __launch_bounds__(256) void k_recheck(ResView<Tin> rv, const float *__restrict__ cent,
-                          int Cp, const int4 *__restrict__ list,
-                          const uint32_t *__restrict__ counters, uint8_t *__restrict__ assign,
-                          int64_t assign_hstride) {
+__device__ __forceinline__ void recheck_part(const ResView<Tin> &rv, const float *__restrict__ cent,
+                                             int Cp, const int4 *__restrict__ list,
+                                             const uint32_t *__restrict__ counters,
+                                             uint8_t *__restrict__ assign, int64_t assign_hstride) {
   constexpr int LPE = D / 8, EPW = 64 / LPE;
   const uint32_t n = counters[0];
   const int lane = threadIdx.x & 63, sub = lane / LPE, li = lane % LPE;
@@ -548,12 +548,12 @@ __global__ __launch_bounds__(256) void k_recheck(ResView<Tin> rv, const float *_
 // same arithmetic as a plain loop.  Smallest distance wins, ties to the
 // smallest index.
 template <typename Tin, int D>
-__global__ __launch_bounds__(256) void k_fallback(ResView<Tin> rv,
-                                                  const float *__restrict__ cent, int C, int Cp,
-                                                  const int2 *__restrict__ list,
-                                                  const uint32_t *__restrict__ counters,
-                                                  uint8_t *__restrict__ assign,
-                                                  int64_t assign_hstride) {
+__device__ __forceinline__ void fallback_part(const ResView<Tin> &rv,
+                                              const float *__restrict__ cent, int C, int Cp,
+                                              const int2 *__restrict__ list,
+                                              const uint32_t *__restrict__ counters,
+                                              uint8_t *__restrict__ assign,
+                                              int64_t assign_hstride) {
   constexpr int D4 = D / 4, HB = D4 / 2;
   __shared__ float4 rs[D4];
   __shared__ double wbest[4];
@@ -650,6 +650,21 @@ __global__ __launch_bounds__(256) void k_fallback(ResView<Tin> rv,
     if (t == 0) assign[(int64_t)q.x * assign_hstride + q.y] = (uint8_t)bj;
     __syncthreads();
   }
+}
+
+// Both kinds of unsettled tokens in one launch: re-checks of two candidates
+// (a wave per EPW entries, grid-stride), then exact scans (a workgroup per
+// entry, grid-stride).  Iterations with few or no candidates cost one small
+// launch.
+template <typename Tin, int D>
+__global__ __launch_bounds__(256) void k_resolve(ResView<Tin> rv, const float *__restrict__ cent,
+                                                 int C, int Cp, const int4 *__restrict__ rlist,
+                                                 const int2 *__restrict__ flist,
+                                                 const uint32_t *__restrict__ counters,
+                                                 uint8_t *__restrict__ assign,
+                                                 int64_t assign_hstride) {
+  recheck_part<Tin, D>(rv, cent, Cp, rlist, counters, assign, assign_hstride);
+  fallback_part<Tin, D>(rv, cent, C, Cp, flist, counters, assign, assign_hstride);
 }
 
 // --------------------------------------------------------------- sort
@@ -1101,15 +1116,10 @@ bool launch_assign(const KmArgs &a, int bslot, hipStream_t s) {
     QVG_CHECK_LAUNCH();
   }
   {
-    TimerScope ts_("kmeans_recheck", s);
-    hipLaunchKernelGGL((k_recheck<Tin, D>), dim3(1024), dim3(256), 0, s, rv, a.ws.cent, a.Cp,
-                       a.ws.recheck, a.ws.counters, a.assign, a.assign_hstride);
-    QVG_CHECK_LAUNCH();
-  }
-  {
-    TimerScope ts_("kmeans_fallback", s);
-    hipLaunchKernelGGL((k_fallback<Tin, D>), dim3(2048), dim3(256), 0, s, rv, a.ws.cent, a.C,
-                       a.Cp, a.ws.fallback, a.ws.counters, a.assign, a.assign_hstride);
+    TimerScope ts_("kmeans_resolve", s);
+    hipLaunchKernelGGL((k_resolve<Tin, D>), dim3(1024), dim3(256), 0, s, rv, a.ws.cent, a.C,
+                       a.Cp, a.ws.recheck, a.ws.fallback, a.ws.counters, a.assign,
+                       a.assign_hstride);
     QVG_CHECK_LAUNCH();
   }
   return true;
