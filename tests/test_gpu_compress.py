@@ -145,3 +145,21 @@ def test_self_forcing_cache_full_size():
     idx = synth.init_indices(1, x.shape[0], p.T, x.shape[1], p.C)
     say("self-forcing full size", tuple(x.shape))
     _check(*_run_both(x, p, idx))
+
+
+def test_centroid_sums_that_can_round():
+    """bf16 data whose channels mix magnitudes ~2^15 with values ~2^-40 (more
+    than 45 binades apart): chunked fp64 partial sums could round, so the
+    update proves nothing and re-sums those clusters in token order; the
+    record must still equal the oracle's (fp64 token-order sums)."""
+    rng = np.random.default_rng(9)
+    H, N, d, C = 2, 3000, 128, 8
+    x = rng.standard_normal((H, N, d))
+    x[:, :, :16] *= 2.0 ** 15
+    tiny = rng.random((H, N, d)) < 0.3
+    x[tiny] = rng.standard_normal(int(tiny.sum())) * 2.0 ** -40
+    x = synth.round_to(x, torch.bfloat16)
+    p = qvg.params(C=C, T=2, iters=3, bits=2, group=64)
+    idx = synth.init_indices(900, H, p.T, N, p.C)
+    say("centroid sums that can round", tuple(x.shape))
+    _check(*_run_both(x, p, idx))
