@@ -37,7 +37,7 @@ size_t up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 // Workspace layout shared by the size query and the carve-up.
 struct Layout {
   size_t rt, tb, cent, ctab, cinit, cbnd, stats, recheck, fallback, counters, sorted, offs, hist,
-      cofs, chunk_j, part, pflag, idx;
+      cofs, chunk_j, part, pflag, stage_re, stage_fb, idx;
   size_t total;
 };
 
@@ -65,6 +65,8 @@ Layout make_layout(int64_t H, int64_t N, int64_t d, int64_t C, int64_t T, bool n
   L.chunk_j = take((size_t)(H * max_chunks((int)N, (int)Cp) * 4));
   L.part = take((size_t)(H * max_chunks((int)N, (int)Cp) * d * 8));
   L.pflag = take((size_t)(H * max_chunks((int)N, (int)Cp) * d * 4));
+  L.stage_re = take((size_t)(H * (NT + 15) * kTile * 16));
+  L.stage_fb = take((size_t)(H * (NT + 15) * kTile * 8));
   L.idx = take(need_idx ? (size_t)(H * T * C * 4) : 0);
   L.total = o;
   return L;
@@ -90,6 +92,8 @@ Ws carve(void *ws, const Layout &L) {
   w.chunk_j = (int32_t *)(b + L.chunk_j);
   w.part = (double *)(b + L.part);
   w.pflag = (uint32_t *)(b + L.pflag);
+  w.stage_re = (int4 *)(b + L.stage_re);
+  w.stage_fb = (int2 *)(b + L.stage_fb);
   w.idx = (int32_t *)(b + L.idx);
   return w;
 }

@@ -48,8 +48,10 @@ struct Ws {
   uint32_t *hist;     // [H][ceil(N/kSortChunk)][256] per-chunk cluster counts
   int32_t *cofs;      // [H][Cp+1] first member-chunk of each cluster
   int32_t *chunk_j;   // [H][max_chunks] cluster of each member-chunk
-  double *part;
-  uint32_t *pflag;   // [H][maxch][D] per chunk and channel: max exponent | min lowest-bit << 16       // [H][max_chunks][d] fp64 partial sums of member-chunks
+  double *part;       // [H][max_chunks][d] fp64 partial sums of member-chunks
+  uint32_t *pflag;    // [H][max_chunks][d] per chunk and channel: max exponent | min lowest-bit << 16
+  int4 *stage_re;     // [H*(NT+15)*32] recheck entries staged per assign workgroup
+  int2 *stage_fb;     // [H*(NT+15)*32] fallback entries staged per assign workgroup
   int32_t *idx;       // [H][T][C] device copy of the seeded init indices
 };
 

@@ -301,7 +301,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const uint32_t *__restrict__ stats, int stat_stride, int bslot, int N, int NT, int CB,
     int groups_per_head, int total_groups, int groups_per_wg, uint8_t *__restrict__ assign,
     int64_t assign_hstride, int4 *__restrict__ recheck, int2 *__restrict__ fallback,
-    uint32_t *__restrict__ counters, float kappa) {
+    int4 *__restrict__ stage_re, int2 *__restrict__ stage_fb, uint32_t *__restrict__ counters,
+    float kappa) {
   constexpr int KC = D / 16;
   constexpr int TPG = 16;  // tiles per work item
   extern __shared__ __align__(16) unsigned char smem[];
@@ -309,6 +310,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   float *cinit_s = reinterpret_cast<float *>(smem + (size_t)CB * KC * 64 * sizeof(half8));
   float4 *cbnd_s = reinterpret_cast<float4 *>(cinit_s + CB * 32);
   __shared__ float4 hmax_s;
+  // unsettled tokens are staged in this workgroup's segment of stage_re /
+  // stage_fb (slots from LDS counters) and copied to the compact lists once
+  // at the end, with one global atomic per list
+  __shared__ uint32_t lcnt[2], gbase[2];
+  if (threadIdx.x == 0) lcnt[0] = lcnt[1] = 0u;  // read after the first barrier
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5;
   const uint32_t halfbits = (uint32_t)half << 2;
@@ -323,6 +329,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   int cached_h = -1;
   const int g_lo = blockIdx.x * groups_per_wg;
   const int g_hi = min(total_groups, g_lo + groups_per_wg);
+  const int64_t seg = (int64_t)g_lo * TPG * kTile;  // this workgroup's staging segment
   for (int g = g_lo; g < g_hi; ++g) {
     const int h = g / groups_per_head;
     const int tile_lo = (g % groups_per_head) * TPG;
@@ -438,7 +445,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         kind = g13 > e1 + eg ? 1 : 2;
       }
     }
-    // list appends: one atomic per wave and list, slots from mbcnt
+    // staged appends: one LDS atomic per wave and list, slots from mbcnt
     const uint64_t m_re = __ballot(kind == 1), m_fb = __ballot(kind == 2);
     const uint32_t lt_re = __builtin_amdgcn_mbcnt_hi((uint32_t)(m_re >> 32),
                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m_re, 0u));
@@ -446,14 +453,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m_fb, 0u));
     uint32_t base_re = 0, base_fb = 0;
     if (lane == 0) {
-      if (m_re) base_re = atomicAdd(counters + 0, (uint32_t)__popcll(m_re));
-      if (m_fb) base_fb = atomicAdd(counters + 1, (uint32_t)__popcll(m_fb));
+      if (m_re) base_re = atomicAdd(&lcnt[0], (uint32_t)__popcll(m_re));
+      if (m_fb) base_fb = atomicAdd(&lcnt[1], (uint32_t)__popcll(m_fb));
     }
     base_re = __shfl(base_re, 0);
     base_fb = __shfl(base_fb, 0);
-    if (kind == 1) recheck[base_re + lt_re] = make_int4(h, tok, j1, j2);
-    if (kind == 2) fallback[base_fb + lt_fb] = make_int2(h, tok);
+    if (kind == 1) stage_re[seg + base_re + lt_re] = make_int4(h, tok, j1, j2);
+    if (kind == 2) stage_fb[seg + base_fb + lt_fb] = make_int2(h, tok);
   }
+  // the workgroup's staged entries go to the compact lists
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    gbase[0] = lcnt[0] ? atomicAdd(counters + 0, lcnt[0]) : 0u;
+    gbase[1] = lcnt[1] ? atomicAdd(counters + 1, lcnt[1]) : 0u;
+  }
+  __syncthreads();
+  const uint32_t n_re = lcnt[0], n_fb = lcnt[1];
+  for (uint32_t q = threadIdx.x; q < n_re; q += blockDim.x) recheck[gbase[0] + q] = stage_re[seg + q];
+  for (uint32_t q = threadIdx.x; q < n_fb; q += blockDim.x) fallback[gbase[1] + q] = stage_fb[seg + q];
 }
 
 // ------------------------------------------------------------ resolve
@@ -1112,7 +1129,8 @@ bool launch_assign(const KmArgs &a, int bslot, hipStream_t s) {
     hipLaunchKernelGGL((k_assign<D>), dim3(grid), dim3(512), lds, s, a.ws.rt, a.ws.tb,
                        a.ws.ctab, a.ws.cinit, a.ws.cbnd, a.ws_stats, a.stat_stride, bslot, a.N,
                        a.NT, CB, groups_per_head, total, per_wg, a.assign, a.assign_hstride,
-                       a.ws.recheck, a.ws.fallback, a.ws.counters, a.kappa);
+                       a.ws.recheck, a.ws.fallback, a.ws.stage_re, a.ws.stage_fb, a.ws.counters,
+                       a.kappa);
     QVG_CHECK_LAUNCH();
   }
   {
