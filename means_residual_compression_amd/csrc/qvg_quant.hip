@@ -385,10 +385,26 @@ __global__ __launch_bounds__(1024) void k_dequant(const uint8_t *__restrict__ co
     // Control flow follows the wave's first token (uniform); lanes past the
     // end load clamped tokens and skip their stores.
     const uint32_t tl = ((uint32_t)lane >> lpt_log2) * U;
-    for (uint32_t rw = (uint32_t)(wave * step_w); rw < n; rw += step) {
-      Batch bt;
-      fetch(rw, rw + tl, bt);
-      emit(rw + tl, bt);
+    if constexpr (T >= 3) {
+      // long add chains: the next step's loads go out before this step's
+      // arithmetic and stores (past the end they re-read clamped tokens)
+      uint32_t rw = (uint32_t)(wave * step_w);
+      if (rw < n) {
+        Batch cur;
+        fetch(rw, rw + tl, cur);
+        for (; rw < n; rw += step) {
+          Batch nxt;
+          fetch(rw + step, rw + step + tl, nxt);
+          emit(rw + tl, cur);
+          cur = nxt;
+        }
+      }
+    } else {
+      for (uint32_t rw = (uint32_t)(wave * step_w); rw < n; rw += step) {
+        Batch bt;
+        fetch(rw, rw + tl, bt);
+        emit(rw + tl, bt);
+      }
     }
     seg = (int64_t)h * N + hi;
   }
