@@ -37,7 +37,7 @@ size_t up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 // Workspace layout shared by the size query and the carve-up.
 struct Layout {
   size_t rt, tb, cent, ctab, cinit, cbnd, stats, recheck, fallback, counters, sorted, offs, hist,
-      cofs, chunk_j, part, pflag, stage_re, stage_fb, idx;
+      cofs, chunk_j, part, pflag, stage_re, stage_fb, span, idx;
   size_t total;
 };
 
@@ -67,6 +67,7 @@ Layout make_layout(int64_t H, int64_t N, int64_t d, int64_t C, int64_t T, bool n
   L.pflag = take((size_t)(H * max_chunks((int)N, (int)Cp) * d * 4));
   L.stage_re = take((size_t)(H * (NT + 15) * kTile * 16));
   L.stage_fb = take((size_t)(H * (NT + 15) * kTile * 8));
+  L.span = take((size_t)(H * kSpanParts * d * 4));
   L.idx = take(need_idx ? (size_t)(H * T * C * 4) : 0);
   L.total = o;
   return L;
@@ -94,6 +95,7 @@ Ws carve(void *ws, const Layout &L) {
   w.pflag = (uint32_t *)(b + L.pflag);
   w.stage_re = (int4 *)(b + L.stage_re);
   w.stage_fb = (int2 *)(b + L.stage_fb);
+  w.span = (uint32_t *)(b + L.span);
   w.idx = (int32_t *)(b + L.idx);
   return w;
 }
@@ -187,10 +189,10 @@ qvg_status run_compress(const void *x, int64_t H, int64_t N, const qvg_params *p
       const int log_slot = t * iters + it;
       ok = in_bf16 ? launch_update<uint16_t, Tc, D>(a, next, !last, last ? rec_c : nullptr,
                                                     rec_hstride, last ? cache_t : nullptr,
-                                                    rec_hstride, log_slot, s)
+                                                    rec_hstride, log_slot, it == 0, s)
                    : launch_update<float, Tc, D>(a, next, !last, last ? rec_c : nullptr,
                                                  rec_hstride, last ? cache_t : nullptr,
-                                                 rec_hstride, log_slot, s);
+                                                 rec_hstride, log_slot, it == 0, s);
       if (!ok) return hip_fail("kmeans_update");
     }
   }
@@ -408,14 +410,16 @@ qvg_status qvg_kmeans_update(const void *r, qvg_dtype dtype, int64_t H, int64_t 
   a.assign = (uint8_t *)assign; a.assign_hstride = N; a.ws = w; a.ws_stats = w.stats;
   a.stat_stride = kStatWords; a.kappa = 0.0f;
   hipStream_t s = (hipStream_t)stream;
+  // cleared stats: the sums' spans are tracked per chunk (S_SPAN unset)
+  if (!launch_fill_u32(w.stats, H * kStatWords, s)) return hip_fail("fill");
   const bool bf = dtype == QVG_BF16;
   bool ok;
   if (d == 64)
-    ok = bf ? launch_update<uint16_t, float, 64>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, s)
-            : launch_update<float, float, 64>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, s);
+    ok = bf ? launch_update<uint16_t, float, 64>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, false, s)
+            : launch_update<float, float, 64>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, false, s);
   else
-    ok = bf ? launch_update<uint16_t, float, 128>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, s)
-            : launch_update<float, float, 128>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, s);
+    ok = bf ? launch_update<uint16_t, float, 128>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, false, s)
+            : launch_update<float, float, 128>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, false, s);
   return ok ? QVG_OK : hip_fail("kmeans_update");
 }
 

@@ -27,6 +27,9 @@ enum StatSlot : int {
   S_B0 = 2,      // bounds of the current centroid table, double-buffered:
                  // [2 + 4*p + 0] max ||c*sc||, [+1] max ||c*sc - fp16(c*sc)||,
                  // [+2] max ||fp16(c*sc)||, [+3] max ||c*sc||^2
+  S_SPAN = 10,   // exactness of the stage's centroid sums over the whole head:
+                 // bit 0 set once checked, bit 1 when some channel's span
+                 // leaves a partial sum of up to N members able to round
   kStatWords = 16,
 };
 
@@ -52,8 +55,11 @@ struct Ws {
   uint32_t *pflag;    // [H][max_chunks][d] per chunk and channel: max exponent | min lowest-bit << 16
   int4 *stage_re;     // [H*(NT+15)*32] recheck entries staged per assign workgroup
   int2 *stage_fb;     // [H*(NT+15)*32] fallback entries staged per assign workgroup
+  uint32_t *span;     // [H][kSpanParts][D] per-channel emax | lmin << 16 of chunk groups
   int32_t *idx;       // [H][T][C] device copy of the seeded init indices
 };
+
+constexpr int kSpanParts = 32;  // chunk groups per head in the span reduction
 
 __host__ __device__ inline int pad32(int x) { return (x + 31) & ~31; }
 // Upper bound on member-chunks per head: every cluster adds at most one

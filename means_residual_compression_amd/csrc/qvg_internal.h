@@ -54,8 +54,11 @@ bool launch_kmeans_stage_begin(const KmArgs &a, hipStream_t s);
 template <typename Tin, int D>
 bool launch_assign(const KmArgs &a, int bslot, hipStream_t s);
 template <typename Tin, typename Tc, int D>
+// reduce_span: after the chunk sums, reduce their spans over each head (the
+// first iteration of a stage), so later iterations can skip the tracking.
 bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int64_t rec_hstride,
-                   float *cache, int64_t cache_hstride, int log_slot, hipStream_t s);
+                   float *cache, int64_t cache_hstride, int log_slot, bool reduce_span,
+                   hipStream_t s);
 
 // Elementwise kernels (qvg_quant.hip).
 bool launch_fill_u32(uint32_t *p, int64_t n, hipStream_t s);

@@ -841,14 +841,16 @@ __device__ __forceinline__ void exact_span(float v, uint32_t &emax, uint32_t &lm
   emax = max(emax, e);
   lmin = min(lmin, v != 0.0f ? l : 0xFFFFu);
 }
-template <typename Tin, int D, int NSUB>
-__global__ __launch_bounds__(256) void k_chunk_sum(ResView<Tin> rv, int Cp,
-                                                   const int32_t *__restrict__ sorted,
-                                                   const int32_t *__restrict__ offs,
-                                                   const int32_t *__restrict__ cofs,
-                                                   const int32_t *__restrict__ chunk_j,
-                                                   int maxch, double *__restrict__ part,
-                                                   uint32_t *__restrict__ pflag) {
+// TRACK: also record the chunk's per-channel spans (not needed once the whole
+// head's spans have shown every cluster sum of this stage exact).
+template <typename Tin, int D, int NSUB, bool TRACK>
+__device__ __forceinline__ void chunk_sum_body(const ResView<Tin> &rv, int Cp,
+                                               const int32_t *__restrict__ sorted,
+                                               const int32_t *__restrict__ offs,
+                                               const int32_t *__restrict__ cofs,
+                                               const int32_t *__restrict__ chunk_j, int maxch,
+                                               double *__restrict__ part,
+                                               uint32_t *__restrict__ pflag) {
   constexpr int LPR = D / 8;              // lanes per member row (8 channels each)
   constexpr int RPI = 64 / LPR;           // member rows per load instruction
   constexpr int MPL = kAccChunk / RPI;    // members per lane
@@ -901,7 +903,7 @@ __global__ __launch_bounds__(256) void k_chunk_sum(ResView<Tin> rv, int Cp,
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           s[e] = __dadd_rn(s[e], (double)v[k][e]);
-          exact_span(v[k][e], emax[e], lmin[e]);
+          if constexpr (TRACK) exact_span(v[k][e], emax[e], lmin[e]);
         }
   }
   // combine the RPI member slots (in any order: the finalize pass only uses
@@ -911,8 +913,10 @@ __global__ __launch_bounds__(256) void k_chunk_sum(ResView<Tin> rv, int Cp,
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       s[e] = __dadd_rn(s[e], __shfl_xor(s[e], off));
-      emax[e] = max(emax[e], (uint32_t)__shfl_xor((int)emax[e], off));
-      lmin[e] = min(lmin[e], (uint32_t)__shfl_xor((int)lmin[e], off));
+      if constexpr (TRACK) {
+        emax[e] = max(emax[e], (uint32_t)__shfl_xor((int)emax[e], off));
+        lmin[e] = min(lmin[e], (uint32_t)__shfl_xor((int)lmin[e], off));
+      }
     }
   if (sub == 0) {
     double *dst = part + ((int64_t)h * maxch + g) * D + q * 8;
@@ -920,9 +924,82 @@ __global__ __launch_bounds__(256) void k_chunk_sum(ResView<Tin> rv, int Cp,
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       dst[e] = s[e];
-      fl[e] = emax[e] | (lmin[e] << 16);
+      if constexpr (TRACK) fl[e] = emax[e] | (lmin[e] << 16);
     }
   }
+}
+
+// A head whose stage spans are known to keep every cluster sum exact (S_SPAN
+// == 1) skips the per-chunk span tracking.
+__device__ __forceinline__ bool head_sums_exact(const uint32_t *stats, int stat_stride, int h) {
+  return (__builtin_amdgcn_readfirstlane(stats[(int64_t)h * stat_stride + S_SPAN]) & 3u) == 1u;
+}
+
+template <typename Tin, int D, int NSUB>
+__global__ __launch_bounds__(256) void k_chunk_sum(ResView<Tin> rv, int Cp,
+                                                   const int32_t *__restrict__ sorted,
+                                                   const int32_t *__restrict__ offs,
+                                                   const int32_t *__restrict__ cofs,
+                                                   const int32_t *__restrict__ chunk_j,
+                                                   int maxch, double *__restrict__ part,
+                                                   uint32_t *__restrict__ pflag,
+                                                   const uint32_t *__restrict__ stats,
+                                                   int stat_stride) {
+  if (head_sums_exact(stats, stat_stride, blockIdx.y))
+    chunk_sum_body<Tin, D, NSUB, false>(rv, Cp, sorted, offs, cofs, chunk_j, maxch, part, pflag);
+  else
+    chunk_sum_body<Tin, D, NSUB, true>(rv, Cp, sorted, offs, cofs, chunk_j, maxch, part, pflag);
+}
+
+// Head-wide spans of a stage's residual, from the per-chunk spans of its first
+// iteration: every token is in exactly one chunk, and the residual is the same
+// in all iterations of the stage, so if emax - lmin + ceil(log2 N) <= 29 in
+// every channel, every partial sum of any cluster (at most N members) of any
+// later iteration is exact.  k_span_part reduces kSpanParts groups of chunks,
+// k_span_final the groups, and sets S_SPAN.
+template <int D>
+__global__ __launch_bounds__(256) void k_span_part(const uint32_t *__restrict__ pflag,
+                                                   const int32_t *__restrict__ cofs, int Cp,
+                                                   int maxch, uint32_t *__restrict__ span) {
+  constexpr int RPP = 256 / D;  // chunk rows per pass
+  const int h = blockIdx.y, y = blockIdx.x;
+  const int total = cofs[(int64_t)h * (Cp + 1) + Cp];
+  const int per = (total + kSpanParts - 1) / kSpanParts;
+  const int g0 = y * per, g1 = min(total, g0 + per);
+  const int ch = threadIdx.x % D, r = threadIdx.x / D;
+  uint32_t emax = 0u, lmin = 0xFFFFu;
+  for (int g = g0 + r; g < g1; g += RPP) {
+    const uint32_t f = pflag[((int64_t)h * maxch + g) * D + ch];
+    emax = max(emax, f & 0xFFFFu);
+    lmin = min(lmin, f >> 16);
+  }
+  __shared__ uint32_t se[256], sl[256];
+  se[threadIdx.x] = emax;
+  sl[threadIdx.x] = lmin;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    for (int q = 1; q < RPP; ++q) {
+      emax = max(emax, se[threadIdx.x + q * D]);
+      lmin = min(lmin, sl[threadIdx.x + q * D]);
+    }
+    span[((int64_t)h * kSpanParts + y) * D + threadIdx.x] = emax | (lmin << 16);
+  }
+}
+template <int D>
+__global__ __launch_bounds__(D) void k_span_final(const uint32_t *__restrict__ span, int N,
+                                                  uint32_t *__restrict__ stats, int stat_stride) {
+  const int h = blockIdx.x;
+  uint32_t emax = 0u, lmin = 0xFFFFu;
+#pragma unroll 8
+  for (int y = 0; y < kSpanParts; ++y) {
+    const uint32_t f = span[((int64_t)h * kSpanParts + y) * D + threadIdx.x];
+    emax = max(emax, f & 0xFFFFu);
+    lmin = min(lmin, f >> 16);
+  }
+  const int lg = N > 1 ? 32 - __builtin_clz((uint32_t)(N - 1)) : 0;
+  const int risky = (int)emax - (int)lmin + lg > 29;
+  const int any = __syncthreads_or(risky);
+  if (threadIdx.x == 0) stats[(int64_t)h * stat_stride + S_SPAN] = 1u | (any ? 2u : 0u);
 }
 
 template <typename Tin, typename Tc, int D>
@@ -946,6 +1023,7 @@ __global__ __launch_bounds__(256) void k_finalize(
                                                offs[(int64_t)h * (Cp + 1) + j]);
   const int c0 = __builtin_amdgcn_readfirstlane(cofs[(int64_t)h * (Cp + 1) + j]);
   const int nch = __builtin_amdgcn_readfirstlane(cofs[(int64_t)h * (Cp + 1) + j + 1]) - c0;
+  const bool head_exact = head_sums_exact(stats, stat_stride, h);
   const double *ph = part + ((int64_t)h * maxch + c0) * D + lane * PER;
   const uint32_t *pf = pflag + ((int64_t)h * maxch + c0) * D + lane * PER;
   double s[PER];
@@ -960,7 +1038,7 @@ __global__ __launch_bounds__(256) void k_finalize(
 #pragma unroll
       for (int m = 0; m < PER; ++m) {
         v[u][m] = ph[(int64_t)min(q + u, nch - 1) * D + m];
-        f[u][m] = pf[(int64_t)min(q + u, nch - 1) * D + m];
+        f[u][m] = head_exact ? 0u : pf[(int64_t)min(q + u, nch - 1) * D + m];
       }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
@@ -977,7 +1055,7 @@ __global__ __launch_bounds__(256) void k_finalize(
   const int lg = n > 1 ? 32 - __builtin_clz((uint32_t)(n - 1)) : 0;
   bool risky = false;
 #pragma unroll
-  for (int m = 0; m < PER; ++m) risky |= emax[m] - lmin[m] + lg > 29;
+  for (int m = 0; m < PER; ++m) risky |= !head_exact && emax[m] - lmin[m] + lg > 29;
   if (__ballot(risky)) {
     const int o0 = __builtin_amdgcn_readfirstlane(offs[(int64_t)h * (Cp + 1) + j]);
     const int32_t *ids = sorted + (int64_t)h * rv.N + o0;
@@ -1145,7 +1223,8 @@ bool launch_assign(const KmArgs &a, int bslot, hipStream_t s) {
 
 template <typename Tin, typename Tc, int D>
 bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int64_t rec_hstride,
-                   float *cache, int64_t cache_hstride, int log_slot, hipStream_t s) {
+                   float *cache, int64_t cache_hstride, int log_slot, bool reduce_span,
+                   hipStream_t s) {
   {
     const int nb = (a.N + kSortChunk - 1) / kSortChunk;
     TimerScope ts_("kmeans_sort", s);
@@ -1164,7 +1243,7 @@ bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int6
 #define QVG_CS(NS)                                                                           \
   hipLaunchKernelGGL((k_chunk_sum<Tin, D, NS>), gcs, dim3(256), 0, s, view_of<Tin>(a, D), a.Cp, \
                      a.ws.sorted, a.ws.offs, a.ws.cofs, a.ws.chunk_j, maxch, a.ws.part,      \
-                     a.ws.pflag)
+                     a.ws.pflag, a.ws_stats, a.stat_stride)
     switch (a.nsub) {
       case 0: QVG_CS(0); break;
       case 1: QVG_CS(1); break;
@@ -1177,6 +1256,14 @@ bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int6
     }
 #undef QVG_CS
     QVG_CHECK_LAUNCH();
+    if (reduce_span) {
+      hipLaunchKernelGGL((k_span_part<D>), dim3(kSpanParts, a.H), dim3(256), 0, s, a.ws.pflag,
+                         a.ws.cofs, a.Cp, maxch, a.ws.span);
+      QVG_CHECK_LAUNCH();
+      hipLaunchKernelGGL((k_span_final<D>), dim3(a.H), dim3(D), 0, s, a.ws.span, a.N, a.ws_stats,
+                         a.stat_stride);
+      QVG_CHECK_LAUNCH();
+    }
     hipLaunchKernelGGL((k_finalize<Tin, Tc, D>), dim3((a.Cp + 3) / 4, a.H), dim3(256), 0, s,
                        view_of<Tin>(a, D), a.ws.sorted, a.ws.pflag, a.C, a.Cp, a.ws.offs, a.ws.cofs, maxch, a.ws.part, a.ws.cent, a.ws_stats,
                        a.ws_stats, a.stat_stride, next_bslot, tables ? a.ws.ctab : nullptr,
@@ -1190,9 +1277,10 @@ bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int6
   template bool launch_kmeans_stage_begin<Tin, D>(const KmArgs &, hipStream_t);               \
   template bool launch_assign<Tin, D>(const KmArgs &, int, hipStream_t);                      \
   template bool launch_update<Tin, float, D>(const KmArgs &, int, bool, float *, int64_t,     \
-                                             float *, int64_t, int, hipStream_t);             \
+                                             float *, int64_t, int, bool, hipStream_t);       \
   template bool launch_update<Tin, uint16_t, D>(const KmArgs &, int, bool, uint16_t *,        \
-                                                int64_t, float *, int64_t, int, hipStream_t);
+                                                int64_t, float *, int64_t, int, bool,         \
+                                                hipStream_t);
 QVG_INST(float, 64)
 QVG_INST(float, 128)
 QVG_INST(uint16_t, 64)
