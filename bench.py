@@ -16,7 +16,9 @@ that sample.
 Other workloads (--workload): decode (decode-side dequant of a 40 x 262144
 token, T=4 record), stream (20 chunks of 3 frames, warm-started against cold
 k-means, per-chunk time and MSE), large (32 K + 32 V head-tensors x 131072
-tokens, T=4, INT2 and INT4, per-stage MSE curve and record sizes).  --copy-calibration runs only a plain 256 MiB device copy,
+tokens, T=4, INT2 and INT4, per-stage MSE curve and record sizes), pro (the
+self-forcing-shaped cache at the QVG-Pro operating point, T=4 and groups of
+16, chosen per tensor kind).  --copy-calibration runs only a plain 256 MiB device copy,
 the reference that the HBM byte counters of the kernels are scaled by.
 
 The `traffic` field of a roofline is the kernel's measured HBM bytes per
@@ -347,6 +349,103 @@ def run_stream(args):
             "roofline": None, "cpu_baseline": None}
 
 
+def run_pro(args):
+    """The self-forcing-shaped cache at the QVG-Pro operating point, chosen per
+    tensor kind (K and V head-tensors go through separate calls, each with its
+    own parameters): T=4 stages, INT2, groups of 16 channels, C=256, 8
+    iterations.  One step = compress K + compress V + fused decompress of both
+    records.  Also reports the record sizes and compression ratio against bf16,
+    the per-kind MSE beside the QVG operating point's (T=1, G=64), and an
+    oracle check of one K and one V head-tensor, bit for bit."""
+    import oracle
+    dev = torch.device("cuda:0")
+    c = synth.CONFIGS[1]
+    log("generating the self-forcing-shaped cache ...")
+    x_cpu = synth.config_cache(1)
+    H, N, d = x_cpu.shape
+    nk = c["heads"]
+    kinds = {"K": slice(0, nk), "V": slice(nk, H)}
+    pre = {k: qvg.preset("pro", iters=c["iters"]) for k in kinds}
+    x = x_cpu.to(dev)
+    xs = {k: x[s].contiguous() for k, s in kinds.items()}
+    idx = {k: synth.init_indices(50 + i, nk, pre[k].T, N, pre[k].C) for i, k in enumerate(kinds)}
+    idx_p = {k: torch.from_numpy(v).pin_memory() for k, v in idx.items()}
+    ws = {k: qvg.alloc_workspace(qvg.workspace_size(nk, N, d, x.dtype, pre[k]), dev) for k in kinds}
+    rec = {k: qvg.empty_record(nk, N, d, pre[k], x.dtype, dev) for k in kinds}
+    out = {k: torch.empty_like(xs[k]) for k in kinds}
+
+    def step():
+        for k in kinds:
+            qvg.compress(xs[k], pre[k], init_idx=idx_p[k], ws=ws[k], out=rec[k])
+        for k in kinds:
+            qvg.decompress(rec[k], pre[k], out=out[k])
+
+    ms = timed(step, args.steps, args.warmup)
+    kt = kernel_times(qvg.KERNELS)
+    log(json.dumps(kt, indent=1))
+    dq = kt["fused_dequant"]
+    dq_bytes = sum(dequant_bytes(nk, N, d, pre[k].C, pre[k].T, pre[k].bits, pre[k].group)
+                   for k in kinds)
+    dq_gbps = dq_bytes / (dq["total_ms"] / args.steps * 1e-3) / 1e9
+    asg = kt["kmeans_assign"]
+    asg_tflops = 2.0 * nk * N * 256 * d / (asg["avg_ms"] * 1e-3) / 1e12
+    per_kind = {}
+    for k in kinds:
+        qvg.decompress(rec[k], pre[k], out=out[k])
+        qp = qvg.preset("qvg", iters=c["iters"])
+        rq = qvg.compress(xs[k], qp, init_idx=torch.from_numpy(idx[k][:, :qp.T].copy()))
+        oq = qvg.decompress(rq, qp)
+        per_kind[k] = {
+            "record_bytes_per_head_tensor": rec[k].nbytes() // nk,
+            "compression_ratio_vs_bf16": N * d * 2 / (rec[k].nbytes() / nk),
+            "mse": _mse(out[k], xs[k]).mean().item(),
+            "qvg_record_bytes_per_head_tensor": rq.nbytes() // nk,
+            "qvg_compression_ratio_vs_bf16": N * d * 2 / (rq.nbytes() / nk),
+            "qvg_mse": _mse(oq, xs[k]).mean().item()}
+        del rq, oq
+    res = {
+        "metric": "compress+decompress tokens/s, QVG-Pro operating point (d=128 C=256 T=4 G=16)",
+        "value": H * N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": "self-forcing-wan-1.3b-shaped KV cache: 12 K + 12 V head-tensors "
+                               "x 32760 tokens, d=128, bf16, QVG-Pro per kind: C=256, T=4, "
+                               "INT2, G=16, 8 iterations",
+                   "presets": {k: {f: getattr(v, f) for f in ("C", "T", "iters", "bits", "group")}
+                               for k, v in pre.items()}},
+        "roofline": {"bound": "mfma", "achieved": asg_tflops, "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": asg_tflops / MFMA_F16_PEAK_TFLOPS,
+                     "traffic": None, "kernel": "kmeans_assign", "avg_ms": asg["avg_ms"]},
+        "dequant_GBps": dq_gbps, "dequant_hbm_frac": dq_gbps / HBM_PEAK_GBPS,
+        "per_kind": per_kind,
+        "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kt.items()},
+    }
+    if args.no_cpu_baseline:
+        res["cpu_baseline"] = None
+        return res
+    log("oracle check of one K and one V head-tensor ...")
+    # both kinds use the same preset here, so one oracle call (a thread each)
+    xb = torch.cat([xs[k][:1] for k in kinds]).cpu().view(torch.int16).numpy().view(np.uint16)
+    ib = np.concatenate([idx[k][:1] for k in kinds])
+    pk = pre["K"]
+    t0 = time.perf_counter()
+    ref = oracle.compress(xb, C=pk.C, T=pk.T, iters=pk.iters, bits=pk.bits, G=pk.group,
+                          init_idx=ib, threads=2)
+    dt = time.perf_counter() - t0
+    parity = True
+    for i, k in enumerate(kinds):
+        for f in ("codes", "scales", "assign"):
+            parity &= np.array_equal(getattr(rec[k], f)[:1].cpu().numpy(), ref[f][i:i + 1])
+        parity &= np.array_equal(rec[k].centroids[:1].cpu().view(torch.int16).numpy()
+                                 .view(np.uint16), ref["cent"][i:i + 1])
+    res["cpu_baseline"] = {"value": 2 * N / dt, "unit": "tokens/s", "cores": 2, "kind": "oracle",
+                           "sample": f"head-tensor 0 of K and of V, all {N} tokens, all "
+                                     f"{pk.T}x{pk.iters} k-means iterations, compress only "
+                                     f"({dt:.1f} s wall, a thread per head-tensor)"}
+    res["parity_sample_bit_exact"] = bool(parity)
+    return res
+
+
 def run_large(args):
     """The long-video cache: 32 K + 32 V head-tensors x 131072 tokens (4 scenes
     of 21 frames on a 39x40 grid), d=128, bf16, C=256, 8 iterations, T=4,
@@ -417,7 +516,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="selfforcing",
-                    choices=["selfforcing", "decode", "stream", "large"])
+                    choices=["selfforcing", "decode", "stream", "large", "pro"])
     ap.add_argument("--large-heads", type=int, default=None,
                     help="K (and V) head-tensors of the long-video cache (default 32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -437,7 +536,7 @@ def main():
         return
     qvg.lib()
     res = {"selfforcing": run_selfforcing, "decode": run_decode, "stream": run_stream,
-           "large": run_large}[args.workload](args)
+           "large": run_large, "pro": run_pro}[args.workload](args)
     print(json.dumps(res), flush=True)
 
 

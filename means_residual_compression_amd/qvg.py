@@ -130,6 +130,24 @@ def params(C: int, T: int, iters: int, bits: int, group: int) -> Params:
     return Params(C, T, iters, bits, group)
 
 
+# The two operating points the howistudyai.com explainer names ("Step-by-step",
+# progressive stages and low-bit quantization; "Error analysis", block-size
+# trade-off): QVG, one stage with groups of 64 channels (highest
+# compression), and QVG-Pro, four stages with groups of 16 (highest
+# fidelity); both INT2 with C = 256 centroids (uint8 assignments).  A preset
+# is chosen per tensor: K and V head-tensors are compressed by separate calls
+# and may use different ones.  The iteration count is not fixed by the pages.
+PRESETS = {"qvg": dict(C=256, T=1, bits=2, group=64),
+           "pro": dict(C=256, T=4, bits=2, group=16)}
+
+
+def preset(name: str, iters: int = 8, **override) -> Params:
+    """Params of a named operating point, with optional field overrides."""
+    kw = dict(PRESETS[name], iters=iters)
+    kw.update(override)
+    return params(**kw)
+
+
 def workspace_size(H, N, d, dtype: torch.dtype, p: Params) -> int:
     code = QVG_BF16 if dtype == torch.bfloat16 else QVG_F32
     n = lib().qvg_workspace_size(H, N, d, code, ct.byref(p))

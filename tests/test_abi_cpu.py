@@ -123,3 +123,13 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(qvg, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         qvg.lib()
+
+
+def test_operating_point_presets():
+    """QVG: one stage, groups of 64; QVG-Pro: four stages, groups of 16; both
+    INT2 with 256 centroids (howistudyai.com explainer, "Step-by-step" and
+    "Error analysis").  Overrides replace single fields."""
+    q, p = qvg.preset("qvg"), qvg.preset("pro", iters=5)
+    assert (q.C, q.T, q.bits, q.group) == (256, 1, 2, 64)
+    assert (p.C, p.T, p.bits, p.group, p.iters) == (256, 4, 2, 16, 5)
+    assert qvg.preset("pro", bits=4).bits == 4

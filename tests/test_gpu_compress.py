@@ -1,7 +1,8 @@
 """End-to-end GPU parity of qvg_compress / qvg_decompress / qvg_compress_stream
 against the CPU oracle on the same seeded inputs (bit-exact records and
 reconstructions), including the workload's tiny fp32 configuration in full,
-the Self-Forcing-shaped bf16 cache at full size, multi-stage and INT4 runs,
+the Self-Forcing-shaped bf16 cache at full size (and at the QVG-Pro operating
+point on a sample of its head-tensors), multi-stage and INT4 runs,
 ragged token counts, the C = N and T = 0 special cases, caller-supplied and
 streamed (warm-started) initialisation, and run-to-run determinism."""
 import numpy as np
@@ -145,6 +146,22 @@ def test_self_forcing_cache_full_size():
     idx = synth.init_indices(1, x.shape[0], p.T, x.shape[1], p.C)
     say("self-forcing full size", tuple(x.shape))
     _check(*_run_both(x, p, idx))
+
+
+def test_pro_preset_self_forcing_full_size():
+    """The QVG-Pro operating point (T=4, INT2, G=16, C=256, 8 iterations) on
+    3 K and 3 V head-tensors of the self-forcing-shaped cache at full length
+    (32760 tokens), one call per tensor kind: records, cache and
+    reconstructions bit-exact against the oracle."""
+    cfg = synth.CONFIGS[1]
+    nk = cfg["heads"]
+    x = synth.config_cache(1)
+    p = qvg.preset("pro", iters=cfg["iters"])
+    for kind, rows in (("K", [0, 5, 11]), ("V", [nk, nk + 6, nk + 11])):
+        xk = x[rows].contiguous()
+        idx = synth.init_indices(60 + rows[0], len(rows), p.T, xk.shape[1], p.C)
+        say("QVG-Pro preset full length", kind, tuple(xk.shape))
+        _check(*_run_both(xk, p, idx))
 
 
 def test_centroid_sums_that_can_round():
