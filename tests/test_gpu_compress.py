@@ -63,6 +63,20 @@ def test_multistage_bf16(T, bits, G, C, N):
     _check(*_run_both(x, p, idx))
 
 
+@pytest.mark.parametrize("N", [1, 7, 31, 33, 65])
+@pytest.mark.parametrize("d,dtype", [(64, torch.float32), (128, torch.bfloat16)])
+def test_tiny_token_counts(N, d, dtype):
+    """A single token, a partial 32-token tile, and just past one tile: every
+    tile, chunk and range boundary of the kernels is ragged."""
+    rng = np.random.default_rng(N * 7 + d)
+    x = synth.round_to(rng.standard_normal((2, N, d)) * np.exp(rng.uniform(-3, 3, (2, N, 1))), dtype)
+    C = min(N, 5)
+    p = qvg.params(C=C, T=2, iters=3, bits=2, group=32)
+    idx = synth.init_indices(700 + N, 2, p.T, N, C)
+    say("tiny token counts", N, d, dtype)
+    _check(*_run_both(x, p, idx))
+
+
 def test_T0_plain_quantization():
     x = synth.video_cache(1, 1, 2, 2, 30, 52, 128, 1e3, torch.bfloat16)
     p = qvg.params(C=1, T=0, iters=1, bits=2, group=64)
