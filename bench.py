@@ -15,7 +15,8 @@ that sample.
 
 Other workloads (--workload): decode (decode-side dequant of a 40 x 262144
 token, T=4 record), stream (20 chunks of 3 frames, warm-started against cold
-k-means, per-chunk time and MSE), large (32 K + 32 V head-tensors x 131072
+k-means, per-chunk time and MSE, and the whole history reconstructed from
+its 20 chunk records in one pass), large (32 K + 32 V head-tensors x 131072
 tokens, T=4, INT2 and INT4, per-stage MSE curve and record sizes), pro (the
 self-forcing-shaped cache at the QVG-Pro operating point, T=4 and groups of
 16, chosen per tensor kind).  --copy-calibration runs only a plain 256 MiB device copy,
@@ -334,6 +335,27 @@ def run_stream(args):
                            "total_ms": sum(times),
                            "tokens_per_s": H * N * len(chunks) / (sum(times) * 1e-3)}
     warm, cold = res_modes["warm"], res_modes["cold"]
+    # the whole history through the compressed-cache container: warm records of
+    # all chunks kept, then reconstructed in one pass against one decompress
+    # call per chunk
+    kv = qvg.CompressedKVCache(p, c["iters_warm"])
+    for ci, x in enumerate(chunks):
+        kv.append(x, init_idx=idx[0] if ci == 0 else None)
+    hist = torch.empty((H, kv.n_tokens(), d), dtype=chunks[0].dtype, device=dev)
+    per = [torch.empty_like(chunks[0]) for _ in chunks]
+    for _ in range(max(1, args.warmup)):
+        kv.reconstruct(out=hist)
+    hms = min(_events_ms(lambda: kv.reconstruct(out=hist))[0] for _ in range(5))
+    sms = min(_events_ms(lambda: [qvg.decompress(r, p, out=o) for r, o in zip(kv.records, per)])[0]
+              for _ in range(5))
+    hbytes = sum(dequant_bytes(H, r.codes.shape[1], d, p.C, p.T, p.bits, p.group)
+                 for r in kv.records)
+    history = {"chunks": len(kv), "tokens_per_head": kv.n_tokens(),
+               "record_bytes": kv.nbytes(), "bf16_bytes": H * kv.n_tokens() * d * 2,
+               "reconstruct_ms": hms, "reconstruct_GBps": hbytes / (hms * 1e-3) / 1e9,
+               "reconstruct_hbm_frac": hbytes / (hms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+               "per_chunk_decompress_ms": sms}
+    del kv, hist, per
     return {"metric": "streamed compress tokens/s (warm-started chunks)",
             "value": warm["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
             "steps": len(chunks), "warmup": args.warmup,
@@ -342,7 +364,7 @@ def run_stream(args):
             "config": {"workload": "stream of 20 chunks x 3 frames (4680 tokens), 12 K + 12 V "
                                    "head-tensors, d=128, bf16, C=256, T=2, INT2 G=64; warm: 3 "
                                    "iterations from the cache, cold: 10 from seeded rows"},
-            "warm": warm, "cold": cold,
+            "warm": warm, "cold": cold, "history": history,
             "warm_speedup": cold["total_ms"] / warm["total_ms"],
             "mse_ratio_warm_over_cold": float(np.mean(warm["mse_per_chunk"][1:]) /
                                               np.mean(cold["mse_per_chunk"][1:])),

@@ -150,6 +150,25 @@ qvg_status qvg_decompress(const qvg_record *rec, qvg_dtype rec_dtype, int64_t H,
                           int64_t d, const qvg_params *p, void *out, qvg_dtype out_dtype,
                           void *stream);
 
+/* Reconstruction of a stream's history from its chunk records (the chunked
+ * streaming of note.zhuruihan.top "Algorithm-System Co-design" and the
+ * howistudyai.com explainer, "Step-by-step": each chunk of frames is
+ * compressed on its own, and reading the cache means reconstructing every
+ * stored chunk).  Chunk c (0 <= c < n_chunks) is a record of n_tokens[c]
+ * tokens as written by qvg_compress / qvg_compress_stream with params p; all
+ * chunks share p, H, d and rec_dtype.  out: device [H][sum n_tokens][d] in
+ * out_dtype; head h's tokens of chunk c start at row h*sum + (n_tokens[0] +
+ * ... + n_tokens[c-1]).  Every element is computed exactly as qvg_decompress
+ * of that chunk computes it.  recs and n_tokens are host arrays, read during
+ * the call only; the records' buffers are device memory.  Chunks go out in
+ * launches of up to 32.  Errors: QVG_ERR_INVALID_ARG for NULL pointers,
+ * n_chunks < 1 or a chunk with n_tokens < 1; QVG_ERR_UNSUPPORTED as in
+ * qvg_decompress, or when the total exceeds 2^30 tokens per head. */
+qvg_status qvg_decompress_chunks(const qvg_record *recs, const int64_t *n_tokens,
+                                 int32_t n_chunks, qvg_dtype rec_dtype, int64_t H, int64_t d,
+                                 const qvg_params *p, void *out, qvg_dtype out_dtype,
+                                 void *stream);
+
 /* ---- single steps of the path (each is one piece of the compress above) ---- */
 
 /* Bytes of workspace qvg_kmeans_assign needs. */

@@ -310,6 +310,55 @@ qvg_status qvg_decompress(const qvg_record *rec, qvg_dtype rec_dtype, int64_t H,
   return QVG_OK;
 }
 
+qvg_status qvg_decompress_chunks(const qvg_record *recs, const int64_t *n_tokens,
+                                 int32_t n_chunks, qvg_dtype rec_dtype, int64_t H, int64_t d,
+                                 const qvg_params *p, void *out, qvg_dtype out_dtype,
+                                 void *stream) {
+  g_err[0] = 0;
+  if (!p || !recs || !n_tokens || !out) return fail(QVG_ERR_INVALID_ARG, "NULL argument");
+  if (n_chunks < 1) return fail(QVG_ERR_INVALID_ARG, "n_chunks=%d must be >= 1", n_chunks);
+  int64_t total = 0;
+  for (int32_t c = 0; c < n_chunks; ++c) {
+    if (n_tokens[c] < 1) return fail(QVG_ERR_INVALID_ARG, "chunk %d has %lld tokens", c, (long long)n_tokens[c]);
+    total += n_tokens[c];
+    if (total > (1 << 30)) return fail(QVG_ERR_UNSUPPORTED, "more than 2^30 tokens per head");
+  }
+  qvg_status st = check_dims(H, total, d, rec_dtype);
+  if (st != QVG_OK) return st;
+  if (out_dtype != QVG_F32 && out_dtype != QVG_BF16) return fail(QVG_ERR_INVALID_ARG, "unknown out dtype");
+  if (p->T < 0 || p->T > kMaxT) return fail(QVG_ERR_UNSUPPORTED, "T=%d must be in [0, 8]", p->T);
+  if (p->T > 0 && (p->C < 1 || p->C > kMaxC)) return fail(QVG_ERR_UNSUPPORTED, "C=%d must be in [1, 256]", p->C);
+  st = check_quant(d, p->bits, p->group);
+  if (st != QVG_OK) return st;
+  for (int32_t c = 0; c < n_chunks; ++c) {
+    const qvg_record &r = recs[c];
+    if (!r.codes || !r.scales) return fail(QVG_ERR_INVALID_ARG, "chunk %d: NULL codes/scales", c);
+    if (p->T > 0 && (!r.assign || !r.centroids))
+      return fail(QVG_ERR_INVALID_ARG, "chunk %d: NULL assign/centroids", c);
+  }
+  int64_t done = 0;
+  for (int32_t c0 = 0; c0 < n_chunks; c0 += kMaxChunksPerLaunch) {
+    ChunkTable tbl{};
+    tbl.n = std::min<int32_t>(kMaxChunksPerLaunch, n_chunks - c0);
+    tbl.out_off = done;
+    tbl.out_hstride = total;
+    tbl.off[0] = 0;
+    for (int q = 0; q < tbl.n; ++q) {
+      const qvg_record &r = recs[c0 + q];
+      tbl.codes[q] = r.codes;
+      tbl.scales[q] = r.scales;
+      tbl.assign[q] = r.assign;
+      tbl.cent[q] = r.centroids;
+      tbl.off[q + 1] = tbl.off[q] + n_tokens[c0 + q];
+    }
+    if (!launch_dequant_chunks(tbl, rec_dtype == QVG_BF16, (int)H, (int)d, p->C, p->T, p->bits,
+                               p->group, out, out_dtype == QVG_BF16, (hipStream_t)stream))
+      return hip_fail("fused_dequant (chunks)");
+    done += tbl.off[tbl.n];
+  }
+  return QVG_OK;
+}
+
 qvg_status qvg_candidate_counts(const void *ws, int64_t H, int64_t N, int64_t d, qvg_dtype dtype,
                                 const qvg_params *p, uint32_t *out, int32_t n_iters) {
   g_err[0] = 0;

@@ -60,6 +60,21 @@ bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int6
                    float *cache, int64_t cache_hstride, int log_slot, bool reduce_span,
                    hipStream_t s);
 
+// Records of consecutive chunks of one stream for one reconstruction launch:
+// chunk c holds tokens [off[c], off[c+1]) of the launch's span, which starts
+// at token out_off of an output with out_hstride tokens per head.
+constexpr int kMaxChunksPerLaunch = 32;
+struct NoChunks {};
+struct ChunkTable {
+  const uint8_t *codes[kMaxChunksPerLaunch];
+  const uint8_t *scales[kMaxChunksPerLaunch];
+  const uint8_t *assign[kMaxChunksPerLaunch];
+  const void *cent[kMaxChunksPerLaunch];
+  int64_t off[kMaxChunksPerLaunch + 1];
+  int64_t out_off, out_hstride;
+  int n;
+};
+
 // Elementwise kernels (qvg_quant.hip).
 bool launch_fill_u32(uint32_t *p, int64_t n, hipStream_t s);
 // r_out = r - chat[assign] (fp32), stats max|r_out| into stats[h*stride+slot]
@@ -77,5 +92,9 @@ bool launch_quant(const void *x, bool bf16, int H, int N, int D, int C, const ui
 bool launch_dequant(const uint8_t *codes, const uint8_t *scales, const uint8_t *assign,
                     const void *cent, bool c_bf16, int H, int N, int D, int C, int T, int bits,
                     int G, void *out, bool out_bf16, hipStream_t s);
+// The same over the records of tbl.n consecutive chunks (at most
+// kMaxChunksPerLaunch); all share T, C, bits, G and the dtypes.
+bool launch_dequant_chunks(const ChunkTable &tbl, bool c_bf16, int H, int D, int C, int T,
+                           int bits, int G, void *out, bool out_bf16, hipStream_t s);
 
 }  // namespace qvg

@@ -11,6 +11,8 @@
 // Thread layout for all three: one lane per 8 consecutive channels of one
 // token (16 B of bf16 / 32 B of fp32), so a token row of d=128 is 16 lanes
 // and every global access of a wave is contiguous.
+#include <type_traits>
+
 #include "qvg_common.h"
 #include "qvg_internal.h"
 
@@ -227,13 +229,16 @@ constexpr int dequant_lut_bytes() {
   return 256 * (8 / BITS) * 4;
 }
 
-template <typename Tc, typename TL, typename To, int BITS, int T>
+template <typename Tc, typename TL, typename To, int BITS, int T, typename Tab>
 __global__ __launch_bounds__(1024) void k_dequant(const uint8_t *__restrict__ codes,
                                                   const uint8_t *__restrict__ scales,
                                                   const uint8_t *__restrict__ assign,
                                                   const Tc *__restrict__ cent, int H, int N, int D,
                                                   int C, int G, int ch_log2, int nranges,
-                                                  To *__restrict__ out) {
+                                                  To *__restrict__ out, Tab tbl) {
+  // Tab = ChunkTable: the rows are those of tbl.n chunk records laid end to
+  // end per head (N = their total), each record with its own tables
+  constexpr bool CH = !std::is_same<Tab, NoChunks>::value;
   constexpr int L = (1 << BITS) - 1;
   constexpr int U = 4;         // consecutive tokens per lane per step
   constexpr int PB = 8 / BITS; // codes per byte
@@ -266,22 +271,40 @@ __global__ __launch_bounds__(1024) void k_dequant(const uint8_t *__restrict__ co
   const int dg_log2 = d_log2 - __builtin_ctz(G);
   const uint32_t coff = k0 * BITS / 8, soff = k0 >> __builtin_ctz(G);
   for (int64_t seg = a; seg < b;) {
+    // the segment: rows [lo, hi) of one head of one record (nrec rows per head)
     const int h = (int)(seg / N);
-    const int64_t lo = seg - (int64_t)h * N, hi = min(b - (int64_t)h * N, (int64_t)N);
+    int64_t lo = seg - (int64_t)h * N, hi = min(b - (int64_t)h * N, (int64_t)N), nrec = N;
+    int64_t orow0 = (int64_t)h * N + lo, next = (int64_t)h * N + hi;
+    const uint8_t *rc = codes, *rs = scales, *ra = assign;
+    const Tc *rcent = cent;
+    if constexpr (CH) {
+      int c = 0;
+      for (int q = 1; q < tbl.n; ++q) c = tbl.off[q] <= lo ? q : c;
+      const int64_t c0 = tbl.off[c];
+      nrec = tbl.off[c + 1] - c0;
+      hi = min(hi, c0 + nrec) - c0;
+      lo -= c0;
+      orow0 = (int64_t)h * tbl.out_hstride + tbl.out_off + c0 + lo;
+      next = (int64_t)h * N + c0 + hi;
+      rc = tbl.codes[c];
+      rs = tbl.scales[c];
+      ra = tbl.assign[c];
+      rcent = static_cast<const Tc *>(tbl.cent[c]);
+    }
     if (T > 0) {
-      __syncthreads();  // the previous head's tables are no longer read
-      stage_tables<Tc, TL>(tab, cent, h, T, C, D, ch, sl * ch);
+      __syncthreads();  // the previous segment's tables are no longer read
+      stage_tables<Tc, TL>(tab, rcent, h, T, C, D, ch, sl * ch);
       __syncthreads();
     }
     // Segment-relative addressing: uniform 64-bit bases, 32-bit lane offsets
     // (the launcher keeps a range's output below 2^31 bytes).
-    const int64_t row0 = (int64_t)h * N + lo;
-    const uint8_t *cbase = codes + (row0 << db_log2);
-    const uint8_t *sbase = scales + (row0 << dg_log2);
+    const int64_t row0 = (int64_t)h * nrec + lo;
+    const uint8_t *cbase = rc + (row0 << db_log2);
+    const uint8_t *sbase = rs + (row0 << dg_log2);
     const uint8_t *abase[T > 0 ? T : 1];
 #pragma unroll
-    for (int t = 0; t < T; ++t) abase[t] = assign + ((int64_t)h * T + t) * N + lo;
-    char *obase = reinterpret_cast<char *>(out + (row0 << d_log2));
+    for (int t = 0; t < T; ++t) abase[t] = ra + ((int64_t)h * T + t) * nrec + lo;
+    char *obase = reinterpret_cast<char *>(out + (orow0 << d_log2));
     const TL *tabt[T > 0 ? T : 1];  // stage tables of this slice
 #pragma unroll
     for (int t = 0; t < T; ++t) tabt[t] = tab + (uint32_t)t * C * ch;
@@ -406,7 +429,7 @@ __global__ __launch_bounds__(1024) void k_dequant(const uint8_t *__restrict__ co
         emit(rw + tl, bt);
       }
     }
-    seg = (int64_t)h * N + hi;
+    seg = next;
   }
 }
 
@@ -491,13 +514,13 @@ static int dequant_slice(int D, int C, int T, size_t esz, size_t lut) {
   return 16;
 }
 
-template <typename Tc, typename TL, typename To, int BITS, int T>
+template <typename Tc, typename TL, typename To, int BITS, int T, typename Tab>
 static bool launch_dequant_t(const uint8_t *codes, const uint8_t *scales, const uint8_t *assign,
                              const void *cent, int H, int N, int D, int C, int G, int ch, void *out,
-                             hipStream_t s) {
+                             const Tab &tbl, hipStream_t s) {
   const size_t lds = dequant_lut_bytes<BITS>() + (size_t)T * C * ch * sizeof(TL);
   static const bool attr =
-      hipFuncSetAttribute((const void *)k_dequant<Tc, TL, To, BITS, T>,
+      hipFuncSetAttribute((const void *)k_dequant<Tc, TL, To, BITS, T, Tab>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
   if (!attr) return false;
   int dev = 0, cus = 256;
@@ -511,20 +534,21 @@ static bool launch_dequant_t(const uint8_t *codes, const uint8_t *scales, const 
   want = std::max<int64_t>(want, (rows * D * (int64_t)sizeof(To) >> 30) + 1);
   const int nranges = (int)std::max<int64_t>(1, std::min<int64_t>(rows, want));
   const int grid = (nranges + 7) / 8 * 8 * slices;
-  hipLaunchKernelGGL((k_dequant<Tc, TL, To, BITS, T>), dim3(grid), dim3(1024), lds, s, codes,
-                     scales, assign, (const Tc *)cent, H, N, D, C, G, __builtin_ctz(ch), nranges,
-                     (To *)out);
+  hipLaunchKernelGGL((k_dequant<Tc, TL, To, BITS, T, Tab>), dim3(grid), dim3(1024), lds, s,
+                     codes, scales, assign, (const Tc *)cent, H, N, D, C, G, __builtin_ctz(ch),
+                     nranges, (To *)out, tbl);
   return true;
 }
 
-template <typename Tc, typename To, int BITS>
+template <typename Tc, typename To, int BITS, typename Tab>
 static bool launch_dequant_b(const uint8_t *codes, const uint8_t *scales, const uint8_t *assign,
                              const void *cent, int H, int N, int D, int C, int T, int G, void *out,
-                             hipStream_t s) {
+                             const Tab &tbl, hipStream_t s) {
   const int ch = dequant_slice(D, C, T, sizeof(Tc), dequant_lut_bytes<BITS>());
   bool ok = false;
   dispatch_nsub(T, [&]<int TT>() {
-    ok = launch_dequant_t<Tc, Tc, To, BITS, TT>(codes, scales, assign, cent, H, N, D, C, G, ch, out, s);
+    ok = launch_dequant_t<Tc, Tc, To, BITS, TT, Tab>(codes, scales, assign, cent, H, N, D, C, G,
+                                                     ch, out, tbl, s);
   });
   return ok;
 }
@@ -536,8 +560,31 @@ bool launch_dequant(const uint8_t *codes, const uint8_t *scales, const uint8_t *
   if (T == 0) C = 1;
   bool ok;
 #define QVG_DQ(TC, TO)                                                                          \
-  ok = bits == 2 ? launch_dequant_b<TC, TO, 2>(codes, scales, assign, cent, H, N, D, C, T, G, out, s) \
-                 : launch_dequant_b<TC, TO, 4>(codes, scales, assign, cent, H, N, D, C, T, G, out, s)
+  ok = bits == 2 ? launch_dequant_b<TC, TO, 2>(codes, scales, assign, cent, H, N, D, C, T, G, out, \
+                                               NoChunks{}, s)                                      \
+                 : launch_dequant_b<TC, TO, 4>(codes, scales, assign, cent, H, N, D, C, T, G, out, \
+                                               NoChunks{}, s)
+  if (c_bf16 && out_bf16) QVG_DQ(uint16_t, uint16_t);
+  else if (c_bf16) QVG_DQ(uint16_t, float);
+  else if (out_bf16) QVG_DQ(float, uint16_t);
+  else QVG_DQ(float, float);
+#undef QVG_DQ
+  if (!ok) return false;
+  QVG_CHECK_LAUNCH();
+  return true;
+}
+
+bool launch_dequant_chunks(const ChunkTable &tbl, bool c_bf16, int H, int D, int C, int T,
+                           int bits, int G, void *out, bool out_bf16, hipStream_t s) {
+  TimerScope ts_("fused_dequant", s);
+  if (T == 0) C = 1;
+  const int N = (int)tbl.off[tbl.n];
+  bool ok;
+#define QVG_DQ(TC, TO)                                                                         \
+  ok = bits == 2 ? launch_dequant_b<TC, TO, 2>(nullptr, nullptr, nullptr, nullptr, H, N, D, C, T, \
+                                               G, out, tbl, s)                                    \
+                 : launch_dequant_b<TC, TO, 4>(nullptr, nullptr, nullptr, nullptr, H, N, D, C, T, \
+                                               G, out, tbl, s)
   if (c_bf16 && out_bf16) QVG_DQ(uint16_t, uint16_t);
   else if (c_bf16) QVG_DQ(uint16_t, float);
   else if (out_bf16) QVG_DQ(float, uint16_t);

@@ -21,7 +21,8 @@ QVG_F32, QVG_BF16 = 0, 1
 _STATUS = {0: "QVG_OK", 1: "QVG_ERR_INVALID_ARG", 2: "QVG_ERR_UNSUPPORTED",
            3: "QVG_ERR_WORKSPACE", 4: "QVG_ERR_HIP"}
 EXPORTS = ["qvg_status_string", "qvg_last_error", "qvg_workspace_size", "qvg_compress",
-           "qvg_compress_stream", "qvg_decompress", "qvg_assign_workspace_size",
+           "qvg_compress_stream", "qvg_decompress", "qvg_decompress_chunks",
+           "qvg_assign_workspace_size",
            "qvg_kmeans_assign", "qvg_update_workspace_size", "qvg_kmeans_update",
            "qvg_sas_subtract", "qvg_group_quant_pack", "qvg_timing_enable", "qvg_timing_reset",
            "qvg_timing_read", "qvg_candidate_counts"]
@@ -81,6 +82,8 @@ def lib() -> ct.CDLL:
             "qvg_compress_stream": ([p, ct.c_int, i64, i64, i64, P, i32, p, ct.c_int, p, R, p,
                                      sz, p], ct.c_int),
             "qvg_decompress": ([R, ct.c_int, i64, i64, i64, P, p, ct.c_int, p], ct.c_int),
+            "qvg_decompress_chunks": ([R, ct.POINTER(i64), i32, ct.c_int, i64, i64, P, p,
+                                       ct.c_int, p], ct.c_int),
             "qvg_assign_workspace_size": ([i64, i64, i64, i32], sz),
             "qvg_kmeans_assign": ([p, ct.c_int, i64, i64, i64, p, i32, p, p, sz, p], ct.c_int),
             "qvg_update_workspace_size": ([i64, i64, i64, i32], sz),
@@ -229,6 +232,87 @@ def decompress(rec: Record, p: Params, out_dtype: torch.dtype | None = None,
     _check(lib().qvg_decompress(ct.byref(r), _dt(rec.centroids), H, N, d, ct.byref(p),
                                 out.data_ptr(), _dt(out), _stream()))
     return out
+
+
+def decompress_chunks(recs: list, p: Params, out_dtype: torch.dtype | None = None,
+                      out: torch.Tensor | None = None) -> torch.Tensor:
+    """Reconstructs a stream's history [H, sum N_c, d] from its chunk records
+    (all with params p), head by head in chunk order, in one pass over the
+    records (launches of up to 32 chunks)."""
+    if not recs:
+        raise ValueError("no chunk records")
+    H = recs[0].codes.shape[0]
+    d = recs[0].codes.shape[2] * 8 // p.bits
+    cdt = recs[0].centroids.dtype
+    n_tok = [r.codes.shape[1] for r in recs]
+    for r in recs:
+        if r.codes.shape[0] != H or r.codes.shape[2] * 8 // p.bits != d or r.centroids.dtype != cdt:
+            raise ValueError("chunk records differ in H, d or dtype")
+    odt = out_dtype or cdt
+    if out is None:
+        out = torch.empty((H, sum(n_tok), d), dtype=odt, device=recs[0].codes.device)
+    arr = (_Record * len(recs))(*[r._c() for r in recs])
+    nt = (ct.c_int64 * len(recs))(*n_tok)
+    _check(lib().qvg_decompress_chunks(arr, nt, len(recs), _dt(recs[0].centroids), H, d,
+                                       ct.byref(p), out.data_ptr(), _dt(out), _stream()))
+    return out
+
+
+class CompressedKVCache:
+    """The compressed KV history of one tensor kind across a stream: one
+    record per chunk (each chunk compressed on its own, warm-started from the
+    previous chunk's centroids), byte accounting, eviction of the oldest
+    chunks, and reconstruction of the whole history in one pass.  Device
+    memory is held by the records (torch tensors); nothing else is allocated
+    beyond one reused workspace."""
+
+    def __init__(self, p: Params, iters_warm: int, max_bytes: int | None = None):
+        self.p, self.iters_warm, self.max_bytes = p, iters_warm, max_bytes
+        self.records: list[Record] = []
+        self.first_token = 0          # stream position of the oldest kept token
+        self._cache = None            # fp32 centroid cache [H, T, C, d]
+        self._ws = None
+
+    def __len__(self) -> int:
+        return len(self.records)
+
+    def n_tokens(self) -> int:
+        return sum(r.codes.shape[1] for r in self.records)
+
+    def nbytes(self) -> int:
+        return sum(r.nbytes() for r in self.records)
+
+    def append(self, chunk: torch.Tensor, init_idx=None) -> Record:
+        """Compresses the next chunk [H, N, d] and appends its record; the
+        first chunk starts cold from init_idx, later ones warm from the cache.
+        Evicts the oldest chunks while the records exceed max_bytes."""
+        H, N, d = chunk.shape
+        need = workspace_size(H, N, d, chunk.dtype, self.p)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = alloc_workspace(need, chunk.device)
+        if self._cache is None:
+            self._cache = torch.zeros((H, self.p.T, self.p.C, d), dtype=torch.float32,
+                                      device=chunk.device)
+            rec = compress_stream(chunk, self.p, self.iters_warm, self._cache, False,
+                                  init_idx=init_idx, ws=self._ws)
+        else:
+            rec = compress_stream(chunk, self.p, self.iters_warm, self._cache, True, ws=self._ws)
+        self.records.append(rec)
+        while self.max_bytes is not None and len(self.records) > 1 and \
+                self.nbytes() > self.max_bytes:
+            self.evict(1)
+        return rec
+
+    def evict(self, n: int = 1):
+        """Drops the n oldest chunk records."""
+        for _ in range(min(n, len(self.records))):
+            self.first_token += self.records[0].codes.shape[1]
+            self.records.pop(0)
+
+    def reconstruct(self, out_dtype: torch.dtype | None = None,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+        """The kept history [H, n_tokens, d] in stream order."""
+        return decompress_chunks(self.records, self.p, out_dtype=out_dtype, out=out)
 
 
 def kmeans_assign(r: torch.Tensor, centroids: torch.Tensor, ws=None) -> torch.Tensor:

@@ -7,6 +7,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 from means_residual_compression_amd import qvg
 
@@ -116,6 +117,47 @@ def test_decompress_and_steps_reject():
                                  ct.byref(r), FAKE, 1 << 40, None) == INVALID
     assert L.qvg_compress_stream(FAKE, 1, 2, 100, 128, ct.byref(p), 3, FAKE, 0, None,
                                  ct.byref(r), FAKE, 1 << 40, None) == INVALID
+
+
+def test_decompress_chunks_rejects():
+    L = qvg.lib()
+    p = qvg.params(16, 2, 3, 2, 64)
+    r = qvg._Record(FAKE, FAKE, FAKE, FAKE)
+    recs = (qvg._Record * 2)(r, r)
+    nt = (ct.c_int64 * 2)(100, 50)
+    call = L.qvg_decompress_chunks
+    assert call(None, nt, 2, 1, 2, 128, ct.byref(p), FAKE, 1, None) == INVALID
+    assert call(recs, nt, 0, 1, 2, 128, ct.byref(p), FAKE, 1, None) == INVALID
+    assert call(recs, (ct.c_int64 * 2)(100, 0), 2, 1, 2, 128, ct.byref(p), FAKE, 1, None) == INVALID
+    assert call(recs, nt, 2, 1, 2, 128, ct.byref(p), None, 1, None) == INVALID
+    assert call(recs, nt, 2, 1, 2, 96, ct.byref(p), FAKE, 1, None) == UNSUPPORTED
+    assert call(recs, (ct.c_int64 * 2)(1 << 29, (1 << 29) + 1), 2, 1, 2, 128, ct.byref(p), FAKE,
+                1, None) == UNSUPPORTED
+    half = (qvg._Record * 2)(r, qvg._Record(FAKE, FAKE, None, FAKE))
+    assert call(half, nt, 2, 1, 2, 128, ct.byref(p), FAKE, 1, None) == INVALID
+    assert "chunk 1" in qvg.lib().qvg_last_error().decode()
+
+
+def test_compressed_cache_accounting():
+    """Byte and token accounting and oldest-first eviction of the container
+    (host logic only: records built from CPU tensors, nothing compressed)."""
+    p = qvg.preset("qvg")
+
+    def rec(n):
+        return qvg.Record(torch.zeros((2, n, 32), dtype=torch.uint8),
+                          torch.zeros((2, n, 2), dtype=torch.uint8),
+                          torch.zeros((2, p.T, n), dtype=torch.uint8),
+                          torch.zeros((2, p.T, p.C, 128), dtype=torch.bfloat16))
+    kv = qvg.CompressedKVCache(p, iters_warm=3)
+    kv.records = [rec(100), rec(60), rec(40)]
+    per_tok = 32 + 2 + p.T
+    tables = p.T * p.C * 128 * 2
+    assert kv.n_tokens() == 200 and len(kv) == 3
+    assert kv.nbytes() == 2 * (200 * per_tok + 3 * tables)
+    kv.evict(2)
+    assert kv.n_tokens() == 40 and kv.first_token == 160 and len(kv) == 1
+    kv.evict(5)
+    assert len(kv) == 0 and kv.first_token == 200 and kv.nbytes() == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
