@@ -510,12 +510,13 @@ template <typename Tin, int D>
 __device__ __forceinline__ void recheck_part(const ResView<Tin> &rv, const float *__restrict__ cent,
                                              int Cp, const int4 *__restrict__ list,
                                              const uint32_t *__restrict__ counters,
-                                             uint8_t *__restrict__ assign, int64_t assign_hstride) {
+                                             uint8_t *__restrict__ assign, int64_t assign_hstride,
+                                             uint32_t b0, uint32_t nb) {
   constexpr int LPE = D / 8, EPW = 64 / LPE;
   const uint32_t n = counters[0];
   const int lane = threadIdx.x & 63, sub = lane / LPE, li = lane % LPE;
-  const uint32_t gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const uint32_t nw = (gridDim.x * blockDim.x) >> 6;
+  const uint32_t gw = ((blockIdx.x - b0) * blockDim.x + threadIdx.x) >> 6;
+  const uint32_t nw = (nb * blockDim.x) >> 6;
   for (uint32_t base = gw * EPW; base < n; base += nw * EPW) {
     const uint32_t e = base + sub;
     const bool live = e < n;
@@ -570,7 +571,7 @@ __device__ __forceinline__ void fallback_part(const ResView<Tin> &rv,
                                               const int2 *__restrict__ list,
                                               const uint32_t *__restrict__ counters,
                                               uint8_t *__restrict__ assign,
-                                              int64_t assign_hstride) {
+                                              int64_t assign_hstride, uint32_t b0, uint32_t nb) {
   constexpr int D4 = D / 4, HB = D4 / 2;
   __shared__ float4 rs[D4];
   __shared__ double wbest[4];
@@ -578,9 +579,16 @@ __device__ __forceinline__ void fallback_part(const ResView<Tin> &rv,
   const uint32_t n = counters[1];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const double tol = order_tol<D>();
-  for (uint32_t e = blockIdx.x; e < n; e += gridDim.x) {
+  for (uint32_t e = blockIdx.x - b0; e < n; e += nb) {
     const int2 q = list[e];
     const float *ch = cent + (int64_t)q.x * Cp * D;
+    // the first half of this thread's centroid row goes out before the
+    // token's residual row
+    const int j = min(t, C - 1);
+    const float4 *c4 = reinterpret_cast<const float4 *>(ch + (int64_t)j * D);
+    float4 c[HB];
+#pragma unroll
+    for (int k = 0; k < HB; ++k) c[k] = c4[k];
     if (t < D4) {
       float v[4];
 #pragma unroll
@@ -588,14 +596,13 @@ __device__ __forceinline__ void fallback_part(const ResView<Tin> &rv,
       rs[t] = make_float4(v[0], v[1], v[2], v[3]);
     }
     __syncthreads();
-    const int j = min(t, C - 1);
-    const float4 *c4 = reinterpret_cast<const float4 *>(ch + (int64_t)j * D);
     double p0 = 0.0, p1 = 0.0, p2 = 0.0, p3 = 0.0;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      float4 c[HB];
+      if (hb == 1) {
 #pragma unroll
-      for (int k = 0; k < HB; ++k) c[k] = c4[hb * HB + k];
+        for (int k = 0; k < HB; ++k) c[k] = c4[HB + k];
+      }
 #pragma unroll
       for (int k = 0; k < HB; ++k) {
         const float4 x = rs[hb * HB + k];
@@ -670,9 +677,9 @@ __device__ __forceinline__ void fallback_part(const ResView<Tin> &rv,
 }
 
 // Both kinds of unsettled tokens in one launch: re-checks of two candidates
-// (a wave per EPW entries, grid-stride), then exact scans (a workgroup per
-// entry, grid-stride).  Iterations with few or no candidates cost one small
-// launch.
+// (a wave per EPW entries, grid-stride over the re-check workgroups) and exact
+// scans (a workgroup per entry, grid-stride over the scan workgroups).
+// Iterations with few or no candidates cost one small launch.
 template <typename Tin, int D>
 __global__ __launch_bounds__(256) void k_resolve(ResView<Tin> rv, const float *__restrict__ cent,
                                                  int C, int Cp, const int4 *__restrict__ rlist,
@@ -680,8 +687,15 @@ __global__ __launch_bounds__(256) void k_resolve(ResView<Tin> rv, const float *_
                                                  const uint32_t *__restrict__ counters,
                                                  uint8_t *__restrict__ assign,
                                                  int64_t assign_hstride) {
-  recheck_part<Tin, D>(rv, cent, Cp, rlist, counters, assign, assign_hstride);
-  fallback_part<Tin, D>(rv, cent, C, Cp, flist, counters, assign, assign_hstride);
+  // The two lists go concurrently: each exact scan is one workgroup's latency
+  // chain, so scans take up to three quarters of the workgroups (all of them
+  // when there are no re-checks) and the re-checks the rest.
+  const uint32_t nre = counters[0], nfb = counters[1], G = gridDim.x;
+  const uint32_t fw = min(nfb, nre ? G - G / 4 : G);
+  if (blockIdx.x < fw)
+    fallback_part<Tin, D>(rv, cent, C, Cp, flist, counters, assign, assign_hstride, 0u, fw);
+  else
+    recheck_part<Tin, D>(rv, cent, Cp, rlist, counters, assign, assign_hstride, fw, G - fw);
 }
 
 // --------------------------------------------------------------- sort
@@ -1213,7 +1227,9 @@ bool launch_assign(const KmArgs &a, int bslot, hipStream_t s) {
   }
   {
     TimerScope ts_("kmeans_resolve", s);
-    hipLaunchKernelGGL((k_resolve<Tin, D>), dim3(1024), dim3(256), 0, s, rv, a.ws.cent, a.C,
+    // every workgroup resident at once (four per CU at <= 128 VGPRs), so that
+    // the scan and re-check workgroups run concurrently
+    hipLaunchKernelGGL((k_resolve<Tin, D>), dim3(4 * cu_count()), dim3(256), 0, s, rv, a.ws.cent, a.C,
                        a.Cp, a.ws.recheck, a.ws.fallback, a.ws.counters, a.assign,
                        a.assign_hstride);
     QVG_CHECK_LAUNCH();
