@@ -189,3 +189,57 @@ def decompress(codes, scales, assign, cent, bits, G, out_bf16=None, threads=None
 
 def bf16_bits_to_f32(b) -> np.ndarray:
     return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ------------------------------------------------------------------ attention
+# The step after the path: attention of a block of queries over the
+# reconstructed history (note.zhuruihan.top "Algorithm-System Co-design":
+# the fused dequantization serves the attention that reads the cache;
+# paper.rainbus.top novelty paragraph: keys are cached before the rotary
+# position embedding, so it is applied after reconstruction).  Plain fp64,
+# except the steps a model takes in lower precision, written out below.
+
+def f32_to_bf16_bits_array(x) -> np.ndarray:
+    """fp32 array -> bf16 bit patterns, round to nearest even, overflow to
+    infinity (finite inputs)."""
+    u = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+
+
+def rope_bf16(k_bits, cos, sin) -> np.ndarray:
+    """Rotary position embedding, rotate-half form, applied to bf16 keys.
+    k_bits: [N, d] bf16 bit patterns; cos, sin: [N, d/2] fp32.  For
+    k < d/2 with a = x_k, b = x_{k+d/2}, c = cos[:, k], s = sin[:, k]:
+        y_k = a*c - b*s,   y_{k+d/2} = b*c + a*s,
+    every product and the sum rounded to fp32 (no fused multiply-add), then
+    y rounded to bf16 (RNE).  Returns bf16 bit patterns [N, d]."""
+    x = bf16_bits_to_f32(k_bits)
+    h = x.shape[1] // 2
+    a, b = x[:, :h], x[:, h:]
+    c = np.asarray(cos, np.float32)
+    s = np.asarray(sin, np.float32)
+    lo = np.float32(a * c) - np.float32(b * s)
+    hi = np.float32(b * c) + np.float32(a * s)
+    return f32_to_bf16_bits_array(np.concatenate([lo, hi], axis=1).astype(np.float32))
+
+
+def attention(q, k_bits, v_bits, scale, rope=None) -> np.ndarray:
+    """O = softmax(scale * q k^T) v per head, in fp64.
+    q: [H, Nq, d] fp32; k_bits, v_bits: [H, N, d] bf16 bit patterns of the
+    reconstructed keys and values; rope: None or (cos, sin), each [N, d/2]
+    fp32, applied to the keys with rope_bf16.  Softmax subtracts the row
+    maximum.  Returns [H, Nq, d] fp64."""
+    q = np.asarray(q, np.float32).astype(np.float64)
+    H, Nq, d = q.shape
+    out = np.empty((H, Nq, d), np.float64)
+    for h in range(H):
+        kb = k_bits[h] if rope is None else rope_bf16(k_bits[h], rope[0], rope[1])
+        K = bf16_bits_to_f32(kb).astype(np.float64)
+        V = bf16_bits_to_f32(v_bits[h]).astype(np.float64)
+        S = float(scale) * (q[h] @ K.T)
+        S -= S.max(axis=1, keepdims=True)
+        P = np.exp(S)
+        P /= P.sum(axis=1, keepdims=True)
+        out[h] = P @ V
+    return out
