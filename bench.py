@@ -19,7 +19,10 @@ k-means, per-chunk time and MSE, and the whole history reconstructed from
 its 20 chunk records in one pass), large (32 K + 32 V head-tensors x 131072
 tokens, T=4, INT2 and INT4, per-stage MSE curve and record sizes), pro (the
 self-forcing-shaped cache at the QVG-Pro operating point, T=4 and groups of
-16, chosen per tensor kind).  --copy-calibration runs only a plain 256 MiB device copy,
+16, chosen per tensor kind), attn (attention of --nq queries per head over the
+decode-side K and V records with the rotary tables, keys and values rebuilt
+on chip, against the two decompress launches an unfused consumer needs first).
+--copy-calibration runs only a plain 256 MiB device copy,
 the reference that the HBM byte counters of the kernels are scaled by.
 
 The `traffic` field of a roofline is the kernel's measured HBM bytes per
@@ -57,6 +60,7 @@ CSRC = os.path.join(ROOT, "means_residual_compression_amd", "csrc")
 KERNEL_SOURCES = {
     "kmeans_assign": ["qvg_kmeans.hip", "qvg_common.h", "qvg_internal.h"],
     "fused_dequant": ["qvg_quant.hip", "qvg_common.h", "qvg_internal.h"],
+    "attention": ["qvg_attn.hip", "qvg_common.h", "qvg_internal.h"],
 }
 COPY_BYTES = 256 << 20
 
@@ -277,6 +281,60 @@ def run_decode(args):
                          "traffic": stored_traffic("fused_dequant", "decode"),
                          "kernel": "fused_dequant", "per_launch": f"{nbytes} B",
                          "avg_ms": dq["avg_ms"]},
+            "cpu_baseline": None}
+
+
+def run_attn(args):
+    """Attention of Nq queries per head over the decode-side K and V records
+    (40 x 262144 tokens each, d=128, T=4, C=256, INT2 G=64, bf16 centroids),
+    pre-rotary keys rotated after reconstruction, with the keys and values
+    rebuilt on chip; against it, the two decompress launches that an unfused
+    consumer runs before it can start."""
+    dev = torch.device("cuda:0")
+    H, N, d, T, C, bits, G, Nq = 40, 262144, 128, 4, 256, 2, 64, args.nq
+    recs = []
+    for seed in (4, 104):
+        log(f"drawing the decode-side record (seed {seed}) ...")
+        codes, scales, assign, cent = synth.random_record(seed, H, N, d, T, C, bits, G)
+        recs.append(qvg.Record(torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev),
+                               torch.from_numpy(assign).to(dev), cent.to(dev)))
+        del codes, scales, assign
+    p = qvg.params(C=C, T=T, iters=1, bits=bits, group=G)
+    cos, sin = (t.to(dev) for t in synth.rope_tables(N, d))
+    q = synth.queries(9, H, Nq, d).to(dev)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    ws = qvg.alloc_workspace(qvg.lib().qvg_attention_workspace_size(H, Nq, N, d), dev)
+    out = torch.empty((H, Nq, d), dtype=torch.float32, device=dev)
+    step = lambda: qvg.attention(q, recs[0], p, recs[1], p, scale, rope=(cos, sin), ws=ws,
+                                 out=out)
+    ms = timed(step, args.steps, args.warmup)
+    at = kernel_times(["attention"])["attention"]
+    # algorithmic bytes: per token and head the codes, scales and T assignment
+    # bytes of K and of V; each stage's centroid table of both; the rotary
+    # tables, queries and output once
+    per_tok = 2 * (d * bits // 8 + d // G + T)
+    nbytes = H * N * per_tok + 2 * H * T * C * d * 2 + 2 * N * (d // 2) * 4 + 2 * H * Nq * d * 4
+    gbps = nbytes / (at["avg_ms"] * 1e-3) / 1e9
+    kv = torch.empty((H, N, d), dtype=torch.bfloat16, device=dev)
+    unfused = lambda: (qvg.decompress(recs[0], p, out=kv), qvg.decompress(recs[1], p, out=kv))
+    ms_unfused = timed(unfused, max(3, args.steps // 2), 1)
+    dq = kernel_times(["fused_dequant"])["fused_dequant"]
+    return {"metric": "fused dequant-attention GB/s (decode-side K and V records, d=128 "
+                      "C=256 T=4)",
+            "value": gbps, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+            "config": {"workload": f"attention of {Nq} queries per head over decode-side K "
+                                   f"and V records, 40 heads x 262144 tokens, d=128, INT2 "
+                                   f"G=64, T=4, C=256, bf16 centroids, rotary keys"},
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                         "traffic": stored_traffic("attention", "attn"),
+                         "kernel": "attention", "per_launch": f"{nbytes} B",
+                         "avg_ms": at["avg_ms"]},
+            "unfused": {"decompress_k_and_v_ms": 2 * dq["avg_ms"],
+                        "fused_attention_ms": at["avg_ms"],
+                        "bf16_kv_bytes_avoided": 2 * H * N * d * 2 * 2},
             "cpu_baseline": None}
 
 
@@ -538,7 +596,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="selfforcing",
-                    choices=["selfforcing", "decode", "stream", "large", "pro"])
+                    choices=["selfforcing", "decode", "stream", "large", "pro", "attn"])
+    ap.add_argument("--nq", type=int, default=16, help="queries per head (attn workload)")
     ap.add_argument("--large-heads", type=int, default=None,
                     help="K (and V) head-tensors of the long-video cache (default 32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -558,7 +617,7 @@ def main():
         return
     qvg.lib()
     res = {"selfforcing": run_selfforcing, "decode": run_decode, "stream": run_stream,
-           "large": run_large, "pro": run_pro}[args.workload](args)
+           "large": run_large, "pro": run_pro, "attn": run_attn}[args.workload](args)
     print(json.dumps(res), flush=True)
 
 

@@ -211,6 +211,42 @@ qvg_status qvg_group_quant_pack(const void *r, qvg_dtype dtype, int64_t H, int64
                                 int32_t bits, int32_t group, uint8_t *codes, uint8_t *scales,
                                 void *stream);
 
+/* Attention of Nq queries over one compressed history, with the keys and
+ * values rebuilt on chip and never written out (note.zhuruihan.top
+ * "Algorithm-System Co-design": dequantization fused into the kernels that
+ * read the cache; paper.rainbus.top novelty paragraph and the howistudyai.com
+ * explainer, "Required resources": keys are cached before the rotary
+ * position embedding, which is applied after reconstruction).
+ *   q: device fp32 [H][Nq][d], 1 <= Nq <= 16.
+ *   k_rec, v_rec: records of the same N tokens (from qvg_compress /
+ *   qvg_compress_stream) with params kp and vp, centroids in rec_dtype.
+ *   Each key and value is the bf16 value qvg_decompress(..., QVG_BF16) gives.
+ *   rope_cos, rope_sin: device fp32 [N][d/2], both NULL for none; else key
+ *   channels k and k + d/2 (k < d/2) become x c - y s and y c + x s, each
+ *   product and the difference/sum rounded to fp32, the results to bf16.
+ *   out: device fp32 [H][Nq][d] = softmax(scale q K^T) V per head, computed
+ *   in fp32, so not bit-reproducible against another summation order.  The
+ *   order: each head's ntiles = ceil(N/64) tiles of 64 tokens go in runs of
+ *   tps = ceil(ntiles / min(ntiles, ceil(2048/H), 1024)) consecutive tiles
+ *   (nsplit = ceil(ntiles/tps) runs); a score is a d-term fused
+ *   multiply-add chain times scale; within a run an output element is a
+ *   fused multiply-add chain over 64*d/256 tokens per tile (rescaled once
+ *   per tile by the running maximum's change), the 256/d thread parts are
+ *   then added, and the runs merged with one more chain.
+ *   ws: device scratch of qvg_attention_workspace_size(H, Nq, N, d) bytes,
+ *   256-byte aligned; all device pointers 16-byte aligned.
+ * Errors: QVG_ERR_INVALID_ARG for NULL pointers, one rope table without the
+ * other, Nq outside [1, 16] or misaligned pointers; QVG_ERR_UNSUPPORTED as in qvg_decompress for kp or vp;
+ * QVG_ERR_WORKSPACE for a small or misaligned workspace.  Inputs must be
+ * finite. */
+qvg_status qvg_attention(const float *q, int64_t H, int64_t Nq, int64_t d,
+                         const qvg_record *k_rec, const qvg_params *kp,
+                         const qvg_record *v_rec, const qvg_params *vp, qvg_dtype rec_dtype,
+                         int64_t N, float scale, const float *rope_cos, const float *rope_sin,
+                         float *out, void *ws, size_t ws_bytes, void *stream);
+/* Workspace bytes qvg_attention needs; 0 for unsupported sizes. */
+size_t qvg_attention_workspace_size(int64_t H, int64_t Nq, int64_t N, int64_t d);
+
 /* ---- diagnostics ---- */
 
 /* After a qvg_compress / qvg_compress_stream call that used workspace `ws`
@@ -226,7 +262,7 @@ qvg_status qvg_candidate_counts(const void *ws, int64_t H, int64_t N, int64_t d,
  * caller's stream).  Kernel names: "kmeans_assign", "kmeans_recheck",
  * "kmeans_fallback", "kmeans_sort", "kmeans_accumulate", "kmeans_init",
  * "kmeans_prepare", "kmeans_tables", "absmax", "sas_subtract",
- * "group_quant_pack", "fused_dequant", "fill".  Host-side bookkeeping only;
+ * "group_quant_pack", "fused_dequant", "attention", "fill".  Host-side bookkeeping only;
  * results of the path are unchanged. */
 void qvg_timing_enable(int on);
 /* Forget all recorded launches (waits for their events). */

@@ -359,6 +359,56 @@ qvg_status qvg_decompress_chunks(const qvg_record *recs, const int64_t *n_tokens
   return QVG_OK;
 }
 
+size_t qvg_attention_workspace_size(int64_t H, int64_t Nq, int64_t N, int64_t d) {
+  if (H < 1 || H > 65535 || N < 1 || N > (1 << 30) || (d != 64 && d != 128) || Nq < 1 ||
+      Nq > kAttnMaxQueries)
+    return 0;
+  const AttnSplit sp = attn_split((int)H, N);
+  return up((size_t)H * sp.nsplit * Nq * (d + 2) * sizeof(float));
+}
+
+qvg_status qvg_attention(const float *q, int64_t H, int64_t Nq, int64_t d,
+                         const qvg_record *k_rec, const qvg_params *kp,
+                         const qvg_record *v_rec, const qvg_params *vp, qvg_dtype rec_dtype,
+                         int64_t N, float scale, const float *rope_cos, const float *rope_sin,
+                         float *out, void *ws, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  if (!q || !out || !k_rec || !v_rec || !kp || !vp) return fail(QVG_ERR_INVALID_ARG, "NULL argument");
+  if (!rope_cos != !rope_sin) return fail(QVG_ERR_INVALID_ARG, "give both rope tables or neither");
+  if (Nq < 1 || Nq > kAttnMaxQueries)
+    return fail(QVG_ERR_INVALID_ARG, "Nq=%lld must be in [1, %d]", (long long)Nq, kAttnMaxQueries);
+  qvg_status st = check_dims(H, N, d, rec_dtype);
+  if (st != QVG_OK) return st;
+  const qvg_record *recs[2] = {k_rec, v_rec};
+  const qvg_params *ps[2] = {kp, vp};
+  AttnRec ar[2];
+  for (int i = 0; i < 2; ++i) {
+    const qvg_params *p = ps[i];
+    const qvg_record &r = *recs[i];
+    const char *who = i ? "values" : "keys";
+    if (p->T < 0 || p->T > kMaxT) return fail(QVG_ERR_UNSUPPORTED, "%s: T=%d must be in [0, 8]", who, p->T);
+    if (p->T > 0 && (p->C < 1 || p->C > kMaxC))
+      return fail(QVG_ERR_UNSUPPORTED, "%s: C=%d must be in [1, 256]", who, p->C);
+    st = check_quant(d, p->bits, p->group);
+    if (st != QVG_OK) return st;
+    if (!r.codes || !r.scales) return fail(QVG_ERR_INVALID_ARG, "%s: NULL codes/scales", who);
+    if (p->T > 0 && (!r.assign || !r.centroids)) return fail(QVG_ERR_INVALID_ARG, "%s: NULL assign/centroids", who);
+    if (((uintptr_t)r.codes & 3) || (p->T > 0 && ((uintptr_t)r.centroids & 15)))
+      return fail(QVG_ERR_INVALID_ARG, "%s: codes must be 4-byte and centroids 16-byte aligned", who);
+    ar[i] = AttnRec{r.codes, r.scales, r.assign, r.centroids, p->T, p->bits, p->group, std::max(p->C, 1)};
+  }
+  if (((uintptr_t)q & 15) || ((uintptr_t)rope_cos & 15) || ((uintptr_t)rope_sin & 15))
+    return fail(QVG_ERR_INVALID_ARG, "q and the rope tables must be 16-byte aligned");
+  const size_t need = qvg_attention_workspace_size(H, Nq, N, d);
+  if (!ws || ws_bytes < need) return fail(QVG_ERR_WORKSPACE, "workspace smaller than %zu bytes", need);
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(QVG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (!launch_attention(q, (int)H, (int)Nq, (int)N, (int)d, ar[0], ar[1], rec_dtype == QVG_BF16,
+                        scale, rope_cos, rope_sin, static_cast<float *>(ws), out,
+                        (hipStream_t)stream))
+    return hip_fail("attention");
+  return QVG_OK;
+}
+
 qvg_status qvg_candidate_counts(const void *ws, int64_t H, int64_t N, int64_t d, qvg_dtype dtype,
                                 const qvg_params *p, uint32_t *out, int32_t n_iters) {
   g_err[0] = 0;

@@ -1,0 +1,381 @@
+// Attention of a few queries over a compressed history.  The keys and values
+// are rebuilt tile by tile in LDS, bit for bit as qvg_decompress produces
+// them in bf16, and are never written to HBM: per token and head the kernel
+// reads only the packed codes, the FP8 scales and the T assignment bytes of
+// each of K and V (plus centroid rows, which stay in L2).
+//
+// note.zhuruihan.top "Algorithm-System Co-design" (dequantization fused into
+// the kernels that consume the cache); paper.rainbus.top novelty paragraph
+// and the howistudyai.com explainer, "Required resources" (keys are cached
+// before the rotary position embedding, which is applied after
+// reconstruction).
+//
+// k_attn_split: one workgroup per (head, split of consecutive 64-token
+// tiles).  Per tile it (1) rebuilds the keys and values of 64 tokens into
+// [token][channel] bf16 rows in LDS, rotating the keys (rotate-half form,
+// fp32 products and difference/sum, then bf16) when tables are given;
+// (2) scores every query against every token in fp32 (one wave per query
+// group, one lane per token) and folds the tile into a running softmax
+// (running max m, running sum l, factor e^(m_old - m_new) for the earlier
+// tiles); (3) accumulates the un-normalised output, one thread per (channel,
+// half or quarter of the tile).  At the end of its split it writes (m, l,
+// o[d]) per query.  k_attn_combine merges the splits.
+//
+// Summation order (for error bounds): an output element of one split is a
+// fused multiply-add chain over the tokens a thread owns (32 or 16 per tile),
+// rescaled once per tile, then the 2 or 4 thread parts are added, then the
+// splits are combined with one more multiply-add chain.
+#include "qvg_common.h"
+#include "qvg_internal.h"
+
+namespace qvg {
+
+namespace {
+
+constexpr int kStagesPerBatch = 2;
+
+__device__ __forceinline__ float bf16f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Channels [k0, k0+8) and [k1, k1+8) of token ti of head h, rebuilt as the
+// fused dequant rebuilds them: level (2q - L) times the decoded scale, plus
+// the stage-T centroid in one fused multiply-add (the product is exact),
+// then + C(t)[pi(t)] for t = T-1..1, each an fp32 add.
+template <typename Tc, int D>
+__device__ __forceinline__ void rebuild_pair(const AttnRec &r, int h, int N, int64_t ti, int k0,
+                                             int k1, int glog2, float a[8], float b[8]) {
+  const int64_t row = (int64_t)h * N + ti;
+  uint32_t w0, w1;
+  if (r.bits == 2) {
+    const uint16_t *c = reinterpret_cast<const uint16_t *>(r.codes + row * (D / 4));
+    w0 = c[k0 >> 3];
+    w1 = c[k1 >> 3];
+  } else {
+    const uint32_t *c = reinterpret_cast<const uint32_t *>(r.codes + row * (D / 2));
+    w0 = c[k0 >> 3];
+    w1 = c[k1 >> 3];
+  }
+  const uint8_t *sc = r.scales + (row << (__builtin_ctz(D) - glog2));
+  const float s0 = e4m3_decode_bits(sc[k0 >> glog2]);
+  const float s1 = e4m3_decode_bits(sc[k1 >> glog2]);
+  const int L = (1 << r.bits) - 1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (float)(2 * (int)((w0 >> (r.bits * e)) & L) - L);
+    b[e] = (float)(2 * (int)((w1 >> (r.bits * e)) & L) - L);
+  }
+  if (r.T == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = a[e] * s0;
+      b[e] = b[e] * s1;
+    }
+    return;
+  }
+  const Tc *cent = static_cast<const Tc *>(r.cent);
+  const uint8_t *asg = r.assign + (int64_t)h * r.T * N + ti;
+  // stages in batches (T-1, T-2), (T-3, T-4), ...: a batch's loads all go
+  // out before its additions
+  for (int t = r.T - 1; t >= 0; t -= kStagesPerBatch) {
+    float ca[kStagesPerBatch][8], cb[kStagesPerBatch][8];
+#pragma unroll
+    for (int u = 0; u < kStagesPerBatch; ++u) {
+      const int tu = max(t - u, 0);  // a missing second stage re-reads the first
+      const int j = min((int)asg[(int64_t)tu * N], r.C - 1);
+      const Tc *crow = cent + (((int64_t)h * r.T + tu) * r.C + j) * D;
+      load8(crow, k0, ca[u]);
+      load8(crow, k1, cb[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kStagesPerBatch; ++u) {
+      if (t - u < 0) break;
+      if (t - u == r.T - 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          a[e] = __builtin_fmaf(a[e], s0, ca[u][e]);
+          b[e] = __builtin_fmaf(b[e], s1, cb[u][e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          a[e] = a[e] + ca[u][e];
+          b[e] = b[e] + cb[u][e];
+        }
+      }
+    }
+  }
+}
+
+// Rotary embedding, rotate-half form, on bf16 inputs x (channel k) and y
+// (channel k + d/2): x' = x c - y s, y' = y c + x s with each product and the
+// difference/sum rounded to fp32 separately, then each result to bf16.
+__device__ __forceinline__ void rotate8(const float x[8], const float y[8], const float c[8],
+                                        const float s[8], uint32_t xo[4], uint32_t yo[4]) {
+#pragma clang fp contract(off)
+  float xr[8], yr[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float xc = x[e] * c[e], ys = y[e] * s[e], yc = y[e] * c[e], xs = x[e] * s[e];
+    xr[e] = xc - ys;
+    yr[e] = yc + xs;
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    xo[m] = pack_bf16_rne(xr[2 * m], xr[2 * m + 1]);
+    yo[m] = pack_bf16_rne(yr[2 * m], yr[2 * m + 1]);
+  }
+}
+
+__device__ __forceinline__ void unpack8(const uint32_t w[4], float v[8]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    v[2 * m] = bf16f(w[m] & 0xFFFFu);
+    v[2 * m + 1] = __uint_as_float(w[m] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ void pack8(const float v[8], uint32_t w[4]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) w[m] = pack_bf16_rne(v[2 * m], v[2 * m + 1]);
+}
+
+__device__ __forceinline__ void st16(uint16_t *p, const uint32_t w[4]) {
+  *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+}  // namespace
+
+template <typename Tc, int D, int NQ>
+__global__ __launch_bounds__(256) void k_attn_split(const float *__restrict__ q, int Nq, int N,
+                                                    int H, AttnRec kr, AttnRec vr, float scale,
+                                                    const float *__restrict__ rcos,
+                                                    const float *__restrict__ rsin, int nsplit,
+                                                    int tiles_per_split,
+                                                    float *__restrict__ part) {
+  constexpr int BN = kAttnBN, RS = D + 8, HD = D / 2, NG = D / 16;
+  constexpr int P = 256 / D, TPP = BN / P;  // output thread parts, tokens each
+  constexpr int QW = NQ >= 4 ? NQ / 4 : 1, NW = NQ >= 4 ? 4 : NQ;  // queries per wave, waves
+  extern __shared__ float4 smem_a[];
+  uint16_t *kt = reinterpret_cast<uint16_t *>(smem_a);  // [BN][RS] keys
+  uint16_t *vt = kt + BN * RS;                          // [BN][RS] values
+  float *qs = reinterpret_cast<float *>(vt + BN * RS);  // [NQ][D] queries
+  float *ps = qs + NQ * D;                              // [NQ][BN] tile weights
+  float *st = ps + NQ * BN;                             // [NQ][4] m, l, rescale
+
+  // XCD-aware order: workgroups dispatch round-robin over the 8 XCDs, so
+  // give each XCD a contiguous run of (head, split) items; one head's
+  // centroid rows then stay in one L2.
+  const int total = H * nsplit, wg = blockIdx.x, xcd = wg & 7, slot = wg >> 3;
+  const int base = total >> 3, rem = total & 7;
+  const int item = xcd * base + min(xcd, rem) + slot;
+  const int h = item / nsplit, sp = item - h * nsplit;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int kg = __builtin_ctz(kr.G), vg = __builtin_ctz(vr.G);
+
+  for (int x = t; x < NQ * D; x += 256) qs[x] = x < Nq * D ? q[(int64_t)h * Nq * D + x] : 0.0f;
+  if (t < NQ) {
+    st[4 * t] = -__builtin_inff();
+    st[4 * t + 1] = 0.0f;
+    st[4 * t + 2] = 0.0f;
+  }
+  float o[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) o[j] = 0.0f;
+  const int ntiles = (N + BN - 1) / BN;
+  const int tb = sp * tiles_per_split, te = min(tb + tiles_per_split, ntiles);
+  const int ko = t % D, kp = t / D;  // output role: channel, token part
+  __syncthreads();
+
+  for (int tile = tb; tile < te; ++tile) {
+    const int64_t i0 = (int64_t)tile * BN;
+    const int nt = (int)min((int64_t)BN, (int64_t)N - i0);
+    // (1) rebuild: item = (token, channel pair-group g): channels g*8.. and
+    // d/2 + g*8..; tokens past the end repeat the last one
+    for (int w = t; w < BN * NG; w += 256) {
+      const int i = w / NG, g = w - i * NG;
+      const int64_t ti = i0 + min(i, nt - 1);
+      const int k0 = g * 8, k1 = HD + g * 8;
+      float a[8], b[8];
+      uint32_t wa[4], wb[4];
+      rebuild_pair<Tc, D>(kr, h, N, ti, k0, k1, kg, a, b);
+      pack8(a, wa);
+      pack8(b, wb);
+      if (rcos) {
+        float c[8], s[8];
+        load8(rcos + ti * HD, k0, c);
+        load8(rsin + ti * HD, k0, s);
+        unpack8(wa, a);
+        unpack8(wb, b);
+        rotate8(a, b, c, s, wa, wb);
+      }
+      st16(kt + i * RS + k0, wa);
+      st16(kt + i * RS + k1, wb);
+      rebuild_pair<Tc, D>(vr, h, N, ti, k0, k1, vg, a, b);
+      pack8(a, wa);
+      pack8(b, wb);
+      st16(vt + i * RS + k0, wa);
+      st16(vt + i * RS + k1, wb);
+    }
+    __syncthreads();
+    // (2) scores and the running softmax: wave w owns queries w, w+4, ...;
+    // lane = token; tokens past the end score -inf (weight 0)
+    if (wave < NW) {
+      float s[QW];
+#pragma unroll
+      for (int j = 0; j < QW; ++j) s[j] = 0.0f;
+      const uint16_t *krow = kt + lane * RS;
+#pragma unroll 4
+      for (int k0 = 0; k0 < D; k0 += 8) {
+        const uint4 kw = *reinterpret_cast<const uint4 *>(krow + k0);
+        const uint32_t ww[4] = {kw.x, kw.y, kw.z, kw.w};
+        float kf[8];
+        unpack8(ww, kf);
+#pragma unroll
+        for (int j = 0; j < QW; ++j) {
+          const float4 qa = *reinterpret_cast<const float4 *>(qs + (wave + 4 * j) * D + k0);
+          const float4 qb = *reinterpret_cast<const float4 *>(qs + (wave + 4 * j) * D + k0 + 4);
+          s[j] = __builtin_fmaf(qa.x, kf[0], s[j]);
+          s[j] = __builtin_fmaf(qa.y, kf[1], s[j]);
+          s[j] = __builtin_fmaf(qa.z, kf[2], s[j]);
+          s[j] = __builtin_fmaf(qa.w, kf[3], s[j]);
+          s[j] = __builtin_fmaf(qb.x, kf[4], s[j]);
+          s[j] = __builtin_fmaf(qb.y, kf[5], s[j]);
+          s[j] = __builtin_fmaf(qb.z, kf[6], s[j]);
+          s[j] = __builtin_fmaf(qb.w, kf[7], s[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < QW; ++j) {
+        const int qq = wave + 4 * j;
+        const float sc = lane < nt ? s[j] * scale : -__builtin_inff();
+        float mt = sc;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
+        const float m_old = st[4 * qq], m_new = fmaxf(m_old, mt);
+        const float alpha = __expf(m_old - m_new);
+        const float p = __expf(sc - m_new);
+        float sum = p;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+        ps[qq * BN + lane] = p;
+        if (lane == 0) {
+          st[4 * qq] = m_new;
+          st[4 * qq + 1] = __builtin_fmaf(st[4 * qq + 1], alpha, sum);
+          st[4 * qq + 2] = alpha;
+        }
+      }
+    }
+    __syncthreads();
+    // (3) output: thread = (channel ko, token part kp)
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) o[j] = o[j] * st[4 * j + 2];
+    const uint16_t *vcol = vt + kp * TPP * RS + ko;
+    const float *pw = ps + kp * TPP;
+#pragma unroll 4
+    for (int i = 0; i < TPP; ++i) {
+      const float v = bf16f(vcol[i * RS]);
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) o[j] = __builtin_fmaf(pw[j * BN + i], v, o[j]);
+    }
+    __syncthreads();
+  }
+
+  // merge the token parts in a fixed order, write (m, l, o[]) per query
+  float *oh = reinterpret_cast<float *>(smem_a);  // [P-1][NQ][D], over kt/vt
+  if (kp > 0) {
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) oh[((kp - 1) * NQ + j) * D + ko] = o[j];
+  }
+  __syncthreads();
+  if (kp == 0) {
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      if (j >= Nq) break;
+      float r = o[j];
+#pragma unroll
+      for (int p2 = 1; p2 < P; ++p2) r += oh[((p2 - 1) * NQ + j) * D + ko];
+      float *dst = part + (((int64_t)h * nsplit + sp) * Nq + j) * (D + 2);
+      dst[2 + ko] = r;
+      if (ko == 0) {
+        dst[0] = st[4 * j];
+        dst[1] = st[4 * j + 1];
+      }
+    }
+  }
+}
+
+// Merges the splits of each (query, head): with M the largest split maximum,
+// O = sum_b o_b e^(m_b - M) / sum_b l_b e^(m_b - M).
+__global__ __launch_bounds__(128) void k_attn_combine(const float *__restrict__ part, int nsplit,
+                                                      int Nq, int D, float *__restrict__ out) {
+  const int qq = blockIdx.x, h = blockIdx.y, k = threadIdx.x;
+  if (k >= D) return;
+  const int64_t stride = (int64_t)Nq * (D + 2);
+  const float *p = part + ((int64_t)h * nsplit * Nq + qq) * (D + 2);
+  float M = -__builtin_inff();
+#pragma unroll 8
+  for (int b = 0; b < nsplit; ++b) M = fmaxf(M, p[b * stride]);
+  float l = 0.0f, acc = 0.0f;
+#pragma unroll 8
+  for (int b = 0; b < nsplit; ++b) {
+    const float w = __expf(p[b * stride] - M);
+    l = __builtin_fmaf(p[b * stride + 1], w, l);
+    acc = __builtin_fmaf(p[b * stride + 2 + k], w, acc);
+  }
+  out[((int64_t)h * Nq + qq) * D + k] = acc / l;
+}
+
+namespace {
+
+int nq_bucket(int Nq) { return Nq <= 1 ? 1 : Nq <= 4 ? 4 : 16; }
+
+template <typename Tc, int D, int NQ>
+bool launch_attn_t(const float *q, int H, int Nq, int N, const AttnRec &kr, const AttnRec &vr,
+                   float scale, const float *rcos, const float *rsin, float *part, float *out,
+                   hipStream_t s) {
+  const AttnSplit sp = attn_split(H, N);
+  hipLaunchKernelGGL((k_attn_split<Tc, D, NQ>), dim3(H * sp.nsplit), dim3(256),
+                     attn_lds_bytes(NQ, D), s, q, Nq, N, H, kr, vr, scale, rcos, rsin, sp.nsplit,
+                     sp.tiles_per_split, part);
+  if (hipGetLastError() != hipSuccess) return false;
+  hipLaunchKernelGGL(k_attn_combine, dim3(Nq, H), dim3(128), 0, s, part, sp.nsplit, Nq, D, out);
+  return hipGetLastError() == hipSuccess;
+}
+
+template <typename Tc, int D>
+bool launch_attn_d(const float *q, int H, int Nq, int N, const AttnRec &kr, const AttnRec &vr,
+                   float scale, const float *rcos, const float *rsin, float *part, float *out,
+                   hipStream_t s) {
+  switch (nq_bucket(Nq)) {
+    case 1: return launch_attn_t<Tc, D, 1>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
+    case 4: return launch_attn_t<Tc, D, 4>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
+    default: return launch_attn_t<Tc, D, 16>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
+  }
+}
+
+}  // namespace
+
+AttnSplit attn_split(int H, int64_t N) {
+  const int ntiles = (int)((N + kAttnBN - 1) / kAttnBN);
+  const int want = std::min(std::min(std::max(1, (kAttnTargetGroups + H - 1) / H), kAttnMaxSplit),
+                            ntiles);
+  const int tps = (ntiles + want - 1) / want;
+  return AttnSplit{(ntiles + tps - 1) / tps, tps};
+}
+
+size_t attn_lds_bytes(int NQ, int D) {
+  return (size_t)2 * kAttnBN * (D + 8) * 2 + (size_t)NQ * D * 4 + (size_t)NQ * kAttnBN * 4 +
+         (size_t)NQ * 16;
+}
+
+bool launch_attention(const float *q, int H, int Nq, int N, int D, const AttnRec &kr,
+                      const AttnRec &vr, bool c_bf16, float scale, const float *rcos,
+                      const float *rsin, float *part, float *out, hipStream_t s) {
+  TimerScope ts_("attention", s);
+  if (D == 64)
+    return c_bf16 ? launch_attn_d<uint16_t, 64>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s)
+                  : launch_attn_d<float, 64>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
+  return c_bf16 ? launch_attn_d<uint16_t, 128>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s)
+                : launch_attn_d<float, 128>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
+}
+
+}  // namespace qvg

@@ -25,7 +25,8 @@ EXPORTS = ["qvg_status_string", "qvg_last_error", "qvg_workspace_size", "qvg_com
            "qvg_assign_workspace_size",
            "qvg_kmeans_assign", "qvg_update_workspace_size", "qvg_kmeans_update",
            "qvg_sas_subtract", "qvg_group_quant_pack", "qvg_timing_enable", "qvg_timing_reset",
-           "qvg_timing_read", "qvg_candidate_counts"]
+           "qvg_timing_read", "qvg_candidate_counts", "qvg_attention",
+           "qvg_attention_workspace_size"]
 
 
 class QvgError(RuntimeError):
@@ -95,6 +96,9 @@ def lib() -> ct.CDLL:
             "qvg_timing_reset": ([], None),
             "qvg_timing_read": ([ct.c_char_p, ct.POINTER(ct.c_double)], i64),
             "qvg_candidate_counts": ([p, i64, i64, i64, ct.c_int, P, p, i32], ct.c_int),
+            "qvg_attention": ([p, i64, i64, i64, R, P, R, P, ct.c_int, i64, ct.c_float, p, p,
+                               p, p, sz, p], ct.c_int),
+            "qvg_attention_workspace_size": ([i64, i64, i64, i64], sz),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -255,6 +259,34 @@ def decompress_chunks(recs: list, p: Params, out_dtype: torch.dtype | None = Non
     nt = (ct.c_int64 * len(recs))(*n_tok)
     _check(lib().qvg_decompress_chunks(arr, nt, len(recs), _dt(recs[0].centroids), H, d,
                                        ct.byref(p), out.data_ptr(), _dt(out), _stream()))
+    return out
+
+
+def attention(q: torch.Tensor, k_rec: Record, kp: Params, v_rec: Record, vp: Params,
+              scale: float, rope: tuple | None = None, ws: torch.Tensor | None = None,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """softmax(scale q K^T) V per head for q [H, Nq, d] fp32 (Nq <= 16) over
+    the keys and values the two records hold, rebuilt on chip; rope = (cos,
+    sin), each [N, d/2] fp32, rotates the rebuilt keys.  Returns [H, Nq, d]
+    fp32."""
+    _dev(q, "q")
+    H, Nq, d = q.shape
+    N = k_rec.codes.shape[1]
+    if v_rec.codes.shape[1] != N or k_rec.centroids.dtype != v_rec.centroids.dtype:
+        raise ValueError("key and value records differ in token count or centroid dtype")
+    if q.dtype != torch.float32 or not q.is_contiguous():
+        raise ValueError("q must be contiguous fp32")
+    if ws is None:
+        ws = alloc_workspace(lib().qvg_attention_workspace_size(H, Nq, N, d), q.device)
+    if out is None:
+        out = torch.empty((H, Nq, d), dtype=torch.float32, device=q.device)
+    cos, sin = rope if rope is not None else (None, None)
+    kr, vr = k_rec._c(), v_rec._c()
+    _check(lib().qvg_attention(
+        q.data_ptr(), H, Nq, d, ct.byref(kr), ct.byref(kp), ct.byref(vr), ct.byref(vp),
+        _dt(k_rec.centroids), N, float(scale), None if cos is None else cos.data_ptr(),
+        None if sin is None else sin.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(),
+        _stream()))
     return out
 
 

@@ -192,3 +192,20 @@ def random_record(seed: int, H: int, N: int, d: int, T: int, C: int, bits: int, 
         for t in range(T):
             cents[h, t] = rng.standard_normal((C, d)) * (0.5 ** (t + 1))
     return codes, scales, assign, round_to(cents, torch.bfloat16)
+
+
+# ---------------------------------------------------------------- attention inputs
+def queries(seed: int, H: int, Nq: int, d: int) -> torch.Tensor:
+    """Decode-step queries [H, Nq, d] fp32 ~ N(0, 1)."""
+    return torch.from_numpy(_rng(seed, 7).standard_normal((H, Nq, d)).astype(np.float32))
+
+
+def rope_tables(N: int, d: int, base: float = 10000.0, start: int = 0):
+    """Rotary-embedding tables of token positions start..start+N-1, rotate-half
+    convention: angle(i, k) = i * base^(-2k/d) for k < d/2, evaluated in
+    float64 and rounded to fp32.  Returns (cos, sin), each [N, d/2] fp32."""
+    pos = np.arange(start, start + N, dtype=np.float64)[:, None]
+    inv = base ** (-2.0 * np.arange(d // 2, dtype=np.float64) / d)
+    ang = pos * inv[None, :]
+    return (torch.from_numpy(np.cos(ang).astype(np.float32)),
+            torch.from_numpy(np.sin(ang).astype(np.float32)))
