@@ -32,36 +32,93 @@ namespace qvg {
 
 namespace {
 
-constexpr int kStagesPerBatch = 2;
-
 __device__ __forceinline__ float bf16f(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Channels [k0, k0+8) and [k1, k1+8) of token ti of head h, rebuilt as the
-// fused dequant rebuilds them: level (2q - L) times the decoded scale, plus
-// the stage-T centroid in one fused multiply-add (the product is exact),
-// then + C(t)[pi(t)] for t = T-1..1, each an fp32 add.
-template <typename Tc, int D>
-__device__ __forceinline__ void rebuild_pair(const AttnRec &r, int h, int N, int64_t ti, int k0,
-                                             int k1, int glog2, float a[8], float b[8]) {
+// First-level loads of one item (token ti, channel groups [k0, k0+8) and
+// [k1, k1+8)) of one record: the two code words, the two scale bytes and the
+// assignment bytes of stages T-1 .. T-4 (those that exist).
+struct RawItem {
+  uint32_t w0, w1, e0, e1;
+  uint32_t j[4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_raw(const AttnRec &r, int h, int N, int64_t ti, int k0, int k1,
+                                         int glog2, RawItem &w) {
   const int64_t row = (int64_t)h * N + ti;
-  uint32_t w0, w1;
   if (r.bits == 2) {
     const uint16_t *c = reinterpret_cast<const uint16_t *>(r.codes + row * (D / 4));
-    w0 = c[k0 >> 3];
-    w1 = c[k1 >> 3];
+    w.w0 = c[k0 >> 3];
+    w.w1 = c[k1 >> 3];
   } else {
     const uint32_t *c = reinterpret_cast<const uint32_t *>(r.codes + row * (D / 2));
-    w0 = c[k0 >> 3];
-    w1 = c[k1 >> 3];
+    w.w0 = c[k0 >> 3];
+    w.w1 = c[k1 >> 3];
   }
   const uint8_t *sc = r.scales + (row << (__builtin_ctz(D) - glog2));
-  const float s0 = e4m3_decode_bits(sc[k0 >> glog2]);
-  const float s1 = e4m3_decode_bits(sc[k1 >> glog2]);
+  w.e0 = sc[k0 >> glog2];
+  w.e1 = sc[k1 >> glog2];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    w.j[u] = u < r.T ? r.assign[((int64_t)h * r.T + (r.T - 1 - u)) * N + ti] : 0u;
+}
+
+// Centroid rows of 8 channels as loaded (bf16 pairs or fp32), unpacked at use.
+template <typename Tc> struct Row8;
+template <> struct Row8<uint16_t> {
+  uint4 v;
+  __device__ __forceinline__ void load(const uint16_t *p) { v = *reinterpret_cast<const uint4 *>(p); }
+  __device__ __forceinline__ void get(float f[8]) const {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      f[2 * m] = __uint_as_float(w[m] << 16);
+      f[2 * m + 1] = __uint_as_float(w[m] & 0xFFFF0000u);
+    }
+  }
+};
+template <> struct Row8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float *p) {
+    a = *reinterpret_cast<const float4 *>(p);
+    b = *reinterpret_cast<const float4 *>(p + 4);
+  }
+  __device__ __forceinline__ void get(float f[8]) const {
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+};
+
+// Gathers of stages T-1 .. T-4 for both channel groups of an item.
+template <typename Tc, int D>
+__device__ __forceinline__ void gather4(const AttnRec &r, int h, int k0, int k1, const RawItem &w,
+                                        Row8<Tc> ga[4], Row8<Tc> gb[4]) {
+  const Tc *cent = static_cast<const Tc *>(r.cent);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (u < r.T) {
+      const int j = min((int)w.j[u], r.C - 1);
+      const Tc *crow = cent + (((int64_t)h * r.T + (r.T - 1 - u)) * r.C + j) * D;
+      ga[u].load(crow + k0);
+      gb[u].load(crow + k1);
+    }
+  }
+}
+
+// The item's 16 channels, rebuilt as the fused dequant rebuilds them: level
+// (2q - L) times the decoded scale plus the stage-T centroid in one fused
+// multiply-add (the product is exact), then + C(t)[pi(t)] for t = T-1..1,
+// each an fp32 add.
+template <typename Tc, int D>
+__device__ __forceinline__ void rebuild(const AttnRec &r, int h, int N, int64_t ti, int k0, int k1,
+                                        const RawItem &w, const Row8<Tc> ga[4],
+                                        const Row8<Tc> gb[4], float a[8], float b[8]) {
+  const float s0 = e4m3_decode_bits(w.e0), s1 = e4m3_decode_bits(w.e1);
   const int L = (1 << r.bits) - 1;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    a[e] = (float)(2 * (int)((w0 >> (r.bits * e)) & L) - L);
-    b[e] = (float)(2 * (int)((w1 >> (r.bits * e)) & L) - L);
+    a[e] = (float)(2 * (int)((w.w0 >> (r.bits * e)) & L) - L);
+    b[e] = (float)(2 * (int)((w.w1 >> (r.bits * e)) & L) - L);
   }
   if (r.T == 0) {
 #pragma unroll
@@ -71,36 +128,40 @@ __device__ __forceinline__ void rebuild_pair(const AttnRec &r, int h, int N, int
     }
     return;
   }
-  const Tc *cent = static_cast<const Tc *>(r.cent);
-  const uint8_t *asg = r.assign + (int64_t)h * r.T * N + ti;
-  // stages in batches (T-1, T-2), (T-3, T-4), ...: a batch's loads all go
-  // out before its additions
-  for (int t = r.T - 1; t >= 0; t -= kStagesPerBatch) {
-    float ca[kStagesPerBatch][8], cb[kStagesPerBatch][8];
+  float ca[8], cb[8];
+  ga[0].get(ca);
+  gb[0].get(cb);
 #pragma unroll
-    for (int u = 0; u < kStagesPerBatch; ++u) {
-      const int tu = max(t - u, 0);  // a missing second stage re-reads the first
-      const int j = min((int)asg[(int64_t)tu * N], r.C - 1);
-      const Tc *crow = cent + (((int64_t)h * r.T + tu) * r.C + j) * D;
-      load8(crow, k0, ca[u]);
-      load8(crow, k1, cb[u]);
-    }
+  for (int e = 0; e < 8; ++e) {
+    a[e] = __builtin_fmaf(a[e], s0, ca[e]);
+    b[e] = __builtin_fmaf(b[e], s1, cb[e]);
+  }
 #pragma unroll
-    for (int u = 0; u < kStagesPerBatch; ++u) {
-      if (t - u < 0) break;
-      if (t - u == r.T - 1) {
+  for (int u = 1; u < 4; ++u) {
+    if (u < r.T) {
+      ga[u].get(ca);
+      gb[u].get(cb);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          a[e] = __builtin_fmaf(a[e], s0, ca[u][e]);
-          b[e] = __builtin_fmaf(b[e], s1, cb[u][e]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          a[e] = a[e] + ca[u][e];
-          b[e] = b[e] + cb[u][e];
-        }
+      for (int e = 0; e < 8; ++e) {
+        a[e] = a[e] + ca[e];
+        b[e] = b[e] + cb[e];
       }
+    }
+  }
+  // stages below T-4 (T > 4), one at a time
+  const Tc *cent = static_cast<const Tc *>(r.cent);
+  for (int t = r.T - 5; t >= 0; --t) {
+    const int j = min((int)r.assign[((int64_t)h * r.T + t) * N + ti], r.C - 1);
+    const Tc *crow = cent + (((int64_t)h * r.T + t) * r.C + j) * D;
+    Row8<Tc> x, y;
+    x.load(crow + k0);
+    y.load(crow + k1);
+    x.get(ca);
+    y.get(cb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = a[e] + ca[e];
+      b[e] = b[e] + cb[e];
     }
   }
 }
@@ -145,7 +206,8 @@ __device__ __forceinline__ void st16(uint16_t *p, const uint32_t w[4]) {
 }  // namespace
 
 template <typename Tc, int D, int NQ>
-__global__ __launch_bounds__(256) void k_attn_split(const float *__restrict__ q, int Nq, int N,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void k_attn_split(const float *__restrict__ q, int Nq, int N,
                                                     int H, AttnRec kr, AttnRec vr, float scale,
                                                     const float *__restrict__ rcos,
                                                     const float *__restrict__ rsin, int nsplit,
@@ -154,6 +216,7 @@ __global__ __launch_bounds__(256) void k_attn_split(const float *__restrict__ q,
   constexpr int BN = kAttnBN, RS = D + 8, HD = D / 2, NG = D / 16;
   constexpr int P = 256 / D, TPP = BN / P;  // output thread parts, tokens each
   constexpr int QW = NQ >= 4 ? NQ / 4 : 1, NW = NQ >= 4 ? 4 : NQ;  // queries per wave, waves
+  constexpr int NIT = BN * NG / 256;                                 // rebuild items per thread
   extern __shared__ float4 smem_a[];
   uint16_t *kt = reinterpret_cast<uint16_t *>(smem_a);  // [BN][RS] keys
   uint16_t *vt = kt + BN * RS;                          // [BN][RS] values
@@ -161,13 +224,19 @@ __global__ __launch_bounds__(256) void k_attn_split(const float *__restrict__ q,
   float *ps = qs + NQ * D;                              // [NQ][BN] tile weights
   float *st = ps + NQ * BN;                             // [NQ][4] m, l, rescale
 
-  // XCD-aware order: workgroups dispatch round-robin over the 8 XCDs, so
-  // give each XCD a contiguous run of (head, split) items; one head's
-  // centroid rows then stay in one L2.
+  // XCD-aware order: workgroups dispatch round-robin over the 8 XCDs, and
+  // each XCD takes a contiguous range of items.  Items run group-major (heads
+  // in groups of ceil(H/8)), then run, then head within the group: an XCD
+  // works on a few heads at a time (their centroid rows stay in its L2), all
+  // at the same runs of tokens (the rotary rows they share are fetched once),
+  // and the XCDs move through the tokens together.
   const int total = H * nsplit, wg = blockIdx.x, xcd = wg & 7, slot = wg >> 3;
   const int base = total >> 3, rem = total & 7;
   const int item = xcd * base + min(xcd, rem) + slot;
-  const int h = item / nsplit, sp = item - h * nsplit;
+  const int HG = (H + 7) >> 3;
+  const int grp = item / (HG * nsplit), r0 = item - grp * HG * nsplit;
+  const int gh = min(HG, H - grp * HG);
+  const int sp = r0 / gh, h = grp * HG + (r0 - sp * gh);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int kg = __builtin_ctz(kr.G), vg = __builtin_ctz(vr.G);
 
@@ -189,31 +258,49 @@ __global__ __launch_bounds__(256) void k_attn_split(const float *__restrict__ q,
     const int64_t i0 = (int64_t)tile * BN;
     const int nt = (int)min((int64_t)BN, (int64_t)N - i0);
     // (1) rebuild: item = (token, channel pair-group g): channels g*8.. and
-    // d/2 + g*8..; tokens past the end repeat the last one
-    for (int w = t; w < BN * NG; w += 256) {
-      const int i = w / NG, g = w - i * NG;
+    // d/2 + g*8..; tokens past the end repeat the last one.  All first-level
+    // loads of the tile go out first, then each item's K gathers (with its
+    // rotary rows), then its V gathers.
+    RawItem rk[NIT], rv[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int w = t + 256 * it, i = w / NG, g = w - i * NG;
+      const int64_t ti = i0 + min(i, nt - 1);
+      load_raw<D>(kr, h, N, ti, g * 8, HD + g * 8, kg, rk[it]);
+      load_raw<D>(vr, h, N, ti, g * 8, HD + g * 8, vg, rv[it]);
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int w = t + 256 * it, i = w / NG, g = w - i * NG;
       const int64_t ti = i0 + min(i, nt - 1);
       const int k0 = g * 8, k1 = HD + g * 8;
+      Row8<Tc> ga[4], gb[4];
+      gather4<Tc, D>(kr, h, k0, k1, rk[it], ga, gb);
+      float c[8], sn[8];
+      if (rcos) {
+        load8(rcos + ti * HD, k0, c);
+        load8(rsin + ti * HD, k0, sn);
+      }
       float a[8], b[8];
       uint32_t wa[4], wb[4];
-      rebuild_pair<Tc, D>(kr, h, N, ti, k0, k1, kg, a, b);
+      rebuild<Tc, D>(kr, h, N, ti, k0, k1, rk[it], ga, gb, a, b);
       pack8(a, wa);
       pack8(b, wb);
       if (rcos) {
-        float c[8], s[8];
-        load8(rcos + ti * HD, k0, c);
-        load8(rsin + ti * HD, k0, s);
         unpack8(wa, a);
         unpack8(wb, b);
-        rotate8(a, b, c, s, wa, wb);
+        rotate8(a, b, c, sn, wa, wb);
       }
       st16(kt + i * RS + k0, wa);
       st16(kt + i * RS + k1, wb);
-      rebuild_pair<Tc, D>(vr, h, N, ti, k0, k1, vg, a, b);
+      __builtin_amdgcn_sched_barrier(0);  // keep the V gathers out of the K phase's registers
+      gather4<Tc, D>(vr, h, k0, k1, rv[it], ga, gb);
+      rebuild<Tc, D>(vr, h, N, ti, k0, k1, rv[it], ga, gb, a, b);
       pack8(a, wa);
       pack8(b, wb);
       st16(vt + i * RS + k0, wa);
       st16(vt + i * RS + k1, wb);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
     // (2) scores and the running softmax: wave w owns queries w, w+4, ...;
@@ -270,11 +357,18 @@ __global__ __launch_bounds__(256) void k_attn_split(const float *__restrict__ q,
     for (int j = 0; j < NQ; ++j) o[j] = o[j] * st[4 * j + 2];
     const uint16_t *vcol = vt + kp * TPP * RS + ko;
     const float *pw = ps + kp * TPP;
-#pragma unroll 4
-    for (int i = 0; i < TPP; ++i) {
-      const float v = bf16f(vcol[i * RS]);
+#pragma unroll 2
+    for (int i = 0; i < TPP; i += 4) {
+      const float v0 = bf16f(vcol[i * RS]), v1 = bf16f(vcol[(i + 1) * RS]);
+      const float v2 = bf16f(vcol[(i + 2) * RS]), v3 = bf16f(vcol[(i + 3) * RS]);
 #pragma unroll
-      for (int j = 0; j < NQ; ++j) o[j] = __builtin_fmaf(pw[j * BN + i], v, o[j]);
+      for (int j = 0; j < NQ; ++j) {
+        const float4 pj = *reinterpret_cast<const float4 *>(pw + j * BN + i);
+        o[j] = __builtin_fmaf(pj.x, v0, o[j]);
+        o[j] = __builtin_fmaf(pj.y, v1, o[j]);
+        o[j] = __builtin_fmaf(pj.z, v2, o[j]);
+        o[j] = __builtin_fmaf(pj.w, v3, o[j]);
+      }
     }
     __syncthreads();
   }
