@@ -237,9 +237,8 @@ qvg_status qvg_group_quant_pack(const void *r, qvg_dtype dtype, int64_t H, int64
  *   256-byte aligned; all device pointers 16-byte aligned.
  * Errors: QVG_ERR_INVALID_ARG for NULL pointers, one rope table without the
  * other, Nq outside [1, 16] or misaligned pointers; QVG_ERR_UNSUPPORTED as in qvg_decompress for kp or vp;
- * QVG_ERR_WORKSPACE for a small or misaligned workspace; QVG_ERR_UNSUPPORTED
- * also when N*d >= 2^30 (each head's rows are addressed with 32-bit
- * offsets).  Inputs must be finite. */
+ * QVG_ERR_WORKSPACE for a small or misaligned workspace.  Inputs must be
+ * finite. */
 qvg_status qvg_attention(const float *q, int64_t H, int64_t Nq, int64_t d,
                          const qvg_record *k_rec, const qvg_params *kp,
                          const qvg_record *v_rec, const qvg_params *vp, qvg_dtype rec_dtype,

@@ -379,9 +379,6 @@ qvg_status qvg_attention(const float *q, int64_t H, int64_t Nq, int64_t d,
     return fail(QVG_ERR_INVALID_ARG, "Nq=%lld must be in [1, %d]", (long long)Nq, kAttnMaxQueries);
   qvg_status st = check_dims(H, N, d, rec_dtype);
   if (st != QVG_OK) return st;
-  if (N * d * 2 >= (int64_t)1 << 31)
-    return fail(QVG_ERR_UNSUPPORTED, "N*d=%lld: attention takes fewer than 2^30 elements per head",
-                (long long)(N * d));
   const qvg_record *recs[2] = {k_rec, v_rec};
   const qvg_params *ps[2] = {kp, vp};
   AttnRec ar[2];
