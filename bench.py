@@ -61,7 +61,7 @@ CSRC = os.path.join(ROOT, "means_residual_compression_amd", "csrc")
 KERNEL_SOURCES = {
     "kmeans_assign": ["qvg_kmeans.hip", "qvg_common.h", "qvg_internal.h"],
     "fused_dequant": ["qvg_quant.hip", "qvg_common.h", "qvg_internal.h"],
-    "attention": ["qvg_attn.hip", "qvg_common.h", "qvg_internal.h"],
+    "attention": ["qvg_attn.hip", "qvg_attn.h", "qvg_common.h", "qvg_internal.h"],
 }
 COPY_BYTES = 256 << 20
 

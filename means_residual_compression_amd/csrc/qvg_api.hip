@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "qvg.h"
+#include "qvg_attn.h"
 #include "qvg_internal.h"
 
 using namespace qvg;

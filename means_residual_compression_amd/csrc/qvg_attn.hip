@@ -26,6 +26,7 @@
 // rescaled once per tile, then the 2 or 4 thread parts are added, then the
 // splits are combined with one more multiply-add chain.
 #include "qvg_common.h"
+#include "qvg_attn.h"
 #include "qvg_internal.h"
 
 namespace qvg {
