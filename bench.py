@@ -345,7 +345,7 @@ def run_attn(args):
                                    f"G=64, T=4, C=256, bf16 centroids, rotary keys"},
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
-                         "traffic": stored_traffic("attention", "attn"),
+                         "traffic": stored_traffic("attention", "attn") if Nq == 1 else None,
                          "kernel": "attention", "per_launch": f"{nbytes} B",
                          "avg_ms": at["avg_ms"]},
             "unfused": {"decompress_k_and_v_ms": 2 * dq["avg_ms"],
