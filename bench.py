@@ -304,7 +304,7 @@ def run_attn(args):
     cos, sin = (t.to(dev) for t in synth.rope_tables(N, d))
     q = synth.queries(9, H, Nq, d).to(dev)
     scale = float(np.float32(1.0 / np.sqrt(d)))
-    ws = qvg.alloc_workspace(qvg.lib().qvg_attention_workspace_size(H, Nq, N, d), dev)
+    ws = qvg.alloc_workspace(qvg.attention_workspace_size(H, Nq, N, d, p), dev)
     out = torch.empty((H, Nq, d), dtype=torch.float32, device=dev)
     step = lambda: qvg.attention(q, recs[0], p, recs[1], p, scale, rope=(cos, sin), ws=ws,
                                  out=out)
@@ -614,7 +614,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="selfforcing",
                     choices=["selfforcing", "decode", "stream", "large", "pro", "attn"])
-    ap.add_argument("--nq", type=int, default=16, help="queries per head (attn workload)")
+    ap.add_argument("--nq", type=int, default=1, help="queries per head (attn workload)")
     ap.add_argument("--large-heads", type=int, default=None,
                     help="K (and V) head-tensors of the long-video cache (default 32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -212,7 +212,7 @@ qvg_status qvg_group_quant_pack(const void *r, qvg_dtype dtype, int64_t H, int64
                                 void *stream);
 
 /* Attention of Nq queries over one compressed history, with the keys and
- * values rebuilt on chip and never written out (note.zhuruihan.top
+ * values reconstructed on chip and never written out (note.zhuruihan.top
  * "Algorithm-System Co-design": dequantization fused into the kernels that
  * read the cache; paper.rainbus.top novelty paragraph and the howistudyai.com
  * explainer, "Required resources": keys are cached before the rotary
@@ -220,32 +220,45 @@ qvg_status qvg_group_quant_pack(const void *r, qvg_dtype dtype, int64_t H, int64
  *   q: device fp32 [H][Nq][d], 1 <= Nq <= 16.
  *   k_rec, v_rec: records of the same N tokens (from qvg_compress /
  *   qvg_compress_stream) with params kp and vp, centroids in rec_dtype.
- *   Each key and value is the bf16 value qvg_decompress(..., QVG_BF16) gives.
+ *   Each key is the bf16 value qvg_decompress(..., QVG_BF16) gives.  Each
+ *   value is the reconstruction level * s_hat + C(T)[pi(T)] + ... +
+ *   C(1)[pi(1)] taken unrounded (paper.rainbus.top method paragraph, DQ).
  *   rope_cos, rope_sin: device fp32 [N][d/2], both NULL for none; else key
  *   channels k and k + d/2 (k < d/2) become x c - y s and y c + x s, each
  *   product and the difference/sum rounded to fp32, the results to bf16.
  *   out: device fp32 [H][Nq][d] = softmax(scale q K^T) V per head, computed
- *   in fp32, so not bit-reproducible against another summation order.  The
- *   order: each head's ntiles = ceil(N/64) tiles of 64 tokens go in runs of
- *   tps = ceil(ntiles / min(ntiles, ceil(2048/H), 1024)) consecutive tiles
- *   (nsplit = ceil(ntiles/tps) runs); a score is a d-term fused
- *   multiply-add chain times scale; within a run an output element is a
- *   fused multiply-add chain over 64*d/256 tokens per tile (rescaled once
- *   per tile by the running maximum's change), the 256/d thread parts are
- *   then added, and the runs merged with one more chain.
- *   ws: device scratch of qvg_attention_workspace_size(H, Nq, N, d) bytes,
- *   256-byte aligned; all device pointers 16-byte aligned.
+ *   in fp32, so not bit-reproducible against another summation order (the
+ *   same inputs give the same bits on every call).  The order:
+ *   - Runs: each head's ntiles = ceil(N/64) tiles of 64 tokens go in runs of
+ *     tps = ceil(ntiles / min(ntiles, ceil(2048/H), 1024)) consecutive tiles
+ *     (nsplit = ceil(ntiles/tps) runs).
+ *   - Scores: a d-term fused multiply-add chain, times scale.
+ *   - Output within a run: a fused multiply-add chain over 64*d/256 tokens
+ *     per tile, rescaled at most once per tile. The 256/d thread parts are
+ *     then added, and the runs merged with one more chain.
+ *   - Weight sums (Nq <= 4 and Nq*T*C <= 4096, values' T and C): the value
+ *     term sum_n p_n C(t)[pi_t(n)] is taken as sum_c C(t)[c] * (the weights
+ *     of the tokens assigned to c). Each weight sum is an add chain over a
+ *     run's tokens (rescaled at most once per tile), merged over runs with a
+ *     chain, then contracted with the table rows in 512/d ranges of
+ *     T*C*d/512 rows, added in order.
+ *   - Otherwise the values are rebuilt in fp32 (the dequant's fused
+ *     multiply-add and adds).
+ *   ws: device scratch of qvg_attention_workspace_size(H, Nq, N, d, vp)
+ *   bytes, 256-byte aligned; all device pointers 16-byte aligned.
  * Errors: QVG_ERR_INVALID_ARG for NULL pointers, one rope table without the
- * other, Nq outside [1, 16] or misaligned pointers; QVG_ERR_UNSUPPORTED as in qvg_decompress for kp or vp;
- * QVG_ERR_WORKSPACE for a small or misaligned workspace.  Inputs must be
- * finite. */
+ * other, Nq outside [1, 16] or misaligned pointers; QVG_ERR_UNSUPPORTED as
+ * in qvg_decompress for kp or vp; QVG_ERR_WORKSPACE for a small or
+ * misaligned workspace.  Inputs must be finite. */
 qvg_status qvg_attention(const float *q, int64_t H, int64_t Nq, int64_t d,
                          const qvg_record *k_rec, const qvg_params *kp,
                          const qvg_record *v_rec, const qvg_params *vp, qvg_dtype rec_dtype,
                          int64_t N, float scale, const float *rope_cos, const float *rope_sin,
                          float *out, void *ws, size_t ws_bytes, void *stream);
-/* Workspace bytes qvg_attention needs; 0 for unsupported sizes. */
-size_t qvg_attention_workspace_size(int64_t H, int64_t Nq, int64_t N, int64_t d);
+/* Workspace bytes qvg_attention needs for value params vp; 0 for
+ * unsupported sizes. */
+size_t qvg_attention_workspace_size(int64_t H, int64_t Nq, int64_t N, int64_t d,
+                                    const qvg_params *vp);
 
 /* ---- diagnostics ---- */
 

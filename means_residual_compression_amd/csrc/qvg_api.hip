@@ -360,12 +360,15 @@ qvg_status qvg_decompress_chunks(const qvg_record *recs, const int64_t *n_tokens
   return QVG_OK;
 }
 
-size_t qvg_attention_workspace_size(int64_t H, int64_t Nq, int64_t N, int64_t d) {
-  if (H < 1 || H > 65535 || N < 1 || N > (1 << 30) || (d != 64 && d != 128) || Nq < 1 ||
-      Nq > kAttnMaxQueries)
+size_t qvg_attention_workspace_size(int64_t H, int64_t Nq, int64_t N, int64_t d,
+                                    const qvg_params *vp) {
+  if (!vp || H < 1 || H > 65535 || N < 1 || N > (1 << 30) || (d != 64 && d != 128) || Nq < 1 ||
+      Nq > kAttnMaxQueries || vp->T < 0 || vp->T > kMaxT || (vp->T > 0 && (vp->C < 1 || vp->C > kMaxC)))
     return 0;
   const AttnSplit sp = attn_split((int)H, N);
-  return up((size_t)H * sp.nsplit * Nq * (d + 2) * sizeof(float));
+  const int C = std::max(vp->C, 1);
+  return up((size_t)H * sp.nsplit * Nq * attn_part_floats((int)Nq, (int)d, vp->T, C) *
+            sizeof(float));
 }
 
 qvg_status qvg_attention(const float *q, int64_t H, int64_t Nq, int64_t d,
@@ -400,7 +403,7 @@ qvg_status qvg_attention(const float *q, int64_t H, int64_t Nq, int64_t d,
   }
   if (((uintptr_t)q & 15) || ((uintptr_t)rope_cos & 15) || ((uintptr_t)rope_sin & 15))
     return fail(QVG_ERR_INVALID_ARG, "q and the rope tables must be 16-byte aligned");
-  const size_t need = qvg_attention_workspace_size(H, Nq, N, d);
+  const size_t need = qvg_attention_workspace_size(H, Nq, N, d, vp);
   if (!ws || ws_bytes < need) return fail(QVG_ERR_WORKSPACE, "workspace smaller than %zu bytes", need);
   if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(QVG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (!launch_attention(q, (int)H, (int)Nq, (int)N, (int)d, ar[0], ar[1], rec_dtype == QVG_BF16,

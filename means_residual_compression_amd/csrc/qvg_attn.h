@@ -6,15 +6,19 @@
 namespace qvg {
 
 // Attention of Nq queries over one compressed history (qvg_attn.hip): the
-// keys and values are rebuilt per tile of kAttnBN tokens in LDS, as
-// launch_dequant rebuilds them (bf16), and never stored.  Each head's tiles
-// are cut into nsplit runs of tiles_per_split consecutive tiles, one
-// workgroup each, so that about kAttnTargetGroups workgroups fill the chip
-// whatever the head count; the split count depends on H and N only.
+// keys are rebuilt per tile of kAttnBN tokens in LDS, as launch_dequant
+// rebuilds them (bf16), and never stored; the values enter unrounded.  Each
+// head's tiles are cut into nsplit runs of tiles_per_split consecutive
+// tiles, one workgroup each, so that about kAttnTargetGroups workgroups fill
+// the chip whatever the head count; the split count depends on H and N only.
 constexpr int kAttnBN = 64;
 constexpr int kAttnTargetGroups = 2048;
 constexpr int kAttnMaxSplit = 1024;
 constexpr int kAttnMaxQueries = 16;
+// Value path by per-centroid weight sums: up to this many queries, and
+// while Nq * T * C weight sums (fp32) fit this many entries of LDS.
+constexpr int kAttnSumQueries = 4;
+constexpr int kAttnSumEntries = 4096;
 struct AttnRec {
   const uint8_t *codes, *scales, *assign;
   const void *cent;
@@ -24,11 +28,14 @@ struct AttnSplit {
   int nsplit, tiles_per_split;
 };
 AttnSplit attn_split(int H, int64_t N);
-// LDS bytes of one split workgroup (NQ query rows, head dim D).
-size_t attn_lds_bytes(int NQ, int D);
-// q [H][Nq][D] fp32, part [H][nsplit][Nq][D+2] fp32 scratch, out [H][Nq][D]
-// fp32; rcos/rsin [N][D/2] fp32 or both null (no rotation).  Both records
-// hold centroids of the same dtype (c_bf16).
+// Whether the values go through per-centroid weight sums (see qvg_attn.hip).
+bool attn_uses_sums(int Nq, int T, int C);
+// Floats of one (run, query) record in the scratch: m, l, o[D], then the
+// T*C weight sums when attn_uses_sums.
+int attn_part_floats(int Nq, int D, int T, int C);
+// q [H][Nq][D] fp32, part [H][nsplit][Nq][attn_part_floats] fp32 scratch,
+// out [H][Nq][D] fp32; rcos/rsin [N][D/2] fp32 or both null (no rotation).
+// Both records hold centroids of the same dtype (c_bf16).
 bool launch_attention(const float *q, int H, int Nq, int N, int D, const AttnRec &kr,
                       const AttnRec &vr, bool c_bf16, float scale, const float *rcos,
                       const float *rsin, float *part, float *out, hipStream_t s);

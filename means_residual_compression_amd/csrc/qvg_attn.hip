@@ -1,30 +1,46 @@
-// Attention of a few queries over a compressed history.  The keys and values
-// are rebuilt tile by tile in LDS, bit for bit as qvg_decompress produces
-// them in bf16, and are never written to HBM: per token and head the kernel
-// reads only the packed codes, the FP8 scales and the T assignment bytes of
-// each of K and V (plus centroid rows, which stay in L2).
+// Attention of a few queries over a compressed history.  Per token and head
+// the kernel reads only the packed codes, the FP8 scales and the T
+// assignment bytes of K and of V (plus centroid rows, which stay in L2); the
+// reconstructed keys and values are never written to HBM.
 //
 // note.zhuruihan.top "Algorithm-System Co-design" (dequantization fused into
 // the kernels that consume the cache); paper.rainbus.top novelty paragraph
 // and the howistudyai.com explainer, "Required resources" (keys are cached
 // before the rotary position embedding, which is applied after
-// reconstruction).
+// reconstruction); paper.rainbus.top method paragraph, DQ (the
+// reconstruction level * s_hat + C(T)[pi(T)] + ... + C(1)[pi(1)]).
 //
-// k_attn_split: one workgroup per (head, split of consecutive 64-token
-// tiles).  Per tile it (1) rebuilds the keys and values of 64 tokens into
-// [token][channel] bf16 rows in LDS, rotating the keys (rotate-half form,
-// fp32 products and difference/sum, then bf16) when tables are given;
-// (2) scores every query against every token in fp32 (one wave per query
-// group, one lane per token) and folds the tile into a running softmax
-// (running max m, running sum l, factor e^(m_old - m_new) for the earlier
-// tiles); (3) accumulates the un-normalised output, one thread per (channel,
-// half or quarter of the tile).  At the end of its split it writes (m, l,
-// o[d]) per query.  k_attn_combine merges the splits.
+// Keys are rebuilt bit for bit as qvg_decompress rebuilds them in bf16 and
+// rotated (rotate-half form, fp32 products and difference/sum, then bf16).
+// Values enter unrounded, in one of two ways:
+//  * weight sums (up to kAttnSumQueries queries, Nq*T*C <= kAttnSumEntries):
+//    sum_n p_n V_n = sum_n p_n (level*s_hat)_n + sum_t sum_c W_t[c] C(t)[c]
+//    with W_t[c] the summed weights of the tokens assigned to c at stage t.
+//    Only the residual level*s_hat (exact in bf16) is staged per token; W
+//    lives in LDS and is contracted with the tables once per head at the end.
+//  * rebuilt values: level*s_hat + stage rows in fp32 (the dequant's
+//    arithmetic without the bf16 rounding), staged per token.
 //
-// Summation order (for error bounds): an output element of one split is a
-// fused multiply-add chain over the tokens a thread owns (32 or 16 per tile),
-// rescaled once per tile, then the 2 or 4 thread parts are added, then the
-// splits are combined with one more multiply-add chain.
+// k_attn_split: one workgroup per (head, run of consecutive 64-token tiles).
+// Per tile it (1) stages the keys and the value rows in LDS; (2) scores every
+// query against every token in fp32 (one wave per query group, one lane per
+// token) and folds the tile into a running softmax per query: a reference
+// maximum m, raised (with the factor e^(m_old - m_new) applied to everything
+// accumulated) only when a tile's maximum exceeds it by more than
+// kLazyRescale; (3) accumulates the un-normalised output, one thread per
+// (channel, half or quarter of the tile), and with weight sums adds each
+// token's weight to W_t[pi_t] (wave w owns the stages t = w mod 4, so every
+// slot has one writer and a fixed order).  At the end of its run it writes
+// (m, l, o[d], W) per query.  k_attn_combine merges the runs and contracts W.
+//
+// Summation order (for error bounds): an output element of one run is a
+// fused multiply-add chain over the tokens a thread owns (32 or 16 per tile,
+// d = 128 or 64), rescaled at most once per tile, then the 2 or 4 thread
+// parts are added, then the runs are combined with one more multiply-add
+// chain.  A weight sum is a chain of adds over the run's tokens assigned to
+// its slot (rescaled at most once per tile), combined over runs with a
+// multiply-add chain, then contracted with the table rows in 512/d row
+// ranges of T*C*d/512 rows each, the ranges added in order.
 #include "qvg_common.h"
 #include "qvg_attn.h"
 #include "qvg_internal.h"
@@ -110,17 +126,32 @@ __device__ __forceinline__ void gather4(const AttnRec &r, int h, int k0, int k1,
 // (2q - L) times the decoded scale plus the stage-T centroid in one fused
 // multiply-add (the product is exact), then + C(t)[pi(t)] for t = T-1..1,
 // each an fp32 add.
+// Signed levels 2q - L of the 8 codes of a code word, from the byte tables
+// (lut2: a byte's 4 INT2 levels; lut4: a byte's 2 INT4 levels).
+__device__ __forceinline__ void levels8(uint32_t w, int bits, const float4 *lut2,
+                                        const float2 *lut4, float v[8]) {
+  if (bits == 2) {
+    const float4 x = lut2[w & 0xFFu], y = lut2[(w >> 8) & 0xFFu];
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float2 x = lut4[(w >> (8 * m)) & 0xFFu];
+      v[2 * m] = x.x;
+      v[2 * m + 1] = x.y;
+    }
+  }
+}
+
 template <typename Tc, int D>
 __device__ __forceinline__ void rebuild(const AttnRec &r, int h, int N, int64_t ti, int k0, int k1,
                                         const RawItem &w, const Row8<Tc> ga[4],
-                                        const Row8<Tc> gb[4], float a[8], float b[8]) {
+                                        const Row8<Tc> gb[4], const float4 *lut2,
+                                        const float2 *lut4, float a[8], float b[8]) {
   const float s0 = e4m3_decode_bits(w.e0), s1 = e4m3_decode_bits(w.e1);
-  const int L = (1 << r.bits) - 1;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    a[e] = (float)(2 * (int)((w.w0 >> (r.bits * e)) & L) - L);
-    b[e] = (float)(2 * (int)((w.w1 >> (r.bits * e)) & L) - L);
-  }
+  levels8(w.w0, r.bits, lut2, lut4, a);
+  levels8(w.w1, r.bits, lut2, lut4, b);
   if (r.T == 0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -206,24 +237,29 @@ __device__ __forceinline__ void st16(uint16_t *p, const uint32_t w[4]) {
 
 }  // namespace
 
-template <typename Tc, int D, int NQ>
+constexpr float kLazyRescale = 8.0f;  // weights stay below e^8 between rescales
+
+template <typename Tc, int D, int NQ, bool SUMS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
-void k_attn_split(const float *__restrict__ q, int Nq, int N,
-                                                    int H, AttnRec kr, AttnRec vr, float scale,
-                                                    const float *__restrict__ rcos,
-                                                    const float *__restrict__ rsin, int nsplit,
-                                                    int tiles_per_split,
-                                                    float *__restrict__ part) {
-  constexpr int BN = kAttnBN, RS = D + 8, HD = D / 2, NG = D / 16;
+void k_attn_split(const float *__restrict__ q, int Nq, int N, int H, AttnRec kr, AttnRec vr,
+                  float scale, const float *__restrict__ rcos, const float *__restrict__ rsin,
+                  int nsplit, int tiles_per_split, int pf, float *__restrict__ part) {
+  constexpr int BN = kAttnBN, RS = D + 8, RSF = D + 4, HD = D / 2, NG = D / 16;
   constexpr int P = 256 / D, TPP = BN / P;  // output thread parts, tokens each
   constexpr int QW = NQ >= 4 ? NQ / 4 : 1, NW = NQ >= 4 ? 4 : NQ;  // queries per wave, waves
   constexpr int NIT = BN * NG / 256;                                 // rebuild items per thread
   extern __shared__ float4 smem_a[];
-  uint16_t *kt = reinterpret_cast<uint16_t *>(smem_a);  // [BN][RS] keys
-  uint16_t *vt = kt + BN * RS;                          // [BN][RS] values
-  float *qs = reinterpret_cast<float *>(vt + BN * RS);  // [NQ][D] queries
-  float *ps = qs + NQ * D;                              // [NQ][BN] tile weights
-  float *st = ps + NQ * BN;                             // [NQ][4] m, l, rescale
+  float4 *lut2 = smem_a;                                   // [256] INT2 levels of a byte
+  float2 *lut4 = reinterpret_cast<float2 *>(lut2 + 256);   // [256] INT4 levels of a byte
+  uint16_t *kt = reinterpret_cast<uint16_t *>(lut4 + 256); // [BN][RS] keys
+  // values: the residuals level * s_hat ([BN][RS] bf16, exact) with weight
+  // sums, else the rebuilt values ([BN][RSF] fp32)
+  uint16_t *vh = kt + BN * RS;
+  float *vf = reinterpret_cast<float *>(kt + BN * RS);
+  float *qs = SUMS ? reinterpret_cast<float *>(vh + BN * RS) : vf + BN * RSF;  // [NQ][D]
+  float *ps = qs + NQ * D;   // [NQ][BN] tile weights
+  float *st = ps + NQ * BN;  // [NQ][4] reference max, sum, rescale factor
+  float *ws = st + 4 * NQ;   // weight sums [Nq][T][C]
 
   // XCD-aware order: workgroups dispatch round-robin over the 8 XCDs, and
   // each XCD takes a contiguous range of items.  Items run group-major (heads
@@ -240,13 +276,22 @@ void k_attn_split(const float *__restrict__ q, int Nq, int N,
   const int sp = r0 / gh, h = grp * HG + (r0 - sp * gh);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int kg = __builtin_ctz(kr.G), vg = __builtin_ctz(vr.G);
+  const int TC = vr.T * vr.C;
+  AttnRec vq = vr;
+  if (SUMS) vq.T = 0;  // the residual only: no assignment bytes, no rows
 
+  // byte -> levels tables (blockDim.x == 256: one entry per thread)
+  lut2[t] = make_float4((float)(2 * (t & 3) - 3), (float)(2 * ((t >> 2) & 3) - 3),
+                        (float)(2 * ((t >> 4) & 3) - 3), (float)(2 * ((t >> 6) & 3) - 3));
+  lut4[t] = make_float2((float)(2 * (t & 15) - 15), (float)(2 * ((t >> 4) & 15) - 15));
   for (int x = t; x < NQ * D; x += 256) qs[x] = x < Nq * D ? q[(int64_t)h * Nq * D + x] : 0.0f;
   if (t < NQ) {
     st[4 * t] = -__builtin_inff();
     st[4 * t + 1] = 0.0f;
     st[4 * t + 2] = 0.0f;
   }
+  if (SUMS)
+    for (int x = t; x < Nq * TC; x += 256) ws[x] = 0.0f;
   float o[NQ];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) o[j] = 0.0f;
@@ -258,17 +303,17 @@ void k_attn_split(const float *__restrict__ q, int Nq, int N,
   for (int tile = tb; tile < te; ++tile) {
     const int64_t i0 = (int64_t)tile * BN;
     const int nt = (int)min((int64_t)BN, (int64_t)N - i0);
-    // (1) rebuild: item = (token, channel pair-group g): channels g*8.. and
+    // (1) stage: item = (token, channel pair-group g): channels g*8.. and
     // d/2 + g*8..; tokens past the end repeat the last one.  All first-level
     // loads of the tile go out first, then each item's K gathers (with its
-    // rotary rows), then its V gathers.
+    // rotary rows), then its values.
     RawItem rk[NIT], rv[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int w = t + 256 * it, i = w / NG, g = w - i * NG;
       const int64_t ti = i0 + min(i, nt - 1);
       load_raw<D>(kr, h, N, ti, g * 8, HD + g * 8, kg, rk[it]);
-      load_raw<D>(vr, h, N, ti, g * 8, HD + g * 8, vg, rv[it]);
+      load_raw<D>(vq, h, N, ti, g * 8, HD + g * 8, vg, rv[it]);
     }
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
@@ -284,7 +329,7 @@ void k_attn_split(const float *__restrict__ q, int Nq, int N,
       }
       float a[8], b[8];
       uint32_t wa[4], wb[4];
-      rebuild<Tc, D>(kr, h, N, ti, k0, k1, rk[it], ga, gb, a, b);
+      rebuild<Tc, D>(kr, h, N, ti, k0, k1, rk[it], ga, gb, lut2, lut4, a, b);
       pack8(a, wa);
       pack8(b, wb);
       if (rcos) {
@@ -294,13 +339,19 @@ void k_attn_split(const float *__restrict__ q, int Nq, int N,
       }
       st16(kt + i * RS + k0, wa);
       st16(kt + i * RS + k1, wb);
-      __builtin_amdgcn_sched_barrier(0);  // keep the V gathers out of the K phase's registers
-      gather4<Tc, D>(vr, h, k0, k1, rv[it], ga, gb);
-      rebuild<Tc, D>(vr, h, N, ti, k0, k1, rv[it], ga, gb, a, b);
-      pack8(a, wa);
-      pack8(b, wb);
-      st16(vt + i * RS + k0, wa);
-      st16(vt + i * RS + k1, wb);
+      __builtin_amdgcn_sched_barrier(0);  // keep the value loads out of the key phase's registers
+      if constexpr (SUMS) {
+        rebuild<Tc, D>(vq, h, N, ti, k0, k1, rv[it], ga, gb, lut2, lut4, a, b);  // level * s_hat
+        pack8(a, wa);  // exact: at most 8 significant bits
+        pack8(b, wb);
+        st16(vh + i * RS + k0, wa);
+        st16(vh + i * RS + k1, wb);
+      } else {
+        gather4<Tc, D>(vr, h, k0, k1, rv[it], ga, gb);
+        rebuild<Tc, D>(vr, h, N, ti, k0, k1, rv[it], ga, gb, lut2, lut4, a, b);
+        store8(vf, i * RSF + k0, a);
+        store8(vf, i * RSF + k1, b);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
@@ -338,8 +389,10 @@ void k_attn_split(const float *__restrict__ q, int Nq, int N,
         float mt = sc;
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
-        const float m_old = st[4 * qq], m_new = fmaxf(m_old, mt);
-        const float alpha = __expf(m_old - m_new);
+        const float m_ref = st[4 * qq];
+        const bool raise = mt > m_ref + kLazyRescale;  // always on the first tile
+        const float m_new = raise ? mt : m_ref;
+        const float alpha = raise ? __expf(m_ref - m_new) : 1.0f;
         const float p = __expf(sc - m_new);
         float sum = p;
 #pragma unroll
@@ -356,12 +409,24 @@ void k_attn_split(const float *__restrict__ q, int Nq, int N,
     // (3) output: thread = (channel ko, token part kp)
 #pragma unroll
     for (int j = 0; j < NQ; ++j) o[j] = o[j] * st[4 * j + 2];
-    const uint16_t *vcol = vt + kp * TPP * RS + ko;
     const float *pw = ps + kp * TPP;
 #pragma unroll 2
     for (int i = 0; i < TPP; i += 4) {
-      const float v0 = bf16f(vcol[i * RS]), v1 = bf16f(vcol[(i + 1) * RS]);
-      const float v2 = bf16f(vcol[(i + 2) * RS]), v3 = bf16f(vcol[(i + 3) * RS]);
+      const int r = kp * TPP + i;
+      float v0, v1, v2, v3;
+      if constexpr (SUMS) {
+        const uint16_t *vc = vh + r * RS + ko;
+        v0 = bf16f(vc[0]);
+        v1 = bf16f(vc[RS]);
+        v2 = bf16f(vc[2 * RS]);
+        v3 = bf16f(vc[3 * RS]);
+      } else {
+        const float *vc = vf + r * RSF + ko;
+        v0 = vc[0];
+        v1 = vc[RSF];
+        v2 = vc[2 * RSF];
+        v3 = vc[3 * RSF];
+      }
 #pragma unroll
       for (int j = 0; j < NQ; ++j) {
         const float4 pj = *reinterpret_cast<const float4 *>(pw + j * BN + i);
@@ -371,16 +436,33 @@ void k_attn_split(const float *__restrict__ q, int Nq, int N,
         o[j] = __builtin_fmaf(pj.w, v3, o[j]);
       }
     }
+    if constexpr (SUMS) {
+      // weight sums: wave w owns stages w, w+4, ...; lane = token
+      const int64_t ti = i0 + min(lane, nt - 1);
+      for (int ts = wave; ts < vr.T; ts += 4) {
+        const int c = min((int)vr.assign[((int64_t)h * vr.T + ts) * N + ti], vr.C - 1);
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+          if (j >= Nq) break;
+          float *wq = ws + (j * vr.T + ts) * vr.C;
+          const float al = st[4 * j + 2];
+          if (al != 1.0f)
+            for (int cc = lane; cc < vr.C; cc += 64) wq[cc] *= al;
+          if (lane < nt) atomicAdd(wq + c, ps[j * BN + lane]);
+        }
+      }
+    }
     __syncthreads();
   }
 
-  // merge the token parts in a fixed order, write (m, l, o[]) per query
-  float *oh = reinterpret_cast<float *>(smem_a);  // [P-1][NQ][D], over kt/vt
+  // merge the token parts in a fixed order, write (m, l, o[], W) per query
+  float *oh = reinterpret_cast<float *>(kt);  // [P-1][NQ][D], over the staged rows
   if (kp > 0) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) oh[((kp - 1) * NQ + j) * D + ko] = o[j];
   }
   __syncthreads();
+  float *rec = part + ((int64_t)h * nsplit + sp) * Nq * pf;
   if (kp == 0) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
@@ -388,7 +470,7 @@ void k_attn_split(const float *__restrict__ q, int Nq, int N,
       float r = o[j];
 #pragma unroll
       for (int p2 = 1; p2 < P; ++p2) r += oh[((p2 - 1) * NQ + j) * D + ko];
-      float *dst = part + (((int64_t)h * nsplit + sp) * Nq + j) * (D + 2);
+      float *dst = rec + j * pf;
       dst[2 + ko] = r;
       if (ko == 0) {
         dst[0] = st[4 * j];
@@ -396,43 +478,95 @@ void k_attn_split(const float *__restrict__ q, int Nq, int N,
       }
     }
   }
+  if (SUMS)
+    for (int x = t; x < Nq * TC; x += 256) {
+      const int j = x / TC;
+      rec[j * pf + 2 + D + (x - j * TC)] = ws[x];
+    }
 }
 
-// Merges the splits of each (query, head): with M the largest split maximum,
-// O = sum_b o_b e^(m_b - M) / sum_b l_b e^(m_b - M).
-__global__ __launch_bounds__(128) void k_attn_combine(const float *__restrict__ part, int nsplit,
-                                                      int Nq, int D, float *__restrict__ out) {
-  const int qq = blockIdx.x, h = blockIdx.y, k = threadIdx.x;
-  if (k >= D) return;
-  const int64_t stride = (int64_t)Nq * (D + 2);
-  const float *p = part + ((int64_t)h * nsplit * Nq + qq) * (D + 2);
+// Merges the runs of each (query, head): with M the largest run maximum and
+// w_b = e^(m_b - M), O = (sum_b w_b o_b + sum_t sum_c (sum_b w_b W_b[t][c])
+// C(t)[c]) / sum_b w_b l_b (the weight-sum term only with weight sums).
+template <typename Tc, bool SUMS>
+__global__ __launch_bounds__(512) void k_attn_combine(const float *__restrict__ part, int nsplit,
+                                                      int Nq, int D, int pf, AttnRec vr,
+                                                      float *__restrict__ out) {
+  __shared__ float wl[2048];  // summed weight per (stage, centroid): T*C <= 2048
+  __shared__ float red[512];
+  const int qq = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int64_t stride = (int64_t)Nq * pf;
+  const float *p = part + ((int64_t)h * nsplit * Nq + qq) * pf;
   float M = -__builtin_inff();
-#pragma unroll 8
   for (int b = 0; b < nsplit; ++b) M = fmaxf(M, p[b * stride]);
-  float l = 0.0f, acc = 0.0f;
-#pragma unroll 8
-  for (int b = 0; b < nsplit; ++b) {
-    const float w = __expf(p[b * stride] - M);
-    l = __builtin_fmaf(p[b * stride + 1], w, l);
-    acc = __builtin_fmaf(p[b * stride + 2 + k], w, acc);
+  const int TC = SUMS ? vr.T * vr.C : 0;
+  if (SUMS) {
+    for (int r = t; r < TC; r += 512) {
+      float acc = 0.0f;
+#pragma unroll 4
+      for (int b = 0; b < nsplit; ++b)
+        acc = __builtin_fmaf(p[b * stride + 2 + D + r], __expf(p[b * stride] - M), acc);
+      wl[r] = acc;
+    }
+    __syncthreads();
   }
-  out[((int64_t)h * Nq + qq) * D + k] = acc / l;
+  const int k = t % D, kp = t / D, np = 512 / D;
+  float acc = 0.0f;
+  if (SUMS) {  // rows [kp*TC/np, (kp+1)*TC/np) of the head's tables
+    const Tc *cent = static_cast<const Tc *>(vr.cent) + (size_t)h * TC * D;
+    const int r0 = kp * TC / np, r1 = (kp + 1) * TC / np;
+#pragma unroll 8
+    for (int r = r0; r < r1; ++r) {
+      float c;
+      if constexpr (sizeof(Tc) == 2)
+        c = __uint_as_float((uint32_t)cent[(size_t)r * D + k] << 16);
+      else
+        c = cent[(size_t)r * D + k];
+      acc = __builtin_fmaf(wl[r], c, acc);
+    }
+  }
+  red[t] = acc;
+  __syncthreads();
+  if (kp == 0) {
+    float l = 0.0f, o = 0.0f;
+    for (int b = 0; b < nsplit; ++b) {
+      const float w = __expf(p[b * stride] - M);
+      l = __builtin_fmaf(p[b * stride + 1], w, l);
+      o = __builtin_fmaf(p[b * stride + 2 + k], w, o);
+    }
+    if (SUMS)
+      for (int j = 0; j < np; ++j) o += red[j * D + k];
+    out[((int64_t)h * Nq + qq) * D + k] = o / l;
+  }
 }
 
 namespace {
 
 int nq_bucket(int Nq) { return Nq <= 1 ? 1 : Nq <= 4 ? 4 : 16; }
 
-template <typename Tc, int D, int NQ>
+size_t attn_lds_bytes(int NQ, int D, bool sums, int Nq, int TC) {
+  const size_t vals = sums ? (size_t)kAttnBN * (D + 8) * 2 : (size_t)kAttnBN * (D + 4) * 4;
+  return (size_t)256 * 24 + (size_t)kAttnBN * (D + 8) * 2 + vals + (size_t)NQ * D * 4 + (size_t)NQ * kAttnBN * 4 +
+         (size_t)NQ * 16 + (sums ? (size_t)Nq * TC * 4 : 0);
+}
+
+template <typename Tc, int D, int NQ, bool SUMS>
 bool launch_attn_t(const float *q, int H, int Nq, int N, const AttnRec &kr, const AttnRec &vr,
                    float scale, const float *rcos, const float *rsin, float *part, float *out,
                    hipStream_t s) {
   const AttnSplit sp = attn_split(H, N);
-  hipLaunchKernelGGL((k_attn_split<Tc, D, NQ>), dim3(H * sp.nsplit), dim3(256),
-                     attn_lds_bytes(NQ, D), s, q, Nq, N, H, kr, vr, scale, rcos, rsin, sp.nsplit,
-                     sp.tiles_per_split, part);
+  const int pf = attn_part_floats(Nq, D, vr.T, vr.C);
+  const int TC = vr.T * vr.C;
+  static const bool lds_ok =
+      hipFuncSetAttribute((const void *)k_attn_split<Tc, D, NQ, SUMS>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024) == hipSuccess;
+  if (!lds_ok) return false;
+  hipLaunchKernelGGL((k_attn_split<Tc, D, NQ, SUMS>), dim3(H * sp.nsplit), dim3(256),
+                     attn_lds_bytes(NQ, D, SUMS, Nq, TC), s, q, Nq, N, H, kr, vr, scale, rcos,
+                     rsin, sp.nsplit, sp.tiles_per_split, pf, part);
   if (hipGetLastError() != hipSuccess) return false;
-  hipLaunchKernelGGL(k_attn_combine, dim3(Nq, H), dim3(128), 0, s, part, sp.nsplit, Nq, D, out);
+  hipLaunchKernelGGL((k_attn_combine<Tc, SUMS>), dim3(Nq, H), dim3(512), 0, s, part, sp.nsplit,
+                     Nq, D, pf, vr, out);
   return hipGetLastError() == hipSuccess;
 }
 
@@ -440,10 +574,15 @@ template <typename Tc, int D>
 bool launch_attn_d(const float *q, int H, int Nq, int N, const AttnRec &kr, const AttnRec &vr,
                    float scale, const float *rcos, const float *rsin, float *part, float *out,
                    hipStream_t s) {
+  if (attn_uses_sums(Nq, vr.T, vr.C)) {
+    if (Nq == 1)
+      return launch_attn_t<Tc, D, 1, true>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
+    return launch_attn_t<Tc, D, 4, true>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
+  }
   switch (nq_bucket(Nq)) {
-    case 1: return launch_attn_t<Tc, D, 1>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
-    case 4: return launch_attn_t<Tc, D, 4>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
-    default: return launch_attn_t<Tc, D, 16>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
+    case 1: return launch_attn_t<Tc, D, 1, false>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
+    case 4: return launch_attn_t<Tc, D, 4, false>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
+    default: return launch_attn_t<Tc, D, 16, false>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
   }
 }
 
@@ -457,9 +596,12 @@ AttnSplit attn_split(int H, int64_t N) {
   return AttnSplit{(ntiles + tps - 1) / tps, tps};
 }
 
-size_t attn_lds_bytes(int NQ, int D) {
-  return (size_t)2 * kAttnBN * (D + 8) * 2 + (size_t)NQ * D * 4 + (size_t)NQ * kAttnBN * 4 +
-         (size_t)NQ * 16;
+bool attn_uses_sums(int Nq, int T, int C) {
+  return Nq <= kAttnSumQueries && (int64_t)Nq * T * C <= kAttnSumEntries;
+}
+
+int attn_part_floats(int Nq, int D, int T, int C) {
+  return D + 2 + (attn_uses_sums(Nq, T, C) ? T * C : 0);
 }
 
 bool launch_attention(const float *q, int H, int Nq, int N, int D, const AttnRec &kr,

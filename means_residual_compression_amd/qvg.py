@@ -98,7 +98,7 @@ def lib() -> ct.CDLL:
             "qvg_candidate_counts": ([p, i64, i64, i64, ct.c_int, P, p, i32], ct.c_int),
             "qvg_attention": ([p, i64, i64, i64, R, P, R, P, ct.c_int, i64, ct.c_float, p, p,
                                p, p, sz, p], ct.c_int),
-            "qvg_attention_workspace_size": ([i64, i64, i64, i64], sz),
+            "qvg_attention_workspace_size": ([i64, i64, i64, i64, P], sz),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -262,6 +262,10 @@ def decompress_chunks(recs: list, p: Params, out_dtype: torch.dtype | None = Non
     return out
 
 
+def attention_workspace_size(H: int, Nq: int, N: int, d: int, vp: Params) -> int:
+    return lib().qvg_attention_workspace_size(H, Nq, N, d, ct.byref(vp))
+
+
 def attention(q: torch.Tensor, k_rec: Record, kp: Params, v_rec: Record, vp: Params,
               scale: float, rope: tuple | None = None, ws: torch.Tensor | None = None,
               out: torch.Tensor | None = None) -> torch.Tensor:
@@ -277,7 +281,7 @@ def attention(q: torch.Tensor, k_rec: Record, kp: Params, v_rec: Record, vp: Par
     if q.dtype != torch.float32 or not q.is_contiguous():
         raise ValueError("q must be contiguous fp32")
     if ws is None:
-        ws = alloc_workspace(lib().qvg_attention_workspace_size(H, Nq, N, d), q.device)
+        ws = alloc_workspace(attention_workspace_size(H, Nq, N, d, vp), q.device)
     if out is None:
         out = torch.empty((H, Nq, d), dtype=torch.float32, device=q.device)
     cos, sin = rope if rope is not None else (None, None)

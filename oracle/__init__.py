@@ -224,10 +224,44 @@ def rope_bf16(k_bits, cos, sin) -> np.ndarray:
     return f32_to_bf16_bits_array(np.concatenate([lo, hi], axis=1).astype(np.float32))
 
 
-def attention(q, k_bits, v_bits, scale, rope=None) -> np.ndarray:
+def reconstruct_exact(codes, scales, assign, cent, bits, G, magnitude=False) -> np.ndarray:
+    """The reconstruction of paper.rainbus.top's DQ step without a final
+    rounding: level(q) * s_hat + C(T)[pi(T)] + ... + C(1)[pi(1)] per element,
+    in fp64 (each term is exact in fp64: an odd level times an E4M3 scale, or
+    a bf16/fp32 centroid).  Codes unpack as stored (element k of a row in
+    byte k*bits/8 at bit offset bits*(k mod 8/bits)); levels are 2q - (2^bits
+    - 1); assignments above C-1 read row C-1.  With magnitude=True returns
+    |level * s_hat| + sum_t |C(t)[pi(t)]| instead (the scale of the rounding
+    errors any evaluation of the sum makes).  cent: [H,T,C,d] fp32 or bf16
+    bit patterns.  Returns [H, N, d] fp64."""
+    codes = np.asarray(codes, np.uint8)
+    H, N, nb = codes.shape
+    d = nb * 8 // bits
+    per, L = 8 // bits, (1 << bits) - 1
+    q = np.empty((H, N, d), np.int64)
+    for k in range(d):
+        q[..., k] = (codes[..., k * bits // 8] >> (bits * (k % per))) & L
+    table = np.array([e4m3_decode(c) for c in range(256)], np.float64)
+    s = np.repeat(table[np.asarray(scales, np.uint8)], G, axis=-1)
+    out = (2 * q - L) * s
+    if magnitude:
+        out = np.abs(out)
+    cent = np.asarray(cent)
+    c64 = (bf16_bits_to_f32(cent) if cent.dtype == np.uint16 else cent).astype(np.float64)
+    T, C = c64.shape[1], c64.shape[2]
+    assign = np.minimum(np.asarray(assign, np.int64), C - 1)
+    for h in range(H):
+        for t in range(T - 1, -1, -1):
+            rows = c64[h, t][assign[h, t]]
+            out[h] += np.abs(rows) if magnitude else rows
+    return out
+
+
+def attention(q, k_bits, v, scale, rope=None) -> np.ndarray:
     """O = softmax(scale * q k^T) v per head, in fp64.
-    q: [H, Nq, d] fp32; k_bits, v_bits: [H, N, d] bf16 bit patterns of the
-    reconstructed keys and values; rope: None or (cos, sin), each [N, d/2]
+    q: [H, Nq, d] fp32; k_bits: [H, N, d] bf16 bit patterns of the
+    reconstructed keys; v: [H, N, d] values (taken as fp64; the attention
+    step uses reconstruct_exact); rope: None or (cos, sin), each [N, d/2]
     fp32, applied to the keys with rope_bf16.  Softmax subtracts the row
     maximum.  Returns [H, Nq, d] fp64."""
     q = np.asarray(q, np.float32).astype(np.float64)
@@ -236,7 +270,7 @@ def attention(q, k_bits, v_bits, scale, rope=None) -> np.ndarray:
     for h in range(H):
         kb = k_bits[h] if rope is None else rope_bf16(k_bits[h], rope[0], rope[1])
         K = bf16_bits_to_f32(kb).astype(np.float64)
-        V = bf16_bits_to_f32(v_bits[h]).astype(np.float64)
+        V = np.asarray(v[h], np.float64)
         S = float(scale) * (q[h] @ K.T)
         S -= S.max(axis=1, keepdims=True)
         P = np.exp(S)

@@ -1,11 +1,13 @@
 """GPU parity of the fused dequant-attention (qvg_attention) with the oracle.
 
-The oracle rebuilds each record's keys and values (oracle.decompress, bf16),
-rotates the keys (oracle.rope_bf16) and evaluates softmax(scale q K^T) V in
-fp64 (oracle.attention).  The kernel works on the same bf16 numbers, so the
-two differ only by the kernel's fp32 roundings of scores, exponentials and
-sums; the test holds every output element to the bound those roundings imply
-for the summation order qvg_attention documents (_bound).  Queries aimed at
+The oracle rebuilds each record's keys (oracle.decompress, bf16) and rotates
+them (oracle.rope_bf16), takes the values unrounded (oracle.reconstruct_exact)
+and evaluates softmax(scale q K^T) V in fp64 (oracle.attention).  The kernel
+uses the same keys, so the two differ only by the kernel's fp32 roundings of
+scores, exponentials, sums and values; the test holds every output element to
+the bound those roundings imply for the summation order qvg_attention
+documents (_bound), on both value paths (weight sums, rebuilt values), and
+requires two calls to agree bit for bit.  Queries aimed at
 single tokens (the first, the last, tile and run boundaries) check that every
 token position takes part: the token they aim at carries most of the weight,
 so a dropped or misplaced token moves the output far beyond the bound."""
@@ -33,21 +35,27 @@ def _gamma(m):
     return m * U / (1 - m * U)
 
 
-def _bound(q, K, V, scale, H, N):
-    """Bound on |kernel - exact| per element for one head; q [Nq, d], K, V
-    [N, d] fp64 holding the exact (bf16 / fp32) values.
+def _bound(q, K, Vabs, scale, H, N, d, vT, vC, sums):
+    """Bound on |kernel - exact| per element for one head; q [Nq, d], K [N, d]
+    fp64 holding the exact (bf16) keys, Vabs [N, d] the magnitude
+    |level*s_hat| + sum_t |C(t)[pi(t)]| of each value (the exact values are
+    level*s_hat + sum_t C(t)[pi(t)]).
 
     Scores: a d-term fp32 multiply-add chain, then one product with scale:
     |s^ - s| <= delta = scale gamma_d sum_k |q_k K_nk| + u |s|.  Each weight
     e^(s - max) then carries a factor e^(+-delta), the exponential's relative
     error (3u times the argument, bounded by the score range, for the
-    argument's roundings, plus 2^-22) and gamma_m from the chain that adds it
-    up (m: the longest chain of the documented order).  Factors shared by a
-    numerator and its denominator (rescales, merge weights) cancel.  Moving
-    the weights of a weighted mean by factors in [a, b] moves it by at most
-    (b/a - 1) max_n |V_n - O| <= (b/a - 1) 2 max|V|; numerator and denominator
-    chains rounding apart add 2 gamma_m |O|, the division u |O|."""
-    d = q.shape[1]
+    argument's roundings, plus 2^-22) and gamma_m from the chains that add it
+    up (m: the longest chain of the documented order; with weight sums also
+    the chain of a weight sum through its run, the merge and the
+    contraction).  Factors shared by a numerator and its denominator
+    (rescales, merge weights) cancel.  Moving the weights of a weighted mean
+    by factors in [a, b] moves it by at most (b/a - 1) max_n |V_n - O| <=
+    (b/a - 1) 2 max|V|; the roundings of the numerator's terms and of the
+    denominator add 2 gamma_m max Vabs, a value rebuilt in fp32 (without
+    weight sums) is within gamma_(T+1) Vabs of exact, the division adds
+    u |O|."""
+    Nq = q.shape[0]
     S = scale * (q @ K.T)
     absdot = np.abs(q) @ np.abs(K).T
     delta = (scale * _gamma(d) * absdot.max(axis=1) + U * np.abs(S).max(axis=1)) * (1 + 1e-6)
@@ -55,10 +63,18 @@ def _bound(q, K, V, scale, H, N):
     tps, nsplit = _runs(H, N)
     P = 256 // d
     m = (64 // P) * tps + tps + P + 2 * nsplit + 8
+    if sums:
+        m = max(m, 64 * tps + tps + 2 * nsplit + vT * vC * d // 512 + 512 // d + 8)
     eps = 2.0 ** -22 + 3 * U * span + _gamma(m)
     ratio = np.exp(2 * delta) * (1 + eps) / (1 - eps) - 1
-    vmax = np.abs(V).max(axis=0)
-    return (2 * ratio[:, None] + 2.1 * _gamma(m) + U) * vmax[None, :]
+    vmax = Vabs.max(axis=0)
+    rebuild = 0.0 if sums else _gamma(vT + 1)
+    return (2 * ratio[:, None] + 2.1 * _gamma(m) + rebuild + U) * vmax[None, :]
+
+
+def _sums(Nq, vpar):
+    T, C = vpar[0], vpar[1]
+    return Nq <= 4 and Nq * T * max(C, 1) <= 4096
 
 
 def _make(seed, H, N, d, kpar, vpar, cdt):
@@ -74,13 +90,19 @@ def _make(seed, H, N, d, kpar, vpar, cdt):
     return out
 
 
-def _oracle_kv(host, p, heads):
+def _oracle_keys(host, p, heads):
     codes, scales, assign, cent = host
     return oracle.decompress(codes[heads], scales[heads], assign[heads], to_oracle(cent)[heads],
                              p.bits, p.group, out_bf16=True)
 
 
-def _aimed_queries(q, K, rope, targets, scale, gap=24.0):
+def _oracle_values(host, p, heads, magnitude=False):
+    codes, scales, assign, cent = host
+    return oracle.reconstruct_exact(codes[heads], scales[heads], assign[heads],
+                                    to_oracle(cent)[heads], p.bits, p.group, magnitude=magnitude)
+
+
+def _aimed_queries(q, K, targets, scale, gap=24.0):
     """Replace queries 1.. with ones aimed at single tokens: q = a K_n for
     the rotated key K_n, with a such that the token's score is gap."""
     for j, n in enumerate(targets, start=1):
@@ -91,14 +113,19 @@ def _aimed_queries(q, K, rope, targets, scale, gap=24.0):
     return q
 
 
-def _check(got, q, kb, vb, scale, rope, H, N, heads):
+def _check(got, q, kb, vh, vp, scale, rope, H, N, heads):
+    """got [H, Nq, d] from the kernel; kb bf16 keys and vh the value record
+    (host) of the checked heads."""
+    d = q.shape[2]
+    sums = _sums(q.shape[1], (vp.T, vp.C))
+    V = _oracle_values(vh, vp, heads)
+    Vabs = _oracle_values(vh, vp, heads, magnitude=True)
     worst = 0.0
     for hi, h in enumerate(heads):
         kbh = kb[hi] if rope is None else oracle.rope_bf16(kb[hi], rope[0], rope[1])
         K = oracle.bf16_bits_to_f32(kbh).astype(np.float64)
-        V = oracle.bf16_bits_to_f32(vb[hi]).astype(np.float64)
-        ref = oracle.attention(q[h:h + 1], kb[hi:hi + 1], vb[hi:hi + 1], scale, rope)[0]
-        tol = _bound(q[h].astype(np.float64), K, V, scale, H, N)
+        ref = oracle.attention(q[h:h + 1], kb[hi:hi + 1], V[hi:hi + 1], scale, rope)[0]
+        tol = _bound(q[h].astype(np.float64), K, Vabs[hi], scale, H, N, d, vp.T, vp.C, sums)
         err = np.abs(got[h].astype(np.float64) - ref)
         bad = np.argwhere(err > tol)
         assert bad.size == 0, (f"head {h}: {len(bad)} elements outside the bound; first "
@@ -113,17 +140,20 @@ CASES = [
     (2, 333, 64, 3, (1, 40, 4, 32), (3, 64, 2, 16), torch.float32, True),
     (3, 20000, 128, 16, (4, 256, 2, 16), (4, 256, 2, 16), torch.bfloat16, True),
     (1, 1, 128, 5, (0, 1, 4, 128), (0, 1, 2, 64), torch.bfloat16, False),
+    (2, 777, 128, 2, (1, 16, 2, 64), (0, 1, 4, 32), torch.bfloat16, True),
     (4, 321, 128, 4, (1, 256, 2, 64), (1, 256, 2, 64), torch.bfloat16, True),
+    (2, 2500, 128, 4, (8, 256, 2, 64), (8, 256, 2, 64), torch.bfloat16, True),
     (5, 130000, 64, 2, (2, 128, 2, 16), (1, 32, 4, 64), torch.float32, False),
 ]
 
 
 @pytest.mark.parametrize("H,N,d,Nq,kpar,vpar,cdt,rope", CASES)
 def test_attention_matches_oracle(H, N, d, Nq, kpar, vpar, cdt, rope):
-    say("attention", H, N, d, Nq, kpar, vpar, cdt, "rope" if rope else "")
+    say("attention", H, N, d, Nq, kpar, vpar, cdt, "rope" if rope else "",
+        "weight sums" if _sums(Nq, vpar) else "rebuilt values")
     (kh, kd, kp), (vh, vd, vp) = _make(17 + N % 97, H, N, d, kpar, vpar, cdt)
     heads = list(range(H))
-    kb, vb = _oracle_kv(kh, kp, heads), _oracle_kv(vh, vp, heads)
+    kb = _oracle_keys(kh, kp, heads)
     tabs = synth.rope_tables(N, d, start=3) if rope else None
     rope_np = (tabs[0].numpy(), tabs[1].numpy()) if rope else None
     scale = float(np.float32(1.0 / np.sqrt(d)))
@@ -134,50 +164,63 @@ def test_attention_matches_oracle(H, N, d, Nq, kpar, vpar, cdt, rope):
     for h in heads:
         kbh = kb[h] if rope_np is None else oracle.rope_bf16(kb[h], *rope_np)
         K = oracle.bf16_bits_to_f32(kbh).astype(np.float64)
-        q[h] = _aimed_queries(q[h], K, rope_np, targets, scale)
+        q[h] = _aimed_queries(q[h], K, targets, scale)
     qd = torch.from_numpy(q).to(DEV)
     rd = (tabs[0].to(DEV), tabs[1].to(DEV)) if rope else None
     out = qvg.attention(qd, kd, kp, vd, vp, scale, rope=rd)
+    again = qvg.attention(qd, kd, kp, vd, vp, scale, rope=rd)
     torch.cuda.synchronize()
-    worst = _check(out.cpu().numpy(), q, kb, vb, scale, rope_np, H, N, heads)
+    got = out.cpu().numpy()
+    assert np.array_equal(got, again.cpu().numpy()), "two calls differ"
+    worst = _check(got, q, kb, vh, vp, scale, rope_np, H, N, heads)
     say("  worst error / bound", worst)
 
 
-def test_attention_decode_record_full_size():
-    """The decode-side record (40 heads x 262144 tokens, d=128, T=4, C=256,
-    INT2, groups of 64) for keys and values, 16 queries per head with the
-    rotary tables, in the launch the benchmark times; heads 0, 17 and 39 are
-    checked against the oracle."""
-    H, N, d, Nq = 40, 262144, 128, 16
-    say("attention full size", H, N, d, Nq)
+@pytest.fixture(scope="module")
+def decode_records():
+    """The decode-side records (40 heads x 262144 tokens, d=128, T=4, C=256,
+    INT2, groups of 64) for keys and values, with the rotary tables."""
+    H, N, d = 40, 262144, 128
     par = (4, 256, 2, 64)
-    (kh, kd, kp), (vh, vd, vp) = _make(4, H, N, d, par, par, torch.bfloat16)
+    say("drawing the decode-side records", H, N, d)
+    recs = _make(4, H, N, d, par, par, torch.bfloat16)
+    return H, N, d, recs, synth.rope_tables(N, d)
+
+
+@pytest.mark.parametrize("Nq", [1, 16])
+def test_attention_decode_record_full_size(decode_records, Nq):
+    """Nq queries per head over the decode-side records, in the launch the
+    benchmark times; heads 0, 17 and 39 are checked against the oracle."""
+    H, N, d, ((kh, kd, kp), (vh, vd, vp)), tabs = decode_records
+    say("attention full size", H, N, d, Nq)
     heads = [0, 17, 39]
-    kb, vb = _oracle_kv(kh, kp, heads), _oracle_kv(vh, vp, heads)
-    tabs = synth.rope_tables(N, d)
+    kb = _oracle_keys(kh, kp, heads)
     rope_np = (tabs[0].numpy(), tabs[1].numpy())
     scale = float(np.float32(1.0 / np.sqrt(d)))
     q = synth.queries(9, H, Nq, d).numpy()
     tps, _ = _runs(H, N)
     for hi, h in enumerate(heads):
         K = oracle.bf16_bits_to_f32(oracle.rope_bf16(kb[hi], *rope_np)).astype(np.float64)
-        q[h] = _aimed_queries(q[h], K, rope_np, [0, N - 1, 64 * tps, 64 * tps - 1, 123457], scale)
+        q[h] = _aimed_queries(q[h], K, [0, N - 1, 64 * tps, 64 * tps - 1, 123457], scale)
     out = qvg.attention(torch.from_numpy(q).to(DEV), kd, kp, vd, vp, scale,
                         rope=(tabs[0].to(DEV), tabs[1].to(DEV)))
     torch.cuda.synchronize()
-    worst = _check(out.cpu().numpy(), q, kb, vb, scale, rope_np, H, N, heads)
+    say("  checking heads", heads)
+    worst = _check(out.cpu().numpy(), q, kb, vh, vp, scale, rope_np, H, N, heads)
     say("  worst error / bound", worst)
 
 
 def test_attention_workspace_and_rejects():
-    """Workspace sizing follows the documented runs; invalid calls fail with
-    the documented status before any launch."""
-    L = qvg.lib()
-    for H, N, d, Nq in ((40, 262144, 128, 16), (3, 20000, 128, 1), (1, 1, 64, 2)):
+    """Workspace sizing follows the documented runs and record layout;
+    invalid calls fail with the documented status before any launch."""
+    vp4 = qvg.params(C=256, T=4, iters=1, bits=2, group=64)
+    for H, N, d, Nq in ((40, 262144, 128, 16), (40, 262144, 128, 1), (3, 20000, 128, 1),
+                        (1, 1, 64, 2)):
         tps, ns = _runs(H, N)
-        assert L.qvg_attention_workspace_size(H, Nq, N, d) >= H * ns * Nq * (d + 2) * 4
-    assert L.qvg_attention_workspace_size(2, 17, 100, 128) == 0
-    assert L.qvg_attention_workspace_size(2, 1, 100, 96) == 0
+        extra = 4 * 256 if _sums(Nq, (4, 256)) else 0
+        assert qvg.attention_workspace_size(H, Nq, N, d, vp4) >= H * ns * Nq * (d + 2 + extra) * 4
+    assert qvg.attention_workspace_size(2, 17, 100, 128, vp4) == 0
+    assert qvg.attention_workspace_size(2, 1, 100, 96, vp4) == 0
     q = torch.zeros((2, 1, 128), device=DEV)
     (kh, kd, kp), (vh, vd, vp) = _make(3, 2, 100, 128, (1, 16, 2, 64), (1, 16, 2, 64),
                                        torch.bfloat16)
