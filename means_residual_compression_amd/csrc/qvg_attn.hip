@@ -240,7 +240,7 @@ __device__ __forceinline__ void st16(uint16_t *p, const uint32_t w[4]) {
 constexpr float kLazyRescale = 8.0f;  // weights stay below e^8 between rescales
 
 template <typename Tc, int D, int NQ, bool SUMS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NQ == 16 ? 2 : 3)))
 void k_attn_split(const float *__restrict__ q, int Nq, int N, int H, AttnRec kr, AttnRec vr,
                   float scale, const float *__restrict__ rcos, const float *__restrict__ rsin,
                   int nsplit, int tiles_per_split, int pf, float *__restrict__ part) {
