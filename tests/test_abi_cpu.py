@@ -175,3 +175,32 @@ def test_operating_point_presets():
     assert (q.C, q.T, q.bits, q.group) == (256, 1, 2, 64)
     assert (p.C, p.T, p.bits, p.group, p.iters) == (256, 4, 2, 16, 5)
     assert qvg.preset("pro", bits=4).bits == 4
+
+
+def test_attention_rejects():
+    """qvg_attention validates before any launch: NULL pointers, a single
+    rope table, Nq outside [1, 16], unsupported d or params, misaligned
+    pointers, and a small workspace return the documented status codes."""
+    L = qvg.lib()
+    p = qvg.params(16, 2, 1, 2, 64)
+    r = qvg._Record(FAKE, FAKE, FAKE, FAKE)
+    ws_need = L.qvg_attention_workspace_size(2, 1, 1000, 128, ct.byref(p))
+    assert ws_need > 0
+
+    def call(q=FAKE, H=2, Nq=1, d=128, kp=p, vp=p, cos=None, sin=None, out=FAKE, ws=FAKE,
+             ws_bytes=1 << 40, N=1000):
+        return L.qvg_attention(q, H, Nq, d, ct.byref(r), ct.byref(kp), ct.byref(r), ct.byref(vp),
+                               qvg.QVG_BF16, N, 0.1, cos, sin, out, ws, ws_bytes, None)
+
+    assert call(q=None) == INVALID
+    assert call(out=None) == INVALID
+    assert call(cos=FAKE) == INVALID and "rope" in L.qvg_last_error().decode()
+    assert call(Nq=0) == INVALID and call(Nq=17) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(kp=qvg.params(16, 2, 1, 3, 64)) == UNSUPPORTED
+    assert call(vp=qvg.params(300, 2, 1, 2, 64)) == UNSUPPORTED
+    assert call(q=FAKE + 4) == INVALID
+    assert call(ws_bytes=ws_need - 1) == WORKSPACE
+    assert call(ws=FAKE + 16) == WORKSPACE
+    assert L.qvg_attention_workspace_size(2, 17, 1000, 128, ct.byref(p)) == 0
+    assert L.qvg_attention_workspace_size(2, 1, 1000, 128, None) == 0
