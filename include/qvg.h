@@ -240,8 +240,8 @@ qvg_status qvg_group_quant_pack(const void *r, qvg_dtype dtype, int64_t H, int64
  *     term sum_n p_n C(t)[pi_t(n)] is taken as sum_c C(t)[c] * (the weights
  *     of the tokens assigned to c). Each weight sum is an add chain over a
  *     run's tokens (rescaled at most once per tile), merged over runs with a
- *     chain, then contracted with the table rows in 512/d ranges of
- *     T*C*d/512 rows, added in order.
+ *     chain, then contracted with the table rows in 2048/d ranges of
+ *     T*C*d/2048 rows, added in order.
  *   - Otherwise the values are rebuilt in fp32 (the dequant's fused
  *     multiply-add and adds).
  *   ws: device scratch of qvg_attention_workspace_size(H, Nq, N, d, vp)

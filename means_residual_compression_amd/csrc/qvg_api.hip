@@ -365,9 +365,7 @@ size_t qvg_attention_workspace_size(int64_t H, int64_t Nq, int64_t N, int64_t d,
   if (!vp || H < 1 || H > 65535 || N < 1 || N > (1 << 30) || (d != 64 && d != 128) || Nq < 1 ||
       Nq > kAttnMaxQueries || vp->T < 0 || vp->T > kMaxT || (vp->T > 0 && (vp->C < 1 || vp->C > kMaxC)))
     return 0;
-  const AttnSplit sp = attn_split((int)H, N);
-  const int C = std::max(vp->C, 1);
-  return up((size_t)H * sp.nsplit * Nq * attn_part_floats((int)Nq, (int)d, vp->T, C) *
+  return up(attn_scratch_floats((int)H, N, (int)Nq, (int)d, vp->T, std::max(vp->C, 1)) *
             sizeof(float));
 }
 

@@ -33,7 +33,11 @@ bool attn_uses_sums(int Nq, int T, int C);
 // Floats of one (run, query) record in the scratch: m, l, o[D], then the
 // T*C weight sums when attn_uses_sums.
 int attn_part_floats(int Nq, int D, int T, int C);
-// q [H][Nq][D] fp32, part [H][nsplit][Nq][attn_part_floats] fp32 scratch,
+// fp32 scratch floats of one call: the run records, then (with weight sums)
+// the contraction parts [H][Nq][8][D].
+size_t attn_scratch_floats(int H, int64_t N, int Nq, int D, int T, int C);
+// q [H][Nq][D] fp32, part [H][nsplit][Nq][attn_part_floats] fp32 scratch
+// (attn_scratch_floats in all),
 // out [H][Nq][D] fp32; rcos/rsin [N][D/2] fp32 or both null (no rotation).
 // Both records hold centroids of the same dtype (c_bf16).
 bool launch_attention(const float *q, int H, int Nq, int N, int D, const AttnRec &kr,

@@ -31,7 +31,8 @@
 // (channel, half or quarter of the tile), and with weight sums adds each
 // token's weight to W_t[pi_t] (wave w owns the stages t = w mod 4, so every
 // slot has one writer and a fixed order).  At the end of its run it writes
-// (m, l, o[d], W) per query.  k_attn_combine merges the runs and contracts W.
+// (m, l, o[d], W) per query.  k_attn_contract merges W over the runs and
+// contracts it with the value tables; k_attn_combine merges the runs.
 //
 // Summation order (for error bounds): an output element of one run is a
 // fused multiply-add chain over the tokens a thread owns (32 or 16 per tile,
@@ -39,8 +40,8 @@
 // parts are added, then the runs are combined with one more multiply-add
 // chain.  A weight sum is a chain of adds over the run's tokens assigned to
 // its slot (rescaled at most once per tile), combined over runs with a
-// multiply-add chain, then contracted with the table rows in 512/d row
-// ranges of T*C*d/512 rows each, the ranges added in order.
+// multiply-add chain, then contracted with the table rows in 2048/d row
+// ranges of T*C*d/2048 rows each, the ranges added in order.
 #include "qvg_common.h"
 #include "qvg_attn.h"
 #include "qvg_internal.h"
@@ -485,59 +486,82 @@ void k_attn_split(const float *__restrict__ q, int Nq, int N, int H, AttnRec kr,
     }
 }
 
-// Merges the runs of each (query, head): with M the largest run maximum and
-// w_b = e^(m_b - M), O = (sum_b w_b o_b + sum_t sum_c (sum_b w_b W_b[t][c])
-// C(t)[c]) / sum_b w_b l_b (the weight-sum term only with weight sums).
-template <typename Tc, bool SUMS>
-__global__ __launch_bounds__(512) void k_attn_combine(const float *__restrict__ part, int nsplit,
-                                                      int Nq, int D, int pf, AttnRec vr,
-                                                      float *__restrict__ out) {
-  __shared__ float wl[2048];  // summed weight per (stage, centroid): T*C <= 2048
-  __shared__ float red[512];
-  const int qq = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+// Weight-sum term, cut into kContractParts row ranges (one workgroup each):
+// with M the largest run maximum and w_b = e^(m_b - M), each range's rows r
+// get W[r] = sum_b w_b W_b[r] (merged in run order) and its share of
+// sum_r W[r] C[r][k] goes to cpart[h][q][z][k]; 256/d threads per channel
+// take consecutive sub-ranges, added in order.
+constexpr int kContractParts = 8;
+
+template <typename Tc>
+__global__ __launch_bounds__(256) void k_attn_contract(const float *__restrict__ part, int nsplit,
+                                                       int Nq, int D, int pf, AttnRec vr,
+                                                       float *__restrict__ cpart) {
+  __shared__ float wl[2048 / kContractParts];  // T*C <= 2048
+  __shared__ float red[256];
+  const int qq = blockIdx.x, h = blockIdx.y, z = blockIdx.z, t = threadIdx.x;
   const int64_t stride = (int64_t)Nq * pf;
   const float *p = part + ((int64_t)h * nsplit * Nq + qq) * pf;
   float M = -__builtin_inff();
   for (int b = 0; b < nsplit; ++b) M = fmaxf(M, p[b * stride]);
-  const int TC = SUMS ? vr.T * vr.C : 0;
-  if (SUMS) {
-    for (int r = t; r < TC; r += 512) {
-      float acc = 0.0f;
+  const int TC = vr.T * vr.C;
+  const int r0 = z * TC / kContractParts, r1 = (z + 1) * TC / kContractParts, n = r1 - r0;
+  for (int r = t; r < n; r += 256) {
+    float acc = 0.0f;
 #pragma unroll 4
-      for (int b = 0; b < nsplit; ++b)
-        acc = __builtin_fmaf(p[b * stride + 2 + D + r], __expf(p[b * stride] - M), acc);
-      wl[r] = acc;
-    }
-    __syncthreads();
+    for (int b = 0; b < nsplit; ++b)
+      acc = __builtin_fmaf(p[b * stride + 2 + D + r0 + r], __expf(p[b * stride] - M), acc);
+    wl[r] = acc;
   }
-  const int k = t % D, kp = t / D, np = 512 / D;
+  __syncthreads();
+  const int k = t % D, kp = t / D, np = 256 / D;
+  const int a0 = kp * n / np, a1 = (kp + 1) * n / np;
+  const Tc *cent = static_cast<const Tc *>(vr.cent) + ((size_t)h * TC + r0) * D;
   float acc = 0.0f;
-  if (SUMS) {  // rows [kp*TC/np, (kp+1)*TC/np) of the head's tables
-    const Tc *cent = static_cast<const Tc *>(vr.cent) + (size_t)h * TC * D;
-    const int r0 = kp * TC / np, r1 = (kp + 1) * TC / np;
 #pragma unroll 8
-    for (int r = r0; r < r1; ++r) {
-      float c;
-      if constexpr (sizeof(Tc) == 2)
-        c = __uint_as_float((uint32_t)cent[(size_t)r * D + k] << 16);
-      else
-        c = cent[(size_t)r * D + k];
-      acc = __builtin_fmaf(wl[r], c, acc);
-    }
+  for (int r = a0; r < a1; ++r) {
+    float c;
+    if constexpr (sizeof(Tc) == 2)
+      c = __uint_as_float((uint32_t)cent[(size_t)r * D + k] << 16);
+    else
+      c = cent[(size_t)r * D + k];
+    acc = __builtin_fmaf(wl[r], c, acc);
   }
   red[t] = acc;
   __syncthreads();
   if (kp == 0) {
-    float l = 0.0f, o = 0.0f;
-    for (int b = 0; b < nsplit; ++b) {
-      const float w = __expf(p[b * stride] - M);
-      l = __builtin_fmaf(p[b * stride + 1], w, l);
-      o = __builtin_fmaf(p[b * stride + 2 + k], w, o);
-    }
-    if (SUMS)
-      for (int j = 0; j < np; ++j) o += red[j * D + k];
-    out[((int64_t)h * Nq + qq) * D + k] = o / l;
+    float o = 0.0f;
+    for (int j2 = 0; j2 < np; ++j2) o += red[j2 * D + k];
+    cpart[(((int64_t)h * Nq + qq) * kContractParts + z) * D + k] = o;
   }
+}
+
+// Merges the runs of each (query, head): with M the largest run maximum and
+// w_b = e^(m_b - M), O = (sum_b w_b o_b + the weight-sum term) / sum_b w_b l_b,
+// the weight-sum term (with weight sums only) being the contraction parts
+// added in order.
+template <bool SUMS>
+__global__ __launch_bounds__(128) void k_attn_combine(const float *__restrict__ part, int nsplit,
+                                                      int Nq, int D, int pf,
+                                                      const float *__restrict__ cpart,
+                                                      float *__restrict__ out) {
+  const int qq = blockIdx.x, h = blockIdx.y, k = threadIdx.x;
+  if (k >= D) return;
+  const int64_t stride = (int64_t)Nq * pf;
+  const float *p = part + ((int64_t)h * nsplit * Nq + qq) * pf;
+  float M = -__builtin_inff();
+  for (int b = 0; b < nsplit; ++b) M = fmaxf(M, p[b * stride]);
+  float l = 0.0f, o = 0.0f;
+  for (int b = 0; b < nsplit; ++b) {
+    const float w = __expf(p[b * stride] - M);
+    l = __builtin_fmaf(p[b * stride + 1], w, l);
+    o = __builtin_fmaf(p[b * stride + 2 + k], w, o);
+  }
+  if (SUMS) {
+    const float *cp = cpart + ((int64_t)h * Nq + qq) * kContractParts * D + k;
+    for (int z = 0; z < kContractParts; ++z) o += cp[z * D];
+  }
+  out[((int64_t)h * Nq + qq) * D + k] = o / l;
 }
 
 namespace {
@@ -565,8 +589,18 @@ bool launch_attn_t(const float *q, int H, int Nq, int N, const AttnRec &kr, cons
                      attn_lds_bytes(NQ, D, SUMS, Nq, TC), s, q, Nq, N, H, kr, vr, scale, rcos,
                      rsin, sp.nsplit, sp.tiles_per_split, pf, part);
   if (hipGetLastError() != hipSuccess) return false;
-  hipLaunchKernelGGL((k_attn_combine<Tc, SUMS>), dim3(Nq, H), dim3(512), 0, s, part, sp.nsplit,
-                     Nq, D, pf, vr, out);
+  float *cpart = part + (size_t)H * sp.nsplit * Nq * pf;
+  if (SUMS && TC > 0) {
+    hipLaunchKernelGGL((k_attn_contract<Tc>), dim3(Nq, H, kContractParts), dim3(256), 0, s, part,
+                       sp.nsplit, Nq, D, pf, vr, cpart);
+    if (hipGetLastError() != hipSuccess) return false;
+  }
+  if (SUMS && TC > 0)
+    hipLaunchKernelGGL(k_attn_combine<true>, dim3(Nq, H), dim3(128), 0, s, part, sp.nsplit, Nq, D,
+                       pf, cpart, out);
+  else
+    hipLaunchKernelGGL(k_attn_combine<false>, dim3(Nq, H), dim3(128), 0, s, part, sp.nsplit, Nq, D,
+                       pf, cpart, out);
   return hipGetLastError() == hipSuccess;
 }
 
@@ -602,6 +636,13 @@ bool attn_uses_sums(int Nq, int T, int C) {
 
 int attn_part_floats(int Nq, int D, int T, int C) {
   return D + 2 + (attn_uses_sums(Nq, T, C) ? T * C : 0);
+}
+
+size_t attn_scratch_floats(int H, int64_t N, int Nq, int D, int T, int C) {
+  const AttnSplit sp = attn_split(H, N);
+  const size_t runs = (size_t)H * sp.nsplit * Nq * attn_part_floats(Nq, D, T, C);
+  const size_t contract = attn_uses_sums(Nq, T, C) ? (size_t)H * Nq * kContractParts * D : 0;
+  return runs + contract;
 }
 
 bool launch_attention(const float *q, int H, int Nq, int N, int D, const AttnRec &kr,
