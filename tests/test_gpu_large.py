@@ -11,6 +11,9 @@
 * The decode-side record: 40 head-tensors x 262144 tokens, T=4, C=256, INT2
   G=64, bf16 centroids; the fused dequant of every token is compared bit for
   bit with the oracle's reconstruction.
+* The stream: 20 chunks of 4680 tokens of 24 head-tensors, the first cold and
+  the rest warm-started from the centroid cache, sampled head-tensors' records
+  and caches compared with the oracle's chain after every chunk.
 """
 import os
 
@@ -73,3 +76,38 @@ def test_decode_record_full_size():
     ref = oracle.decompress(codes, scales, assign, to_oracle(cent), bits, G, out_bf16=True,
                             threads=_threads())
     assert np.array_equal(got, ref), mismatch_report(got, ref)
+
+
+def test_stream_full_size():
+    """The stream workload as the benchmark runs it: 12 K + 12 V head-tensors,
+    20 chunks of 3 frames (4680 tokens each), d=128, bf16, C=256, T=2, INT2
+    G=64; chunk 0 cold (10 iterations from seeded rows), chunks 1-19
+    warm-started from the previous chunk's fp32 centroid cache (3
+    iterations).  After every chunk the records and caches of head-tensors 0
+    (K) and 12 (V) equal the oracle's chain bit for bit."""
+    c = synth.CONFIGS[2]
+    heads = [0, c["heads"]]
+    p = qvg.params(C=c["C"], T=c["T"], iters=c["iters"], bits=c["bits"], group=c["group"])
+    cache, ref_cache = None, None
+    for ci in range(c["chunks"]):
+        x = torch.cat([synth.stream_chunk(2, k, c["heads"], ci, c["F"], c["Hg"], c["Wg"], c["d"],
+                                          c["outlier"][k], c["dtype"]) for k in c["kinds"]], 0)
+        H, N, d = x.shape
+        if cache is None:
+            cache = torch.zeros((H, p.T, p.C, d), dtype=torch.float32, device=DEV)
+        warm = ci > 0
+        idx = None if warm else synth.init_indices(2000, H, p.T, N, p.C)
+        say("stream chunk", ci, "warm" if warm else "cold", (H, N, d))
+        rec = qvg.compress_stream(x.to(DEV), p, c["iters_warm"], cache, warm, init_idx=idx)
+        torch.cuda.synchronize()
+        ref = oracle.compress(to_oracle(x)[heads], C=p.C, T=p.T,
+                              iters=c["iters_warm"] if warm else p.iters, bits=p.bits,
+                              G=p.group, init_idx=None if warm else idx[heads],
+                              init_c=ref_cache, threads=_threads())
+        ref_cache = ref["cache"]
+        sub = qvg.Record(rec.codes[heads], rec.scales[heads], rec.assign[heads],
+                         rec.centroids[heads])
+        bad = rec_equal(sub, ref)
+        assert not bad, f"chunk {ci}: {bad} differ from the oracle"
+        got_cache = cache[heads].cpu().numpy()
+        assert np.array_equal(got_cache, ref_cache), f"chunk {ci}: centroid cache differs"
