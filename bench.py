@@ -271,6 +271,20 @@ def run_decode(args):
     dq = kt["fused_dequant"]
     nbytes = dequant_bytes(H, N, d, C, T, bits, G)
     gbps = nbytes / (dq["avg_ms"] * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        ncores = len(os.sched_getaffinity(0))
+        sel = list(range(min(16, H, ncores)))
+        cb = cent.view(torch.int16).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oracle.decompress(codes[sel], scales[sel], assign[sel], cb[sel], bits, G, out_bf16=True,
+                          threads=len(sel))
+        dt = time.perf_counter() - t0
+        cpu = {"value": dequant_bytes(len(sel), N, d, C, T, bits, G) / dt / 1e9, "unit": "GB/s",
+               "cores": len(sel), "kind": "oracle",
+               "sample": f"{len(sel)} of {H} head-tensors, all {N} tokens, decompress "
+                         f"({dt:.2f} s wall, {ncores} host cores visible)"}
     return {"metric": "fused-dequant GB/s (decode-side record, d=128 C=256 T=4)",
             "value": gbps, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
@@ -282,7 +296,7 @@ def run_decode(args):
                          "traffic": stored_traffic("fused_dequant", "decode"),
                          "kernel": "fused_dequant", "per_launch": f"{nbytes} B",
                          "avg_ms": dq["avg_ms"]},
-            "cpu_baseline": None}
+            "cpu_baseline": cpu}
 
 
 def run_attn(args):
@@ -293,12 +307,14 @@ def run_attn(args):
     to bf16, rotate the keys and evaluate the attention with torch)."""
     dev = torch.device("cuda:0")
     H, N, d, T, C, bits, G, Nq = 40, 262144, 128, 4, 256, 2, 64, args.nq
-    recs = []
+    recs, host0 = [], []
     for seed in (4, 104):
         log(f"drawing the decode-side record (seed {seed}) ...")
         codes, scales, assign, cent = synth.random_record(seed, H, N, d, T, C, bits, G)
         recs.append(qvg.Record(torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev),
                                torch.from_numpy(assign).to(dev), cent.to(dev)))
+        host0.append((codes[:1].copy(), scales[:1].copy(), assign[:1].copy(),
+                      cent[:1].view(torch.int16).numpy().view(np.uint16).copy()))
         del codes, scales, assign
     p = qvg.params(C=C, T=T, iters=1, bits=bits, group=G)
     cos, sin = (t.to(dev) for t in synth.rope_tables(N, d))
@@ -335,6 +351,22 @@ def run_attn(args):
 
     ms_unfused = timed(unfused, max(3, args.steps // 2), 1)
     dq = kernel_times(["fused_dequant"])["fused_dequant"]
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's attention of head-tensor 0: keys decompressed (bf16) and
+        # rotated, values reconstructed unrounded, softmax and products in fp64
+        import oracle
+        (kc, ks, ka, kcent), (vc, vs, va, vcent) = host0
+        q0 = q[:1].cpu().numpy()
+        rope = (cos.cpu().numpy(), sin.cpu().numpy())
+        t0 = time.perf_counter()
+        kb = oracle.decompress(kc, ks, ka, kcent, bits, G, out_bf16=True, threads=1)
+        vx = oracle.reconstruct_exact(vc, vs, va, vcent, bits, G)
+        oracle.attention(q0, kb, vx, scale, rope)
+        dt = time.perf_counter() - t0
+        cpu = {"value": (nbytes / H) / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"head-tensor 0 of {H}, all {N} tokens, {Nq} queries "
+                         f"({dt:.2f} s wall, one thread; numpy fp64)"}
     return {"metric": "fused dequant-attention GB/s (decode-side K and V records, d=128 "
                       "C=256 T=4)",
             "value": gbps, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -352,7 +384,7 @@ def run_attn(args):
                         "total_ms": ms_unfused,
                         "fused_attention_ms": at["avg_ms"],
                         "bf16_kv_bytes_avoided": 2 * H * N * d * 2 * 2},
-            "cpu_baseline": None}
+            "cpu_baseline": cpu}
 
 
 def _mse(x, y):
