@@ -215,6 +215,25 @@ def run_selfforcing(args):
                           "kernel": "fused_dequant",
                           "per_launch": f"{dq_bytes} B", "avg_ms": dq["avg_ms"]},
     }
+    # the other hot-path kernels against HBM: algorithmic bytes per launch
+    # (bf16 input x: 2 B per element; stage t also reads t assignment bytes
+    # per token; averages over the T stages where launches differ by stage)
+    hbm_bytes = {
+        # one read of the stage residual's sources per iteration
+        "kmeans_accumulate": H * N * (2 * d + (p.T - 1) / 2),
+        # x and every stage's assignment in; codes and scales out
+        "group_quant_pack": H * N * (2 * d + p.T + d * p.bits / 8 + d / p.group),
+        # x (+ assignments) in; fp16 fragments and per-token bounds out
+        "kmeans_prepare": H * N * (4 * d + 8 + (p.T - 1) / 2),
+        "absmax": H * N * 2 * d,
+    }
+    for k, nb in hbm_bytes.items():
+        if k in kt:
+            gb = nb / (kt[k]["avg_ms"] * 1e-3) / 1e9
+            rooflines[k] = {"bound": "hbm", "achieved": gb, "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": gb / HBM_PEAK_GBPS, "traffic": None,
+                            "kernel": k, "per_launch": f"{nb:.0f} B",
+                            "avg_ms": kt[k]["avg_ms"]}
     if dominant not in rooflines:
         dominant = "kmeans_assign"
     res = {
