@@ -154,20 +154,27 @@ struct ResView {
   const uint8_t *pi;
   const T *cent;
   int N, D, C, Ts, nsub;
+  int dlog2;  // log2(D): D is 64 or 128, so row offsets are shifts
 
   __device__ __forceinline__ int stage_j(int h, int s, int64_t i) const {
     return min((int)pi[((int64_t)h * Ts + s) * N + i], C - 1);
   }
+  // Row j of stage s of head h: a per-(head, stage) base (uniform) plus a
+  // 32-bit row offset (j < 256).
   __device__ __forceinline__ const T *stage_row(int h, int s, int j) const {
-    return cent + (((int64_t)h * Ts + s) * C + j) * D;
+    return cent + (((int64_t)h * Ts + s) * C << dlog2) + ((uint32_t)j << dlog2);
+  }
+  // Element offset of row i of head h of x.
+  __device__ __forceinline__ int64_t xrow(int h, int64_t i) const {
+    return ((int64_t)h * N + i) << dlog2;
   }
   __device__ __forceinline__ float get(int h, int64_t i, int k) const {
-    float v = Elem<T>::get(x, ((int64_t)h * N + i) * D + k);
+    float v = Elem<T>::get(x, xrow(h, i) + k);
     for (int s = 0; s < nsub; ++s) v = v - Elem<T>::get(stage_row(h, s, stage_j(h, s, i)), k);
     return v;
   }
   __device__ __forceinline__ void load8(int h, int64_t i, int k0, float v[8]) const {
-    ::qvg::load8(x, ((int64_t)h * N + i) * D + k0, v);
+    ::qvg::load8(x, xrow(h, i) + k0, v);
     for (int s = 0; s < nsub; ++s) {
       float c[8];
       ::qvg::load8(stage_row(h, s, stage_j(h, s, i)), k0, c);
@@ -183,7 +190,7 @@ struct ResView {
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) js[s] = stage_j(h, s, i);
     float c[NSUB > 0 ? NSUB : 1][8];
-    ::qvg::load8(x, ((int64_t)h * N + i) * D + k0, v);
+    ::qvg::load8(x, xrow(h, i) + k0, v);
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) ::qvg::load8(stage_row(h, s, js[s]), k0, c[s]);
 #pragma unroll

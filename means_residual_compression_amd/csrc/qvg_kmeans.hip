@@ -1166,6 +1166,7 @@ ResView<T> view_of(const KmArgs &a, int D) {
   v.cent = (const T *)a.rec_cent;
   v.N = a.N;
   v.D = D;
+  v.dlog2 = __builtin_ctz(D);
   v.C = a.C;
   v.Ts = a.Ts;
   v.nsub = a.nsub;

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void k_quant(ResView<T> rv, int G, uint8_t *__
   constexpr int L = (1 << BITS) - 1, MID = 1 << (BITS - 1);
   const int h = blockIdx.y;
   const int N = rv.N, D = rv.D;
-  const int lpt = D / 8, lpg = G / 8;
+  const int lpt = D / 8, lpg = G / 8, glog2 = __builtin_ctz(G);
   const int tpb = (int)blockDim.x / lpt;  // tokens per block and slot
   const int q = (int)threadIdx.x % lpt;
   const int64_t t0 = (int64_t)blockIdx.x * tpb * QU + threadIdx.x / lpt;
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void k_quant(ResView<T> rv, int G, uint8_t *__
   }
   float v[QU][8];
 #pragma unroll
-  for (int u = 0; u < QU; ++u) load8(rv.x, ((int64_t)h * N + min(tok[u], (int64_t)N - 1)) * D + q * 8, v[u]);
+  for (int u = 0; u < QU; ++u) load8(rv.x, rv.xrow(h, min(tok[u], (int64_t)N - 1)) + q * 8, v[u]);
   float c[QU][NSUB > 0 ? NSUB : 1][8];
 #pragma unroll
   for (int u = 0; u < QU; ++u)
@@ -129,11 +129,11 @@ __global__ __launch_bounds__(256) void k_quant(ResView<T> rv, int G, uint8_t *__
     if (tok[u] >= N) continue;
     const int64_t row = (int64_t)h * N + tok[u];
     if (BITS == 2) {
-      reinterpret_cast<uint16_t *>(codes + row * (D / 4))[q] = (uint16_t)packed;
+      reinterpret_cast<uint16_t *>(codes + (row << (rv.dlog2 - 2)))[q] = (uint16_t)packed;
     } else {
-      reinterpret_cast<uint32_t *>(codes + row * (D / 2))[q] = packed;
+      reinterpret_cast<uint32_t *>(codes + (row << (rv.dlog2 - 1)))[q] = packed;
     }
-    if (q % lpg == 0) scales[row * (D / G) + q / lpg] = (uint8_t)e;
+    if (q % lpg == 0) scales[(row << (rv.dlog2 - glog2)) + q / lpg] = (uint8_t)e;
   }
 }
 
@@ -475,6 +475,7 @@ static void launch_quant_t(const void *x, int H, int N, int D, int C, const uint
   rv.cent = (const T *)cent;
   rv.N = N;
   rv.D = D;
+  rv.dlog2 = __builtin_ctz(D);
   rv.C = C;
   rv.Ts = Ts;
   rv.nsub = nsub;
