@@ -120,11 +120,29 @@ __global__ __launch_bounds__(256) void k_quant(ResView<T> rv, int G, uint8_t *__
     const uint32_t e = e4m3_encode(sc);
     const float sh = e4m3_decode(e);
     uint32_t packed = 0;
+    if constexpr (BITS == 2) {
+      // code = #{B in {-2, 0, 2} : fl(r / s_hat) >= B} (the clamped floor(u/2)
+      // + 2).  With round-to-nearest-even, fl(x) >= B exactly when x >= tau(B):
+      // tau(-2) = -2 - 2^-23, tau(0) = -2^-150, tau(2) = 2 - 2^-24 (half the gap
+      // to B's lower neighbour; a tie rounds to B, whose last bit is even).
+      // So fl(r / s_hat) >= B iff r >= tau(B) * s_hat, a product exact in fp64
+      // (at most 25 + 4 significant bits): no division.  s_hat = 0 gives 2.
+      const double sd = (double)sh;
+      const double t1 = (-2.0 - 0x1p-23) * sd, t2 = -0x1p-150 * sd, t3 = (2.0 - 0x1p-24) * sd;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      int cd = MID;
-      if (sh != 0.0f) cd = min(max(floor_half(v[u][k] / sh) + MID, 0), L);
-      packed |= (uint32_t)cd << (BITS * k);
+      for (int k = 0; k < 8; ++k) {
+        const double r = (double)v[u][k];
+        int cd = (r >= t1) + (r >= t2) + (r >= t3);
+        if (sh == 0.0f) cd = MID;
+        packed |= (uint32_t)cd << (2 * k);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        int cd = MID;
+        if (sh != 0.0f) cd = min(max(floor_half(v[u][k] / sh) + MID, 0), L);
+        packed |= (uint32_t)cd << (BITS * k);
+      }
     }
     if (tok[u] >= N) continue;
     const int64_t row = (int64_t)h * N + tok[u];

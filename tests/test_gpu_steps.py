@@ -43,6 +43,49 @@ def test_group_quant_pack(dtype, d, bits, G):
         assert np.array_equal(codes[h].cpu().numpy(), c_ref), mismatch_report(codes[h].cpu(), c_ref)
 
 
+def _boundary_rows(dtype, G=64, d=128):
+    """Rows whose groups have maximum 3 s_hat for an E4M3 value s_hat (so the
+    group's scale is exactly s_hat) and hold every INT2 decision boundary
+    r = B s_hat (B = -2, 0, 2), the neighbouring values of the input dtype on
+    both sides, signed zeros, the smallest subnormals, and the group maximum
+    with both signs; the rest of each group is seeded noise below the maximum."""
+    f32 = dtype == torch.float32
+    s_codes = [0x01, 0x05, 0x08, 0x0F, 0x20, 0x33, 0x38, 0x3B, 0x44, 0x55, 0x66, 0x7E]
+    rng = np.random.default_rng(77)
+    rows = []
+    for sc in s_codes:
+        sh = oracle.e4m3_decode(sc)
+        for sign in (1.0, -1.0):
+            g = np.empty(G, np.float64)
+            vals = [sign * 3 * sh, -sign * 3 * sh, 0.0, -0.0]
+            for B in (-2.0, 0.0, 2.0):
+                x = torch.tensor([B * sh], dtype=torch.float64).to(dtype)
+                up = torch.nextafter(x, torch.tensor([np.inf], dtype=dtype))
+                dn = torch.nextafter(x, torch.tensor([-np.inf], dtype=dtype))
+                vals += [float(x), float(up), float(dn)]
+            tiny = 2.0 ** -149 if f32 else 2.0 ** -133
+            vals += [tiny, -tiny]
+            g[:len(vals)] = vals
+            g[len(vals):] = rng.uniform(-2.9 * sh, 2.9 * sh, G - len(vals))
+            rows.append(g)
+    r = np.stack(rows).reshape(-1, d)  # two groups per token at d = 128
+    return synth.round_to(r[None], dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_group_quant_pack_int2_boundaries(dtype):
+    """INT2 codes at and next to every decision boundary (the kernel decides
+    them by exact threshold comparisons, the oracle by IEEE division) equal
+    the oracle's bit for bit, across the E4M3 scale range."""
+    r = _boundary_rows(dtype)
+    say("group_quant_pack boundaries", dtype, tuple(r.shape))
+    codes, scales = qvg.group_quant_pack(r.to(DEV), 2, 64)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.quantize(as_f32(r)[0], 2, 64)
+    assert np.array_equal(scales[0].cpu().numpy(), s_ref), mismatch_report(scales[0].cpu(), s_ref)
+    assert np.array_equal(codes[0].cpu().numpy(), c_ref), mismatch_report(codes[0].cpu(), c_ref)
+
+
 @pytest.mark.parametrize("rdt,cdt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.float32),
                                      (torch.float32, torch.bfloat16)])
 def test_sas_subtract(rdt, cdt):
