@@ -204,3 +204,27 @@ def test_attention_rejects():
     assert call(ws=FAKE + 16) == WORKSPACE
     assert L.qvg_attention_workspace_size(2, 17, 1000, 128, ct.byref(p)) == 0
     assert L.qvg_attention_workspace_size(2, 1, 1000, 128, None) == 0
+
+
+def _runs(H, N):
+    """Runs of 64-token tiles per head as qvg.h documents them: tps =
+    ceil(ntiles / min(ntiles, ceil(2048/H), 1024)), nsplit = ceil(ntiles/tps)."""
+    ntiles = -(-N // 64)
+    tps = -(-ntiles // min(ntiles, -(-2048 // H), 1024))
+    return tps, -(-ntiles // tps)
+
+
+@pytest.mark.parametrize("H,N,d,Nq,T,C", [(40, 262144, 128, 1, 4, 256), (40, 262144, 128, 16, 4, 256),
+                                          (3, 20000, 128, 4, 1, 256), (1, 1, 64, 2, 0, 1),
+                                          (5, 130000, 64, 2, 1, 32), (2, 2500, 128, 4, 8, 256),
+                                          (65535, 70, 128, 1, 2, 16)])
+def test_attention_workspace_follows_documented_layout(H, N, d, Nq, T, C):
+    """The scratch qvg_attention asks for is the documented run records (m, l,
+    o[d] and, with weight sums, the T*C sums per run and query) plus the
+    eight contraction parts per (head, query), rounded up to 256 bytes."""
+    p = qvg.params(C, T, 1, 2, 64)
+    tps, ns = _runs(H, N)
+    sums = Nq <= 4 and Nq * T * C <= 4096
+    floats = H * ns * Nq * (d + 2 + (T * C if sums else 0)) + (H * Nq * 8 * d if sums else 0)
+    want = -(-floats * 4 // 256) * 256
+    assert qvg.lib().qvg_attention_workspace_size(H, Nq, N, d, ct.byref(p)) == want
