@@ -231,17 +231,6 @@ __device__ __forceinline__ void lds_row8(const uint16_t *row, uint32_t kl, uint3
   }
 }
 
-// Scale bytes of U consecutive rows holding 2^CG scale bytes each (CG <= 2,
-// so the U rows span at most 16 bytes): one load, then byte `soff` of each row.
-template <int CG, int U>
-__device__ __forceinline__ void scale_span(const uint8_t *sp, uint32_t soff, uint32_t *sb) {
-  constexpr int NB = U << CG;
-  uint32_t w[(NB + 3) / 4] = {};
-  __builtin_memcpy(w, sp, NB);
-#pragma unroll
-  for (int u = 0; u < U; ++u) sb[u] = (w[(u << CG) >> 2] >> (8 * (((u << CG) & 3) + soff))) & 0xFFu;
-}
-
 template <int BITS>
 constexpr int dequant_lut_bytes() {
   return 256 * (8 / BITS) * 4;
@@ -329,50 +318,44 @@ __global__ __launch_bounds__(1024) void k_dequant(const uint8_t *__restrict__ co
     const uint32_t n = (uint32_t)(hi - lo);
     const uint32_t step_w = (uint32_t)(tpw * U);  // tokens per wave step
     const uint32_t step = (uint32_t)nw * step_w;
+    // One step's loads, kept as loaded: fetch_* only issue them and emit()
+    // takes the bytes apart, so that a prefetched step's loads stay in flight
+    // while the current step computes.  aw[t]: stage t's assignment bytes of
+    // the U tokens (byte u = token u); sw[u], packed[u]: token u's scale byte
+    // and code bytes.
     struct Batch {
-      uint32_t js[U][T > 0 ? T : 1];
+      uint32_t aw[T > 0 ? T : 1];
+      uint32_t sw[U];
       uint32_t packed[U];
-      uint32_t sb[U];
     };
-    // Global loads of one step.  A lane's U tokens are consecutive
-    // (rel .. rel+U-1), so where the whole wave step lies inside the segment
-    // (a wave-uniform test) each stage's assignment bytes and, for D/G <= 4,
-    // the scale bytes come in one wide load each; the tail loads per token,
-    // clamped to the last token.
-    auto fetch = [&](uint32_t rw, uint32_t rel, Batch &bt) {
-      if (rw + step_w <= n) {
+    // Global loads of one step; a lane's U tokens are rel .. rel+U-1.  Where
+    // the whole wave step lies inside the segment (fetch_full) each stage's
+    // assignment bytes come in one load; the last, partial step (fetch_tail)
+    // loads them per token, clamped to the last token, and packs them alike.
+    // Both load in one fixed sequence (no data-dependent control flow), so
+    // the compiler can leave a prefetched step's loads in flight.
+    auto fetch_token = [&](uint32_t i, int u, Batch &bt) {
+      if constexpr (BITS == 2)
+        bt.packed[u] = *reinterpret_cast<const uint16_t *>(cbase + ((i << db_log2) + coff));
+      else
+        bt.packed[u] = *reinterpret_cast<const uint32_t *>(cbase + ((i << db_log2) + coff));
+      bt.sw[u] = sbase[(i << dg_log2) + soff];
+    };
+    auto fetch_full = [&](uint32_t rel, Batch &bt) {
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-          uint32_t aw = 0;
-          __builtin_memcpy(&aw, abase[t] + rel, U);
+      for (int u = 0; u < U; ++u) fetch_token(rel + (uint32_t)u, u, bt);
 #pragma unroll
-          for (int u = 0; u < U; ++u) bt.js[u][t] = (aw >> (8 * u)) & 0xFFu;
-        }
-        const uint8_t *sp = sbase + (rel << dg_log2);
-        switch (dg_log2) {
-          case 0: scale_span<0, U>(sp, soff, bt.sb); break;
-          case 1: scale_span<1, U>(sp, soff, bt.sb); break;
-          case 2: scale_span<2, U>(sp, soff, bt.sb); break;
-          default:
+      for (int t = 0; t < T; ++t) __builtin_memcpy(&bt.aw[t], abase[t] + rel, U);
+    };
+    auto fetch_tail = [&](uint32_t rel, Batch &bt) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) bt.sb[u] = sp[(u << dg_log2) + soff];
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const uint32_t i = min(rel + (uint32_t)u, n - 1);
-#pragma unroll
-          for (int t = 0; t < T; ++t) bt.js[u][t] = abase[t][i];
-          bt.sb[u] = sbase[(i << dg_log2) + soff];
-        }
-      }
+      for (int t = 0; t < T; ++t) bt.aw[t] = 0;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t i = min(rel + (uint32_t)u, n - 1);
-        if constexpr (BITS == 2)
-          bt.packed[u] = *reinterpret_cast<const uint16_t *>(cbase + ((i << db_log2) + coff));
-        else
-          bt.packed[u] = *reinterpret_cast<const uint32_t *>(cbase + ((i << db_log2) + coff));
+        fetch_token(i, u, bt);
+#pragma unroll
+        for (int t = 0; t < T; ++t) bt.aw[t] |= (uint32_t)abase[t][i] << (8 * u);
       }
     };
     auto emit = [&](uint32_t rel, const Batch &bt) {
@@ -381,7 +364,7 @@ __global__ __launch_bounds__(1024) void k_dequant(const uint8_t *__restrict__ co
       float v[U][8];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float sh = e4m3_decode_bits(bt.sb[u]);
+        const float sh = e4m3_decode_bits(bt.sw[u]);
 #pragma unroll
         for (int m = 0; m < 8 / PB; ++m) {  // code bytes of the 8 channels
           const uint32_t byte = (bt.packed[u] >> (8 * m)) & 0xFFu;
@@ -395,12 +378,12 @@ __global__ __launch_bounds__(1024) void k_dequant(const uint8_t *__restrict__ co
         }
         if constexpr (T > 0) {
           float c[8];
-          lds_row8(tabt[T - 1] + (min(bt.js[u][T - 1], (uint32_t)C - 1) << ch_log2), kl, ch, c);
+          lds_row8(tabt[T - 1] + (min((bt.aw[T - 1] >> (8 * u)) & 0xFFu, (uint32_t)C - 1) << ch_log2), kl, ch, c);
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[u][e] = __builtin_fmaf(v[u][e], sh, c[e]);
 #pragma unroll
           for (int t = T - 2; t >= 0; --t) {
-            lds_row8(tabt[t] + (min(bt.js[u][t], (uint32_t)C - 1) << ch_log2), kl, ch, c);
+            lds_row8(tabt[t] + (min((bt.aw[t] >> (8 * u)) & 0xFFu, (uint32_t)C - 1) << ch_log2), kl, ch, c);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[u][e] = v[u][e] + c[e];
           }
@@ -423,29 +406,45 @@ __global__ __launch_bounds__(1024) void k_dequant(const uint8_t *__restrict__ co
           store8_stream(reinterpret_cast<To *>(obase + (((i << d_log2) + k0) * (uint32_t)sizeof(To))), v[u]);
       }
     };
-    // Control flow follows the wave's first token (uniform); lanes past the
-    // end load clamped tokens and skip their stores.
+    // Steps run in wave-uniform control flow (rw is the wave's first token);
+    // lanes past the end of the partial step load clamped tokens and skip
+    // their stores.
     const uint32_t tl = ((uint32_t)lane >> lpt_log2) * U;
+    uint32_t rw = (uint32_t)(wave * step_w);
+    auto full = [&](uint32_t r) { return __builtin_amdgcn_readfirstlane(r + step_w <= n ? 1 : 0) != 0; };
     if constexpr (T >= 3) {
-      // long add chains: the next step's loads go out before this step's
-      // arithmetic and stores (past the end they re-read clamped tokens)
-      uint32_t rw = (uint32_t)(wave * step_w);
-      if (rw < n) {
-        Batch cur;
-        fetch(rw, rw + tl, cur);
-        for (; rw < n; rw += step) {
-          Batch nxt;
-          fetch(rw + step, rw + step + tl, nxt);
-          emit(rw + tl, cur);
-          cur = nxt;
+      // long add chains: the next full step's loads go out before this
+      // step's arithmetic and stores (after the last full step they re-read
+      // it).  Two batches alternate, so that no loaded register is copied.
+      if (full(rw)) {
+        Batch b0, b1;
+        fetch_full(rw + tl, b0);
+        for (;;) {
+          uint32_t rn = rw + step;
+          bool more = full(rn);
+          fetch_full((more ? rn : rw) + tl, b1);
+          emit(rw + tl, b0);
+          rw = rn;
+          if (!more) break;
+          rn = rw + step;
+          more = full(rn);
+          fetch_full((more ? rn : rw) + tl, b0);
+          emit(rw + tl, b1);
+          rw = rn;
+          if (!more) break;
         }
       }
     } else {
-      for (uint32_t rw = (uint32_t)(wave * step_w); rw < n; rw += step) {
+      for (; full(rw); rw += step) {
         Batch bt;
-        fetch(rw, rw + tl, bt);
+        fetch_full(rw + tl, bt);
         emit(rw + tl, bt);
       }
+    }
+    if (rw < n) {  // the partial step
+      Batch bt;
+      fetch_tail(rw + tl, bt);
+      emit(rw + tl, bt);
     }
     seg = next;
   }
