@@ -113,6 +113,8 @@ def test_sas_subtract(rdt, cdt):
     (8, 256, 2, 64, torch.bfloat16, torch.float32),
     (8, 256, 4, 32, torch.float32, torch.bfloat16, 64),
     (2, 200, 2, 8, torch.bfloat16, torch.bfloat16, 64),
+    (4, 256, 2, 128, torch.bfloat16, torch.bfloat16),  # one scale per row
+    (3, 96, 4, 64, torch.float32, torch.float32, 64),
 ]])
 def test_fused_dequant(T, C, bits, G, cdt, odt, d):
     H, N = 3, 2085
@@ -127,6 +129,25 @@ def test_fused_dequant(T, C, bits, G, cdt, odt, d):
     ref = oracle.decompress(codes, scales, assign, to_oracle(cent), bits, G,
                             out_bf16=odt == torch.bfloat16)
     got = bits16(out) if odt == torch.bfloat16 else out.cpu().numpy()
+    assert np.array_equal(got, ref), mismatch_report(got, ref)
+
+
+@pytest.mark.parametrize("N", [1, 7, 32, 33, 4096, 4127])
+@pytest.mark.parametrize("T", [2, 4])
+def test_fused_dequant_step_edges(T, N):
+    """Token counts around a wave's step: rows that leave every wave a partial
+    step only, exact multiples of the step (no partial step) and a ragged tail
+    after many full steps, with and without the prefetching loop (T >= 3)."""
+    H, d, C, bits, G = 2, 128, 256, 2, 64
+    codes, scales, assign, cent = synth.random_record(31 + N, H, N, d, T, C, bits, G)
+    p = qvg.params(C=C, T=T, iters=1, bits=bits, group=G)
+    rec = qvg.Record(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                     torch.from_numpy(assign).to(DEV), cent.to(DEV))
+    say("fused_dequant step edges", T, N)
+    out = qvg.decompress(rec, p, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.decompress(codes, scales, assign, to_oracle(cent), bits, G, out_bf16=True)
+    got = bits16(out)
     assert np.array_equal(got, ref), mismatch_report(got, ref)
 
 
