@@ -474,24 +474,65 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 }
 
 // ------------------------------------------------------------ resolve
-// Exact fp64 squared distance, channel order, no fused multiply-add: the same
-// arithmetic as a plain sequential loop.
-template <typename Tin, int D>
-__device__ __attribute__((noinline)) double exact_dist(const ResView<Tin> &rv, int h, int64_t i,
-                                                       const float *__restrict__ c) {
-  double acc = 0.0;
-#pragma unroll 1
-  for (int k = 0; k < D; k += 8) {
-    float v[8], w[8];
-    rv.load8(h, i, k, v);
-    load8(c, k, w);
+// Exact fp64 squared distances of token i to NC centroid rows, channel order,
+// no fused multiply-add: the same arithmetic as a plain sequential loop per
+// centroid.  The residual row is rebuilt in fp32 (x minus the NSUB stage rows
+// in stage order) KC channels at a time, every load of a chunk issued
+// together (the stage indices are read once, so no load waits on another),
+// and the NC distances share the residual loads.
+template <typename Tin, int D, int NC, int NSUB>
+__device__ __forceinline__ void exact_dist_n(const ResView<Tin> &rv, int h, int64_t i,
+                                             const float *c0, const float *c1, double *out) {
+  constexpr int KC = 8;
+  const float *cr[2] = {c0, c1};
+  const Tin *sr[NSUB > 0 ? NSUB : 1];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const double df = (double)v[m] - (double)w[m];
-      acc = __dadd_rn(acc, __dmul_rn(df, df));
+  for (int s = 0; s < NSUB; ++s) sr[s] = rv.stage_row(h, s, rv.stage_j(h, s, i));
+  const Tin *xr = rv.x + rv.xrow(h, i);
+  double acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = 0.0;
+#pragma unroll 1
+  for (int k0 = 0; k0 < D; k0 += KC) {
+    float v[KC], w[NC][KC], cs[NSUB > 0 ? NSUB : 1][KC];
+#pragma unroll
+    for (int q = 0; q < KC / 8; ++q) {
+      ::qvg::load8(xr, k0 + 8 * q, v + 8 * q);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) load8(cr[c], k0 + 8 * q, w[c] + 8 * q);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) ::qvg::load8(sr[s], k0 + 8 * q, cs[s] + 8 * q);
     }
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+      for (int m = 0; m < KC; ++m) v[m] = v[m] - cs[s][m];
+#pragma unroll
+    for (int m = 0; m < KC; ++m)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const double df = (double)v[m] - (double)w[c][m];
+        acc[c] = __dadd_rn(acc[c], __dmul_rn(df, df));
+      }
   }
-  return acc;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) out[c] = acc[c];
+}
+
+template <typename Tin, int D, int NC>
+__device__ __forceinline__ void exact_dist(const ResView<Tin> &rv, int h, int64_t i,
+                                                     const float *c0, const float *c1,
+                                                     double *out) {
+  switch (rv.nsub) {
+    case 0: exact_dist_n<Tin, D, NC, 0>(rv, h, i, c0, c1, out); break;
+    case 1: exact_dist_n<Tin, D, NC, 1>(rv, h, i, c0, c1, out); break;
+    case 2: exact_dist_n<Tin, D, NC, 2>(rv, h, i, c0, c1, out); break;
+    case 3: exact_dist_n<Tin, D, NC, 3>(rv, h, i, c0, c1, out); break;
+    case 4: exact_dist_n<Tin, D, NC, 4>(rv, h, i, c0, c1, out); break;
+    case 5: exact_dist_n<Tin, D, NC, 5>(rv, h, i, c0, c1, out); break;
+    case 6: exact_dist_n<Tin, D, NC, 6>(rv, h, i, c0, c1, out); break;
+    default: exact_dist_n<Tin, D, NC, kMaxT - 1>(rv, h, i, c0, c1, out); break;
+  }
 }
 
 // Both the sequential fp64 sum and any other fp64 summation order of the D
@@ -549,8 +590,9 @@ __device__ __forceinline__ void recheck_part(const ResView<Tin> &rv, const float
       } else if (diff < -tol) {
         j = q.w;
       } else {
-        const double d1 = exact_dist<Tin, D>(rv, q.x, q.y, cb + (int64_t)q.z * D);
-        const double d2 = exact_dist<Tin, D>(rv, q.x, q.y, cb + (int64_t)q.w * D);
+        double dd[2];
+        exact_dist<Tin, D, 2>(rv, q.x, q.y, cb + (int64_t)q.z * D, cb + (int64_t)q.w * D, dd);
+        const double d1 = dd[0], d2 = dd[1];
         j = (d2 < d1 || (d2 == d1 && q.w < q.z)) ? q.w : q.z;
       }
       assign[(int64_t)q.x * assign_hstride + q.y] = (uint8_t)j;
@@ -646,7 +688,8 @@ __device__ __forceinline__ void fallback_part(const ResView<Tin> &rv,
     const bool any_near = wnear[0] | wnear[1] | wnear[2] | wnear[3];
     if (any_near) {  // uniform over the workgroup
       const bool mine = t < C && (t == bj || dp - best <= tol * (dp + best));
-      double sb = mine ? exact_dist<Tin, D>(rv, q.x, q.y, ch + (int64_t)t * D) : __builtin_inf();
+      double sb = __builtin_inf();
+      if (mine) exact_dist<Tin, D, 1>(rv, q.x, q.y, ch + (int64_t)t * D, nullptr, &sb);
       int sj = mine ? t : 0x7fffffff;
       for (int o = 32; o > 0; o >>= 1) {
         const double ob = __shfl_xor(sb, o);
@@ -681,7 +724,7 @@ __device__ __forceinline__ void fallback_part(const ResView<Tin> &rv,
 // scans (a workgroup per entry, grid-stride over the scan workgroups).
 // Iterations with few or no candidates cost one small launch.
 template <typename Tin, int D>
-__global__ __launch_bounds__(256) void k_resolve(ResView<Tin> rv, const float *__restrict__ cent,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_resolve(ResView<Tin> rv, const float *__restrict__ cent,
                                                  int C, int Cp, const int4 *__restrict__ rlist,
                                                  const int2 *__restrict__ flist,
                                                  const uint32_t *__restrict__ counters,
