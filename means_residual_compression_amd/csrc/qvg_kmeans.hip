@@ -772,6 +772,25 @@ __global__ __launch_bounds__(256) void k_hist(const uint8_t *__restrict__ assign
   hist[((int64_t)h * nb + b) * kMaxC + threadIdx.x] = cnt[threadIdx.x];
 }
 
+// Inclusive scan of one value per thread over a 256-thread workgroup: a
+// shuffle scan inside each wave, then the totals of the lower waves (two
+// barriers; ws holds at least 4 words of shared memory).  Integer adds, so
+// the result does not depend on the order.
+__device__ __forceinline__ uint32_t scan256_incl(uint32_t v, uint32_t *ws) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) ws[wave] = v;
+  __syncthreads();
+  uint32_t add = 0;
+  for (int w = 0; w < wave; ++w) add += ws[w];
+  __syncthreads();  // ws may be written again by the next scan
+  return v + add;
+}
+
 __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ assign,
                                                  int64_t assign_hstride, int N, int Cp,
                                                  const uint32_t *__restrict__ hist,
@@ -779,7 +798,7 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ass
                                                  int32_t *__restrict__ offs,
                                                  int32_t *__restrict__ cofs,
                                                  int32_t *__restrict__ chunk_j, int maxch) {
-  __shared__ uint32_t scan[kMaxC];
+  __shared__ uint32_t scan[4];
   __shared__ uint32_t wbase[4][kMaxC];
   const int h = blockIdx.y, b = blockIdx.x, nb = gridDim.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -804,17 +823,9 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ass
     tot += c;
     pre += bb < b ? c : 0u;
   }
-  // exclusive scan of the totals over the 256 byte values (Hillis-Steele);
-  // assignment bytes >= C (corrupt input only) get slots after the clusters
-  uint32_t mine = tot;
-  scan[t] = mine;
-  __syncthreads();
-  for (int o = 1; o < kMaxC; o <<= 1) {
-    const uint32_t add = t >= o ? scan[t - o] : 0u;
-    __syncthreads();
-    scan[t] = mine = mine + add;
-    __syncthreads();
-  }
+  // exclusive scan of the totals over the 256 byte values; assignment bytes
+  // >= C (corrupt input only) get slots after the clusters
+  const uint32_t mine = scan256_incl(tot, scan);
   const uint32_t excl = mine - tot;
   if (b == 0) {
     if (t <= Cp) offs[(int64_t)h * (Cp + 1) + t] = (int32_t)excl;
@@ -822,16 +833,7 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ass
     // chunks of kAccChunk consecutive members per cluster: exclusive scan of
     // the chunk counts of clusters 0..Cp-1, and the chunk -> cluster map
     const uint32_t nch = t < Cp ? (tot + kAccChunk - 1) / kAccChunk : 0u;
-    __syncthreads();
-    uint32_t cm = nch;
-    scan[t] = cm;
-    __syncthreads();
-    for (int o = 1; o < kMaxC; o <<= 1) {
-      const uint32_t add = t >= o ? scan[t - o] : 0u;
-      __syncthreads();
-      scan[t] = cm = cm + add;
-      __syncthreads();
-    }
+    const uint32_t cm = scan256_incl(nch, scan);
     const uint32_t cex = cm - nch;
     if (t <= Cp) cofs[(int64_t)h * (Cp + 1) + t] = (int32_t)cex;
     if (Cp == kMaxC && t == kMaxC - 1) cofs[(int64_t)h * (Cp + 1) + Cp] = (int32_t)cm;
