@@ -231,6 +231,19 @@ __device__ __forceinline__ void lds_row8(const uint16_t *row, uint32_t kl, uint3
   }
 }
 
+// Row j of a stage table from a lane's base (the table plus the lane's channel
+// offset, in bytes) with one shift-add: bf16 rows are 2^rsh bytes.
+__device__ __forceinline__ void lds_row8_at(const char *lane_base, uint32_t j, uint32_t rsh,
+                                            float c[8]) {
+  const uint4 w = *reinterpret_cast<const uint4 *>(lane_base + (j << rsh));
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[2 * i] = __uint_as_float(u[i] << 16);
+    c[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+  }
+}
+
 template <int BITS>
 constexpr int dequant_lut_bytes() {
   return 256 * (8 / BITS) * 4;
@@ -315,6 +328,12 @@ __global__ __launch_bounds__(1024) void k_dequant(const uint8_t *__restrict__ co
     const TL *tabt[T > 0 ? T : 1];  // stage tables of this slice
 #pragma unroll
     for (int t = 0; t < T; ++t) tabt[t] = tab + (uint32_t)t * C * ch;
+    // bf16 tables: each stage's table plus this lane's channel offset, in bytes
+    constexpr bool TB = std::is_same<TL, uint16_t>::value;
+    const uint32_t rsh = (uint32_t)ch_log2 + 1;
+    const char *tlane[T > 0 ? T : 1];
+#pragma unroll
+    for (int t = 0; t < T; ++t) tlane[t] = reinterpret_cast<const char *>(tabt[t] + kl);
     const uint32_t n = (uint32_t)(hi - lo);
     const uint32_t step_w = (uint32_t)(tpw * U);  // tokens per wave step
     const uint32_t step = (uint32_t)nw * step_w;
@@ -378,12 +397,16 @@ __global__ __launch_bounds__(1024) void k_dequant(const uint8_t *__restrict__ co
         }
         if constexpr (T > 0) {
           float c[8];
-          lds_row8(tabt[T - 1] + (min((bt.aw[T - 1] >> (8 * u)) & 0xFFu, (uint32_t)C - 1) << ch_log2), kl, ch, c);
+          const uint32_t jT = min((bt.aw[T - 1] >> (8 * u)) & 0xFFu, (uint32_t)C - 1);
+          if constexpr (TB) lds_row8_at(tlane[T - 1], jT, rsh, c);
+          else lds_row8(tabt[T - 1] + (jT << ch_log2), kl, ch, c);
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[u][e] = __builtin_fmaf(v[u][e], sh, c[e]);
 #pragma unroll
           for (int t = T - 2; t >= 0; --t) {
-            lds_row8(tabt[t] + (min((bt.aw[t] >> (8 * u)) & 0xFFu, (uint32_t)C - 1) << ch_log2), kl, ch, c);
+            const uint32_t jt = min((bt.aw[t] >> (8 * u)) & 0xFFu, (uint32_t)C - 1);
+            if constexpr (TB) lds_row8_at(tlane[t], jt, rsh, c);
+            else lds_row8(tabt[t] + (jt << ch_log2), kl, ch, c);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[u][e] = v[u][e] + c[e];
           }
