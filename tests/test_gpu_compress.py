@@ -98,6 +98,33 @@ def test_C_equals_N_is_lossless(dtype):
     assert int(rec.scales.max()) == 0
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_exact_ties_at_later_stages(dtype):
+    """Stage 1 starts from every token's own row (C = N), so its residual is
+    exactly zero; every later stage starts from centroids +a*e and -a*e (an
+    exact tie for every token) plus distant rows.  Each token of stages 2..4
+    then needs the exact sequential distances of its two tied candidates on a
+    residual rebuilt from 1..3 earlier stages, and the tie goes to the smaller
+    index."""
+    N, T = 200, 4
+    x = synth.video_cache(0, 1, 2, 1, 10, 20, 64, 50.0, dtype)
+    H, d = x.shape[0], x.shape[2]
+    rng = np.random.default_rng(17)
+    init_c = np.zeros((H, T, N, d), np.float32)
+    init_c[:, 0] = x.float().numpy()
+    e = np.zeros(d, np.float32)
+    e[3] = 1.5
+    for t in range(1, T):
+        init_c[:, t] = (rng.standard_normal((H, N, d)) * 40 + 100).astype(np.float32)
+        init_c[:, t, 0] = e
+        init_c[:, t, 1] = -e
+    p = qvg.params(C=N, T=T, iters=2, bits=2, group=32)
+    say("exact ties at later stages", dtype)
+    rec, out, cache, ref, ref_out = _run_both(x, p, init_c=init_c)
+    _check(rec, out, cache, ref, ref_out)
+    assert int(rec.assign[:, 1].max()) == 0  # every token took the smaller tied index
+
+
 def test_duplicate_init_indices_and_caller_init():
     x = synth.video_cache(1, 0, 2, 3, 30, 52, 128, 1e2, torch.bfloat16)
     N = x.shape[1]
