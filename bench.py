@@ -421,6 +421,34 @@ def _events_ms(fn):
     return e0.elapsed_time(e1), r
 
 
+def cpu_baseline_stream(chunks_cpu, p, idx0, iters_warm):
+    """The oracle on the host's cores: chunk 0 cold (untimed, for its cache),
+    then the given warm chunks, each warm-started from the previous chunk's
+    fp32 centroids, timed."""
+    import oracle
+    ncores = len(os.sched_getaffinity(0))
+    H, N = chunks_cpu[0].shape[:2]
+    threads = min(ncores, H)
+
+    def host(x):
+        return x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 \
+            else x.numpy()
+    ref = oracle.compress(host(chunks_cpu[0]), C=p.C, T=p.T, iters=p.iters, bits=p.bits,
+                          G=p.group, init_idx=idx0, threads=threads)
+    cache = ref["cache"]
+    t0 = time.perf_counter()
+    for x in chunks_cpu[1:]:
+        ref = oracle.compress(host(x), C=p.C, T=p.T, iters=iters_warm, bits=p.bits, G=p.group,
+                              init_c=cache, threads=threads)
+        cache = ref["cache"]
+    dt = time.perf_counter() - t0
+    nw = len(chunks_cpu) - 1
+    return {"value": nw * H * N / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"warm chunks 1-{nw} of the stream, all {H} head-tensors x {N} tokens, "
+                      f"{iters_warm} iterations per stage from the previous chunk's cache, after "
+                      f"chunk 0 cold (untimed); {dt:.1f} s wall, {ncores} host cores visible"}
+
+
 def run_stream(args):
     """A 60-frame stream in 20 chunks of 3 frames (4680 tokens) of 12 K + 12 V
     head-tensors: cold chunks (10 iterations from seeded rows) against warm
@@ -428,11 +456,14 @@ def run_stream(args):
     dev = torch.device("cuda:0")
     c = synth.CONFIGS[2]
     log("generating the stream chunks ...")
-    chunks = []
+    chunks, chunks_cpu = [], []
     for ci in range(c["chunks"]):
         parts = [synth.stream_chunk(2, k, c["heads"], ci, c["F"], c["Hg"], c["Wg"], c["d"],
                                     c["outlier"][k], c["dtype"]) for k in c["kinds"]]
-        chunks.append(torch.cat(parts, 0).to(dev))
+        xc = torch.cat(parts, 0)
+        if ci < 5:  # the host baseline's sample
+            chunks_cpu.append(xc)
+        chunks.append(xc.to(dev))
     H, N, d = chunks[0].shape
     p = qvg.params(C=c["C"], T=c["T"], iters=c["iters"], bits=c["bits"], group=c["group"])
     ws = qvg.alloc_workspace(qvg.workspace_size(H, N, d, chunks[0].dtype, p), dev)
@@ -482,6 +513,28 @@ def run_stream(args):
                "reconstruct_hbm_frac": hbytes / (hms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                "per_chunk_decompress_ms": sms}
     del kv, hist, per
+    # per-kernel durations over one more warm pass (HIP events around every
+    # launch); the roofline is the k-means assign's, the dominant kernel
+    qvg.timing_reset()
+    qvg.timing_enable(True)
+    for x in chunks[1:]:
+        qvg.compress_stream(x, p, c["iters_warm"], cache, True, ws=ws, out=rec)
+    torch.cuda.synchronize()
+    qvg.timing_enable(False)
+    kt = kernel_times(qvg.KERNELS)
+    asg = kt["kmeans_assign"]
+    asg_flops = 2.0 * H * N * p.C * d
+    asg_tflops = asg_flops / (asg["avg_ms"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": asg_tflops, "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": asg_tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                "kernel": "kmeans_assign",
+                "per_launch": f"{asg_flops:.4g} flop (2*N*C*d over {H} head-tensors)",
+                "avg_ms": asg["avg_ms"]}
+    cb = None
+    if not args.no_cpu_baseline:
+        log("oracle baseline on the host cores ...")
+        cb = cpu_baseline_stream(chunks_cpu, p, synth.init_indices(2000, H, p.T, N, p.C),
+                                 c["iters_warm"])
     return {"metric": "streamed compress tokens/s (warm-started chunks)",
             "value": warm["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
             "steps": len(chunks), "warmup": args.warmup,
@@ -494,7 +547,8 @@ def run_stream(args):
             "warm_speedup": cold["total_ms"] / warm["total_ms"],
             "mse_ratio_warm_over_cold": float(np.mean(warm["mse_per_chunk"][1:]) /
                                               np.mean(cold["mse_per_chunk"][1:])),
-            "roofline": None, "cpu_baseline": None}
+            "roofline": roofline, "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kt.items()},
+            "cpu_baseline": cb}
 
 
 def run_pro(args):
