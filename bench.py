@@ -174,9 +174,9 @@ def cpu_baseline_selfforcing(x_cpu, p, idx, rec_gpu, heads):
 # --------------------------------------------------------------- workloads
 def run_selfforcing(args):
     dev = torch.device("cuda:0")
-    c = synth.CONFIGS[1]
+    c = synth.CONFIGS["self_forcing"]
     log("generating the self-forcing-shaped cache ...")
-    x_cpu = synth.config_cache(1)
+    x_cpu = synth.config_cache("self_forcing")
     H, N, d = x_cpu.shape
     p = qvg.params(C=c["C"], T=c["T"], iters=c["iters"], bits=c["bits"], group=c["group"])
     idx = synth.init_indices(1, H, p.T, N, p.C)
@@ -454,7 +454,7 @@ def run_stream(args):
     head-tensors: cold chunks (10 iterations from seeded rows) against warm
     chunks (3 iterations from the previous chunk's fp32 centroids)."""
     dev = torch.device("cuda:0")
-    c = synth.CONFIGS[2]
+    c = synth.CONFIGS["stream"]
     log("generating the stream chunks ...")
     chunks, chunks_cpu = [], []
     for ci in range(c["chunks"]):
@@ -561,9 +561,9 @@ def run_pro(args):
     oracle check of one K and one V head-tensor, bit for bit."""
     import oracle
     dev = torch.device("cuda:0")
-    c = synth.CONFIGS[1]
+    c = synth.CONFIGS["self_forcing"]
     log("generating the self-forcing-shaped cache ...")
-    x_cpu = synth.config_cache(1)
+    x_cpu = synth.config_cache("self_forcing")
     H, N, d = x_cpu.shape
     nk = c["heads"]
     kinds = {"K": slice(0, nk), "V": slice(nk, H)}
@@ -653,10 +653,10 @@ def run_large(args):
     of 21 frames on a 39x40 grid), d=128, bf16, C=256, 8 iterations, T=4,
     INT2 and INT4 (G=64); the per-stage MSE curve and the record sizes."""
     dev = torch.device("cuda:0")
-    c = synth.CONFIGS[3]
+    c = synth.CONFIGS["long_video"]
     heads = args.large_heads or c["heads"]
     log(f"generating the long-video cache ({2 * heads} head-tensors) ...")
-    x = synth.config_cache(3, heads=heads, workers=min(16, len(os.sched_getaffinity(0)))).to(dev)
+    x = synth.config_cache("long_video", heads=heads, workers=min(16, len(os.sched_getaffinity(0)))).to(dev)
     H, N, d = x.shape
     idx = torch.from_numpy(synth.init_indices(3, H, c["T"], N, c["C"])).pin_memory()
     out = torch.empty_like(x)

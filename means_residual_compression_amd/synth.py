@@ -81,13 +81,13 @@ def _head_rounded(args):
     return round_to(video_head(seed, F, Hg, Wg, d, outlier_scale, scene_len, n_tokens), dtype)
 
 
-def video_cache(cfg: int, kind: int, heads: int, F: int, Hg: int, Wg: int, d: int,
+def video_cache(family: int, kind: int, heads: int, F: int, Hg: int, Wg: int, d: int,
                 outlier_scale: float, dtype: torch.dtype, scene_len: int | None = None,
                 n_tokens: int | None = None, head_ids=None, workers: int = 1) -> torch.Tensor:
-    """[heads, N, d] CPU tensor; head h uses seed (1000 + 100*cfg + h, kind).
+    """[heads, N, d] CPU tensor; head h uses seed (1000 + 100*family + h, kind).
     `workers` > 1 draws the heads in that many processes (same values)."""
     ids = list(range(heads) if head_ids is None else head_ids)
-    jobs = [(_seed(cfg, kind, h), F, Hg, Wg, d, outlier_scale, scene_len, n_tokens, dtype)
+    jobs = [(_seed(family, kind, h), F, Hg, Wg, d, outlier_scale, scene_len, n_tokens, dtype)
             for h in ids]
     if workers > 1 and len(jobs) > 1:
         import concurrent.futures as cf
@@ -100,12 +100,12 @@ def video_cache(cfg: int, kind: int, heads: int, F: int, Hg: int, Wg: int, d: in
     return torch.stack(hs)
 
 
-def _seed(cfg: int, kind: int, h: int) -> int:
-    return (1000 + 100 * cfg + h) * 2 + kind
+def _seed(family: int, kind: int, h: int) -> int:
+    return (1000 + 100 * family + h) * 2 + kind
 
 
 # ---------------------------------------------------------------- stream chunks
-def stream_chunk(cfg: int, kind: int, heads: int, chunk: int, frames_per_chunk: int,
+def stream_chunk(family: int, kind: int, heads: int, chunk: int, frames_per_chunk: int,
                  Hg: int, Wg: int, d: int, outlier_scale: float,
                  dtype: torch.dtype) -> torch.Tensor:
     """Chunk `chunk` of a continuing video: global frames
@@ -114,8 +114,8 @@ def stream_chunk(cfg: int, kind: int, heads: int, chunk: int, frames_per_chunk: 
     P = Hg * Wg
     out = np.empty((heads, frames_per_chunk * P, d), dtype=np.float64)
     for h in range(heads):
-        base, drift, _ = _head_fields(_rng(_seed(cfg, kind, h)), Hg, Wg, d, outlier_scale)
-        rng = _rng(_seed(cfg, kind, h), chunk + 1)
+        base, drift, _ = _head_fields(_rng(_seed(family, kind, h)), Hg, Wg, d, outlier_scale)
+        rng = _rng(_seed(family, kind, h), chunk + 1)
         for j in range(frames_per_chunk):
             f = chunk * frames_per_chunk + j
             frame = base + 0.05 * f * drift + 0.1 * rng.standard_normal((Hg, Wg, d))
@@ -137,28 +137,29 @@ def init_indices(seed: int, H: int, T: int, N: int, C: int) -> np.ndarray:
 
 # ---------------------------------------------------------------- named workloads
 CONFIGS = {
-    # name: (cfg id, F, Hg, Wg, d, heads per kind, dtype, kinds, scene_len, N)
-    0: dict(F=16, Hg=16, Wg=16, d=64, heads=1, dtype=torch.float32, kinds=(K_KIND,),
+    # name: seed family, F, Hg, Wg, d, heads per kind, dtype, kinds, method
+    # parameters (and scene_len, N, chunking where they apply)
+    "tiny": dict(seed=0, F=16, Hg=16, Wg=16, d=64, heads=1, dtype=torch.float32, kinds=(K_KIND,),
             outlier={K_KIND: 50.0}, C=16, T=1, iters=10, bits=2, group=32),
-    1: dict(F=21, Hg=30, Wg=52, d=128, heads=12, dtype=torch.bfloat16, kinds=(K_KIND, V_KIND),
+    "self_forcing": dict(seed=1, F=21, Hg=30, Wg=52, d=128, heads=12, dtype=torch.bfloat16, kinds=(K_KIND, V_KIND),
             outlier=OUTLIER_SCALE, C=256, T=2, iters=8, bits=2, group=64),
-    2: dict(F=3, Hg=30, Wg=52, d=128, heads=12, dtype=torch.bfloat16, kinds=(K_KIND, V_KIND),
+    "stream": dict(seed=2, F=3, Hg=30, Wg=52, d=128, heads=12, dtype=torch.bfloat16, kinds=(K_KIND, V_KIND),
             outlier=OUTLIER_SCALE, C=256, T=2, iters=10, iters_warm=3, bits=2, group=64,
             chunks=20),
-    3: dict(F=85, Hg=39, Wg=40, d=128, heads=32, dtype=torch.bfloat16, kinds=(K_KIND, V_KIND),
+    "long_video": dict(seed=3, F=85, Hg=39, Wg=40, d=128, heads=32, dtype=torch.bfloat16, kinds=(K_KIND, V_KIND),
             outlier=OUTLIER_SCALE, C=256, T=4, iters=8, bits=2, group=64, scene_len=21,
             n_tokens=131072),
 }
 
 
-def config_cache(cfg: int, heads: int | None = None, n_tokens: int | None = None,
+def config_cache(name: str, heads: int | None = None, n_tokens: int | None = None,
                  workers: int = 1) -> torch.Tensor:
     """All head-tensors of a configuration stacked K-then-V: [kinds*heads, N, d].
     `heads`/`n_tokens` give a smaller sample of the same workload."""
-    c = CONFIGS[cfg]
+    c = CONFIGS[name]
     nh = c["heads"] if heads is None else heads
     N = c.get("n_tokens") if n_tokens is None else n_tokens
-    parts = [video_cache(cfg, k, nh, c["F"], c["Hg"], c["Wg"], c["d"], c["outlier"][k],
+    parts = [video_cache(c["seed"], k, nh, c["F"], c["Hg"], c["Wg"], c["d"], c["outlier"][k],
                          c["dtype"], c.get("scene_len"), N, workers=workers)
              for k in c["kinds"]]
     return torch.cat(parts, 0)

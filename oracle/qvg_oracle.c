@@ -22,7 +22,7 @@
  *          dequantize, then add back C(t)[pi(t)] from stage T down to stage 1.
  *   [FMT]  howistudyai.com "Step-by-step": assignments stored as uint8 (K=256).
  *
- * Readings taken where the pages are silent (each also listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - distance is squared Euclidean; argmin ties go to the smallest index;
  *   - one k-means iteration = assign then update; the returned pi comes from
  *     the last assign and the returned centroids from the last update;

@@ -43,8 +43,8 @@ def _check(rec, out, cache, ref, ref_out):
 
 def test_tiny_fp32_config_full():
     """16 frames x 16x16 grid, d=64, fp32, C=16, 10 iterations, T=1, INT2 G=32."""
-    c = synth.CONFIGS[0]
-    x = synth.config_cache(0)
+    c = synth.CONFIGS["tiny"]
+    x = synth.config_cache("tiny")
     p = qvg.params(C=c["C"], T=c["T"], iters=c["iters"], bits=c["bits"], group=c["group"])
     idx = synth.init_indices(100, x.shape[0], p.T, x.shape[1], p.C)
     say("tiny fp32 config", tuple(x.shape))
@@ -180,8 +180,8 @@ def test_self_forcing_cache_full_size():
     """21 frames x 30x52 = 32760 tokens, d=128, bf16, C=256, 8 iterations,
     T=2, INT2 G=64: all 12 K and 12 V head-tensors, record and reconstruction
     bit-exact against the oracle."""
-    cfg = synth.CONFIGS[1]
-    x = synth.config_cache(1)
+    cfg = synth.CONFIGS["self_forcing"]
+    x = synth.config_cache("self_forcing")
     p = qvg.params(C=cfg["C"], T=cfg["T"], iters=cfg["iters"], bits=cfg["bits"],
                    group=cfg["group"])
     idx = synth.init_indices(1, x.shape[0], p.T, x.shape[1], p.C)
@@ -194,9 +194,9 @@ def test_pro_preset_self_forcing_full_size():
     3 K and 3 V head-tensors of the self-forcing-shaped cache at full length
     (32760 tokens), one call per tensor kind: records, cache and
     reconstructions bit-exact against the oracle."""
-    cfg = synth.CONFIGS[1]
+    cfg = synth.CONFIGS["self_forcing"]
     nk = cfg["heads"]
-    x = synth.config_cache(1)
+    x = synth.config_cache("self_forcing")
     p = qvg.preset("pro", iters=cfg["iters"])
     for kind, rows in (("K", [0, 5, 11]), ("V", [nk, nk + 6, nk + 11])):
         xk = x[rows].contiguous()

@@ -33,7 +33,7 @@ def _threads():
 
 
 def _large_heads(kinds):
-    c = synth.CONFIGS[3]
+    c = synth.CONFIGS["long_video"]
     parts = [synth.video_cache(3, k, 1, c["F"], c["Hg"], c["Wg"], c["d"], c["outlier"][k],
                                c["dtype"], c["scene_len"], c["n_tokens"], head_ids=[0])
              for k in kinds]
@@ -85,7 +85,7 @@ def test_stream_full_size():
     warm-started from the previous chunk's fp32 centroid cache (3
     iterations).  After every chunk the records and caches of head-tensors 0
     (K) and 12 (V) equal the oracle's chain bit for bit."""
-    c = synth.CONFIGS[2]
+    c = synth.CONFIGS["stream"]
     heads = [0, c["heads"]]
     p = qvg.params(C=c["C"], T=c["T"], iters=c["iters"], bits=c["bits"], group=c["group"])
     cache, ref_cache = None, None

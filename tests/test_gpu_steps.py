@@ -210,7 +210,7 @@ def test_fused_dequant_bf16_rounding():
 
 
 def _video(H, N, d, kind_mix=True, seed_cfg=1):
-    c = synth.CONFIGS[1]
+    c = synth.CONFIGS["self_forcing"]
     heads = []
     for h in range(H):
         kind = h % 2 if kind_mix else 0
