@@ -519,6 +519,7 @@ __device__ __forceinline__ void exact_dist_n(const ResView<Tin> &rv, int h, int6
   for (int c = 0; c < NC; ++c) out[c] = acc[c];
 }
 
+// The view's stage count (runtime) dispatched to the compile-time form.
 template <typename Tin, int D, int NC>
 __device__ __forceinline__ void exact_dist(const ResView<Tin> &rv, int h, int64_t i,
                                                      const float *c0, const float *c1,
@@ -722,7 +723,9 @@ __device__ __forceinline__ void fallback_part(const ResView<Tin> &rv,
 // Both kinds of unsettled tokens in one launch: re-checks of two candidates
 // (a wave per EPW entries, grid-stride over the re-check workgroups) and exact
 // scans (a workgroup per entry, grid-stride over the scan workgroups).
-// Iterations with few or no candidates cost one small launch.
+// Iterations with few or no candidates cost one small launch.  Held to 128
+// registers (4 waves per SIMD, the whole grid resident) with the sequential
+// replica inlined.
 template <typename Tin, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_resolve(ResView<Tin> rv, const float *__restrict__ cent,
                                                  int C, int Cp, const int4 *__restrict__ rlist,
