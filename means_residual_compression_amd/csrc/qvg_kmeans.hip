@@ -807,10 +807,31 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ass
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const uint8_t *a = assign + (int64_t)h * assign_hstride;
   const int lo = b * kSortChunk, hi = min(N, lo + kSortChunk);
+  // this wave's quarter of the chunk: token wlo + lane + 64k is jk[k] (loaded
+  // first, so the loads overlap the count reads below; kSortChunk / 4 = 4 * 64)
+  static_assert(kSortChunk % 256 == 0, "four waves of whole 64-token rounds");
+  constexpr int QW = kSortChunk / 4, KW = QW / 64;
+  const int wlo = min(hi, lo + wave * QW), whi = min(hi, wlo + QW);
+  uint32_t jk[KW];
+#pragma unroll
+  for (int k = 0; k < KW; ++k) {
+    const int i = wlo + lane + 64 * k;
+    jk[k] = i < whi ? (uint32_t)a[i] : 0u;
+  }
   // this chunk's predecessors and all chunks, for byte value t
   const uint32_t *hh = hist + (int64_t)h * nb * kMaxC + t;
   uint32_t pre = 0, tot = 0;
   int bb = 0;
+  for (; bb + 32 <= nb; bb += 32) {  // 32 loads in flight per round
+    uint32_t c[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) c[u] = hh[(int64_t)(bb + u) * kMaxC];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      tot += c[u];
+      pre += bb + u < b ? c[u] : 0u;
+    }
+  }
   for (; bb + 8 <= nb; bb += 8) {
     uint32_t c[8];
 #pragma unroll
@@ -845,9 +866,9 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ass
   // per-wave counts inside the chunk (each wave owns a quarter, in order)
   for (int w = 0; w < 4; ++w) wbase[w][t] = 0;
   __syncthreads();
-  const int q = (kSortChunk / 4);
-  const int wlo = min(hi, lo + wave * q), whi = min(hi, wlo + q);
-  for (int i = wlo + lane; i < whi; i += 64) atomicAdd(&wbase[wave][a[i]], 1u);
+#pragma unroll
+  for (int k = 0; k < KW; ++k)
+    if (wlo + lane + 64 * k < whi) atomicAdd(&wbase[wave][jk[k]], 1u);
   __syncthreads();
   {
     uint32_t run = excl + pre;
@@ -860,10 +881,13 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ass
   __syncthreads();
   int32_t *out = sorted + (int64_t)h * N;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int g = wlo; g < whi; g += 64) {
+#pragma unroll
+  for (int k = 0; k < KW; ++k) {
+    const int g = wlo + 64 * k;
+    if (g >= whi) break;  // wave-uniform
     const int i = g + lane;
     const bool valid = i < whi;
-    const uint32_t j = valid ? a[i] : 0u;
+    const uint32_t j = jk[k];
     uint64_t m = __ballot(valid);
 #pragma unroll
     for (int bit = 0; bit < 8; ++bit) {
