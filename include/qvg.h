@@ -16,11 +16,13 @@
  *  - Device pointers are HIP device memory owned by the caller, contiguous,
  *    row-major, with the shapes given below.  Host pointers are marked (host).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
- *    asynchronously and no entry point synchronises the stream.  The one host
- *    array argument (init_idx) is read by a host-to-device copy enqueued on
- *    `stream`: from pageable memory the HIP runtime stages it before the call
- *    returns; from pinned memory the caller must keep it unchanged until the
- *    stream has passed the call.
+ *    asynchronously and no entry point synchronises the stream.  The one
+ *    array argument that may live on the host (init_idx) is then read by a
+ *    host-to-device copy enqueued on `stream`: from pageable memory the HIP
+ *    runtime stages it before the call returns; from pinned memory the caller
+ *    must keep it unchanged until the stream has passed the call.  Given in
+ *    device memory it is read by the kernels (no copy), and the seeded draw
+ *    (neither init_idx nor init_centroids) runs on the device too.
  *  - Arguments are validated on the host before anything is enqueued; an
  *    invalid call returns a status and enqueues nothing.  The library never
  *    aborts and allocates no device memory: scratch comes from the caller's
@@ -63,6 +65,15 @@ typedef enum { QVG_F32 = 0, QVG_BF16 = 1 } qvg_dtype;
  *   bits   2 or 4 (INT2 / INT4 codes).
  *   group  G, channels per quantization group along d; d % G == 0 and
  *          G % 8 == 0, 8 <= G <= 256.
+ *   seed   seed of the cold-start draw (used when a compress call is given
+ *          neither init_idx nor init_centroids): stage t (1-based) of head h
+ *          (0-based within the call) starts from the rows perm[0..C) of a
+ *          partial Fisher-Yates shuffle of 0..N-1, where step j swaps
+ *          perm[j] with perm[j + (z_j mod (N - j))] and z_j is output j of
+ *          splitmix64 (Steele, Lea and Flood 2014) started from
+ *          seed ^ (0x9E3779B97F4A7C15 * (h+1)) ^ (0xD1B54A32D192ED03 * t),
+ *          all arithmetic modulo 2^64.  The pages only say the start is a
+ *          set of seeded token rows; this draw is the pinned reading.
  * Supported head dims: d in {64, 128}. */
 typedef struct {
     int32_t C;
@@ -70,6 +81,7 @@ typedef struct {
     int32_t iters;
     int32_t bits;
     int32_t group;
+    uint64_t seed;
 } qvg_params;
 
 /* A compressed record of H head-tensors (paper.rainbus.top, method paragraph:
@@ -115,10 +127,14 @@ size_t qvg_workspace_size(int64_t H, int64_t N, int64_t d, qvg_dtype dtype,
  * going to the upper level; a zero scale gives the middle code everywhere.
  *
  * Stage-t k-means starts from:
- *   init_idx (host, int32 [H][T][C]): rows init_idx[h][t][0..C) of R(t-1);
- *            indices must be in [0, N) (duplicates allowed);
- *   else init_centroids (device, fp32 [H][T][C][d]).
- * Exactly one of them must be non-NULL when T >= 1.
+ *   init_idx (int32 [H][T][C], host or device memory): rows
+ *            init_idx[h][t][0..C) of R(t-1); duplicates allowed.  Host
+ *            indices outside [0, N) are rejected (QVG_ERR_INVALID_ARG);
+ *            device indices are not read by the host and are clamped to
+ *            [0, N-1] by the kernel;
+ *   else init_centroids (device, fp32 [H][T][C][d]);
+ *   else (both NULL) rows of R(t-1) drawn from p->seed (see qvg_params).
+ * At most one of init_idx and init_centroids may be non-NULL.
  * cache_out (device, fp32 [H][T][C][d], nullable) receives each stage's final
  * fp32 centroids before rounding (the streaming centroid cache).
  * Workspace: `ws` of at least qvg_workspace_size() bytes. */
@@ -133,8 +149,9 @@ qvg_status qvg_compress(const void *x, qvg_dtype dtype, int64_t H, int64_t N, in
  *   cache (device, fp32 [H][T][C][d]) is read as the stage initialisation when
  *   warm != 0 and is overwritten with this chunk's final centroids.
  *   warm != 0: k-means runs `iters_warm` iterations from the cache.
- *   warm == 0: k-means runs p->iters iterations from init_idx (host, as in
- *   qvg_compress).
+ *   warm == 0: k-means runs p->iters iterations from init_idx (host or
+ *   device, as in qvg_compress), or from rows drawn from p->seed when
+ *   init_idx is NULL.
  * The record is self-contained: decompress needs no other chunk. */
 qvg_status qvg_compress_stream(const void *chunk, qvg_dtype dtype, int64_t H, int64_t N,
                                int64_t d, const qvg_params *p, int32_t iters_warm, float *cache,

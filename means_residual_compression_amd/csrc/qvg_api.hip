@@ -139,10 +139,24 @@ float kappa_for(int64_t d) {
   return std::nextafter((float)k, 1.0f);
 }
 
+// True when p is device (or managed) memory that kernels can read; pageable
+// or pinned host memory is false.  The query's error for unregistered host
+// pointers is cleared.
+bool device_resident(const void *p) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged;
+}
+
+// idx: device rows [H][T][C] of every stage start, or nullptr when the
+// stages start from init_c.
 template <typename Tin, typename Tc, int D>
 qvg_status run_compress(const void *x, int64_t H, int64_t N, const qvg_params *p, int32_t iters,
-                        bool use_idx, const float *init_c, float *cache_out, const qvg_record *out,
-                        const Ws &w, hipStream_t s) {
+                        const int32_t *idx, const float *init_c, float *cache_out,
+                        const qvg_record *out, const Ws &w, hipStream_t s) {
   const int T = p->T, C = p->C;
   const int Cp = std::max(32, pad32(C));
   const int NT = (int)((N + kTile - 1) / kTile);
@@ -166,9 +180,9 @@ qvg_status run_compress(const void *x, int64_t H, int64_t N, const qvg_params *p
     KmArgs a;
     a.H = (int)H; a.N = (int)N; a.C = C; a.Cp = Cp; a.NT = NT;
     a.x = x; a.rec_pi = out->assign; a.rec_cent = out->centroids; a.Ts = T; a.nsub = t;
-    a.idx = use_idx ? w.idx + (int64_t)t * C : nullptr;
+    a.idx = idx ? idx + (int64_t)t * C : nullptr;
     a.idx_hstride = (int64_t)T * C;
-    a.init = use_idx ? nullptr : init_c + (int64_t)t * C * D;
+    a.init = idx ? nullptr : init_c + (int64_t)t * C * D;
     a.init_hstride = rec_hstride;
     a.assign = out->assign + (int64_t)t * N;
     a.assign_hstride = (int64_t)T * N;
@@ -215,16 +229,21 @@ qvg_status compress_impl(const void *x, qvg_dtype dtype, int64_t H, int64_t N, i
   if (p->T > 0) {
     if (!out->assign || !out->centroids)
       return fail(QVG_ERR_INVALID_ARG, "out->assign and out->centroids must be non-NULL when T >= 1");
-    if ((init_idx == nullptr) == (init_c == nullptr))
-      return fail(QVG_ERR_INVALID_ARG, "exactly one of init_idx and init_centroids must be given");
+    if (init_idx && init_c)
+      return fail(QVG_ERR_INVALID_ARG, "give at most one of init_idx and init_centroids");
   }
-  const bool use_idx = p->T > 0 && init_idx != nullptr;
-  const Layout L = make_layout(H, N, d, p->C, p->T, use_idx);
+  // stage starts: host rows (validated, then copied), device rows (read by
+  // the kernels), caller centroids, or rows drawn from p->seed on the device
+  const bool rows = p->T > 0 && init_c == nullptr;
+  const bool rows_dev = rows && init_idx != nullptr && device_resident(init_idx);
+  const bool rows_host = rows && init_idx != nullptr && !rows_dev;
+  const bool rows_seeded = rows && init_idx == nullptr;
+  const Layout L = make_layout(H, N, d, p->C, p->T, rows_host || rows_seeded);
   if (!ws) return fail(QVG_ERR_WORKSPACE, "workspace is NULL");
   if (ws_bytes < L.total)
     return fail(QVG_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, L.total);
   if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(QVG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (use_idx) {
+  if (rows_host) {
     const int64_t n = H * p->T * p->C;
     for (int64_t q = 0; q < n; ++q)
       if (init_idx[q] < 0 || init_idx[q] >= N)
@@ -233,15 +252,18 @@ qvg_status compress_impl(const void *x, qvg_dtype dtype, int64_t H, int64_t N, i
   }
   const Ws w = carve(ws, L);
   hipStream_t s = (hipStream_t)stream;
-  if (use_idx &&
+  if (rows_host &&
       hipMemcpyAsync(w.idx, init_idx, (size_t)(H * p->T * p->C) * 4, hipMemcpyHostToDevice, s) != hipSuccess)
     return hip_fail("copy init_idx");
+  if (rows_seeded && !launch_sample_rows((int)H, p->T, (int)N, p->C, p->seed, w.idx, s))
+    return hip_fail("seeded rows");
+  const int32_t *idx = rows_dev ? init_idx : (rows ? w.idx : nullptr);
   const bool bf = dtype == QVG_BF16;
   if (d == 64)
-    return bf ? run_compress<uint16_t, uint16_t, 64>(x, H, N, p, iters, use_idx, init_c, cache_out, out, w, s)
-              : run_compress<float, float, 64>(x, H, N, p, iters, use_idx, init_c, cache_out, out, w, s);
-  return bf ? run_compress<uint16_t, uint16_t, 128>(x, H, N, p, iters, use_idx, init_c, cache_out, out, w, s)
-            : run_compress<float, float, 128>(x, H, N, p, iters, use_idx, init_c, cache_out, out, w, s);
+    return bf ? run_compress<uint16_t, uint16_t, 64>(x, H, N, p, iters, idx, init_c, cache_out, out, w, s)
+              : run_compress<float, float, 64>(x, H, N, p, iters, idx, init_c, cache_out, out, w, s);
+  return bf ? run_compress<uint16_t, uint16_t, 128>(x, H, N, p, iters, idx, init_c, cache_out, out, w, s)
+            : run_compress<float, float, 128>(x, H, N, p, iters, idx, init_c, cache_out, out, w, s);
 }
 
 }  // namespace
@@ -285,7 +307,6 @@ qvg_status qvg_compress_stream(const void *chunk, qvg_dtype dtype, int64_t H, in
   if (warm)
     return compress_impl(chunk, dtype, H, N, d, p, iters_warm, nullptr, cache, cache, out, ws,
                          ws_bytes, stream);
-  if (p->T > 0 && !init_idx) return fail(QVG_ERR_INVALID_ARG, "a cold chunk needs init_idx");
   return compress_impl(chunk, dtype, H, N, d, p, p->iters, init_idx, nullptr, cache, out, ws,
                        ws_bytes, stream);
 }

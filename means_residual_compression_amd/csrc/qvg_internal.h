@@ -46,6 +46,9 @@ struct KmArgs {
 };
 
 bool launch_stage_bound(uint32_t *prev_stats, int stat_stride, int H, hipStream_t s);
+// Seeded cold-start rows idx[h][t][0..C) for every head and stage (the draw
+// documented with qvg_params.seed).
+bool launch_sample_rows(int H, int T, int N, int C, uint64_t seed, int32_t *idx, hipStream_t s);
 template <typename Tin>
 bool launch_absmax(const void *x, int H, int64_t per_head, uint32_t *stats, int stat_stride,
                    int slot, hipStream_t s);

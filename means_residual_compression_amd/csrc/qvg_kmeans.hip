@@ -98,6 +98,74 @@ __global__ void k_stage_bound(uint32_t *stats, int stat_stride, int H) {
   st[kStatWords + S_MAXR] = __float_as_uint((r + fmaxf(r, c)) * (1.0f + 0x1p-7f));
 }
 
+// ------------------------------------------------------- seeded rows
+// Cold-start rows of stage t (1-based) of head h: a partial Fisher-Yates
+// shuffle of 0..N-1 driven by splitmix64 (Steele, Lea and Flood 2014; output
+// j is the generator state seed_ht + (j+1)*0x9E3779B97F4A7C15 passed through
+// the two published xor-shift-multiply rounds and a final xor-shift), with
+// seed_ht = seed ^ (0x9E3779B97F4A7C15*(h+1)) ^ (0xD1B54A32D192ED03*t).  Step j
+// swaps positions j and j + (z_j mod (N-j)); row j is the value then at
+// position j.  One wave per (head, stage): the C offsets are computed in
+// parallel (the generator is a counter), the swaps run in order on a sparse
+// permutation: positions below C in a dense LDS array, positions from C on in
+// a list of at most C (position, value) pairs searched by the whole wave.
+__device__ __forceinline__ uint64_t splitmix_at(uint64_t s, uint64_t k) {
+  uint64_t z = s + 0x9E3779B97F4A7C15ull * k;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__global__ __launch_bounds__(64) void k_sample(int N, int C, int T, uint64_t seed,
+                                               int32_t *__restrict__ idx) {
+  __shared__ uint32_t off[kMaxC];
+  __shared__ int32_t front[kMaxC], bpos[kMaxC], bval[kMaxC];
+  const int h = blockIdx.y, t = blockIdx.x + 1, lane = threadIdx.x;
+  const uint64_t s0 = seed ^ (0x9E3779B97F4A7C15ull * (uint64_t)(h + 1)) ^
+                      (0xD1B54A32D192ED03ull * (uint64_t)t);
+  for (int j = lane; j < C; j += 64) {
+    off[j] = (uint32_t)(splitmix_at(s0, (uint64_t)j + 1) % (uint64_t)(N - j));
+    front[j] = j;
+  }
+  __syncthreads();
+  int32_t *out = idx + ((int64_t)h * T + (t - 1)) * C;
+  int nb = 0;  // entries of the list (wave-uniform)
+  for (int j = 0; j < C; ++j) {
+    const int k = j + (int)off[j];
+    const int32_t vj = front[j];
+    int32_t vk;
+    if (k < C) {
+      vk = front[k];
+      __syncthreads();
+      if (lane == 0) front[k] = vj;
+    } else {
+      int at = -1;
+      for (int q = lane; q < nb; q += 64)
+        if (bpos[q] == k) at = q;
+      const uint64_t m = __ballot(at >= 0);
+      const int pos = m ? __shfl(at, __builtin_ctzll(m)) : -1;
+      if (pos >= 0) {
+        vk = bval[pos];
+        __syncthreads();
+        if (lane == 0) bval[pos] = vj;
+      } else {
+        vk = k;
+        __syncthreads();
+        if (lane == 0) {
+          bpos[nb] = k;
+          bval[nb] = vj;
+        }
+        ++nb;
+      }
+    }
+    if (lane == 0) {
+      front[j] = vk;
+      out[j] = vk;
+    }
+    __syncthreads();
+  }
+}
+
 // --------------------------------------------------------------- init
 // Wave per (head, centroid): cent[h][j] = R[h][idx[h][j]] (gather) or
 // init[h][j] (copy); stats max |c| into S_MAXC.  Padded centroids j >= C
@@ -117,7 +185,9 @@ __global__ void k_init(ResView<Tin> rv, const int32_t *__restrict__ idx,
     float v = 0.0f;
     if (j < C) {
       if (idx) {
-        const int64_t row = idx[(int64_t)h * idx_hstride + j];
+        // rows outside [0, N) only arrive from unchecked device arrays: clamped
+        const int64_t row = min(max((int64_t)idx[(int64_t)h * idx_hstride + j], (int64_t)0),
+                                (int64_t)rv.N - 1);
         v = rv.get(h, row, k);
       } else {
         v = init[(int64_t)h * init_hstride + (int64_t)j * D + k];
@@ -1209,6 +1279,13 @@ bool allow_lds(const void *fn, size_t bytes) {
          hipSuccess;
 }
 }  // namespace
+
+bool launch_sample_rows(int H, int T, int N, int C, uint64_t seed, int32_t *idx, hipStream_t s) {
+  TimerScope ts_("kmeans_init", s);
+  hipLaunchKernelGGL(k_sample, dim3(T, H), dim3(64), 0, s, N, C, T, seed, idx);
+  QVG_CHECK_LAUNCH();
+  return true;
+}
 
 bool launch_stage_bound(uint32_t *prev_stats, int stat_stride, int H, hipStream_t s) {
   TimerScope ts_("kmeans_init", s);

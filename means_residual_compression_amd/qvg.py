@@ -37,7 +37,7 @@ class QvgError(RuntimeError):
 
 class Params(ct.Structure):
     _fields_ = [("C", ct.c_int32), ("T", ct.c_int32), ("iters", ct.c_int32),
-                ("bits", ct.c_int32), ("group", ct.c_int32)]
+                ("bits", ct.c_int32), ("group", ct.c_int32), ("seed", ct.c_uint64)]
 
 
 class _Record(ct.Structure):
@@ -133,8 +133,10 @@ def _dev(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be a contiguous device tensor")
 
 
-def params(C: int, T: int, iters: int, bits: int, group: int) -> Params:
-    return Params(C, T, iters, bits, group)
+def params(C: int, T: int, iters: int, bits: int, group: int, seed: int = 0) -> Params:
+    """Method parameters; `seed` drives the cold-start draw when a compress
+    call gets neither init_idx nor init_centroids."""
+    return Params(C, T, iters, bits, group, seed)
 
 
 # The two operating points the howistudyai.com explainer names ("Step-by-step",
@@ -177,13 +179,14 @@ def empty_record(H, N, d, p: Params, dtype: torch.dtype, device) -> Record:
 
 
 def _idx_ptr(init_idx):
-    """Host int32 [H, T, C] indices: a numpy array, or a CPU torch tensor
-    (pinned memory keeps the library's host-to-device copy asynchronous)."""
+    """int32 [H, T, C] start rows: a numpy array or a CPU torch tensor (pinned
+    memory keeps the library's host-to-device copy asynchronous), or a device
+    tensor (read by the kernels, no copy)."""
     if init_idx is None:
         return None, None
     if isinstance(init_idx, torch.Tensor):
-        if init_idx.is_cuda or init_idx.dtype != torch.int32 or not init_idx.is_contiguous():
-            raise ValueError("init_idx must be a contiguous host int32 tensor")
+        if init_idx.dtype != torch.int32 or not init_idx.is_contiguous():
+            raise ValueError("init_idx must be a contiguous int32 tensor")
         return init_idx, ct.c_void_p(init_idx.data_ptr())
     a = np.ascontiguousarray(init_idx, dtype=np.int32)
     return a, a.ctypes.data_as(ct.c_void_p)
@@ -191,7 +194,9 @@ def _idx_ptr(init_idx):
 
 def compress(x: torch.Tensor, p: Params, init_idx=None, init_centroids=None, cache_out=None,
              ws: torch.Tensor | None = None, out: Record | None = None) -> Record:
-    """x: [H, N, d] bf16/fp32 device tensor.  init_idx: host int32 [H, T, C]."""
+    """x: [H, N, d] bf16/fp32 device tensor.  Stage starts: init_idx (int32
+    [H, T, C], host or device), else init_centroids (fp32 [H, T, C, d]), else
+    rows drawn from p.seed."""
     _dev(x, "x")
     H, N, d = x.shape
     out = out or empty_record(H, N, d, p, x.dtype, x.device)
@@ -320,7 +325,8 @@ class CompressedKVCache:
 
     def append(self, chunk: torch.Tensor, init_idx=None) -> Record:
         """Compresses the next chunk [H, N, d] and appends its record; the
-        first chunk starts cold from init_idx, later ones warm from the cache.
+        first chunk starts cold from init_idx (or from rows drawn from
+        p.seed when it is None), later ones warm from the cache.
         Evicts the oldest chunks while the records exceed max_bytes."""
         H, N, d = chunk.shape
         need = workspace_size(H, N, d, chunk.dtype, self.p)

@@ -55,6 +55,8 @@ def video_head(seed: int, F: int, Hg: int, Wg: int, d: int, outlier_scale: float
     rng = _rng(seed)
     P = Hg * Wg
     N = F * P if n_tokens is None else n_tokens
+    if N > F * P:
+        raise ValueError(f"n_tokens={N} exceeds the {F} x {Hg} x {Wg} frame grid")
     out = np.empty((N, d), dtype=np.float64)
     fields = None
     for f in range(F):

@@ -48,7 +48,10 @@ def lib():
         L.qvgo_subtract.argtypes = [p, i64, i32, p, p, p]
         L.qvgo_quantize.argtypes = [p, i64, i32, i32, i32, p, p]
         L.qvgo_compress.argtypes = [p, i32, i64, i64, i32, i32, i32, i32, i32, i32, p, p,
-                                    p, p, p, p, p, i32]
+                                    ct.c_uint64, p, p, p, p, p, i32]
+        L.qvgo_splitmix64.argtypes, L.qvgo_splitmix64.restype = [p], ct.c_uint64
+        L.qvgo_sample_rows.argtypes = [i64, i32, ct.c_uint64, i64, i32, p]
+        L.qvgo_sample_rows.restype = None
         L.qvgo_decompress.argtypes = [p, p, p, p, i32, i64, i64, i32, i32, i32, i32, i32,
                                       p, i32, i32]
         for f in ("qvgo_assign", "qvgo_update", "qvgo_kmeans", "qvgo_quantize", "qvgo_subtract",
@@ -147,14 +150,29 @@ def _as_store(X):
     return _c(X, np.float32), DT_F32
 
 
-def compress(X, C, T, iters, bits, G, init_idx=None, init_c=None, threads=None):
-    """X: [H, N, d] fp32, or bf16 bit patterns as uint16.  Returns dict with
-    codes, scales, assign [H,T,N] uint8, cent [H,T,C,d] (same storage as X),
-    cache [H,T,C,d] fp32."""
+def splitmix64(state: int, n: int):
+    """The first n outputs of splitmix64 started from `state`."""
+    st = ct.c_uint64(state)
+    return [int(lib().qvgo_splitmix64(ct.byref(st))) for _ in range(n)]
+
+
+def sample_rows(N: int, C: int, seed: int, h: int, t: int) -> np.ndarray:
+    """Cold-start rows of stage t (1-based) of head h: C distinct indices in
+    [0, N) from the seeded partial Fisher-Yates shuffle."""
+    rows = np.empty(C, np.int32)
+    lib().qvgo_sample_rows(N, C, ct.c_uint64(seed), h, t, _ptr(rows))
+    return rows
+
+
+def compress(X, C, T, iters, bits, G, init_idx=None, init_c=None, seed=None, threads=None):
+    """X: [H, N, d] fp32, or bf16 bit patterns as uint16.  Stage starts come
+    from init_idx rows, else init_c centroids, else rows drawn with
+    sample_rows(seed).  Returns dict with codes, scales, assign [H,T,N] uint8,
+    cent [H,T,C,d] (same storage as X), cache [H,T,C,d] fp32."""
     X, dt = _as_store(X)
     H, N, d = X.shape
-    if T > 0 and init_idx is None and init_c is None:
-        raise ValueError("cold start needs init_idx or init_c")
+    if T > 0 and init_idx is None and init_c is None and seed is None:
+        raise ValueError("cold start needs init_idx, init_c or a seed")
     idx = None if init_idx is None else _c(init_idx, np.int32)
     ic = None if init_c is None else _c(init_c, np.float32)
     out = dict(codes=np.empty((H, N, d * bits // 8), np.uint8),
@@ -163,7 +181,7 @@ def compress(X, C, T, iters, bits, G, init_idx=None, init_c=None, threads=None):
                cent=np.zeros((H, T, C, d), X.dtype),
                cache=np.zeros((H, T, C, d), np.float32))
     lib().qvgo_compress(_ptr(X), dt, H, N, d, C, T, iters, bits, G, _ptr(idx), _ptr(ic),
-                        _ptr(out["codes"]), _ptr(out["scales"]), _ptr(out["assign"]),
+                        ct.c_uint64(0 if seed is None else seed), _ptr(out["codes"]), _ptr(out["scales"]), _ptr(out["assign"]),
                         _ptr(out["cent"]), _ptr(out["cache"]), threads or default_threads())
     return out
 

@@ -176,6 +176,45 @@ void qvgo_kmeans(const float *R, int64_t N, int d, float *C, int nC, int iters, 
     }
 }
 
+/* ------------------------------------------------------ seeded sampler */
+/* Cold-start rows of stage t (1-based) of head h (0-based): C distinct token
+ * indices drawn without replacement.  The pages only say the initial
+ * centroids are seeded token rows; the draw is pinned as follows.
+ * splitmix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+ * generators", 2014; constants as published by Vigna): the state advances
+ * by 0x9E3779B97F4A7C15 and each output is the state passed through two
+ * xor-shift-multiply rounds and a final xor-shift.  All arithmetic is
+ * modulo 2^64. */
+uint64_t qvgo_splitmix64(uint64_t *state)
+{
+    uint64_t z = (*state += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+/* The generator of (seed, h, t) starts from seed ^ (0x9E3779B97F4A7C15 *
+ * (h+1)) ^ (0xD1B54A32D192ED03 * t).  A partial Fisher-Yates shuffle of
+ * perm = 0..N-1 then picks the rows: for j = 0..C-1 it swaps perm[j] with
+ * perm[j + (next() mod (N - j))], and row j is perm[j].  (The slight
+ * modulo bias is part of the definition.)  Requires 1 <= C <= N. */
+void qvgo_sample_rows(int64_t N, int C, uint64_t seed, int64_t h, int t, int32_t *rows)
+{
+    int32_t *perm = (int32_t *)malloc((size_t)N * sizeof(int32_t));
+    uint64_t st = seed ^ (0x9E3779B97F4A7C15ull * (uint64_t)(h + 1)) ^
+                  (0xD1B54A32D192ED03ull * (uint64_t)t);
+    for (int64_t i = 0; i < N; ++i) perm[i] = (int32_t)i;
+    for (int j = 0; j < C; ++j) {
+        uint64_t r = qvgo_splitmix64(&st) % (uint64_t)(N - j);
+        int64_t k = j + (int64_t)r;
+        int32_t tmp = perm[j];
+        perm[j] = perm[k];
+        perm[k] = tmp;
+        rows[j] = perm[j];
+    }
+    free(perm);
+}
+
 /* ---------------------------------------------------------- quantization */
 /* [Q] symmetric per-group quantization of one token row r[0..d) with b bits
  * and G channels per group, writing packed codes (d*b/8 bytes) and E4M3
@@ -255,8 +294,9 @@ static float round_store(float v, int dtype, void *base, int64_t idx)
  * Outputs: codes [N][d*b/8], scales [N][d/G], assign [T][N] (uint8),
  * cent [T][C][d] in the input dtype, cache [T][C][d] fp32 (may be NULL). */
 static void compress_head(const void *X, int dtype, int64_t N, int d, const qvgo_params *p,
-                          const int32_t *init_idx, const float *init_c, uint8_t *codes,
-                          uint8_t *scales, uint8_t *assign, void *cent, float *cache)
+                          const int32_t *init_idx, const float *init_c, int seeded,
+                          uint64_t seed, int64_t h, uint8_t *codes, uint8_t *scales,
+                          uint8_t *assign, void *cent, float *cache)
 {
     const int C = p->C;
     float *R = (float *)malloc((size_t)N * d * sizeof(float));
@@ -265,10 +305,14 @@ static void compress_head(const void *X, int dtype, int64_t N, int d, const qvgo
     int32_t *pi = (int32_t *)malloc((size_t)N * sizeof(int32_t));
     for (int64_t i = 0; i < N * d; ++i) R[i] = load_val(X, dtype, i);
 
+    int32_t *rows = (int32_t *)malloc((size_t)C * sizeof(int32_t));
     for (int t = 0; t < p->T; ++t) {
-        if (init_idx) {
+        if (init_idx || seeded) {
+            /* rows of R(t-1): the stage input, i.e. the previous stage's residual */
+            if (seeded) qvgo_sample_rows(N, C, seed, h, t + 1, rows);
+            else memcpy(rows, init_idx + (int64_t)t * C, (size_t)C * sizeof(int32_t));
             for (int j = 0; j < C; ++j)
-                memcpy(Cc + (int64_t)j * d, R + (int64_t)init_idx[t * C + j] * d, d * sizeof(float));
+                memcpy(Cc + (int64_t)j * d, R + (int64_t)rows[j] * d, d * sizeof(float));
         } else {
             memcpy(Cc, init_c + (int64_t)t * C * d, (size_t)C * d * sizeof(float));
         }
@@ -282,6 +326,7 @@ static void compress_head(const void *X, int dtype, int64_t N, int d, const qvgo
         }
     }
     qvgo_quantize(R, N, d, p->bits, p->G, codes, scales);
+    free(rows);
     free(R);
     free(Cc);
     free(Ch);
@@ -312,7 +357,7 @@ typedef struct {
     int mode; /* 0 compress, 1 decompress */
     int tid, nthreads;
     const void *X; int dtype; int64_t H, N; int d; qvgo_params p;
-    const int32_t *init_idx; const float *init_c;
+    const int32_t *init_idx; const float *init_c; int seeded; uint64_t seed;
     uint8_t *codes, *scales, *assign; void *cent; float *cache;
     void *out; int odtype;
 } job_t;
@@ -332,8 +377,9 @@ static void *worker(void *arg)
         if (j->mode == 0) {
             compress_head((const char *)j->X + h * N * d * esize(j->dtype), j->dtype, N, (int)d,
                           &j->p, j->init_idx ? j->init_idx + h * T * C : NULL,
-                          j->init_c ? j->init_c + h * T * C * d : NULL, codes, scales, assign,
-                          cent, j->cache ? j->cache + h * T * C * d : NULL);
+                          j->init_c ? j->init_c + h * T * C * d : NULL, j->seeded, j->seed, h,
+                          codes, scales, assign, cent,
+                          j->cache ? j->cache + h * T * C * d : NULL);
         } else {
             decompress_head(codes, scales, assign, cent, j->dtype, N, (int)d, &j->p,
                             (char *)j->out + h * N * d * esize(j->odtype), j->odtype);
@@ -359,19 +405,21 @@ static void run_jobs(job_t *proto, int nthreads)
 }
 
 /* Whole compress over H head-tensors X[H][N][d] (dtype 0 = fp32, 1 = bf16).
- * init_idx: [H][T][C] int32 or NULL; init_c: [H][T][C][d] fp32 or NULL.
+ * Stage starts: init_idx [H][T][C] int32 rows, else init_c [H][T][C][d] fp32,
+ * else (both NULL) rows drawn by qvgo_sample_rows(N, C, seed, h, t).
  * codes [H][N][d*b/8], scales [H][N][d/G], assign [H][T][N], cent [H][T][C][d]
  * (input dtype), cache [H][T][C][d] fp32 or NULL. */
 void qvgo_compress(const void *X, int dtype, int64_t H, int64_t N, int d, int C, int T,
                    int iters, int bits, int G, const int32_t *init_idx, const float *init_c,
-                   uint8_t *codes, uint8_t *scales, uint8_t *assign, void *cent, float *cache,
-                   int nthreads)
+                   uint64_t seed, uint8_t *codes, uint8_t *scales, uint8_t *assign, void *cent,
+                   float *cache, int nthreads)
 {
     job_t j;
     memset(&j, 0, sizeof j);
     j.mode = 0; j.X = X; j.dtype = dtype; j.H = H; j.N = N; j.d = d;
     j.p.C = C; j.p.T = T; j.p.iters = iters; j.p.bits = bits; j.p.G = G;
     j.init_idx = init_idx; j.init_c = init_c;
+    j.seeded = init_idx == NULL && init_c == NULL; j.seed = seed;
     j.codes = codes; j.scales = scales; j.assign = assign; j.cent = cent; j.cache = cache;
     run_jobs(&j, nthreads);
 }

@@ -221,3 +221,51 @@ def test_centroid_sums_that_can_round():
     idx = synth.init_indices(900, H, p.T, N, p.C)
     say("centroid sums that can round", tuple(x.shape))
     _check(*_run_both(x, p, idx))
+
+
+@pytest.mark.parametrize("H,N,C,T,seed", [(1, 40, 40, 1, 3), (2, 300, 16, 2, 11),
+                                          (3, 4681, 256, 2, 2 ** 63 + 5), (1, 32760, 256, 1, 1)])
+def test_seeded_start_matches_oracle(H, N, C, T, seed):
+    """Neither init_idx nor init_centroids: both sides draw the stage-start
+    rows from p.seed with their own splitmix64 + partial Fisher-Yates."""
+    x = synth.video_cache(3, 0, H, -(-N // (30 * 52)), 30, 52, 128, 1e2, torch.bfloat16,
+                          n_tokens=N)
+    p = qvg.params(C=C, T=T, iters=2, bits=2, group=64, seed=seed)
+    say("seeded start", H, N, C, T, seed)
+    rec = qvg.compress(x.to(DEV), p)
+    out = qvg.decompress(rec, p)
+    torch.cuda.synchronize()
+    ref = oracle.compress(to_oracle(x), C=C, T=T, iters=2, bits=2, G=64, seed=seed)
+    ref_out = oracle.decompress(ref["codes"], ref["scales"], ref["assign"], ref["cent"], 2, 64)
+    _check(rec, out, torch.from_numpy(ref["cache"]), ref, ref_out)
+
+
+def test_device_rows_equal_host_rows():
+    """init_idx in device memory is read by the kernels and gives the record
+    the host copy of the same rows gives (and the oracle's)."""
+    x = synth.video_cache(4, 1, 2, 2, 30, 52, 128, 1e3, torch.bfloat16, n_tokens=3001)
+    p = qvg.params(C=64, T=2, iters=3, bits=2, group=64)
+    idx = synth.init_indices(41, 2, p.T, x.shape[1], p.C)
+    say("device rows")
+    a = qvg.compress(x.to(DEV), p, init_idx=idx)
+    b = qvg.compress(x.to(DEV), p, init_idx=torch.from_numpy(idx).to(DEV))
+    torch.cuda.synchronize()
+    for f in ("codes", "scales", "assign", "centroids"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+    ref = oracle.compress(to_oracle(x), C=p.C, T=p.T, iters=p.iters, bits=2, G=64, init_idx=idx)
+    assert not rec_equal(b, ref)
+
+
+def test_cold_stream_chunk_draws_from_seed():
+    """A cold streamed chunk without init_idx starts from the seeded rows and
+    fills the centroid cache like the oracle."""
+    x = synth.video_cache(5, 0, 2, 3, 30, 52, 128, 1e2, torch.bfloat16)
+    p = qvg.params(C=32, T=2, iters=3, bits=2, group=64, seed=99)
+    cache = torch.zeros((2, p.T, p.C, 128), dtype=torch.float32, device=DEV)
+    say("cold stream chunk, seeded")
+    rec = qvg.compress_stream(x.to(DEV), p, 2, cache, False)
+    out = qvg.decompress(rec, p)
+    torch.cuda.synchronize()
+    ref = oracle.compress(to_oracle(x), C=p.C, T=p.T, iters=p.iters, bits=2, G=64, seed=99)
+    ref_out = oracle.decompress(ref["codes"], ref["scales"], ref["assign"], ref["cent"], 2, 64)
+    _check(rec, out, cache, ref, ref_out)
