@@ -158,6 +158,29 @@ qvg_status qvg_compress_stream(const void *chunk, qvg_dtype dtype, int64_t H, in
                                int warm, const int32_t *init_idx, const qvg_record *out, void *ws,
                                size_t ws_bytes, void *stream);
 
+/* Bytes of the device array qvg_compress_stream_static uses as scratch. */
+#define QVG_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* qvg_compress_stream without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments, results and errors are those
+ * of qvg_compress_stream.  Scratch is a file-scope device array of
+ * QVG_STATIC_SCRATCH_BYTES (64 MiB) per GPU, held until the process ends;
+ * its address is looked up once per device on the first call made with
+ * that device current.  Nothing is allocated: sizes whose workspace
+ * (qvg_workspace_size) exceeds the array return QVG_ERR_WORKSPACE before
+ * anything is enqueued; 24 head-tensors of 4680 tokens, d = 128, C = 256
+ * need 51 MiB.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (different streams, or host threads without ordering)
+ * race and must be serialised by the caller.  The array keeps the last
+ * call's contents; the call clears what must start at zero itself.  For
+ * a call free of host-to-device copies, give init_idx in device memory or
+ * leave it NULL (seeded draw). */
+qvg_status qvg_compress_stream_static(const void *chunk, qvg_dtype dtype, int64_t H, int64_t N,
+                                      int64_t d, const qvg_params *p, int32_t iters_warm,
+                                      float *cache, int warm, const int32_t *init_idx,
+                                      const qvg_record *out, void *stream);
+
 /* Fused decompression (paper.rainbus.top method paragraph, DQ;
  * note.zhuruihan.top "Algorithm-System Co-design", fused dequantization
  * kernel): per element x = level(q) * scale, then x += C(t)[pi(t)] for

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -266,6 +267,32 @@ qvg_status compress_impl(const void *x, qvg_dtype dtype, int64_t H, int64_t N, i
             : run_compress<float, float, 128>(x, H, N, p, iters, idx, init_c, cache_out, out, w, s);
 }
 
+// Device scratch of qvg_compress_stream_static: one array per GPU, held until
+// the process ends.  In host code `scratch` only names the symbol; its device
+// address on each GPU comes from hipGetSymbolAddress with that GPU current.
+static __device__ __align__(256) unsigned char scratch[QVG_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Address of the current device's scratch (looked up once per device).
+qvg_status static_scratch(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hip_fail("hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(QVG_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return hip_fail("hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QVG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -309,6 +336,27 @@ qvg_status qvg_compress_stream(const void *chunk, qvg_dtype dtype, int64_t H, in
                          ws_bytes, stream);
   return compress_impl(chunk, dtype, H, N, d, p, p->iters, init_idx, nullptr, cache, out, ws,
                        ws_bytes, stream);
+}
+
+qvg_status qvg_compress_stream_static(const void *chunk, qvg_dtype dtype, int64_t H, int64_t N,
+                                      int64_t d, const qvg_params *p, int32_t iters_warm,
+                                      float *cache, int warm, const int32_t *init_idx,
+                                      const qvg_record *out, void *stream) {
+  g_err[0] = 0;
+  if (!p) return fail(QVG_ERR_INVALID_ARG, "params is NULL");
+  if (p->T > 0 && !cache) return fail(QVG_ERR_INVALID_ARG, "cache must be non-NULL when T >= 1");
+  qvg_status st = check_params(H, N, d, dtype, p, warm ? iters_warm : p->iters);
+  if (st != QVG_OK) return st;
+  const size_t need = make_layout(H, N, d, p->C, p->T, p->T > 0).total;
+  if (need > (size_t)QVG_STATIC_SCRATCH_BYTES)
+    return fail(QVG_ERR_WORKSPACE,
+                "these sizes need %zu bytes of scratch, more than the %u of the static array",
+                need, (unsigned)QVG_STATIC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != QVG_OK) return st;
+  return qvg_compress_stream(chunk, dtype, H, N, d, p, iters_warm, cache, warm, init_idx, out, ws,
+                             (size_t)QVG_STATIC_SCRATCH_BYTES, stream);
 }
 
 qvg_status qvg_decompress(const qvg_record *rec, qvg_dtype rec_dtype, int64_t H, int64_t N,

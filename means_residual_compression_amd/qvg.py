@@ -21,7 +21,8 @@ QVG_F32, QVG_BF16 = 0, 1
 _STATUS = {0: "QVG_OK", 1: "QVG_ERR_INVALID_ARG", 2: "QVG_ERR_UNSUPPORTED",
            3: "QVG_ERR_WORKSPACE", 4: "QVG_ERR_HIP"}
 EXPORTS = ["qvg_status_string", "qvg_last_error", "qvg_workspace_size", "qvg_compress",
-           "qvg_compress_stream", "qvg_decompress", "qvg_decompress_chunks",
+           "qvg_compress_stream", "qvg_compress_stream_static", "qvg_decompress",
+           "qvg_decompress_chunks",
            "qvg_assign_workspace_size",
            "qvg_kmeans_assign", "qvg_update_workspace_size", "qvg_kmeans_update",
            "qvg_sas_subtract", "qvg_group_quant_pack", "qvg_timing_enable", "qvg_timing_reset",
@@ -82,6 +83,8 @@ def lib() -> ct.CDLL:
             "qvg_compress": ([p, ct.c_int, i64, i64, i64, P, p, p, p, R, p, sz, p], ct.c_int),
             "qvg_compress_stream": ([p, ct.c_int, i64, i64, i64, P, i32, p, ct.c_int, p, R, p,
                                      sz, p], ct.c_int),
+            "qvg_compress_stream_static": ([p, ct.c_int, i64, i64, i64, P, i32, p, ct.c_int, p,
+                                            R, p], ct.c_int),
             "qvg_decompress": ([R, ct.c_int, i64, i64, i64, P, p, ct.c_int, p], ct.c_int),
             "qvg_decompress_chunks": ([R, ct.POINTER(i64), i32, ct.c_int, i64, i64, P, p,
                                        ct.c_int, p], ct.c_int),
@@ -225,6 +228,26 @@ def compress_stream(chunk: torch.Tensor, p: Params, iters_warm: int, cache: torc
     _check(lib().qvg_compress_stream(
         chunk.data_ptr(), _dt(chunk), H, N, d, ct.byref(p), iters_warm, cache.data_ptr(),
         1 if warm else 0, idx_p, ct.byref(rec), ws.data_ptr(), ws.numel(), _stream()))
+    del keep
+    return out
+
+
+STATIC_SCRATCH_BYTES = 64 << 20  # QVG_STATIC_SCRATCH_BYTES in include/qvg.h
+
+
+def compress_stream_static(chunk: torch.Tensor, p: Params, iters_warm: int, cache: torch.Tensor,
+                           warm: bool, init_idx=None, out: Record | None = None) -> Record:
+    """qvg_compress_stream on the library's static device scratch: no
+    workspace argument (the record is still caller memory; pass `out` to
+    allocate nothing at all)."""
+    _dev(chunk, "chunk")
+    H, N, d = chunk.shape
+    out = out or empty_record(H, N, d, p, chunk.dtype, chunk.device)
+    keep, idx_p = _idx_ptr(init_idx)
+    rec = out._c()
+    _check(lib().qvg_compress_stream_static(
+        chunk.data_ptr(), _dt(chunk), H, N, d, ct.byref(p), iters_warm, cache.data_ptr(),
+        1 if warm else 0, idx_p, ct.byref(rec), _stream()))
     del keep
     return out
 
