@@ -21,7 +21,8 @@ tokens, T=4, INT2 and INT4, per-stage MSE curve and record sizes), pro (the
 self-forcing-shaped cache at the QVG-Pro operating point, T=4 and groups of
 16, chosen per tensor kind), attn (attention of --nq queries per head over the
 decode-side K and V records with the rotary tables, keys and values rebuilt
-on chip, against an unfused consumer: both records decompressed to bf16, then
+on chip, against an unfused consumer: the keys decompressed to bf16 and the
+values to fp32 (the unrounded reconstruction the fused kernel uses), then
 rotary keys and the attention in torch).
 --copy-calibration runs only a plain 256 MiB device copy,
 the reference that the HBM byte counters of the kernels are scaled by.
@@ -121,6 +122,79 @@ def dequant_bytes(H, N, d, C, T, bits, G, out_bytes=2, c_bytes=2):
     return H * N * per_tok + H * T * C * d * c_bytes
 
 
+def cpu_model():
+    """The host CPU's model name (for the baseline's record)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _event_ms(fn, reps):
+    """Average milliseconds of `reps` calls of fn between two events on the
+    current stream (for torch's own fill and copy kernels)."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    e0.record(s)
+    for _ in range(reps):
+        fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def decode_leg(reps=100):
+    """The decode-side read path at its full size: a video-shaped cache of 20 K
+    + 20 V head-tensors x 262144 tokens (39x40 grid, scene cut every 21 frames,
+    drawn on the device) compressed on the GPU at T=4, C=256, INT2 G=64, 8
+    iterations; then the fused dequant of that record, `reps` launches, against
+    HBM's peak, with the measured fill and copy rates of the same output buffer
+    beside it."""
+    dev = torch.device("cuda:0")
+    c = synth.CONFIGS["long_video"]
+    N, d, hk = 262144, 128, 20
+    log("drawing the decode-side cache on the device and compressing it ...")
+    x = torch.cat([synth.video_cache_device(4, k, hk, c["Hg"], c["Wg"], d, synth.OUTLIER_SCALE[k],
+                                            N, c["scene_len"], torch.bfloat16, dev)
+                   for k in c["kinds"]])
+    H = x.shape[0]
+    p = qvg.params(C=256, T=4, iters=8, bits=2, group=64, seed=4)
+    rec = qvg.compress(x, p)
+    out = torch.empty_like(x)
+    for _ in range(3):
+        qvg.decompress(rec, p, out=out)
+    torch.cuda.synchronize()
+    qvg.timing_reset()
+    qvg.timing_enable(True)
+    for _ in range(reps):
+        qvg.decompress(rec, p, out=out)
+    torch.cuda.synchronize()
+    qvg.timing_enable(False)
+    ms, n = qvg.timing_read("fused_dequant")
+    avg = ms / n
+    nbytes = dequant_bytes(H, N, d, p.C, p.T, p.bits, p.group)
+    gbps = nbytes / (avg * 1e-3) / 1e9
+    out_bytes = out.numel() * out.element_size()
+    fill_ms = _event_ms(lambda: out.fill_(1.0), 20)
+    copy_ms = _event_ms(lambda: out.copy_(x), 20)
+    res = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+           "frac": gbps / HBM_PEAK_GBPS, "traffic": stored_traffic("fused_dequant", "decode"),
+           "kernel": "fused_dequant", "per_launch": f"{nbytes} B", "avg_ms": avg,
+           "launches": n,
+           "workload": "record from GPU compress of a video-shaped cache, 20 K + 20 V "
+                       "head-tensors x 262144 tokens, d=128, T=4, C=256, INT2 G=64",
+           "measured_ceilings_GBps": {"fill (write only, same buffer)": out_bytes / (fill_ms * 1e-3) / 1e9,
+                                      "copy (read + write)": 2 * out_bytes / (copy_ms * 1e-3) / 1e9}}
+    del x, rec, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def timed(step, steps, warmup):
     """Wall time per step of `steps` steps after `warmup` untimed ones, with
     no per-kernel events inside the timed region (each event pair costs a
@@ -166,6 +240,7 @@ def cpu_baseline_selfforcing(x_cpu, p, idx, rec_gpu, heads):
         rec_gpu.centroids[sel].cpu().view(torch.int16).numpy().view(np.uint16), ref["cent"])
     tokens = len(sel) * xs.shape[1]
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{len(sel)} of {x_cpu.shape[0]} head-tensors, all {xs.shape[1]} tokens, "
                       f"all {p.T}x{p.iters} k-means iterations, compress + decompress "
                       f"({dt:.1f} s wall, {ncores} host cores visible)"}, parity, ref_out, sel
@@ -242,9 +317,10 @@ def run_selfforcing(args):
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "bf16",
         "arith": "bf16 in/out; fp16 MFMA distance keys, fp64 exact distances and means, "
                  "fp32 residuals and quantization",
+        "video_tokens_per_s": N / (ms * 1e-3),
         "data": "synthetic",
         "config": {"workload": "self-forcing-wan-1.3b-shaped KV cache: 12 K + 12 V head-tensors "
                                "x 32760 tokens (21 frames x 30x52), d=128, bf16",
@@ -262,6 +338,8 @@ def run_selfforcing(args):
         "kernels_launches_per_step": {k: v["launches"] // args.steps for k, v in kt.items()},
         "record_bytes_per_head_tensor": rec.nbytes() // H,
     }
+    if not args.no_decode_leg:
+        res["roofline_other"]["fused_dequant_decode"] = decode_leg()
     if not args.no_cpu_baseline:
         log("oracle baseline on the host cores ...")
         cb, parity, _, _ = cpu_baseline_selfforcing(x_cpu, p, idx, rec,
@@ -301,13 +379,13 @@ def run_decode(args):
                           threads=len(sel))
         dt = time.perf_counter() - t0
         cpu = {"value": dequant_bytes(len(sel), N, d, C, T, bits, G) / dt / 1e9, "unit": "GB/s",
-               "cores": len(sel), "kind": "oracle",
+               "cores": len(sel), "kind": "oracle", "cpu_model": cpu_model(),
                "sample": f"{len(sel)} of {H} head-tensors, all {N} tokens, decompress "
                          f"({dt:.2f} s wall, {ncores} host cores visible)"}
     return {"metric": "fused-dequant GB/s (decode-side record, d=128 C=256 T=4)",
             "value": gbps, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "decode-side record 40 heads x 262144 tokens, d=128, INT2 "
                                    "G=64, T=4, C=256, bf16 centroids and output"},
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
@@ -322,8 +400,8 @@ def run_attn(args):
     """Attention of Nq queries per head over the decode-side K and V records
     (40 x 262144 tokens each, d=128, T=4, C=256, INT2 G=64, bf16 centroids),
     pre-rotary keys rotated after reconstruction, with the keys and values
-    rebuilt on chip; against it, the unfused consumer (decompress both records
-    to bf16, rotate the keys and evaluate the attention with torch)."""
+    rebuilt on chip; against it, the unfused consumer (keys decompressed to bf16,
+    values to fp32, keys rotated and the attention evaluated with torch)."""
     dev = torch.device("cuda:0")
     H, N, d, T, C, bits, G, Nq = 40, 262144, 128, 4, 256, 2, 64, args.nq
     recs, host0 = [], []
@@ -351,22 +429,24 @@ def run_attn(args):
     per_tok = 2 * (d * bits // 8 + d // G + T)
     nbytes = H * N * per_tok + 2 * H * T * C * d * 2 + 2 * N * (d // 2) * 4 + 2 * H * Nq * d * 4
     gbps = nbytes / (at["avg_ms"] * 1e-3) / 1e9
-    # the unfused consumer: both records decompressed to bf16, the keys
-    # rotated and the attention evaluated with torch (bf16 products, fp32
-    # softmax), every intermediate in HBM
+    # the unfused consumer: the records decompressed (keys bf16, values fp32),
+    # the keys rotated and the attention evaluated with torch (bf16 score
+    # products, fp32 softmax and value products), every intermediate in HBM
     kd = torch.empty((H, N, d), dtype=torch.bfloat16, device=dev)
-    vd = torch.empty((H, N, d), dtype=torch.bfloat16, device=dev)
+    # values as the fused kernel takes them: the reconstruction unrounded
+    # (fp32), so both consumers compute the same attention
+    vd = torch.empty((H, N, d), dtype=torch.float32, device=dev)
     qT = q.transpose(1, 2).contiguous().to(torch.bfloat16)  # [H, d, Nq]
     cosf, sinf = cos[None], sin[None]
 
     def unfused():
         qvg.decompress(recs[0], p, out=kd)
-        qvg.decompress(recs[1], p, out=vd)
+        qvg.decompress(recs[1], p, out_dtype=torch.float32, out=vd)
         x1, x2 = kd[..., : d // 2].float(), kd[..., d // 2:].float()
         kr = torch.cat((x1 * cosf - x2 * sinf, x2 * cosf + x1 * sinf), -1).to(torch.bfloat16)
         s = torch.bmm(kr, qT).float() * scale                       # [H, N, Nq]
         w = torch.softmax(s, dim=1).transpose(1, 2).contiguous()    # [H, Nq, N]
-        return torch.bmm(w.to(torch.bfloat16), vd)
+        return torch.bmm(w, vd)                                     # fp32
 
     ms_unfused = timed(unfused, max(3, args.steps // 2), 1)
     dq = kernel_times(["fused_dequant"])["fused_dequant"]
@@ -383,14 +463,14 @@ def run_attn(args):
         vx = oracle.reconstruct_exact(vc, vs, va, vcent, bits, G)
         oracle.attention(q0, kb, vx, scale, rope)
         dt = time.perf_counter() - t0
-        cpu = {"value": (nbytes / H) / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        cpu = {"value": (nbytes / H) / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle", "cpu_model": cpu_model(),
                "sample": f"head-tensor 0 of {H}, all {N} tokens, {Nq} queries "
                          f"({dt:.2f} s wall, one thread; numpy fp64)"}
     return {"metric": "fused dequant-attention GB/s (decode-side K and V records, d=128 "
                       "C=256 T=4)",
             "value": gbps, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": f"attention of {Nq} queries per head over decode-side K "
                                    f"and V records, 40 heads x 262144 tokens, d=128, INT2 "
                                    f"G=64, T=4, C=256, bf16 centroids, rotary keys"},
@@ -443,7 +523,7 @@ def cpu_baseline_stream(chunks_cpu, p, idx0, iters_warm):
         cache = ref["cache"]
     dt = time.perf_counter() - t0
     nw = len(chunks_cpu) - 1
-    return {"value": nw * H * N / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": nw * H * N / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"warm chunks 1-{nw} of the stream, all {H} head-tensors x {N} tokens, "
                       f"{iters_warm} iterations per stage from the previous chunk's cache, after "
                       f"chunk 0 cold (untimed); {dt:.1f} s wall, {ncores} host cores visible"}
@@ -539,7 +619,7 @@ def run_stream(args):
             "value": warm["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
             "steps": len(chunks), "warmup": args.warmup,
             "ms_per_step": warm["total_ms"] / len(chunks), "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "stream of 20 chunks x 3 frames (4680 tokens), 12 K + 12 V "
                                    "head-tensors, d=128, bf16, C=256, T=2, INT2 G=64; warm: 3 "
                                    "iterations from the cache, cold: 10 from seeded rows"},
@@ -609,7 +689,7 @@ def run_pro(args):
         "metric": "compress+decompress tokens/s, QVG-Pro operating point (d=128 C=256 T=4 G=16)",
         "value": H * N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "self-forcing-wan-1.3b-shaped KV cache: 12 K + 12 V head-tensors "
                                "x 32760 tokens, d=128, bf16, QVG-Pro per kind: C=256, T=4, "
                                "INT2, G=16, 8 iterations",
@@ -640,7 +720,7 @@ def run_pro(args):
             parity &= np.array_equal(getattr(rec[k], f)[:1].cpu().numpy(), ref[f][i:i + 1])
         parity &= np.array_equal(rec[k].centroids[:1].cpu().view(torch.int16).numpy()
                                  .view(np.uint16), ref["cent"][i:i + 1])
-    res["cpu_baseline"] = {"value": 2 * N / dt, "unit": "tokens/s", "cores": 2, "kind": "oracle",
+    res["cpu_baseline"] = {"value": 2 * N / dt, "unit": "tokens/s", "cores": 2, "kind": "oracle", "cpu_model": cpu_model(),
                            "sample": f"head-tensor 0 of K and of V, all {N} tokens, all "
                                      f"{pk.T}x{pk.iters} k-means iterations, compress only "
                                      f"({dt:.1f} s wall, a thread per head-tensor)"}
@@ -710,18 +790,43 @@ def run_large(args):
         xb = xs.view(torch.int16).numpy().view(np.uint16)
         threads = min(ncores, len(sel))
         p = qvg.params(C=c["C"], T=c["T"], iters=c["iters"], bits=2, group=c["group"])
+        idx_s = synth.init_indices(33, len(sel), p.T, ns, p.C)
         t0 = time.perf_counter()
-        oracle.compress(xb, C=p.C, T=p.T, iters=p.iters, bits=p.bits, G=p.group,
-                        init_idx=synth.init_indices(33, len(sel), p.T, ns, p.C), threads=threads)
+        ref = oracle.compress(xb, C=p.C, T=p.T, iters=p.iters, bits=p.bits, G=p.group,
+                              init_idx=idx_s, threads=threads)
         dt = time.perf_counter() - t0
+        # the same sample through the GPU path at the configured 8 iterations:
+        # INT2 records bit for bit, and INT4 codes and scales against the
+        # oracle's quantizer applied to its own final residual
+        xs_dev = xs.to(dev)
+        rec2 = qvg.compress(xs_dev, p, init_idx=idx_s)
+        p4 = qvg.params(C=p.C, T=p.T, iters=p.iters, bits=4, group=p.group)
+        rec4 = qvg.compress(xs_dev, p4, init_idx=idx_s)
+        torch.cuda.synchronize()
+        parity = all(np.array_equal(getattr(rec2, f).cpu().numpy(), ref[f])
+                     for f in ("codes", "scales", "assign"))
+        parity = parity and np.array_equal(
+            rec2.centroids.cpu().view(torch.int16).numpy().view(np.uint16), ref["cent"])
+        parity4 = True
+        for i in range(len(sel)):
+            r = oracle.bf16_bits_to_f32(xb[i])
+            for t in range(p.T):
+                r = oracle.subtract(r, ref["assign"][i, t].astype(np.int32),
+                                    oracle.bf16_bits_to_f32(ref["cent"][i, t]))
+            c4, s4 = oracle.quantize(r, 4, p.group)
+            parity4 = parity4 and np.array_equal(rec4.codes[i].cpu().numpy(), c4) and \
+                np.array_equal(rec4.scales[i].cpu().numpy(), s4)
         cb = {"value": len(sel) * ns / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+              "cpu_model": cpu_model(),
               "sample": f"first {ns} tokens of {len(sel)} of {H} head-tensors, INT2, all "
                         f"{p.T}x{p.iters} k-means iterations, compress ({dt:.1f} s wall, "
-                        f"{ncores} host cores visible)"}
+                        f"{ncores} host cores visible)",
+              "parity_sample_bit_exact": {"int2_record": bool(parity),
+                                          "int4_codes_scales": bool(parity4)}}
     return {"metric": "compress tokens/s, d=128 C=256 T=4 (long-video cache)",
             "value": r2["compress_tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": r2["compress_ms"],
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic",
             "config": {"workload": f"long-video cache: {heads} K + {heads} V head-tensors x "
                                    "131072 tokens (4 scenes x 21 frames x 39x40), d=128, bf16, "
@@ -746,6 +851,8 @@ def main():
     ap.add_argument("--large-heads", type=int, default=None,
                     help="K (and V) head-tensors of the long-video cache (default 32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-leg", action="store_true",
+                    help="skip the decode-side dequant at 40 x 262144 tokens in the default run")
     ap.add_argument("--cpu-heads", type=int, default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()

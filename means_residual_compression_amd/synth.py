@@ -102,6 +102,33 @@ def video_cache(family: int, kind: int, heads: int, F: int, Hg: int, Wg: int, d:
     return torch.stack(hs)
 
 
+def video_cache_device(family: int, kind: int, heads: int, Hg: int, Wg: int, d: int,
+                       outlier_scale: float, n_tokens: int, scene_len: int, dtype: torch.dtype,
+                       device) -> torch.Tensor:
+    """The video-shaped recipe of video_head (base + 0.05*f*drift + N(0, 0.1^2)
+    noise, 4 outlier channels of base scaled, base and drift re-drawn every
+    scene_len frames) drawn on the device with torch's seeded generator, for
+    caches too large to draw on the host quickly.  Same distribution as
+    video_cache, different random streams.  Returns [heads, n_tokens, d]."""
+    P = Hg * Wg
+    F = -(-n_tokens // P)
+    out = torch.empty((heads, F * P, d), dtype=dtype, device=device)
+    for h in range(heads):
+        g = torch.Generator(device=device)
+        g.manual_seed(_seed(family, kind, h))
+        for f0 in range(0, F, scene_len):
+            base = torch.randn((P, d), generator=g, device=device)
+            drift = torch.randn((P, d), generator=g, device=device)
+            outl = torch.randperm(d, generator=g, device=device)[:4]
+            base[:, outl] *= outlier_scale
+            nf = min(scene_len, F - f0)
+            fl = torch.arange(nf, device=device, dtype=torch.float32).view(nf, 1, 1)
+            noise = torch.randn((nf, P, d), generator=g, device=device)
+            frames = base + 0.05 * fl * drift + 0.1 * noise
+            out[h, f0 * P:(f0 + nf) * P] = frames.reshape(nf * P, d).to(dtype)
+    return out[:, :n_tokens].contiguous()
+
+
 def _seed(family: int, kind: int, h: int) -> int:
     return (1000 + 100 * family + h) * 2 + kind
 

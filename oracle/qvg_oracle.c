@@ -167,13 +167,53 @@ void qvgo_subtract(const float *R, int64_t N, int d, const int32_t *pi, const fl
             out[i * d + k] = R[i * d + k] - C[(int64_t)pi[i] * d + k];
 }
 
-/* Lloyd's k-means from the given initial centroids: iters x (assign, update). */
-void qvgo_kmeans(const float *R, int64_t N, int d, float *C, int nC, int iters, int32_t *pi)
+/* The assignment of tokens [lo, hi) by one thread (each token's argmin is
+ * independent of the others, so splitting the tokens changes nothing). */
+typedef struct {
+    const float *R; int64_t lo, hi; int d; const float *C; int nC; int32_t *pi;
+} assign_part_t;
+
+static void *assign_part(void *arg)
+{
+    assign_part_t *a = (assign_part_t *)arg;
+    qvgo_assign(a->R + a->lo * a->d, a->hi - a->lo, a->d, a->C, a->nC, a->pi + a->lo);
+    return NULL;
+}
+
+static void assign_threads(const float *R, int64_t N, int d, const float *C, int nC, int32_t *pi,
+                           int nthreads)
+{
+    if (nthreads <= 1 || N < 2 * nthreads) {
+        qvgo_assign(R, N, d, C, nC, pi);
+        return;
+    }
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * nthreads);
+    assign_part_t *parts = (assign_part_t *)malloc(sizeof(assign_part_t) * nthreads);
+    for (int t = 0; t < nthreads; ++t) {
+        parts[t].R = R; parts[t].d = d; parts[t].C = C; parts[t].nC = nC; parts[t].pi = pi;
+        parts[t].lo = N * t / nthreads;
+        parts[t].hi = N * (t + 1) / nthreads;
+        pthread_create(&th[t], NULL, assign_part, &parts[t]);
+    }
+    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+    free(th);
+    free(parts);
+}
+
+/* Lloyd's k-means from the given initial centroids: iters x (assign, update);
+ * the assignment may use `threads` threads over token ranges. */
+static void kmeans_threads(const float *R, int64_t N, int d, float *C, int nC, int iters,
+                           int32_t *pi, int threads)
 {
     for (int it = 0; it < iters; ++it) {
-        qvgo_assign(R, N, d, C, nC, pi);
+        assign_threads(R, N, d, C, nC, pi, threads);
         qvgo_update(R, N, d, pi, nC, C, NULL);
     }
+}
+
+void qvgo_kmeans(const float *R, int64_t N, int d, float *C, int nC, int iters, int32_t *pi)
+{
+    kmeans_threads(R, N, d, C, nC, iters, pi, 1);
 }
 
 /* ------------------------------------------------------ seeded sampler */
@@ -269,6 +309,7 @@ void qvgo_quantize(const float *R, int64_t N, int d, int bits, int G, uint8_t *c
 /* ------------------------------------------------------- whole-path, per head */
 typedef struct {
     int C, T, iters, bits, G;
+    int assign_threads; /* threads of one head's assignment step */
 } qvgo_params;
 
 static float load_val(const void *base, int dtype, int64_t idx)
@@ -316,7 +357,7 @@ static void compress_head(const void *X, int dtype, int64_t N, int d, const qvgo
         } else {
             memcpy(Cc, init_c + (int64_t)t * C * d, (size_t)C * d * sizeof(float));
         }
-        qvgo_kmeans(R, N, d, Cc, C, p->iters, pi);
+        kmeans_threads(R, N, d, Cc, C, p->iters, pi, p->assign_threads);
         if (cache) memcpy(cache + (int64_t)t * C * d, Cc, (size_t)C * d * sizeof(float));
         for (int64_t q = 0; q < (int64_t)C * d; ++q)
             Ch[q] = round_store(Cc[q], dtype, cent, (int64_t)t * C * d + q);
@@ -420,6 +461,10 @@ void qvgo_compress(const void *X, int dtype, int64_t H, int64_t N, int d, int C,
     j.p.C = C; j.p.T = T; j.p.iters = iters; j.p.bits = bits; j.p.G = G;
     j.init_idx = init_idx; j.init_c = init_c;
     j.seeded = init_idx == NULL && init_c == NULL; j.seed = seed;
+    /* fewer heads than threads: the spare threads split each head's tokens */
+    if (nthreads < 1) nthreads = 1;
+    j.p.assign_threads = H < nthreads ? (int)(nthreads / H) : 1;
+    if (H < nthreads) nthreads = (int)H;
     j.codes = codes; j.scales = scales; j.assign = assign; j.cent = cent; j.cache = cache;
     run_jobs(&j, nthreads);
 }

@@ -4,13 +4,16 @@
   first 32 tokens of frame 84, scenes cut every 21 frames), d=128, bf16,
   C=256, T=4 stages, INT2 and INT4 with G=64.  Whole records (assignments,
   centroids, codes, scales, fp32 centroid cache) and reconstructions are
-  compared bit for bit with the oracle on one K and one V head-tensor.  The
-  oracle needs ~100 s per head at the workload's 8 iterations, so these runs
-  use 2 iterations per stage: every kernel and every stage transition still
-  runs at full size.
+  compared bit for bit with the oracle on one K and one V head-tensor, at the
+  workload's 8 iterations per stage (the oracle splits each head's
+  assignment over the host's threads).
 * The decode-side record: 40 head-tensors x 262144 tokens, T=4, C=256, INT2
   G=64, bf16 centroids; the fused dequant of every token is compared bit for
-  bit with the oracle's reconstruction.
+  bit with the oracle's reconstruction.  And the decode shape as the
+  benchmark measures it: a video-shaped cache of 20 K + 20 V head-tensors x
+  262144 tokens compressed on the GPU (T=4, 8 iterations) and decompressed,
+  with a K and a V head-tensor's record and reconstruction checked against
+  the oracle's compress of the same input.
 * The stream: 20 chunks of 4680 tokens of 24 head-tensors, the first cold and
   the rest warm-started from the centroid cache, sampled head-tensors' records
   and caches compared with the oracle's chain after every chunk.
@@ -44,7 +47,7 @@ def _large_heads(kinds):
 def test_large_cache_full_size(bits, kinds):
     x, c = _large_heads(kinds)
     H, N, d = x.shape
-    p = qvg.params(C=c["C"], T=c["T"], iters=2, bits=bits, group=c["group"])
+    p = qvg.params(C=c["C"], T=c["T"], iters=c["iters"], bits=bits, group=c["group"])
     idx = synth.init_indices(3, H, p.T, N, p.C)
     say("large cache", tuple(x.shape), "bits", bits)
     cache = torch.zeros((H, p.T, p.C, d), dtype=torch.float32, device=DEV)
@@ -52,7 +55,7 @@ def test_large_cache_full_size(bits, kinds):
     out = qvg.decompress(rec, p)
     torch.cuda.synchronize()
     ref = oracle.compress(to_oracle(x), C=p.C, T=p.T, iters=p.iters, bits=p.bits, G=p.group,
-                          init_idx=idx, threads=min(H, _threads()))
+                          init_idx=idx, threads=_threads())
     bad = rec_equal(rec, ref)
     assert not bad, f"record fields differ from the oracle: {bad}"
     assert np.array_equal(cache.cpu().numpy(), ref["cache"])
@@ -111,3 +114,30 @@ def test_stream_full_size():
         assert not bad, f"chunk {ci}: {bad} differ from the oracle"
         got_cache = cache[heads].cpu().numpy()
         assert np.array_equal(got_cache, ref_cache), f"chunk {ci}: centroid cache differs"
+
+
+def test_decode_shape_record_from_gpu_compress():
+    c = synth.CONFIGS["long_video"]
+    N, d, hk = 262144, 128, 20
+    x = torch.cat([synth.video_cache_device(4, k, hk, c["Hg"], c["Wg"], d, c["outlier"][k], N,
+                                            c["scene_len"], torch.bfloat16, DEV)
+                   for k in c["kinds"]])
+    p = qvg.params(C=256, T=4, iters=c["iters"], bits=2, group=64, seed=4)
+    say("decode shape from GPU compress", tuple(x.shape))
+    rec = qvg.compress(x, p)
+    out = qvg.decompress(rec, p)
+    torch.cuda.synchronize()
+    sel = [0, hk]  # one K and one V head-tensor
+    xs = x[sel].cpu()
+    got = bits16(out[sel])
+    sub = qvg.Record(rec.codes[sel], rec.scales[sel], rec.assign[sel], rec.centroids[sel])
+    del out, x
+    ref = oracle.compress(to_oracle(xs), C=p.C, T=p.T, iters=p.iters, bits=2, G=64, seed=None,
+                          init_idx=np.stack([np.stack([oracle.sample_rows(N, p.C, 4, h, t + 1)
+                                                       for t in range(p.T)]) for h in sel]),
+                          threads=_threads())
+    bad = rec_equal(sub, ref)
+    assert not bad, f"record fields differ from the oracle: {bad}"
+    ref_out = oracle.decompress(ref["codes"], ref["scales"], ref["assign"], ref["cent"], 2, 64,
+                                threads=_threads())
+    assert np.array_equal(got, ref_out), mismatch_report(got, ref_out)

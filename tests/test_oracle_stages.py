@@ -131,3 +131,15 @@ def test_seeded_compress_uses_the_drawn_rows(oracle):
     b = oracle.compress(X, C=C, T=T, iters=3, bits=2, G=16, init_idx=idx)
     for k in ("codes", "scales", "assign", "cent", "cache"):
         np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_threaded_assignment_changes_nothing(oracle):
+    """The oracle splits one head's assignment over threads when the call has
+    fewer heads than threads; every token's argmin is its own, so the record
+    is the same as with one thread."""
+    rng = np.random.default_rng(8)
+    X = rng.normal(0, 1, (1, 3001, 32)).astype(np.float32)
+    a = oracle.compress(X, C=24, T=2, iters=3, bits=2, G=32, seed=5, threads=1)
+    b = oracle.compress(X, C=24, T=2, iters=3, bits=2, G=32, seed=5, threads=7)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
