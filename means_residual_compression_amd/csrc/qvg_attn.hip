@@ -292,7 +292,7 @@ void k_attn_split(const float *__restrict__ q, int Nq, int N, int H, AttnRec kr,
     st[4 * t + 2] = 0.0f;
   }
   if (SUMS)
-    for (int x = t; x < Nq * TC; x += 256) ws[x] = 0.0f;
+    for (int x = t; x < Nq * TC; x += 256) ws[x] = 0ull;
   float o[NQ];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) o[j] = 0.0f;
@@ -564,6 +564,399 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float *__restrict__ 
   out[((int64_t)h * Nq + qq) * D + k] = o / l;
 }
 
+// ------------------------------------------------------------- two passes
+// With bf16 centroid tables, keys of 1 to 4 stages, weight sums and up to
+// kAttnSumQueries queries, the attention takes two passes over the records
+// instead of k_attn_split:
+//  * k_attn_scores (keys only): four lanes per token, each holding a quarter
+//    of the rotate-half channel pairs (positions k .. k + d/8 - 1 of both
+//    halves), rebuild the key in registers as k_attn_split does, rotate it and
+//    take its products with each query in a chain of d/4 fused multiply-adds;
+//    two butterfly adds give all four lanes the same score, which is scaled
+//    and written to the scratch, with the largest score of each run.  Nothing
+//    goes through LDS but the level tables (and the queries when Nq > 1), and
+//    every wave scores its own tokens.
+//  * k_attn_values: with M the head's largest score, every weight is
+//    p_n = e^(s_n - M), so no running maximum is kept and nothing is
+//    rescaled.  A lane owns 8 channels and a slot of each tile's tokens and
+//    accumulates sum_n (p_n s_hat_n) level_n in registers (one fused
+//    multiply-add chain per lane over the run); the wave that owns stage t
+//    (t = w mod 4, lane = token) adds each token's weight, rounded to a
+//    multiple of 2^-40, to W_t[pi_t(n)] in LDS as a 64-bit integer (integer
+//    LDS atomics are an order of magnitude faster than float ones here, and
+//    integer sums do not depend on the order of the adds).  The run's
+//    (M, l, o, W) record, W converted back to fp32 once, is merged by
+//    k_attn_contract and k_attn_combine; with one maximum for all runs their
+//    merge weights are 1.
+// Summation order: a score is 4 chains of d/4 fused multiply-adds, added in
+// pairs, times scale.  An output element of one run is 4 (d = 128) or 2
+// (d = 64) tokens per tile per lane in one chain over the run, the lanes of a
+// wave added pairwise (2 or 3 levels), then the 4 waves in order; l is a chain
+// over wave 0's lanes' tokens, added pairwise over the lanes.  A weight sum
+// of a run is exact in units of 2^-40 (each weight within 2^-41 of its
+// unit multiple), rounded once to fp32.
+
+// Workgroup -> (head, run), XCD-aware as in k_attn_split.
+__device__ __forceinline__ void attn_item(int H, int nsplit, int &h, int &sp) {
+  const int total = H * nsplit, wg = blockIdx.x, xcd = wg & 7, slot = wg >> 3;
+  const int base = total >> 3, rem = total & 7;
+  const int item = xcd * base + min(xcd, rem) + slot;
+  const int HG = (H + 7) >> 3;
+  const int grp = item / (HG * nsplit), r0 = item - grp * HG * nsplit;
+  const int gh = min(HG, H - grp * HG);
+  sp = r0 / gh;
+  h = grp * HG + (r0 - sp * gh);
+}
+
+// Code words of GPT consecutive groups of 8 channels starting at channel k of
+// a record row (16 bits per group for INT2, 32 for INT4).
+template <int BITS, int GPT>
+__device__ __forceinline__ void load_codes(const uint8_t *rowp, int k, uint32_t w[GPT]) {
+  const uint8_t *p = rowp + k * BITS / 8;
+  if constexpr (BITS == 2 && GPT == 2) {
+    const uint32_t x = *reinterpret_cast<const uint32_t *>(p);
+    w[0] = x & 0xFFFFu;
+    w[1] = x >> 16;
+  } else if constexpr (BITS == 2) {
+    w[0] = *reinterpret_cast<const uint16_t *>(p);
+  } else if constexpr (GPT == 2) {
+    const uint2 x = *reinterpret_cast<const uint2 *>(p);
+    w[0] = x.x;
+    w[1] = x.y;
+  } else {
+    w[0] = *reinterpret_cast<const uint32_t *>(p);
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ void init_level_lut(float4 *lut2, float2 *lut4) {
+  const int t = threadIdx.x;  // blockDim.x == 256
+  if constexpr (BITS == 2)
+    lut2[t] = make_float4((float)(2 * (t & 3) - 3), (float)(2 * ((t >> 2) & 3) - 3),
+                          (float)(2 * ((t >> 4) & 3) - 3), (float)(2 * ((t >> 6) & 3) - 3));
+  else
+    lut4[t] = make_float2((float)(2 * (t & 15) - 15), (float)(2 * ((t >> 4) & 15) - 15));
+}
+
+#ifndef QVG_ATTN_WPE
+#define QVG_ATTN_WPE 1
+#endif
+template <int D, int NQ, int KT, int BITS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QVG_ATTN_WPE))) void k_attn_scores(const float *__restrict__ q, int Nq, int N,
+                                                     int H, AttnRec kr, float scale,
+                                                     const float *__restrict__ rcos,
+                                                     const float *__restrict__ rsin, int nsplit,
+                                                     int tps, float *__restrict__ scores,
+                                                     float *__restrict__ rmax) {
+  constexpr int HD = D / 2, GPT = D / 64;  // groups of 8 pair positions per lane
+  constexpr int QR = NQ == 1 ? 2 * GPT * 8 : 1;
+  __shared__ float4 lut2[BITS == 2 ? 256 : 1];
+  __shared__ float2 lut4[BITS == 4 ? 256 : 1];
+  __shared__ float qs[NQ == 1 ? 1 : NQ * D];
+  __shared__ float red[4][NQ];
+  int h, sp;
+  attn_item(H, nsplit, h, sp);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int part = t & 3, tok = t >> 2;
+  const int k0 = part * (GPT * 8);  // this lane's first pair position
+  init_level_lut<BITS>(lut2, lut4);
+  float qr[QR];
+  if constexpr (NQ == 1) {
+#pragma unroll
+    for (int g = 0; g < GPT; ++g) {
+      load8(q + (int64_t)h * D, k0 + 8 * g, qr + 16 * g);
+      load8(q + (int64_t)h * D, HD + k0 + 8 * g, qr + 16 * g + 8);
+    }
+  } else {
+    for (int x = t; x < NQ * D; x += 256) qs[x] = x < Nq * D ? q[(int64_t)h * Nq * D + x] : 0.0f;
+  }
+  __syncthreads();
+  float mx[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) mx[j] = -__builtin_inff();
+  const int C = kr.C, kg = __builtin_ctz(kr.G);
+  const uint16_t *cent = static_cast<const uint16_t *>(kr.cent) + (int64_t)h * KT * C * D;
+  const uint8_t *asg = kr.assign + (int64_t)h * KT * N;
+  const int ntiles = (N + kAttnBN - 1) / kAttnBN;
+  const int tb = sp * tps, te = min(tb + tps, ntiles);
+  // First-level loads of a tile: code words, scale bytes and assignment bytes
+  // of this lane's token (tokens past the end repeat the last one).
+  struct Raw {
+    uint32_t wa[GPT], wb[GPT], ea[GPT], eb[GPT], j[KT];
+  };
+  auto fetch = [&](int tile, Raw &r) {
+    const int i0 = tile * kAttnBN, nt = min(kAttnBN, N - i0);
+    const int ti = i0 + min(tok, nt - 1);
+    const int64_t row = (int64_t)h * N + ti;
+    const uint8_t *crow = kr.codes + row * (D * BITS / 8);
+    load_codes<BITS, GPT>(crow, k0, r.wa);
+    load_codes<BITS, GPT>(crow, HD + k0, r.wb);
+    const uint8_t *sc = kr.scales + (row << (__builtin_ctz(D) - kg));
+#pragma unroll
+    for (int g = 0; g < GPT; ++g) {
+      r.ea[g] = sc[(k0 + 8 * g) >> kg];
+      r.eb[g] = sc[(HD + k0 + 8 * g) >> kg];
+    }
+#pragma unroll
+    for (int u = 0; u < KT; ++u) r.j[u] = asg[(int64_t)(KT - 1 - u) * N + ti];  // u = 0: last stage
+  };
+  Raw cur;
+  fetch(tb, cur);
+  for (int tile = tb; tile < te; ++tile) {
+    const int i0 = tile * kAttnBN;
+    const int nt = min(kAttnBN, N - i0);
+    const int ti = i0 + min(tok, nt - 1);
+    // this tile's table rows and rotary rows go out first, then the next
+    // tile's first-level loads, which stay in flight while this tile computes
+    Row8<uint16_t> ga[GPT][KT], gb[GPT][KT];
+    float c[GPT][8], sn[GPT][8];
+#pragma unroll
+    for (int g = 0; g < GPT; ++g) {
+      const int ka = k0 + 8 * g, kb = HD + k0 + 8 * g;
+#pragma unroll
+      for (int u = 0; u < KT; ++u) {
+        const uint32_t ju = min(cur.j[u], (uint32_t)C - 1);
+        const uint16_t *cr = cent + ((int64_t)(KT - 1 - u) * C + ju) * D;
+        ga[g][u].load(cr + ka);
+        gb[g][u].load(cr + kb);
+      }
+      if (rcos) {
+        load8(rcos + (int64_t)ti * HD, ka, c[g]);
+        load8(rsin + (int64_t)ti * HD, ka, sn[g]);
+      }
+    }
+    Raw nx;
+    fetch(min(tile + 1, te - 1), nx);
+    float s[NQ];
+#pragma unroll
+    for (int jq = 0; jq < NQ; ++jq) s[jq] = 0.0f;
+#pragma unroll
+    for (int g = 0; g < GPT; ++g) {
+      const int ka = k0 + 8 * g, kb = HD + k0 + 8 * g;
+      float a[8], b[8], ca[8], cb[8];
+      levels8(cur.wa[g], BITS, lut2, lut4, a);
+      levels8(cur.wb[g], BITS, lut2, lut4, b);
+      const float s0 = e4m3_decode_bits(cur.ea[g]), s1 = e4m3_decode_bits(cur.eb[g]);
+      ga[g][0].get(ca);
+      gb[g][0].get(cb);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a[e] = __builtin_fmaf(a[e], s0, ca[e]);
+        b[e] = __builtin_fmaf(b[e], s1, cb[e]);
+      }
+#pragma unroll
+      for (int u = 1; u < KT; ++u) {
+        ga[g][u].get(ca);
+        gb[g][u].get(cb);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          a[e] = a[e] + ca[e];
+          b[e] = b[e] + cb[e];
+        }
+      }
+      uint32_t pa[4], pb[4];
+      pack8(a, pa);
+      pack8(b, pb);
+      if (rcos) {
+        unpack8(pa, a);
+        unpack8(pb, b);
+        rotate8(a, b, c[g], sn[g], pa, pb);
+      }
+      unpack8(pa, a);
+      unpack8(pb, b);
+#pragma unroll
+      for (int jq = 0; jq < NQ; ++jq) {
+        float qa[8], qb[8];
+        if constexpr (NQ == 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qa[e] = qr[16 * g + e], qb[e] = qr[16 * g + 8 + e];
+        } else {
+          load8(qs + jq * D, ka, qa);
+          load8(qs + jq * D, kb, qb);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[jq] = __builtin_fmaf(qa[e], a[e], s[jq]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[jq] = __builtin_fmaf(qb[e], b[e], s[jq]);
+      }
+    }
+    const bool valid = tok < nt;
+#pragma unroll
+    for (int jq = 0; jq < NQ; ++jq) {
+      float v = s[jq];
+      v = v + __shfl_xor(v, 1);
+      v = v + __shfl_xor(v, 2);
+      v = v * scale;
+      if (part == 0 && valid && jq < Nq) scores[((int64_t)h * Nq + jq) * N + ti] = v;
+      mx[jq] = fmaxf(mx[jq], valid ? v : -__builtin_inff());
+    }
+    cur = nx;
+  }
+  // the run's largest score per query
+#pragma unroll
+  for (int jq = 0; jq < NQ; ++jq) {
+    float m = mx[jq];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) red[wave][jq] = m;
+  }
+  __syncthreads();
+  if (t < Nq)
+    rmax[((int64_t)h * Nq + t) * nsplit + sp] =
+        fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
+}
+
+template <int D, int NQ, int BITS>
+__global__ __launch_bounds__(256) void k_attn_values(const float *__restrict__ scores,
+                                                     const float *__restrict__ rmax, int Nq, int N,
+                                                     int H, AttnRec vr, int nsplit, int tps, int pf,
+                                                     float *__restrict__ part) {
+  constexpr int CG = D / 8, SL = 256 / CG, TPT = kAttnBN / SL;  // groups, slots, tokens
+  __shared__ float4 lut2[BITS == 2 ? 256 : 1];
+  __shared__ float4 lut4v[BITS == 4 ? 128 : 1];  // [256] float2, 16-byte aligned
+  __shared__ float4 lred4[(NQ + 3) / 4];
+  float2 *lut4 = reinterpret_cast<float2 *>(lut4v);
+  float *lred = reinterpret_cast<float *>(lred4);
+  // [Nq][T][C] weight sums in units of 2^-40, then [4][NQ][D] wave outputs
+  extern __shared__ unsigned long long ws[];
+  int h, sp;
+  attn_item(H, nsplit, h, sp);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int cg = t % CG, slot = t / CG;
+  const int T = vr.T, C = vr.C, TC = T * C, vg = __builtin_ctz(vr.G);
+  init_level_lut<BITS>(lut2, lut4);
+  for (int x = t; x < Nq * TC; x += 256) ws[x] = 0ull;
+  float M[NQ];
+#pragma unroll
+  for (int jq = 0; jq < NQ; ++jq) {
+    M[jq] = -__builtin_inff();
+    if (jq < Nq)
+      for (int b = 0; b < nsplit; ++b) M[jq] = fmaxf(M[jq], rmax[((int64_t)h * Nq + jq) * nsplit + b]);
+  }
+  __syncthreads();
+  float o[NQ][8], l[NQ];
+#pragma unroll
+  for (int jq = 0; jq < NQ; ++jq) {
+    l[jq] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[jq][e] = 0.0f;
+  }
+  const float *sh = scores + (int64_t)h * Nq * N;
+  const int ntiles = (N + kAttnBN - 1) / kAttnBN;
+  const int tb = sp * tps, te = min(tb + tps, ntiles);
+  const int dv = __builtin_ctz(D) - vg;
+  // A tile's loads: this lane's code words, scale bytes and scores of tokens
+  // slot, slot + SL, ... (residual term) and of token `lane` (weights), with
+  // the assignment byte of stage `wave`; tokens past the end repeat the last.
+  struct Raw {
+    uint32_t w[TPT], e[TPT], a;
+    float s[TPT][NQ], sw[NQ];
+  };
+  auto fetch = [&](int tile, Raw &r) {
+    const int i0 = tile * kAttnBN, nt = min(kAttnBN, N - i0);
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int ti = i0 + min(slot + SL * u, nt - 1);
+      const int64_t row = (int64_t)h * N + ti;
+      load_codes<BITS, 1>(vr.codes + row * (D * BITS / 8), cg * 8, &r.w[u]);
+      r.e[u] = vr.scales[(row << dv) + ((cg * 8) >> vg)];
+#pragma unroll
+      for (int jq = 0; jq < NQ; ++jq) r.s[u][jq] = jq < Nq ? sh[(int64_t)jq * N + ti] : 0.0f;
+    }
+    const int tl = i0 + min(lane, nt - 1);
+#pragma unroll
+    for (int jq = 0; jq < NQ; ++jq) r.sw[jq] = jq < Nq ? sh[(int64_t)jq * N + tl] : 0.0f;
+    r.a = wave < T ? vr.assign[((int64_t)h * T + wave) * N + tl] : 0u;
+  };
+  Raw cur;
+  fetch(tb, cur);
+  for (int tile = tb; tile < te; ++tile) {
+    const int i0 = tile * kAttnBN;
+    const int nt = min(kAttnBN, N - i0);
+    Raw nx;
+    fetch(min(tile + 1, te - 1), nx);
+    // residual term: this lane's 8 channels of tokens slot, slot + SL, ...
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const bool valid = slot + SL * u < nt;
+      float lv[8];
+      levels8(cur.w[u], BITS, lut2, lut4, lv);
+      const float shat = e4m3_decode_bits(cur.e[u]);
+#pragma unroll
+      for (int jq = 0; jq < NQ; ++jq) {
+        const float p = (valid && jq < Nq) ? __expf(cur.s[u][jq] - M[jq]) : 0.0f;
+        const float ps = p * shat;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[jq][e] = __builtin_fmaf(ps, lv[e], o[jq][e]);
+      }
+    }
+    // weight sums (wave w: stages w, w + 4, ...) and l (wave 0); lane = token
+    if (wave == 0 || wave < T) {
+      float p[NQ];
+#pragma unroll
+      for (int jq = 0; jq < NQ; ++jq)
+        p[jq] = (lane < nt && jq < Nq) ? __expf(cur.sw[jq] - M[jq]) : 0.0f;
+      if (wave == 0)
+#pragma unroll
+        for (int jq = 0; jq < NQ; ++jq) l[jq] += p[jq];
+      const int tl = i0 + min(lane, nt - 1);
+      // each weight rounded to a multiple of 2^-40 (integer adds, so
+      // exact and independent of their order)
+      unsigned long long pq[NQ];
+#pragma unroll
+      for (int jq = 0; jq < NQ; ++jq) pq[jq] = __float2ull_rn(p[jq] * 0x1p40f);
+      for (int ts = wave; ts < T; ts += 4) {
+        const uint32_t raw = ts == wave ? cur.a : vr.assign[((int64_t)h * T + ts) * N + tl];
+        const int c = min((int)raw, C - 1);
+        if (lane < nt)
+#pragma unroll
+          for (int jq = 0; jq < NQ; ++jq)
+            if (jq < Nq) atomicAdd(ws + (jq * T + ts) * C + c, pq[jq]);
+      }
+    }
+    cur = nx;
+  }
+  // combine the token slots: pairwise over a wave's lanes, then the waves in order
+  float *wout = reinterpret_cast<float *>(ws + Nq * TC);  // [4][NQ][D]
+#pragma unroll
+  for (int off = CG; off < 64; off <<= 1)
+#pragma unroll
+    for (int jq = 0; jq < NQ; ++jq)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[jq][e] = o[jq][e] + __shfl_xor(o[jq][e], off);
+  if (lane < CG)
+#pragma unroll
+    for (int jq = 0; jq < NQ; ++jq)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wout[(wave * NQ + jq) * D + cg * 8 + e] = o[jq][e];
+  if (wave == 0)
+#pragma unroll
+    for (int jq = 0; jq < NQ; ++jq) {
+      float v = l[jq];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off);
+      if (lane == 0) lred[jq] = v;
+    }
+  __syncthreads();
+  float *rec = part + ((int64_t)h * nsplit + sp) * Nq * pf;
+  for (int x = t; x < Nq * D; x += 256) {
+    const int jq = x / D, k = x - jq * D;
+    const float r = ((wout[(0 * NQ + jq) * D + k] + wout[(1 * NQ + jq) * D + k]) +
+                     wout[(2 * NQ + jq) * D + k]) + wout[(3 * NQ + jq) * D + k];
+    rec[jq * pf + 2 + k] = r;
+  }
+#pragma unroll
+  for (int jq = 0; jq < NQ; ++jq)
+    if (t == jq && jq < Nq) {
+      rec[jq * pf] = M[jq];
+      rec[jq * pf + 1] = lred[jq];
+    }
+  for (int x = t; x < Nq * TC; x += 256) {
+    const int jq = x / TC;
+    rec[jq * pf + 2 + D + (x - jq * TC)] = __ull2float_rn(ws[x]) * 0x1p-40f;
+  }
+}
+
 namespace {
 
 int nq_bucket(int Nq) { return Nq <= 1 ? 1 : Nq <= 4 ? 4 : 16; }
@@ -604,10 +997,69 @@ bool launch_attn_t(const float *q, int H, int Nq, int N, const AttnRec &kr, cons
   return hipGetLastError() == hipSuccess;
 }
 
+// The two-pass path (k_attn_scores, k_attn_values); the scratch holds the
+// run records, the contraction parts, the scores [H][Nq][N] and the run
+// maxima [H][Nq][nsplit], in that order.
+template <int D, int NQ, int KT>
+bool launch_scores_t(const float *q, int H, int Nq, int N, const AttnRec &kr, float scale,
+                     const float *rcos, const float *rsin, const AttnSplit &sp, float *scores,
+                     float *rmax, hipStream_t s) {
+  if (kr.bits == 2)
+    hipLaunchKernelGGL((k_attn_scores<D, NQ, KT, 2>), dim3(H * sp.nsplit), dim3(256), 0, s, q, Nq,
+                       N, H, kr, scale, rcos, rsin, sp.nsplit, sp.tiles_per_split, scores, rmax);
+  else
+    hipLaunchKernelGGL((k_attn_scores<D, NQ, KT, 4>), dim3(H * sp.nsplit), dim3(256), 0, s, q, Nq,
+                       N, H, kr, scale, rcos, rsin, sp.nsplit, sp.tiles_per_split, scores, rmax);
+  return hipGetLastError() == hipSuccess;
+}
+
+template <int D, int NQ>
+bool launch_attn_2p(const float *q, int H, int Nq, int N, const AttnRec &kr, const AttnRec &vr,
+                    float scale, const float *rcos, const float *rsin, float *part, float *out,
+                    hipStream_t s) {
+  const AttnSplit sp = attn_split(H, N);
+  const int pf = attn_part_floats(Nq, D, vr.T, vr.C);
+  const int TC = vr.T * vr.C;
+  float *cpart = part + (size_t)H * sp.nsplit * Nq * pf;
+  float *scores = cpart + (size_t)H * Nq * kContractParts * D;
+  float *rmax = scores + (size_t)H * Nq * N;
+  bool ok = false;
+  switch (kr.T) {
+    case 1: ok = launch_scores_t<D, NQ, 1>(q, H, Nq, N, kr, scale, rcos, rsin, sp, scores, rmax, s); break;
+    case 2: ok = launch_scores_t<D, NQ, 2>(q, H, Nq, N, kr, scale, rcos, rsin, sp, scores, rmax, s); break;
+    case 3: ok = launch_scores_t<D, NQ, 3>(q, H, Nq, N, kr, scale, rcos, rsin, sp, scores, rmax, s); break;
+    case 4: ok = launch_scores_t<D, NQ, 4>(q, H, Nq, N, kr, scale, rcos, rsin, sp, scores, rmax, s); break;
+  }
+  if (!ok) return false;
+  const size_t lds = (size_t)Nq * TC * sizeof(unsigned long long) + (size_t)4 * NQ * D * sizeof(float);
+  if (vr.bits == 2)
+    hipLaunchKernelGGL((k_attn_values<D, NQ, 2>), dim3(H * sp.nsplit), dim3(256), lds, s, scores,
+                       rmax, Nq, N, H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
+  else
+    hipLaunchKernelGGL((k_attn_values<D, NQ, 4>), dim3(H * sp.nsplit), dim3(256), lds, s, scores,
+                       rmax, Nq, N, H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
+  if (hipGetLastError() != hipSuccess) return false;
+  if (TC > 0) {
+    hipLaunchKernelGGL((k_attn_contract<uint16_t>), dim3(Nq, H, kContractParts), dim3(256), 0, s,
+                       part, sp.nsplit, Nq, D, pf, vr, cpart);
+    if (hipGetLastError() != hipSuccess) return false;
+    hipLaunchKernelGGL(k_attn_combine<true>, dim3(Nq, H), dim3(128), 0, s, part, sp.nsplit, Nq, D,
+                       pf, cpart, out);
+  } else {
+    hipLaunchKernelGGL(k_attn_combine<false>, dim3(Nq, H), dim3(128), 0, s, part, sp.nsplit, Nq, D,
+                       pf, cpart, out);
+  }
+  return hipGetLastError() == hipSuccess;
+}
+
 template <typename Tc, int D>
 bool launch_attn_d(const float *q, int H, int Nq, int N, const AttnRec &kr, const AttnRec &vr,
                    float scale, const float *rcos, const float *rsin, float *part, float *out,
                    hipStream_t s) {
+  if (attn_two_pass(Nq, kr.T, vr.T, vr.C, sizeof(Tc) == 2)) {
+    if (Nq == 1) return launch_attn_2p<D, 1>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
+    return launch_attn_2p<D, 4>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
+  }
   if (attn_uses_sums(Nq, vr.T, vr.C)) {
     if (Nq == 1)
       return launch_attn_t<Tc, D, 1, true>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
@@ -634,6 +1086,10 @@ bool attn_uses_sums(int Nq, int T, int C) {
   return Nq <= kAttnSumQueries && (int64_t)Nq * T * C <= kAttnSumEntries;
 }
 
+bool attn_two_pass(int Nq, int kT, int vT, int vC, bool c_bf16) {
+  return c_bf16 && kT >= 1 && kT <= 4 && attn_uses_sums(Nq, vT, vC);
+}
+
 int attn_part_floats(int Nq, int D, int T, int C) {
   return D + 2 + (attn_uses_sums(Nq, T, C) ? T * C : 0);
 }
@@ -642,7 +1098,9 @@ size_t attn_scratch_floats(int H, int64_t N, int Nq, int D, int T, int C) {
   const AttnSplit sp = attn_split(H, N);
   const size_t runs = (size_t)H * sp.nsplit * Nq * attn_part_floats(Nq, D, T, C);
   const size_t contract = attn_uses_sums(Nq, T, C) ? (size_t)H * Nq * kContractParts * D : 0;
-  return runs + contract;
+  // scores and run maxima of the two-pass path (which needs weight sums)
+  const size_t two = attn_uses_sums(Nq, T, C) ? (size_t)H * Nq * (N + sp.nsplit) : 0;
+  return runs + contract + two;
 }
 
 bool launch_attention(const float *q, int H, int Nq, int N, int D, const AttnRec &kr,

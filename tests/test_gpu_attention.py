@@ -69,7 +69,11 @@ def _bound(q, K, Vabs, scale, H, N, d, vT, vC, sums):
     ratio = np.exp(2 * delta) * (1 + eps) / (1 - eps) - 1
     vmax = Vabs.max(axis=0)
     rebuild = 0.0 if sums else _gamma(vT + 1)
-    return (2 * ratio[:, None] + 2.1 * _gamma(m) + rebuild + U) * vmax[None, :]
+    # weight sums kept in units of 2^-40 (each weight rounded to a unit): at
+    # most 2^-41 per token and stage on a weight of at most 1, against a
+    # denominator of at least 1 (the largest score's weight)
+    fixed = vT * N * 2.0 ** -41 if sums else 0.0
+    return (2 * ratio[:, None] + 2.1 * _gamma(m) + rebuild + fixed + U) * vmax[None, :]
 
 
 def _sums(Nq, vpar):
