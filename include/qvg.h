@@ -285,14 +285,14 @@ qvg_status qvg_group_quant_pack(const void *r, qvg_dtype dtype, int64_t H, int64
  *   - Otherwise the values are rebuilt in fp32 (the dequant's fused
  *     multiply-add and adds).
  *   With bf16 centroids, keys of 1 to 4 stages and weight sums, the call
- *   takes two passes instead (same runs): the scores first, each the sum of
- *   4 fused multiply-add chains of d/4 terms added in pairs, times scale;
- *   then, with M the head's largest score, weights e^(s - M) (never
- *   rescaled): per run a fused multiply-add chain of (weight * s_hat) *
- *   level over 4 (d = 128) or 2 (d = 64) tokens per tile, the 16 or 32
- *   chains added pairwise and by wave, and weight sums kept exactly in
- *   units of 2^-40 (each weight rounded to the nearest unit) and rounded to
- *   fp32 once per run; runs merged as above with weights 1.
+ *   takes two passes instead (same runs for the values): the scores first,
+ *   each d/8 (d/4 for d = 64) fused multiply-add chains of 16 terms added
+ *   pairwise, times scale; then, with m the run's largest score, weights
+ *   e^(s - m) (never rescaled): per run a fused multiply-add chain of
+ *   (weight * s_hat) * level over 4 (d = 128) or 2 (d = 64) tokens per
+ *   tile, the 16 or 32 chains added pairwise and by wave, and weight sums
+ *   kept exactly in units of 2^-40 (each weight rounded to the nearest
+ *   unit) and rounded to fp32 once per run; runs merged as above.
  *   ws: device scratch of qvg_attention_workspace_size(H, Nq, N, d, vp)
  *   bytes, 256-byte aligned; all device pointers 16-byte aligned.
  * Errors: QVG_ERR_INVALID_ARG for NULL pointers, one rope table without the

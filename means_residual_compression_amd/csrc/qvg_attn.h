@@ -31,14 +31,15 @@ AttnSplit attn_split(int H, int64_t N);
 // Whether the values go through per-centroid weight sums (see qvg_attn.hip).
 bool attn_uses_sums(int Nq, int T, int C);
 // Whether the call takes the two-pass path (k_attn_scores, k_attn_values):
-// bf16 centroids, keys of 1 to 4 stages and weight sums.
-bool attn_two_pass(int Nq, int kT, int vT, int vC, bool c_bf16);
+// bf16 centroids, keys of 1 to 4 stages, weight sums, N * 2d < 2^32 and at
+// most 256 heads.
+bool attn_two_pass(int H, int Nq, int kT, int vT, int vC, bool c_bf16, int64_t N, int D);
 // Floats of one (run, query) record in the scratch: m, l, o[D], then the
 // T*C weight sums when attn_uses_sums.
 int attn_part_floats(int Nq, int D, int T, int C);
 // fp32 scratch floats of one call: the run records, then (with weight sums)
-// the contraction parts [H][Nq][8][D], the scores [H][Nq][N] and the run
-// maxima [H][Nq][nsplit] of the two-pass path.
+// the contraction parts [H][Nq][8][D] and the scores [H][Nq][N] of the
+// two-pass path.
 size_t attn_scratch_floats(int H, int64_t N, int Nq, int D, int T, int C);
 // q [H][Nq][D] fp32, part [H][nsplit][Nq][attn_part_floats] fp32 scratch
 // (attn_scratch_floats in all),

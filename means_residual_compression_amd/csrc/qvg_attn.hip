@@ -227,6 +227,12 @@ __device__ __forceinline__ void unpack8(const uint32_t w[4], float v[8]) {
   }
 }
 
+// bf16 rounding (RNE) of x, as the fp32 value: v_cvt_pk_bf16_f32 of (0, x)
+// leaves bf16(x) in the high half and zero in the low half.
+__device__ __forceinline__ float round_bf16(float x) {
+  return __uint_as_float(pack_bf16_rne(0.0f, x));
+}
+
 __device__ __forceinline__ void pack8(const float v[8], uint32_t w[4]) {
 #pragma unroll
   for (int m = 0; m < 4; ++m) w[m] = pack_bf16_rne(v[2 * m], v[2 * m + 1]);
@@ -568,33 +574,34 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float *__restrict__ 
 // With bf16 centroid tables, keys of 1 to 4 stages, weight sums and up to
 // kAttnSumQueries queries, the attention takes two passes over the records
 // instead of k_attn_split:
-//  * k_attn_scores (keys only): four lanes per token, each holding a quarter
-//    of the rotate-half channel pairs (positions k .. k + d/8 - 1 of both
-//    halves), rebuild the key in registers as k_attn_split does, rotate it and
-//    take its products with each query in a chain of d/4 fused multiply-adds;
-//    two butterfly adds give all four lanes the same score, which is scaled
-//    and written to the scratch, with the largest score of each run.  Nothing
-//    goes through LDS but the level tables (and the queries when Nq > 1), and
-//    every wave scores its own tokens.
-//  * k_attn_values: with M the head's largest score, every weight is
-//    p_n = e^(s_n - M), so no running maximum is kept and nothing is
-//    rescaled.  A lane owns 8 channels and a slot of each tile's tokens and
-//    accumulates sum_n (p_n s_hat_n) level_n in registers (one fused
-//    multiply-add chain per lane over the run); the wave that owns stage t
-//    (t = w mod 4, lane = token) adds each token's weight, rounded to a
-//    multiple of 2^-40, to W_t[pi_t(n)] in LDS as a 64-bit integer (integer
-//    LDS atomics are an order of magnitude faster than float ones here, and
-//    integer sums do not depend on the order of the adds).  The run's
-//    (M, l, o, W) record, W converted back to fp32 once, is merged by
-//    k_attn_contract and k_attn_combine; with one maximum for all runs their
-//    merge weights are 1.
-// Summation order: a score is 4 chains of d/4 fused multiply-adds, added in
-// pairs, times scale.  An output element of one run is 4 (d = 128) or 2
-// (d = 64) tokens per tile per lane in one chain over the run, the lanes of a
-// wave added pairwise (2 or 3 levels), then the 4 waves in order; l is a chain
-// over wave 0's lanes' tokens, added pairwise over the lanes.  A weight sum
-// of a run is exact in units of 2^-40 (each weight within 2^-41 of its
-// unit multiple), rounded once to fp32.
+//  * k_attn_scores (keys only): a workgroup takes a run of tokens for the
+//    group of heads one XCD owns (their tables stay in its L2).  Eight lanes
+//    per token (d = 128; four for d = 64), each holding 8 rotate-half channel
+//    pairs (channels k .. k+7 and d/2 + k ..), rebuild the key in registers
+//    as k_attn_split does, rotate it and take its products with each query
+//    in a chain of 16 fused multiply-adds; butterfly adds give all lanes of
+//    the token the same score, which is scaled and written to the scratch.
+//    A lane loads its token's rotary rows once and keeps them while it
+//    scores the token for every head of the group.  Only the level tables
+//    and the queries go through LDS, and every wave scores its own tokens.
+//  * k_attn_values: with m the run's largest score (read back from the
+//    scores), every weight is p_n = e^(s_n - m), so no running maximum is
+//    kept and nothing is rescaled.  A lane owns 8 channels and a slot of
+//    each tile's tokens and accumulates sum_n (p_n s_hat_n) level_n in
+//    registers (one fused multiply-add chain per lane over the run); the wave
+//    that owns stage t (t = w mod 4, lane = token) adds each token's weight,
+//    rounded to a multiple of 2^-40, to W_t[pi_t(n)] in LDS as a 64-bit
+//    integer (integer LDS atomics are an order of magnitude faster than float
+//    ones here, and integer sums do not depend on the order of the adds).
+//    The run's (m, l, o, W) record, W converted back to fp32 once, is merged
+//    by k_attn_contract and k_attn_combine.
+// Summation order: a score is d/8 (or d/4) chains of 16 fused multiply-adds,
+// added pairwise, times scale.  An output element of one run is 4 (d = 128)
+// or 2 (d = 64) tokens per tile per lane in one chain over the run, the lanes
+// of a wave added pairwise (2 or 3 levels), then the 4 waves in order; l is a
+// chain over wave 0's lanes' tokens, added pairwise over the lanes.  A
+// weight sum of a run is exact in units of 2^-40 (each weight within 2^-41 of
+// its unit multiple), rounded once to fp32.
 
 // Workgroup -> (head, run), XCD-aware as in k_attn_split.
 __device__ __forceinline__ void attn_item(int H, int nsplit, int &h, int &sp) {
@@ -638,183 +645,152 @@ __device__ __forceinline__ void init_level_lut(float4 *lut2, float2 *lut4) {
     lut4[t] = make_float2((float)(2 * (t & 15) - 15), (float)(2 * ((t >> 4) & 15) - 15));
 }
 
-#ifndef QVG_ATTN_WPE
-#define QVG_ATTN_WPE 1
-#endif
+// Scores: workgroup -> (group of the heads an XCD owns, run of tiles).  A
+// lane keeps its token's rotary rows in registers while it scores the token
+// for every head of the group.
 template <int D, int NQ, int KT, int BITS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QVG_ATTN_WPE))) void k_attn_scores(const float *__restrict__ q, int Nq, int N,
+__global__ __launch_bounds__(256) void k_attn_scores(const float *__restrict__ q, int Nq, int N,
                                                      int H, AttnRec kr, float scale,
                                                      const float *__restrict__ rcos,
                                                      const float *__restrict__ rsin, int nsplit,
-                                                     int tps, float *__restrict__ scores,
-                                                     float *__restrict__ rmax) {
-  constexpr int HD = D / 2, GPT = D / 64;  // groups of 8 pair positions per lane
-  constexpr int QR = NQ == 1 ? 2 * GPT * 8 : 1;
+                                                     int tps, float *__restrict__ scores) {
+  constexpr int HD = D / 2, LPT = D / 16;  // lanes per token: 8 pair positions each
+  constexpr int TB = 256 / LPT;            // tokens per workgroup pass
   __shared__ float4 lut2[BITS == 2 ? 256 : 1];
   __shared__ float2 lut4[BITS == 4 ? 256 : 1];
-  __shared__ float qs[NQ == 1 ? 1 : NQ * D];
-  __shared__ float red[4][NQ];
-  int h, sp;
-  attn_item(H, nsplit, h, sp);
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int part = t & 3, tok = t >> 2;
-  const int k0 = part * (GPT * 8);  // this lane's first pair position
+  extern __shared__ float qs[];  // [gh][NQ][D] queries of the group's heads
+  const int HG = (H + 7) >> 3, ngroups = (H + HG - 1) / HG;
+  const int total = ngroups * nsplit, wg = blockIdx.x, xcd = wg & 7, slot = wg >> 3;
+  const int item = xcd * (total >> 3) + min(xcd, total & 7) + slot;
+  const int grp = item / nsplit, sp = item - grp * nsplit;
+  const int h0 = grp * HG, gh = min(HG, H - h0);
+  const int t = threadIdx.x;
+  const int part = t % LPT, tok = t / LPT;
+  const int ka = part * 8, kb = HD + part * 8;  // this lane's channels ka.., kb..
   init_level_lut<BITS>(lut2, lut4);
-  float qr[QR];
-  if constexpr (NQ == 1) {
-#pragma unroll
-    for (int g = 0; g < GPT; ++g) {
-      load8(q + (int64_t)h * D, k0 + 8 * g, qr + 16 * g);
-      load8(q + (int64_t)h * D, HD + k0 + 8 * g, qr + 16 * g + 8);
-    }
-  } else {
-    for (int x = t; x < NQ * D; x += 256) qs[x] = x < Nq * D ? q[(int64_t)h * Nq * D + x] : 0.0f;
+  for (int x = t; x < gh * NQ * D; x += 256) {
+    const int hq = x / D, k = x - hq * D, hh = hq / NQ, jq = hq - hh * NQ;
+    qs[x] = jq < Nq ? q[((int64_t)(h0 + hh) * Nq + jq) * D + k] : 0.0f;
   }
   __syncthreads();
-  float mx[NQ];
-#pragma unroll
-  for (int j = 0; j < NQ; ++j) mx[j] = -__builtin_inff();
   const int C = kr.C, kg = __builtin_ctz(kr.G);
-  const uint16_t *cent = static_cast<const uint16_t *>(kr.cent) + (int64_t)h * KT * C * D;
-  const uint8_t *asg = kr.assign + (int64_t)h * KT * N;
   const int ntiles = (N + kAttnBN - 1) / kAttnBN;
-  const int tb = sp * tps, te = min(tb + tps, ntiles);
-  // First-level loads of a tile: code words, scale bytes and assignment bytes
-  // of this lane's token (tokens past the end repeat the last one).
+  const int t0 = sp * tps * kAttnBN, t1 = min(min(sp * tps + tps, ntiles) * kAttnBN, N);
+  const char *rc = reinterpret_cast<const char *>(rcos), *rs = reinterpret_cast<const char *>(rsin);
+  // First-level loads of one (pass, head) step: code words, scale bytes and
+  // assignment bytes of this lane's token (tokens past the run repeat its
+  // last one).  Head bases are uniform, lane offsets 32-bit (the launcher
+  // keeps every offset below 2^32 bytes).
   struct Raw {
-    uint32_t wa[GPT], wb[GPT], ea[GPT], eb[GPT], j[KT];
+    uint32_t wa, wb, ea, eb, j[KT];
   };
-  auto fetch = [&](int tile, Raw &r) {
-    const int i0 = tile * kAttnBN, nt = min(kAttnBN, N - i0);
-    const int ti = i0 + min(tok, nt - 1);
-    const int64_t row = (int64_t)h * N + ti;
-    const uint8_t *crow = kr.codes + row * (D * BITS / 8);
-    load_codes<BITS, GPT>(crow, k0, r.wa);
-    load_codes<BITS, GPT>(crow, HD + k0, r.wb);
-    const uint8_t *sc = kr.scales + (row << (__builtin_ctz(D) - kg));
+  auto fetch = [&](int b0, int h, Raw &r) {
+    const uint32_t ti = (uint32_t)min(b0 + tok, t1 - 1);
+    const uint8_t *crow = kr.codes + (int64_t)h * N * (D * BITS / 8) + ti * (uint32_t)(D * BITS / 8);
+    load_codes<BITS, 1>(crow, ka, &r.wa);
+    load_codes<BITS, 1>(crow, kb, &r.wb);
+    const uint8_t *scl = kr.scales + ((int64_t)h * N << (__builtin_ctz(D) - kg));
+    const uint32_t so = ti << (__builtin_ctz(D) - kg);
+    r.ea = scl[so + (ka >> kg)];
+    r.eb = scl[so + (kb >> kg)];
+    const uint8_t *asg = kr.assign + (int64_t)h * KT * N;
 #pragma unroll
-    for (int g = 0; g < GPT; ++g) {
-      r.ea[g] = sc[(k0 + 8 * g) >> kg];
-      r.eb[g] = sc[(HD + k0 + 8 * g) >> kg];
-    }
-#pragma unroll
-    for (int u = 0; u < KT; ++u) r.j[u] = asg[(int64_t)(KT - 1 - u) * N + ti];  // u = 0: last stage
+    for (int u = 0; u < KT; ++u) r.j[u] = asg[(uint32_t)(KT - 1 - u) * (uint32_t)N + ti];  // u = 0: last stage
   };
   Raw cur;
-  fetch(tb, cur);
-  for (int tile = tb; tile < te; ++tile) {
-    const int i0 = tile * kAttnBN;
-    const int nt = min(kAttnBN, N - i0);
-    const int ti = i0 + min(tok, nt - 1);
-    // this tile's table rows and rotary rows go out first, then the next
-    // tile's first-level loads, which stay in flight while this tile computes
-    Row8<uint16_t> ga[GPT][KT], gb[GPT][KT];
-    float c[GPT][8], sn[GPT][8];
+  fetch(t0, h0, cur);
+  float c[8], sn[8];
+  int b0 = t0, hh = 0;       // this step
+  int nb0 = t0, nhh = 0;     // the next step
+  while (b0 < t1) {
+    if (++nhh == gh) nhh = 0, nb0 += TB;
+    const int h = h0 + hh;
+    const uint32_t ti = (uint32_t)min(b0 + tok, t1 - 1);
+    // this step's table rows (and, for the group's first head, the token's
+    // rotary rows) go out first, then the next step's first-level loads,
+    // which stay in flight while this step computes
+    Row8<uint16_t> ga[KT], gb[KT];
+    const char *cent = reinterpret_cast<const char *>(static_cast<const uint16_t *>(kr.cent) +
+                                                      (int64_t)h * KT * C * D);
 #pragma unroll
-    for (int g = 0; g < GPT; ++g) {
-      const int ka = k0 + 8 * g, kb = HD + k0 + 8 * g;
-#pragma unroll
-      for (int u = 0; u < KT; ++u) {
-        const uint32_t ju = min(cur.j[u], (uint32_t)C - 1);
-        const uint16_t *cr = cent + ((int64_t)(KT - 1 - u) * C + ju) * D;
-        ga[g][u].load(cr + ka);
-        gb[g][u].load(cr + kb);
-      }
-      if (rcos) {
-        load8(rcos + (int64_t)ti * HD, ka, c[g]);
-        load8(rsin + (int64_t)ti * HD, ka, sn[g]);
-      }
+    for (int u = 0; u < KT; ++u) {
+      const uint32_t ju = min(cur.j[u], (uint32_t)C - 1);
+      const uint32_t off = (((uint32_t)(KT - 1 - u) * (uint32_t)C + ju) * D + ka) * 2u;
+      ga[u].load(reinterpret_cast<const uint16_t *>(cent + off));
+      gb[u].load(reinterpret_cast<const uint16_t *>(cent + off + HD * 2));
+    }
+    if (rcos && hh == 0) {
+      const uint32_t ro = (ti * HD + ka) * 4u;
+      load8(reinterpret_cast<const float *>(rc + ro), 0, c);
+      load8(reinterpret_cast<const float *>(rs + ro), 0, sn);
     }
     Raw nx;
-    fetch(min(tile + 1, te - 1), nx);
-    float s[NQ];
+    fetch(min(nb0, t1 - 1), h0 + nhh, nx);
+    float a[8], b[8], ca[8], cb[8];
+    levels8(cur.wa, BITS, lut2, lut4, a);
+    levels8(cur.wb, BITS, lut2, lut4, b);
+    const float s0 = e4m3_decode_bits(cur.ea), s1 = e4m3_decode_bits(cur.eb);
+    ga[0].get(ca);
+    gb[0].get(cb);
 #pragma unroll
-    for (int jq = 0; jq < NQ; ++jq) s[jq] = 0.0f;
+    for (int e = 0; e < 8; ++e) {
+      a[e] = __builtin_fmaf(a[e], s0, ca[e]);
+      b[e] = __builtin_fmaf(b[e], s1, cb[e]);
+    }
 #pragma unroll
-    for (int g = 0; g < GPT; ++g) {
-      const int ka = k0 + 8 * g, kb = HD + k0 + 8 * g;
-      float a[8], b[8], ca[8], cb[8];
-      levels8(cur.wa[g], BITS, lut2, lut4, a);
-      levels8(cur.wb[g], BITS, lut2, lut4, b);
-      const float s0 = e4m3_decode_bits(cur.ea[g]), s1 = e4m3_decode_bits(cur.eb[g]);
-      ga[g][0].get(ca);
-      gb[g][0].get(cb);
+    for (int u = 1; u < KT; ++u) {
+      ga[u].get(ca);
+      gb[u].get(cb);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        a[e] = __builtin_fmaf(a[e], s0, ca[e]);
-        b[e] = __builtin_fmaf(b[e], s1, cb[e]);
-      }
-#pragma unroll
-      for (int u = 1; u < KT; ++u) {
-        ga[g][u].get(ca);
-        gb[g][u].get(cb);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          a[e] = a[e] + ca[e];
-          b[e] = b[e] + cb[e];
-        }
-      }
-      uint32_t pa[4], pb[4];
-      pack8(a, pa);
-      pack8(b, pb);
-      if (rcos) {
-        unpack8(pa, a);
-        unpack8(pb, b);
-        rotate8(a, b, c[g], sn[g], pa, pb);
-      }
-      unpack8(pa, a);
-      unpack8(pb, b);
-#pragma unroll
-      for (int jq = 0; jq < NQ; ++jq) {
-        float qa[8], qb[8];
-        if constexpr (NQ == 1) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qa[e] = qr[16 * g + e], qb[e] = qr[16 * g + 8 + e];
-        } else {
-          load8(qs + jq * D, ka, qa);
-          load8(qs + jq * D, kb, qb);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s[jq] = __builtin_fmaf(qa[e], a[e], s[jq]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s[jq] = __builtin_fmaf(qb[e], b[e], s[jq]);
+        a[e] = a[e] + ca[e];
+        b[e] = b[e] + cb[e];
       }
     }
-    const bool valid = tok < nt;
+    // the bf16 key, rotated (fp32 products and difference/sum, then bf16)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = round_bf16(a[e]), b[e] = round_bf16(b[e]);
+    if (rcos) {
+#pragma clang fp contract(off)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xc = a[e] * c[e], ys = b[e] * sn[e], yc = b[e] * c[e], xs = a[e] * sn[e];
+        a[e] = round_bf16(xc - ys);
+        b[e] = round_bf16(yc + xs);
+      }
+    }
+    const bool valid = b0 + tok < t1;
+    const float *qh = qs + hh * NQ * D;
 #pragma unroll
     for (int jq = 0; jq < NQ; ++jq) {
-      float v = s[jq];
-      v = v + __shfl_xor(v, 1);
-      v = v + __shfl_xor(v, 2);
+      float qa[8], qb[8];
+      load8(qh + jq * D, ka, qa);
+      load8(qh + jq * D, kb, qb);
+      float v = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v = __builtin_fmaf(qa[e], a[e], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v = __builtin_fmaf(qb[e], b[e], v);
+#pragma unroll
+      for (int off = 1; off < LPT; off <<= 1) v = v + __shfl_xor(v, off);
       v = v * scale;
       if (part == 0 && valid && jq < Nq) scores[((int64_t)h * Nq + jq) * N + ti] = v;
-      mx[jq] = fmaxf(mx[jq], valid ? v : -__builtin_inff());
     }
     cur = nx;
+    b0 = nb0;
+    hh = nhh;
   }
-  // the run's largest score per query
-#pragma unroll
-  for (int jq = 0; jq < NQ; ++jq) {
-    float m = mx[jq];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if (lane == 0) red[wave][jq] = m;
-  }
-  __syncthreads();
-  if (t < Nq)
-    rmax[((int64_t)h * Nq + t) * nsplit + sp] =
-        fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
 }
 
 template <int D, int NQ, int BITS>
-__global__ __launch_bounds__(256) void k_attn_values(const float *__restrict__ scores,
-                                                     const float *__restrict__ rmax, int Nq, int N,
-                                                     int H, AttnRec vr, int nsplit, int tps, int pf,
-                                                     float *__restrict__ part) {
+__global__ __launch_bounds__(256) void k_attn_values(const float *__restrict__ scores, int Nq,
+                                                     int N, int H, AttnRec vr, int nsplit, int tps,
+                                                     int pf, float *__restrict__ part) {
   constexpr int CG = D / 8, SL = 256 / CG, TPT = kAttnBN / SL;  // groups, slots, tokens
   __shared__ float4 lut2[BITS == 2 ? 256 : 1];
   __shared__ float4 lut4v[BITS == 4 ? 128 : 1];  // [256] float2, 16-byte aligned
   __shared__ float4 lred4[(NQ + 3) / 4];
+  __shared__ float mred[4][NQ];
   float2 *lut4 = reinterpret_cast<float2 *>(lut4v);
   float *lred = reinterpret_cast<float *>(lred4);
   // [Nq][T][C] weight sums in units of 2^-40, then [4][NQ][D] wave outputs
@@ -826,14 +802,9 @@ __global__ __launch_bounds__(256) void k_attn_values(const float *__restrict__ s
   const int T = vr.T, C = vr.C, TC = T * C, vg = __builtin_ctz(vr.G);
   init_level_lut<BITS>(lut2, lut4);
   for (int x = t; x < Nq * TC; x += 256) ws[x] = 0ull;
-  float M[NQ];
-#pragma unroll
-  for (int jq = 0; jq < NQ; ++jq) {
-    M[jq] = -__builtin_inff();
-    if (jq < Nq)
-      for (int b = 0; b < nsplit; ++b) M[jq] = fmaxf(M[jq], rmax[((int64_t)h * Nq + jq) * nsplit + b]);
-  }
-  __syncthreads();
+  const float *sh = scores + (int64_t)h * Nq * N;
+  const int ntiles = (N + kAttnBN - 1) / kAttnBN;
+  const int tb = sp * tps, te = min(tb + tps, ntiles);
   float o[NQ][8], l[NQ];
 #pragma unroll
   for (int jq = 0; jq < NQ; ++jq) {
@@ -841,9 +812,6 @@ __global__ __launch_bounds__(256) void k_attn_values(const float *__restrict__ s
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[jq][e] = 0.0f;
   }
-  const float *sh = scores + (int64_t)h * Nq * N;
-  const int ntiles = (N + kAttnBN - 1) / kAttnBN;
-  const int tb = sp * tps, te = min(tb + tps, ntiles);
   const int dv = __builtin_ctz(D) - vg;
   // A tile's loads: this lane's code words, scale bytes and scores of tokens
   // slot, slot + SL, ... (residual term) and of token `lane` (weights), with
@@ -870,6 +838,29 @@ __global__ __launch_bounds__(256) void k_attn_values(const float *__restrict__ s
   };
   Raw cur;
   fetch(tb, cur);
+  // M: the run's largest score per query (8 loads in flight per round;
+  // clamped indices repeat a token, which does not change a maximum)
+  const int r0 = tb * kAttnBN, r1 = min(te * kAttnBN, N);
+  float M[NQ];
+#pragma unroll
+  for (int jq = 0; jq < NQ; ++jq) {
+    float m = -__builtin_inff();
+    if (jq < Nq)
+      for (int i0 = r0 + t; i0 < r1; i0 += 256 * 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = sh[(int64_t)jq * N + min(i0 + 256 * u, r1 - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m = fmaxf(m, v[u]);
+      }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) mred[wave][jq] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int jq = 0; jq < NQ; ++jq)
+    M[jq] = fmaxf(fmaxf(mred[0][jq], mred[1][jq]), fmaxf(mred[2][jq], mred[3][jq]));
   for (int tile = tb; tile < te; ++tile) {
     const int i0 = tile * kAttnBN;
     const int nt = min(kAttnBN, N - i0);
@@ -998,18 +989,24 @@ bool launch_attn_t(const float *q, int H, int Nq, int N, const AttnRec &kr, cons
 }
 
 // The two-pass path (k_attn_scores, k_attn_values); the scratch holds the
-// run records, the contraction parts, the scores [H][Nq][N] and the run
-// maxima [H][Nq][nsplit], in that order.
+// run records, the contraction parts and the scores [H][Nq][N], in that
+// order.  The scores pass cuts each head group's tiles into its own runs, so
+// that about kAttnTargetGroups workgroups fill the chip.
 template <int D, int NQ, int KT>
 bool launch_scores_t(const float *q, int H, int Nq, int N, const AttnRec &kr, float scale,
-                     const float *rcos, const float *rsin, const AttnSplit &sp, float *scores,
-                     float *rmax, hipStream_t s) {
+                     const float *rcos, const float *rsin, float *scores, hipStream_t s) {
+  const int HG = (H + 7) / 8, ngroups = (H + HG - 1) / HG;
+  const int ntiles = (N + kAttnBN - 1) / kAttnBN;
+  const int want = std::min(std::min(std::max(1, (kAttnTargetGroups + ngroups - 1) / ngroups),
+                                     kAttnMaxSplit), ntiles);
+  const int tps = (ntiles + want - 1) / want, nsplit = (ntiles + tps - 1) / tps;
+  const size_t lds = (size_t)HG * NQ * D * sizeof(float);
   if (kr.bits == 2)
-    hipLaunchKernelGGL((k_attn_scores<D, NQ, KT, 2>), dim3(H * sp.nsplit), dim3(256), 0, s, q, Nq,
-                       N, H, kr, scale, rcos, rsin, sp.nsplit, sp.tiles_per_split, scores, rmax);
+    hipLaunchKernelGGL((k_attn_scores<D, NQ, KT, 2>), dim3(ngroups * nsplit), dim3(256), lds, s, q,
+                       Nq, N, H, kr, scale, rcos, rsin, nsplit, tps, scores);
   else
-    hipLaunchKernelGGL((k_attn_scores<D, NQ, KT, 4>), dim3(H * sp.nsplit), dim3(256), 0, s, q, Nq,
-                       N, H, kr, scale, rcos, rsin, sp.nsplit, sp.tiles_per_split, scores, rmax);
+    hipLaunchKernelGGL((k_attn_scores<D, NQ, KT, 4>), dim3(ngroups * nsplit), dim3(256), lds, s, q,
+                       Nq, N, H, kr, scale, rcos, rsin, nsplit, tps, scores);
   return hipGetLastError() == hipSuccess;
 }
 
@@ -1022,22 +1019,21 @@ bool launch_attn_2p(const float *q, int H, int Nq, int N, const AttnRec &kr, con
   const int TC = vr.T * vr.C;
   float *cpart = part + (size_t)H * sp.nsplit * Nq * pf;
   float *scores = cpart + (size_t)H * Nq * kContractParts * D;
-  float *rmax = scores + (size_t)H * Nq * N;
   bool ok = false;
   switch (kr.T) {
-    case 1: ok = launch_scores_t<D, NQ, 1>(q, H, Nq, N, kr, scale, rcos, rsin, sp, scores, rmax, s); break;
-    case 2: ok = launch_scores_t<D, NQ, 2>(q, H, Nq, N, kr, scale, rcos, rsin, sp, scores, rmax, s); break;
-    case 3: ok = launch_scores_t<D, NQ, 3>(q, H, Nq, N, kr, scale, rcos, rsin, sp, scores, rmax, s); break;
-    case 4: ok = launch_scores_t<D, NQ, 4>(q, H, Nq, N, kr, scale, rcos, rsin, sp, scores, rmax, s); break;
+    case 1: ok = launch_scores_t<D, NQ, 1>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
+    case 2: ok = launch_scores_t<D, NQ, 2>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
+    case 3: ok = launch_scores_t<D, NQ, 3>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
+    case 4: ok = launch_scores_t<D, NQ, 4>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
   }
   if (!ok) return false;
   const size_t lds = (size_t)Nq * TC * sizeof(unsigned long long) + (size_t)4 * NQ * D * sizeof(float);
   if (vr.bits == 2)
     hipLaunchKernelGGL((k_attn_values<D, NQ, 2>), dim3(H * sp.nsplit), dim3(256), lds, s, scores,
-                       rmax, Nq, N, H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
+                       Nq, N, H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
   else
     hipLaunchKernelGGL((k_attn_values<D, NQ, 4>), dim3(H * sp.nsplit), dim3(256), lds, s, scores,
-                       rmax, Nq, N, H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
+                       Nq, N, H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
   if (hipGetLastError() != hipSuccess) return false;
   if (TC > 0) {
     hipLaunchKernelGGL((k_attn_contract<uint16_t>), dim3(Nq, H, kContractParts), dim3(256), 0, s,
@@ -1056,7 +1052,7 @@ template <typename Tc, int D>
 bool launch_attn_d(const float *q, int H, int Nq, int N, const AttnRec &kr, const AttnRec &vr,
                    float scale, const float *rcos, const float *rsin, float *part, float *out,
                    hipStream_t s) {
-  if (attn_two_pass(Nq, kr.T, vr.T, vr.C, sizeof(Tc) == 2)) {
+  if (attn_two_pass(H, Nq, kr.T, vr.T, vr.C, sizeof(Tc) == 2, N, D)) {
     if (Nq == 1) return launch_attn_2p<D, 1>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
     return launch_attn_2p<D, 4>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
   }
@@ -1086,8 +1082,11 @@ bool attn_uses_sums(int Nq, int T, int C) {
   return Nq <= kAttnSumQueries && (int64_t)Nq * T * C <= kAttnSumEntries;
 }
 
-bool attn_two_pass(int Nq, int kT, int vT, int vC, bool c_bf16) {
-  return c_bf16 && kT >= 1 && kT <= 4 && attn_uses_sums(Nq, vT, vC);
+bool attn_two_pass(int H, int Nq, int kT, int vT, int vC, bool c_bf16, int64_t N, int D) {
+  // k_attn_scores addresses the rotary rows with 32-bit byte offsets and
+  // keeps a head group's queries in LDS
+  return c_bf16 && kT >= 1 && kT <= 4 && attn_uses_sums(Nq, vT, vC) &&
+         N * 2 * D < ((int64_t)1 << 32) && H <= 256;
 }
 
 int attn_part_floats(int Nq, int D, int T, int C) {
@@ -1098,8 +1097,8 @@ size_t attn_scratch_floats(int H, int64_t N, int Nq, int D, int T, int C) {
   const AttnSplit sp = attn_split(H, N);
   const size_t runs = (size_t)H * sp.nsplit * Nq * attn_part_floats(Nq, D, T, C);
   const size_t contract = attn_uses_sums(Nq, T, C) ? (size_t)H * Nq * kContractParts * D : 0;
-  // scores and run maxima of the two-pass path (which needs weight sums)
-  const size_t two = attn_uses_sums(Nq, T, C) ? (size_t)H * Nq * (N + sp.nsplit) : 0;
+  // scores of the two-pass path (which needs weight sums)
+  const size_t two = attn_uses_sums(Nq, T, C) ? (size_t)H * Nq * N : 0;
   return runs + contract + two;
 }
 
