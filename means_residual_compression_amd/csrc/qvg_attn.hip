@@ -492,6 +492,22 @@ void k_attn_split(const float *__restrict__ q, int Nq, int N, int H, AttnRec kr,
     }
 }
 
+// Largest run maximum m_b of one (head, query): blockDim.x threads load the
+// runs' maxima in parallel, then reduce through `red` (blockDim.x floats).
+__device__ __forceinline__ float runs_max(const float *p, int64_t stride, int nsplit, float *red) {
+  float m = -__builtin_inff();
+  for (int b = threadIdx.x; b < nsplit; b += blockDim.x) m = fmaxf(m, p[b * stride]);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();  // red may be written again by the caller
+  return r;
+}
+
 // Weight-sum term, cut into kContractParts row ranges (one workgroup each):
 // with M the largest run maximum and w_b = e^(m_b - M), each range's rows r
 // get W[r] = sum_b w_b W_b[r] (merged in run order) and its share of
@@ -505,18 +521,25 @@ __global__ __launch_bounds__(256) void k_attn_contract(const float *__restrict__
                                                        float *__restrict__ cpart) {
   __shared__ float wl[2048 / kContractParts];  // T*C <= 2048
   __shared__ float red[256];
+  __shared__ float wb[kAttnMaxSplit];            // w_b per run
   const int qq = blockIdx.x, h = blockIdx.y, z = blockIdx.z, t = threadIdx.x;
   const int64_t stride = (int64_t)Nq * pf;
   const float *p = part + ((int64_t)h * nsplit * Nq + qq) * pf;
-  float M = -__builtin_inff();
-  for (int b = 0; b < nsplit; ++b) M = fmaxf(M, p[b * stride]);
+  const float M = runs_max(p, stride, nsplit, red);
+  for (int b = t; b < nsplit; b += 256) wb[b] = __expf(p[b * stride] - M);
+  __syncthreads();
   const int TC = vr.T * vr.C;
   const int r0 = z * TC / kContractParts, r1 = (z + 1) * TC / kContractParts, n = r1 - r0;
   for (int r = t; r < n; r += 256) {
     float acc = 0.0f;
-#pragma unroll 4
-    for (int b = 0; b < nsplit; ++b)
-      acc = __builtin_fmaf(p[b * stride + 2 + D + r0 + r], __expf(p[b * stride] - M), acc);
+    for (int b0 = 0; b0 < nsplit; b0 += 8) {  // 8 loads in flight, added in run order
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = p[min(b0 + u, nsplit - 1) * stride + 2 + D + r0 + r];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (b0 + u < nsplit) acc = __builtin_fmaf(v[u], wb[b0 + u], acc);
+    }
     wl[r] = acc;
   }
   __syncthreads();
@@ -551,17 +574,29 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float *__restrict__ 
                                                       int Nq, int D, int pf,
                                                       const float *__restrict__ cpart,
                                                       float *__restrict__ out) {
+  __shared__ float red[128];
   const int qq = blockIdx.x, h = blockIdx.y, k = threadIdx.x;
-  if (k >= D) return;
   const int64_t stride = (int64_t)Nq * pf;
   const float *p = part + ((int64_t)h * nsplit * Nq + qq) * pf;
-  float M = -__builtin_inff();
-  for (int b = 0; b < nsplit; ++b) M = fmaxf(M, p[b * stride]);
+  const float M = runs_max(p, stride, nsplit, red);
+  if (k >= D) return;
   float l = 0.0f, o = 0.0f;
-  for (int b = 0; b < nsplit; ++b) {
-    const float w = __expf(p[b * stride] - M);
-    l = __builtin_fmaf(p[b * stride + 1], w, l);
-    o = __builtin_fmaf(p[b * stride + 2 + k], w, o);
+  for (int b0 = 0; b0 < nsplit; b0 += 8) {  // 8 runs' loads in flight, merged in run order
+    float m[8], lb[8], ob[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t b = min(b0 + u, nsplit - 1) * stride;
+      m[u] = p[b];
+      lb[u] = p[b + 1];
+      ob[u] = p[b + 2 + k];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (b0 + u < nsplit) {
+        const float w = __expf(m[u] - M);
+        l = __builtin_fmaf(lb[u], w, l);
+        o = __builtin_fmaf(ob[u], w, o);
+      }
   }
   if (SUMS) {
     const float *cp = cpart + ((int64_t)h * Nq + qq) * kContractParts * D + k;
