@@ -290,7 +290,8 @@ qvg_status qvg_group_quant_pack(const void *r, qvg_dtype dtype, int64_t H, int64
  *   pairwise, times scale; then, with m the run's largest score, weights
  *   e^(s - m) (never rescaled): per run a fused multiply-add chain of
  *   (weight * s_hat) * level over 4 (d = 128) or 2 (d = 64) tokens per
- *   tile, the 16 or 32 chains added pairwise and by wave, and weight sums
+ *   tile (one query: over 1 token per pass of 64 or 128), the chains of a
+ *   wave added pairwise and the 4 waves in order, and weight sums
  *   kept exactly in units of 2^-40 (each weight rounded to the nearest
  *   unit) and rounded to fp32 once per run; runs merged as above.
  *   ws: device scratch of qvg_attention_workspace_size(H, Nq, N, d, vp)

@@ -983,6 +983,147 @@ __global__ __launch_bounds__(256) void k_attn_values(const float *__restrict__ s
   }
 }
 
+// k_attn_values for one query: a lane owns 32 consecutive channels of one
+// token per pass (four lanes per token for d = 128, two for d = 64), so a
+// token's weight is computed by 4 (or 2) lanes rather than 16, and the lane
+// accumulates its 32 channels in registers.  Weight sums, l and the record
+// are as in k_attn_values.  Summation order: an output element of one run is
+// a fused multiply-add chain over the run's tokens of that lane position
+// (one per pass), the 16 (or 32) lane chains of a wave added pairwise, then
+// the 4 waves in order.
+template <int D, int BITS>
+__global__ __launch_bounds__(256) void k_attn_values1(const float *__restrict__ scores, int N,
+                                                      int H, AttnRec vr, int nsplit, int tps,
+                                                      int pf, float *__restrict__ part) {
+  constexpr int LPT = D / 32, TPP = 256 / LPT;  // lanes per token, tokens per pass
+  constexpr int NW = BITS == 2 ? 2 : 4;         // code words (32 bits) per lane
+  constexpr int WCH = TPP / 64;                 // 64-token chunks per pass (weight sums)
+  __shared__ float4 lut2[BITS == 2 ? 256 : 1];
+  __shared__ float4 lut4v[BITS == 4 ? 128 : 1];  // [256] float2, 16-byte aligned
+  __shared__ float mred[4];
+  __shared__ float lred;
+  float2 *lut4 = reinterpret_cast<float2 *>(lut4v);
+  // [T][C] weight sums in units of 2^-40, then [4][D] wave outputs
+  extern __shared__ unsigned long long ws[];
+  int h, sp;
+  attn_item(H, nsplit, h, sp);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int part_ = t % LPT, tok = t / LPT, k0 = part_ * 32;
+  const int T = vr.T, C = vr.C, TC = T * C, vg = __builtin_ctz(vr.G);
+  init_level_lut<BITS>(lut2, lut4);
+  for (int x = t; x < TC; x += 256) ws[x] = 0ull;
+  const float *sh = scores + (int64_t)h * N;
+  const int ntiles = (N + kAttnBN - 1) / kAttnBN;
+  const int tb = sp * tps, te = min(tb + tps, ntiles);
+  const int r0 = tb * kAttnBN, r1 = min(te * kAttnBN, N);
+  const uint8_t *codes = vr.codes + (int64_t)h * N * (D * BITS / 8);
+  const uint8_t *scl = vr.scales + ((int64_t)h * N << (__builtin_ctz(D) - vg));
+  const int dv = __builtin_ctz(D) - vg;
+  // A pass's loads: this lane's code words, scale bytes and score, and for
+  // the weight sums the score and stage-`wave` assignment byte of token
+  // `lane` of each 64-token chunk; tokens past the run repeat its last one.
+  struct Raw {
+    uint32_t w[NW], e[4], a[WCH];
+    float s, sw[WCH];
+  };
+  auto fetch = [&](int b0, Raw &r) {
+    const uint32_t ti = (uint32_t)min(b0 + tok, r1 - 1);
+    const uint8_t *crow = codes + ti * (uint32_t)(D * BITS / 8) + k0 * BITS / 8;
+    if constexpr (BITS == 2) {
+      const uint2 x = *reinterpret_cast<const uint2 *>(crow);
+      r.w[0] = x.x, r.w[1] = x.y;
+    } else {
+      const uint4 x = *reinterpret_cast<const uint4 *>(crow);
+      r.w[0] = x.x, r.w[1] = x.y, r.w[2] = x.z, r.w[3] = x.w;
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) r.e[g] = scl[(ti << dv) + ((k0 + 8 * g) >> vg)];
+    r.s = sh[ti];
+#pragma unroll
+    for (int c = 0; c < WCH; ++c) {
+      const uint32_t tl = (uint32_t)min(b0 + 64 * c + lane, r1 - 1);
+      r.sw[c] = sh[tl];
+      r.a[c] = wave < T ? vr.assign[((int64_t)h * T + wave) * N + tl] : 0u;
+    }
+  };
+  Raw cur;
+  fetch(r0, cur);
+  // m: the run's largest score (8 loads in flight per round)
+  {
+    float m = -__builtin_inff();
+    for (int i0 = r0 + t; i0 < r1; i0 += 256 * 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = sh[min(i0 + 256 * u, r1 - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) m = fmaxf(m, v[u]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) mred[wave] = m;
+  }
+  __syncthreads();
+  const float M = fmaxf(fmaxf(mred[0], mred[1]), fmaxf(mred[2], mred[3]));
+  float o[32], l = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) o[e] = 0.0f;
+  for (int b0 = r0; b0 < r1; b0 += TPP) {
+    Raw nx;
+    fetch(min(b0 + TPP, r1 - 1), nx);
+    // residual term: this lane's 32 channels of its token
+    const float p = b0 + tok < r1 ? __expf(cur.s - M) : 0.0f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float lv[8];
+      const uint32_t w = BITS == 2 ? (cur.w[g >> 1] >> (16 * (g & 1))) & 0xFFFFu : cur.w[g];
+      levels8(w, BITS, lut2, lut4, lv);
+      const float ps = p * e4m3_decode_bits(cur.e[g]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[8 * g + e] = __builtin_fmaf(ps, lv[e], o[8 * g + e]);
+    }
+    // weight sums (wave w: stages w, w + 4, ...) and l (wave 0); lane = token
+    if (wave == 0 || wave < T) {
+#pragma unroll
+      for (int c = 0; c < WCH; ++c) {
+        const bool valid = b0 + 64 * c + lane < r1;
+        const float pw = valid ? __expf(cur.sw[c] - M) : 0.0f;
+        if (wave == 0) l += pw;
+        const unsigned long long pq = __float2ull_rn(pw * 0x1p40f);
+        const int tl = min(b0 + 64 * c + lane, r1 - 1);
+        for (int ts = wave; ts < T; ts += 4) {
+          const uint32_t raw = ts == wave ? cur.a[c] : vr.assign[((int64_t)h * T + ts) * N + tl];
+          if (valid) atomicAdd(ws + ts * C + min((int)raw, C - 1), pq);
+        }
+      }
+    }
+    cur = nx;
+  }
+  // combine: lanes of one channel range are lane % LPT apart by multiples of
+  // LPT within a wave (added pairwise), then the 4 waves in order
+  float *wout = reinterpret_cast<float *>(ws + TC);  // [4][D]
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1)
+#pragma unroll
+    for (int e = 0; e < 32; ++e) o[e] = o[e] + __shfl_xor(o[e], off);
+  if (lane < LPT)
+#pragma unroll
+    for (int e = 0; e < 32; ++e) wout[wave * D + k0 + e] = o[e];
+  if (wave == 0) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) l = l + __shfl_xor(l, off);
+    if (lane == 0) lred = l;
+  }
+  __syncthreads();
+  float *rec = part + ((int64_t)h * nsplit + sp) * pf;
+  for (int k = t; k < D; k += 256)
+    rec[2 + k] = ((wout[k] + wout[D + k]) + wout[2 * D + k]) + wout[3 * D + k];
+  if (t == 0) {
+    rec[0] = M;
+    rec[1] = lred;
+  }
+  for (int x = t; x < TC; x += 256) rec[2 + D + x] = __ull2float_rn(ws[x]) * 0x1p-40f;
+}
+
 namespace {
 
 int nq_bucket(int Nq) { return Nq <= 1 ? 1 : Nq <= 4 ? 4 : 16; }
@@ -1063,7 +1204,13 @@ bool launch_attn_2p(const float *q, int H, int Nq, int N, const AttnRec &kr, con
   }
   if (!ok) return false;
   const size_t lds = (size_t)Nq * TC * sizeof(unsigned long long) + (size_t)4 * NQ * D * sizeof(float);
-  if (vr.bits == 2)
+  if (NQ == 1 && vr.bits == 2)
+    hipLaunchKernelGGL((k_attn_values1<D, 2>), dim3(H * sp.nsplit), dim3(256), lds, s, scores, N,
+                       H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
+  else if (NQ == 1)
+    hipLaunchKernelGGL((k_attn_values1<D, 4>), dim3(H * sp.nsplit), dim3(256), lds, s, scores, N,
+                       H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
+  else if (vr.bits == 2)
     hipLaunchKernelGGL((k_attn_values<D, NQ, 2>), dim3(H * sp.nsplit), dim3(256), lds, s, scores,
                        Nq, N, H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
   else

@@ -148,6 +148,11 @@ CASES = [
     (4, 321, 128, 4, (1, 256, 2, 64), (1, 256, 2, 64), torch.bfloat16, True),
     (2, 2500, 128, 4, (8, 256, 2, 64), (8, 256, 2, 64), torch.bfloat16, True),
     (5, 130000, 64, 2, (2, 128, 2, 16), (1, 32, 4, 64), torch.float32, False),
+    # two-pass variants: d=64 one query (INT4 and INT2 with groups of 8), and
+    # three queries with INT4 values
+    (2, 4099, 64, 1, (3, 128, 4, 16), (2, 64, 4, 32), torch.bfloat16, True),
+    (3, 5000, 64, 1, (4, 256, 2, 8), (4, 256, 2, 8), torch.bfloat16, True),
+    (2, 3001, 128, 3, (2, 64, 4, 32), (3, 128, 4, 16), torch.bfloat16, True),
 ]
 
 
