@@ -609,8 +609,8 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float *__restrict__ 
 // With bf16 centroid tables, keys of 1 to 4 stages, weight sums and up to
 // kAttnSumQueries queries, the attention takes two passes over the records
 // instead of k_attn_split:
-//  * k_attn_scores (keys only): a workgroup takes a run of tokens for the
-//    group of heads one XCD owns (their tables stay in its L2).  Eight lanes
+//  * k_attn_scores (keys only): a workgroup takes a run of tokens for a
+//    group of heads (score_group).  Eight lanes
 //    per token (d = 128; four for d = 64), each holding 8 rotate-half channel
 //    pairs (channels k .. k+7 and d/2 + k ..), rebuild the key in registers
 //    as k_attn_split does, rotate it and take its products with each query
@@ -680,9 +680,20 @@ __device__ __forceinline__ void init_level_lut(float4 *lut2, float2 *lut4) {
     lut4[t] = make_float2((float)(2 * (t & 15) - 15), (float)(2 * ((t >> 4) & 15) - 15));
 }
 
-// Scores: workgroup -> (group of the heads an XCD owns, run of tiles).  A
-// lane keeps its token's rotary rows in registers while it scores the token
-// for every head of the group.
+// Heads per scores workgroup: half of them (at most 32, and at most 32 KB of
+// queries in LDS).  Each token's rotary rows are then read by the XCDs
+// of two groups, and an XCD's L2 holds the tables of one group; smaller
+// groups re-read the rotary rows on more XCDs, larger ones lose the tables
+// from L2 (measured on the decode-side records: 5, 10, 20 and 40 heads per
+// group fetch 1.69, 1.36, 1.29 and 1.26 GB and take 663, 654, 655 and 708 us).
+__host__ __device__ inline int score_group(int H, int NQ, int D) {
+  const int cap = 8192 / (NQ * D) < 32 ? 8192 / (NQ * D) : 32;
+  return (H + 1) / 2 < cap ? (H + 1) / 2 : cap;
+}
+
+// Scores: workgroup -> (group of heads, run of tiles), consecutive items on
+// one XCD.  A lane keeps its token's rotary rows in registers while it
+// scores the token for every head of the group.
 template <int D, int NQ, int KT, int BITS>
 __global__ __launch_bounds__(256) void k_attn_scores(const float *__restrict__ q, int Nq, int N,
                                                      int H, AttnRec kr, float scale,
@@ -694,7 +705,7 @@ __global__ __launch_bounds__(256) void k_attn_scores(const float *__restrict__ q
   __shared__ float4 lut2[BITS == 2 ? 256 : 1];
   __shared__ float2 lut4[BITS == 4 ? 256 : 1];
   extern __shared__ float qs[];  // [gh][NQ][D] queries of the group's heads
-  const int HG = (H + 7) >> 3, ngroups = (H + HG - 1) / HG;
+  const int HG = score_group(H, NQ, D), ngroups = (H + HG - 1) / HG;
   const int total = ngroups * nsplit, wg = blockIdx.x, xcd = wg & 7, slot = wg >> 3;
   const int item = xcd * (total >> 3) + min(xcd, total & 7) + slot;
   const int grp = item / nsplit, sp = item - grp * nsplit;
@@ -1171,7 +1182,7 @@ bool launch_attn_t(const float *q, int H, int Nq, int N, const AttnRec &kr, cons
 template <int D, int NQ, int KT>
 bool launch_scores_t(const float *q, int H, int Nq, int N, const AttnRec &kr, float scale,
                      const float *rcos, const float *rsin, float *scores, hipStream_t s) {
-  const int HG = (H + 7) / 8, ngroups = (H + HG - 1) / HG;
+  const int HG = score_group(H, NQ, D), ngroups = (H + HG - 1) / HG;
   const int ntiles = (N + kAttnBN - 1) / kAttnBN;
   const int want = std::min(std::min(std::max(1, (kAttnTargetGroups + ngroups - 1) / ngroups),
                                      kAttnMaxSplit), ntiles);
