@@ -39,11 +39,15 @@ size_t up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 // Workspace layout shared by the size query and the carve-up.
 struct Layout {
   size_t rt, tb, cent, ctab, cinit, cbnd, stats, recheck, fallback, counters, sorted, offs, hist,
-      cofs, chunk_j, part, pflag, stage_re, stage_fb, span, idx;
+      cofs, chunk_j, part, pflag, stage_re, stage_fb, span, idx, isum, lminv, prev, mcnt;
   size_t total;
+  bool incremental;
 };
 
-Layout make_layout(int64_t H, int64_t N, int64_t d, int64_t C, int64_t T, bool need_idx) {
+// incremental: room for the state of the incremental centroid update (the
+// compress paths; the lone assign has no update).
+Layout make_layout(int64_t H, int64_t N, int64_t d, int64_t C, int64_t T, bool need_idx,
+                   bool incremental = true) {
   const int64_t Cp = std::max<int64_t>(32, pad32((int)C));
   const int64_t NT = (N + kTile - 1) / kTile;
   const int64_t Ts = std::max<int64_t>(T, 1);
@@ -71,6 +75,11 @@ Layout make_layout(int64_t H, int64_t N, int64_t d, int64_t C, int64_t T, bool n
   L.stage_fb = take((size_t)(H * (NT + 15) * kTile * 8));
   L.span = take((size_t)(H * kSpanParts * d * 4));
   L.idx = take(need_idx ? (size_t)(H * T * C * 4) : 0);
+  L.incremental = incremental;
+  L.isum = take(incremental ? (size_t)(H * Cp * d * 8) : 0);
+  L.lminv = take(incremental ? (size_t)(H * d * 4) : 0);
+  L.prev = take(incremental ? (size_t)(2 * H * N) : 0);
+  L.mcnt = take(incremental ? (size_t)(H * ((N + kSortChunk - 1) / kSortChunk) * 4) : 0);
   L.total = o;
   return L;
 }
@@ -99,6 +108,11 @@ Ws carve(void *ws, const Layout &L) {
   w.stage_fb = (int2 *)(b + L.stage_fb);
   w.span = (uint32_t *)(b + L.span);
   w.idx = (int32_t *)(b + L.idx);
+  const bool inc = L.incremental;
+  w.isum = inc ? (long long *)(b + L.isum) : nullptr;
+  w.lminv = inc ? (uint32_t *)(b + L.lminv) : nullptr;
+  w.prev = inc ? (uint8_t *)(b + L.prev) : nullptr;
+  w.mcnt = inc ? (uint32_t *)(b + L.mcnt) : nullptr;
   return w;
 }
 
@@ -205,10 +219,10 @@ qvg_status run_compress(const void *x, int64_t H, int64_t N, const qvg_params *p
       const int log_slot = t * iters + it;
       ok = in_bf16 ? launch_update<uint16_t, Tc, D>(a, next, !last, last ? rec_c : nullptr,
                                                     rec_hstride, last ? cache_t : nullptr,
-                                                    rec_hstride, log_slot, it == 0, s)
+                                                    rec_hstride, log_slot, it, s)
                    : launch_update<float, Tc, D>(a, next, !last, last ? rec_c : nullptr,
                                                  rec_hstride, last ? cache_t : nullptr,
-                                                 rec_hstride, log_slot, it == 0, s);
+                                                 rec_hstride, log_slot, it, s);
       if (!ok) return hip_fail("kmeans_update");
     }
   }
@@ -496,7 +510,7 @@ qvg_status qvg_candidate_counts(const void *ws, int64_t H, int64_t N, int64_t d,
 
 size_t qvg_assign_workspace_size(int64_t H, int64_t N, int64_t d, int32_t C) {
   if (check_dims(H, N, d, QVG_F32) != QVG_OK || C < 1 || C > kMaxC || C > N) return 0;
-  return make_layout(H, N, d, C, 1, false).total;
+  return make_layout(H, N, d, C, 1, false, false).total;
 }
 
 qvg_status qvg_kmeans_assign(const void *r, qvg_dtype dtype, int64_t H, int64_t N, int64_t d,
@@ -507,7 +521,7 @@ qvg_status qvg_kmeans_assign(const void *r, qvg_dtype dtype, int64_t H, int64_t 
   if (st != QVG_OK) return st;
   if (C < 1 || C > kMaxC || C > N) return fail(QVG_ERR_UNSUPPORTED, "C=%d must be in [1, min(256, N)]", C);
   if (!r || !centroids || !assign) return fail(QVG_ERR_INVALID_ARG, "NULL pointer argument");
-  const Layout L = make_layout(H, N, d, C, 1, false);
+  const Layout L = make_layout(H, N, d, C, 1, false, false);
   if (!ws || ws_bytes < L.total) return fail(QVG_ERR_WORKSPACE, "workspace smaller than %zu bytes", L.total);
   if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(QVG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   const Ws w = carve(ws, L);
@@ -585,11 +599,11 @@ qvg_status qvg_kmeans_update(const void *r, qvg_dtype dtype, int64_t H, int64_t 
   const bool bf = dtype == QVG_BF16;
   bool ok;
   if (d == 64)
-    ok = bf ? launch_update<uint16_t, float, 64>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, false, s)
-            : launch_update<float, float, 64>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, false, s);
+    ok = bf ? launch_update<uint16_t, float, 64>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, -1, s)
+            : launch_update<float, float, 64>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, -1, s);
   else
-    ok = bf ? launch_update<uint16_t, float, 128>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, false, s)
-            : launch_update<float, float, 128>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, false, s);
+    ok = bf ? launch_update<uint16_t, float, 128>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, -1, s)
+            : launch_update<float, float, 128>(a, S_B0, false, nullptr, 0, nullptr, 0, -1, -1, s);
   return ok ? QVG_OK : hip_fail("kmeans_update");
 }
 

@@ -57,6 +57,12 @@ struct Ws {
   int2 *stage_fb;     // [H*(NT+15)*32] fallback entries staged per assign workgroup
   uint32_t *span;     // [H][kSpanParts][D] per-channel emax | lmin << 16 of chunk groups
   int32_t *idx;       // [H][T][C] device copy of the seeded init indices
+  // Incremental update of heads whose stage sums are exact (null: always the
+  // full update).
+  long long *isum;    // [H][Cp][D] cluster sums as integers, units 2^(lmin - 150)
+  uint32_t *lminv;    // [H][D] per-channel lowest-bit bound lmin of the stage residual
+  uint8_t *prev;      // [2][H][N] assignments at the last two updates (iteration parity)
+  uint32_t *mcnt;     // [H][ceil(N/kSortChunk)] moved tokens listed by each sort block
 };
 
 constexpr int kSpanParts = 32;  // chunk groups per head in the span reduction

@@ -57,11 +57,13 @@ bool launch_kmeans_stage_begin(const KmArgs &a, hipStream_t s);
 template <typename Tin, int D>
 bool launch_assign(const KmArgs &a, int bslot, hipStream_t s);
 template <typename Tin, typename Tc, int D>
-// reduce_span: after the chunk sums, reduce their spans over each head (the
-// first iteration of a stage), so later iterations can skip the tracking.
+// iter: the iteration within the stage, or -1 for a lone update.  Iteration 0
+// reduces the chunk sums' spans over each head, so later iterations skip the
+// tracking; with a.ws.isum set it also keeps the sums of heads whose stage
+// sums are exact, and later iterations update those heads from the tokens
+// whose assignment changed.
 bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int64_t rec_hstride,
-                   float *cache, int64_t cache_hstride, int log_slot, bool reduce_span,
-                   hipStream_t s);
+                   float *cache, int64_t cache_hstride, int log_slot, int iter, hipStream_t s);
 
 // Records of consecutive chunks of one stream for one reconstruction launch:
 // chunk c holds tokens [off[c], off[c+1]) of the launch's span, which starts

@@ -24,6 +24,15 @@
 // when those show that some partial sum of the cluster could round, the
 // cluster is summed again in one sequential token-order pass.  Either way the
 // sum equals the sequential fp64 sum of a plain loop.
+//
+// The first iteration of a stage also reduces those spans over each head.
+// When they show every sum of the stage exact (the usual case), the sums are
+// kept as integers in units of each channel's lowest bit, and every later
+// iteration of the stage only moves the tokens whose assignment changed from
+// their old cluster's sum to the new one (k_hist lists them, k_delta adds
+// them): integer sums do not depend on the order, so they stay the sequential
+// fp64 sums.  Heads without that proof are summed in token order by
+// k_finalize from a scan of the assignments.
 #include "qvg_common.h"
 #include "qvg_internal.h"
 
@@ -59,6 +68,13 @@ __device__ __forceinline__ float block_max(float m) {
   if (threadIdx.x == 0)
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, part[w]);
   return m;
+}
+
+// A head whose stage spans are known to keep every cluster sum exact (S_SPAN
+// == 1): it skips the per-chunk span tracking, and after the first iteration
+// of the stage its sums are updated incrementally (k_delta).
+__device__ __forceinline__ bool head_sums_exact(const uint32_t *stats, int stat_stride, int h) {
+  return (__builtin_amdgcn_readfirstlane(stats[(int64_t)h * stat_stride + S_SPAN]) & 3u) == 1u;
 }
 
 template <typename Tin>
@@ -820,16 +836,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 // chunk's start position per cluster from the counts and writes the ids with
 // ranks taken from ballots, so token order is kept within every cluster.
 // k_hist also clears the next bound slot of the head and (first chunk of head
-// 0) logs and clears the candidate-list counters.
+// 0) logs and clears the candidate-list counters.  With prev set it copies the
+// assignments to prev[par ^ 1]; with `delta` set, a head whose stage sums are
+// exact also lists the tokens of this block whose assignment differs from
+// prev[par] (the previous update's) in its own segment moved[h][lo ..) (in no
+// particular order), and their number in mcnt[h][b].
 __global__ __launch_bounds__(256) void k_hist(const uint8_t *__restrict__ assign,
                                               int64_t assign_hstride, int N,
                                               uint32_t *__restrict__ hist, uint32_t *stats,
                                               int stat_stride, int clear_slot,
-                                              uint32_t *counters, int log_slot) {
+                                              uint32_t *counters, int log_slot,
+                                              uint8_t *__restrict__ prev, int par, int delta,
+                                              int32_t *__restrict__ moved,
+                                              uint32_t *__restrict__ mcnt) {
   __shared__ uint32_t cnt[kMaxC];
+  __shared__ uint32_t nmv;
   const int h = blockIdx.y, b = blockIdx.x;
-  const int nb = gridDim.x;
+  const int nb = gridDim.x, H = gridDim.y;
   cnt[threadIdx.x] = 0;
+  if (threadIdx.x == 0) nmv = 0u;
   if (b == 0 && threadIdx.x < 4) stats[(int64_t)h * stat_stride + clear_slot + threadIdx.x] = 0;
   if (b == 0 && h == 0 && threadIdx.x < 2) {
     // keep the finished iteration's candidate counts for diagnostics
@@ -837,12 +862,35 @@ __global__ __launch_bounds__(256) void k_hist(const uint8_t *__restrict__ assign
       counters[4 + 2 * log_slot + threadIdx.x] = counters[threadIdx.x];
     counters[threadIdx.x] = 0;
   }
+  const bool track = prev && delta && head_sums_exact(stats, stat_stride, h);
   __syncthreads();
   const uint8_t *a = assign + (int64_t)h * assign_hstride;
+  const uint8_t *pr = prev ? prev + ((int64_t)par * H + h) * N : nullptr;
+  uint8_t *pw = prev ? prev + ((int64_t)(par ^ 1) * H + h) * N : nullptr;
   const int lo = b * kSortChunk, hi = min(N, lo + kSortChunk);
-  for (int i = lo + threadIdx.x; i < hi; i += 256) atomicAdd(&cnt[a[i]], 1u);
+  int32_t *seg = moved + (int64_t)h * N + lo;
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int i0 = lo; i0 < hi; i0 += 256) {  // uniform trip count (ballots below)
+    const int i = i0 + (int)threadIdx.x;
+    const bool in = i < hi;
+    const uint32_t j = in ? (uint32_t)a[i] : 0u;
+    if (in) {
+      atomicAdd(&cnt[j], 1u);
+      if (pw) pw[i] = (uint8_t)j;
+    }
+    if (track) {
+      const bool ch = in && (uint32_t)pr[i] != j;
+      const uint64_t m = __ballot(ch);
+      uint32_t base = 0;
+      if (m && lane == 0) base = atomicAdd(&nmv, (uint32_t)__popcll(m));
+      base = __shfl(base, 0);
+      if (ch) seg[base + __popcll(m & lt)] = i;
+    }
+  }
   __syncthreads();
   hist[((int64_t)h * nb + b) * kMaxC + threadIdx.x] = cnt[threadIdx.x];
+  if (track && threadIdx.x == 0) mcnt[(int64_t)h * nb + b] = nmv;
 }
 
 // Inclusive scan of one value per thread over a 256-thread workgroup: a
@@ -1085,12 +1133,6 @@ __device__ __forceinline__ void chunk_sum_body(const ResView<Tin> &rv, int Cp,
   }
 }
 
-// A head whose stage spans are known to keep every cluster sum exact (S_SPAN
-// == 1) skips the per-chunk span tracking.
-__device__ __forceinline__ bool head_sums_exact(const uint32_t *stats, int stat_stride, int h) {
-  return (__builtin_amdgcn_readfirstlane(stats[(int64_t)h * stat_stride + S_SPAN]) & 3u) == 1u;
-}
-
 template <typename Tin, int D, int NSUB>
 __global__ __launch_bounds__(256) void k_chunk_sum(ResView<Tin> rv, int Cp,
                                                    const int32_t *__restrict__ sorted,
@@ -1143,7 +1185,8 @@ __global__ __launch_bounds__(256) void k_span_part(const uint32_t *__restrict__ 
 }
 template <int D>
 __global__ __launch_bounds__(D) void k_span_final(const uint32_t *__restrict__ span, int N,
-                                                  uint32_t *__restrict__ stats, int stat_stride) {
+                                                  uint32_t *__restrict__ stats, int stat_stride,
+                                                  uint32_t *__restrict__ lminv) {
   const int h = blockIdx.x;
   uint32_t emax = 0u, lmin = 0xFFFFu;
 #pragma unroll 8
@@ -1154,8 +1197,136 @@ __global__ __launch_bounds__(D) void k_span_final(const uint32_t *__restrict__ s
   }
   const int lg = N > 1 ? 32 - __builtin_clz((uint32_t)(N - 1)) : 0;
   const int risky = (int)emax - (int)lmin + lg > 29;
+  if (lminv) lminv[(int64_t)h * D + threadIdx.x] = lmin;
   const int any = __syncthreads_or(risky);
   if (threadIdx.x == 0) stats[(int64_t)h * stat_stride + S_SPAN] = 1u | (any ? 2u : 0u);
+}
+
+// ------------------------------------------------------ incremental update
+// For a head whose stage sums are exact (S_SPAN == 1), every value of channel
+// k of the stage residual is an integer multiple of 2^(lmin_k - 150) and every
+// sum of distinct members is below 2^53 of those units (the span condition),
+// so the cluster sums are kept as int64 multiples of 2^(lmin_k - 150): integer
+// adds are exact in any order, and the fp64 value of a sum is the sequential
+// fp64 sum.  From the second iteration of the stage on, only the tokens whose
+// assignment changed since the previous update (listed by k_hist) move their
+// rows: subtracted from the old cluster's sum, added to the new one.
+__device__ __forceinline__ long long to_units(double v, uint32_t lmin) {
+  return (long long)ldexp(v, 150 - (int)lmin);  // an integer below 2^53: exact
+}
+__device__ __forceinline__ double from_units(long long q, uint32_t lmin) {
+  return ldexp((double)q, (int)lmin - 150);
+}
+
+// One workgroup per (8 channels, head), all workgroups of a head on one XCD
+// (workgroups are dealt to the 8 XCDs in turn by id), so the moved rows they
+// share come from HBM once and from that XCD's L2 afterwards.  The sums of the
+// workgroup's channels for every cluster live in LDS (rows padded to 9 words
+// against bank conflicts); the moved tokens of up to 512 sort blocks at a time
+// are located through a prefix sum of the blocks' counts; up to four tokens
+// per lane are in flight (fewer for later stages, which hold more rows), each
+// row rebuilt as R(t) = x - C(1)[pi(1)] - ... (the arithmetic of the full
+// update) and added with 64-bit LDS atomics.  The workgroup then adds its
+// slice to isum (it is the slice's only writer; the slice is loaded first).
+constexpr int kDeltaRow = 9;
+constexpr int kDeltaThreads = 512;
+__host__ __device__ inline int delta_grid(int H, int D) { return 8 * ((H + 7) / 8) * (D / 8); }
+
+template <typename Tin, int D, int NSUB>
+__global__ __launch_bounds__(kDeltaThreads) void k_delta(
+    ResView<Tin> rv, int H, int Cp, const uint8_t *__restrict__ assign, int64_t assign_hstride,
+    const uint8_t *__restrict__ prev, int par, const int32_t *__restrict__ moved,
+    const uint32_t *__restrict__ mcnt, int nb, const uint32_t *__restrict__ lminv,
+    long long *__restrict__ isum, const uint32_t *__restrict__ stats, int stat_stride) {
+  constexpr int U = NSUB <= 1 ? 4 : (NSUB <= 3 ? 2 : 1);
+  constexpr int S = D / 8;                       // channel slices per head
+  constexpr int QS = kMaxC * 8 / kDeltaThreads;  // isum words per thread
+  __shared__ unsigned long long acc[kMaxC * kDeltaRow];
+  __shared__ uint32_t pre[kDeltaThreads + 1];
+  __shared__ uint32_t wsum[kDeltaThreads / 64];
+  const int xcd = blockIdx.x % 8, k = blockIdx.x / 8;
+  const int h = xcd + 8 * (k / S), k0 = (k % S) * 8;
+  if (h >= H) return;
+  const int N = rv.N;
+  // independent loads first: the slice of isum and the channel bounds
+  long long *dst = isum + (int64_t)h * Cp * D + k0;
+  long long old[QS];
+#pragma unroll
+  for (int r = 0; r < QS; ++r) {
+    const int q = r * kDeltaThreads + (int)threadIdx.x;
+    old[r] = q < Cp * 8 ? dst[(int64_t)(q >> 3) * D + (q & 7)] : 0ll;
+  }
+  uint32_t lm[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) lm[e] = lminv[(int64_t)h * D + k0 + e];
+  if (!head_sums_exact(stats, stat_stride, h)) return;
+  for (int q = threadIdx.x; q < Cp * kDeltaRow; q += kDeltaThreads) acc[q] = 0ull;
+  const uint8_t *ah = assign + (int64_t)h * assign_hstride;
+  const uint8_t *ph = prev + ((int64_t)par * H + h) * N;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  bool any = false;
+  for (int b0 = 0; b0 < nb; b0 += kDeltaThreads) {
+    // exclusive prefix of the counts of blocks b0 .. b0+511
+    uint32_t c = b0 + (int)threadIdx.x < nb ? mcnt[(int64_t)h * nb + b0 + threadIdx.x] : 0u;
+    c = min(c, (uint32_t)kSortChunk);
+    uint32_t v = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t u = __shfl_up(v, o);
+      if (lane >= o) v += u;
+    }
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    uint32_t add = 0;
+    for (int w = 0; w < wave; ++w) add += wsum[w];
+    pre[threadIdx.x + 1] = v + add;
+    if (threadIdx.x == 0) pre[0] = 0u;
+    __syncthreads();
+    const int tot = (int)pre[kDeltaThreads];
+    any |= tot > 0;
+    for (int f0 = 0; f0 < tot; f0 += U * kDeltaThreads) {
+      int tok[U];
+      bool ok[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int f = min(f0 + u * kDeltaThreads + (int)threadIdx.x, tot - 1);
+        ok[u] = f0 + u * kDeltaThreads + (int)threadIdx.x < tot;
+        int lo = 0, hi = kDeltaThreads;  // last block with pre[block] <= f
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if ((int)pre[mid] <= f) lo = mid; else hi = mid;
+        }
+        const int64_t at = (int64_t)(b0 + lo) * kSortChunk + (f - (int)pre[lo]);
+        tok[u] = min(max(moved[(int64_t)h * N + min(at, (int64_t)N - 1)], 0), N - 1);
+      }
+      uint32_t jn[U], jo[U];
+      float v8[U][8];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        jn[u] = ah[tok[u]];
+        jo[u] = ph[tok[u]];
+        rv.template load8_n<NSUB>(h, tok[u], k0, v8[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (!ok[u] || jn[u] >= (uint32_t)Cp || jo[u] >= (uint32_t)Cp) continue;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const long long q = to_units((double)v8[u][e], lm[e]);
+          atomicAdd(&acc[jn[u] * kDeltaRow + e], (unsigned long long)q);
+          atomicAdd(&acc[jo[u] * kDeltaRow + e], (unsigned long long)(-q));
+        }
+      }
+    }
+    __syncthreads();  // pre and wsum are rewritten by the next pass
+  }
+  if (!any) return;  // uniform: nothing moved
+#pragma unroll
+  for (int r = 0; r < QS; ++r) {
+    const int q = r * kDeltaThreads + (int)threadIdx.x;
+    if (q < Cp * 8)
+      dst[(int64_t)(q >> 3) * D + (q & 7)] = old[r] + (long long)acc[(q >> 3) * kDeltaRow + (q & 7)];
+  }
 }
 
 template <typename Tin, typename Tc, int D>
@@ -1165,8 +1336,12 @@ __global__ __launch_bounds__(256) void k_finalize(
     const double *__restrict__ part, float *__restrict__ cent, const uint32_t *stats,
     uint32_t *stats_w, int stat_stride, int bslot, half8 *__restrict__ ctab,
     float *__restrict__ cinit, float4 *__restrict__ cbnd, Tc *__restrict__ rec_c,
-    int64_t rec_hstride, float *__restrict__ cache, int64_t cache_hstride) {
+    int64_t rec_hstride, float *__restrict__ cache, int64_t cache_hstride,
+    long long *__restrict__ isum, const uint32_t *__restrict__ lminv,
+    const uint32_t *__restrict__ hist, int nb, int mode, const uint8_t *__restrict__ assign,
+    int64_t assign_hstride) {
   constexpr int PER = D / 64;
+  __shared__ int32_t mem[4][64];  // member ids per wave (mode 2, inexact heads)
   const int h = blockIdx.y;
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -1175,14 +1350,78 @@ __global__ __launch_bounds__(256) void k_finalize(
     if (ctab) emit_pad<D>(h, j, Cp, ctab, cinit, cbnd);
     return;
   }
-  const int n = __builtin_amdgcn_readfirstlane(offs[(int64_t)h * (Cp + 1) + j + 1] -
-                                               offs[(int64_t)h * (Cp + 1) + j]);
+  const bool head_exact = head_sums_exact(stats, stat_stride, h);
+  // mode 1 (first iteration of a stage): keep the exact sums as integers;
+  // mode 2 (later iterations): exact heads read them, as updated by k_delta
+  long long *isj = isum ? isum + ((int64_t)h * Cp + j) * D + lane * PER : nullptr;
+  const uint32_t *lmj = lminv ? lminv + (int64_t)h * D + lane * PER : nullptr;
+  double s[PER];
+  int n;
+  if (mode == 2 && head_exact) {
+    // member count: the column of this iteration's per-chunk histograms
+    uint32_t c = 0u;
+    for (int b = lane; b < nb; b += 64) c += hist[((int64_t)h * nb + b) * kMaxC + j];
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+    n = (int)__builtin_amdgcn_readfirstlane(c);
+#pragma unroll
+    for (int m = 0; m < PER; ++m) s[m] = from_units(isj[m], lmj[m]);
+  } else if (mode == 2) {
+    // a head whose sums are not exact, after the first iteration (no sort
+    // ran): the members are found in token order by scanning the
+    // assignments and added one by one (the plain sequential sum; members
+    // are buffered 64 at a time so that 32 rows are loaded together)
+    const uint8_t *ah = assign + (int64_t)h * assign_hstride;
+    const int wv = threadIdx.x >> 6, N = rv.N;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int m = 0; m < PER; ++m) s[m] = 0.0;
+    n = 0;
+    int nbuf = 0;  // wave-uniform
+    auto flush = [&]() {
+      for (int q = 0; q < nbuf; q += 32) {
+        const int32_t myid = mem[wv][min(q + (lane & 31), nbuf - 1)];
+        float v[32][PER];
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+          const int64_t row = __builtin_amdgcn_readlane(myid, u);
+#pragma unroll
+          for (int m = 0; m < PER; ++m) v[u][m] = rv.get(h, row, lane * PER + m);
+        }
+#pragma unroll
+        for (int u = 0; u < 32; ++u)
+          if (q + u < nbuf)
+#pragma unroll
+            for (int m = 0; m < PER; ++m) s[m] = __dadd_rn(s[m], (double)v[u][m]);
+      }
+      nbuf = 0;
+    };
+    for (int i0 = 0; i0 < N; i0 += 8 * 64) {
+      uint32_t av[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k * 64 + lane;
+        av[k] = i < N ? (uint32_t)ah[i] : 0xFFFFFFFFu;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const bool me = av[k] == (uint32_t)j;
+        const uint64_t mb = __ballot(me);
+        const int c = __popcll(mb);
+        if (c == 0) continue;
+        if (nbuf + c > 64) flush();
+        if (me) mem[wv][nbuf + __popcll(mb & lt)] = i0 + k * 64 + lane;
+        nbuf += c;
+        n += c;
+      }
+    }
+    flush();
+  } else {
+  n = __builtin_amdgcn_readfirstlane(offs[(int64_t)h * (Cp + 1) + j + 1] -
+                                     offs[(int64_t)h * (Cp + 1) + j]);
   const int c0 = __builtin_amdgcn_readfirstlane(cofs[(int64_t)h * (Cp + 1) + j]);
   const int nch = __builtin_amdgcn_readfirstlane(cofs[(int64_t)h * (Cp + 1) + j + 1]) - c0;
-  const bool head_exact = head_sums_exact(stats, stat_stride, h);
   const double *ph = part + ((int64_t)h * maxch + c0) * D + lane * PER;
   const uint32_t *pf = pflag + ((int64_t)h * maxch + c0) * D + lane * PER;
-  double s[PER];
   int emax[PER], lmin[PER];
 #pragma unroll
   for (int m = 0; m < PER; ++m) s[m] = 0.0, emax[m] = 0, lmin[m] = 0xFFFF;
@@ -1232,6 +1471,10 @@ __global__ __launch_bounds__(256) void k_finalize(
 #pragma unroll
           for (int m = 0; m < PER; ++m) s[m] = __dadd_rn(s[m], (double)v[u][m]);
     }
+  }
+  if (mode == 1 && head_exact)
+#pragma unroll
+    for (int m = 0; m < PER; ++m) isj[m] = to_units(s[m], lmj[m]);
   }
   float *cj = cent + ((int64_t)h * Cp + j) * D + lane * PER;
   float cv[PER];
@@ -1389,51 +1632,73 @@ bool launch_assign(const KmArgs &a, int bslot, hipStream_t s) {
 
 template <typename Tin, typename Tc, int D>
 bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int64_t rec_hstride,
-                   float *cache, int64_t cache_hstride, int log_slot, bool reduce_span,
-                   hipStream_t s) {
+                   float *cache, int64_t cache_hstride, int log_slot, int iter, hipStream_t s) {
+  // after the first iteration of a stage (with the incremental state), heads
+  // with exact sums move only the changed tokens (k_delta) and the others are
+  // summed by k_finalize from a scan of the assignments: no sort, no chunk sums
+  const bool inc = a.ws.isum != nullptr && iter >= 0;
+  const bool delta = inc && iter > 0;
+  const int mode = inc ? (iter == 0 ? 1 : 2) : 0;
+  const int par = iter > 0 ? iter & 1 : 0;
+  const int nb = (a.N + kSortChunk - 1) / kSortChunk;
+  const int maxch = max_chunks(a.N, a.Cp);
   {
-    const int nb = (a.N + kSortChunk - 1) / kSortChunk;
     TimerScope ts_("kmeans_sort", s);
     hipLaunchKernelGGL(k_hist, dim3(nb, a.H), dim3(256), 0, s, a.assign, a.assign_hstride, a.N,
-                       a.ws.hist, a.ws_stats, a.stat_stride, next_bslot, a.ws.counters, log_slot);
+                       a.ws.hist, a.ws_stats, a.stat_stride, next_bslot, a.ws.counters, log_slot,
+                       inc ? a.ws.prev : nullptr, par, delta ? 1 : 0, a.ws.sorted, a.ws.mcnt);
     QVG_CHECK_LAUNCH();
-    hipLaunchKernelGGL(k_scatter, dim3(nb, a.H), dim3(256), 0, s, a.assign, a.assign_hstride,
-                       a.N, a.Cp, a.ws.hist, a.ws.sorted, a.ws.offs, a.ws.cofs, a.ws.chunk_j,
-                       max_chunks(a.N, a.Cp));
-    QVG_CHECK_LAUNCH();
+    if (!delta) {
+      hipLaunchKernelGGL(k_scatter, dim3(nb, a.H), dim3(256), 0, s, a.assign, a.assign_hstride,
+                         a.N, a.Cp, a.ws.hist, a.ws.sorted, a.ws.offs, a.ws.cofs, a.ws.chunk_j,
+                         maxch);
+      QVG_CHECK_LAUNCH();
+    }
   }
   {
-    const int maxch = max_chunks(a.N, a.Cp);
     TimerScope ts_("kmeans_accumulate", s);
-    const dim3 gcs((maxch + 3) / 4, a.H);
+    if (delta) {
+      dispatch_nsub(a.nsub, [&]<int NS>() {
+        hipLaunchKernelGGL((k_delta<Tin, D, NS>), dim3(delta_grid(a.H, D)), dim3(kDeltaThreads),
+                           0, s, view_of<Tin>(a, D), a.H, a.Cp, a.assign, a.assign_hstride,
+                           a.ws.prev, par, a.ws.sorted, a.ws.mcnt, nb, a.ws.lminv, a.ws.isum,
+                           a.ws_stats, a.stat_stride);
+      });
+      QVG_CHECK_LAUNCH();
+    } else {
+      const dim3 gcs((maxch + 3) / 4, a.H);
 #define QVG_CS(NS)                                                                           \
   hipLaunchKernelGGL((k_chunk_sum<Tin, D, NS>), gcs, dim3(256), 0, s, view_of<Tin>(a, D), a.Cp, \
                      a.ws.sorted, a.ws.offs, a.ws.cofs, a.ws.chunk_j, maxch, a.ws.part,      \
                      a.ws.pflag, a.ws_stats, a.stat_stride)
-    switch (a.nsub) {
-      case 0: QVG_CS(0); break;
-      case 1: QVG_CS(1); break;
-      case 2: QVG_CS(2); break;
-      case 3: QVG_CS(3); break;
-      case 4: QVG_CS(4); break;
-      case 5: QVG_CS(5); break;
-      case 6: QVG_CS(6); break;
-      default: QVG_CS(7); break;
-    }
+      switch (a.nsub) {
+        case 0: QVG_CS(0); break;
+        case 1: QVG_CS(1); break;
+        case 2: QVG_CS(2); break;
+        case 3: QVG_CS(3); break;
+        case 4: QVG_CS(4); break;
+        case 5: QVG_CS(5); break;
+        case 6: QVG_CS(6); break;
+        default: QVG_CS(7); break;
+      }
 #undef QVG_CS
-    QVG_CHECK_LAUNCH();
-    if (reduce_span) {
-      hipLaunchKernelGGL((k_span_part<D>), dim3(kSpanParts, a.H), dim3(256), 0, s, a.ws.pflag,
-                         a.ws.cofs, a.Cp, maxch, a.ws.span);
       QVG_CHECK_LAUNCH();
-      hipLaunchKernelGGL((k_span_final<D>), dim3(a.H), dim3(D), 0, s, a.ws.span, a.N, a.ws_stats,
-                         a.stat_stride);
-      QVG_CHECK_LAUNCH();
+      if (iter == 0) {
+        hipLaunchKernelGGL((k_span_part<D>), dim3(kSpanParts, a.H), dim3(256), 0, s, a.ws.pflag,
+                           a.ws.cofs, a.Cp, maxch, a.ws.span);
+        QVG_CHECK_LAUNCH();
+        hipLaunchKernelGGL((k_span_final<D>), dim3(a.H), dim3(D), 0, s, a.ws.span, a.N,
+                           a.ws_stats, a.stat_stride, inc ? a.ws.lminv : nullptr);
+        QVG_CHECK_LAUNCH();
+      }
     }
     hipLaunchKernelGGL((k_finalize<Tin, Tc, D>), dim3((a.Cp + 3) / 4, a.H), dim3(256), 0, s,
-                       view_of<Tin>(a, D), a.ws.sorted, a.ws.pflag, a.C, a.Cp, a.ws.offs, a.ws.cofs, maxch, a.ws.part, a.ws.cent, a.ws_stats,
-                       a.ws_stats, a.stat_stride, next_bslot, tables ? a.ws.ctab : nullptr,
-                       a.ws.cinit, a.ws.cbnd, rec_c, rec_hstride, cache, cache_hstride);
+                       view_of<Tin>(a, D), a.ws.sorted, a.ws.pflag, a.C, a.Cp, a.ws.offs,
+                       a.ws.cofs, maxch, a.ws.part, a.ws.cent, a.ws_stats, a.ws_stats,
+                       a.stat_stride, next_bslot, tables ? a.ws.ctab : nullptr, a.ws.cinit,
+                       a.ws.cbnd, rec_c, rec_hstride, cache, cache_hstride,
+                       inc ? a.ws.isum : nullptr, inc ? a.ws.lminv : nullptr, a.ws.hist, nb,
+                       mode, a.assign, a.assign_hstride);
     QVG_CHECK_LAUNCH();
   }
   return true;
@@ -1443,9 +1708,9 @@ bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int6
   template bool launch_kmeans_stage_begin<Tin, D>(const KmArgs &, hipStream_t);               \
   template bool launch_assign<Tin, D>(const KmArgs &, int, hipStream_t);                      \
   template bool launch_update<Tin, float, D>(const KmArgs &, int, bool, float *, int64_t,     \
-                                             float *, int64_t, int, bool, hipStream_t);       \
+                                             float *, int64_t, int, int, hipStream_t);       \
   template bool launch_update<Tin, uint16_t, D>(const KmArgs &, int, bool, uint16_t *,        \
-                                                int64_t, float *, int64_t, int, bool,         \
+                                                int64_t, float *, int64_t, int, int,          \
                                                 hipStream_t);
 QVG_INST(float, 64)
 QVG_INST(float, 128)

@@ -223,6 +223,25 @@ def test_centroid_sums_that_can_round():
     _check(*_run_both(x, p, idx))
 
 
+def test_incremental_and_full_updates_in_one_call():
+    """Heads 0 and 2 hold plain bf16 video data (every centroid sum exact, so
+    from the second iteration on their sums move only the tokens whose
+    assignment changed); head 1 mixes ~2^15 with ~2^-40 values (full update
+    every iteration).  Six iterations, two stages, ragged N: the record and
+    the cache must equal the oracle's."""
+    rng = np.random.default_rng(17)
+    H, N, d, C = 3, 2777, 128, 32
+    x = synth.video_cache(5, 0, H, 2, 30, 52, 128, 1e2, torch.float64, n_tokens=N).numpy()
+    x[1, :, :16] *= 2.0 ** 15
+    tiny = rng.random((N, d)) < 0.3
+    x[1][tiny] = rng.standard_normal(int(tiny.sum())) * 2.0 ** -40
+    x = synth.round_to(x, torch.bfloat16)
+    p = qvg.params(C=C, T=2, iters=6, bits=2, group=64)
+    idx = synth.init_indices(901, H, p.T, N, p.C)
+    say("incremental and full updates", tuple(x.shape))
+    _check(*_run_both(x, p, idx))
+
+
 @pytest.mark.parametrize("H,N,C,T,seed", [(1, 40, 40, 1, 3), (2, 300, 16, 2, 11),
                                           (3, 4681, 256, 2, 2 ** 63 + 5), (1, 32760, 256, 1, 1)])
 def test_seeded_start_matches_oracle(H, N, C, T, seed):
