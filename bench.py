@@ -294,7 +294,9 @@ def run_selfforcing(args):
     # (bf16 input x: 2 B per element; stage t also reads t assignment bytes
     # per token; averages over the T stages where launches differ by stage)
     hbm_bytes = {
-        # one read of the stage residual's sources per iteration
+        # one read of the stage residual's sources per full update (the first
+        # iteration of a stage; later ones move only the changed tokens and
+        # are timed as kmeans_delta)
         "kmeans_accumulate": H * N * (2 * d + (p.T - 1) / 2),
         # x and every stage's assignment in; codes and scales out
         "group_quant_pack": H * N * (2 * d + p.T + d * p.bits / 8 + d / p.group),

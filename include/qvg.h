@@ -322,11 +322,14 @@ qvg_status qvg_candidate_counts(const void *ws, int64_t H, int64_t N, int64_t d,
 
 /* Per-kernel launch timing.  While enabled, every kernel launch of the
  * library is bracketed by two HIP events recorded on its launch stream (the
- * caller's stream).  Kernel names: "kmeans_assign", "kmeans_recheck",
- * "kmeans_fallback", "kmeans_sort", "kmeans_accumulate", "kmeans_init",
+ * caller's stream).  Kernel names: "kmeans_assign", "kmeans_resolve" (the
+ * exact re-checks and scans), "kmeans_sort" and "kmeans_accumulate" (the
+ * update of a stage's first iteration, which sorts and sums every member),
+ * "kmeans_delta" (the updates of the later iterations, which move only the
+ * tokens whose assignment changed where that is exact and cheaper), "kmeans_init",
  * "kmeans_prepare", "kmeans_tables", "absmax", "sas_subtract",
- * "group_quant_pack", "fused_dequant", "attention", "fill".  Host-side bookkeeping only;
- * results of the path are unchanged. */
+ * "group_quant_pack", "fused_dequant", "attention", "fill".  Host-side
+ * bookkeeping only; results of the path are unchanged. */
 void qvg_timing_enable(int on);
 /* Forget all recorded launches (waits for their events). */
 void qvg_timing_reset(void);

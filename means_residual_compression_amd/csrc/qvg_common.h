@@ -30,6 +30,7 @@ enum StatSlot : int {
   S_SPAN = 10,   // exactness of the stage's centroid sums over the whole head:
                  // bit 0 set once checked, bit 1 when some channel's span
                  // leaves a partial sum of up to N members able to round
+  S_INC = 11,    // 1 when this iteration's update of the head is incremental
   kStatWords = 16,
 };
 
@@ -63,6 +64,7 @@ struct Ws {
   uint32_t *lminv;    // [H][D] per-channel lowest-bit bound lmin of the stage residual
   uint8_t *prev;      // [2][H][N] assignments at the last two updates (iteration parity)
   uint32_t *mcnt;     // [H][ceil(N/kSortChunk)] moved tokens listed by each sort block
+  uint32_t *mtot;     // [2][H] moved tokens per head (iteration parity)
 };
 
 constexpr int kSpanParts = 32;  // chunk groups per head in the span reduction

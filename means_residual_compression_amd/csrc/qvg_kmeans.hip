@@ -29,10 +29,11 @@
 // When they show every sum of the stage exact (the usual case), the sums are
 // kept as integers in units of each channel's lowest bit, and every later
 // iteration of the stage only moves the tokens whose assignment changed from
-// their old cluster's sum to the new one (k_hist lists them, k_delta adds
+// their old cluster's sum to the new one (k_hist lists them, k_accum_delta adds
 // them): integer sums do not depend on the order, so they stay the sequential
-// fp64 sums.  Heads without that proof are summed in token order by
-// k_finalize from a scan of the assignments.
+// fp64 sums.  k_scatter decides per head and iteration: heads without that
+// proof, or with more than a quarter of their tokens moved, take the full
+// update.
 #include "qvg_common.h"
 #include "qvg_internal.h"
 
@@ -72,9 +73,13 @@ __device__ __forceinline__ float block_max(float m) {
 
 // A head whose stage spans are known to keep every cluster sum exact (S_SPAN
 // == 1): it skips the per-chunk span tracking, and after the first iteration
-// of the stage its sums are updated incrementally (k_delta).
+// of the stage its sums are updated incrementally (k_accum_delta).
 __device__ __forceinline__ bool head_sums_exact(const uint32_t *stats, int stat_stride, int h) {
   return (__builtin_amdgcn_readfirstlane(stats[(int64_t)h * stat_stride + S_SPAN]) & 3u) == 1u;
+}
+// This iteration updates the head incrementally (set by k_scatter).
+__device__ __forceinline__ bool head_incremental(const uint32_t *stats, int stat_stride, int h) {
+  return __builtin_amdgcn_readfirstlane(stats[(int64_t)h * stat_stride + S_INC]) == 1u;
 }
 
 template <typename Tin>
@@ -837,10 +842,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 // ranks taken from ballots, so token order is kept within every cluster.
 // k_hist also clears the next bound slot of the head and (first chunk of head
 // 0) logs and clears the candidate-list counters.  With prev set it copies the
-// assignments to prev[par ^ 1]; with `delta` set, a head whose stage sums are
-// exact also lists the tokens of this block whose assignment differs from
-// prev[par] (the previous update's) in its own segment moved[h][lo ..) (in no
-// particular order), and their number in mcnt[h][b].
+// assignments to prev[par ^ 1] and clears the next iteration's per-head total
+// mtot[par ^ 1][h]; with `delta` set, a head whose stage sums are exact also
+// lists the tokens of this block whose assignment differs from prev[par] (the
+// previous update's) in its own segment moved[h][lo ..) (in no particular
+// order), their number in mcnt[h][b], and adds it to mtot[par][h].
 __global__ __launch_bounds__(256) void k_hist(const uint8_t *__restrict__ assign,
                                               int64_t assign_hstride, int N,
                                               uint32_t *__restrict__ hist, uint32_t *stats,
@@ -848,7 +854,8 @@ __global__ __launch_bounds__(256) void k_hist(const uint8_t *__restrict__ assign
                                               uint32_t *counters, int log_slot,
                                               uint8_t *__restrict__ prev, int par, int delta,
                                               int32_t *__restrict__ moved,
-                                              uint32_t *__restrict__ mcnt) {
+                                              uint32_t *__restrict__ mcnt,
+                                              uint32_t *__restrict__ mtot) {
   __shared__ uint32_t cnt[kMaxC];
   __shared__ uint32_t nmv;
   const int h = blockIdx.y, b = blockIdx.x;
@@ -863,6 +870,7 @@ __global__ __launch_bounds__(256) void k_hist(const uint8_t *__restrict__ assign
     counters[threadIdx.x] = 0;
   }
   const bool track = prev && delta && head_sums_exact(stats, stat_stride, h);
+  if (prev && b == 0 && threadIdx.x == 0) mtot[(par ^ 1) * H + h] = 0u;
   __syncthreads();
   const uint8_t *a = assign + (int64_t)h * assign_hstride;
   const uint8_t *pr = prev ? prev + ((int64_t)par * H + h) * N : nullptr;
@@ -890,7 +898,10 @@ __global__ __launch_bounds__(256) void k_hist(const uint8_t *__restrict__ assign
   }
   __syncthreads();
   hist[((int64_t)h * nb + b) * kMaxC + threadIdx.x] = cnt[threadIdx.x];
-  if (track && threadIdx.x == 0) mcnt[(int64_t)h * nb + b] = nmv;
+  if (track && threadIdx.x == 0) {
+    mcnt[(int64_t)h * nb + b] = nmv;
+    if (nmv) atomicAdd(&mtot[par * H + h], nmv);
+  }
 }
 
 // Inclusive scan of one value per thread over a 256-thread workgroup: a
@@ -912,16 +923,29 @@ __device__ __forceinline__ uint32_t scan256_incl(uint32_t v, uint32_t *ws) {
   return v + add;
 }
 
+// With stats set, k_scatter first decides how this iteration updates the head
+// (written to S_INC by block 0): incrementally when `delta` is set, the
+// head's stage sums are exact and at most N/4 of its tokens moved (mtot[par]);
+// then only the full update sorts.  Past a quarter of the tokens, gathering
+// every moved row once per channel slice costs more than one pass over all.
 __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ assign,
                                                  int64_t assign_hstride, int N, int Cp,
                                                  const uint32_t *__restrict__ hist,
                                                  int32_t *__restrict__ sorted,
                                                  int32_t *__restrict__ offs,
                                                  int32_t *__restrict__ cofs,
-                                                 int32_t *__restrict__ chunk_j, int maxch) {
+                                                 int32_t *__restrict__ chunk_j, int maxch,
+                                                 uint32_t *stats, int stat_stride, int delta,
+                                                 const uint32_t *__restrict__ mtot, int par) {
   __shared__ uint32_t scan[4];
   __shared__ uint32_t wbase[4][kMaxC];
   const int h = blockIdx.y, b = blockIdx.x, nb = gridDim.x;
+  if (stats) {
+    const bool inc = delta && head_sums_exact(stats, stat_stride, h) &&
+                     __builtin_amdgcn_readfirstlane(mtot[par * gridDim.y + h]) <= (uint32_t)(N / 4);
+    if (b == 0 && threadIdx.x == 0) stats[(int64_t)h * stat_stride + S_INC] = inc ? 1u : 0u;
+    if (inc) return;
+  }
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const uint8_t *a = assign + (int64_t)h * assign_hstride;
   const int lo = b * kSortChunk, hi = min(N, lo + kSortChunk);
@@ -1054,13 +1078,11 @@ __device__ __forceinline__ void chunk_sum_body(const ResView<Tin> &rv, int Cp,
                                                const int32_t *__restrict__ cofs,
                                                const int32_t *__restrict__ chunk_j, int maxch,
                                                double *__restrict__ part,
-                                               uint32_t *__restrict__ pflag) {
+                                               uint32_t *__restrict__ pflag, int h, int g) {
   constexpr int LPR = D / 8;              // lanes per member row (8 channels each)
   constexpr int RPI = 64 / LPR;           // member rows per load instruction
   constexpr int MPL = kAccChunk / RPI;    // members per lane
   constexpr int MB = 4;                   // members per lane in flight
-  const int h = blockIdx.y;
-  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int total = __builtin_amdgcn_readfirstlane(cofs[(int64_t)h * (Cp + 1) + Cp]);
   if (g >= total) return;
@@ -1143,10 +1165,14 @@ __global__ __launch_bounds__(256) void k_chunk_sum(ResView<Tin> rv, int Cp,
                                                    uint32_t *__restrict__ pflag,
                                                    const uint32_t *__restrict__ stats,
                                                    int stat_stride) {
-  if (head_sums_exact(stats, stat_stride, blockIdx.y))
-    chunk_sum_body<Tin, D, NSUB, false>(rv, Cp, sorted, offs, cofs, chunk_j, maxch, part, pflag);
+  const int h = blockIdx.y, g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (head_incremental(stats, stat_stride, h)) return;  // updated from its moved tokens
+  if (head_sums_exact(stats, stat_stride, h))
+    chunk_sum_body<Tin, D, NSUB, false>(rv, Cp, sorted, offs, cofs, chunk_j, maxch, part, pflag,
+                                        h, g);
   else
-    chunk_sum_body<Tin, D, NSUB, true>(rv, Cp, sorted, offs, cofs, chunk_j, maxch, part, pflag);
+    chunk_sum_body<Tin, D, NSUB, true>(rv, Cp, sorted, offs, cofs, chunk_j, maxch, part, pflag,
+                                       h, g);
 }
 
 // Head-wide spans of a stage's residual, from the per-chunk spans of its first
@@ -1233,18 +1259,19 @@ constexpr int kDeltaThreads = 512;
 __host__ __device__ inline int delta_grid(int H, int D) { return 8 * ((H + 7) / 8) * (D / 8); }
 
 template <typename Tin, int D, int NSUB>
-__global__ __launch_bounds__(kDeltaThreads) void k_delta(
-    ResView<Tin> rv, int H, int Cp, const uint8_t *__restrict__ assign, int64_t assign_hstride,
-    const uint8_t *__restrict__ prev, int par, const int32_t *__restrict__ moved,
-    const uint32_t *__restrict__ mcnt, int nb, const uint32_t *__restrict__ lminv,
-    long long *__restrict__ isum, const uint32_t *__restrict__ stats, int stat_stride) {
+__device__ __forceinline__ void delta_body(
+    const ResView<Tin> &rv, int H, int Cp, const uint8_t *__restrict__ assign,
+    int64_t assign_hstride, const uint8_t *__restrict__ prev, int par,
+    const int32_t *__restrict__ moved, const uint32_t *__restrict__ mcnt, int nb,
+    const uint32_t *__restrict__ lminv, long long *__restrict__ isum,
+    const uint32_t *__restrict__ stats, int stat_stride, int id) {
   constexpr int U = NSUB <= 1 ? 4 : (NSUB <= 3 ? 2 : 1);
   constexpr int S = D / 8;                       // channel slices per head
   constexpr int QS = kMaxC * 8 / kDeltaThreads;  // isum words per thread
   __shared__ unsigned long long acc[kMaxC * kDeltaRow];
   __shared__ uint32_t pre[kDeltaThreads + 1];
   __shared__ uint32_t wsum[kDeltaThreads / 64];
-  const int xcd = blockIdx.x % 8, k = blockIdx.x / 8;
+  const int xcd = id % 8, k = id / 8;
   const int h = xcd + 8 * (k / S), k0 = (k % S) * 8;
   if (h >= H) return;
   const int N = rv.N;
@@ -1259,7 +1286,7 @@ __global__ __launch_bounds__(kDeltaThreads) void k_delta(
   uint32_t lm[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) lm[e] = lminv[(int64_t)h * D + k0 + e];
-  if (!head_sums_exact(stats, stat_stride, h)) return;
+  if (!head_incremental(stats, stat_stride, h)) return;
   for (int q = threadIdx.x; q < Cp * kDeltaRow; q += kDeltaThreads) acc[q] = 0ull;
   const uint8_t *ah = assign + (int64_t)h * assign_hstride;
   const uint8_t *ph = prev + ((int64_t)par * H + h) * N;
@@ -1329,6 +1356,48 @@ __global__ __launch_bounds__(kDeltaThreads) void k_delta(
   }
 }
 
+// The incremental update on its own (stages with more than three earlier
+// stages, whose chunk sums keep 256-thread workgroups).
+template <typename Tin, int D, int NSUB>
+__global__ __launch_bounds__(kDeltaThreads) void k_delta(
+    ResView<Tin> rv, int H, int Cp, const uint8_t *__restrict__ assign, int64_t assign_hstride,
+    const uint8_t *__restrict__ prev, int par, const int32_t *__restrict__ moved,
+    const uint32_t *__restrict__ mcnt, int nb, const uint32_t *__restrict__ lminv,
+    long long *__restrict__ isum, const uint32_t *__restrict__ stats, int stat_stride) {
+  delta_body<Tin, D, NSUB>(rv, H, Cp, assign, assign_hstride, prev, par, moved, mcnt, nb, lminv,
+                           isum, stats, stat_stride, blockIdx.x);
+}
+
+// The accumulate launch of the iterations after a stage's first (stages with
+// at most three earlier stages): workgroups 0 .. H*gx-1 sum the member chunks
+// of heads updated in full (8 waves, one chunk each, as k_chunk_sum),
+// workgroups from doff (a multiple of 8, so that the XCD of a delta workgroup
+// follows its id) update the others from their moved tokens.
+template <typename Tin, int D, int NSUB>
+__global__ __launch_bounds__(kDeltaThreads) void k_accum_delta(
+    ResView<Tin> rv, int H, int Cp, const int32_t *__restrict__ sorted,
+    const int32_t *__restrict__ offs, const int32_t *__restrict__ cofs,
+    const int32_t *__restrict__ chunk_j, int maxch, double *__restrict__ part,
+    uint32_t *__restrict__ pflag, int gx, int doff, const uint8_t *__restrict__ assign,
+    int64_t assign_hstride, const uint8_t *__restrict__ prev, int par,
+    const uint32_t *__restrict__ mcnt, int nb, const uint32_t *__restrict__ lminv,
+    long long *__restrict__ isum, const uint32_t *__restrict__ stats, int stat_stride) {
+  const int bid = blockIdx.x;
+  if (bid < gx * H) {
+    const int h = bid / gx, g = (bid % gx) * (kDeltaThreads / 64) + (int)(threadIdx.x >> 6);
+    if (head_incremental(stats, stat_stride, h)) return;
+    if (head_sums_exact(stats, stat_stride, h))
+      chunk_sum_body<Tin, D, NSUB, false>(rv, Cp, sorted, offs, cofs, chunk_j, maxch, part,
+                                          pflag, h, g);
+    else
+      chunk_sum_body<Tin, D, NSUB, true>(rv, Cp, sorted, offs, cofs, chunk_j, maxch, part,
+                                         pflag, h, g);
+  } else if (bid >= doff) {
+    delta_body<Tin, D, NSUB>(rv, H, Cp, assign, assign_hstride, prev, par, sorted, mcnt, nb,
+                             lminv, isum, stats, stat_stride, bid - doff);
+  }
+}
+
 template <typename Tin, typename Tc, int D>
 __global__ __launch_bounds__(256) void k_finalize(
     ResView<Tin> rv, const int32_t *__restrict__ sorted, const uint32_t *__restrict__ pflag,
@@ -1338,10 +1407,8 @@ __global__ __launch_bounds__(256) void k_finalize(
     float *__restrict__ cinit, float4 *__restrict__ cbnd, Tc *__restrict__ rec_c,
     int64_t rec_hstride, float *__restrict__ cache, int64_t cache_hstride,
     long long *__restrict__ isum, const uint32_t *__restrict__ lminv,
-    const uint32_t *__restrict__ hist, int nb, int mode, const uint8_t *__restrict__ assign,
-    int64_t assign_hstride) {
+    const uint32_t *__restrict__ hist, int nb) {
   constexpr int PER = D / 64;
-  __shared__ int32_t mem[4][64];  // member ids per wave (mode 2, inexact heads)
   const int h = blockIdx.y;
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -1351,13 +1418,15 @@ __global__ __launch_bounds__(256) void k_finalize(
     return;
   }
   const bool head_exact = head_sums_exact(stats, stat_stride, h);
-  // mode 1 (first iteration of a stage): keep the exact sums as integers;
-  // mode 2 (later iterations): exact heads read them, as updated by k_delta
+  // with the incremental state (isum set): a head updated incrementally in
+  // this iteration (k_accum_delta) reads its integer sums; an exact head updated in
+  // full stores them for the iterations after
+  const bool from_isum = isum && head_incremental(stats, stat_stride, h);
   long long *isj = isum ? isum + ((int64_t)h * Cp + j) * D + lane * PER : nullptr;
   const uint32_t *lmj = lminv ? lminv + (int64_t)h * D + lane * PER : nullptr;
   double s[PER];
   int n;
-  if (mode == 2 && head_exact) {
+  if (from_isum) {
     // member count: the column of this iteration's per-chunk histograms
     uint32_t c = 0u;
     for (int b = lane; b < nb; b += 64) c += hist[((int64_t)h * nb + b) * kMaxC + j];
@@ -1365,56 +1434,6 @@ __global__ __launch_bounds__(256) void k_finalize(
     n = (int)__builtin_amdgcn_readfirstlane(c);
 #pragma unroll
     for (int m = 0; m < PER; ++m) s[m] = from_units(isj[m], lmj[m]);
-  } else if (mode == 2) {
-    // a head whose sums are not exact, after the first iteration (no sort
-    // ran): the members are found in token order by scanning the
-    // assignments and added one by one (the plain sequential sum; members
-    // are buffered 64 at a time so that 32 rows are loaded together)
-    const uint8_t *ah = assign + (int64_t)h * assign_hstride;
-    const int wv = threadIdx.x >> 6, N = rv.N;
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-    for (int m = 0; m < PER; ++m) s[m] = 0.0;
-    n = 0;
-    int nbuf = 0;  // wave-uniform
-    auto flush = [&]() {
-      for (int q = 0; q < nbuf; q += 32) {
-        const int32_t myid = mem[wv][min(q + (lane & 31), nbuf - 1)];
-        float v[32][PER];
-#pragma unroll
-        for (int u = 0; u < 32; ++u) {
-          const int64_t row = __builtin_amdgcn_readlane(myid, u);
-#pragma unroll
-          for (int m = 0; m < PER; ++m) v[u][m] = rv.get(h, row, lane * PER + m);
-        }
-#pragma unroll
-        for (int u = 0; u < 32; ++u)
-          if (q + u < nbuf)
-#pragma unroll
-            for (int m = 0; m < PER; ++m) s[m] = __dadd_rn(s[m], (double)v[u][m]);
-      }
-      nbuf = 0;
-    };
-    for (int i0 = 0; i0 < N; i0 += 8 * 64) {
-      uint32_t av[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int i = i0 + k * 64 + lane;
-        av[k] = i < N ? (uint32_t)ah[i] : 0xFFFFFFFFu;
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const bool me = av[k] == (uint32_t)j;
-        const uint64_t mb = __ballot(me);
-        const int c = __popcll(mb);
-        if (c == 0) continue;
-        if (nbuf + c > 64) flush();
-        if (me) mem[wv][nbuf + __popcll(mb & lt)] = i0 + k * 64 + lane;
-        nbuf += c;
-        n += c;
-      }
-    }
-    flush();
   } else {
   n = __builtin_amdgcn_readfirstlane(offs[(int64_t)h * (Cp + 1) + j + 1] -
                                      offs[(int64_t)h * (Cp + 1) + j]);
@@ -1472,7 +1491,7 @@ __global__ __launch_bounds__(256) void k_finalize(
           for (int m = 0; m < PER; ++m) s[m] = __dadd_rn(s[m], (double)v[u][m]);
     }
   }
-  if (mode == 1 && head_exact)
+  if (isum && head_exact)
 #pragma unroll
     for (int m = 0; m < PER; ++m) isj[m] = to_units(s[m], lmj[m]);
   }
@@ -1633,36 +1652,40 @@ bool launch_assign(const KmArgs &a, int bslot, hipStream_t s) {
 template <typename Tin, typename Tc, int D>
 bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int64_t rec_hstride,
                    float *cache, int64_t cache_hstride, int log_slot, int iter, hipStream_t s) {
-  // after the first iteration of a stage (with the incremental state), heads
-  // with exact sums move only the changed tokens (k_delta) and the others are
-  // summed by k_finalize from a scan of the assignments: no sort, no chunk sums
+  // after the first iteration of a stage (with the incremental state), each
+  // head is updated either from its changed tokens (k_accum_delta) or in full (sort
+  // and chunk sums), as k_scatter decides from its exactness and moved count
   const bool inc = a.ws.isum != nullptr && iter >= 0;
   const bool delta = inc && iter > 0;
-  const int mode = inc ? (iter == 0 ? 1 : 2) : 0;
   const int par = iter > 0 ? iter & 1 : 0;
   const int nb = (a.N + kSortChunk - 1) / kSortChunk;
   const int maxch = max_chunks(a.N, a.Cp);
+  // the iterations after a stage's first are timed as one unit, kmeans_delta
+  // (their heads may take either update)
   {
-    TimerScope ts_("kmeans_sort", s);
+    TimerScope ts_(delta ? "kmeans_delta" : "kmeans_sort", s);
     hipLaunchKernelGGL(k_hist, dim3(nb, a.H), dim3(256), 0, s, a.assign, a.assign_hstride, a.N,
                        a.ws.hist, a.ws_stats, a.stat_stride, next_bslot, a.ws.counters, log_slot,
-                       inc ? a.ws.prev : nullptr, par, delta ? 1 : 0, a.ws.sorted, a.ws.mcnt);
+                       inc ? a.ws.prev : nullptr, par, delta ? 1 : 0, a.ws.sorted, a.ws.mcnt,
+                       a.ws.mtot);
     QVG_CHECK_LAUNCH();
-    if (!delta) {
-      hipLaunchKernelGGL(k_scatter, dim3(nb, a.H), dim3(256), 0, s, a.assign, a.assign_hstride,
-                         a.N, a.Cp, a.ws.hist, a.ws.sorted, a.ws.offs, a.ws.cofs, a.ws.chunk_j,
-                         maxch);
-      QVG_CHECK_LAUNCH();
-    }
+    hipLaunchKernelGGL(k_scatter, dim3(nb, a.H), dim3(256), 0, s, a.assign, a.assign_hstride,
+                       a.N, a.Cp, a.ws.hist, a.ws.sorted, a.ws.offs, a.ws.cofs, a.ws.chunk_j,
+                       maxch, a.ws_stats, a.stat_stride, delta ? 1 : 0, a.ws.mtot, par);
+    QVG_CHECK_LAUNCH();
   }
   {
-    TimerScope ts_("kmeans_accumulate", s);
-    if (delta) {
+    TimerScope ts_(delta ? "kmeans_delta" : "kmeans_accumulate", s);
+    if (delta && a.nsub <= 3) {
+      const int gx = (maxch + kDeltaThreads / 64 - 1) / (kDeltaThreads / 64);
+      const int doff = (gx * a.H + 7) / 8 * 8;
       dispatch_nsub(a.nsub, [&]<int NS>() {
-        hipLaunchKernelGGL((k_delta<Tin, D, NS>), dim3(delta_grid(a.H, D)), dim3(kDeltaThreads),
-                           0, s, view_of<Tin>(a, D), a.H, a.Cp, a.assign, a.assign_hstride,
-                           a.ws.prev, par, a.ws.sorted, a.ws.mcnt, nb, a.ws.lminv, a.ws.isum,
-                           a.ws_stats, a.stat_stride);
+        if constexpr (NS <= 3)
+          hipLaunchKernelGGL((k_accum_delta<Tin, D, NS>), dim3(doff + delta_grid(a.H, D)),
+                             dim3(kDeltaThreads), 0, s, view_of<Tin>(a, D), a.H, a.Cp,
+                             a.ws.sorted, a.ws.offs, a.ws.cofs, a.ws.chunk_j, maxch, a.ws.part,
+                             a.ws.pflag, gx, doff, a.assign, a.assign_hstride, a.ws.prev, par,
+                             a.ws.mcnt, nb, a.ws.lminv, a.ws.isum, a.ws_stats, a.stat_stride);
       });
       QVG_CHECK_LAUNCH();
     } else {
@@ -1691,14 +1714,22 @@ bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int6
                            a.ws_stats, a.stat_stride, inc ? a.ws.lminv : nullptr);
         QVG_CHECK_LAUNCH();
       }
+      if (delta) {
+        dispatch_nsub(a.nsub, [&]<int NS>() {
+          hipLaunchKernelGGL((k_delta<Tin, D, NS>), dim3(delta_grid(a.H, D)),
+                             dim3(kDeltaThreads), 0, s, view_of<Tin>(a, D), a.H, a.Cp, a.assign,
+                             a.assign_hstride, a.ws.prev, par, a.ws.sorted, a.ws.mcnt, nb,
+                             a.ws.lminv, a.ws.isum, a.ws_stats, a.stat_stride);
+        });
+        QVG_CHECK_LAUNCH();
+      }
     }
     hipLaunchKernelGGL((k_finalize<Tin, Tc, D>), dim3((a.Cp + 3) / 4, a.H), dim3(256), 0, s,
                        view_of<Tin>(a, D), a.ws.sorted, a.ws.pflag, a.C, a.Cp, a.ws.offs,
                        a.ws.cofs, maxch, a.ws.part, a.ws.cent, a.ws_stats, a.ws_stats,
                        a.stat_stride, next_bslot, tables ? a.ws.ctab : nullptr, a.ws.cinit,
                        a.ws.cbnd, rec_c, rec_hstride, cache, cache_hstride,
-                       inc ? a.ws.isum : nullptr, inc ? a.ws.lminv : nullptr, a.ws.hist, nb,
-                       mode, a.assign, a.assign_hstride);
+                       inc ? a.ws.isum : nullptr, inc ? a.ws.lminv : nullptr, a.ws.hist, nb);
     QVG_CHECK_LAUNCH();
   }
   return true;

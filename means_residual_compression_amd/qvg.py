@@ -426,7 +426,7 @@ def group_quant_pack(r: torch.Tensor, bits: int, group: int):
 
 # ------------------------------------------------------------ diagnostics
 KERNELS = ["kmeans_assign", "kmeans_resolve", "kmeans_sort",
-           "kmeans_accumulate", "kmeans_init", "kmeans_prepare", "kmeans_tables", "absmax",
+           "kmeans_accumulate", "kmeans_delta", "kmeans_init", "kmeans_prepare", "kmeans_tables", "absmax",
            "sas_subtract", "group_quant_pack", "fused_dequant", "fill"]
 
 

@@ -242,6 +242,19 @@ def test_incremental_and_full_updates_in_one_call():
     _check(*_run_both(x, p, idx))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_incremental_updates_of_deep_stages(dtype):
+    """Eight stages of four iterations: stages 5..8 (four or more earlier
+    stages) take the incremental update as a launch of its own, stages 2..4
+    inside the chunk-sum launch; both must give the oracle's record."""
+    H, N, C = 2, 3001, 16
+    x = synth.video_cache(6, 1, H, 2, 30, 52, 128, 1e2, dtype, n_tokens=N)
+    p = qvg.params(C=C, T=8, iters=4, bits=2, group=64)
+    idx = synth.init_indices(902, H, p.T, N, p.C)
+    say("incremental updates of deep stages", tuple(x.shape), dtype)
+    _check(*_run_both(x, p, idx))
+
+
 @pytest.mark.parametrize("H,N,C,T,seed", [(1, 40, 40, 1, 3), (2, 300, 16, 2, 11),
                                           (3, 4681, 256, 2, 2 ** 63 + 5), (1, 32760, 256, 1, 1)])
 def test_seeded_start_matches_oracle(H, N, C, T, seed):
