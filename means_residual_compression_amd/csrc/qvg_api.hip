@@ -39,7 +39,7 @@ size_t up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 // Workspace layout shared by the size query and the carve-up.
 struct Layout {
   size_t rt, tb, cent, ctab, cinit, cbnd, stats, recheck, fallback, counters, sorted, offs, hist,
-      cofs, chunk_j, part, pflag, stage_re, stage_fb, span, idx, isum, lminv, prev, mcnt, mtot;
+      cofs, chunk_j, part, pflag, stage_re, stage_fb, span, idx, isum, lminv, prev, mcnt;
   size_t total;
   bool incremental;
 };
@@ -80,7 +80,6 @@ Layout make_layout(int64_t H, int64_t N, int64_t d, int64_t C, int64_t T, bool n
   L.lminv = take(incremental ? (size_t)(H * d * 4) : 0);
   L.prev = take(incremental ? (size_t)(2 * H * N) : 0);
   L.mcnt = take(incremental ? (size_t)(H * ((N + kSortChunk - 1) / kSortChunk) * 4) : 0);
-  L.mtot = take(incremental ? (size_t)(2 * H * 4) : 0);
   L.total = o;
   return L;
 }
@@ -114,7 +113,6 @@ Ws carve(void *ws, const Layout &L) {
   w.lminv = inc ? (uint32_t *)(b + L.lminv) : nullptr;
   w.prev = inc ? (uint8_t *)(b + L.prev) : nullptr;
   w.mcnt = inc ? (uint32_t *)(b + L.mcnt) : nullptr;
-  w.mtot = inc ? (uint32_t *)(b + L.mtot) : nullptr;
   return w;
 }
 

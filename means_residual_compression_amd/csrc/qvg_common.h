@@ -64,7 +64,6 @@ struct Ws {
   uint32_t *lminv;    // [H][D] per-channel lowest-bit bound lmin of the stage residual
   uint8_t *prev;      // [2][H][N] assignments at the last two updates (iteration parity)
   uint32_t *mcnt;     // [H][ceil(N/kSortChunk)] moved tokens listed by each sort block
-  uint32_t *mtot;     // [2][H] moved tokens per head (iteration parity)
 };
 
 constexpr int kSpanParts = 32;  // chunk groups per head in the span reduction

@@ -82,6 +82,23 @@ __device__ __forceinline__ bool head_incremental(const uint32_t *stats, int stat
   return __builtin_amdgcn_readfirstlane(stats[(int64_t)h * stat_stride + S_INC]) == 1u;
 }
 
+// Sum over a workgroup of up to 1024 threads, returned to every thread.
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v) {
+  __shared__ uint32_t part[16];
+  __shared__ uint32_t total;
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) part[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += part[w];
+    total = t;
+  }
+  __syncthreads();
+  return total;
+}
+
 template <typename Tin>
 __device__ __forceinline__ float head_scale(const uint32_t *st) {
   return ldexpf(1.0f, -scale_exp(fmaxf(stat_f(st, S_MAXR), stat_f(st, S_MAXC))));
@@ -842,11 +859,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 // ranks taken from ballots, so token order is kept within every cluster.
 // k_hist also clears the next bound slot of the head and (first chunk of head
 // 0) logs and clears the candidate-list counters.  With prev set it copies the
-// assignments to prev[par ^ 1] and clears the next iteration's per-head total
-// mtot[par ^ 1][h]; with `delta` set, a head whose stage sums are exact also
-// lists the tokens of this block whose assignment differs from prev[par] (the
-// previous update's) in its own segment moved[h][lo ..) (in no particular
-// order), their number in mcnt[h][b], and adds it to mtot[par][h].
+// assignments to prev[par ^ 1]; with `delta` set, a head whose stage sums are
+// exact also lists the tokens of this block whose assignment differs from
+// prev[par] (the previous update's) in its own segment moved[h][lo ..) (in no
+// particular order), and their number in mcnt[h][b].
 __global__ __launch_bounds__(256) void k_hist(const uint8_t *__restrict__ assign,
                                               int64_t assign_hstride, int N,
                                               uint32_t *__restrict__ hist, uint32_t *stats,
@@ -854,8 +870,7 @@ __global__ __launch_bounds__(256) void k_hist(const uint8_t *__restrict__ assign
                                               uint32_t *counters, int log_slot,
                                               uint8_t *__restrict__ prev, int par, int delta,
                                               int32_t *__restrict__ moved,
-                                              uint32_t *__restrict__ mcnt,
-                                              uint32_t *__restrict__ mtot) {
+                                              uint32_t *__restrict__ mcnt) {
   __shared__ uint32_t cnt[kMaxC];
   __shared__ uint32_t nmv;
   const int h = blockIdx.y, b = blockIdx.x;
@@ -870,7 +885,6 @@ __global__ __launch_bounds__(256) void k_hist(const uint8_t *__restrict__ assign
     counters[threadIdx.x] = 0;
   }
   const bool track = prev && delta && head_sums_exact(stats, stat_stride, h);
-  if (prev && b == 0 && threadIdx.x == 0) mtot[(par ^ 1) * H + h] = 0u;
   __syncthreads();
   const uint8_t *a = assign + (int64_t)h * assign_hstride;
   const uint8_t *pr = prev ? prev + ((int64_t)par * H + h) * N : nullptr;
@@ -898,10 +912,7 @@ __global__ __launch_bounds__(256) void k_hist(const uint8_t *__restrict__ assign
   }
   __syncthreads();
   hist[((int64_t)h * nb + b) * kMaxC + threadIdx.x] = cnt[threadIdx.x];
-  if (track && threadIdx.x == 0) {
-    mcnt[(int64_t)h * nb + b] = nmv;
-    if (nmv) atomicAdd(&mtot[par * H + h], nmv);
-  }
+  if (track && threadIdx.x == 0) mcnt[(int64_t)h * nb + b] = nmv;
 }
 
 // Inclusive scan of one value per thread over a 256-thread workgroup: a
@@ -925,9 +936,10 @@ __device__ __forceinline__ uint32_t scan256_incl(uint32_t v, uint32_t *ws) {
 
 // With stats set, k_scatter first decides how this iteration updates the head
 // (written to S_INC by block 0): incrementally when `delta` is set, the
-// head's stage sums are exact and at most N/4 of its tokens moved (mtot[par]);
-// then only the full update sorts.  Past a quarter of the tokens, gathering
-// every moved row once per channel slice costs more than one pass over all.
+// head's stage sums are exact and at most N/4 of its tokens moved (the sum of
+// the blocks' counts mcnt[h][..]); then only the full update sorts.  Past a
+// quarter of the tokens, gathering every moved row once per channel slice
+// costs more than one pass over all.
 __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ assign,
                                                  int64_t assign_hstride, int N, int Cp,
                                                  const uint32_t *__restrict__ hist,
@@ -936,13 +948,17 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ass
                                                  int32_t *__restrict__ cofs,
                                                  int32_t *__restrict__ chunk_j, int maxch,
                                                  uint32_t *stats, int stat_stride, int delta,
-                                                 const uint32_t *__restrict__ mtot, int par) {
+                                                 const uint32_t *__restrict__ mcnt) {
   __shared__ uint32_t scan[4];
   __shared__ uint32_t wbase[4][kMaxC];
   const int h = blockIdx.y, b = blockIdx.x, nb = gridDim.x;
   if (stats) {
-    const bool inc = delta && head_sums_exact(stats, stat_stride, h) &&
-                     __builtin_amdgcn_readfirstlane(mtot[par * gridDim.y + h]) <= (uint32_t)(N / 4);
+    bool inc = false;
+    if (delta && head_sums_exact(stats, stat_stride, h)) {  // uniform
+      uint32_t m = 0;
+      for (int q = threadIdx.x; q < nb; q += 256) m += mcnt[(int64_t)h * nb + q];
+      inc = block_sum_u32(m) <= (uint32_t)(N / 4);
+    }
     if (b == 0 && threadIdx.x == 0) stats[(int64_t)h * stat_stride + S_INC] = inc ? 1u : 0u;
     if (inc) return;
   }
@@ -1666,12 +1682,11 @@ bool launch_update(const KmArgs &a, int next_bslot, bool tables, Tc *rec_c, int6
     TimerScope ts_(delta ? "kmeans_delta" : "kmeans_sort", s);
     hipLaunchKernelGGL(k_hist, dim3(nb, a.H), dim3(256), 0, s, a.assign, a.assign_hstride, a.N,
                        a.ws.hist, a.ws_stats, a.stat_stride, next_bslot, a.ws.counters, log_slot,
-                       inc ? a.ws.prev : nullptr, par, delta ? 1 : 0, a.ws.sorted, a.ws.mcnt,
-                       a.ws.mtot);
+                       inc ? a.ws.prev : nullptr, par, delta ? 1 : 0, a.ws.sorted, a.ws.mcnt);
     QVG_CHECK_LAUNCH();
     hipLaunchKernelGGL(k_scatter, dim3(nb, a.H), dim3(256), 0, s, a.assign, a.assign_hstride,
                        a.N, a.Cp, a.ws.hist, a.ws.sorted, a.ws.offs, a.ws.cofs, a.ws.chunk_j,
-                       maxch, a.ws_stats, a.stat_stride, delta ? 1 : 0, a.ws.mtot, par);
+                       maxch, a.ws_stats, a.stat_stride, delta ? 1 : 0, a.ws.mcnt);
     QVG_CHECK_LAUNCH();
   }
   {
