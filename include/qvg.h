@@ -170,7 +170,7 @@ qvg_status qvg_compress_stream(const void *chunk, qvg_dtype dtype, int64_t H, in
  * that device current.  Nothing is allocated: sizes whose workspace
  * (qvg_workspace_size) exceeds the array return QVG_ERR_WORKSPACE before
  * anything is enqueued; 24 head-tensors of 4680 tokens, d = 128, C = 256
- * need 51 MiB.  Every call on one GPU shares that GPU's array: calls that
+ * need 57 MiB.  Every call on one GPU shares that GPU's array: calls that
  * overlap on one GPU (different streams, or host threads without ordering)
  * race and must be serialised by the caller.  The array keeps the last
  * call's contents; the call clears what must start at zero itself.  For
