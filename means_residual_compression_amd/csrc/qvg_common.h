@@ -31,6 +31,9 @@ enum StatSlot : int {
                  // bit 0 set once checked, bit 1 when some channel's span
                  // leaves a partial sum of up to N members able to round
   S_INC = 11,    // 1 when this iteration's update of the head is incremental
+  S_SPANW = 12,  // the stage's widest channel span, max over channels of emax - lmin
+  S_ISUM = 13,   // 1 while the head's integer sums are exact (no cluster of its last
+                 // full update had to be summed again in token order)
   kStatWords = 16,
 };
 

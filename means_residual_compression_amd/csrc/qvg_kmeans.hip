@@ -81,6 +81,26 @@ __device__ __forceinline__ bool head_sums_exact(const uint32_t *stats, int stat_
 __device__ __forceinline__ bool head_incremental(const uint32_t *stats, int stat_stride, int h) {
   return __builtin_amdgcn_readfirstlane(stats[(int64_t)h * stat_stride + S_INC]) == 1u;
 }
+__device__ __forceinline__ int ceil_log2(uint32_t n) {
+  return n > 1 ? 32 - __builtin_clz(n - 1) : 0;
+}
+// The head's cluster sums fit int64 in units of each channel's lowest bit for
+// any set of up to N members (|v| < 2^(span + 24) units each): sums of them
+// are exact in any order.
+__device__ __forceinline__ bool head_int_sums(const uint32_t *stats, int stat_stride, int h,
+                                              int N) {
+  const uint32_t *st = stats + (int64_t)h * stat_stride;
+  const uint32_t chk = __builtin_amdgcn_readfirstlane(st[S_SPAN]);
+  const int w = (int)__builtin_amdgcn_readfirstlane(st[S_SPANW]);
+  return (chk & 1u) && w + 24 + ceil_log2((uint32_t)N) <= 62;
+}
+// A head that may be updated incrementally in this iteration: integer sums
+// possible and exact after its last full update.
+__device__ __forceinline__ bool head_inc_candidate(const uint32_t *stats, int stat_stride, int h,
+                                                   int N) {
+  return head_int_sums(stats, stat_stride, h, N) &&
+         __builtin_amdgcn_readfirstlane(stats[(int64_t)h * stat_stride + S_ISUM]) == 1u;
+}
 
 // Sum over a workgroup of up to 1024 threads, returned to every thread.
 __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v) {
@@ -97,6 +117,23 @@ __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v) {
   }
   __syncthreads();
   return total;
+}
+
+// Max over a workgroup of up to 1024 threads, returned to every thread.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
+  __shared__ uint32_t part[16];
+  __shared__ uint32_t best;
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) part[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) m = max(m, part[w]);
+    best = m;
+  }
+  __syncthreads();
+  return best;
 }
 
 template <typename Tin>
@@ -859,10 +896,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 // ranks taken from ballots, so token order is kept within every cluster.
 // k_hist also clears the next bound slot of the head and (first chunk of head
 // 0) logs and clears the candidate-list counters.  With prev set it copies the
-// assignments to prev[par ^ 1]; with `delta` set, a head whose stage sums are
-// exact also lists the tokens of this block whose assignment differs from
-// prev[par] (the previous update's) in its own segment moved[h][lo ..) (in no
-// particular order), and their number in mcnt[h][b].
+// assignments to prev[par ^ 1]; with `delta` set, a head that may be updated
+// incrementally (head_inc_candidate) also lists the tokens of this block whose
+// assignment differs from prev[par] (the previous update's) in its own segment
+// moved[h][lo ..) (in no particular order), and their number in mcnt[h][b].
 __global__ __launch_bounds__(256) void k_hist(const uint8_t *__restrict__ assign,
                                               int64_t assign_hstride, int N,
                                               uint32_t *__restrict__ hist, uint32_t *stats,
@@ -884,7 +921,7 @@ __global__ __launch_bounds__(256) void k_hist(const uint8_t *__restrict__ assign
       counters[4 + 2 * log_slot + threadIdx.x] = counters[threadIdx.x];
     counters[threadIdx.x] = 0;
   }
-  const bool track = prev && delta && head_sums_exact(stats, stat_stride, h);
+  const bool track = prev && delta && head_inc_candidate(stats, stat_stride, h, N);
   __syncthreads();
   const uint8_t *a = assign + (int64_t)h * assign_hstride;
   const uint8_t *pr = prev ? prev + ((int64_t)par * H + h) * N : nullptr;
@@ -934,10 +971,12 @@ __device__ __forceinline__ uint32_t scan256_incl(uint32_t v, uint32_t *ws) {
   return v + add;
 }
 
-// With stats set, k_scatter first decides how this iteration updates the head
-// (written to S_INC by block 0): incrementally when `delta` is set, the
-// head's stage sums are exact and at most N/4 of its tokens moved (the sum of
-// the blocks' counts mcnt[h][..]); then only the full update sorts.  Past a
+// With stats set, k_scatter decides how this iteration updates the head
+// (written to S_INC by block 0): incrementally when `delta` is set, the head is
+// a candidate (head_inc_candidate), every cluster's fp64 sum is exact (its
+// member count n satisfies span + ceil(log2 n) <= 29, so the integer sum is
+// the sequential one) and at most N/4 of its tokens moved (the sum of the
+// blocks' counts mcnt[h][..]); then only the full update sorts.  Past a
 // quarter of the tokens, gathering every moved row once per channel slice
 // costs more than one pass over all.
 __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ assign,
@@ -952,17 +991,24 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ass
   __shared__ uint32_t scan[4];
   __shared__ uint32_t wbase[4][kMaxC];
   const int h = blockIdx.y, b = blockIdx.x, nb = gridDim.x;
-  if (stats) {
-    bool inc = false;
-    if (delta && head_sums_exact(stats, stat_stride, h)) {  // uniform
-      uint32_t m = 0;
-      for (int q = threadIdx.x; q < nb; q += 256) m += mcnt[(int64_t)h * nb + q];
-      inc = block_sum_u32(m) <= (uint32_t)(N / 4);
-    }
-    if (b == 0 && threadIdx.x == 0) stats[(int64_t)h * stat_stride + S_INC] = inc ? 1u : 0u;
-    if (inc) return;
-  }
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // heads that are no candidate, or whose sums are exact for any member set
+  // (then every cluster's are), are decided before the counts are read
+  bool decided = true;
+  if (stats) {
+    const bool cand = delta && head_inc_candidate(stats, stat_stride, h, N);  // uniform
+    decided = !cand || head_sums_exact(stats, stat_stride, h);
+    if (decided) {
+      bool inc = false;
+      if (cand) {
+        uint32_t m = 0;
+        for (int q = t; q < nb; q += 256) m += mcnt[(int64_t)h * nb + q];
+        inc = block_sum_u32(m) <= (uint32_t)(N / 4);
+      }
+      if (b == 0 && t == 0) stats[(int64_t)h * stat_stride + S_INC] = inc ? 1u : 0u;
+      if (inc) return;
+    }
+  }
   const uint8_t *a = assign + (int64_t)h * assign_hstride;
   const int lo = b * kSortChunk, hi = min(N, lo + kSortChunk);
   // this wave's quarter of the chunk: token wlo + lane + 64k is jk[k] (loaded
@@ -1004,6 +1050,16 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t *__restrict__ ass
     const uint32_t c = hh[(int64_t)bb * kMaxC];
     tot += c;
     pre += bb < b ? c : 0u;
+  }
+  if (!decided) {  // a candidate whose sums are exact cluster by cluster
+    uint32_t m = 0;
+    for (int q = t; q < nb; q += 256) m += mcnt[(int64_t)h * nb + q];
+    const uint32_t moved = block_sum_u32(m);
+    const uint32_t most = block_max_u32(tot);  // largest cluster of this iteration
+    const int w = (int)__builtin_amdgcn_readfirstlane(stats[(int64_t)h * stat_stride + S_SPANW]);
+    const bool inc = moved <= (uint32_t)(N / 4) && w + ceil_log2(most) <= 29;
+    if (b == 0 && t == 0) stats[(int64_t)h * stat_stride + S_INC] = inc ? 1u : 0u;
+    if (inc) return;
   }
   // exclusive scan of the totals over the 256 byte values; assignment bytes
   // >= C (corrupt input only) get slots after the clusters
@@ -1179,10 +1235,12 @@ __global__ __launch_bounds__(256) void k_chunk_sum(ResView<Tin> rv, int Cp,
                                                    const int32_t *__restrict__ chunk_j,
                                                    int maxch, double *__restrict__ part,
                                                    uint32_t *__restrict__ pflag,
-                                                   const uint32_t *__restrict__ stats,
-                                                   int stat_stride) {
+                                                   uint32_t *stats, int stat_stride) {
   const int h = blockIdx.y, g = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (head_incremental(stats, stat_stride, h)) return;  // updated from its moved tokens
+  // summed in full: its integer sums are exact unless k_finalize has to sum a
+  // cluster again in token order (it then clears the flag)
+  if (blockIdx.x == 0 && threadIdx.x == 0) stats[(int64_t)h * stat_stride + S_ISUM] = 1u;
   if (head_sums_exact(stats, stat_stride, h))
     chunk_sum_body<Tin, D, NSUB, false>(rv, Cp, sorted, offs, cofs, chunk_j, maxch, part, pflag,
                                         h, g);
@@ -1240,8 +1298,16 @@ __global__ __launch_bounds__(D) void k_span_final(const uint32_t *__restrict__ s
   const int lg = N > 1 ? 32 - __builtin_clz((uint32_t)(N - 1)) : 0;
   const int risky = (int)emax - (int)lmin + lg > 29;
   if (lminv) lminv[(int64_t)h * D + threadIdx.x] = lmin;
+  // the widest span over the channels that hold a nonzero value
+  __shared__ int wmax;
+  if (threadIdx.x == 0) wmax = 0;
   const int any = __syncthreads_or(risky);
-  if (threadIdx.x == 0) stats[(int64_t)h * stat_stride + S_SPAN] = 1u | (any ? 2u : 0u);
+  if (lmin != 0xFFFFu) atomicMax(&wmax, (int)emax - (int)lmin);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    stats[(int64_t)h * stat_stride + S_SPAN] = 1u | (any ? 2u : 0u);
+    stats[(int64_t)h * stat_stride + S_SPANW] = (uint32_t)max(wmax, 0);
+  }
 }
 
 // ------------------------------------------------------ incremental update
@@ -1397,11 +1463,12 @@ __global__ __launch_bounds__(kDeltaThreads) void k_accum_delta(
     uint32_t *__restrict__ pflag, int gx, int doff, const uint8_t *__restrict__ assign,
     int64_t assign_hstride, const uint8_t *__restrict__ prev, int par,
     const uint32_t *__restrict__ mcnt, int nb, const uint32_t *__restrict__ lminv,
-    long long *__restrict__ isum, const uint32_t *__restrict__ stats, int stat_stride) {
+    long long *__restrict__ isum, uint32_t *stats, int stat_stride) {
   const int bid = blockIdx.x;
   if (bid < gx * H) {
     const int h = bid / gx, g = (bid % gx) * (kDeltaThreads / 64) + (int)(threadIdx.x >> 6);
     if (head_incremental(stats, stat_stride, h)) return;
+    if (bid % gx == 0 && threadIdx.x == 0) stats[(int64_t)h * stat_stride + S_ISUM] = 1u;
     if (head_sums_exact(stats, stat_stride, h))
       chunk_sum_body<Tin, D, NSUB, false>(rv, Cp, sorted, offs, cofs, chunk_j, maxch, part,
                                           pflag, h, g);
@@ -1435,8 +1502,10 @@ __global__ __launch_bounds__(256) void k_finalize(
   }
   const bool head_exact = head_sums_exact(stats, stat_stride, h);
   // with the incremental state (isum set): a head updated incrementally in
-  // this iteration (k_accum_delta) reads its integer sums; an exact head updated in
-  // full stores them for the iterations after
+  // this iteration (k_accum_delta) reads its integer sums; a head updated in
+  // full whose sums fit the integers stores them for the iterations after, or
+  // marks them unusable when a cluster had to be summed again in token order
+  // (that sum may have rounded)
   const bool from_isum = isum && head_incremental(stats, stat_stride, h);
   long long *isj = isum ? isum + ((int64_t)h * Cp + j) * D + lane * PER : nullptr;
   const uint32_t *lmj = lminv ? lminv + (int64_t)h * D + lane * PER : nullptr;
@@ -1507,9 +1576,14 @@ __global__ __launch_bounds__(256) void k_finalize(
           for (int m = 0; m < PER; ++m) s[m] = __dadd_rn(s[m], (double)v[u][m]);
     }
   }
-  if (isum && head_exact)
+  if (isum && head_int_sums(stats, stat_stride, h, rv.N)) {
+    if (__ballot(risky)) {
+      if (lane == 0) stats_w[(int64_t)h * stat_stride + S_ISUM] = 0u;
+    } else {
 #pragma unroll
-    for (int m = 0; m < PER; ++m) isj[m] = to_units(s[m], lmj[m]);
+      for (int m = 0; m < PER; ++m) isj[m] = to_units(s[m], lmj[m]);
+    }
+  }
   }
   float *cj = cent + ((int64_t)h * Cp + j) * D + lane * PER;
   float cv[PER];

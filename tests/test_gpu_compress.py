@@ -255,6 +255,21 @@ def test_incremental_updates_of_deep_stages(dtype):
     _check(*_run_both(x, p, idx))
 
 
+def test_incremental_updates_with_per_cluster_exactness():
+    """fp32 values in [1, 2): every channel spans 23 bits, so a sum over all N
+    tokens could round (23 + ceil(log2 N) > 29) and the head-wide proof fails;
+    the integer sums still fit (23 + 24 + 10 <= 62), and iterations whose
+    largest cluster has at most 64 members (23 + 6 <= 29) are updated from the
+    moved tokens, the others in full.  The record must equal the oracle's."""
+    rng = np.random.default_rng(23)
+    H, N, d, C = 2, 1000, 64, 32
+    x = torch.from_numpy(rng.uniform(1.0, 2.0, (H, N, d)).astype(np.float32))
+    p = qvg.params(C=C, T=2, iters=6, bits=2, group=32)
+    idx = synth.init_indices(903, H, p.T, N, p.C)
+    say("incremental updates with per-cluster exactness", tuple(x.shape))
+    _check(*_run_both(x, p, idx))
+
+
 @pytest.mark.parametrize("H,N,C,T,seed", [(1, 40, 40, 1, 3), (2, 300, 16, 2, 11),
                                           (3, 4681, 256, 2, 2 ** 63 + 5), (1, 32760, 256, 1, 1)])
 def test_seeded_start_matches_oracle(H, N, C, T, seed):
