@@ -26,13 +26,14 @@
 // sum equals the sequential fp64 sum of a plain loop.
 //
 // The first iteration of a stage also reduces those spans over each head.
-// When they show every sum of the stage exact (the usual case), the sums are
-// kept as integers in units of each channel's lowest bit, and every later
-// iteration of the stage only moves the tokens whose assignment changed from
+// When they show that the cluster sums fit int64 in units of each channel's
+// lowest bit (the usual case), the sums are kept as such integers, and later
+// iterations of the stage only move the tokens whose assignment changed from
 // their old cluster's sum to the new one (k_hist lists them, k_accum_delta adds
-// them): integer sums do not depend on the order, so they stay the sequential
-// fp64 sums.  k_scatter decides per head and iteration: heads without that
-// proof, or with more than a quarter of their tokens moved, take the full
+// them): integer sums do not depend on the order, and when every cluster's
+// member count keeps its fp64 partial sums exact they are the sequential fp64
+// sums.  k_scatter decides per head and iteration; heads that fail those
+// conditions, or with more than a quarter of their tokens moved, take the full
 // update.
 #include "qvg_common.h"
 #include "qvg_internal.h"
@@ -72,8 +73,7 @@ __device__ __forceinline__ float block_max(float m) {
 }
 
 // A head whose stage spans are known to keep every cluster sum exact (S_SPAN
-// == 1): it skips the per-chunk span tracking, and after the first iteration
-// of the stage its sums are updated incrementally (k_accum_delta).
+// == 1): it skips the per-chunk span tracking.
 __device__ __forceinline__ bool head_sums_exact(const uint32_t *stats, int stat_stride, int h) {
   return (__builtin_amdgcn_readfirstlane(stats[(int64_t)h * stat_stride + S_SPAN]) & 3u) == 1u;
 }
