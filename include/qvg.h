@@ -276,7 +276,8 @@ qvg_status qvg_group_quant_pack(const void *r, qvg_dtype dtype, int64_t H, int64
  *   - Output within a run: a fused multiply-add chain over 64*d/256 tokens
  *     per tile, rescaled at most once per tile. The 256/d thread parts are
  *     then added, and the runs merged with one more chain.
- *   - Weight sums (Nq <= 4 and Nq*T*C <= 4096, values' T and C): the value
+ *   - Weight sums (one pass: Nq <= 4 and Nq*T*C <= 4096, values' T and C;
+ *     two passes, below: min(Nq, 4)*T*C <= 4096): the value
  *     term sum_n p_n C(t)[pi_t(n)] is taken as sum_c C(t)[c] * (the weights
  *     of the tokens assigned to c). Each weight sum is an add chain over a
  *     run's tokens (rescaled at most once per tile), merged over runs with a
@@ -284,8 +285,10 @@ qvg_status qvg_group_quant_pack(const void *r, qvg_dtype dtype, int64_t H, int64
  *     T*C*d/2048 rows, added in order.
  *   - Otherwise the values are rebuilt in fp32 (the dequant's fused
  *     multiply-add and adds).
- *   With bf16 centroids, keys of 1 to 4 stages and weight sums, the call
- *   takes two passes instead (same runs for the values): the scores first,
+ *   With bf16 centroids, keys of 1 to 4 stages, weight sums, N*2d < 2^32
+ *   and H <= 256, the call takes two passes instead (same runs for the
+ *   values; queries in groups of 4, each group's weight sums held at once):
+ *   the scores first,
  *   each d/8 (d/4 for d = 64) fused multiply-add chains of 16 terms added
  *   pairwise, times scale; then, with m the run's largest score, weights
  *   e^(s - m) (never rescaled): per run a fused multiply-add chain of

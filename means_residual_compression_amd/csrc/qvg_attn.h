@@ -15,8 +15,10 @@ constexpr int kAttnBN = 64;
 constexpr int kAttnTargetGroups = 2048;
 constexpr int kAttnMaxSplit = 1024;
 constexpr int kAttnMaxQueries = 16;
-// Value path by per-centroid weight sums: up to this many queries, and
-// while Nq * T * C weight sums (fp32) fit this many entries of LDS.
+// Value path by per-centroid weight sums: up to this many queries per
+// workgroup, and while their T * C weight sums each fit this many entries of
+// LDS in all.  The one-pass path handles all queries in one workgroup; the
+// two-pass path takes up to kAttnMaxQueries queries in groups of this many.
 constexpr int kAttnSumQueries = 4;
 constexpr int kAttnSumEntries = 4096;
 struct AttnRec {
@@ -28,18 +30,21 @@ struct AttnSplit {
   int nsplit, tiles_per_split;
 };
 AttnSplit attn_split(int H, int64_t N);
-// Whether the values go through per-centroid weight sums (see qvg_attn.hip).
-bool attn_uses_sums(int Nq, int T, int C);
+// Whether the values go through per-centroid weight sums on the one-pass
+// path (all Nq queries in one workgroup) and on the two-pass path (groups of
+// kAttnSumQueries) (see qvg_attn.hip).
+bool attn_sums_one_pass(int Nq, int T, int C);
+bool attn_sums_two_pass(int Nq, int T, int C);
 // Whether the call takes the two-pass path (k_attn_scores, k_attn_values):
 // bf16 centroids, keys of 1 to 4 stages, weight sums, N * 2d < 2^32 and at
 // most 256 heads.
 bool attn_two_pass(int H, int Nq, int kT, int vT, int vC, bool c_bf16, int64_t N, int D);
 // Floats of one (run, query) record in the scratch: m, l, o[D], then the
-// T*C weight sums when attn_uses_sums.
-int attn_part_floats(int Nq, int D, int T, int C);
-// fp32 scratch floats of one call: the run records, then (with weight sums)
-// the contraction parts [H][Nq][8][D] and the scores [H][Nq][N] of the
-// two-pass path.
+// T*C weight sums when the path uses them.
+int attn_part_floats(int Nq, int D, int T, int C, bool two_pass);
+// fp32 scratch floats of one call (the larger of the two paths' layouts):
+// the run records, then (with weight sums) the contraction parts
+// [H][Nq][8][D] and the scores [H][Nq][N] of the two-pass path.
 size_t attn_scratch_floats(int H, int64_t N, int Nq, int D, int T, int C);
 // q [H][Nq][D] fp32, part [H][nsplit][Nq][attn_part_floats] fp32 scratch
 // (attn_scratch_floats in all),

@@ -831,7 +831,8 @@ __global__ __launch_bounds__(256) void k_attn_scores(const float *__restrict__ q
 template <int D, int NQ, int BITS>
 __global__ __launch_bounds__(256) void k_attn_values(const float *__restrict__ scores, int Nq,
                                                      int N, int H, AttnRec vr, int nsplit, int tps,
-                                                     int pf, float *__restrict__ part) {
+                                                     int pf, float *__restrict__ part, int q0,
+                                                     int NqT) {
   constexpr int CG = D / 8, SL = 256 / CG, TPT = kAttnBN / SL;  // groups, slots, tokens
   __shared__ float4 lut2[BITS == 2 ? 256 : 1];
   __shared__ float4 lut4v[BITS == 4 ? 128 : 1];  // [256] float2, 16-byte aligned
@@ -848,7 +849,8 @@ __global__ __launch_bounds__(256) void k_attn_values(const float *__restrict__ s
   const int T = vr.T, C = vr.C, TC = T * C, vg = __builtin_ctz(vr.G);
   init_level_lut<BITS>(lut2, lut4);
   for (int x = t; x < Nq * TC; x += 256) ws[x] = 0ull;
-  const float *sh = scores + (int64_t)h * Nq * N;
+  // this launch's queries q0 .. q0+Nq-1 of the call's NqT
+  const float *sh = scores + ((int64_t)h * NqT + q0) * N;
   const int ntiles = (N + kAttnBN - 1) / kAttnBN;
   const int tb = sp * tps, te = min(tb + tps, ntiles);
   float o[NQ][8], l[NQ];
@@ -975,7 +977,7 @@ __global__ __launch_bounds__(256) void k_attn_values(const float *__restrict__ s
       if (lane == 0) lred[jq] = v;
     }
   __syncthreads();
-  float *rec = part + ((int64_t)h * nsplit + sp) * Nq * pf;
+  float *rec = part + (((int64_t)h * nsplit + sp) * NqT + q0) * pf;
   for (int x = t; x < Nq * D; x += 256) {
     const int jq = x / D, k = x - jq * D;
     const float r = ((wout[(0 * NQ + jq) * D + k] + wout[(1 * NQ + jq) * D + k]) +
@@ -1150,7 +1152,7 @@ bool launch_attn_t(const float *q, int H, int Nq, int N, const AttnRec &kr, cons
                    float scale, const float *rcos, const float *rsin, float *part, float *out,
                    hipStream_t s) {
   const AttnSplit sp = attn_split(H, N);
-  const int pf = attn_part_floats(Nq, D, vr.T, vr.C);
+  const int pf = attn_part_floats(Nq, D, vr.T, vr.C, false);
   const int TC = vr.T * vr.C;
   static const bool lds_ok =
       hipFuncSetAttribute((const void *)k_attn_split<Tc, D, NQ, SUMS>,
@@ -1202,7 +1204,7 @@ bool launch_attn_2p(const float *q, int H, int Nq, int N, const AttnRec &kr, con
                     float scale, const float *rcos, const float *rsin, float *part, float *out,
                     hipStream_t s) {
   const AttnSplit sp = attn_split(H, N);
-  const int pf = attn_part_floats(Nq, D, vr.T, vr.C);
+  const int pf = attn_part_floats(Nq, D, vr.T, vr.C, true);
   const int TC = vr.T * vr.C;
   float *cpart = part + (size_t)H * sp.nsplit * Nq * pf;
   float *scores = cpart + (size_t)H * Nq * kContractParts * D;
@@ -1214,19 +1216,31 @@ bool launch_attn_2p(const float *q, int H, int Nq, int N, const AttnRec &kr, con
     case 4: ok = launch_scores_t<D, NQ, 4>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
   }
   if (!ok) return false;
-  const size_t lds = (size_t)Nq * TC * sizeof(unsigned long long) + (size_t)4 * NQ * D * sizeof(float);
-  if (NQ == 1 && vr.bits == 2)
-    hipLaunchKernelGGL((k_attn_values1<D, 2>), dim3(H * sp.nsplit), dim3(256), lds, s, scores, N,
-                       H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
-  else if (NQ == 1)
-    hipLaunchKernelGGL((k_attn_values1<D, 4>), dim3(H * sp.nsplit), dim3(256), lds, s, scores, N,
-                       H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
-  else if (vr.bits == 2)
-    hipLaunchKernelGGL((k_attn_values<D, NQ, 2>), dim3(H * sp.nsplit), dim3(256), lds, s, scores,
-                       Nq, N, H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
-  else
-    hipLaunchKernelGGL((k_attn_values<D, NQ, 4>), dim3(H * sp.nsplit), dim3(256), lds, s, scores,
-                       Nq, N, H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
+  if (NQ == 1) {
+    const size_t lds = (size_t)TC * sizeof(unsigned long long) + (size_t)4 * D * sizeof(float);
+    if (vr.bits == 2)
+      hipLaunchKernelGGL((k_attn_values1<D, 2>), dim3(H * sp.nsplit), dim3(256), lds, s, scores,
+                         N, H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
+    else
+      hipLaunchKernelGGL((k_attn_values1<D, 4>), dim3(H * sp.nsplit), dim3(256), lds, s, scores,
+                         N, H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
+  } else {
+    // the values in groups of up to kAttnSumQueries queries, whose weight
+    // sums fit in LDS; the scores pass served all of them at once
+    for (int q0 = 0; q0 < Nq; q0 += kAttnSumQueries) {
+      const int nq = std::min(kAttnSumQueries, Nq - q0);
+      const size_t lds = (size_t)nq * TC * sizeof(unsigned long long) +
+                         (size_t)4 * kAttnSumQueries * D * sizeof(float);
+      if (vr.bits == 2)
+        hipLaunchKernelGGL((k_attn_values<D, kAttnSumQueries, 2>), dim3(H * sp.nsplit), dim3(256),
+                           lds, s, scores, nq, N, H, vr, sp.nsplit, sp.tiles_per_split, pf, part,
+                           q0, Nq);
+      else
+        hipLaunchKernelGGL((k_attn_values<D, kAttnSumQueries, 4>), dim3(H * sp.nsplit), dim3(256),
+                           lds, s, scores, nq, N, H, vr, sp.nsplit, sp.tiles_per_split, pf, part,
+                           q0, Nq);
+    }
+  }
   if (hipGetLastError() != hipSuccess) return false;
   if (TC > 0) {
     hipLaunchKernelGGL((k_attn_contract<uint16_t>), dim3(Nq, H, kContractParts), dim3(256), 0, s,
@@ -1247,9 +1261,10 @@ bool launch_attn_d(const float *q, int H, int Nq, int N, const AttnRec &kr, cons
                    hipStream_t s) {
   if (attn_two_pass(H, Nq, kr.T, vr.T, vr.C, sizeof(Tc) == 2, N, D)) {
     if (Nq == 1) return launch_attn_2p<D, 1>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
-    return launch_attn_2p<D, 4>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
+    if (Nq <= 4) return launch_attn_2p<D, 4>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
+    return launch_attn_2p<D, 16>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
   }
-  if (attn_uses_sums(Nq, vr.T, vr.C)) {
+  if (attn_sums_one_pass(Nq, vr.T, vr.C)) {
     if (Nq == 1)
       return launch_attn_t<Tc, D, 1, true>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
     return launch_attn_t<Tc, D, 4, true>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
@@ -1271,27 +1286,35 @@ AttnSplit attn_split(int H, int64_t N) {
   return AttnSplit{(ntiles + tps - 1) / tps, tps};
 }
 
-bool attn_uses_sums(int Nq, int T, int C) {
+bool attn_sums_one_pass(int Nq, int T, int C) {
   return Nq <= kAttnSumQueries && (int64_t)Nq * T * C <= kAttnSumEntries;
+}
+
+bool attn_sums_two_pass(int Nq, int T, int C) {
+  return Nq <= kAttnMaxQueries &&
+         (int64_t)std::min(Nq, kAttnSumQueries) * T * C <= kAttnSumEntries;
 }
 
 bool attn_two_pass(int H, int Nq, int kT, int vT, int vC, bool c_bf16, int64_t N, int D) {
   // k_attn_scores addresses the rotary rows with 32-bit byte offsets and
   // keeps a head group's queries in LDS
-  return c_bf16 && kT >= 1 && kT <= 4 && attn_uses_sums(Nq, vT, vC) &&
+  return c_bf16 && kT >= 1 && kT <= 4 && attn_sums_two_pass(Nq, vT, vC) &&
          N * 2 * D < ((int64_t)1 << 32) && H <= 256;
 }
 
-int attn_part_floats(int Nq, int D, int T, int C) {
-  return D + 2 + (attn_uses_sums(Nq, T, C) ? T * C : 0);
+int attn_part_floats(int Nq, int D, int T, int C, bool two_pass) {
+  const bool sums = two_pass ? attn_sums_two_pass(Nq, T, C) : attn_sums_one_pass(Nq, T, C);
+  return D + 2 + (sums ? T * C : 0);
 }
 
 size_t attn_scratch_floats(int H, int64_t N, int Nq, int D, int T, int C) {
+  // sized for the larger of the two paths' layouts: the two-pass path uses
+  // weight sums whenever the one-pass path does, and for more queries
   const AttnSplit sp = attn_split(H, N);
-  const size_t runs = (size_t)H * sp.nsplit * Nq * attn_part_floats(Nq, D, T, C);
-  const size_t contract = attn_uses_sums(Nq, T, C) ? (size_t)H * Nq * kContractParts * D : 0;
-  // scores of the two-pass path (which needs weight sums)
-  const size_t two = attn_uses_sums(Nq, T, C) ? (size_t)H * Nq * N : 0;
+  const bool sums = attn_sums_two_pass(Nq, T, C);
+  const size_t runs = (size_t)H * sp.nsplit * Nq * attn_part_floats(Nq, D, T, C, true);
+  const size_t contract = sums ? (size_t)H * Nq * kContractParts * D : 0;
+  const size_t two = sums ? (size_t)H * Nq * N : 0;  // the two-pass path's scores
   return runs + contract + two;
 }
 

@@ -220,10 +220,11 @@ def test_attention_workspace_follows_documented_layout(H, N, d, Nq, T, C):
     o[d] and, with weight sums, the T*C sums per run and query) plus, with
     weight sums, the eight contraction parts per (head, query) and the
     two-pass scores (one per head, query and token), rounded up to 256
-    bytes."""
+    bytes.  Weight sums: up to 16 queries, taken 4 at a time, while 4 (or
+    Nq, if fewer) times T*C sums fit 4096 entries."""
     p = qvg.params(C, T, 1, 2, 64)
     tps, ns = _runs(H, N)
-    sums = Nq <= 4 and Nq * T * C <= 4096
+    sums = Nq <= 16 and min(Nq, 4) * T * C <= 4096
     floats = H * ns * Nq * (d + 2 + (T * C if sums else 0)) + (H * Nq * (8 * d + N) if sums else 0)
     want = -(-floats * 4 // 256) * 256
     assert qvg.lib().qvg_attention_workspace_size(H, Nq, N, d, ct.byref(p)) == want

@@ -76,8 +76,19 @@ def _bound(q, K, Vabs, scale, H, N, d, vT, vC, sums):
     return (2 * ratio[:, None] + 2.1 * _gamma(m) + rebuild + fixed + U) * vmax[None, :]
 
 
-def _sums(Nq, vpar):
+def _two_pass(H, N, d, Nq, kT, vpar, cdt):
+    """Whether the call takes the documented two-pass path."""
     T, C = vpar[0], vpar[1]
+    return (cdt == torch.bfloat16 and 1 <= kT <= 4 and min(Nq, 4) * T * max(C, 1) <= 4096
+            and N * 2 * d < 2 ** 32 and H <= 256)
+
+
+def _sums(H, N, d, Nq, kT, vpar, cdt):
+    """Whether the values go through weight sums: on the two-pass path for up
+    to 16 queries in groups of 4, else for up to 4 queries at once."""
+    T, C = vpar[0], vpar[1]
+    if _two_pass(H, N, d, Nq, kT, vpar, cdt):
+        return True
     return Nq <= 4 and Nq * T * max(C, 1) <= 4096
 
 
@@ -117,11 +128,10 @@ def _aimed_queries(q, K, targets, scale, gap=24.0):
     return q
 
 
-def _check(got, q, kb, vh, vp, scale, rope, H, N, heads):
+def _check(got, q, kb, vh, vp, scale, rope, H, N, heads, sums):
     """got [H, Nq, d] from the kernel; kb bf16 keys and vh the value record
-    (host) of the checked heads."""
+    (host) of the checked heads; sums: whether the call used weight sums."""
     d = q.shape[2]
-    sums = _sums(q.shape[1], (vp.T, vp.C))
     V = _oracle_values(vh, vp, heads)
     Vabs = _oracle_values(vh, vp, heads, magnitude=True)
     worst = 0.0
@@ -153,13 +163,22 @@ CASES = [
     (2, 4099, 64, 1, (3, 128, 4, 16), (2, 64, 4, 32), torch.bfloat16, True),
     (3, 5000, 64, 1, (4, 256, 2, 8), (4, 256, 2, 8), torch.bfloat16, True),
     (2, 3001, 128, 3, (2, 64, 4, 32), (3, 128, 4, 16), torch.bfloat16, True),
+    # two-pass with more than 4 queries (values in groups of 4): a ragged 7
+    # (groups of 4 and 3) with INT4 values, 16 at d=64, and 5 (a group of 1)
+    (3, 4500, 128, 7, (2, 128, 2, 32), (2, 256, 4, 32), torch.bfloat16, True),
+    (2, 6000, 64, 16, (1, 64, 4, 16), (4, 64, 2, 8), torch.bfloat16, False),
+    (4, 700, 128, 5, (3, 256, 2, 64), (1, 256, 2, 64), torch.bfloat16, True),
+    # 16 queries whose weight sums do not fit (T*C = 2048): rebuilt values
+    (2, 2500, 128, 16, (2, 64, 2, 64), (8, 256, 2, 64), torch.bfloat16, False),
 ]
 
 
 @pytest.mark.parametrize("H,N,d,Nq,kpar,vpar,cdt,rope", CASES)
 def test_attention_matches_oracle(H, N, d, Nq, kpar, vpar, cdt, rope):
+    sums = _sums(H, N, d, Nq, kpar[0], vpar, cdt)
     say("attention", H, N, d, Nq, kpar, vpar, cdt, "rope" if rope else "",
-        "weight sums" if _sums(Nq, vpar) else "rebuilt values")
+        "two passes" if _two_pass(H, N, d, Nq, kpar[0], vpar, cdt) else "one pass",
+        "weight sums" if sums else "rebuilt values")
     (kh, kd, kp), (vh, vd, vp) = _make(17 + N % 97, H, N, d, kpar, vpar, cdt)
     heads = list(range(H))
     kb = _oracle_keys(kh, kp, heads)
@@ -181,7 +200,7 @@ def test_attention_matches_oracle(H, N, d, Nq, kpar, vpar, cdt, rope):
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     assert np.array_equal(got, again.cpu().numpy()), "two calls differ"
-    worst = _check(got, q, kb, vh, vp, scale, rope_np, H, N, heads)
+    worst = _check(got, q, kb, vh, vp, scale, rope_np, H, N, heads, sums)
     say("  worst error / bound", worst)
 
 
@@ -215,7 +234,8 @@ def test_attention_decode_record_full_size(decode_records, Nq):
                         rope=(tabs[0].to(DEV), tabs[1].to(DEV)))
     torch.cuda.synchronize()
     say("  checking heads", heads)
-    worst = _check(out.cpu().numpy(), q, kb, vh, vp, scale, rope_np, H, N, heads)
+    sums = _sums(H, N, d, Nq, kp.T, (vp.T, vp.C), torch.bfloat16)
+    worst = _check(out.cpu().numpy(), q, kb, vh, vp, scale, rope_np, H, N, heads, sums)
     say("  worst error / bound", worst)
 
 
@@ -226,7 +246,7 @@ def test_attention_workspace_and_rejects():
     for H, N, d, Nq in ((40, 262144, 128, 16), (40, 262144, 128, 1), (3, 20000, 128, 1),
                         (1, 1, 64, 2)):
         tps, ns = _runs(H, N)
-        extra = 4 * 256 if _sums(Nq, (4, 256)) else 0
+        extra = 4 * 256 if min(Nq, 4) * 4 * 256 <= 4096 else 0
         contract = H * Nq * 8 * d if extra else 0
         assert qvg.attention_workspace_size(H, Nq, N, d, vp4) >= (
             H * ns * Nq * (d + 2 + extra) + contract) * 4
