@@ -290,7 +290,12 @@ qvg_status qvg_group_quant_pack(const void *r, qvg_dtype dtype, int64_t H, int64
  *   values; queries in groups of 4, each group's weight sums held at once):
  *   the scores first,
  *   each d/8 (d/4 for d = 64) fused multiply-add chains of 16 terms added
- *   pairwise, times scale; then, with m the run's largest score, weights
+ *   pairwise, times scale (one query); for 2 to 16 queries each query is
+ *   split into two bf16 parts, hi = bf16(q) and lo = bf16(q - hi) (so
+ *   |q - hi - lo| <= 2^-16 |q|), and the 2d exact products of the parts
+ *   with the bf16 key are summed in fp32 on the matrix cores (the hi parts
+ *   of 32-channel blocks in order, then the lo parts; the order within a
+ *   block is the hardware's), times scale; then, with m the run's largest score, weights
  *   e^(s - m) (never rescaled): per run a fused multiply-add chain of
  *   (weight * s_hat) * level over 4 (d = 128) or 2 (d = 64) tokens per
  *   tile (one query: over 1 token per pass of 64 or 128), the chains of a

@@ -691,6 +691,29 @@ __host__ __device__ inline int score_group(int H, int NQ, int D) {
   return (H + 1) / 2 < cap ? (H + 1) / 2 : cap;
 }
 
+// The rebuilt key channels x (a) and their rotate-half partners y (b) as
+// bf16 operand words: each rounded to bf16, then (with rotation) x c - y s
+// and y c + x s from fp32 products and an fp32 difference/sum, rounded to
+// bf16 in the packing.
+__device__ __forceinline__ void rotate_pack(float a[8], float b[8], bool rot, const float c[8],
+                                            const float sn[8], uint32_t wa[4], uint32_t wb[4]) {
+  if (rot) {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = round_bf16(a[e]), y = round_bf16(b[e]);
+      const float xc = x * c[e], ys = y * sn[e], yc = y * c[e], xs = x * sn[e];
+      a[e] = xc - ys;
+      b[e] = yc + xs;
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    wa[m] = pack_bf16_rne(a[2 * m], a[2 * m + 1]);
+    wb[m] = pack_bf16_rne(b[2 * m], b[2 * m + 1]);
+  }
+}
+
 // Scores: workgroup -> (group of heads, run of tiles), consecutive items on
 // one XCD.  A lane keeps its token's rotary rows in registers while it
 // scores the token for every head of the group.
@@ -823,6 +846,168 @@ __global__ __launch_bounds__(256) void k_attn_scores(const float *__restrict__ q
       if (part == 0 && valid && jq < Nq) scores[((int64_t)h * Nq + jq) * N + ti] = v;
     }
     cur = nx;
+    b0 = nb0;
+    hh = nhh;
+  }
+}
+
+// Scores of 2 to 16 queries on the matrix cores (v_mfma_f32_16x16x32_bf16):
+// the same workgroups, runs and head groups as k_attn_scores, but a wave
+// step covers 16 tokens with four lanes per token.  Lane l holds token
+// l % 16 and, in each 32-channel block kb, channels kb*32 + 8*(l/16) .. +7,
+// which is the B-operand layout of the instruction; a rotate-half partner
+// (k + d/2) lies in block kb + d/64 of the same lane.  The lane rebuilds its
+// d/4 key channels with k_attn_scores' arithmetic, rotates them and packs
+// the bf16 results straight into operands.  Each query is split into two
+// bf16 parts (hi = bf16(q), lo = bf16(q - hi), so |q - hi - lo| <= 2^-16 |q|),
+// kept in LDS in A-operand layout; 2 d/32 products give a 16 x 16 tile of
+// (query, token) scores in fp32, scaled and written like k_attn_scores'.
+template <int D, int KT, int BITS>
+__global__ __launch_bounds__(256) void k_attn_scores_mq(const float *__restrict__ q, int Nq, int N,
+                                                        int H, AttnRec kr, float scale,
+                                                        const float *__restrict__ rcos,
+                                                        const float *__restrict__ rsin, int nsplit,
+                                                        int tps, float *__restrict__ scores) {
+  constexpr int HD = D / 2, KB = D / 32, HKB = KB / 2;
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  typedef float floatx4_t __attribute__((ext_vector_type(4)));
+  __shared__ float4 lut2[BITS == 2 ? 256 : 1];
+  __shared__ float2 lut4[BITS == 4 ? 256 : 1];
+  extern __shared__ uint4 qop[];  // [gh][2 parts][KB][64 lanes] A operands
+  const int HG = score_group(H, kAttnMaxQueries, D), ngroups = (H + HG - 1) / HG;
+  const int total = ngroups * nsplit, wg = blockIdx.x, xcd = wg & 7, slot = wg >> 3;
+  const int item = xcd * (total >> 3) + min(xcd, total & 7) + slot;
+  const int grp = item / nsplit, sp = item - grp * nsplit;
+  const int h0 = grp * HG, gh = min(HG, H - h0);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int tok = wave * 16 + (lane & 15);  // token of the 64-token step
+  const int c0 = (lane >> 4) * 8;           // channel offset within each block
+  init_level_lut<BITS>(lut2, lut4);
+  // the queries as two bf16 parts in A-operand layout: lane l of block kb
+  // holds query l % 16, channels kb*32 + 8*(l/16) .. +7 (zero past Nq)
+  for (int x = t; x < gh * KB * 64; x += 256) {
+    const int hh = x / (KB * 64), r = x - hh * (KB * 64), kb = r >> 6, ln = r & 63;
+    const int i = ln & 15, k = kb * 32 + (ln >> 4) * 8;
+    float v[8];
+    if (i < Nq) {
+      load8(q + ((int64_t)(h0 + hh) * Nq + i) * D, k, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+    }
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      hi[m] = pack_bf16_rne(v[2 * m], v[2 * m + 1]);
+      const float r0 = v[2 * m] - __uint_as_float(hi[m] << 16);  // exact
+      const float r1 = v[2 * m + 1] - __uint_as_float(hi[m] & 0xFFFF0000u);
+      lo[m] = pack_bf16_rne(r0, r1);
+    }
+    qop[((hh * 2 + 0) * KB + kb) * 64 + ln] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    qop[((hh * 2 + 1) * KB + kb) * 64 + ln] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  }
+  __syncthreads();
+  const int C = kr.C, kg = __builtin_ctz(kr.G);
+  const int ntiles = (N + kAttnBN - 1) / kAttnBN;
+  const int t0 = sp * tps * kAttnBN, t1 = min(min(sp * tps + tps, ntiles) * kAttnBN, N);
+  const char *rc = reinterpret_cast<const char *>(rcos), *rs = reinterpret_cast<const char *>(rsin);
+  // First-level loads of one (pass, head) step, as in k_attn_scores.
+  struct Raw {
+    uint32_t w[KB], e[KB], j[KT];
+  };
+  auto fetch = [&](int b0, int h, Raw &r) {
+    const uint32_t ti = (uint32_t)min(b0 + tok, t1 - 1);
+    const uint8_t *crow = kr.codes + (int64_t)h * N * (D * BITS / 8) + ti * (uint32_t)(D * BITS / 8);
+    const uint8_t *scl = kr.scales + ((int64_t)h * N << (__builtin_ctz(D) - kg));
+    const uint32_t so = ti << (__builtin_ctz(D) - kg);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      load_codes<BITS, 1>(crow, kb * 32 + c0, &r.w[kb]);
+      r.e[kb] = scl[so + ((kb * 32 + c0) >> kg)];
+    }
+    const uint8_t *asg = kr.assign + (int64_t)h * KT * N;
+#pragma unroll
+    for (int u = 0; u < KT; ++u) r.j[u] = asg[(uint32_t)(KT - 1 - u) * (uint32_t)N + ti];  // u = 0: last stage
+  };
+  Raw cur;
+  fetch(t0, h0, cur);
+  float c[HKB][8], sn[HKB][8];
+  int b0 = t0, hh = 0;
+  int nb0 = t0, nhh = 0;
+  while (b0 < t1) {
+    if (++nhh == gh) nhh = 0, nb0 += kAttnBN;
+    const int h = h0 + hh;
+    const uint32_t ti = (uint32_t)min(b0 + tok, t1 - 1);
+    const char *cent = reinterpret_cast<const char *>(static_cast<const uint16_t *>(kr.cent) +
+                                                      (int64_t)h * KT * C * D);
+    uint32_t kop[KB][4];  // the lane's rotated bf16 key channels, B operands
+    Raw nx;
+#pragma unroll
+    for (int hb = 0; hb < HKB; ++hb) {
+      // channels hb*32 + c0 .. (x) and their partners d/2 later (y): the
+      // table rows (and, for the group's first head, the rotary rows) go out
+      // first; after the last half's, the next step's first-level loads,
+      // which stay in flight while this step computes
+      Row8<uint16_t> ga[KT], gb[KT];
+#pragma unroll
+      for (int u = 0; u < KT; ++u) {
+        const uint32_t ju = min(cur.j[u], (uint32_t)C - 1);
+        const uint32_t off = (((uint32_t)(KT - 1 - u) * (uint32_t)C + ju) * D + hb * 32 + c0) * 2u;
+        ga[u].load(reinterpret_cast<const uint16_t *>(cent + off));
+        gb[u].load(reinterpret_cast<const uint16_t *>(cent + off + HD * 2));
+      }
+      if (rcos && hh == 0) {
+        const uint32_t ro = (ti * HD + hb * 32 + c0) * 4u;
+        load8(reinterpret_cast<const float *>(rc + ro), 0, c[hb]);
+        load8(reinterpret_cast<const float *>(rs + ro), 0, sn[hb]);
+      }
+      if (hb == HKB - 1) fetch(min(nb0, t1 - 1), h0 + nhh, nx);
+      float a[8], b[8], ca[8], cb[8];
+      levels8(cur.w[hb], BITS, lut2, lut4, a);
+      levels8(cur.w[hb + HKB], BITS, lut2, lut4, b);
+      const float s0 = e4m3_decode_bits(cur.e[hb]), s1 = e4m3_decode_bits(cur.e[hb + HKB]);
+      ga[0].get(ca);
+      gb[0].get(cb);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a[e] = __builtin_fmaf(a[e], s0, ca[e]);
+        b[e] = __builtin_fmaf(b[e], s1, cb[e]);
+      }
+#pragma unroll
+      for (int u = 1; u < KT; ++u) {
+        ga[u].get(ca);
+        gb[u].get(cb);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          a[e] = a[e] + ca[e];
+          b[e] = b[e] + cb[e];
+        }
+      }
+      rotate_pack(a, b, rcos != nullptr, c[hb], sn[hb], kop[hb], kop[hb + HKB]);
+    }
+    cur = nx;
+    // 16 queries x 16 tokens: the hi parts of every block, then the lo parts
+    floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint4 *qa = qop + (hh * 2) * KB * 64 + lane;
+#pragma unroll
+    for (int part = 0; part < 2; ++part)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const uint4 av = qa[(part * KB + kb) * 64];
+        const uint4 bv = make_uint4(kop[kb][0], kop[kb][1], kop[kb][2], kop[kb][3]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                      __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0,
+                                                      0);
+      }
+    // lane l: token l % 16 of the wave, queries 4*(l/16) .. +3
+    const uint32_t tw = (uint32_t)b0 + (uint32_t)(wave * 16 + (lane & 15));
+    if (tw < (uint32_t)t1) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = (lane >> 4) * 4 + r;
+        if (i < Nq) scores[((int64_t)h * Nq + i) * N + tw] = acc[r] * scale;
+      }
+    }
     b0 = nb0;
     hh = nhh;
   }
@@ -1199,6 +1384,24 @@ bool launch_scores_t(const float *q, int H, int Nq, int N, const AttnRec &kr, fl
   return hipGetLastError() == hipSuccess;
 }
 
+template <int D, int KT>
+bool launch_scores_mq_t(const float *q, int H, int Nq, int N, const AttnRec &kr, float scale,
+                        const float *rcos, const float *rsin, float *scores, hipStream_t s) {
+  const int HG = score_group(H, kAttnMaxQueries, D), ngroups = (H + HG - 1) / HG;
+  const int ntiles = (N + kAttnBN - 1) / kAttnBN;
+  const int want = std::min(std::min(std::max(1, (kAttnTargetGroups + ngroups - 1) / ngroups),
+                                     kAttnMaxSplit), ntiles);
+  const int tps = (ntiles + want - 1) / want, nsplit = (ntiles + tps - 1) / tps;
+  const size_t lds = (size_t)HG * 2 * (D / 32) * 64 * sizeof(uint4);
+  if (kr.bits == 2)
+    hipLaunchKernelGGL((k_attn_scores_mq<D, KT, 2>), dim3(ngroups * nsplit), dim3(256), lds, s, q,
+                       Nq, N, H, kr, scale, rcos, rsin, nsplit, tps, scores);
+  else
+    hipLaunchKernelGGL((k_attn_scores_mq<D, KT, 4>), dim3(ngroups * nsplit), dim3(256), lds, s, q,
+                       Nq, N, H, kr, scale, rcos, rsin, nsplit, tps, scores);
+  return hipGetLastError() == hipSuccess;
+}
+
 template <int D, int NQ>
 bool launch_attn_2p(const float *q, int H, int Nq, int N, const AttnRec &kr, const AttnRec &vr,
                     float scale, const float *rcos, const float *rsin, float *part, float *out,
@@ -1209,11 +1412,20 @@ bool launch_attn_2p(const float *q, int H, int Nq, int N, const AttnRec &kr, con
   float *cpart = part + (size_t)H * sp.nsplit * Nq * pf;
   float *scores = cpart + (size_t)H * Nq * kContractParts * D;
   bool ok = false;
-  switch (kr.T) {
-    case 1: ok = launch_scores_t<D, NQ, 1>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
-    case 2: ok = launch_scores_t<D, NQ, 2>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
-    case 3: ok = launch_scores_t<D, NQ, 3>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
-    case 4: ok = launch_scores_t<D, NQ, 4>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
+  if (NQ == 1) {
+    switch (kr.T) {
+      case 1: ok = launch_scores_t<D, 1, 1>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
+      case 2: ok = launch_scores_t<D, 1, 2>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
+      case 3: ok = launch_scores_t<D, 1, 3>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
+      case 4: ok = launch_scores_t<D, 1, 4>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
+    }
+  } else {
+    switch (kr.T) {
+      case 1: ok = launch_scores_mq_t<D, 1>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
+      case 2: ok = launch_scores_mq_t<D, 2>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
+      case 3: ok = launch_scores_mq_t<D, 3>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
+      case 4: ok = launch_scores_mq_t<D, 4>(q, H, Nq, N, kr, scale, rcos, rsin, scores, s); break;
+    }
   }
   if (!ok) return false;
   if (NQ == 1) {
@@ -1261,8 +1473,7 @@ bool launch_attn_d(const float *q, int H, int Nq, int N, const AttnRec &kr, cons
                    hipStream_t s) {
   if (attn_two_pass(H, Nq, kr.T, vr.T, vr.C, sizeof(Tc) == 2, N, D)) {
     if (Nq == 1) return launch_attn_2p<D, 1>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
-    if (Nq <= 4) return launch_attn_2p<D, 4>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
-    return launch_attn_2p<D, 16>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
+    return launch_attn_2p<D, kAttnMaxQueries>(q, H, Nq, N, kr, vr, scale, rcos, rsin, part, out, s);
   }
   if (attn_sums_one_pass(Nq, vr.T, vr.C)) {
     if (Nq == 1)
