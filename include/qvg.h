@@ -287,21 +287,24 @@ qvg_status qvg_group_quant_pack(const void *r, qvg_dtype dtype, int64_t H, int64
  *     multiply-add and adds).
  *   With bf16 centroids, keys of 1 to 4 stages, weight sums, N*2d < 2^32
  *   and H <= 256, the call takes two passes instead (same runs for the
- *   values; queries in groups of 4, each group's weight sums held at once):
- *   the scores first,
- *   each d/8 (d/4 for d = 64) fused multiply-add chains of 16 terms added
- *   pairwise, times scale (one query); for 2 to 16 queries each query is
- *   split into two bf16 parts, hi = bf16(q) and lo = bf16(q - hi) (so
- *   |q - hi - lo| <= 2^-16 |q|), and the 2d exact products of the parts
- *   with the bf16 key are summed in fp32 on the matrix cores (the hi parts
- *   of 32-channel blocks in order, then the lo parts; the order within a
- *   block is the hardware's), times scale; then, with m the run's largest score, weights
- *   e^(s - m) (never rescaled): per run a fused multiply-add chain of
- *   (weight * s_hat) * level over 4 (d = 128) or 2 (d = 64) tokens per
- *   tile (one query: over 1 token per pass of 64 or 128), the chains of a
- *   wave added pairwise and the 4 waves in order, and weight sums
- *   kept exactly in units of 2^-40 (each weight rounded to the nearest
- *   unit) and rounded to fp32 once per run; runs merged as above.
+ *   values; queries in groups of 4, each group's weight sums held at once).
+ *   The scores first: for one query, d/8 (d/4 for d = 64) fused
+ *   multiply-add chains of 16 terms added pairwise, times scale; for 2 to
+ *   16 queries, each query split into two bf16 parts, hi = bf16(q) and
+ *   lo = bf16(q - hi) (so |q - hi - lo| <= 2^-16 |q|), and the 2d exact
+ *   products of the parts with the bf16 key summed in fp32 on the matrix
+ *   cores (the hi parts of the 32-channel blocks in order, then the lo
+ *   parts; the order within a block is the hardware's), times scale.  Then,
+ *   with m the run's largest score, weights e^(s - m) (never rescaled): for
+ *   one query, per run a fused multiply-add chain of (weight * s_hat) *
+ *   level over 1 token per pass of 64 or 128, the chains of a wave added
+ *   pairwise and the 4 waves in order; for 2 to 16 queries, each weight
+ *   split into two bf16 parts (|p - hi - lo| <= 2^-16 p) and the products
+ *   with s_hat * level (exact in bf16) summed in fp32 on the matrix cores
+ *   over the run (per 32-token block the hi parts, then the lo parts).
+ *   Weight sums are kept exactly in units of 2^-40 (each weight rounded to
+ *   the nearest unit) and rounded to fp32 once per run; runs merged as
+ *   above.
  *   ws: device scratch of qvg_attention_workspace_size(H, Nq, N, d, vp)
  *   bytes, 256-byte aligned; all device pointers 16-byte aligned.
  * Errors: QVG_ERR_INVALID_ARG for NULL pointers, one rope table without the

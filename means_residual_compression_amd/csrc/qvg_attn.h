@@ -35,7 +35,7 @@ AttnSplit attn_split(int H, int64_t N);
 // kAttnSumQueries) (see qvg_attn.hip).
 bool attn_sums_one_pass(int Nq, int T, int C);
 bool attn_sums_two_pass(int Nq, int T, int C);
-// Whether the call takes the two-pass path (k_attn_scores, k_attn_values):
+// Whether the call takes the two-pass path (scores, then values):
 // bf16 centroids, keys of 1 to 4 stages, weight sums, N * 2d < 2^32 and at
 // most 256 heads.
 bool attn_two_pass(int H, int Nq, int kT, int vT, int vC, bool c_bf16, int64_t N, int D);

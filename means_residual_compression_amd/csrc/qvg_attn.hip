@@ -606,37 +606,35 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float *__restrict__ 
 }
 
 // ------------------------------------------------------------- two passes
-// With bf16 centroid tables, keys of 1 to 4 stages, weight sums and up to
-// kAttnSumQueries queries, the attention takes two passes over the records
-// instead of k_attn_split:
-//  * k_attn_scores (keys only): a workgroup takes a run of tokens for a
-//    group of heads (score_group).  Eight lanes
-//    per token (d = 128; four for d = 64), each holding 8 rotate-half channel
-//    pairs (channels k .. k+7 and d/2 + k ..), rebuild the key in registers
-//    as k_attn_split does, rotate it and take its products with each query
-//    in a chain of 16 fused multiply-adds; butterfly adds give all lanes of
-//    the token the same score, which is scaled and written to the scratch.
-//    A lane loads its token's rotary rows once and keeps them while it
-//    scores the token for every head of the group.  Only the level tables
-//    and the queries go through LDS, and every wave scores its own tokens.
-//  * k_attn_values: with m the run's largest score (read back from the
-//    scores), every weight is p_n = e^(s_n - m), so no running maximum is
-//    kept and nothing is rescaled.  A lane owns 8 channels and a slot of
-//    each tile's tokens and accumulates sum_n (p_n s_hat_n) level_n in
-//    registers (one fused multiply-add chain per lane over the run); the wave
-//    that owns stage t (t = w mod 4, lane = token) adds each token's weight,
-//    rounded to a multiple of 2^-40, to W_t[pi_t(n)] in LDS as a 64-bit
-//    integer (integer LDS atomics are an order of magnitude faster than float
-//    ones here, and integer sums do not depend on the order of the adds).
-//    The run's (m, l, o, W) record, W converted back to fp32 once, is merged
-//    by k_attn_contract and k_attn_combine.
-// Summation order: a score is d/8 (or d/4) chains of 16 fused multiply-adds,
-// added pairwise, times scale.  An output element of one run is 4 (d = 128)
-// or 2 (d = 64) tokens per tile per lane in one chain over the run, the lanes
-// of a wave added pairwise (2 or 3 levels), then the 4 waves in order; l is a
-// chain over wave 0's lanes' tokens, added pairwise over the lanes.  A
-// weight sum of a run is exact in units of 2^-40 (each weight within 2^-41 of
-// its unit multiple), rounded once to fp32.
+// With bf16 centroid tables, keys of 1 to 4 stages and weight sums (up to
+// 16 queries, kAttnSumQueries at a time), the attention takes two passes
+// over the records instead of k_attn_split:
+//  * k_attn_scores (keys only, one query): a workgroup takes a run of tokens
+//    for a group of heads (score_group).  Eight lanes per token (d = 128;
+//    four for d = 64), each holding 8 rotate-half channel pairs (channels
+//    k .. k+7 and d/2 + k ..), rebuild the key in registers as k_attn_split
+//    does, rotate it and take its product with the query in a chain of 16
+//    fused multiply-adds; butterfly adds give all lanes of the token the
+//    same score, which is scaled and written to the scratch.  A lane loads
+//    its token's rotary rows once and keeps them while it scores the token
+//    for every head of the group.  Only the level tables and the queries go
+//    through LDS, and every wave scores its own tokens.
+//    k_attn_scores_mq does the same for 2 to 16 queries on the matrix cores.
+//  * k_attn_values1 (one query) and k_attn_values_mq (up to
+//    kAttnSumQueries per launch): with m the run's largest score (read back
+//    from the scores), every weight is p_n = e^(s_n - m), so no running
+//    maximum is kept and nothing is rescaled.  The residual term
+//    sum_n (p_n s_hat_n) level_n is accumulated in registers (fused
+//    multiply-add chains for one query, matrix-core products otherwise);
+//    each token's weight, rounded to a multiple of 2^-40, is added to
+//    W_t[pi_t(n)] in LDS as a 64-bit integer (integer LDS atomics are an
+//    order of magnitude faster than float ones here, and integer sums do not
+//    depend on the order of the adds).  The run's (m, l, o, W) record, W
+//    converted back to fp32 once, is merged by k_attn_contract and
+//    k_attn_combine.
+// Summation orders are given with each kernel; a weight sum of a run is
+// exact in units of 2^-40 (each weight within 2^-41 of its unit multiple),
+// rounded once to fp32.
 
 // Workgroup -> (head, run), XCD-aware as in k_attn_split.
 __device__ __forceinline__ void attn_item(int H, int nsplit, int &h, int &sp) {
@@ -1013,70 +1011,53 @@ __global__ __launch_bounds__(256) void k_attn_scores_mq(const float *__restrict_
   }
 }
 
-template <int D, int NQ, int BITS>
-__global__ __launch_bounds__(256) void k_attn_values(const float *__restrict__ scores, int Nq,
-                                                     int N, int H, AttnRec vr, int nsplit, int tps,
-                                                     int pf, float *__restrict__ part, int q0,
-                                                     int NqT) {
-  constexpr int CG = D / 8, SL = 256 / CG, TPT = kAttnBN / SL;  // groups, slots, tokens
+// Values of up to kAttnSumQueries queries per launch (2 to 16 per call),
+// the residual term on the matrix cores.  Per 64-token tile:
+//  * thread (query = wave, token = lane) takes its weight p = e^(s - m),
+//    adds it to l, stores it as two bf16 parts (hi = bf16(p),
+//    lo = bf16(p - hi), |p - hi - lo| <= 2^-16 p) in the P tile and adds it,
+//    rounded to a multiple of 2^-40, to the weight sum of its cluster in
+//    every stage (64-bit LDS integers, exact in any order);
+//  * thread (token group, channel group) decodes level * s_hat of 8
+//    channels of d/32 tokens, exact in bf16 (an odd level below 16 times an
+//    E4M3 value), into the transposed value tile V^T [d][64];
+//  * wave w multiplies the P tile (A: queries x tokens) by V^T (B: tokens x
+//    channels) for its d/64 16-channel tiles, hi parts then lo parts of each
+//    32-token block, accumulating in fp32.
+constexpr int kValuesAhead = 4;
+template <int D, int BITS, int PT>
+__global__ __launch_bounds__(256) void k_attn_values_mq(const float *__restrict__ scores, int Nq,
+                                                        int N, int H, AttnRec vr, int nsplit,
+                                                        int tps, int pf, float *__restrict__ part,
+                                                        int q0, int NqT) {
+  constexpr int NQG = kAttnSumQueries;  // queries per launch (= waves)
+  constexpr int TPTH = D / 32;           // tokens per thread in the decode
+  constexpr int NTG = kAttnBN / TPTH;    // token groups
+  constexpr int CTW = D / 64;            // 16-channel tiles per wave
+  constexpr int VS = kAttnBN + 8;        // V^T row stride (bf16), padded
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  typedef float floatx4_t __attribute__((ext_vector_type(4)));
   __shared__ float4 lut2[BITS == 2 ? 256 : 1];
-  __shared__ float4 lut4v[BITS == 4 ? 128 : 1];  // [256] float2, 16-byte aligned
-  __shared__ float4 lred4[(NQ + 3) / 4];
-  __shared__ float mred[4][NQ];
+  __shared__ float4 lut4v[BITS == 4 ? 128 : 1];
+  __shared__ __align__(16) uint16_t vt[D * VS];            // V^T tile
+  __shared__ __align__(16) uint16_t pt[2 * NQG * VS];      // P tile: [part][query][token]
+  __shared__ float mred[4][NQG], lred[NQG];
   float2 *lut4 = reinterpret_cast<float2 *>(lut4v);
-  float *lred = reinterpret_cast<float *>(lred4);
-  // [Nq][T][C] weight sums in units of 2^-40, then [4][NQ][D] wave outputs
-  extern __shared__ unsigned long long ws[];
+  extern __shared__ unsigned long long ws[];  // [Nq][T][C] weight sums in units of 2^-40
   int h, sp;
   attn_item(H, nsplit, h, sp);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int cg = t % CG, slot = t / CG;
   const int T = vr.T, C = vr.C, TC = T * C, vg = __builtin_ctz(vr.G);
   init_level_lut<BITS>(lut2, lut4);
   for (int x = t; x < Nq * TC; x += 256) ws[x] = 0ull;
-  // this launch's queries q0 .. q0+Nq-1 of the call's NqT
-  const float *sh = scores + ((int64_t)h * NqT + q0) * N;
+  const float *sh = scores + ((int64_t)h * NqT + q0) * N;  // this launch's queries
   const int ntiles = (N + kAttnBN - 1) / kAttnBN;
   const int tb = sp * tps, te = min(tb + tps, ntiles);
-  float o[NQ][8], l[NQ];
-#pragma unroll
-  for (int jq = 0; jq < NQ; ++jq) {
-    l[jq] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[jq][e] = 0.0f;
-  }
-  const int dv = __builtin_ctz(D) - vg;
-  // A tile's loads: this lane's code words, scale bytes and scores of tokens
-  // slot, slot + SL, ... (residual term) and of token `lane` (weights), with
-  // the assignment byte of stage `wave`; tokens past the end repeat the last.
-  struct Raw {
-    uint32_t w[TPT], e[TPT], a;
-    float s[TPT][NQ], sw[NQ];
-  };
-  auto fetch = [&](int tile, Raw &r) {
-    const int i0 = tile * kAttnBN, nt = min(kAttnBN, N - i0);
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      const int ti = i0 + min(slot + SL * u, nt - 1);
-      const int64_t row = (int64_t)h * N + ti;
-      load_codes<BITS, 1>(vr.codes + row * (D * BITS / 8), cg * 8, &r.w[u]);
-      r.e[u] = vr.scales[(row << dv) + ((cg * 8) >> vg)];
-#pragma unroll
-      for (int jq = 0; jq < NQ; ++jq) r.s[u][jq] = jq < Nq ? sh[(int64_t)jq * N + ti] : 0.0f;
-    }
-    const int tl = i0 + min(lane, nt - 1);
-#pragma unroll
-    for (int jq = 0; jq < NQ; ++jq) r.sw[jq] = jq < Nq ? sh[(int64_t)jq * N + tl] : 0.0f;
-    r.a = wave < T ? vr.assign[((int64_t)h * T + wave) * N + tl] : 0u;
-  };
-  Raw cur;
-  fetch(tb, cur);
-  // M: the run's largest score per query (8 loads in flight per round;
-  // clamped indices repeat a token, which does not change a maximum)
+  // M: the run's largest score per query
   const int r0 = tb * kAttnBN, r1 = min(te * kAttnBN, N);
-  float M[NQ];
+  float M[NQG];
 #pragma unroll
-  for (int jq = 0; jq < NQ; ++jq) {
+  for (int jq = 0; jq < NQG; ++jq) {
     float m = -__builtin_inff();
     if (jq < Nq)
       for (int i0 = r0 + t; i0 < r1; i0 += 256 * 8) {
@@ -1092,85 +1073,137 @@ __global__ __launch_bounds__(256) void k_attn_values(const float *__restrict__ s
   }
   __syncthreads();
 #pragma unroll
-  for (int jq = 0; jq < NQ; ++jq)
+  for (int jq = 0; jq < NQG; ++jq)
     M[jq] = fmaxf(fmaxf(mred[0][jq], mred[1][jq]), fmaxf(mred[2][jq], mred[3][jq]));
-  for (int tile = tb; tile < te; ++tile) {
-    const int i0 = tile * kAttnBN;
-    const int nt = min(kAttnBN, N - i0);
-    Raw nx;
-    fetch(min(tile + 1, te - 1), nx);
-    // residual term: this lane's 8 channels of tokens slot, slot + SL, ...
+  const float Mw = M[wave];  // this thread's query in the weight phase
+  const bool qok = wave < Nq;
+  // decode role: tokens TPTH*g .. +TPTH-1, channels 8*cg .. +7
+  const int g = t % NTG, cg = t / NTG;
+  const int dv = __builtin_ctz(D) - vg;
+  const uint8_t *codes = vr.codes + (int64_t)h * N * (D * BITS / 8);
+  const uint8_t *scl = vr.scales + ((int64_t)h * N << dv);
+  const uint8_t *asg = vr.assign + (int64_t)h * T * N;
+  // one tile's global loads: the score and the PT >= T assignment bytes of
+  // token `lane` (stages past T repeat the last one), the codes and scale
+  // bytes of the decode role
+  struct Raw {
+    float s;
+    uint32_t a[PT];
+    uint32_t w[TPTH], e[TPTH];
+  };
+  const int Tl = max(T - 1, 0);
+  auto fetch = [&](int tile, Raw &r) {
+    const int i0 = tile * kAttnBN, nt = min(kAttnBN, N - i0);
+    const int tl = i0 + min(lane, nt - 1);
+    r.s = qok ? sh[(int64_t)wave * N + tl] : 0.0f;
+    if (T > 0) {  // uniform
 #pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      const bool valid = slot + SL * u < nt;
-      float lv[8];
-      levels8(cur.w[u], BITS, lut2, lut4, lv);
-      const float shat = e4m3_decode_bits(cur.e[u]);
+      for (int ts = 0; ts < PT; ++ts) r.a[ts] = asg[(int64_t)min(ts, Tl) * N + tl];
+    }
 #pragma unroll
-      for (int jq = 0; jq < NQ; ++jq) {
-        const float p = (valid && jq < Nq) ? __expf(cur.s[u][jq] - M[jq]) : 0.0f;
-        const float ps = p * shat;
+    for (int u = 0; u < TPTH; ++u) {
+      const int ti = i0 + min(TPTH * g + u, nt - 1);
+      load_codes<BITS, 1>(codes + (int64_t)ti * (D * BITS / 8), cg * 8, &r.w[u]);
+      r.e[u] = scl[((int64_t)ti << dv) + ((cg * 8) >> vg)];
+    }
+  };
+  float lsum = 0.0f;
+  floatx4_t acc[CTW];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[jq][e] = __builtin_fmaf(ps, lv[e], o[jq][e]);
+  for (int c = 0; c < CTW; ++c) acc[c] = (floatx4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  // tile k's loads sit in buffer k mod kValuesAhead, issued kValuesAhead
+  // tiles before its use (the kernel is bound by load latency otherwise)
+  auto process = [&](int tile, const Raw &r) {
+    const int nt = min(kAttnBN, N - tile * kAttnBN);
+    // weights of (query wave, token lane)
+    {
+      const float p = (qok && lane < nt) ? __expf(r.s - Mw) : 0.0f;
+      lsum += p;
+      const uint32_t hi = pack_bf16_rne(0.0f, p) >> 16;
+      const float rem = p - __uint_as_float(hi << 16);  // exact
+      const uint32_t lo = pack_bf16_rne(0.0f, rem) >> 16;
+      pt[(0 * NQG + wave) * VS + lane] = (uint16_t)hi;
+      pt[(1 * NQG + wave) * VS + lane] = (uint16_t)lo;
+      if (qok && lane < nt) {
+        const unsigned long long pq = __float2ull_rn(p * 0x1p40f);
+#pragma unroll
+        for (int ts = 0; ts < PT; ++ts)
+          if (ts < T) atomicAdd(ws + (wave * T + ts) * C + min((int)r.a[ts], C - 1), pq);
       }
     }
-    // weight sums (wave w: stages w, w + 4, ...) and l (wave 0); lane = token
-    if (wave == 0 || wave < T) {
-      float p[NQ];
+    // level * s_hat of this thread's tokens and channels, transposed
+    {
+      float v[TPTH][8];
 #pragma unroll
-      for (int jq = 0; jq < NQ; ++jq)
-        p[jq] = (lane < nt && jq < Nq) ? __expf(cur.sw[jq] - M[jq]) : 0.0f;
-      if (wave == 0)
+      for (int u = 0; u < TPTH; ++u) {
+        levels8(r.w[u], BITS, lut2, lut4, v[u]);
+        const float shat = e4m3_decode_bits(r.e[u]);
 #pragma unroll
-        for (int jq = 0; jq < NQ; ++jq) l[jq] += p[jq];
-      const int tl = i0 + min(lane, nt - 1);
-      // each weight rounded to a multiple of 2^-40 (integer adds, so
-      // exact and independent of their order)
-      unsigned long long pq[NQ];
+        for (int e = 0; e < 8; ++e) v[u][e] = v[u][e] * shat;  // exact
+      }
 #pragma unroll
-      for (int jq = 0; jq < NQ; ++jq) pq[jq] = __float2ull_rn(p[jq] * 0x1p40f);
-      for (int ts = wave; ts < T; ts += 4) {
-        const uint32_t raw = ts == wave ? cur.a : vr.assign[((int64_t)h * T + ts) * N + tl];
-        const int c = min((int)raw, C - 1);
-        if (lane < nt)
-#pragma unroll
-          for (int jq = 0; jq < NQ; ++jq)
-            if (jq < Nq) atomicAdd(ws + (jq * T + ts) * C + c, pq[jq]);
+      for (int e = 0; e < 8; ++e) {
+        uint16_t *row = vt + (cg * 8 + e) * VS + TPTH * g;
+        if constexpr (TPTH == 4) {
+          *reinterpret_cast<uint2 *>(row) =
+              make_uint2(pack_bf16_rne(v[0][e], v[1][e]), pack_bf16_rne(v[2][e], v[3][e]));
+        } else {
+          *reinterpret_cast<uint32_t *>(row) = pack_bf16_rne(v[0][e], v[1][e]);
+        }
       }
     }
-    cur = nx;
+    __syncthreads();
+    // O[q][k] += sum_n P[q][n] V[n][k]: A lane l = query l % 16 (zero past
+    // Nq), tokens 8*(l/16) ..; B lane l = channel l % 16 of the tile
+    const int qi = lane & 15, kq = (lane >> 4) * 8;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 ah = make_uint4(0u, 0u, 0u, 0u), al = ah;
+      if (qi < Nq) {
+        ah = *reinterpret_cast<const uint4 *>(pt + (0 * NQG + qi) * VS + ks * 32 + kq);
+        al = *reinterpret_cast<const uint4 *>(pt + (1 * NQG + qi) * VS + ks * 32 + kq);
+      }
+#pragma unroll
+      for (int c = 0; c < CTW; ++c) {
+        const int ct = wave * CTW + c;
+        const uint4 bv = *reinterpret_cast<const uint4 *>(vt + (ct * 16 + qi) * VS + ks * 32 + kq);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah),
+                                                         __builtin_bit_cast(bf16x8_t, bv), acc[c],
+                                                         0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al),
+                                                         __builtin_bit_cast(bf16x8_t, bv), acc[c],
+                                                         0, 0, 0);
+      }
+    }
+    __syncthreads();  // the tiles are rewritten next
+  };
+  Raw buf[kValuesAhead];
+#pragma unroll
+  for (int k = 0; k < kValuesAhead; ++k) fetch(min(tb + k, te - 1), buf[k]);
+  for (int tile = tb; tile < te; tile += kValuesAhead) {
+#pragma unroll
+    for (int k = 0; k < kValuesAhead; ++k) {
+      if (tile + k < te) process(tile + k, buf[k]);  // uniform
+      // unconditional, so that every path issues the same loads
+      fetch(min(tile + k + kValuesAhead, te - 1), buf[k]);
+    }
   }
-  // combine the token slots: pairwise over a wave's lanes, then the waves in order
-  float *wout = reinterpret_cast<float *>(ws + Nq * TC);  // [4][NQ][D]
+  // l per query: this wave's lanes, pairwise
 #pragma unroll
-  for (int off = CG; off < 64; off <<= 1)
-#pragma unroll
-    for (int jq = 0; jq < NQ; ++jq)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[jq][e] = o[jq][e] + __shfl_xor(o[jq][e], off);
-  if (lane < CG)
-#pragma unroll
-    for (int jq = 0; jq < NQ; ++jq)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) wout[(wave * NQ + jq) * D + cg * 8 + e] = o[jq][e];
-  if (wave == 0)
-#pragma unroll
-    for (int jq = 0; jq < NQ; ++jq) {
-      float v = l[jq];
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off);
-      if (lane == 0) lred[jq] = v;
-    }
+  for (int off = 1; off < 64; off <<= 1) lsum = lsum + __shfl_xor(lsum, off);
+  if (lane == 0) lred[wave] = lsum;
   __syncthreads();
   float *rec = part + (((int64_t)h * nsplit + sp) * NqT + q0) * pf;
-  for (int x = t; x < Nq * D; x += 256) {
-    const int jq = x / D, k = x - jq * D;
-    const float r = ((wout[(0 * NQ + jq) * D + k] + wout[(1 * NQ + jq) * D + k]) +
-                     wout[(2 * NQ + jq) * D + k]) + wout[(3 * NQ + jq) * D + k];
-    rec[jq * pf + 2 + k] = r;
+  // lanes 0..15 hold rows (queries) 0..3 of their channel columns
+  if (lane < 16) {
+#pragma unroll
+    for (int c = 0; c < CTW; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (r < Nq) rec[r * pf + 2 + (wave * CTW + c) * 16 + lane] = acc[c][r];
   }
 #pragma unroll
-  for (int jq = 0; jq < NQ; ++jq)
+  for (int jq = 0; jq < NQG; ++jq)
     if (t == jq && jq < Nq) {
       rec[jq * pf] = M[jq];
       rec[jq * pf + 1] = lred[jq];
@@ -1181,14 +1214,14 @@ __global__ __launch_bounds__(256) void k_attn_values(const float *__restrict__ s
   }
 }
 
-// k_attn_values for one query: a lane owns 32 consecutive channels of one
-// token per pass (four lanes per token for d = 128, two for d = 64), so a
-// token's weight is computed by 4 (or 2) lanes rather than 16, and the lane
-// accumulates its 32 channels in registers.  Weight sums, l and the record
-// are as in k_attn_values.  Summation order: an output element of one run is
-// a fused multiply-add chain over the run's tokens of that lane position
-// (one per pass), the 16 (or 32) lane chains of a wave added pairwise, then
-// the 4 waves in order.
+// Values of one query: a lane owns 32 consecutive channels of one token per
+// pass (four lanes per token for d = 128, two for d = 64), so a token's
+// weight is computed by 4 (or 2) lanes, and the lane accumulates its 32
+// channels in registers; the wave that owns stage t (t = w mod 4, lane =
+// token) adds the weights to the stage's sums.  Summation order: an output
+// element of one run is a fused multiply-add chain over the run's tokens of
+// that lane position (one per pass), the 16 (or 32) lane chains of a wave
+// added pairwise, then the 4 waves in order.
 template <int D, int BITS>
 __global__ __launch_bounds__(256) void k_attn_values1(const float *__restrict__ scores, int N,
                                                       int H, AttnRec vr, int nsplit, int tps,
@@ -1362,7 +1395,7 @@ bool launch_attn_t(const float *q, int H, int Nq, int N, const AttnRec &kr, cons
   return hipGetLastError() == hipSuccess;
 }
 
-// The two-pass path (k_attn_scores, k_attn_values); the scratch holds the
+// The two-pass path (scores, then values); the scratch holds the
 // run records, the contraction parts and the scores [H][Nq][N], in that
 // order.  The scores pass cuts each head group's tiles into its own runs, so
 // that about kAttnTargetGroups workgroups fill the chip.
@@ -1441,16 +1474,20 @@ bool launch_attn_2p(const float *q, int H, int Nq, int N, const AttnRec &kr, con
     // sums fit in LDS; the scores pass served all of them at once
     for (int q0 = 0; q0 < Nq; q0 += kAttnSumQueries) {
       const int nq = std::min(kAttnSumQueries, Nq - q0);
-      const size_t lds = (size_t)nq * TC * sizeof(unsigned long long) +
-                         (size_t)4 * kAttnSumQueries * D * sizeof(float);
-      if (vr.bits == 2)
-        hipLaunchKernelGGL((k_attn_values<D, kAttnSumQueries, 2>), dim3(H * sp.nsplit), dim3(256),
-                           lds, s, scores, nq, N, H, vr, sp.nsplit, sp.tiles_per_split, pf, part,
-                           q0, Nq);
+      const size_t lds = (size_t)nq * TC * sizeof(unsigned long long);
+      const dim3 grid(H * sp.nsplit);
+      if (vr.bits == 2 && vr.T <= 4)
+        hipLaunchKernelGGL((k_attn_values_mq<D, 2, 4>), grid, dim3(256), lds, s, scores, nq, N, H,
+                           vr, sp.nsplit, sp.tiles_per_split, pf, part, q0, Nq);
+      else if (vr.bits == 2)
+        hipLaunchKernelGGL((k_attn_values_mq<D, 2, kMaxT>), grid, dim3(256), lds, s, scores, nq, N,
+                           H, vr, sp.nsplit, sp.tiles_per_split, pf, part, q0, Nq);
+      else if (vr.T <= 4)
+        hipLaunchKernelGGL((k_attn_values_mq<D, 4, 4>), grid, dim3(256), lds, s, scores, nq, N, H,
+                           vr, sp.nsplit, sp.tiles_per_split, pf, part, q0, Nq);
       else
-        hipLaunchKernelGGL((k_attn_values<D, kAttnSumQueries, 4>), dim3(H * sp.nsplit), dim3(256),
-                           lds, s, scores, nq, N, H, vr, sp.nsplit, sp.tiles_per_split, pf, part,
-                           q0, Nq);
+        hipLaunchKernelGGL((k_attn_values_mq<D, 4, kMaxT>), grid, dim3(256), lds, s, scores, nq, N,
+                           H, vr, sp.nsplit, sp.tiles_per_split, pf, part, q0, Nq);
     }
   }
   if (hipGetLastError() != hipSuccess) return false;

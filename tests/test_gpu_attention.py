@@ -49,7 +49,11 @@ def _bound(q, K, Vabs, scale, H, N, d, vT, vC, sums, mfma=False):
     taken in an unknown order with each addition off by at most 2^-23
     relative (twice the round-to-nearest bound; a probe of the instruction
     stayed within 4.7 * 2^-24 of the exact sum over 128 products):
-    delta = scale (2^-16 + 1.01 gamma'_2d) sum_k |q_k K_nk| + u |s|.  Each weight
+    delta = scale (2^-16 + 1.01 gamma'_2d) sum_k |q_k K_nk| + u |s|.  The
+    values of those calls also go through the matrix cores: each weight is
+    split the same way (a factor within 1 +- 2^-16 on its residual term) and
+    the run's 2 * 64 * tps products are summed with the same 2^-23 per
+    addition, i.e. a chain of 4 * 64 * tps in units of u.  Each weight
     e^(s - max) then carries a factor e^(+-delta), the exponential's relative
     error (3u times the argument, bounded by the score range, for the
     argument's roundings, plus 2^-22) and gamma_m from the chains that add it
@@ -77,7 +81,9 @@ def _bound(q, K, Vabs, scale, H, N, d, vT, vC, sums, mfma=False):
     m = (64 // P) * tps + tps + P + 2 * nsplit + 8
     if sums:
         m = max(m, 64 * tps + tps + 2 * nsplit + vT * vC * d // 2048 + 2048 // d + 8)
-    eps = 2.0 ** -22 + 3 * U * span + _gamma(m)
+    if mfma:
+        m = max(m, 4 * 64 * tps + tps + 2 * nsplit + vT * vC * d // 2048 + 2048 // d + 8)
+    eps = 2.0 ** -22 + 3 * U * span + _gamma(m) + (2.0 ** -16 if mfma else 0.0)
     ratio = np.exp(2 * delta) * (1 + eps) / (1 - eps) - 1
     vmax = Vabs.max(axis=0)
     rebuild = 0.0 if sums else _gamma(vT + 1)
