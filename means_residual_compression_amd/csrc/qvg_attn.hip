@@ -1012,35 +1012,42 @@ __global__ __launch_bounds__(256) void k_attn_scores_mq(const float *__restrict_
 }
 
 // Values of up to kAttnSumQueries queries per launch (2 to 16 per call),
-// the residual term on the matrix cores.  Per 64-token tile:
-//  * thread (query = wave, token = lane) takes its weight p = e^(s - m),
-//    adds it to l, stores it as two bf16 parts (hi = bf16(p),
-//    lo = bf16(p - hi), |p - hi - lo| <= 2^-16 p) in the P tile and adds it,
-//    rounded to a multiple of 2^-40, to the weight sum of its cluster in
-//    every stage (64-bit LDS integers, exact in any order);
-//  * thread (token group, channel group) decodes level * s_hat of 8
-//    channels of d/32 tokens, exact in bf16 (an odd level below 16 times an
-//    E4M3 value), into the transposed value tile V^T [d][64];
-//  * wave w multiplies the P tile (A: queries x tokens) by V^T (B: tokens x
-//    channels) for its d/64 16-channel tiles, hi parts then lo parts of each
-//    32-token block, accumulating in fp32.
+// the residual term on the matrix cores.  Each wave owns d/4 channels and
+// runs without workgroup barriers: per 64-token tile it
+//  * takes the weights p = e^(s - m) of every token (lane) and query, and
+//    stores them as two bf16 parts (hi = bf16(p), lo = bf16(p - hi),
+//    |p - hi - lo| <= 2^-16 p) in its own P tile; wave 0 adds them to l;
+//  * adds each weight, rounded to a multiple of 2^-40, to the weight sum of
+//    the token's cluster in the stages t = w mod 4 (64-bit LDS integers,
+//    exact in any order);
+//  * decodes level * s_hat of its channels (exact in bf16: an odd level
+//    below 16 times an E4M3 value) into its own transposed tile V^T;
+//  * multiplies P (A: queries x tokens) by V^T (B: tokens x channels) with
+//    v_mfma_f32_16x16x32_bf16, hi parts then lo parts of each 32-token
+//    block, accumulating in fp32.
+// A wave's LDS writes and later reads of its own tiles are ordered by the
+// in-order LDS queue of the wave.  The tiles' 16-byte granules are
+// XOR-swizzled by row so that the operand reads spread over the banks.
 constexpr int kValuesAhead = 4;
 template <int D, int BITS, int PT>
 __global__ __launch_bounds__(256) void k_attn_values_mq(const float *__restrict__ scores, int Nq,
                                                         int N, int H, AttnRec vr, int nsplit,
                                                         int tps, int pf, float *__restrict__ part,
                                                         int q0, int NqT) {
-  constexpr int NQG = kAttnSumQueries;  // queries per launch (= waves)
-  constexpr int TPTH = D / 32;           // tokens per thread in the decode
-  constexpr int NTG = kAttnBN / TPTH;    // token groups
-  constexpr int CTW = D / 64;            // 16-channel tiles per wave
-  constexpr int VS = kAttnBN + 8;        // V^T row stride (bf16), padded
+  constexpr int NQG = kAttnSumQueries;  // queries per launch
+  constexpr int CW = D / 4;              // channels per wave
+  constexpr int CTW = CW / 16;           // 16-channel tiles per wave
+  constexpr int TPL = CW / 8;            // tokens per lane in the decode
+  constexpr int NTG = kAttnBN / TPL;     // token groups
+  constexpr int SPW = (PT + 3) / 4;      // stages per wave
   typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
   typedef float floatx4_t __attribute__((ext_vector_type(4)));
-  __shared__ float4 lut2[BITS == 2 ? 256 : 1];
+  // INT2 levels by nibble (two codes per float2 entry): 16 entries cover the
+  // banks once, so random lookups do not conflict; INT4 by byte
+  __shared__ float2 lutn[BITS == 2 ? 16 : 1];
   __shared__ float4 lut4v[BITS == 4 ? 128 : 1];
-  __shared__ __align__(16) uint16_t vt[D * VS];            // V^T tile
-  __shared__ __align__(16) uint16_t pt[2 * NQG * VS];      // P tile: [part][query][token]
+  __shared__ __align__(16) uint16_t vt_all[4][CW * kAttnBN];        // per wave V^T
+  __shared__ __align__(16) uint16_t pt_all[4][2 * NQG * kAttnBN];   // per wave P
   __shared__ float mred[4][NQG], lred[NQG];
   float2 *lut4 = reinterpret_cast<float2 *>(lut4v);
   extern __shared__ unsigned long long ws[];  // [Nq][T][C] weight sums in units of 2^-40
@@ -1048,7 +1055,12 @@ __global__ __launch_bounds__(256) void k_attn_values_mq(const float *__restrict_
   attn_item(H, nsplit, h, sp);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int T = vr.T, C = vr.C, TC = T * C, vg = __builtin_ctz(vr.G);
-  init_level_lut<BITS>(lut2, lut4);
+  uint16_t *vt = vt_all[wave], *pt = pt_all[wave];
+  if constexpr (BITS == 2) {
+    if (t < 16) lutn[t] = make_float2((float)(2 * (t & 3) - 3), (float)(2 * (t >> 2) - 3));
+  } else {
+    init_level_lut<BITS>(nullptr, lut4);
+  }
   for (int x = t; x < Nq * TC; x += 256) ws[x] = 0ull;
   const float *sh = scores + ((int64_t)h * NqT + q0) * N;  // this launch's queries
   const int ntiles = (N + kAttnBN - 1) / kAttnBN;
@@ -1071,102 +1083,127 @@ __global__ __launch_bounds__(256) void k_attn_values_mq(const float *__restrict_
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
     if (lane == 0) mred[wave][jq] = m;
   }
-  __syncthreads();
+  __syncthreads();  // also orders the LUT and the cleared sums before use
 #pragma unroll
   for (int jq = 0; jq < NQG; ++jq)
     M[jq] = fmaxf(fmaxf(mred[0][jq], mred[1][jq]), fmaxf(mred[2][jq], mred[3][jq]));
-  const float Mw = M[wave];  // this thread's query in the weight phase
-  const bool qok = wave < Nq;
-  // decode role: tokens TPTH*g .. +TPTH-1, channels 8*cg .. +7
-  const int g = t % NTG, cg = t / NTG;
+  // decode role: tokens TPL*g .. +TPL-1, channels wave*CW + 8*c8 .. +7
+  const int g = lane % NTG, c8 = lane / NTG;
+  const int kw = wave * CW + c8 * 8;  // first channel of the lane's group
   const int dv = __builtin_ctz(D) - vg;
   const uint8_t *codes = vr.codes + (int64_t)h * N * (D * BITS / 8);
   const uint8_t *scl = vr.scales + ((int64_t)h * N << dv);
   const uint8_t *asg = vr.assign + (int64_t)h * T * N;
-  // one tile's global loads: the score and the PT >= T assignment bytes of
-  // token `lane` (stages past T repeat the last one), the codes and scale
-  // bytes of the decode role
+  // one tile's global loads: the scores of token `lane`, its assignment
+  // bytes in this wave's stages (past T: the last stage, unused), the
+  // decode role's code words and scale bytes
   struct Raw {
-    float s;
-    uint32_t a[PT];
-    uint32_t w[TPTH], e[TPTH];
+    float s[NQG];
+    uint32_t a[SPW];
+    uint32_t w[TPL], e[TPL];
   };
   const int Tl = max(T - 1, 0);
   auto fetch = [&](int tile, Raw &r) {
     const int i0 = tile * kAttnBN, nt = min(kAttnBN, N - i0);
     const int tl = i0 + min(lane, nt - 1);
-    r.s = qok ? sh[(int64_t)wave * N + tl] : 0.0f;
+#pragma unroll
+    for (int jq = 0; jq < NQG; ++jq) r.s[jq] = jq < Nq ? sh[(int64_t)jq * N + tl] : 0.0f;
     if (T > 0) {  // uniform
 #pragma unroll
-      for (int ts = 0; ts < PT; ++ts) r.a[ts] = asg[(int64_t)min(ts, Tl) * N + tl];
+      for (int u = 0; u < SPW; ++u) r.a[u] = asg[(int64_t)min(wave + 4 * u, Tl) * N + tl];
     }
 #pragma unroll
-    for (int u = 0; u < TPTH; ++u) {
-      const int ti = i0 + min(TPTH * g + u, nt - 1);
-      load_codes<BITS, 1>(codes + (int64_t)ti * (D * BITS / 8), cg * 8, &r.w[u]);
-      r.e[u] = scl[((int64_t)ti << dv) + ((cg * 8) >> vg)];
+    for (int u = 0; u < TPL; ++u) {
+      const int ti = i0 + min(TPL * g + u, nt - 1);
+      load_codes<BITS, 1>(codes + (int64_t)ti * (D * BITS / 8), kw, &r.w[u]);
+      r.e[u] = scl[((int64_t)ti << dv) + (kw >> vg)];
     }
   };
-  float lsum = 0.0f;
+  float lsum[NQG];
+#pragma unroll
+  for (int jq = 0; jq < NQG; ++jq) lsum[jq] = 0.0f;
   floatx4_t acc[CTW];
 #pragma unroll
   for (int c = 0; c < CTW; ++c) acc[c] = (floatx4_t){0.0f, 0.0f, 0.0f, 0.0f};
-  // tile k's loads sit in buffer k mod kValuesAhead, issued kValuesAhead
-  // tiles before its use (the kernel is bound by load latency otherwise)
+  const int qi = lane & 15, kq = lane >> 4;  // operand row / column, 8-token granule
   auto process = [&](int tile, const Raw &r) {
     const int nt = min(kAttnBN, N - tile * kAttnBN);
-    // weights of (query wave, token lane)
-    {
-      const float p = (qok && lane < nt) ? __expf(r.s - Mw) : 0.0f;
-      lsum += p;
+    // weights of token `lane`: P tile (granules swizzled by query) and sums
+    unsigned long long pq[NQG];
+#pragma unroll
+    for (int jq = 0; jq < NQG; ++jq) {
+      const bool ok = jq < Nq && lane < nt;
+      const float p = ok ? __expf(r.s[jq] - M[jq]) : 0.0f;
+      lsum[jq] += p;
       const uint32_t hi = pack_bf16_rne(0.0f, p) >> 16;
       const float rem = p - __uint_as_float(hi << 16);  // exact
       const uint32_t lo = pack_bf16_rne(0.0f, rem) >> 16;
-      pt[(0 * NQG + wave) * VS + lane] = (uint16_t)hi;
-      pt[(1 * NQG + wave) * VS + lane] = (uint16_t)lo;
-      if (qok && lane < nt) {
-        const unsigned long long pq = __float2ull_rn(p * 0x1p40f);
+      const int col = (((lane >> 3) ^ jq) << 3) | (lane & 7);
+      pt[(0 * NQG + jq) * kAttnBN + col] = (uint16_t)hi;
+      pt[(1 * NQG + jq) * kAttnBN + col] = (uint16_t)lo;
+      pq[jq] = __float2ull_rn(p * 0x1p40f);
+    }
+    if (lane < nt) {
 #pragma unroll
-        for (int ts = 0; ts < PT; ++ts)
-          if (ts < T) atomicAdd(ws + (wave * T + ts) * C + min((int)r.a[ts], C - 1), pq);
+      for (int u = 0; u < SPW; ++u) {
+        const int ts = wave + 4 * u;
+        if (ts < T) {
+          const int c = min((int)r.a[u], C - 1);
+#pragma unroll
+          for (int jq = 0; jq < NQG; ++jq)
+            if (jq < Nq) atomicAdd(ws + (jq * T + ts) * C + c, pq[jq]);
+        }
       }
     }
-    // level * s_hat of this thread's tokens and channels, transposed
+    // level * s_hat of this lane's tokens and channels into V^T (row k =
+    // channel within the wave, granules swizzled by k mod 8)
     {
-      float v[TPTH][8];
+      float v[TPL][8];
 #pragma unroll
-      for (int u = 0; u < TPTH; ++u) {
-        levels8(r.w[u], BITS, lut2, lut4, v[u]);
+      for (int u = 0; u < TPL; ++u) {
+        if constexpr (BITS == 2) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {  // codes 2m, 2m+1
+            const float2 x = lutn[(r.w[u] >> (4 * m)) & 0xFu];
+            v[u][2 * m] = x.x;
+            v[u][2 * m + 1] = x.y;
+          }
+        } else {
+          levels8(r.w[u], BITS, nullptr, lut4, v[u]);
+        }
         const float shat = e4m3_decode_bits(r.e[u]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[u][e] = v[u][e] * shat;  // exact
       }
+      const int n0 = TPL * g;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        uint16_t *row = vt + (cg * 8 + e) * VS + TPTH * g;
-        if constexpr (TPTH == 4) {
-          *reinterpret_cast<uint2 *>(row) =
+        const int k = c8 * 8 + e;
+        uint16_t *dst = vt + k * kAttnBN + ((((n0 >> 3) ^ e) << 3) | (n0 & 7));
+        if constexpr (TPL == 4) {
+          *reinterpret_cast<uint2 *>(dst) =
               make_uint2(pack_bf16_rne(v[0][e], v[1][e]), pack_bf16_rne(v[2][e], v[3][e]));
         } else {
-          *reinterpret_cast<uint32_t *>(row) = pack_bf16_rne(v[0][e], v[1][e]);
+          *reinterpret_cast<uint32_t *>(dst) = pack_bf16_rne(v[0][e], v[1][e]);
         }
       }
     }
-    __syncthreads();
-    // O[q][k] += sum_n P[q][n] V[n][k]: A lane l = query l % 16 (zero past
-    // Nq), tokens 8*(l/16) ..; B lane l = channel l % 16 of the tile
-    const int qi = lane & 15, kq = (lane >> 4) * 8;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    // O[q][k] += sum_n P[q][n] V[n][k] over the two 32-token blocks
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      const int gr = ks * 4 + kq;  // 8-token granule of the block
       uint4 ah = make_uint4(0u, 0u, 0u, 0u), al = ah;
       if (qi < Nq) {
-        ah = *reinterpret_cast<const uint4 *>(pt + (0 * NQG + qi) * VS + ks * 32 + kq);
-        al = *reinterpret_cast<const uint4 *>(pt + (1 * NQG + qi) * VS + ks * 32 + kq);
+        const int col = (gr ^ qi) << 3;
+        ah = *reinterpret_cast<const uint4 *>(pt + (0 * NQG + qi) * kAttnBN + col);
+        al = *reinterpret_cast<const uint4 *>(pt + (1 * NQG + qi) * kAttnBN + col);
       }
 #pragma unroll
       for (int c = 0; c < CTW; ++c) {
-        const int ct = wave * CTW + c;
-        const uint4 bv = *reinterpret_cast<const uint4 *>(vt + (ct * 16 + qi) * VS + ks * 32 + kq);
+        const int k = c * 16 + qi;
+        const uint4 bv =
+            *reinterpret_cast<const uint4 *>(vt + k * kAttnBN + ((gr ^ (k & 7)) << 3));
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah),
                                                          __builtin_bit_cast(bf16x8_t, bv), acc[c],
                                                          0, 0, 0);
@@ -1175,8 +1212,11 @@ __global__ __launch_bounds__(256) void k_attn_values_mq(const float *__restrict_
                                                          0, 0, 0);
       }
     }
-    __syncthreads();  // the tiles are rewritten next
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   };
+  // tile k's loads sit in buffer k mod kValuesAhead, issued kValuesAhead
+  // tiles before its use; every path issues the same loads, so that the
+  // compiler's waits stay counted
   Raw buf[kValuesAhead];
 #pragma unroll
   for (int k = 0; k < kValuesAhead; ++k) fetch(min(tb + k, te - 1), buf[k]);
@@ -1184,15 +1224,20 @@ __global__ __launch_bounds__(256) void k_attn_values_mq(const float *__restrict_
 #pragma unroll
     for (int k = 0; k < kValuesAhead; ++k) {
       if (tile + k < te) process(tile + k, buf[k]);  // uniform
-      // unconditional, so that every path issues the same loads
       fetch(min(tile + k + kValuesAhead, te - 1), buf[k]);
     }
   }
-  // l per query: this wave's lanes, pairwise
+  // l per query: wave 0's lanes, pairwise
+  if (wave == 0) {
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) lsum = lsum + __shfl_xor(lsum, off);
-  if (lane == 0) lred[wave] = lsum;
-  __syncthreads();
+    for (int jq = 0; jq < NQG; ++jq) {
+      float v = lsum[jq];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off);
+      if (lane == 0) lred[jq] = v;
+    }
+  }
+  __syncthreads();  // l, and every weight sum, are complete
   float *rec = part + (((int64_t)h * nsplit + sp) * NqT + q0) * pf;
   // lanes 0..15 hold rows (queries) 0..3 of their channel columns
   if (lane < 16) {
@@ -1200,7 +1245,7 @@ __global__ __launch_bounds__(256) void k_attn_values_mq(const float *__restrict_
     for (int c = 0; c < CTW; ++c)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (r < Nq) rec[r * pf + 2 + (wave * CTW + c) * 16 + lane] = acc[c][r];
+        if (r < Nq) rec[r * pf + 2 + wave * CW + c * 16 + lane] = acc[c][r];
   }
 #pragma unroll
   for (int jq = 0; jq < NQG; ++jq)
