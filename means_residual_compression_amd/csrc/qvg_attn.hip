@@ -1274,7 +1274,7 @@ __global__ __launch_bounds__(256) void k_attn_values1(const float *__restrict__ 
   constexpr int LPT = D / 32, TPP = 256 / LPT;  // lanes per token, tokens per pass
   constexpr int NW = BITS == 2 ? 2 : 4;         // code words (32 bits) per lane
   constexpr int WCH = TPP / 64;                 // 64-token chunks per pass (weight sums)
-  __shared__ float4 lut2[BITS == 2 ? 256 : 1];
+  __shared__ float2 lutn[BITS == 2 ? 16 : 1];     // INT2 levels by nibble
   __shared__ float4 lut4v[BITS == 4 ? 128 : 1];  // [256] float2, 16-byte aligned
   __shared__ float mred[4];
   __shared__ float lred;
@@ -1286,7 +1286,11 @@ __global__ __launch_bounds__(256) void k_attn_values1(const float *__restrict__ 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int part_ = t % LPT, tok = t / LPT, k0 = part_ * 32;
   const int T = vr.T, C = vr.C, TC = T * C, vg = __builtin_ctz(vr.G);
-  init_level_lut<BITS>(lut2, lut4);
+  if constexpr (BITS == 2) {
+    if (t < 16) lutn[t] = make_float2((float)(2 * (t & 3) - 3), (float)(2 * (t >> 2) - 3));
+  } else {
+    init_level_lut<BITS>(nullptr, lut4);
+  }
   for (int x = t; x < TC; x += 256) ws[x] = 0ull;
   const float *sh = scores + (int64_t)h * N;
   const int ntiles = (N + kAttnBN - 1) / kAttnBN;
@@ -1352,7 +1356,16 @@ __global__ __launch_bounds__(256) void k_attn_values1(const float *__restrict__ 
     for (int g = 0; g < 4; ++g) {
       float lv[8];
       const uint32_t w = BITS == 2 ? (cur.w[g >> 1] >> (16 * (g & 1))) & 0xFFFFu : cur.w[g];
-      levels8(w, BITS, lut2, lut4, lv);
+      if constexpr (BITS == 2) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {  // codes 2m, 2m+1
+          const float2 x = lutn[(w >> (4 * m)) & 0xFu];
+          lv[2 * m] = x.x;
+          lv[2 * m + 1] = x.y;
+        }
+      } else {
+        levels8(w, BITS, nullptr, lut4, lv);
+      }
       const float ps = p * e4m3_decode_bits(cur.e[g]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[8 * g + e] = __builtin_fmaf(ps, lv[e], o[8 * g + e]);
