@@ -190,6 +190,9 @@ CASES = [
     (4, 700, 128, 5, (3, 256, 2, 64), (1, 256, 2, 64), torch.bfloat16, True),
     # 16 queries whose weight sums do not fit (T*C = 2048): rebuilt values
     (2, 2500, 128, 16, (2, 64, 2, 64), (8, 256, 2, 64), torch.bfloat16, False),
+    # two passes with value records of more than 4 stages (INT2 and INT4)
+    (2, 1500, 128, 6, (2, 64, 2, 64), (8, 64, 2, 32), torch.bfloat16, True),
+    (1, 2000, 64, 3, (1, 32, 4, 16), (6, 32, 4, 16), torch.bfloat16, False),
 ]
 
 
