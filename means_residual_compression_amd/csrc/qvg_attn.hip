@@ -1326,8 +1326,6 @@ __global__ __launch_bounds__(256) void k_attn_values1(const float *__restrict__ 
       r.a[c] = wave < T ? vr.assign[((int64_t)h * T + wave) * N + tl] : 0u;
     }
   };
-  Raw cur;
-  fetch(r0, cur);
   // m: the run's largest score (8 loads in flight per round)
   {
     float m = -__builtin_inff();
@@ -1347,15 +1345,15 @@ __global__ __launch_bounds__(256) void k_attn_values1(const float *__restrict__ 
   float o[32], l = 0.0f;
 #pragma unroll
   for (int e = 0; e < 32; ++e) o[e] = 0.0f;
-  for (int b0 = r0; b0 < r1; b0 += TPP) {
-    Raw nx;
-    fetch(min(b0 + TPP, r1 - 1), nx);
+  // pass k's loads sit in buffer k mod kValuesAhead, issued kValuesAhead
+  // passes before its use; every path issues the same loads
+  auto process = [&](int b0, const Raw &r) {
     // residual term: this lane's 32 channels of its token
-    const float p = b0 + tok < r1 ? __expf(cur.s - M) : 0.0f;
+    const float p = b0 + tok < r1 ? __expf(r.s - M) : 0.0f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       float lv[8];
-      const uint32_t w = BITS == 2 ? (cur.w[g >> 1] >> (16 * (g & 1))) & 0xFFFFu : cur.w[g];
+      const uint32_t w = BITS == 2 ? (r.w[g >> 1] >> (16 * (g & 1))) & 0xFFFFu : r.w[g];
       if constexpr (BITS == 2) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {  // codes 2m, 2m+1
@@ -1366,7 +1364,7 @@ __global__ __launch_bounds__(256) void k_attn_values1(const float *__restrict__ 
       } else {
         levels8(w, BITS, nullptr, lut4, lv);
       }
-      const float ps = p * e4m3_decode_bits(cur.e[g]);
+      const float ps = p * e4m3_decode_bits(r.e[g]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[8 * g + e] = __builtin_fmaf(ps, lv[e], o[8 * g + e]);
     }
@@ -1375,17 +1373,27 @@ __global__ __launch_bounds__(256) void k_attn_values1(const float *__restrict__ 
 #pragma unroll
       for (int c = 0; c < WCH; ++c) {
         const bool valid = b0 + 64 * c + lane < r1;
-        const float pw = valid ? __expf(cur.sw[c] - M) : 0.0f;
+        const float pw = valid ? __expf(r.sw[c] - M) : 0.0f;
         if (wave == 0) l += pw;
         const unsigned long long pq = __float2ull_rn(pw * 0x1p40f);
         const int tl = min(b0 + 64 * c + lane, r1 - 1);
         for (int ts = wave; ts < T; ts += 4) {
-          const uint32_t raw = ts == wave ? cur.a[c] : vr.assign[((int64_t)h * T + ts) * N + tl];
+          const uint32_t raw = ts == wave ? r.a[c] : vr.assign[((int64_t)h * T + ts) * N + tl];
           if (valid) atomicAdd(ws + ts * C + min((int)raw, C - 1), pq);
         }
       }
     }
-    cur = nx;
+  };
+  Raw buf[kValuesAhead];
+#pragma unroll
+  for (int q = 0; q < kValuesAhead; ++q) fetch(min(r0 + q * TPP, r1 - 1), buf[q]);
+  for (int b0 = r0; b0 < r1; b0 += kValuesAhead * TPP) {
+#pragma unroll
+    for (int q = 0; q < kValuesAhead; ++q) {
+      const int bq = b0 + q * TPP;
+      if (bq < r1) process(bq, buf[q]);  // uniform
+      fetch(min(bq + kValuesAhead * TPP, r1 - 1), buf[q]);
+    }
   }
   // combine: lanes of one channel range are lane % LPT apart by multiples of
   // LPT within a wave (added pairwise), then the 4 waves in order
