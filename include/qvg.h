@@ -287,7 +287,7 @@ qvg_status qvg_group_quant_pack(const void *r, qvg_dtype dtype, int64_t H, int64
  *     multiply-add and adds).
  *   With bf16 centroids, keys of 1 to 4 stages, weight sums, N*2d < 2^32
  *   and H <= 256, the call takes two passes instead (same runs for the
- *   values; queries in groups of 4, each group's weight sums held at once).
+ *   values; every query's weight sums held at once).
  *   The scores first: for one query, d/8 (d/4 for d = 64) fused
  *   multiply-add chains of 16 terms added pairwise, times scale; for 2 to
  *   16 queries, each query split into two bf16 parts, hi = bf16(q) and

@@ -15,10 +15,12 @@ constexpr int kAttnBN = 64;
 constexpr int kAttnTargetGroups = 2048;
 constexpr int kAttnMaxSplit = 1024;
 constexpr int kAttnMaxQueries = 16;
-// Value path by per-centroid weight sums: up to this many queries per
-// workgroup, and while their T * C weight sums each fit this many entries of
-// LDS in all.  The one-pass path handles all queries in one workgroup; the
-// two-pass path takes up to kAttnMaxQueries queries in groups of this many.
+// Value path by per-centroid weight sums: on the one-pass path up to this
+// many queries, while their T * C weight sums fit kAttnSumEntries entries of
+// LDS in all; on the two-pass path up to kAttnMaxQueries queries while this
+// many (or Nq, if fewer) queries' sums would fit, i.e. all Nq queries' sums
+// fit 4 * kAttnSumEntries (k_attn_values_mq takes up to this many queries,
+// k_attn_values_all more).
 constexpr int kAttnSumQueries = 4;
 constexpr int kAttnSumEntries = 4096;
 struct AttnRec {
@@ -31,8 +33,7 @@ struct AttnSplit {
 };
 AttnSplit attn_split(int H, int64_t N);
 // Whether the values go through per-centroid weight sums on the one-pass
-// path (all Nq queries in one workgroup) and on the two-pass path (groups of
-// kAttnSumQueries) (see qvg_attn.hip).
+// path and on the two-pass path (see qvg_attn.hip).
 bool attn_sums_one_pass(int Nq, int T, int C);
 bool attn_sums_two_pass(int Nq, int T, int C);
 // Whether the call takes the two-pass path (scores, then values):

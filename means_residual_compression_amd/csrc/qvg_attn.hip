@@ -1011,8 +1011,8 @@ __global__ __launch_bounds__(256) void k_attn_scores_mq(const float *__restrict_
   }
 }
 
-// Values of up to kAttnSumQueries queries per launch (2 to 16 per call),
-// the residual term on the matrix cores.  Each wave owns d/4 channels and
+// Values of 2 to kAttnSumQueries queries, the residual term on the matrix
+// cores.  Each wave owns d/4 channels and
 // runs without workgroup barriers: per 64-token tile it
 //  * takes the weights p = e^(s - m) of every token (lane) and query, and
 //    stores them as two bf16 parts (hi = bf16(p), lo = bf16(p - hi),
@@ -1032,8 +1032,8 @@ constexpr int kValuesAhead = 4;
 template <int D, int BITS, int PT>
 __global__ __launch_bounds__(256) void k_attn_values_mq(const float *__restrict__ scores, int Nq,
                                                         int N, int H, AttnRec vr, int nsplit,
-                                                        int tps, int pf, float *__restrict__ part,
-                                                        int q0, int NqT) {
+                                                        int tps, int pf,
+                                                        float *__restrict__ part) {
   constexpr int NQG = kAttnSumQueries;  // queries per launch
   constexpr int CW = D / 4;              // channels per wave
   constexpr int CTW = CW / 16;           // 16-channel tiles per wave
@@ -1062,7 +1062,7 @@ __global__ __launch_bounds__(256) void k_attn_values_mq(const float *__restrict_
     init_level_lut<BITS>(nullptr, lut4);
   }
   for (int x = t; x < Nq * TC; x += 256) ws[x] = 0ull;
-  const float *sh = scores + ((int64_t)h * NqT + q0) * N;  // this launch's queries
+  const float *sh = scores + (int64_t)h * Nq * N;
   const int ntiles = (N + kAttnBN - 1) / kAttnBN;
   const int tb = sp * tps, te = min(tb + tps, ntiles);
   // M: the run's largest score per query
@@ -1238,7 +1238,7 @@ __global__ __launch_bounds__(256) void k_attn_values_mq(const float *__restrict_
     }
   }
   __syncthreads();  // l, and every weight sum, are complete
-  float *rec = part + (((int64_t)h * nsplit + sp) * NqT + q0) * pf;
+  float *rec = part + ((int64_t)h * nsplit + sp) * Nq * pf;
   // lanes 0..15 hold rows (queries) 0..3 of their channel columns
   if (lane < 16) {
 #pragma unroll
@@ -1254,6 +1254,225 @@ __global__ __launch_bounds__(256) void k_attn_values_mq(const float *__restrict_
       rec[jq * pf + 1] = lred[jq];
     }
   for (int x = t; x < Nq * TC; x += 256) {
+    const int jq = x / TC;
+    rec[jq * pf + 2 + D + (x - jq * TC)] = __ull2float_rn(ws[x]) * 0x1p-40f;
+  }
+}
+
+// Values of 2 to 16 queries in one launch, the residual term on the matrix
+// cores.  A workgroup of d/16 waves takes one run; every query's weight sums
+// sit in LDS at once (Nq*T*C 64-bit integers), so the value record is read
+// once per call.  Per 64-token tile:
+//  * thread (query q = w + k*d/16, token = lane) takes its weight
+//    p = e^(s - m_q), adds it to its l, stores it as two bf16 parts (hi =
+//    bf16(p), lo = bf16(p - hi), |p - hi - lo| <= 2^-16 p) in the shared P
+//    tile (double-buffered: one barrier per tile), and adds it, rounded to a
+//    multiple of 2^-40, to the weight sum of the token's cluster in every
+//    stage (exact in any order);
+//  * wave w decodes level * s_hat of its 16 channels (exact in bf16) into its
+//    own transposed tile V^T, ordered before its reads by the wave's in-order
+//    LDS queue;
+//  * after the barrier, wave w multiplies P (A: 16 queries x tokens) by its
+//    V^T (B: tokens x 16 channels) with v_mfma_f32_16x16x32_bf16, hi parts
+//    then lo parts of each 32-token block, accumulating in fp32.
+// Tile granules are XOR-swizzled by row (bank spread); loads run
+// kValuesAhead tiles ahead.
+template <int D, int BITS, int PT>
+__global__ __launch_bounds__(D * 4) void k_attn_values_all(const float *__restrict__ scores, int Nq,
+                                                           int N, int H, AttnRec vr, int nsplit,
+                                                           int tps, int pf,
+                                                           float *__restrict__ part) {
+  constexpr int NW = D / 16;             // waves, one 16-channel tile each
+  constexpr int NT = NW * 64;            // threads
+  constexpr int QPT = kAttnMaxQueries / NW;  // (query, token) weights per thread and tile
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  typedef float floatx4_t __attribute__((ext_vector_type(4)));
+  __shared__ float2 lutn[BITS == 2 ? 16 : 1];
+  __shared__ float4 lut4v[BITS == 4 ? 128 : 1];
+  __shared__ __align__(16) uint16_t vt_all[NW][16 * kAttnBN];  // per wave V^T
+  __shared__ __align__(16) uint16_t pt_all[2][2 * 16 * kAttnBN];  // P: [buf][part][query][token]
+  __shared__ float mred[NW][kAttnMaxQueries], lred[kAttnMaxQueries], Ms[kAttnMaxQueries];
+  float2 *lut4 = reinterpret_cast<float2 *>(lut4v);
+  extern __shared__ unsigned long long ws[];  // [Nq][T][C] weight sums in units of 2^-40
+  int h, sp;
+  attn_item(H, nsplit, h, sp);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int T = vr.T, C = vr.C, TC = T * C, vg = __builtin_ctz(vr.G);
+  uint16_t *vt = vt_all[wave];
+  if constexpr (BITS == 2) {
+    if (t < 16) lutn[t] = make_float2((float)(2 * (t & 3) - 3), (float)(2 * (t >> 2) - 3));
+  } else {
+    if (t < 256) lut4[t] = make_float2((float)(2 * (t & 15) - 15), (float)(2 * ((t >> 4) & 15) - 15));
+  }
+  for (int x = t; x < Nq * TC; x += NT) ws[x] = 0ull;
+  const float *sh = scores + (int64_t)h * Nq * N;
+  const int ntiles = (N + kAttnBN - 1) / kAttnBN;
+  const int tb = sp * tps, te = min(tb + tps, ntiles);
+  // the run's largest score per query
+  const int r0 = tb * kAttnBN, r1 = min(te * kAttnBN, N);
+  for (int jq = 0; jq < Nq; ++jq) {
+    float m = -__builtin_inff();
+    for (int i0 = r0 + t; i0 < r1; i0 += NT * 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = sh[(int64_t)jq * N + min(i0 + NT * u, r1 - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) m = fmaxf(m, v[u]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) mred[wave][jq] = m;
+  }
+  __syncthreads();
+  if (t < kAttnMaxQueries) {
+    float m = -__builtin_inff();
+    if (t < Nq)
+#pragma unroll
+      for (int w = 0; w < NW; ++w) m = fmaxf(m, mred[w][t]);
+    Ms[t] = m;
+  }
+  __syncthreads();  // also orders the level table and the cleared sums
+  float Mq[QPT];
+  bool qok[QPT];
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int qq = wave + k * NW;
+    qok[k] = qq < Nq;
+    Mq[k] = qok[k] ? Ms[qq] : 0.0f;
+  }
+  // decode role: tokens 2g, 2g+1, channels 16*wave + 8*c8 .. +7
+  const int g = lane & 31, c8 = lane >> 5;
+  const int kw = wave * 16 + c8 * 8;
+  const int dv = __builtin_ctz(D) - vg;
+  const uint8_t *codes = vr.codes + (int64_t)h * N * (D * BITS / 8);
+  const uint8_t *scl = vr.scales + ((int64_t)h * N << dv);
+  const uint8_t *asg = vr.assign + (int64_t)h * T * N;
+  const int Tl = max(T - 1, 0);
+  struct Raw {
+    float s[QPT];
+    uint32_t a[PT];
+    uint32_t w[2], e[2];
+  };
+  auto fetch = [&](int tile, Raw &r) {
+    const int i0 = tile * kAttnBN, nt = min(kAttnBN, N - i0);
+    const int tl = i0 + min(lane, nt - 1);
+#pragma unroll
+    for (int k = 0; k < QPT; ++k)
+      r.s[k] = qok[k] ? sh[(int64_t)(wave + k * NW) * N + tl] : 0.0f;
+    if (T > 0) {  // uniform; stages past T repeat the last one (unused)
+#pragma unroll
+      for (int u = 0; u < PT; ++u) r.a[u] = asg[(int64_t)min(u, Tl) * N + tl];
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int ti = i0 + min(2 * g + u, nt - 1);
+      load_codes<BITS, 1>(codes + (int64_t)ti * (D * BITS / 8), kw, &r.w[u]);
+      r.e[u] = scl[((int64_t)ti << dv) + (kw >> vg)];
+    }
+  };
+  float lsum[QPT];
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) lsum[k] = 0.0f;
+  floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int qi = lane & 15, kq = lane >> 4;
+  auto process = [&](int tile, const Raw &r) {
+    const int nt = min(kAttnBN, N - tile * kAttnBN);
+    uint16_t *pt = pt_all[(tile - tb) & 1];
+    // weights of (query wave + k*NW, token lane)
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int qq = wave + k * NW;
+      const bool ok = qok[k] && lane < nt;
+      const float p = ok ? __expf(r.s[k] - Mq[k]) : 0.0f;
+      lsum[k] += p;
+      const uint32_t hi = pack_bf16_rne(0.0f, p) >> 16;
+      const float rem = p - __uint_as_float(hi << 16);  // exact
+      const uint32_t lo = pack_bf16_rne(0.0f, rem) >> 16;
+      const int col = (((lane >> 3) ^ (qq & 7)) << 3) | (lane & 7);
+      pt[(0 * 16 + qq) * kAttnBN + col] = (uint16_t)hi;
+      pt[(1 * 16 + qq) * kAttnBN + col] = (uint16_t)lo;
+      if (ok) {
+        const unsigned long long pq = __float2ull_rn(p * 0x1p40f);
+#pragma unroll
+        for (int ts = 0; ts < PT; ++ts)
+          if (ts < T) atomicAdd(ws + (qq * T + ts) * C + min((int)r.a[ts], C - 1), pq);
+      }
+    }
+    // level * s_hat of tokens 2g, 2g+1 and this lane's 8 channels into V^T
+    {
+      float v[2][8];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if constexpr (BITS == 2) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {  // codes 2m, 2m+1
+            const float2 x = lutn[(r.w[u] >> (4 * m)) & 0xFu];
+            v[u][2 * m] = x.x;
+            v[u][2 * m + 1] = x.y;
+          }
+        } else {
+          levels8(r.w[u], BITS, nullptr, lut4, v[u]);
+        }
+        const float shat = e4m3_decode_bits(r.e[u]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[u][e] = v[u][e] * shat;  // exact
+      }
+      const int n0 = 2 * g;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = c8 * 8 + e;
+        *reinterpret_cast<uint32_t *>(vt + k * kAttnBN + ((((n0 >> 3) ^ e) << 3) | (n0 & 7))) =
+            pack_bf16_rne(v[0][e], v[1][e]);
+      }
+    }
+    __syncthreads();  // the P tile is complete (it is rewritten two tiles on)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int gr = ks * 4 + kq;  // 8-token granule of the block
+      uint4 ah = make_uint4(0u, 0u, 0u, 0u), al = ah;
+      if (qi < Nq) {
+        const int col = (gr ^ (qi & 7)) << 3;
+        ah = *reinterpret_cast<const uint4 *>(pt + (0 * 16 + qi) * kAttnBN + col);
+        al = *reinterpret_cast<const uint4 *>(pt + (1 * 16 + qi) * kAttnBN + col);
+      }
+      const uint4 bv = *reinterpret_cast<const uint4 *>(vt + qi * kAttnBN + ((gr ^ (qi & 7)) << 3));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah),
+                                                    __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al),
+                                                    __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+    }
+  };
+  Raw buf[kValuesAhead];
+#pragma unroll
+  for (int k = 0; k < kValuesAhead; ++k) fetch(min(tb + k, te - 1), buf[k]);
+  for (int tile = tb; tile < te; tile += kValuesAhead) {
+#pragma unroll
+    for (int k = 0; k < kValuesAhead; ++k) {
+      if (tile + k < te) process(tile + k, buf[k]);  // uniform
+      fetch(min(tile + k + kValuesAhead, te - 1), buf[k]);
+    }
+  }
+  // l of queries wave + k*NW: the wave's lanes, pairwise
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    float v = lsum[k];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off);
+    if (lane == 0) lred[wave + k * NW] = v;
+  }
+  __syncthreads();  // l, and every weight sum, are complete
+  float *rec = part + ((int64_t)h * nsplit + sp) * Nq * pf;
+  // lane l holds queries 4*(l/16) .. +3 of channel 16*wave + l % 16
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int qq = kq * 4 + r;
+    if (qq < Nq) rec[qq * pf + 2 + wave * 16 + qi] = acc[r];
+  }
+  if (t < Nq) {
+    rec[t * pf] = Ms[t];
+    rec[t * pf + 1] = lred[t];
+  }
+  for (int x = t; x < Nq * TC; x += NT) {
     const int jq = x / TC;
     rec[jq * pf + 2 + D + (x - jq * TC)] = __ull2float_rn(ws[x]) * 0x1p-40f;
   }
@@ -1536,24 +1755,49 @@ bool launch_attn_2p(const float *q, int H, int Nq, int N, const AttnRec &kr, con
       hipLaunchKernelGGL((k_attn_values1<D, 4>), dim3(H * sp.nsplit), dim3(256), lds, s, scores,
                          N, H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
   } else {
-    // the values in groups of up to kAttnSumQueries queries, whose weight
-    // sums fit in LDS; the scores pass served all of them at once
-    for (int q0 = 0; q0 < Nq; q0 += kAttnSumQueries) {
-      const int nq = std::min(kAttnSumQueries, Nq - q0);
-      const size_t lds = (size_t)nq * TC * sizeof(unsigned long long);
+    // more than kAttnSumQueries queries: one launch with every query's
+    // weight sums at once (Nq*T*C <= 16384 64-bit words), so the value record
+    // is read once; otherwise one launch of the per-wave kernel
+    if (Nq > kAttnSumQueries) {
+      static const bool lds_ok =
+          hipFuncSetAttribute((const void *)k_attn_values_all<D, 2, 4>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024) == hipSuccess &&
+          hipFuncSetAttribute((const void *)k_attn_values_all<D, 2, kMaxT>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024) == hipSuccess &&
+          hipFuncSetAttribute((const void *)k_attn_values_all<D, 4, 4>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024) == hipSuccess &&
+          hipFuncSetAttribute((const void *)k_attn_values_all<D, 4, kMaxT>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024) == hipSuccess;
+      if (!lds_ok) return false;
+      const size_t lds = (size_t)Nq * TC * sizeof(unsigned long long);
+      const dim3 grid(H * sp.nsplit), block(D * 4);
+      if (vr.bits == 2 && vr.T <= 4)
+        hipLaunchKernelGGL((k_attn_values_all<D, 2, 4>), grid, block, lds, s, scores, Nq, N, H, vr,
+                           sp.nsplit, sp.tiles_per_split, pf, part);
+      else if (vr.bits == 2)
+        hipLaunchKernelGGL((k_attn_values_all<D, 2, kMaxT>), grid, block, lds, s, scores, Nq, N, H,
+                           vr, sp.nsplit, sp.tiles_per_split, pf, part);
+      else if (vr.T <= 4)
+        hipLaunchKernelGGL((k_attn_values_all<D, 4, 4>), grid, block, lds, s, scores, Nq, N, H, vr,
+                           sp.nsplit, sp.tiles_per_split, pf, part);
+      else
+        hipLaunchKernelGGL((k_attn_values_all<D, 4, kMaxT>), grid, block, lds, s, scores, Nq, N, H,
+                           vr, sp.nsplit, sp.tiles_per_split, pf, part);
+    } else {
+      const size_t lds = (size_t)Nq * TC * sizeof(unsigned long long);
       const dim3 grid(H * sp.nsplit);
       if (vr.bits == 2 && vr.T <= 4)
-        hipLaunchKernelGGL((k_attn_values_mq<D, 2, 4>), grid, dim3(256), lds, s, scores, nq, N, H,
-                           vr, sp.nsplit, sp.tiles_per_split, pf, part, q0, Nq);
+        hipLaunchKernelGGL((k_attn_values_mq<D, 2, 4>), grid, dim3(256), lds, s, scores, Nq, N, H,
+                           vr, sp.nsplit, sp.tiles_per_split, pf, part);
       else if (vr.bits == 2)
-        hipLaunchKernelGGL((k_attn_values_mq<D, 2, kMaxT>), grid, dim3(256), lds, s, scores, nq, N,
-                           H, vr, sp.nsplit, sp.tiles_per_split, pf, part, q0, Nq);
+        hipLaunchKernelGGL((k_attn_values_mq<D, 2, kMaxT>), grid, dim3(256), lds, s, scores, Nq, N,
+                           H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
       else if (vr.T <= 4)
-        hipLaunchKernelGGL((k_attn_values_mq<D, 4, 4>), grid, dim3(256), lds, s, scores, nq, N, H,
-                           vr, sp.nsplit, sp.tiles_per_split, pf, part, q0, Nq);
+        hipLaunchKernelGGL((k_attn_values_mq<D, 4, 4>), grid, dim3(256), lds, s, scores, Nq, N, H,
+                           vr, sp.nsplit, sp.tiles_per_split, pf, part);
       else
-        hipLaunchKernelGGL((k_attn_values_mq<D, 4, kMaxT>), grid, dim3(256), lds, s, scores, nq, N,
-                           H, vr, sp.nsplit, sp.tiles_per_split, pf, part, q0, Nq);
+        hipLaunchKernelGGL((k_attn_values_mq<D, 4, kMaxT>), grid, dim3(256), lds, s, scores, Nq, N,
+                           H, vr, sp.nsplit, sp.tiles_per_split, pf, part);
     }
   }
   if (hipGetLastError() != hipSuccess) return false;
