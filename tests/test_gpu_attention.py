@@ -193,6 +193,8 @@ CASES = [
     # two passes with value records of more than 4 stages (INT2 and INT4)
     (2, 1500, 128, 6, (2, 64, 2, 64), (8, 64, 2, 32), torch.bfloat16, True),
     (1, 2000, 64, 3, (1, 32, 4, 16), (6, 32, 4, 16), torch.bfloat16, False),
+    # more than 4 queries in one values launch: d=64, INT4 values of 6 stages
+    (2, 1800, 64, 9, (2, 64, 2, 32), (6, 32, 4, 16), torch.bfloat16, True),
 ]
 
 
